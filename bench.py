@@ -1,0 +1,252 @@
+"""Benchmark of the sparse video attention path on one MI355X.
+
+One step = one pass of the whole SVG1 hot path over the HunyuanVideo-shaped
+layer workload.  Shape: 33 frames x 3600 tokens + 256 text tokens
+(N = 119,056; 118,800 of them video), 24 heads, d = 128, bf16, 128x64 tiles,
+masks at ~31% tile density.  The pass:
+    profile heads (1191 sampled rows) -> block masks -> CSR lists
+    -> permute Q, K, V -> block-sparse attention -> unpermute O
+Inputs are synthetic and seeded (synth/), resident in HBM before timing.
+
+Printed metric: effective block-sparse attention TFLOP/s.  The flop count is
+4*d per valid (query, key) pair inside the kept tiles, divided by the whole
+step time.  Also reported: the attention kernel's own rate (HIP events on
+its stream), the speedup over this library's dense attention on the same
+tensors, per-stage times, the MFMA roofline fraction, and the CPU oracle's
+rate on a bounded sample.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA peak
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--dense-reps", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--density", default="k5", help="mask widths: k5 (31%%), k4 (26%%), cog_rule (~2%%)")
+    return ap.parse_args()
+
+
+def gen_inputs(w):
+    """Seeded Q, K, V (bf16 bits) for every head, generated in parallel."""
+    import concurrent.futures
+    import numpy as np
+    from synth.generators import structured_qkv
+
+    with concurrent.futures.ThreadPoolExecutor(max_workers=8) as ex:
+        parts = list(ex.map(lambda h: structured_qkv(w, heads=[h]), range(w.H)))
+    return {x: np.concatenate([p[x] for p in parts]) for x in "qkv"}
+
+
+def cpu_baseline(w, ks, wt, labels, seconds):
+    """The oracle's block-sparse attention on a bounded sample of this
+    workload's q-blocks, in TFLOP/s with the same flop accounting."""
+    import numpy as np
+    from oracle import masks, layout, attention
+    from oracle.numerics import as_f64
+    from synth.generators import structured_qkv
+
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = cores
+    rng = np.random.default_rng(0)
+    # one head of each label present (inputs and layout prepared untimed)
+    heads = []
+    for lab in (0, 1):
+        hs = [h for h in range(w.H) if int(labels[h]) == lab]
+        if hs:
+            heads.append(hs[0])
+    prepared = []
+    for h in heads:
+        lab = int(labels[h])
+        g = structured_qkv(w, heads=[h])
+        qd, kd, vd = (as_f64(g[x][0], w.dtype) for x in "qkv")
+        xs = layout.permute(np.stack([qd, kd, vd]), w.F, w.S, w.T, [lab] * 3)
+        bm = masks.block_bitmap_ranges(lab, w.F, w.S, w.T, ks, wt, w.bq, w.bk)
+        prepared.append((h, xs, bm))
+    flops = 0.0
+    elapsed = 0.0
+    blocks = 0
+    while elapsed < seconds:
+        h, xs, bm = prepared[blocks % len(prepared)]
+        qbs = rng.integers(0, w.nqb, size=4)
+        ts = time.perf_counter()
+        attention.block_sparse_attention(xs[0], xs[1], xs[2], bm, w.bq, w.bk, qblocks=qbs)
+        elapsed += time.perf_counter() - ts
+        sub = np.zeros_like(bm)
+        sub[qbs] = bm[qbs]
+        flops += 4.0 * w.d * masks.valid_pairs(sub, w.N, w.bq, w.bk)
+        blocks += len(qbs)
+    return {"value": round(flops / elapsed / 1e12, 6), "unit": "TFLOP/s", "cores": int(min(cores, blas_threads)),
+            "kind": "oracle",
+            "sample": f"float64 numpy block-sparse attention on {blocks} random 128-row q-blocks of heads "
+                      f"{heads} of this workload, {elapsed:.1f} s of attention time"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path shards by head "
+              f"with no exchange, see the design notes.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from sparse_attention_video_online_amd import svg
+    from synth import HUNYUAN_LAYER as w
+    from synth.configs import HUNYUAN_DENSITY_POINTS
+    from synth.generators import sample_rows
+
+    ks, wt = HUNYUAN_DENSITY_POINTS[args.density]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    host = gen_inputs(w)
+    q, k, v = (torch.from_numpy(host[x].view(np.int16)).to(dev).view(torch.bfloat16) for x in "qkv")
+    del host
+    sidx = torch.from_numpy(sample_rows(w)).to(dev)
+    F, S, T, H, d, N, bq, bk = w.F, w.S, w.T, w.H, w.d, w.N, w.bq, w.bk
+    nqb, nkb = w.nqb, w.nkb
+
+    # preallocated buffers: nothing is allocated inside the timed region
+    labels = torch.empty(H, dtype=torch.int32, device=dev)
+    mse = torch.empty(H, 2, dtype=torch.float32, device=dev)
+    prof_ws = torch.empty(svg.workspace_bytes(svg.SVG_OP_PROFILE, svg.dims(F, S, T, H, d), sidx.numel()),
+                          dtype=torch.uint8, device=dev)
+    bmask = torch.empty(H, nqb, nkb, dtype=torch.uint8, device=dev)
+    rows = H * nqb
+    row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=dev)
+    kv_idx = torch.empty(rows * nkb, dtype=torch.int32, device=dev)
+    comp_ws = torch.empty(max(1, svg.lib().svg_workspace_bytes(svg.SVG_OP_COMPACT, None, rows, nkb)),
+                          dtype=torch.uint8, device=dev)
+    qp, kp, vp, op, o = (torch.empty_like(q) for _ in range(5))
+    stream = torch.cuda.current_stream()
+    ev_a0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ev_a1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+
+    def step(i=None, stage_events=None):
+        def mark(j):
+            if stage_events is not None:
+                stage_events[j].record(stream)
+        mark(0)
+        svg.svg_profile_heads(q, k, v, sidx, F, S, T, ks, wt, labels=labels, mse=mse, ws=prof_ws)
+        mark(1)
+        svg.svg_build_block_mask(labels, F, S, T, H, d, ks, wt, bq, bk, out=bmask)
+        svg.svg_compact_block_mask(bmask, row_ptr=row_ptr, kv_idx=kv_idx, ws=comp_ws)
+        mark(2)
+        svg.svg_layout_permute(q, F, S, T, labels, out=qp)
+        svg.svg_layout_permute(k, F, S, T, labels, out=kp)
+        svg.svg_layout_permute(v, F, S, T, labels, out=vp)
+        mark(3)
+        if i is not None:
+            ev_a0[i].record(stream)
+        svg.svg_block_sparse_attn_csr(qp, kp, vp, row_ptr, kv_idx, F, S, T, bq, bk, out=op)
+        if i is not None:
+            ev_a1[i].record(stream)
+        mark(4)
+        svg.svg_layout_unpermute(op, F, S, T, labels, out=o)
+        mark(5)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(ev_a0, ev_a1)]))
+    print(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step (wall {wall:.2f} s), "
+          f"attention {attn_ms:.3f} ms", file=sys.stderr, flush=True)
+
+    # per-stage breakdown (one extra step with events between stages)
+    se = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    step(None, se)
+    torch.cuda.synchronize()
+    names = ["profile", "mask_and_lists", "permute_qkv", "attention", "unpermute_o"]
+    stage_ms = {n: se[j].elapsed_time(se[j + 1]) for j, n in enumerate(names)}
+
+    # work done: valid pairs in kept tiles (from the device bitmap)
+    rows_valid = torch.clamp(N - torch.arange(nqb, device=dev) * bq, max=bq).double()
+    cols_valid = torch.clamp(N - torch.arange(nkb, device=dev) * bk, max=bk).double()
+    pairs = float((bmask.double() * rows_valid[None, :, None] * cols_valid[None, None, :]).sum())
+    flops = 4.0 * d * pairs
+    tiles = int(bmask.sum())
+    density = tiles / float(H * nqb * nkb)
+    dense_flops = 4.0 * d * float(N) * N * H
+    lab_host = labels.cpu().numpy()
+
+    # dense baseline: this library's attention with every tile kept
+    dense = torch.empty_like(q)
+    svg.svg_dense_attn(qp, kp, vp, F, S, T, bq, bk, out=dense)
+    torch.cuda.synchronize()
+    d0 = torch.cuda.Event(enable_timing=True)
+    d1 = torch.cuda.Event(enable_timing=True)
+    d0.record(stream)
+    for _ in range(args.dense_reps):
+        svg.svg_dense_attn(qp, kp, vp, F, S, T, bq, bk, out=dense)
+    d1.record(stream)
+    torch.cuda.synchronize()
+    dense_ms = d0.elapsed_time(d1) / args.dense_reps
+    print(f"[bench] dense attention {dense_ms:.3f} ms", file=sys.stderr, flush=True)
+
+    attn_tflops = flops / (attn_ms * 1e-3) / 1e12
+    result = {
+        "metric": "effective block-sparse attn TFLOP/s (whole SVG1 layer step) + speedup vs dense, N=119,056",
+        "value": round(flops / (ms_per_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded structured heads; no model weights)",
+        "config": {"workload": w.name, "F": F, "S": S, "T": T, "N": N, "N_video": F * S, "H": H, "d": d,
+                   "bq": bq, "bk": bk, "ks_frames": ks, "wt_tokens": wt, "n_samples": int(sidx.numel()),
+                   "tile_density": round(density, 4), "kept_tiles": tiles,
+                   "labels": "".join(str(int(x)) for x in lab_host), "parallelism": "single GPU"},
+        "attn_ms": round(attn_ms, 4),
+        "attn_tflops": round(attn_tflops, 2),
+        "dense_ms": round(dense_ms, 4),
+        "dense_tflops": round(dense_flops / (dense_ms * 1e-3) / 1e12, 2),
+        "speedup_vs_dense_attn": round(dense_ms / attn_ms, 3),
+        "speedup_vs_dense_layer": round(dense_ms / ms_per_step, 3),
+        "stage_ms": {kk: round(vv, 4) for kk, vv in stage_ms.items()},
+        "roofline": {"bound": "mfma", "kernel": "attn_fwd_mfma<128,128> (block-sparse)",
+                     "achieved": round(attn_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "flop_per_launch": flops},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, ks, wt, lab_host, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,205 @@
+/*
+ * svg.h -- C ABI of the MI355X (gfx950) sparse video attention library.
+ *
+ * The library implements the training-free sparse 3D attention of Sparse
+ * VideoGen for one GPU:
+ *   - online head profiling (spatial vs temporal);
+ *   - a frame-major <-> position-major layout permutation;
+ *   - block-sparse flash attention over kept tiles.
+ * The SVG2-style semantic path is declared in svg2.h.
+ * Sources are cited per entry point:
+ *   [SVG1]  "Sparse VideoGen: Accelerating Video Diffusion Transformers with
+ *           Spatial-Temporal Sparsity", English abstract (arxivdaily listing).
+ *   [SVG-W] "Sparse-VideoGen and the sparsity hiding inside video diffusion
+ *           attention" (project write-up), sections "Three generations of the
+ *           same idea" and the install section.
+ *   [HVA]   "HyperVAttention: Efficient Sparse Attention with Spatio-Temporal
+ *           Clustering for Video Diffusion", sections Problem and Surprising
+ *           findings.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensors are [H][N][d] contiguous, batch 1, with N = F*S + T.  Video
+ *   tokens come first in frame-major order: token (f, p) sits at f*S + p,
+ *   for frame f < F and position p < S.  The T text tokens follow.
+ * - Every tensor or index pointer is a DEVICE pointer owned by the caller.
+ *   The library never allocates, frees or synchronises device memory.  It
+ *   enqueues all work on `stream` (a hipStream_t; NULL = the null stream)
+ *   and never blocks on it.  Workspace buffers are caller-owned device
+ *   memory of at least svg_workspace_bytes(...) bytes.
+ * - Each call validates its arguments on the host before it enqueues
+ *   anything.  On a bad argument it returns a non-zero svg_status and
+ *   enqueues nothing.  svg_last_error() then gives a message (per host
+ *   thread).
+ * - A HIP launch failure returns SVG_ERR_HIP, with the HIP error name in
+ *   svg_last_error().  Faults inside a kernel surface on the caller's next
+ *   synchronisation, as with any HIP kernel.
+ * - Device-resident index inputs (sample_idx, labels, init_idx, CSR lists,
+ *   offsets, permutations) are the caller's contract.  Kernels clamp
+ *   nothing: out-of-range indices are undefined behaviour.
+ * - softmax_scale < 0 selects 1/sqrt(d).
+ * - Block shapes (bq x bk): (16,16), (64,64), (128,64).  Head dim d: 64 or
+ *   128.  bf16 inputs use MFMA kernels for (64,64) and (128,64).
+ *   fp32 inputs, and bf16 at (16,16), use the plain vector kernels.
+ */
+#ifndef SVG_H_
+#define SVG_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SVG_OK = 0,
+  SVG_ERR_NULL = 1,         /* a required pointer is NULL                    */
+  SVG_ERR_SHAPE = 2,        /* sizes out of range or inconsistent            */
+  SVG_ERR_DTYPE = 3,        /* unknown dtype                                 */
+  SVG_ERR_UNSUPPORTED = 4,  /* head dim / block shape without a kernel       */
+  SVG_ERR_RANGE = 5,        /* bad parameter value, or input aliases output  */
+  SVG_ERR_WORKSPACE = 6,    /* workspace missing or smaller than required    */
+  SVG_ERR_HIP = 7           /* HIP runtime error                             */
+} svg_status;
+
+typedef enum { SVG_F32 = 0, SVG_BF16 = 1 } svg_dtype;
+
+enum { SVG_SPATIAL = 0, SVG_TEMPORAL = 1 };
+
+/* Problem statement of [SVG1]: F frames of S tokens, T text tokens, H heads,
+ * head dim d.  N = F*S + T < 2^31 / d. */
+typedef struct { int32_t F, S, T, H, d; } svg_dims;
+
+/* Token masks (readings of [SVG1]):
+ *   spatial:  a video query of frame f keeps the video keys of frames
+ *             f-ks_frames .. f+ks_frames.
+ *   temporal: a video query at position p keeps the video keys whose
+ *             position-major index r = p'*F + f' lies in
+ *             [p*F - wt_tokens, p*F + F - 1 + wt_tokens].
+ *   Both:     every query keeps the text keys; a text query keeps all keys.
+ */
+typedef struct { int32_t ks_frames, wt_tokens; } svg_mask_params;
+
+/* Workspace queries.  `a`, `b` are per-op extra sizes (see each op). */
+typedef enum {
+  SVG_OP_PROFILE = 0,        /* a = n_samples                                  */
+  SVG_OP_BLOCK_SPARSE = 1,   /* a = bq, b = bk  (bitmap -> CSR inside ws)      */
+  SVG_OP_COMPACT = 2         /* a = rows, b = nKB                              */
+} svg_op;
+
+/* Bytes of workspace an op needs for these sizes (host-only, no HIP call). */
+size_t svg_workspace_bytes(svg_op op, const svg_dims *dims, int32_t a, int32_t b);
+
+/* Message of the last non-OK status returned on this host thread. */
+const char *svg_last_error(void);
+
+/* Library version string. */
+const char *svg_version(void);
+
+/* ---------------------------------------------------------------------------
+ * Online profiling ([SVG1]: an online profiling strategy predicts each head's
+ * type; [SVG-W] "Three generations": it identifies the pattern dynamically).
+ *
+ * For the sampled query rows sample_idx[0..n_samples) (original frame-major
+ * indices, shared by all heads), computes per head:
+ *   - the full attention output;
+ *   - the spatial-masked output;
+ *   - the temporal-masked output.
+ * Each softmax is normalised over its own kept keys with its own maximum.
+ * Then
+ *   mse[h][0] = mean over samples and d of (O_spatial - O_full)^2,
+ *   mse[h][1] = the same for O_temporal,
+ *   labels[h] = SVG_SPATIAL if mse[h][0] <= mse[h][1], else SVG_TEMPORAL.
+ * Q, K, V: [H][N][d] of `dtype`.  labels: int32[H].  mse: float[H][2] or
+ * NULL.  ws: svg_workspace_bytes(SVG_OP_PROFILE, dims, n_samples, 0).
+ * 1 <= n_samples <= N; sample_idx in [0, N).
+ * ------------------------------------------------------------------------- */
+svg_status svg_profile_heads(const svg_dims *dims, svg_dtype dtype,
+                             const void *Q, const void *K, const void *V,
+                             const int32_t *sample_idx, int32_t n_samples,
+                             const svg_mask_params *mask, float softmax_scale,
+                             int32_t *labels, float *mse,
+                             void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Layout transformation ([SVG1]: the hardware-efficient tensor layout
+ * transformation).
+ *
+ * svg_layout_permute:   Y[h][p*F + f] = X[h][f*S + p] for heads with
+ *                       labels[h] == SVG_TEMPORAL (position-major order).
+ *                       Text rows and other heads are copied unchanged.
+ * svg_layout_unpermute: the inverse, X[h][f*S + p] = Y[h][p*F + f].
+ * labels == NULL permutes every head.  X and Y are [H][N][d] of `dtype` and
+ * must not overlap (SVG_ERR_RANGE if X == Y).
+ * ------------------------------------------------------------------------- */
+svg_status svg_layout_permute(const svg_dims *dims, svg_dtype dtype, const void *X, void *Y,
+                              const int32_t *labels, void *stream);
+svg_status svg_layout_unpermute(const svg_dims *dims, svg_dtype dtype, const void *X, void *Y,
+                                const int32_t *labels, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Block mask ([SVG-W] install section: block-sparse attention over per-block
+ * keep flags).
+ *
+ * For each head h, takes the token mask of labels[h] in that head's
+ * executing layout:
+ *   spatial:  frame-major order (the identity);
+ *   temporal: position-major order, as produced by svg_layout_permute.
+ * block_mask[h][qb][kb] = 1 iff some query row of block qb and some key of
+ * block kb (both < N) are kept by the mask.  This is the any-overlap cover.
+ * block_mask: uint8 [H][nQB][nKB], nQB = ceil(N/bq), nKB = ceil(N/bk).
+ * ------------------------------------------------------------------------- */
+svg_status svg_build_block_mask(const svg_dims *dims, const svg_mask_params *mask,
+                                const int32_t *labels, int32_t bq, int32_t bk,
+                                uint8_t *block_mask, void *stream);
+
+/* Compacts a bitmap uint8[rows][nKB] into CSR lists.  Each row's kept
+ * column blocks are written in ascending order.
+ *   row_ptr: int32[rows + 1].  row_ptr[rows] = total kept blocks.
+ *   kv_idx:  int32 with capacity rows * nKB.
+ * ws: svg_workspace_bytes(SVG_OP_COMPACT, NULL, rows, nKB). */
+svg_status svg_compact_block_mask(int32_t rows, int32_t nkb, const uint8_t *block_mask,
+                                  int32_t *row_ptr, int32_t *kv_idx,
+                                  void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Block-sparse flash attention ([SVG1]: custom kernels on the transformed
+ * layout; [SVG-W] install section: block-sparse attention).
+ *
+ * For query row i of q-block qb:
+ *   O[h][i] = sum_j softmax_j(scale * Q[h][i] . K[h][j]) V[h][j]
+ * over exactly the keys j < N of the kept tiles (qb, kb).  Kept tiles are
+ * computed whole, and skipped tiles cost no memory traffic.  A row with no
+ * kept tile gets O = 0.  Accumulation is fp32.  O has the input dtype.
+ * Q, K, V, O: [H][N][d] in the executing layout; O must not alias the
+ * inputs.
+ *
+ * svg_block_sparse_attn:     takes the bitmap, compacts it into ws, then
+ *                            runs the attention.  ws:
+ *                            svg_workspace_bytes(SVG_OP_BLOCK_SPARSE,
+ *                            dims, bq, bk).
+ * svg_block_sparse_attn_csr: takes prebuilt CSR lists over the H*nQB rows
+ *                            (row h*nQB + qb), ascending kv-block ids.
+ * svg_dense_attn:            every tile kept (the dense baseline), with no
+ *                            list memory.
+ * ------------------------------------------------------------------------- */
+svg_status svg_block_sparse_attn(const svg_dims *dims, svg_dtype dtype,
+                                 const void *Q, const void *K, const void *V,
+                                 const uint8_t *block_mask, int32_t bq, int32_t bk,
+                                 float softmax_scale, void *O,
+                                 void *ws, size_t ws_bytes, void *stream);
+svg_status svg_block_sparse_attn_csr(const svg_dims *dims, svg_dtype dtype,
+                                     const void *Q, const void *K, const void *V,
+                                     const int32_t *row_ptr, const int32_t *kv_idx,
+                                     int32_t bq, int32_t bk, float softmax_scale,
+                                     void *O, void *stream);
+svg_status svg_dense_attn(const svg_dims *dims, svg_dtype dtype,
+                          const void *Q, const void *K, const void *V,
+                          int32_t bq, int32_t bk, float softmax_scale,
+                          void *O, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SVG_H_ */

@@ -1,0 +1,231 @@
+// Building blocks of the gfx950 MFMA flash-attention kernels (internal).
+//
+// Layout of one wave's work (32 queries, 64-key tiles, head dim D):
+//   S^T = K Q^T with v_mfma_f32_32x32x16_bf16.  A = K rows from LDS.  B =
+//   the wave's Q rows, held in registers for the whole key loop.  Lane l
+//   serves query (l & 31).  Its 16 accumulator values per 32-key block are
+//   keys 8*(r/4) + 4*(l/32) + (r%4), r = 0..15.  So lanes l and l^32 split
+//   one query's keys.
+//   O^T += V^T P^T.  B = P^T straight from the S^T accumulator registers,
+//   rounded to bf16.  A = V^T from LDS, stored with each 16-key chunk's
+//   keys in the order {0-3, 8-11 | 4-7, 12-15}: the two lane halves'
+//   accumulator key order.  The reduction index of the MFMA then pairs each
+//   P value with its own V row.
+#pragma once
+
+#include "svg_common.h"
+
+namespace svgk {
+namespace core {
+
+constexpr int BK = 64;
+
+template <int D, int NT>
+struct Tile {
+  static constexpr int KSTR = D * 2 + 16;        // K row stride (bytes): padded against bank conflicts
+  static constexpr int KBYTES = BK * KSTR;
+  static constexpr int VSTR = BK * 2;            // V^T row stride (bytes): XOR-swizzled 16-byte blocks
+  static constexpr int VBYTES = D * VSTR;
+  static constexpr int STAGE = KBYTES + VBYTES;
+  static constexpr int DC = D / 8;               // 16-byte chunks per row
+  static constexpr int UNITS = (BK / 4) * DC;    // load unit = 4 consecutive keys x 8 dims
+  static constexpr int UPT = (UNITS + NT - 1) / NT;
+};
+
+// 16-byte block swizzle of V^T rows: consecutive rows (one MFMA operand
+// read) and rows 8 apart (one staging write) land on different banks.
+__device__ __forceinline__ int vt_swz(int d) { return (d ^ (d >> 3)) & 7; }
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8 &a, const bf16x8 &b, const f32x16 &c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Register staging of one K/V tile.  rowof(key_in_tile) gives the global
+// row of a key, or -1 for a key that does not exist (it is zero-filled).
+template <int D, int NT>
+struct Regs {
+  u32x4 k[Tile<D, NT>::UPT][4];
+  u32x4 v[Tile<D, NT>::UPT][4];
+};
+
+template <int D, int NT, typename RowOf>
+__device__ __forceinline__ void load_tile(const bf16_t *__restrict__ Kh, const bf16_t *__restrict__ Vh,
+                                          int tid, RowOf rowof, Regs<D, NT> &R) {
+  using C = Tile<D, NT>;
+#pragma unroll
+  for (int i = 0; i < C::UPT; ++i) {
+    const int u = tid + i * NT;
+    if (C::UNITS % NT == 0 || u < C::UNITS) {
+      const int g = u / C::DC, dc = u % C::DC;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = rowof(4 * g + r);
+        if (row >= 0) {
+          R.k[i][r] = *reinterpret_cast<const u32x4 *>(Kh + (size_t)row * D + dc * 8);
+          R.v[i][r] = *reinterpret_cast<const u32x4 *>(Vh + (size_t)row * D + dc * 8);
+        } else {
+          R.k[i][r] = u32x4{0, 0, 0, 0};
+          R.v[i][r] = u32x4{0, 0, 0, 0};
+        }
+      }
+    }
+  }
+}
+
+template <int D, int NT>
+__device__ __forceinline__ void store_tile(char *__restrict__ stage, int tid, const Regs<D, NT> &R) {
+  using C = Tile<D, NT>;
+  char *Ks = stage;
+  char *Vs = stage + C::KBYTES;
+#pragma unroll
+  for (int i = 0; i < C::UPT; ++i) {
+    const int u = tid + i * NT;
+    if (C::UNITS % NT == 0 || u < C::UNITS) {
+      const int g = u / C::DC, dc = u % C::DC;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        *reinterpret_cast<u32x4 *>(Ks + (4 * g + r) * C::KSTR + dc * 16) = R.k[i][r];
+      // keys 4g..4g+3 -> V^T slots 16*(g/4) + {0, 8, 4, 12}[g%4] .. +3
+      const int og = g & 3;
+      const int slot = 16 * (g >> 2) + (((og & 1) << 3) | ((og & 2) << 1));
+      const int blk = slot >> 3, half = (slot >> 2) & 1;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int d = dc * 8 + 2 * m + e;
+          uint32_t lo, hi;
+          if (e == 0) {
+            lo = (R.v[i][0][m] & 0xFFFFu) | (R.v[i][1][m] << 16);
+            hi = (R.v[i][2][m] & 0xFFFFu) | (R.v[i][3][m] << 16);
+          } else {
+            lo = (R.v[i][0][m] >> 16) | (R.v[i][1][m] & 0xFFFF0000u);
+            hi = (R.v[i][2][m] >> 16) | (R.v[i][3][m] & 0xFFFF0000u);
+          }
+          *reinterpret_cast<u32x2 *>(Vs + d * C::VSTR + ((blk ^ vt_swz(d)) << 4) + half * 8) =
+              u32x2{lo, hi};
+        }
+      }
+    }
+  }
+}
+
+// Q fragment of one wave: row `qrow` (or zeros when qrow < 0).
+template <int D>
+__device__ __forceinline__ void load_q(const bf16_t *__restrict__ Qh, int qrow, int hi, bf16x8 (&qf)[D / 16]) {
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    u32x4 v = u32x4{0, 0, 0, 0};
+    if (qrow >= 0) v = *reinterpret_cast<const u32x4 *>(Qh + (size_t)qrow * D + ks * 16 + hi * 8);
+    qf[ks] = __builtin_bit_cast(bf16x8, v);
+  }
+}
+
+// S^T for the 64 keys of the staged tile: s0 = keys 0-31, s1 = keys 32-63.
+template <int D, int NT>
+__device__ __forceinline__ void qk_tile(const char *__restrict__ Ks, const bf16x8 (&qf)[D / 16], int l32,
+                                        int hi, f32x16 &s0, f32x16 &s1) {
+  using C = Tile<D, NT>;
+  s0 = f32x16{};
+  s1 = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(Ks + l32 * C::KSTR + (ks * 16 + hi * 8) * 2);
+    const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(Ks + (32 + l32) * C::KSTR + (ks * 16 + hi * 8) * 2);
+    s0 = mfma32(a0, qf[ks], s0);
+    s1 = mfma32(a1, qf[ks], s1);
+  }
+}
+
+// Key index (0..63, within the tile) of accumulator value r of block b.
+__device__ __forceinline__ int acc_key(int b, int r, int hi) { return 32 * b + 8 * (r >> 2) + 4 * hi + (r & 3); }
+
+// Keys at tile positions >= nvalid do not exist: set their scores to -inf.
+__device__ __forceinline__ void mask_tail(f32x16 &s0, f32x16 &s1, int nvalid, int hi) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    if (acc_key(0, r, hi) >= nvalid) s0[r] = -INFINITY;
+    if (acc_key(1, r, hi) >= nvalid) s1[r] = -INFINITY;
+  }
+}
+
+// One online-softmax step for the lane's query.  Updates m_run (raw-score
+// max) and l_run (this lane's partial sum).  Returns the rescale factor of
+// the accumulated output.  pb = the tile's probabilities as bf16 MFMA B
+// operands, one per 16-key chunk.  c = scale * log2(e).
+__device__ __forceinline__ float softmax_step(const f32x16 &s0, const f32x16 &s1, float c, float &m_run,
+                                              float &l_run, bf16x8 (&pb)[4]) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float m_new = fmaxf(m_run, mx);
+  const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
+  const float alpha = fast_exp2((m_run - m_ref) * c);
+  m_run = m_new;
+  const float mc = m_ref * c;
+  float rs = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const f32x16 &s = (j < 2) ? s0 : s1;
+    const int base = (j & 1) * 8;
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float p0 = fast_exp2(__builtin_fmaf(s[base + 2 * i], c, -mc));
+      const float p1 = fast_exp2(__builtin_fmaf(s[base + 2 * i + 1], c, -mc));
+      rs += p0 + p1;
+      w[i] = pack_bf16x2(p0, p1);
+    }
+    pb[j] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+  }
+  l_run = l_run * alpha + rs;
+  return alpha;
+}
+
+template <int D>
+__device__ __forceinline__ void rescale(f32x16 (&o)[D / 32], float alpha) {
+  if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+  }
+}
+
+// O^T += V^T P^T for the staged tile.
+template <int D, int NT>
+__device__ __forceinline__ void pv_tile(const char *__restrict__ Vs, const bf16x8 (&pb)[4], int l32, int hi,
+                                        f32x16 (&o)[D / 32]) {
+  using C = Tile<D, NT>;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int d = 32 * db + l32;
+      const bf16x8 a = *reinterpret_cast<const bf16x8 *>(Vs + d * C::VSTR + (((2 * j + hi) ^ vt_swz(d)) << 4));
+      o[db] = mfma32(a, pb[j], o[db]);
+    }
+  }
+}
+
+// Final O row of the lane's query: O^T / l, written as bf16 (lane holds
+// dims 32*db + 8*g + 4*hi + 0..3).
+template <int D>
+__device__ __forceinline__ void store_o(bf16_t *__restrict__ orow, const f32x16 (&o)[D / 32], float l_run,
+                                        int hi) {
+  const float lt = l_run + __shfl_xor(l_run, 32);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  if (orow == nullptr) return;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = 32 * db + 8 * g + 4 * hi;
+      const uint32_t w0 = pack_bf16x2(o[db][4 * g + 0] * inv, o[db][4 * g + 1] * inv);
+      const uint32_t w1 = pack_bf16x2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+      *reinterpret_cast<u32x2 *>(orow + d0) = u32x2{w0, w1};
+    }
+  }
+}
+
+}  // namespace core
+}  // namespace svgk

@@ -1,0 +1,469 @@
+// SVG2-style semantic path: k-means of Q and K per head, stable cluster
+// permutation, top-p cluster-pair selection, and variable-size block-sparse
+// attention over the selected pairs.
+//
+// Sources: the Sparse-VideoGen write-up, section "Three generations of the
+// same idea".  SVG2 permutes tokens by semantic cluster, uses a flash
+// k-means kernel, and runs a dynamic attention kernel.  Its install section:
+// block-sparse attention with varied block sizes.  HyperVAttention, sections
+// Problem and Surprising findings: cluster blocks are irregular, so tiled
+// kernels waste work.  The varlen kernel here therefore tiles the
+// concatenation of a query cluster's selected key ranges.  It does not tile
+// each cluster on its own.
+#include "attn_core.h"
+
+namespace svgk {
+namespace {
+
+// ---------------------------------------------------------------------------
+// k-means (Lloyd).  Distances in fp32 from fp32 copies of the centroids.
+// Member sums in fp64: a sum of bf16 values is exact in fp64, so atomics in
+// any order give the same bits.
+
+template <typename T>
+__global__ __launch_bounds__(128)
+void km_init(const T *__restrict__ X, const int32_t *__restrict__ init_idx, int N, int D, int k,
+             double *__restrict__ cent) {
+  const int h = blockIdx.y, j = blockIdx.x;
+  const int src = init_idx[h * k + j];
+  for (int e = threadIdx.x; e < D; e += blockDim.x)
+    cent[((size_t)h * k + j) * D + e] = (double)to_f32<T>(X[((size_t)h * N + src) * D + e]);
+}
+
+__global__ __launch_bounds__(256)
+void km_zero(double *__restrict__ sums, int32_t *__restrict__ counts, size_t nsum, size_t ncnt) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < nsum) sums[i] = 0.0;
+  if (i < ncnt) counts[i] = 0;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256)
+void km_assign(const T *__restrict__ X, const double *__restrict__ cent, int N, int k,
+               int32_t *__restrict__ assign, double *__restrict__ sums, int32_t *__restrict__ counts) {
+  extern __shared__ float cs[];  // [k][D]
+  const int h = blockIdx.y;
+  const double *ch = cent + (size_t)h * k * D;
+  for (int e = threadIdx.x; e < k * D; e += blockDim.x) cs[e] = (float)ch[e];
+  __syncthreads();
+  const int n = blockIdx.x * blockDim.x + threadIdx.x;
+  if (n >= N) return;
+  const T *xr = X + ((size_t)h * N + n) * D;
+  float x[D];
+#pragma unroll
+  for (int e = 0; e < D; ++e) x[e] = to_f32<T>(xr[e]);
+  float best = INFINITY;
+  int arg = 0;
+  for (int j = 0; j < k; ++j) {
+    const float *c = cs + j * D;
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < D; ++e) {
+      const float df = x[e] - c[e];
+      s = __builtin_fmaf(df, df, s);
+    }
+    if (s < best) {  // strict: ties keep the lower index
+      best = s;
+      arg = j;
+    }
+  }
+  assign[(size_t)h * N + n] = arg;
+  atomicAdd(&counts[h * k + arg], 1);
+  double *sr = sums + ((size_t)h * k + arg) * D;
+#pragma unroll
+  for (int e = 0; e < D; ++e) atomicAdd(&sr[e], (double)x[e]);
+}
+
+__global__ __launch_bounds__(128)
+void km_finalize(double *__restrict__ cent, double *__restrict__ sums, int32_t *__restrict__ counts,
+                 int32_t *__restrict__ sizes, int k, int D) {
+  const int h = blockIdx.y, j = blockIdx.x;
+  const int cnt = counts[h * k + j];
+  const size_t base = ((size_t)h * k + j) * D;
+  for (int e = threadIdx.x; e < D; e += blockDim.x) {
+    if (cnt > 0) cent[base + e] = sums[base + e] / (double)cnt;
+    sums[base + e] = 0.0;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    sizes[h * k + j] = cnt;
+    counts[h * k + j] = 0;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Stable counting sort of tokens by cluster.  One work-group per head,
+// 1024 threads = 16 waves.  Tokens are taken in rounds of 1024 in index
+// order.  Inside a wave, equal cluster ids are found with 8 ballots (one per
+// id bit).  A token's rank among equal ids in earlier lanes is a popcount.
+// Waves are ordered through per-wave, per-cluster counts in LDS.
+
+constexpr int kSortThreads = 1024;
+constexpr int kSortWaves = kSortThreads / 64;
+
+__global__ __launch_bounds__(kSortThreads)
+void cluster_sort(const int32_t *__restrict__ assign, int N, int k, int32_t *__restrict__ perm,
+                  int32_t *__restrict__ offs) {
+  __shared__ int32_t hist[256];
+  __shared__ int32_t start[256];     // offs[c] + tokens of cluster c placed in earlier rounds
+  __shared__ int32_t wcnt[kSortWaves][256];
+  const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int32_t *a = assign + (size_t)h * N;
+  int32_t *p = perm + (size_t)h * N;
+  for (int c = tid; c < 256; c += kSortThreads) hist[c] = 0;
+  __syncthreads();
+  for (int n = tid; n < N; n += kSortThreads) atomicAdd(&hist[a[n]], 1);
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int c = 0; c < k; ++c) {
+      offs[(size_t)h * (k + 1) + c] = run;
+      start[c] = run;
+      run += hist[c];
+    }
+    offs[(size_t)h * (k + 1) + k] = run;
+  }
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int base = 0; base < N; base += kSortThreads) {
+    for (int e = tid; e < kSortWaves * 256; e += kSortThreads) (&wcnt[0][0])[e] = 0;
+    __syncthreads();
+    const int n = base + tid;
+    const bool valid = n < N;
+    const int c = valid ? a[n] : 0;
+    uint64_t same = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const uint64_t bal = __ballot(valid && ((c >> b) & 1));
+      same &= ((c >> b) & 1) ? bal : ~bal;
+    }
+    const int rank = __popcll(same & below);
+    if (valid && rank == 0) wcnt[wave][c] = __popcll(same);
+    __syncthreads();
+    for (int cc = tid; cc < k; cc += kSortThreads) {  // exclusive prefix over waves
+      int run = 0;
+      for (int w = 0; w < kSortWaves; ++w) {
+        const int t = wcnt[w][cc];
+        wcnt[w][cc] = run;
+        run += t;
+      }
+      hist[cc] = run;  // this round's count of cluster cc
+    }
+    __syncthreads();
+    if (valid) p[start[c] + wcnt[wave][c] + rank] = n;
+    __syncthreads();
+    for (int cc = tid; cc < k; cc += kSortThreads) start[cc] += hist[cc];
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Top-p pair selection, in fp64.  Kernel 1: one work-group per (head, query
+// cluster), one thread per key cluster.  It writes the row's count to
+// pair_ptr[h][i+1] and its ascending list to the row's full-width slot
+// pair_idx[h][i*kk ...].  Kernel 2: one work-group per head.  It scans the
+// counts and moves each row left to its final offset (row by row: a row's
+// target never overlaps a later row's slot).
+
+__global__ __launch_bounds__(256)
+void select_rows(const double *__restrict__ cq, const double *__restrict__ ck, const int32_t *__restrict__ size_k,
+                 int kq, int kk, int D, double top_p, double scale, int32_t *__restrict__ pair_ptr,
+                 int32_t *__restrict__ pair_idx) {
+  __shared__ double prob[256];
+  __shared__ double red[256];
+  __shared__ int32_t order[256];
+  __shared__ int32_t keep[256];
+  __shared__ int32_t nsel;
+  const int h = blockIdx.y, i = blockIdx.x, j = threadIdx.x;
+  const bool live = j < kk && size_k[h * kk + j] > 0;
+  double l = -INFINITY;
+  if (live) {
+    const double *a = cq + ((size_t)h * kq + i) * D;
+    const double *b = ck + ((size_t)h * kk + j) * D;
+    double s = 0.0;
+    for (int e = 0; e < D; ++e) s = fma(a[e], b[e], s);
+    l = s * scale + log((double)size_k[h * kk + j]);
+  }
+  red[j] = l;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (j < off) red[j] = fmax(red[j], red[j + off]);
+    __syncthreads();
+  }
+  const double mx = red[0];
+  __syncthreads();
+  const double e = live ? exp(l - mx) : 0.0;
+  red[j] = e;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (j < off) red[j] += red[j + off];
+    __syncthreads();
+  }
+  const double pj = e / red[0];
+  prob[j] = live ? pj : -1.0;
+  keep[j] = 0;
+  __syncthreads();
+  if (live) {  // rank by (probability desc, index asc)
+    int rank = 0;
+    for (int t = 0; t < kk; ++t) {
+      const double pt = prob[t];
+      rank += (pt > pj) || (pt == pj && t < j);
+    }
+    order[rank] = j;
+  }
+  __syncthreads();
+  if (j == 0) {
+    int nlive = 0;
+    for (int t = 0; t < kk; ++t) nlive += prob[t] >= 0.0;
+    double run = 0.0;
+    int n = nlive;
+    for (int r = 0; r < nlive; ++r) {
+      run += prob[order[r]];
+      if (run >= top_p) {
+        n = r + 1;
+        break;
+      }
+    }
+    nsel = n;
+  }
+  __syncthreads();
+  if (j < nsel) keep[order[j]] = 1;
+  __syncthreads();
+  if (j == 0) {
+    int32_t *row = pair_idx + (size_t)h * kq * kk + (size_t)i * kk;
+    int m = 0;
+    for (int t = 0; t < kk; ++t)
+      if (keep[t]) row[m++] = t;
+    pair_ptr[(size_t)h * (kq + 1) + i + 1] = m;
+  }
+}
+
+__global__ __launch_bounds__(256)
+void select_compact(int kq, int kk, int32_t *__restrict__ pair_ptr, int32_t *__restrict__ pair_idx) {
+  const int h = blockIdx.x, tid = threadIdx.x;
+  int32_t *ptr = pair_ptr + (size_t)h * (kq + 1);
+  int32_t *idx = pair_idx + (size_t)h * kq * kk;
+  int run = 0;
+  for (int i = 0; i < kq; ++i) {
+    const int n = ptr[i + 1];
+    const int v = tid < n ? idx[(size_t)i * kk + tid] : 0;
+    __syncthreads();
+    if (tid < n) idx[run + tid] = v;
+    if (tid == 0) ptr[i] = run;
+    run += n;
+    __syncthreads();
+  }
+  if (tid == 0) ptr[kq] = run;
+}
+
+// ---------------------------------------------------------------------------
+// Variable-size block-sparse attention over cluster pairs.
+//
+// Work list: per head, each query cluster is cut into tiles of BQ rows.  A
+// work-group takes one tile and walks the concatenation of its cluster's
+// selected key ranges, in 64-key tiles.  Key j of that concatenation lives
+// at row k_offs[c] + (j - start of c's range) of Kp / Vp, for its cluster
+// c.  Only the last tile has keys past the end.
+
+struct QTile { int cluster, r0, r1, pad; };
+
+template <int BQ>
+__global__ __launch_bounds__(64)
+void varlen_tiles(const int32_t *__restrict__ q_offs, int kq, int max_tiles, QTile *__restrict__ tiles,
+                  int32_t *__restrict__ ntiles) {
+  const int h = blockIdx.x;
+  if (threadIdx.x != 0) return;
+  const int32_t *o = q_offs + (size_t)h * (kq + 1);
+  QTile *t = tiles + (size_t)h * max_tiles;
+  int n = 0;
+  for (int i = 0; i < kq; ++i)
+    for (int r = o[i]; r < o[i + 1]; r += BQ) t[n++] = QTile{i, r, min(o[i + 1], r + BQ), 0};
+  ntiles[h] = n;
+}
+
+constexpr int kMaxSel = 256;
+
+template <int D, int BQ>
+__global__ __launch_bounds__(BQ / 32 * 64, 2)
+void varlen_attn(const bf16_t *__restrict__ Qp, const bf16_t *__restrict__ Kp, const bf16_t *__restrict__ Vp,
+                 const int32_t *__restrict__ k_offs, int kq, int kk, const int32_t *__restrict__ pair_ptr,
+                 const int32_t *__restrict__ pair_idx, const int32_t *__restrict__ q_perm,
+                 const QTile *__restrict__ tiles, const int32_t *__restrict__ ntiles, int max_tiles, int N,
+                 float c, bf16_t *__restrict__ O) {
+  constexpr int NT = BQ / 32 * 64;
+  using C = core::Tile<D, NT>;
+  __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE];
+  __shared__ int32_t seg_v[kMaxSel + 1];   // start of each selected range in the concatenation
+  __shared__ int32_t seg_row[kMaxSel];     // its first row in Kp / Vp
+
+  const int h = blockIdx.y, t = blockIdx.x;
+  if (t >= ntiles[h]) return;
+  const QTile qt = tiles[(size_t)h * max_tiles + t];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const size_t hoff = (size_t)h * N * D;
+  const int32_t *ptr = pair_ptr + (size_t)h * (kq + 1);
+  const int32_t *sel = pair_idx + (size_t)h * kq * kk + ptr[qt.cluster];
+  const int nsel = ptr[qt.cluster + 1] - ptr[qt.cluster];
+  const int32_t *ko = k_offs + (size_t)h * (kk + 1);
+  if (tid == 0) {
+    int run = 0;
+    for (int m = 0; m < nsel; ++m) {
+      const int cl = sel[m];
+      seg_v[m] = run;
+      seg_row[m] = ko[cl];
+      run += ko[cl + 1] - ko[cl];
+    }
+    seg_v[nsel] = run;
+  }
+  __syncthreads();
+  const int nkeys = seg_v[nsel];
+
+  const int qrow = qt.r0 + wave * 32 + l32;
+  const bool qvalid = qrow < qt.r1;
+  bf16x8 qf[D / 16];
+  core::load_q<D>(Qp + hoff, qvalid ? qrow : -1, hi, qf);
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int ntile = (nkeys + core::BK - 1) / core::BK;
+  auto rows_of = [&](int tile) {
+    return [=](int j) {
+      const int v = tile * core::BK + j;
+      if (v >= nkeys) return -1;
+      int lo = 0, hi_ = nsel - 1;  // last segment with seg_v <= v
+      while (lo < hi_) {
+        const int mid = (lo + hi_ + 1) >> 1;
+        if (seg_v[mid] <= v) lo = mid; else hi_ = mid - 1;
+      }
+      return seg_row[lo] + (v - seg_v[lo]);
+    };
+  };
+  core::Regs<D, NT> R;
+  if (ntile > 0) {
+    core::load_tile<D, NT>(Kp + hoff, Vp + hoff, tid, rows_of(0), R);
+    core::store_tile<D, NT>(smem, tid, R);
+  }
+  __syncthreads();
+  for (int it = 0; it < ntile; ++it) {
+    const bool more = it + 1 < ntile;
+    if (more) core::load_tile<D, NT>(Kp + hoff, Vp + hoff, tid, rows_of(it + 1), R);
+    const char *Ks = smem + (it & 1) * C::STAGE;
+    const char *Vs = Ks + C::KBYTES;
+    f32x16 s0, s1;
+    core::qk_tile<D, NT>(Ks, qf, l32, hi, s0, s1);
+    if ((it + 1) * core::BK > nkeys) core::mask_tail(s0, s1, nkeys - it * core::BK, hi);
+    bf16x8 pb[4];
+    const float alpha = core::softmax_step(s0, s1, c, m_run, l_run, pb);
+    core::rescale<D>(o, alpha);
+    core::pv_tile<D, NT>(Vs, pb, l32, hi, o);
+    if (more) core::store_tile<D, NT>(smem + ((it + 1) & 1) * C::STAGE, tid, R);
+    __syncthreads();
+  }
+  bf16_t *orow = nullptr;
+  if (qvalid) {
+    const int dst = q_perm ? q_perm[(size_t)h * N + qrow] : qrow;
+    orow = O + hoff + (size_t)dst * D;
+  }
+  core::store_o<D>(orow, o, l_run, hi);
+}
+
+template <int D>
+constexpr int varlen_bq() { return D == 128 ? 128 : 64; }
+
+int varlen_max_tiles(const Dims &dm, int kq, int bq) { return (dm.N + bq - 1) / bq + kq; }
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+}  // namespace
+
+size_t kmeans_ws_bytes(const Dims &dm, int k) {
+  return align256((size_t)dm.H * k * dm.d * sizeof(double)) + align256((size_t)dm.H * k * sizeof(int32_t));
+}
+
+hipError_t launch_kmeans(const Dims &dm, bool bf16, const void *X, int k, int iters, const int32_t *init_idx,
+                         int32_t *assign, double *centroids, int32_t *sizes, void *ws, hipStream_t st) {
+  double *sums = (double *)ws;
+  int32_t *counts = (int32_t *)((char *)ws + align256((size_t)dm.H * k * dm.d * sizeof(double)));
+  const size_t nsum = (size_t)dm.H * k * dm.d, ncnt = (size_t)dm.H * k;
+  hipLaunchKernelGGL(km_zero, dim3((unsigned)((nsum + 255) / 256)), dim3(256), 0, st, sums, counts, nsum, ncnt);
+  if (bf16)
+    hipLaunchKernelGGL(km_init<bf16_t>, dim3(k, dm.H), dim3(128), 0, st, (const bf16_t *)X, init_idx, dm.N, dm.d, k,
+                       centroids);
+  else
+    hipLaunchKernelGGL(km_init<float>, dim3(k, dm.H), dim3(128), 0, st, (const float *)X, init_idx, dm.N, dm.d, k,
+                       centroids);
+  const size_t lds = (size_t)k * dm.d * sizeof(float);
+  const dim3 grid((dm.N + 255) / 256, dm.H);
+  if (lds > 65536) {  // centroid table above 64 KiB: raise the dynamic LDS limit
+    const void *fn = bf16 ? (dm.d == 64 ? (const void *)km_assign<bf16_t, 64> : (const void *)km_assign<bf16_t, 128>)
+                          : (dm.d == 64 ? (const void *)km_assign<float, 64> : (const void *)km_assign<float, 128>);
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  for (int it = 0; it < iters; ++it) {
+    if (bf16 && dm.d == 64)
+      hipLaunchKernelGGL((km_assign<bf16_t, 64>), grid, dim3(256), lds, st, (const bf16_t *)X, centroids, dm.N, k,
+                         assign, sums, counts);
+    else if (bf16)
+      hipLaunchKernelGGL((km_assign<bf16_t, 128>), grid, dim3(256), lds, st, (const bf16_t *)X, centroids, dm.N, k,
+                         assign, sums, counts);
+    else if (dm.d == 64)
+      hipLaunchKernelGGL((km_assign<float, 64>), grid, dim3(256), lds, st, (const float *)X, centroids, dm.N, k,
+                         assign, sums, counts);
+    else
+      hipLaunchKernelGGL((km_assign<float, 128>), grid, dim3(256), lds, st, (const float *)X, centroids, dm.N, k,
+                         assign, sums, counts);
+    hipLaunchKernelGGL(km_finalize, dim3(k, dm.H), dim3(128), 0, st, centroids, sums, counts, sizes, k, dm.d);
+  }
+  return hipGetLastError();
+}
+
+size_t cluster_permute_ws_bytes(const Dims &, int) { return 0; }
+
+hipError_t launch_cluster_permute(const Dims &dm, const int32_t *assign, int k, int32_t *perm, int32_t *offs,
+                                  void *, hipStream_t st) {
+  hipLaunchKernelGGL(cluster_sort, dim3(dm.H), dim3(kSortThreads), 0, st, assign, dm.N, k, perm, offs);
+  return hipGetLastError();
+}
+
+hipError_t launch_select_pairs(const Dims &dm, const double *cq, const double *ck, const int32_t *size_k, int kq,
+                               int kk, double top_p, double scale, int32_t *pair_ptr, int32_t *pair_idx,
+                               hipStream_t st) {
+  hipLaunchKernelGGL(select_rows, dim3(kq, dm.H), dim3(256), 0, st, cq, ck, size_k, kq, kk, dm.d, top_p, scale,
+                     pair_ptr, pair_idx);
+  hipLaunchKernelGGL(select_compact, dim3(dm.H), dim3(256), 0, st, kq, kk, pair_ptr, pair_idx);
+  return hipGetLastError();
+}
+
+size_t varlen_ws_bytes(const Dims &dm, int kq, int) {
+  const int bq = dm.d == 128 ? 128 : 64;
+  return align256((size_t)dm.H * varlen_max_tiles(dm, kq, bq) * sizeof(QTile)) + align256((size_t)dm.H * 4);
+}
+
+hipError_t launch_varlen(const Dims &dm, bool bf16, const void *Qp, const void *Kp, const void *Vp,
+                         const int32_t *q_offs, const int32_t *k_offs, int kq, int kk, const int32_t *pair_ptr,
+                         const int32_t *pair_idx, const int32_t *q_perm, float scale, void *O, void *ws,
+                         hipStream_t st) {
+  if (!bf16) return hipErrorInvalidValue;
+  const float c = scale * kLog2e;
+  const int bq = dm.d == 128 ? 128 : 64;
+  const int mt = varlen_max_tiles(dm, kq, bq);
+  QTile *tiles = (QTile *)ws;
+  int32_t *ntiles = (int32_t *)((char *)ws + align256((size_t)dm.H * mt * sizeof(QTile)));
+  if (dm.d == 128) {
+    hipLaunchKernelGGL(varlen_tiles<128>, dim3(dm.H), dim3(64), 0, st, q_offs, kq, mt, tiles, ntiles);
+    hipLaunchKernelGGL((varlen_attn<128, 128>), dim3(mt, dm.H), dim3(256), 0, st, (const bf16_t *)Qp,
+                       (const bf16_t *)Kp, (const bf16_t *)Vp, k_offs, kq, kk, pair_ptr, pair_idx, q_perm, tiles,
+                       ntiles, mt, dm.N, c, (bf16_t *)O);
+  } else {
+    hipLaunchKernelGGL(varlen_tiles<64>, dim3(dm.H), dim3(64), 0, st, q_offs, kq, mt, tiles, ntiles);
+    hipLaunchKernelGGL((varlen_attn<64, 64>), dim3(mt, dm.H), dim3(128), 0, st, (const bf16_t *)Qp,
+                       (const bf16_t *)Kp, (const bf16_t *)Vp, k_offs, kq, kk, pair_ptr, pair_idx, q_perm, tiles,
+                       ntiles, mt, dm.N, c, (bf16_t *)O);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace svgk

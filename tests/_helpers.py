@@ -1,0 +1,51 @@
+"""Shared helpers for the GPU parity tests: upload seeded inputs, download
+outputs, and the tolerance checks."""
+
+import numpy as np
+import torch
+
+from oracle.numerics import as_f64
+
+DEV = "cuda:0"
+
+# bf16 attention outputs against the float64 oracle
+BF16_MAX_ABS, BF16_REL_L2 = 2e-2, 1e-2
+# fp32 attention outputs against the float64 oracle: one fp32 rounding per
+# accumulated term over <= a few thousand terms
+F32_MAX_ABS, F32_REL_L2 = 1e-4, 1e-5
+
+
+def to_dev(x: np.ndarray, dtype: str):
+    """Stored tensor (bf16 bits as uint16, or float32) -> device tensor."""
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(DEV)
+
+
+def to_host_bits(t):
+    """Device tensor -> stored form (uint16 bits for bf16, float32 otherwise)."""
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def to_f64(t):
+    if t.dtype == torch.bfloat16:
+        return as_f64(to_host_bits(t), "bf16")
+    return t.double().cpu().numpy()
+
+
+def ints(x):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).to(DEV)
+
+
+def check_close(got, ref, max_abs, rel_l2, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    err = np.abs(got - ref)
+    mx = float(err.max()) if err.size else 0.0
+    rl2 = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30))
+    assert mx <= max_abs and rl2 <= rel_l2, f"{what}: max-abs {mx:.3e} rel-L2 {rl2:.3e}"
+    return mx, rl2

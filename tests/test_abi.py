@@ -1,0 +1,97 @@
+"""The C ABI library loads, exports every function include/*.h declares, and
+rejects bad arguments on the host with the documented status (CPU only: every
+call here returns from host validation before any HIP call)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+svg = pytest.importorskip("sparse_attention_video_online_amd.svg")
+
+
+def declared_functions():
+    names = []
+    for h in ("svg.h", "svg2.h"):
+        text = open(os.path.join(ROOT, "include", h)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(svg2?_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert "svg_block_sparse_attn" in names and "svg_varlen_attn" in names and len(names) >= 17
+    lib = ctypes.CDLL(svg.LIB_PATH)
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+    assert set(names) <= set(svg.SIGNATURES), set(names) - set(svg.SIGNATURES)
+
+
+def test_version_string():
+    assert b"gfx950" in svg.lib().svg_version()
+
+
+FAKE = ctypes.c_void_p(0x10000)      # never dereferenced: validation fails first
+FAKE2 = ctypes.c_void_p(0x20000000)
+
+
+def dims(F=4, S=64, T=16, H=2, d=64):
+    return ctypes.byref(svg.svg_dims(F, S, T, H, d))
+
+
+def status(name, *args):
+    return getattr(svg.lib(), name)(*args)
+
+
+def test_null_and_shape_errors():
+    L = svg.lib()
+    assert L.svg_dense_attn(None, 0, FAKE, FAKE, FAKE, 16, 16, -1.0, FAKE2, None) == svg.SVG_ERR_NULL
+    assert "dims" in svg.last_error()
+    assert L.svg_dense_attn(dims(), 0, None, FAKE, FAKE, 16, 16, -1.0, FAKE2, None) == svg.SVG_ERR_NULL
+    assert L.svg_dense_attn(dims(d=96), 0, FAKE, FAKE, FAKE, 16, 16, -1.0, FAKE2, None) == svg.SVG_ERR_UNSUPPORTED
+    assert L.svg_dense_attn(dims(H=0), 0, FAKE, FAKE, FAKE, 16, 16, -1.0, FAKE2, None) == svg.SVG_ERR_SHAPE
+    assert L.svg_dense_attn(dims(), 7, FAKE, FAKE, FAKE, 16, 16, -1.0, FAKE2, None) == svg.SVG_ERR_DTYPE
+    assert L.svg_dense_attn(dims(), 0, FAKE, FAKE, FAKE, 32, 32, -1.0, FAKE2, None) == svg.SVG_ERR_UNSUPPORTED
+    assert "block shape" in svg.last_error()
+
+
+def test_aliasing_and_workspace_errors():
+    L = svg.lib()
+    assert L.svg_dense_attn(dims(), 0, FAKE, FAKE2, FAKE2, 16, 16, -1.0, FAKE, None) == svg.SVG_ERR_RANGE
+    assert L.svg_layout_permute(dims(), 1, FAKE, FAKE, None, None) == svg.SVG_ERR_RANGE
+    mp = svg.svg_mask_params(0, 32)
+    assert L.svg_profile_heads(dims(), 0, FAKE, FAKE, FAKE, FAKE, 8, ctypes.byref(mp), -1.0, FAKE2, None,
+                               FAKE2, 16, None) == svg.SVG_ERR_WORKSPACE
+    assert L.svg_profile_heads(dims(), 0, FAKE, FAKE, FAKE, FAKE, 0, ctypes.byref(mp), -1.0, FAKE2, None,
+                               FAKE2, 1 << 30, None) == svg.SVG_ERR_RANGE
+    bad = svg.svg_mask_params(-1, 0)
+    assert L.svg_build_block_mask(dims(), ctypes.byref(bad), FAKE, 16, 16, FAKE2, None) == svg.SVG_ERR_RANGE
+    assert L.svg_block_sparse_attn(dims(), 0, FAKE, FAKE, FAKE, FAKE, 16, 16, -1.0, FAKE2, FAKE2, 8, None) \
+        == svg.SVG_ERR_WORKSPACE
+    assert L.svg_compact_block_mask(10, 0, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == svg.SVG_ERR_SHAPE
+
+
+def test_workspace_sizes():
+    L = svg.lib()
+    d = dims(F=13, S=1350, T=224, H=8, d=64)
+    ws = L.svg_workspace_bytes(svg.SVG_OP_BLOCK_SPARSE, d, 64, 64)
+    rows, nkb = 8 * 278, 278
+    assert ws >= rows * 4 + (rows + 1) * 4 + rows * nkb * 4
+    assert L.svg_workspace_bytes(svg.SVG_OP_BLOCK_SPARSE, d, 32, 32) == 0
+    assert L.svg_workspace_bytes(svg.SVG_OP_PROFILE, d, 178, 0) >= 3 * 8 * 178 * 64 * 4
+
+
+def test_svg2_validation():
+    L = svg.lib()
+    flat = dims(F=1, S=1000, T=0, H=2, d=64)
+    assert L.svg_kmeans(flat, 1, FAKE, 300, 10, FAKE, FAKE, FAKE, FAKE, FAKE2, 1 << 30, None) == svg.SVG_ERR_RANGE
+    assert L.svg_kmeans(flat, 1, FAKE, 64, 0, FAKE, FAKE, FAKE, FAKE, FAKE2, 1 << 30, None) == svg.SVG_ERR_RANGE
+    assert L.svg_select_pairs(flat, FAKE, FAKE, FAKE, 64, 256, 1.5, -1.0, FAKE, FAKE, None) == svg.SVG_ERR_RANGE
+    assert L.svg_select_pairs(flat, FAKE, FAKE, FAKE, 64, 512, 0.9, -1.0, FAKE, FAKE, None) == svg.SVG_ERR_RANGE
+    assert L.svg_permute_rows(flat, 1, FAKE, FAKE2, FAKE, 0, None) == svg.SVG_ERR_RANGE
+    assert L.svg_varlen_attn(flat, 1, FAKE, FAKE, FAKE, None, FAKE, 64, 256, FAKE, FAKE, None, -1.0, FAKE2,
+                             FAKE2, 1 << 30, None) == svg.SVG_ERR_NULL
