@@ -1,4 +1,5 @@
-// Online head profiling on sampled query rows.
+// Online head profiling on sampled query rows (vector-ALU version, used for
+// fp32 inputs; bf16 inputs go to the MFMA profiler in profile_mfma.hip).
 //
 // The SVG1 abstract: an online profiling strategy predicts whether each head
 // is spatial or temporal.  The project write-up ("Three generations"):
@@ -124,8 +125,15 @@ hipError_t launch_t(const Dims &dm, const void *Q, const void *K, const void *V,
 
 }  // namespace
 
+size_t profile_mfma_ws_bytes(const Dims &dm, int n_samples);
+hipError_t launch_profile_mfma(const Dims &dm, const void *Q, const void *K, const void *V,
+                               const int32_t *sample_idx, int n_s, int ks, int wt, float scale, int32_t *labels,
+                               float *mse, void *ws, hipStream_t st);
+
 size_t profile_ws_bytes(const Dims &dm, int n_samples) {
-  return ((size_t)3 * dm.H * n_samples * dm.d * sizeof(float) + 255) / 256 * 256;
+  const size_t simt = ((size_t)3 * dm.H * n_samples * dm.d * sizeof(float) + 255) / 256 * 256;
+  const size_t mfma = profile_mfma_ws_bytes(dm, n_samples);
+  return simt > mfma ? simt : mfma;
 }
 
 hipError_t launch_profile(const Dims &dm, bool bf16, const void *Q, const void *K, const void *V,
@@ -133,11 +141,8 @@ hipError_t launch_profile(const Dims &dm, bool bf16, const void *Q, const void *
                           int32_t *labels, float *mse, void *ws, hipStream_t st) {
   const float c = scale * kLog2e;
   if (dm.H == 0) return hipSuccess;
-  if (bf16) {
-    if (dm.d == 64)
-      return launch_t<bf16_t, 64>(dm, Q, K, V, sample_idx, n_samples, ks, wt, c, labels, mse, ws, st);
-    if (dm.d == 128)
-      return launch_t<bf16_t, 128>(dm, Q, K, V, sample_idx, n_samples, ks, wt, c, labels, mse, ws, st);
+  if (bf16) {  // bf16 runs on the MFMA profiler
+    return launch_profile_mfma(dm, Q, K, V, sample_idx, n_samples, ks, wt, scale, labels, mse, ws, st);
   } else {
     if (dm.d == 64)
       return launch_t<float, 64>(dm, Q, K, V, sample_idx, n_samples, ks, wt, c, labels, mse, ws, st);

@@ -1,0 +1,258 @@
+"""GPU parity of the SVG2 semantic path against the float64 oracle.
+
+Bit-exact: k-means assignments and sizes, centroids (member sums of bf16
+values are exact in float64 on both sides), cluster permutations and offsets,
+top-p pair lists.  Toleranced: varlen attention outputs (bf16: max-abs 2e-2,
+rel-L2 1e-2).  Inputs: the seeded Gaussian-mixture workload (synth/).
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from conftest import GOLDEN
+from _helpers import to_dev, to_f64, ints, check_close, BF16_MAX_ABS, BF16_REL_L2
+from oracle import svg2 as osvg2
+from oracle.attention import dense_attention
+from oracle.numerics import as_f64
+from synth import SVG2_COG
+from synth.generators import mixture_qkv, random_qkv
+
+pytestmark = pytest.mark.gpu
+
+svg = pytest.importorskip("sparse_attention_video_online_amd.svg")
+
+W = SVG2_COG
+_cache = {}
+
+
+def sync():
+    torch.cuda.synchronize()
+
+
+def data():
+    if "g" not in _cache:
+        _cache["g"] = mixture_qkv(W)
+    return _cache["g"]
+
+
+def oracle_head(h):
+    """Oracle k-means (Q and K), sizes, pairs of head h (cached)."""
+    key = ("oracle", h)
+    if key not in _cache:
+        g = data()
+        q, k = as_f64(g["q"][h], "bf16"), as_f64(g["k"][h], "bf16")
+        aq, cq, sq, _ = osvg2.kmeans(q, g["init_q"][h], W.iters)
+        ak, ck, sk, _ = osvg2.kmeans(k, g["init_k"][h], W.iters)
+        ptr, idx, _ = osvg2.select_pairs(cq, ck, sk, W.top_p)
+        _cache[key] = dict(aq=aq, cq=cq, sq=sq, ak=ak, ck=ck, sk=sk, ptr=ptr, idx=idx)
+    return _cache[key]
+
+
+def gpu_pipeline():
+    if "gpu" not in _cache:
+        g = data()
+        q, k, v = (to_dev(g[x], "bf16") for x in "qkv")
+        aq, cq, sq = svg.svg_kmeans(q, W.kq, W.iters, ints(g["init_q"]))
+        ak, ck, sk = svg.svg_kmeans(k, W.kk, W.iters, ints(g["init_k"]))
+        pq, oq = svg.svg_cluster_permute(aq, W.kq, W.d)
+        pk, ok = svg.svg_cluster_permute(ak, W.kk, W.d)
+        qp = svg.svg_permute_rows(q, pq)
+        kp = svg.svg_permute_rows(k, pk)
+        vp = svg.svg_permute_rows(v, pk)
+        ptr, idx = svg.svg_select_pairs(cq, ck, sk, W.top_p)
+        o = svg.svg_varlen_attn(qp, kp, vp, oq, ok, ptr, idx, q_perm=pq)
+        sync()
+        _cache["gpu"] = dict(aq=aq, cq=cq, sq=sq, ak=ak, ck=ck, sk=sk, pq=pq, oq=oq, pk=pk, ok=ok,
+                             ptr=ptr, idx=idx, o=o)
+    return _cache["gpu"]
+
+
+def test_kmeans_bit_exact_all_heads():
+    r = gpu_pipeline()
+    for h in range(W.H):
+        o = oracle_head(h)
+        np.testing.assert_array_equal(r["aq"][h].cpu().numpy(), o["aq"])
+        np.testing.assert_array_equal(r["ak"][h].cpu().numpy(), o["ak"])
+        np.testing.assert_array_equal(r["sq"][h].cpu().numpy(), o["sq"])
+        np.testing.assert_array_equal(r["sk"][h].cpu().numpy(), o["sk"])
+        np.testing.assert_array_equal(r["cq"][h].cpu().numpy(), o["cq"])
+        np.testing.assert_array_equal(r["ck"][h].cpu().numpy(), o["ck"])
+
+
+def test_kmeans_recovers_components():
+    r = gpu_pipeline()
+    g = data()
+    np.testing.assert_array_equal(r["aq"].cpu().numpy(), g["comp_q"])
+    np.testing.assert_array_equal(r["ak"].cpu().numpy(), g["comp_k"])
+
+
+@pytest.mark.parametrize("N,d,k,iters,dtype", [(1000, 64, 7, 3, "bf16"), (333, 128, 256, 2, "bf16"),
+                                               (517, 64, 1, 1, "f32"), (300, 128, 16, 4, "f32")])
+def test_kmeans_small_shapes(N, d, k, iters, dtype):
+    H = 2
+    x, _, _ = random_qkv(H, N, d, seed=N + k, dtype=dtype)
+    rng = np.random.default_rng(k)
+    init = np.stack([rng.choice(N, size=k, replace=False) for _ in range(H)]).astype(np.int32)
+    a, c, s = svg.svg_kmeans(to_dev(x, dtype), k, iters, ints(init))
+    sync()
+    for h in range(H):
+        oa, oc, os_, margin = osvg2.kmeans(as_f64(x[h], dtype), init[h], iters)
+        if margin < 1e-4:
+            pytest.skip(f"random input has a near-tie (margin {margin:.1e})")
+        np.testing.assert_array_equal(a[h].cpu().numpy(), oa)
+        np.testing.assert_array_equal(s[h].cpu().numpy(), os_)
+        np.testing.assert_allclose(c[h].cpu().numpy(), oc, rtol=1e-12, atol=1e-12)
+
+
+def test_kmeans_duplicate_init_tie_goes_to_lower_index():
+    H, N, d = 1, 64, 64
+    x, _, _ = random_qkv(H, N, d, seed=5, dtype="f32")
+    init = np.array([[3, 3, 10]], dtype=np.int32)    # clusters 0 and 1 start equal
+    a, c, s = svg.svg_kmeans(to_dev(x, "f32"), 3, 1, ints(init))
+    sync()
+    oa, oc, os_, _ = osvg2.kmeans(as_f64(x[0], "f32"), init[0], 1)
+    np.testing.assert_array_equal(a[0].cpu().numpy(), oa)
+    assert s[0, 1].item() == 0                       # the tie never picks cluster 1
+    np.testing.assert_array_equal(c[0, 1].cpu().numpy(), x[0, 3].astype(np.float64))
+
+
+def test_cluster_permute_bit_exact():
+    r = gpu_pipeline()
+    for h in range(W.H):
+        for side, kk in (("q", W.kq), ("k", W.kk)):
+            perm, offs = osvg2.cluster_permute(r["a" + side][h].cpu().numpy(), kk)
+            np.testing.assert_array_equal(r["p" + side][h].cpu().numpy(), perm)
+            np.testing.assert_array_equal(r["o" + side][h].cpu().numpy(), offs)
+
+
+@pytest.mark.parametrize("N,k", [(1, 1), (1023, 5), (1025, 256), (4000, 37)])
+def test_cluster_permute_random_with_empty_clusters(N, k):
+    rng = np.random.default_rng(N + k)
+    H = 3
+    a = rng.integers(0, k, size=(H, N)).astype(np.int32)
+    if k > 2:
+        a[a == 1] = 0                                 # cluster 1 empty
+    perm, offs = svg.svg_cluster_permute(ints(a), k)
+    sync()
+    for h in range(H):
+        p, o = osvg2.cluster_permute(a[h], k)
+        np.testing.assert_array_equal(perm[h].cpu().numpy(), p)
+        np.testing.assert_array_equal(offs[h].cpu().numpy(), o)
+
+
+def test_permute_rows_gather_and_scatter():
+    H, N, d = 2, 777, 64
+    x, _, _ = random_qkv(H, N, d, seed=77, dtype="bf16")
+    rng = np.random.default_rng(1)
+    perm = np.stack([rng.permutation(N) for _ in range(H)]).astype(np.int32)
+    xd = to_dev(x, "bf16")
+    y = svg.svg_permute_rows(xd, ints(perm))
+    z = svg.svg_permute_rows(y, ints(perm), inverse=True)
+    sync()
+    yh = y.view(torch.int16).cpu().numpy().view(np.uint16)
+    for h in range(H):
+        np.testing.assert_array_equal(yh[h], x[h][perm[h]])
+    np.testing.assert_array_equal(z.view(torch.int16).cpu().numpy().view(np.uint16), x)
+
+
+def test_select_pairs_bit_exact_from_oracle_centroids():
+    cq = np.stack([oracle_head(h)["cq"] for h in range(W.H)])
+    ck = np.stack([oracle_head(h)["ck"] for h in range(W.H)])
+    sk = np.stack([oracle_head(h)["sk"] for h in range(W.H)]).astype(np.int32)
+    ptr, idx = svg.svg_select_pairs(torch.from_numpy(cq).cuda(), torch.from_numpy(ck).cuda(),
+                                    ints(sk), W.top_p)
+    sync()
+    for h in range(W.H):
+        o = oracle_head(h)
+        np.testing.assert_array_equal(ptr[h].cpu().numpy(), o["ptr"])
+        np.testing.assert_array_equal(idx[h].cpu().numpy()[:o["ptr"][-1]], o["idx"])
+
+
+def test_select_pairs_hand_cases_and_extremes():
+    with open(os.path.join(GOLDEN, "topp_small.json")) as f:
+        g = json.load(f)
+    for case in g["cases"]:
+        sizes = np.array([case["sizes"]], dtype=np.int32)
+        kk = sizes.shape[1]
+        ck = np.random.default_rng(kk).standard_normal((1, kk, 64))
+        ptr, idx = svg.svg_select_pairs(torch.zeros(1, 1, 64, dtype=torch.float64, device="cuda:0"),
+                                        torch.from_numpy(ck).cuda(), ints(sizes), case["p"])
+        sync()
+        got = idx[0].cpu().numpy()[:ptr[0, 1].item()]
+        np.testing.assert_array_equal(got, case["expect"])
+    rng = np.random.default_rng(3)
+    cq, ck = rng.standard_normal((2, 5, 64)), rng.standard_normal((2, 40, 64))
+    sizes = rng.integers(1, 30, size=(2, 40)).astype(np.int32)
+    sizes[:, 7] = 0
+    for p in (1.0, 1e-9, 0.5):
+        ptr, idx = svg.svg_select_pairs(torch.from_numpy(cq).cuda(), torch.from_numpy(ck).cuda(), ints(sizes), p)
+        sync()
+        for h in range(2):
+            optr, oidx, _ = osvg2.select_pairs(cq[h], ck[h], sizes[h], p)
+            np.testing.assert_array_equal(ptr[h].cpu().numpy(), optr)
+            np.testing.assert_array_equal(idx[h].cpu().numpy()[:optr[-1]], oidx)
+
+
+def test_varlen_attention_pipeline_end_to_end():
+    """GPU pipeline (k-means, permutes, pairs, varlen attention, un-permute)
+    against the oracle's varlen attention with the oracle's own clusters and
+    pairs, in original token order, all heads."""
+    r = gpu_pipeline()
+    g = data()
+    got = to_f64(r["o"])
+    for h in range(W.H):
+        o = oracle_head(h)
+        q, k, v = (as_f64(g[x][h], "bf16") for x in "qkv")
+        ref = osvg2.varlen_attention(q, k, v, o["aq"], o["ak"], o["ptr"], o["idx"])
+        check_close(got[h], ref, BF16_MAX_ABS, BF16_REL_L2, f"svg2 head {h}")
+
+
+def test_varlen_all_pairs_equals_dense():
+    """Every pair selected: varlen attention is dense attention (sampled rows)."""
+    H, N, d, kq, kk = 2, 1500, 128, 5, 9
+    q, k, v = random_qkv(H, N, d, seed=11, dtype="bf16")
+    rng = np.random.default_rng(2)
+    aq = rng.integers(0, kq, size=(H, N)).astype(np.int32)
+    ak = rng.integers(0, kk, size=(H, N)).astype(np.int32)
+    pq, oq = svg.svg_cluster_permute(ints(aq), kq, d)
+    pk, ok = svg.svg_cluster_permute(ints(ak), kk, d)
+    qd, kd, vd = (to_dev(t, "bf16") for t in (q, k, v))
+    qp, kp, vp = svg.svg_permute_rows(qd, pq), svg.svg_permute_rows(kd, pk), svg.svg_permute_rows(vd, pk)
+    ptr = torch.from_numpy(np.tile(np.arange(0, kq * kk + 1, kk, dtype=np.int32), (H, 1))).cuda()
+    idx = torch.from_numpy(np.tile(np.tile(np.arange(kk, dtype=np.int32), kq), (H, 1))).cuda()
+    o = svg.svg_varlen_attn(qp, kp, vp, oq, ok, ptr, idx, q_perm=pq)
+    sync()
+    got = to_f64(o)
+    rows = np.r_[0:100, 700:760, N - 50:N]
+    for h in range(H):
+        ref = dense_attention(as_f64(q[h], "bf16"), as_f64(k[h], "bf16"), as_f64(v[h], "bf16"), rows=rows)
+        check_close(got[h][rows], ref, BF16_MAX_ABS, BF16_REL_L2, f"all-pairs head {h}")
+
+
+def test_varlen_k_zero_mean_of_selected_clusters():
+    H, N, d, kq, kk = 1, 900, 64, 4, 6
+    q, v, _ = random_qkv(H, N, d, seed=12, dtype="bf16")
+    kz = np.zeros_like(q)
+    rng = np.random.default_rng(4)
+    aq = rng.integers(0, kq, size=(H, N)).astype(np.int32)
+    ak = rng.integers(0, kk, size=(H, N)).astype(np.int32)
+    ptr_np = np.array([[0, 2, 3, 5, 6]], dtype=np.int32)
+    idx_np = np.zeros((H, kq * kk), dtype=np.int32)
+    idx_np[0, :6] = [1, 4, 0, 2, 5, 3]
+    pq, oq = svg.svg_cluster_permute(ints(aq), kq, d)
+    pk, ok = svg.svg_cluster_permute(ints(ak), kk, d)
+    qp = svg.svg_permute_rows(to_dev(q, "bf16"), pq)
+    kp = svg.svg_permute_rows(to_dev(kz, "bf16"), pk)
+    vp = svg.svg_permute_rows(to_dev(v, "bf16"), pk)
+    o = svg.svg_varlen_attn(qp, kp, vp, oq, ok, ints(ptr_np), ints(idx_np), q_perm=pq)
+    sync()
+    got = to_f64(o)[0]
+    vv = as_f64(v[0], "bf16")
+    for i in range(N):
+        sel = idx_np[0, ptr_np[0, aq[0, i]]:ptr_np[0, aq[0, i] + 1]]
+        ref = vv[np.isin(ak[0], sel)].mean(axis=0)
+        check_close(got[i], ref, 1e-2, 1e-2, f"kzero row {i}")
