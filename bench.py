@@ -38,7 +38,32 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--density", default="k5", help="mask widths: k5 (31%%), k4 (26%%), cog_rule (~2%%)")
+    ap.add_argument("--workload", default="hunyuan_layer", choices=["hunyuan_layer", "svg2"],
+                    help="hunyuan_layer: the SVG1 layer step (default, the headline line); "
+                         "svg2: the SVG2 semantic path on the CogVideoX-shaped mixture workload")
+    ap.add_argument("--pmc-target", action="store_true",
+                    help="launch the block-sparse attention kernel once and a plain 1.46 GB copy "
+                         "(layout kernel with every head spatial) once, for hardware-counter runs")
     return ap.parse_args()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the block-sparse kernel, from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE record, scaled by the same counters on a
+    copy of known size.  None if that record is missing or was taken on
+    different kernel sources than the ones built here."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "attn_fwd_mfma_hunyuan_layer_traffic.json")
+    try:
+        rec = json.load(open(path))
+        h = hashlib.sha256()
+        for src in rec["sources"]:
+            h.update(open(os.path.join(ROOT, src), "rb").read())
+        if h.hexdigest() != rec["source_sha256"]:
+            return None
+        return int(rec["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def gen_inputs(w):
@@ -100,12 +125,127 @@ def cpu_baseline(w, ks, wt, labels, seconds):
                       f"{heads} of this workload, {elapsed:.1f} s of attention time"}
 
 
+def bench_svg2(args):
+    """SVG2 path on the CogVideoX-shaped mixture workload (13 x 1350 + 224
+    tokens, 8 heads, d = 64, bf16; k_q = 64, k_k = 256, 10 Lloyd iterations,
+    top-p 0.9).  One step = k-means of Q and K, stable cluster sort of both,
+    row gathers of Q, K, V, top-p pair selection, varlen attention written
+    back in original order."""
+    import numpy as np
+    import torch
+    from sparse_attention_video_online_amd import svg
+    from synth import SVG2_COG as w
+    from synth.generators import mixture_qkv
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    g = mixture_qkv(w)
+    up = lambda x: torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+    q, k, v = up(g["q"]), up(g["k"]), up(g["v"])
+    iq = torch.from_numpy(g["init_q"]).to(dev)
+    ik = torch.from_numpy(g["init_k"]).to(dev)
+    H, N, d = w.H, w.N, w.d
+    i32 = lambda *shape: torch.empty(*shape, dtype=torch.int32, device=dev)
+    aq, ak = i32(H, N), i32(H, N)
+    cq = torch.empty(H, w.kq, d, dtype=torch.float64, device=dev)
+    ck = torch.empty(H, w.kk, d, dtype=torch.float64, device=dev)
+    sq, sk = i32(H, w.kq), i32(H, w.kk)
+    pq, pk, oq, ok = i32(H, N), i32(H, N), i32(H, w.kq + 1), i32(H, w.kk + 1)
+    ptr, idx = i32(H, w.kq + 1), i32(H, w.kq * w.kk)
+    qp, kp, vp, o = (torch.empty_like(q) for _ in range(4))
+    dm = svg.svg_dims(1, N, 0, H, d)
+    ws_kq = torch.empty(svg.workspace_bytes(svg.SVG2_OP_KMEANS, dm, w.kq, svg2=True), dtype=torch.uint8, device=dev)
+    ws_kk = torch.empty(svg.workspace_bytes(svg.SVG2_OP_KMEANS, dm, w.kk, svg2=True), dtype=torch.uint8, device=dev)
+    ws_cp = torch.empty(1, dtype=torch.uint8, device=dev)
+    ws_vl = torch.empty(svg.workspace_bytes(svg.SVG2_OP_VARLEN, dm, w.kq, w.kk, svg2=True), dtype=torch.uint8,
+                        device=dev)
+    stream = torch.cuda.current_stream()
+    names = ["kmeans_q", "kmeans_k", "cluster_sort_qk", "gather_qkv", "select_pairs", "varlen_attn"]
+
+    def step(ev=None):
+        def mark(j):
+            if ev is not None:
+                ev[j].record(stream)
+        mark(0)
+        svg.svg_kmeans(q, w.kq, w.iters, iq, assign=aq, centroids=cq, sizes=sq, ws=ws_kq)
+        mark(1)
+        svg.svg_kmeans(k, w.kk, w.iters, ik, assign=ak, centroids=ck, sizes=sk, ws=ws_kk)
+        mark(2)
+        svg.svg_cluster_permute(aq, w.kq, d, perm=pq, offs=oq, ws=ws_cp)
+        svg.svg_cluster_permute(ak, w.kk, d, perm=pk, offs=ok, ws=ws_cp)
+        mark(3)
+        svg.svg_permute_rows(q, pq, out=qp)
+        svg.svg_permute_rows(k, pk, out=kp)
+        svg.svg_permute_rows(v, pk, out=vp)
+        mark(4)
+        svg.svg_select_pairs(cq, ck, sk, w.top_p, pair_ptr=ptr, pair_idx=idx)
+        mark(5)
+        svg.svg_varlen_attn(qp, kp, vp, oq, ok, ptr, idx, q_perm=pq, out=o, ws=ws_vl)
+        mark(6)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(7)]
+    step(ev)
+    torch.cuda.synchronize()
+    stage_ms = {n: ev[j].elapsed_time(ev[j + 1]) for j, n in enumerate(names)}
+
+    # work: attention pairs from the selected clusters; bytes of the copies
+    optr, oidx = ptr.cpu().numpy(), idx.cpu().numpy()
+    qs, ks_ = np.diff(oq.cpu().numpy(), axis=1), np.diff(ok.cpu().numpy(), axis=1)
+    pairs = 0
+    for h in range(H):
+        for i in range(w.kq):
+            sel = oidx[h, optr[h, i]:optr[h, i + 1]]
+            pairs += int(qs[h, i]) * int(ks_[h, sel].sum())
+    attn_flops = 4.0 * d * pairs
+    gather_bytes = 3 * 2 * H * N * d * 2
+    km_flops = 3.0 * w.iters * H * N * d * (w.kq + w.kk)   # sub + fma per dim per centroid
+    result = {
+        "metric": "SVG2 semantic path ms per step (k-means, cluster sort, gathers, top-p, varlen attention)",
+        "value": round(ms_per_step, 4), "unit": "ms", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded Gaussian mixture)",
+        "config": {"workload": w.name, "N": N, "H": H, "d": d, "kq": w.kq, "kk": w.kk, "iters": w.iters,
+                   "top_p": w.top_p, "pair_density": round(pairs / (H * float(N) * N), 4)},
+        "stage_ms": {kk_: round(vv, 4) for kk_, vv in stage_ms.items()},
+        "varlen_tflops": round(attn_flops / (stage_ms["varlen_attn"] * 1e-3) / 1e12, 2),
+        "gather_gbs": round(gather_bytes / (stage_ms["gather_qkv"] * 1e-3) / 1e9, 1),
+        "kmeans_vector_tflops": round(km_flops / ((stage_ms["kmeans_q"] + stage_ms["kmeans_k"]) * 1e-3) / 1e12, 2),
+    }
+    if not args.no_cpu_baseline:
+        from oracle import svg2 as osvg2
+        from oracle.numerics import as_f64
+        t0 = time.perf_counter()
+        qd, kd, vd = (as_f64(g[x][0], "bf16") for x in "qkv")
+        oaq, ocq, osq, _ = osvg2.kmeans(qd, g["init_q"][0], w.iters)
+        oak, ock, osk, _ = osvg2.kmeans(kd, g["init_k"][0], w.iters)
+        optr0, oidx0, _ = osvg2.select_pairs(ocq, ock, osk, w.top_p)
+        osvg2.varlen_attention(qd, kd, vd, oaq, oak, optr0, oidx0)
+        t = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": round(t * H * 1e3, 1), "unit": "ms", "cores": len(os.sched_getaffinity(0)),
+                                  "kind": "oracle",
+                                  "sample": f"float64 oracle SVG2 pipeline on head 0 ({t:.1f} s), times {H} heads"}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path shards by head "
               f"with no exchange, see the design notes.", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload == "svg2":
+        return bench_svg2(args)
 
     import numpy as np
     import torch
@@ -162,6 +302,20 @@ def main():
         mark(4)
         svg.svg_layout_unpermute(op, F, S, T, labels, out=o)
         mark(5)
+
+    if args.pmc_target:
+        # the layer's inputs for the attention kernel, then one launch each of
+        # the attention kernel and a plain copy of known size (H*N*d*2 bytes
+        # read and written)
+        step()
+        torch.cuda.synchronize()
+        svg.svg_block_sparse_attn_csr(qp, kp, vp, row_ptr, kv_idx, F, S, T, bq, bk, out=op)
+        spatial = torch.zeros(H, dtype=torch.int32, device=dev)
+        svg.svg_layout_permute(q, F, S, T, spatial, out=o)
+        torch.cuda.synchronize()
+        print(json.dumps({"pmc_target": True, "copy_bytes_each_way": q.numel() * 2,
+                          "kept_tiles": int(bmask.sum())}), flush=True)
+        return
 
     for _ in range(args.warmup):
         step()
@@ -240,7 +394,8 @@ def main():
         "stage_ms": {kk: round(vv, 4) for kk, vv in stage_ms.items()},
         "roofline": {"bound": "mfma", "kernel": "attn_fwd_mfma<128,128> (block-sparse)",
                      "achieved": round(attn_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic() if args.density == "k5" else None,
                      "flop_per_launch": flops},
     }
     if not args.no_cpu_baseline:

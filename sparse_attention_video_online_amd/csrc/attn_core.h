@@ -149,21 +149,28 @@ __device__ __forceinline__ void mask_tail(f32x16 &s0, f32x16 &s1, int nvalid, in
   }
 }
 
-// One online-softmax step for the lane's query.  Updates m_run (raw-score
-// max) and l_run (this lane's partial sum).  Returns the rescale factor of
-// the accumulated output.  pb = the tile's probabilities as bf16 MFMA B
-// operands, one per 16-key chunk.  c = scale * log2(e).
+// One online-softmax step for the lane's query.  m_run is the reference
+// maximum the exponentials are taken against.  It moves only when the tile
+// raises the row maximum by more than 2^kLazyLog2 in exp2 units, so most
+// tiles need no rescale of O.  Probabilities then stay <= 2^kLazyLog2, and
+// l_run and O share the same reference, so O / l is unchanged.  l_run is
+// this lane's partial sum.  Returns the rescale factor of the accumulated
+// output.  pb = the tile's probabilities as bf16 MFMA B operands, one per
+// 16-key chunk.  c = scale * log2(e).
+constexpr float kLazyLog2 = 8.f;
+
 __device__ __forceinline__ float softmax_step(const f32x16 &s0, const f32x16 &s1, float c, float &m_run,
                                               float &l_run, bf16x8 (&pb)[4]) {
   float mx = -INFINITY;
 #pragma unroll
   for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
   mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float m_new = fmaxf(m_run, mx);
-  const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
-  const float alpha = fast_exp2((m_run - m_ref) * c);
-  m_run = m_new;
-  const float mc = m_ref * c;
+  float alpha = 1.f;
+  if (mx > m_run && (mx - m_run) * c > kLazyLog2) {  // m_run = -inf: always taken
+    alpha = fast_exp2((m_run - mx) * c);
+    m_run = mx;
+  }
+  const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
   float rs = 0.f;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -191,19 +198,22 @@ __device__ __forceinline__ void rescale(f32x16 (&o)[D / 32], float alpha) {
   }
 }
 
-// O^T += V^T P^T for the staged tile.
+// O^T += V^T P^T for the staged tile.  The four V^T operands of a 16-key
+// chunk are read before its MFMAs so the LDS latency overlaps the math.
 template <int D, int NT>
 __device__ __forceinline__ void pv_tile(const char *__restrict__ Vs, const bf16x8 (&pb)[4], int l32, int hi,
                                         f32x16 (&o)[D / 32]) {
   using C = Tile<D, NT>;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
+    bf16x8 a[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
       const int d = 32 * db + l32;
-      const bf16x8 a = *reinterpret_cast<const bf16x8 *>(Vs + d * C::VSTR + (((2 * j + hi) ^ vt_swz(d)) << 4));
-      o[db] = mfma32(a, pb[j], o[db]);
+      a[db] = *reinterpret_cast<const bf16x8 *>(Vs + d * C::VSTR + (((2 * j + hi) ^ vt_swz(d)) << 4));
     }
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) o[db] = mfma32(a[db], pb[j], o[db]);
   }
 }
 
