@@ -77,7 +77,8 @@ size_t block_sparse_ws(const Dims &dm, int bq, int bk) {
 hipError_t run_attention(const Dims &dm, svg_dtype dtype, const void *Q, const void *K,
                          const void *V, void *O, const int32_t *row_ptr, const int32_t *kv_idx,
                          int bq, int bk, float scale, hipStream_t st) {
-  if (dtype == SVG_BF16 && bk == 64)
+  // the MFMA kernel addresses a head with 32-bit byte offsets
+  if (dtype == SVG_BF16 && bk == 64 && (int64_t)dm.N * dm.d * 2 < ((int64_t)1 << 31))
     return svgk::launch_attn_mfma(dm, Q, K, V, O, row_ptr, kv_idx, bq, bk, scale, st);
   return svgk::launch_attn_simt(dm, dtype == SVG_BF16, Q, K, V, O, row_ptr, kv_idx, bq, bk, scale, st);
 }

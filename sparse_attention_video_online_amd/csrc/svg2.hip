@@ -16,9 +16,12 @@ namespace svgk {
 namespace {
 
 // ---------------------------------------------------------------------------
-// k-means (Lloyd).  Distances in fp32 from fp32 copies of the centroids.
-// Member sums in fp64: a sum of bf16 values is exact in fp64, so atomics in
-// any order give the same bits.
+// k-means (Lloyd).  Assign: distances in fp32 from fp32 copies of the
+// centroids, strict "<" so ties keep the lower index.  Update: the members of
+// each cluster are put in index order by the stable counting sort below.
+// Then one work-group per cluster sums them in fp64, dimension by dimension,
+// in that order (the oracle's order), and divides.  No atomics.  The sums are
+// deterministic, and exact for bf16 inputs.
 
 template <typename T>
 __global__ __launch_bounds__(128)
@@ -30,17 +33,10 @@ void km_init(const T *__restrict__ X, const int32_t *__restrict__ init_idx, int 
     cent[((size_t)h * k + j) * D + e] = (double)to_f32<T>(X[((size_t)h * N + src) * D + e]);
 }
 
-__global__ __launch_bounds__(256)
-void km_zero(double *__restrict__ sums, int32_t *__restrict__ counts, size_t nsum, size_t ncnt) {
-  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < nsum) sums[i] = 0.0;
-  if (i < ncnt) counts[i] = 0;
-}
-
 template <typename T, int D>
 __global__ __launch_bounds__(256)
 void km_assign(const T *__restrict__ X, const double *__restrict__ cent, int N, int k,
-               int32_t *__restrict__ assign, double *__restrict__ sums, int32_t *__restrict__ counts) {
+               int32_t *__restrict__ assign) {
   extern __shared__ float cs[];  // [k][D]
   const int h = blockIdx.y;
   const double *ch = cent + (size_t)h * k * D;
@@ -68,27 +64,24 @@ void km_assign(const T *__restrict__ X, const double *__restrict__ cent, int N, 
     }
   }
   assign[(size_t)h * N + n] = arg;
-  atomicAdd(&counts[h * k + arg], 1);
-  double *sr = sums + ((size_t)h * k + arg) * D;
-#pragma unroll
-  for (int e = 0; e < D; ++e) atomicAdd(&sr[e], (double)x[e]);
 }
 
+// Centroid of cluster j = mean of its members, taken in sorted (= index)
+// order.  An empty cluster keeps its centroid.
+template <typename T>
 __global__ __launch_bounds__(128)
-void km_finalize(double *__restrict__ cent, double *__restrict__ sums, int32_t *__restrict__ counts,
-                 int32_t *__restrict__ sizes, int k, int D) {
-  const int h = blockIdx.y, j = blockIdx.x;
-  const int cnt = counts[h * k + j];
-  const size_t base = ((size_t)h * k + j) * D;
-  for (int e = threadIdx.x; e < D; e += blockDim.x) {
-    if (cnt > 0) cent[base + e] = sums[base + e] / (double)cnt;
-    sums[base + e] = 0.0;
+void km_update(const T *__restrict__ X, const int32_t *__restrict__ perm, const int32_t *__restrict__ offs, int N,
+               int k, int D, double *__restrict__ cent, int32_t *__restrict__ sizes) {
+  const int h = blockIdx.y, j = blockIdx.x, e = threadIdx.x;
+  const int o0 = offs[(size_t)h * (k + 1) + j], o1 = offs[(size_t)h * (k + 1) + j + 1];
+  const int32_t *p = perm + (size_t)h * N;
+  const T *Xh = X + (size_t)h * N * D;
+  if (e < D && o1 > o0) {
+    double s = 0.0;
+    for (int n = o0; n < o1; ++n) s += (double)to_f32<T>(Xh[(size_t)p[n] * D + e]);
+    cent[((size_t)h * k + j) * D + e] = s / (double)(o1 - o0);
   }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    sizes[h * k + j] = cnt;
-    counts[h * k + j] = 0;
-  }
+  if (e == 0) sizes[h * k + j] = o1 - o0;
 }
 
 // ---------------------------------------------------------------------------
@@ -379,15 +372,13 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 }  // namespace
 
 size_t kmeans_ws_bytes(const Dims &dm, int k) {
-  return align256((size_t)dm.H * k * dm.d * sizeof(double)) + align256((size_t)dm.H * k * sizeof(int32_t));
+  return align256((size_t)dm.H * dm.N * sizeof(int32_t)) + align256((size_t)dm.H * (k + 1) * sizeof(int32_t));
 }
 
 hipError_t launch_kmeans(const Dims &dm, bool bf16, const void *X, int k, int iters, const int32_t *init_idx,
                          int32_t *assign, double *centroids, int32_t *sizes, void *ws, hipStream_t st) {
-  double *sums = (double *)ws;
-  int32_t *counts = (int32_t *)((char *)ws + align256((size_t)dm.H * k * dm.d * sizeof(double)));
-  const size_t nsum = (size_t)dm.H * k * dm.d, ncnt = (size_t)dm.H * k;
-  hipLaunchKernelGGL(km_zero, dim3((unsigned)((nsum + 255) / 256)), dim3(256), 0, st, sums, counts, nsum, ncnt);
+  int32_t *perm = (int32_t *)ws;
+  int32_t *offs = (int32_t *)((char *)ws + align256((size_t)dm.H * dm.N * sizeof(int32_t)));
   if (bf16)
     hipLaunchKernelGGL(km_init<bf16_t>, dim3(k, dm.H), dim3(128), 0, st, (const bf16_t *)X, init_idx, dm.N, dm.d, k,
                        centroids);
@@ -396,26 +387,32 @@ hipError_t launch_kmeans(const Dims &dm, bool bf16, const void *X, int k, int it
                        centroids);
   const size_t lds = (size_t)k * dm.d * sizeof(float);
   const dim3 grid((dm.N + 255) / 256, dm.H);
+  const void *fn = bf16 ? (dm.d == 64 ? (const void *)km_assign<bf16_t, 64> : (const void *)km_assign<bf16_t, 128>)
+                        : (dm.d == 64 ? (const void *)km_assign<float, 64> : (const void *)km_assign<float, 128>);
   if (lds > 65536) {  // centroid table above 64 KiB: raise the dynamic LDS limit
-    const void *fn = bf16 ? (dm.d == 64 ? (const void *)km_assign<bf16_t, 64> : (const void *)km_assign<bf16_t, 128>)
-                          : (dm.d == 64 ? (const void *)km_assign<float, 64> : (const void *)km_assign<float, 128>);
     const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
   for (int it = 0; it < iters; ++it) {
     if (bf16 && dm.d == 64)
       hipLaunchKernelGGL((km_assign<bf16_t, 64>), grid, dim3(256), lds, st, (const bf16_t *)X, centroids, dm.N, k,
-                         assign, sums, counts);
+                         assign);
     else if (bf16)
       hipLaunchKernelGGL((km_assign<bf16_t, 128>), grid, dim3(256), lds, st, (const bf16_t *)X, centroids, dm.N, k,
-                         assign, sums, counts);
+                         assign);
     else if (dm.d == 64)
       hipLaunchKernelGGL((km_assign<float, 64>), grid, dim3(256), lds, st, (const float *)X, centroids, dm.N, k,
-                         assign, sums, counts);
+                         assign);
     else
       hipLaunchKernelGGL((km_assign<float, 128>), grid, dim3(256), lds, st, (const float *)X, centroids, dm.N, k,
-                         assign, sums, counts);
-    hipLaunchKernelGGL(km_finalize, dim3(k, dm.H), dim3(128), 0, st, centroids, sums, counts, sizes, k, dm.d);
+                         assign);
+    hipLaunchKernelGGL(cluster_sort, dim3(dm.H), dim3(kSortThreads), 0, st, assign, dm.N, k, perm, offs);
+    if (bf16)
+      hipLaunchKernelGGL(km_update<bf16_t>, dim3(k, dm.H), dim3(128), 0, st, (const bf16_t *)X, perm, offs, dm.N, k,
+                         dm.d, centroids, sizes);
+    else
+      hipLaunchKernelGGL(km_update<float>, dim3(k, dm.H), dim3(128), 0, st, (const float *)X, perm, offs, dm.N, k,
+                         dm.d, centroids, sizes);
   }
   return hipGetLastError();
 }
