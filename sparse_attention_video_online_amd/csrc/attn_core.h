@@ -149,27 +149,32 @@ __device__ __forceinline__ void mask_tail(f32x16 &s0, f32x16 &s1, int nvalid, in
   }
 }
 
-// One online-softmax step for the lane's query.  m_run is the reference
-// maximum the exponentials are taken against.  It moves only when the tile
-// raises the row maximum by more than 2^kLazyLog2 in exp2 units, so most
-// tiles need no rescale of O.  Probabilities then stay <= 2^kLazyLog2, and
-// l_run and O share the same reference, so O / l is unchanged.  l_run is
-// this lane's partial sum.  Returns the rescale factor of the accumulated
-// output.  pb = the tile's probabilities as bf16 MFMA B operands, one per
-// 16-key chunk.  c = scale * log2(e).
 constexpr float kLazyLog2 = 8.f;
 
-__device__ __forceinline__ float softmax_step(const f32x16 &s0, const f32x16 &s1, float c, float &m_run,
-                                              float &l_run, bf16x8 (&pb)[4]) {
+// Row maximum of the lane's query over the tile (both lane halves).
+__device__ __forceinline__ float row_max(const f32x16 &s0, const f32x16 &s1) {
   float mx = -INFINITY;
 #pragma unroll
   for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  float alpha = 1.f;
-  if (mx > m_run && (mx - m_run) * c > kLazyLog2) {  // m_run = -inf: always taken
-    alpha = fast_exp2((m_run - mx) * c);
-    m_run = mx;
-  }
+  return fmaxf(mx, __shfl_xor(mx, 32));
+}
+
+// Moves the reference maximum if the tile raised the row maximum by more
+// than 2^kLazyLog2 (exp2 units), rescales l_run accordingly, and returns the
+// factor the accumulated output must be multiplied by.  Branch-free.
+__device__ __forceinline__ float update_ref(float mx, float c, float &m_run, float &l_run) {
+  const bool move = mx > m_run && (mx - m_run) * c > kLazyLog2;  // m_run = -inf: always moves
+  const float a_move = fast_exp2((m_run - mx) * c);
+  const float alpha = move ? a_move : 1.f;
+  m_run = move ? mx : m_run;
+  l_run *= alpha;
+  return alpha;
+}
+
+// Probabilities of the tile against the reference m_run, packed as bf16 MFMA
+// B operands (one per 16-key chunk); their sum is added to l_run.
+__device__ __forceinline__ void probs(const f32x16 &s0, const f32x16 &s1, float c, float m_run, float &l_run,
+                                      bf16x8 (&pb)[4]) {
   const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
   float rs = 0.f;
 #pragma unroll
@@ -186,7 +191,20 @@ __device__ __forceinline__ float softmax_step(const f32x16 &s0, const f32x16 &s1
     }
     pb[j] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
   }
-  l_run = l_run * alpha + rs;
+  l_run += rs;
+}
+
+// One online-softmax step for the lane's query: m_run is the reference
+// maximum the exponentials are taken against.  It moves only when the tile
+// raises the row maximum by more than 2^kLazyLog2 in exp2 units, so most
+// tiles need no rescale of O.  Probabilities then stay <= 2^kLazyLog2, and
+// l_run and O share the reference, so O / l is unchanged.  l_run is this
+// lane's partial sum.  Returns the rescale factor of the accumulated output.
+// c = scale * log2(e).
+__device__ __forceinline__ float softmax_step(const f32x16 &s0, const f32x16 &s1, float c, float &m_run,
+                                              float &l_run, bf16x8 (&pb)[4]) {
+  const float alpha = update_ref(row_max(s0, s1), c, m_run, l_run);
+  probs(s0, s1, c, m_run, l_run, pb);
   return alpha;
 }
 
@@ -234,6 +252,182 @@ __device__ __forceinline__ void store_o(bf16_t *__restrict__ orow, const f32x16 
       const uint32_t w1 = pack_bf16x2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
       *reinterpret_cast<u32x2 *>(orow + d0) = u32x2{w0, w1};
     }
+  }
+}
+
+
+// ===========================================================================
+// Direct-to-LDS pipeline (gfx950).
+//
+// K and V tiles are copied from global memory into LDS by the load unit
+// itself (global_load_lds_dwordx4: lane l's 16 bytes land at LDS
+// base + 16*l), so no registers stage them.  Both tiles are row-major, 64 rows
+// of D bf16, and each row's 16-byte chunks are XOR-swizzled:
+//   K: chunk ^ swz_k(key)   so the 16 lanes of one ds_read_b128 (16 keys, one
+//                           logical chunk) hit 16 different bank groups;
+//   V: chunk ^ swz_v(key)   so the ds_read_b64_tr_b16 transposed reads of the
+//                           V^T operand are conflict-free.
+// The V^T MFMA operand is read transposed from row-major V.  In each 16-lane
+// group, ds_read_b64_tr_b16 returns to lane i the i-th halfword of four
+// 8-byte rows.  Lane j of the group points at V[key_(j/4)][d0 + 4*(j%4)], so
+// lane i receives V[key_0..3][d0 + i]: four keys of its own d.  Two such
+// reads give the eight keys an operand lane needs.
+// ===========================================================================
+
+template <int D>
+struct DTile {
+  static constexpr int ROWB = D * 2;          // bytes per row
+  static constexpr int CPR = D / 8;           // 16-byte chunks per row
+  static constexpr int TBYTES = BK * ROWB;    // one K or V tile
+  static constexpr int UNITS = BK * CPR;      // 16-byte units per tile
+  static constexpr int BLOCKS = UNITS / 64;   // 1 KB DMA blocks per tile
+};
+
+template <int D>
+__device__ __forceinline__ int swz_k(int key) { return D == 128 ? (key & 15) : ((key >> 1) & 7); }
+template <int D>
+__device__ __forceinline__ int swz_v(int key) { return D == 128 ? 4 * (key & 3) : 2 * (key & 3); }
+
+typedef short v4s16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) v4s16 lds_v4s16_t;
+
+// Copy one tile (64 rows) of X into LDS at `tile`.  rowof(r) gives the global
+// row of tile row r and must return a readable row (callers clamp rows past
+// the end; their scores are masked).  Wave `wave` of NW issues its share of
+// the 1 KB blocks.
+template <int D, int NW, bool ISV, typename RowOf>
+__device__ __forceinline__ void dma_tile(const bf16_t *__restrict__ Xh, char *tile, int wave, int lane,
+                                         RowOf rowof) {
+  using T = DTile<D>;
+  constexpr int PER_WAVE = T::BLOCKS / NW;
+  static_assert(T::BLOCKS % NW == 0, "tile blocks must split evenly over the waves");
+#pragma unroll
+  for (int i = 0; i < PER_WAVE; ++i) {
+    const int blk = wave * PER_WAVE + i;
+    const int p = blk * 64 + lane;                 // 16-byte unit written by this lane
+    const int row = p / T::CPR, pc = p % T::CPR;
+    const int c = pc ^ (ISV ? swz_v<D>(row) : swz_k<D>(row));
+    const bf16_t *src = Xh + (size_t)rowof(row) * D + c * 8;
+    __builtin_amdgcn_global_load_lds((const void *)src, (lds_void_t *)(tile + blk * 1024), 16, 0, 0);
+  }
+}
+
+// Per-lane byte offsets (within a tile) of the 16-byte units this lane's
+// DMA instructions copy, for every row inside N.  The tile's global base is
+// uniform, so each DMA is "scalar base + vector offset" with no per-tile
+// address arithmetic.
+template <int D, int NW, bool ISV>
+__device__ __forceinline__ void dma_offsets(int wave, int lane, int (&off)[DTile<D>::BLOCKS / NW]) {
+  using T = DTile<D>;
+  constexpr int PER_WAVE = T::BLOCKS / NW;
+#pragma unroll
+  for (int i = 0; i < PER_WAVE; ++i) {
+    const int p = (wave * PER_WAVE + i) * 64 + lane;
+    const int row = p / T::CPR, pc = p % T::CPR;
+    const int c = pc ^ (ISV ? swz_v<D>(row) : swz_k<D>(row));
+    off[i] = row * T::ROWB + c * 16;
+  }
+}
+
+// DMA of a whole tile (every row < N): `src` = the tile's first row in global
+// memory, `tile` = its LDS stage, `wave` uniform.
+template <int D, int NW>
+__device__ __forceinline__ void dma_full(const char *src, char *tile, int wave, const int (&off)[DTile<D>::BLOCKS / NW]) {
+  constexpr int PER_WAVE = DTile<D>::BLOCKS / NW;
+#pragma unroll
+  for (int i = 0; i < PER_WAVE; ++i)
+    __builtin_amdgcn_global_load_lds((const void *)(src + off[i]), (lds_void_t *)(tile + (wave * PER_WAVE + i) * 1024),
+                                     16, 0, 0);
+}
+
+// The same through a buffer resource over the head (base = the head's first
+// row, `head_bytes` long): the tile's byte offset goes in a scalar, each
+// lane's unit offset in one vector register, and no address arithmetic runs
+// per tile.
+template <int D, int NW>
+__device__ __forceinline__ void dma_full_buf(const void *head, int head_bytes, int tile_byte_off, char *tile,
+                                             int wave, const int *off) {
+  constexpr int PER_WAVE = DTile<D>::BLOCKS / NW;
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(head), (short)0, head_bytes, 0x00020000);
+#pragma unroll
+  for (int i = 0; i < PER_WAVE; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t *)(tile + (wave * PER_WAVE + i) * 1024), 16, off[i],
+                                             tile_byte_off, 0, 0);
+}
+
+// Row maximum with three-input maxima (v_max3_f32).
+__device__ __forceinline__ float row_max3(const f32x16 &s0, const f32x16 &s1) {
+  float a = fmaxf(fmaxf(s0[0], s0[1]), s0[2]);
+  float b = fmaxf(fmaxf(s1[0], s1[1]), s1[2]);
+#pragma unroll
+  for (int r = 3; r < 15; r += 2) {
+    a = fmaxf(fmaxf(a, s0[r]), s0[r + 1]);
+    b = fmaxf(fmaxf(b, s1[r]), s1[r + 1]);
+  }
+  a = fmaxf(fmaxf(a, s0[15]), b);
+  a = fmaxf(a, s1[15]);
+  return fmaxf(a, __shfl_xor(a, 32));
+}
+
+// Per-lane byte offsets of the K operand reads (one per 16-dim step; the
+// second 32-key block is +32 rows).
+template <int D>
+__device__ __forceinline__ void k_offsets(int l32, int hi, int (&off)[D / 16]) {
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+    off[ks] = l32 * DTile<D>::ROWB + (((2 * ks + hi) ^ swz_k<D>(l32)) << 4);
+}
+
+// Per-lane byte offsets of the transposed V reads, one per 32-dim block; the
+// chunk (j) and half (s) terms are added as immediates.
+template <int D>
+__device__ __forceinline__ void v_offsets(int lane, int (&off)[D / 32]) {
+  const int G = lane >> 4, r = (lane & 15) >> 2, q = lane & 3;
+  const int key = 4 * (G >> 1) + r;  // + 16*j + 8*s, which leaves key & 3 unchanged
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    const int d = 32 * db + 16 * (G & 1) + 4 * q;
+    off[db] = key * DTile<D>::ROWB + (((d >> 3) ^ swz_v<D>(key)) << 4) + (d & 7) * 2;
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void qk_tile_dma(const char *__restrict__ Ks, const bf16x8 (&qf)[D / 16],
+                                            const int (&koff)[D / 16], f32x16 &s0, f32x16 &s1) {
+  s0 = f32x16{};
+  s1 = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(Ks + koff[ks]);
+    const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(Ks + koff[ks] + 32 * DTile<D>::ROWB);
+    s0 = mfma32(a0, qf[ks], s0);
+    s1 = mfma32(a1, qf[ks], s1);
+  }
+}
+
+__device__ __forceinline__ v4s16 ds_read_tr16(const char *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s16_t *)(p));
+}
+
+template <int D>
+__device__ __forceinline__ void pv_tile_dma(const char *__restrict__ Vs, const bf16x8 (&pb)[4],
+                                            const int (&voff)[D / 32], f32x16 (&o)[D / 32]) {
+  constexpr int RB = DTile<D>::ROWB;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    bf16x8 a[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const v4s16 lo = ds_read_tr16(Vs + voff[db] + (16 * j) * RB);
+      const v4s16 hi = ds_read_tr16(Vs + voff[db] + (16 * j + 8) * RB);
+      typedef short v8s16 __attribute__((ext_vector_type(8)));
+      const v8s16 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      a[db] = __builtin_bit_cast(bf16x8, both);
+    }
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) o[db] = mfma32(a[db], pb[j], o[db]);
   }
 }
 
