@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--pmc-target", action="store_true",
                     help="launch the block-sparse attention kernel once and a plain 1.46 GB copy "
                          "(layout kernel with every head spatial) once, for hardware-counter runs")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="host only: turn the rocprofv3 FETCH_SIZE and WRITE_SIZE counter CSVs of two "
+                         "--pmc-target runs into the per-launch HBM traffic record under profiles/")
     return ap.parse_args()
 
 
@@ -57,13 +60,67 @@ def measured_traffic():
     try:
         rec = json.load(open(path))
         h = hashlib.sha256()
-        for src in rec["sources"]:
+        for src in TRAFFIC_SOURCES:
             h.update(open(os.path.join(ROOT, src), "rb").read())
         if h.hexdigest() != rec["source_sha256"]:
             return None
         return int(rec["traffic_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
         return None
+
+
+TRAFFIC_SOURCES = ["sparse_attention_video_online_amd/csrc/attn_mfma.hip",
+                   "sparse_attention_video_online_amd/csrc/attn_core.h",
+                   "sparse_attention_video_online_amd/csrc/svg_common.h"]
+
+
+def record_traffic(fetch_csv, write_csv):
+    """Writes the HBM traffic record of the block-sparse kernel from two
+    counter runs of `--pmc-target`.  FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch) of the attention launches are averaged.  Each is scaled by the
+    ratio of the known bytes of the plain copy (the last layout launch, which
+    reads and writes H*N*d*2 bytes) to what the same counter reads for it."""
+    import csv
+    import hashlib
+
+    def rows(path, counter):
+        att, copy = [], []
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                if "attn_fwd_mfma<128, 128, false>" in r["Kernel_Name"]:
+                    att.append((int(r["Dispatch_Id"]), float(r["Counter_Value"])))
+                elif "layout_kernel" in r["Kernel_Name"]:
+                    copy.append((int(r["Dispatch_Id"]), float(r["Counter_Value"])))
+        att = [v for _, v in sorted(set(att))]
+        copy = [v for _, v in sorted(set(copy))]
+        return att, copy[-1]
+
+    from synth import HUNYUAN_LAYER as w
+    copy_bytes = w.H * w.N * w.d * 2
+    fa, fc = rows(fetch_csv, "FETCH_SIZE")
+    wa, wc = rows(write_csv, "WRITE_SIZE")
+    fs, wsc = copy_bytes / (fc * 1024.0), copy_bytes / (wc * 1024.0)
+    fetch = sum(fa) / len(fa) * 1024.0 * fs
+    write = sum(wa) / len(wa) * 1024.0 * wsc
+    h = hashlib.sha256()
+    for src in TRAFFIC_SOURCES:
+        h.update(open(os.path.join(ROOT, src), "rb").read())
+    rec = {"kernel": "attn_fwd_mfma<128,128> block-sparse", "workload": "hunyuan_layer (k5 masks)",
+           "source_sha256": h.hexdigest(), "sources": TRAFFIC_SOURCES,
+           "fetch_size_kib_per_launch": [round(x, 3) for x in fa],
+           "write_size_kib_per_launch": [round(x, 3) for x in wa],
+           "copy_kernel_bytes_each_way": copy_bytes,
+           "copy_fetch_size_kib": round(fc, 3), "copy_write_size_kib": round(wc, 3),
+           "fetch_scale": round(fs, 6), "write_scale": round(wsc, 6),
+           "hbm_fetch_bytes_per_launch": int(fetch), "hbm_write_bytes_per_launch": int(write),
+           "traffic_bytes_per_launch": int(fetch + write)}
+    out = os.path.join(ROOT, "profiles", "attn_fwd_mfma_hunyuan_layer_traffic.json")
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
 
 
 def gen_inputs(w):
@@ -239,6 +296,8 @@ def bench_svg2(args):
 
 def main():
     args = parse()
+    if args.record_traffic:
+        return record_traffic(*args.record_traffic)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path shards by head "
               f"with no exchange, see the design notes.", file=sys.stderr)
