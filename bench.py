@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--pmc-target", action="store_true",
                     help="launch the block-sparse attention kernel once and a plain 1.46 GB copy "
                          "(layout kernel with every head spatial) once, for hardware-counter runs")
+    ap.add_argument("--v-layout", default="vt", choices=["vt", "rowmajor"],
+                    help="vt: V permuted straight into the key-tiled transposed layout and the 256-row "
+                         "attention kernel (default); rowmajor: row-major V and the 128-row kernel")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="host only: turn the rocprofv3 FETCH_SIZE and WRITE_SIZE counter CSVs of two "
                          "--pmc-target runs into the per-launch HBM traffic record under profiles/")
@@ -69,9 +72,10 @@ def measured_traffic():
         return None
 
 
-TRAFFIC_SOURCES = ["sparse_attention_video_online_amd/csrc/attn_mfma.hip",
+TRAFFIC_SOURCES = ["sparse_attention_video_online_amd/csrc/attn_vt.hip",
                    "sparse_attention_video_online_amd/csrc/attn_core.h",
                    "sparse_attention_video_online_amd/csrc/svg_common.h"]
+TRAFFIC_KERNEL = "attn_fwd_vt<128, 128, false>"
 
 
 def record_traffic(fetch_csv, write_csv):
@@ -89,7 +93,7 @@ def record_traffic(fetch_csv, write_csv):
             for r in csv.DictReader(f):
                 if r["Counter_Name"] != counter:
                     continue
-                if "attn_fwd_mfma<128, 128, false>" in r["Kernel_Name"]:
+                if TRAFFIC_KERNEL in r["Kernel_Name"]:
                     att.append((int(r["Dispatch_Id"]), float(r["Counter_Value"])))
                 elif "layout_kernel" in r["Kernel_Name"]:
                     copy.append((int(r["Dispatch_Id"]), float(r["Counter_Value"])))
@@ -107,7 +111,7 @@ def record_traffic(fetch_csv, write_csv):
     h = hashlib.sha256()
     for src in TRAFFIC_SOURCES:
         h.update(open(os.path.join(ROOT, src), "rb").read())
-    rec = {"kernel": "attn_fwd_mfma<128,128> block-sparse", "workload": "hunyuan_layer (k5 masks)",
+    rec = {"kernel": TRAFFIC_KERNEL + " block-sparse", "workload": "hunyuan_layer (k5 masks)",
            "source_sha256": h.hexdigest(), "sources": TRAFFIC_SOURCES,
            "fetch_size_kib_per_launch": [round(x, 3) for x in fa],
            "write_size_kib_per_launch": [round(x, 3) for x in wa],
@@ -335,9 +339,17 @@ def main():
     comp_ws = torch.empty(max(1, svg.lib().svg_workspace_bytes(svg.SVG_OP_COMPACT, None, rows, nkb)),
                           dtype=torch.uint8, device=dev)
     qp, kp, vp, op, o = (torch.empty_like(q) for _ in range(5))
+    use_vt = args.v_layout == "vt"
+    vt = torch.empty(svg.svg_vt_elems(H, N, d), dtype=q.dtype, device=dev) if use_vt else None
     stream = torch.cuda.current_stream()
     ev_a0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ev_a1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+
+    def attend():
+        if use_vt:
+            svg.svg_block_sparse_attn_csr_vt(qp, kp, vt, row_ptr, kv_idx, F, S, T, bq, bk, out=op)
+        else:
+            svg.svg_block_sparse_attn_csr(qp, kp, vp, row_ptr, kv_idx, F, S, T, bq, bk, out=op)
 
     def step(i=None, stage_events=None):
         def mark(j):
@@ -351,11 +363,14 @@ def main():
         mark(2)
         svg.svg_layout_permute(q, F, S, T, labels, out=qp)
         svg.svg_layout_permute(k, F, S, T, labels, out=kp)
-        svg.svg_layout_permute(v, F, S, T, labels, out=vp)
+        if use_vt:
+            svg.svg_layout_permute_vt(v, F, S, T, labels, out=vt)
+        else:
+            svg.svg_layout_permute(v, F, S, T, labels, out=vp)
         mark(3)
         if i is not None:
             ev_a0[i].record(stream)
-        svg.svg_block_sparse_attn_csr(qp, kp, vp, row_ptr, kv_idx, F, S, T, bq, bk, out=op)
+        attend()
         if i is not None:
             ev_a1[i].record(stream)
         mark(4)
@@ -368,7 +383,7 @@ def main():
         # read and written)
         step()
         torch.cuda.synchronize()
-        svg.svg_block_sparse_attn_csr(qp, kp, vp, row_ptr, kv_idx, F, S, T, bq, bk, out=op)
+        attend()
         spatial = torch.zeros(H, dtype=torch.int32, device=dev)
         svg.svg_layout_permute(q, F, S, T, spatial, out=o)
         torch.cuda.synchronize()
@@ -414,13 +429,19 @@ def main():
 
     # dense baseline: this library's attention with every tile kept
     dense = torch.empty_like(q)
-    svg.svg_dense_attn(qp, kp, vp, F, S, T, bq, bk, out=dense)
+
+    def dense_attend():
+        if use_vt:
+            svg.svg_dense_attn_vt(qp, kp, vt, F, S, T, bq, bk, out=dense)
+        else:
+            svg.svg_dense_attn(qp, kp, vp, F, S, T, bq, bk, out=dense)
+    dense_attend()
     torch.cuda.synchronize()
     d0 = torch.cuda.Event(enable_timing=True)
     d1 = torch.cuda.Event(enable_timing=True)
     d0.record(stream)
     for _ in range(args.dense_reps):
-        svg.svg_dense_attn(qp, kp, vp, F, S, T, bq, bk, out=dense)
+        dense_attend()
     d1.record(stream)
     torch.cuda.synchronize()
     dense_ms = d0.elapsed_time(d1) / args.dense_reps
@@ -443,7 +464,8 @@ def main():
         "config": {"workload": w.name, "F": F, "S": S, "T": T, "N": N, "N_video": F * S, "H": H, "d": d,
                    "bq": bq, "bk": bk, "ks_frames": ks, "wt_tokens": wt, "n_samples": int(sidx.numel()),
                    "tile_density": round(density, 4), "kept_tiles": tiles,
-                   "labels": "".join(str(int(x)) for x in lab_host), "parallelism": "single GPU"},
+                   "labels": "".join(str(int(x)) for x in lab_host), "v_layout": args.v_layout,
+                   "parallelism": "single GPU"},
         "attn_ms": round(attn_ms, 4),
         "attn_tflops": round(attn_tflops, 2),
         "dense_ms": round(dense_ms, 4),
@@ -451,10 +473,11 @@ def main():
         "speedup_vs_dense_attn": round(dense_ms / attn_ms, 3),
         "speedup_vs_dense_layer": round(dense_ms / ms_per_step, 3),
         "stage_ms": {kk: round(vv, 4) for kk, vv in stage_ms.items()},
-        "roofline": {"bound": "mfma", "kernel": "attn_fwd_mfma<128,128> (block-sparse)",
+        "roofline": {"bound": "mfma",
+                     "kernel": ("attn_fwd_vt<128,128>" if use_vt else "attn_fwd_mfma<128,128>") + " (block-sparse)",
                      "achieved": round(attn_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic() if args.density == "k5" else None,
+                     "traffic": measured_traffic() if (args.density == "k5" and use_vt) else None,
                      "flop_per_launch": flops},
     }
     if not args.no_cpu_baseline:

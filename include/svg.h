@@ -199,6 +199,40 @@ svg_status svg_dense_attn(const svg_dims *dims, svg_dtype dtype,
                           int32_t bq, int32_t bk, float softmax_scale,
                           void *O, void *stream);
 
+/* ---------------------------------------------------------------------------
+ * The same attention with V in the key-tiled transposed layout "Vt" ([SVG1]:
+ * custom kernels on the transformed layout).  The layout is this library's
+ * choice for the gfx950 matrix cores: the pages fix only the token order,
+ * not how a kernel stores V.
+ *
+ * Vt of a [H][N][d] bf16 tensor V (executing layout), nKB = ceil(N/64):
+ *   Vt[((h*nKB + kb)*d + c)*64 + j] = V[h][kb*64 + j][c]   if kb*64 + j < N
+ *                                   = 0                    otherwise
+ * i.e. per 64-key block, the 64 keys of each dim are contiguous.  Size
+ * svg_vt_elems(dims) = H*nKB*64*d bf16 values; the caller owns it.
+ *
+ * svg_layout_permute_vt: Vt of svg_layout_permute(V) in one pass (each
+ *   head's executing layout per labels; labels == NULL permutes every head).
+ *   bf16 only.  V and Vt must not overlap.
+ * svg_block_sparse_attn_csr_vt, svg_dense_attn_vt: as
+ *   svg_block_sparse_attn_csr and svg_dense_attn, with V given as Vt.  Each
+ *   output row equals theirs up to fp32 summation order.  bf16 only,
+ *   (bq, bk) = (64, 64) or (128, 64), nKB <= 8192, N*d*2 < 2^31; otherwise
+ *   SVG_ERR_UNSUPPORTED and nothing is enqueued.
+ * ------------------------------------------------------------------------- */
+size_t svg_vt_elems(const svg_dims *dims);
+svg_status svg_layout_permute_vt(const svg_dims *dims, svg_dtype dtype, const void *V, void *Vt,
+                                 const int32_t *labels, void *stream);
+svg_status svg_block_sparse_attn_csr_vt(const svg_dims *dims, svg_dtype dtype,
+                                        const void *Q, const void *K, const void *Vt,
+                                        const int32_t *row_ptr, const int32_t *kv_idx,
+                                        int32_t bq, int32_t bk, float softmax_scale,
+                                        void *O, void *stream);
+svg_status svg_dense_attn_vt(const svg_dims *dims, svg_dtype dtype,
+                             const void *Q, const void *K, const void *Vt,
+                             int32_t bq, int32_t bk, float softmax_scale,
+                             void *O, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

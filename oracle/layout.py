@@ -35,3 +35,19 @@ def unpermute(y, F, S, T, labels):
         if lab == TEMPORAL:
             x[h] = y[h, e]
     return x
+
+
+def key_tiled_transpose(x, bk=64):
+    """The library's key-tiled transposed storage of V (a storage format of
+    this library, not of the pages): out[h, kb, c, j] = x[h, kb*bk + j, c] for
+    kb*bk + j < N, else 0.  Shape [H][ceil(N/bk)][d][bk].
+
+    x: [H][N][d] (any dtype; padding uses that dtype's zero).
+    """
+    H, N, d = x.shape
+    nkb = -(-N // bk)
+    out = np.zeros((H, nkb, d, bk), dtype=x.dtype)
+    for kb in range(nkb):
+        rows = x[:, kb * bk:min(N, (kb + 1) * bk), :]          # [H][<=bk][d]
+        out[:, kb, :, :rows.shape[1]] = np.transpose(rows, (0, 2, 1))
+    return out

@@ -68,6 +68,12 @@ bool overlaps(const void *a, const void *b, size_t bytes) {
   return x < y + bytes && y < x + bytes;
 }
 
+// [a, a + la) and [b, b + lb) share a byte
+bool overlaps2(const void *a, size_t la, const void *b, size_t lb) {
+  const char *x = (const char *)a, *y = (const char *)b;
+  return x < y + lb && y < x + la;
+}
+
 size_t block_sparse_ws(const Dims &dm, int bq, int bk) {
   const size_t nqb = (dm.N + bq - 1) / bq, nkb = (dm.N + bk - 1) / bk;
   const size_t rows = (size_t)dm.H * nqb;
@@ -240,6 +246,74 @@ svg_status svg_dense_attn(const svg_dims *dims, svg_dtype dtype, const void *Q, 
   return hip_status(run_attention(dm, dtype, Q, K, V, O, nullptr, nullptr, bq, bk,
                                   resolve_scale(softmax_scale, dm.d), (hipStream_t)stream),
                     "svg_dense_attn");
+}
+
+// Key-tiled transposed V (Vt) and the attention entry points that take it.
+
+size_t svg_vt_elems(const svg_dims *dims) {
+  if (dims == nullptr || dims->H < 1 || dims->d < 1) return 0;
+  const int64_t N = (int64_t)dims->F * dims->S + dims->T;
+  if (N < 1) return 0;
+  return (size_t)dims->H * (size_t)((N + 63) / 64) * 64 * (size_t)dims->d;
+}
+
+svg_status svg_layout_permute_vt(const svg_dims *dims, svg_dtype dtype, const void *V, void *Vt,
+                                 const int32_t *labels, void *stream) {
+  Dims dm{};
+  svg_status s;
+  if ((s = check_dims(dims, &dm)) != SVG_OK) return s;
+  if ((s = check_dtype(dtype)) != SVG_OK) return s;
+  if (dtype != SVG_BF16) return fail(SVG_ERR_UNSUPPORTED, "layout_permute_vt: bf16 only");
+  if (!V || !Vt) return fail(SVG_ERR_NULL, "layout_permute_vt: NULL tensor");
+  const size_t vbytes = (size_t)dm.H * dm.N * dm.d * 2, tbytes = svg_vt_elems(dims) * 2;
+  if (overlaps2(V, vbytes, Vt, tbytes))
+    return fail(SVG_ERR_RANGE, "layout_permute_vt: V and Vt overlap");
+  return hip_status(svgk::launch_layout_vt(dm, V, Vt, labels, (hipStream_t)stream), "svg_layout_permute_vt");
+}
+
+static svg_status vt_checks(const svg_dims *dims, svg_dtype dtype, const void *Q, const void *K,
+                            const void *Vt, const void *O, int bq, int bk, Dims *dm) {
+  svg_status s;
+  if ((s = check_dims(dims, dm, false)) != SVG_OK) return s;
+  if ((s = check_dtype(dtype)) != SVG_OK) return s;
+  if (dtype != SVG_BF16) return fail(SVG_ERR_UNSUPPORTED, "attention on Vt: bf16 only");
+  if (bk != 64 || (bq != 64 && bq != 128))
+    return fail(SVG_ERR_UNSUPPORTED, "attention on Vt: block shape %dx%d unsupported ((64,64), (128,64))", bq, bk);
+  const int64_t nkb = (dm->N + 63) / 64;
+  if (nkb > svgk::attn_vt_max_kv_blocks())
+    return fail(SVG_ERR_UNSUPPORTED, "attention on Vt: %lld kv-blocks > %d", (long long)nkb,
+                svgk::attn_vt_max_kv_blocks());
+  if ((int64_t)dm->N * dm->d * 2 >= ((int64_t)1 << 31))
+    return fail(SVG_ERR_UNSUPPORTED, "attention on Vt: one head is >= 2 GiB");
+  if (!Q || !K || !Vt || !O) return fail(SVG_ERR_NULL, "attention on Vt: NULL tensor");
+  const size_t bytes = (size_t)dm->H * dm->N * dm->d * 2, tbytes = svg_vt_elems(dims) * 2;
+  if (overlaps(O, Q, bytes) || overlaps(O, K, bytes) || overlaps2(O, bytes, Vt, tbytes))
+    return fail(SVG_ERR_RANGE, "attention on Vt: O overlaps an input");
+  return SVG_OK;
+}
+
+svg_status svg_block_sparse_attn_csr_vt(const svg_dims *dims, svg_dtype dtype, const void *Q,
+                                        const void *K, const void *Vt, const int32_t *row_ptr,
+                                        const int32_t *kv_idx, int32_t bq, int32_t bk,
+                                        float softmax_scale, void *O, void *stream) {
+  Dims dm{};
+  svg_status s;
+  if ((s = vt_checks(dims, dtype, Q, K, Vt, O, bq, bk, &dm)) != SVG_OK) return s;
+  if (!row_ptr || !kv_idx) return fail(SVG_ERR_NULL, "block_sparse_attn_csr_vt: NULL list");
+  return hip_status(svgk::launch_attn_vt(dm, Q, K, Vt, O, row_ptr, kv_idx, bq, bk,
+                                         resolve_scale(softmax_scale, dm.d), (hipStream_t)stream),
+                    "svg_block_sparse_attn_csr_vt");
+}
+
+svg_status svg_dense_attn_vt(const svg_dims *dims, svg_dtype dtype, const void *Q, const void *K,
+                             const void *Vt, int32_t bq, int32_t bk, float softmax_scale, void *O,
+                             void *stream) {
+  Dims dm{};
+  svg_status s;
+  if ((s = vt_checks(dims, dtype, Q, K, Vt, O, bq, bk, &dm)) != SVG_OK) return s;
+  return hip_status(svgk::launch_attn_vt(dm, Q, K, Vt, O, nullptr, nullptr, bq, bk,
+                                         resolve_scale(softmax_scale, dm.d), (hipStream_t)stream),
+                    "svg_dense_attn_vt");
 }
 
 // ---------------------------------------------------------------------------

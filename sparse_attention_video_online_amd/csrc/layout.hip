@@ -57,7 +57,60 @@ void permute_rows_kernel(const u32x4 *__restrict__ X, const int32_t *__restrict_
     Y[hoff + (int64_t)src * vpr + v] = X[hoff + (int64_t)n * vpr + v];
 }
 
+// Vt tile (h, kb): the 64 executing-layout rows kb*64.. of head h, transposed
+// to [d][64 keys], zero past N.  Executing row r of a permuted head reads
+// frame-major row f*S + p (r = p*F + f, video rows only).  The tile is
+// staged in LDS row-major with a padded stride; every global access is a
+// 16-byte vector and consecutive threads touch consecutive 16-byte units.
+template <int D>
+__global__ __launch_bounds__(256)
+void vt_kernel(const u32x4 *__restrict__ X, u32x4 *__restrict__ Y, const int32_t *__restrict__ labels,
+               int F, int S, int N, int nkb) {
+  constexpr int STR = D + 8;                 // padded row stride (halfwords)
+  constexpr int CPR = D / 8;                 // 16-byte units per row
+  __shared__ __attribute__((aligned(16))) uint16_t t[64 * STR];
+  const int kb = blockIdx.x, h = blockIdx.y;
+  const bool perm = labels == nullptr || labels[h] == 1;
+  const u32x4 *Xh = X + (size_t)h * N * CPR;
+  for (int u = threadIdx.x; u < 64 * CPR; u += 256) {
+    const int row = u / CPR, ch = u - row * CPR;
+    const int r = kb * 64 + row;
+    u32x4 v = u32x4{0, 0, 0, 0};
+    if (r < N) {
+      int src = r;
+      if (perm && r < F * S) {
+        const int p = r / F, f = r - p * F;
+        src = f * S + p;
+      }
+      v = Xh[(size_t)src * CPR + ch];
+    }
+    *reinterpret_cast<u32x4 *>(t + row * STR + ch * 8) = v;
+  }
+  __syncthreads();
+  u32x4 *Yt = Y + ((size_t)h * nkb + kb) * (D * 8);
+  for (int u = threadIdx.x; u < D * 8; u += 256) {
+    const int d = u >> 3, kc = u & 7;
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = (uint32_t)t[(8 * kc + 2 * i) * STR + d] | ((uint32_t)t[(8 * kc + 2 * i + 1) * STR + d] << 16);
+    Yt[u] = u32x4{w[0], w[1], w[2], w[3]};
+  }
+}
+
 }  // namespace
+
+hipError_t launch_layout_vt(const Dims &dm, const void *V, void *Vt, const int32_t *labels, hipStream_t st) {
+  const int nkb = (dm.N + 63) / 64;
+  if (dm.N == 0 || dm.H == 0) return hipSuccess;
+  if (dm.d == 128)
+    hipLaunchKernelGGL(vt_kernel<128>, dim3(nkb, dm.H), dim3(256), 0, st, (const u32x4 *)V, (u32x4 *)Vt, labels,
+                       dm.F, dm.S, dm.N, nkb);
+  else
+    hipLaunchKernelGGL(vt_kernel<64>, dim3(nkb, dm.H), dim3(256), 0, st, (const u32x4 *)V, (u32x4 *)Vt, labels,
+                       dm.F, dm.S, dm.N, nkb);
+  return hipGetLastError();
+}
 
 hipError_t launch_layout(const Dims &dm, int elem_bytes, const void *X, void *Y,
                          const int32_t *labels, bool inverse, hipStream_t st) {

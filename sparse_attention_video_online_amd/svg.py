@@ -60,6 +60,10 @@ SIGNATURES = {
     "svg_block_sparse_attn": [_DIMS, _I, _P, _P, _P, _P, _I, _I, _F, _P, _P, _Z, _P],
     "svg_block_sparse_attn_csr": [_DIMS, _I, _P, _P, _P, _P, _P, _I, _I, _F, _P, _P],
     "svg_dense_attn": [_DIMS, _I, _P, _P, _P, _I, _I, _F, _P, _P],
+    "svg_vt_elems": [_DIMS],
+    "svg_layout_permute_vt": [_DIMS, _I, _P, _P, _P, _P],
+    "svg_block_sparse_attn_csr_vt": [_DIMS, _I, _P, _P, _P, _P, _P, _I, _I, _F, _P, _P],
+    "svg_dense_attn_vt": [_DIMS, _I, _P, _P, _P, _I, _I, _F, _P, _P],
     "svg2_workspace_bytes": [_I, _DIMS, _I, _I],
     "svg_kmeans": [_DIMS, _I, _P, _I, _I, _P, _P, _P, _P, _P, _Z, _P],
     "svg_cluster_permute": [_DIMS, _P, _I, _P, _P, _P, _Z, _P],
@@ -67,7 +71,7 @@ SIGNATURES = {
     "svg_select_pairs": [_DIMS, _P, _P, _P, _I, _I, _D, _F, _P, _P, _P],
     "svg_varlen_attn": [_DIMS, _I, _P, _P, _P, _P, _P, _I, _I, _P, _P, _P, _F, _P, _P, _Z, _P],
 }
-_RESTYPES = {"svg_workspace_bytes": _Z, "svg2_workspace_bytes": _Z,
+_RESTYPES = {"svg_workspace_bytes": _Z, "svg2_workspace_bytes": _Z, "svg_vt_elems": _Z,
              "svg_last_error": ctypes.c_char_p, "svg_version": ctypes.c_char_p}
 
 
@@ -232,6 +236,52 @@ def svg_dense_attn(q, k, v, F, S, T, bq, bk, scale=-1.0, out=None):
     out = torch.empty_like(q) if out is None else out
     _check(_lib.svg_dense_attn(ctypes.byref(dm), dt, _ptr(q), _ptr(k), _ptr(v), bq, bk, scale, _ptr(out),
                                _stream()), "svg_dense_attn")
+    return out
+
+
+def svg_vt_elems(H, N, d):
+    """Elements of the key-tiled transposed V of a [H][N][d] tensor."""
+    dm = svg_dims(1, N, 0, H, d)
+    return int(_lib.svg_vt_elems(ctypes.byref(dm)))
+
+
+def svg_layout_permute_vt(v, F, S, T, labels=None, out=None):
+    """Vt (key-tiled transposed layout, shape [H][nKB][d][64]) of the
+    executing-layout V."""
+    H, N, d = v.shape
+    dm = svg_dims(F, S, T, H, d)
+    nkb = -(-N // 64)
+    out = torch.empty(H, nkb, d, 64, dtype=v.dtype, device=v.device) if out is None else out
+    _need(out, "Vt", v.dtype, svg_vt_elems(H, N, d))
+    _check(_lib.svg_layout_permute_vt(ctypes.byref(dm), _dtype(v), _ptr(v), _ptr(out), _ptr(labels), _stream()),
+           "svg_layout_permute_vt")
+    return out
+
+
+def _qk_vt(q, k, vt, F, S, T):
+    H, N, d = q.shape
+    if N != F * S + T:
+        raise ValueError(f"N={N} != F*S+T={F * S + T}")
+    for t, n in ((q, "Q"), (k, "K")):
+        _need(t, n, q.dtype, H * N * d)
+    _need(vt, "Vt", q.dtype, svg_vt_elems(H, N, d))
+    return svg_dims(F, S, T, H, d), _dtype(q)
+
+
+def svg_block_sparse_attn_csr_vt(q, k, vt, row_ptr, kv_idx, F, S, T, bq, bk, scale=-1.0, out=None):
+    dm, dt = _qk_vt(q, k, vt, F, S, T)
+    out = torch.empty_like(q) if out is None else out
+    _check(_lib.svg_block_sparse_attn_csr_vt(ctypes.byref(dm), dt, _ptr(q), _ptr(k), _ptr(vt), _ptr(row_ptr),
+                                             _ptr(kv_idx), bq, bk, scale, _ptr(out), _stream()),
+           "svg_block_sparse_attn_csr_vt")
+    return out
+
+
+def svg_dense_attn_vt(q, k, vt, F, S, T, bq, bk, scale=-1.0, out=None):
+    dm, dt = _qk_vt(q, k, vt, F, S, T)
+    out = torch.empty_like(q) if out is None else out
+    _check(_lib.svg_dense_attn_vt(ctypes.byref(dm), dt, _ptr(q), _ptr(k), _ptr(vt), bq, bk, scale, _ptr(out),
+                                  _stream()), "svg_dense_attn_vt")
     return out
 
 

@@ -95,3 +95,26 @@ def test_svg2_validation():
     assert L.svg_permute_rows(flat, 1, FAKE, FAKE2, FAKE, 0, None) == svg.SVG_ERR_RANGE
     assert L.svg_varlen_attn(flat, 1, FAKE, FAKE, FAKE, None, FAKE, 64, 256, FAKE, FAKE, None, -1.0, FAKE2,
                              FAKE2, 1 << 30, None) == svg.SVG_ERR_NULL
+
+
+def test_vt_entry_points_validate_on_host():
+    L = svg.lib()
+    # Vt element count: H * ceil(N/64) * 64 * d
+    assert L.svg_vt_elems(dims(F=4, S=64, T=16, H=2, d=64)) == 2 * 5 * 64 * 64
+    assert L.svg_vt_elems(None) == 0
+    bf16 = svg.SVG_BF16
+    assert L.svg_dense_attn_vt(dims(), 0, FAKE, FAKE, FAKE, 64, 64, -1.0, FAKE2, None) == svg.SVG_ERR_UNSUPPORTED
+    assert "bf16" in svg.last_error()
+    assert L.svg_dense_attn_vt(dims(), bf16, FAKE, FAKE, FAKE, 16, 16, -1.0, FAKE2, None) == svg.SVG_ERR_UNSUPPORTED
+    assert L.svg_dense_attn_vt(dims(), bf16, FAKE, None, FAKE, 64, 64, -1.0, FAKE2, None) == svg.SVG_ERR_NULL
+    # more than 8192 kv-blocks per head
+    big = dims(F=1, S=8192 * 64 + 1, T=0, H=1, d=64)
+    assert L.svg_dense_attn_vt(big, bf16, FAKE, FAKE, FAKE, 128, 64, -1.0, FAKE2, None) == svg.SVG_ERR_UNSUPPORTED
+    assert "kv-blocks" in svg.last_error()
+    assert L.svg_block_sparse_attn_csr_vt(dims(), bf16, FAKE, FAKE, FAKE, None, FAKE, 64, 64, -1.0, FAKE2,
+                                          None) == svg.SVG_ERR_NULL
+    # O overlapping an input
+    assert L.svg_dense_attn_vt(dims(), bf16, FAKE, FAKE2, FAKE, 64, 64, -1.0, FAKE, None) == svg.SVG_ERR_RANGE
+    assert L.svg_layout_permute_vt(dims(), 0, FAKE, FAKE2, None, None) == svg.SVG_ERR_UNSUPPORTED
+    assert L.svg_layout_permute_vt(dims(), bf16, FAKE, FAKE, None, None) == svg.SVG_ERR_RANGE
+    assert L.svg_layout_permute_vt(dims(), bf16, None, FAKE2, None, None) == svg.SVG_ERR_NULL

@@ -1,0 +1,254 @@
+"""GPU parity of the key-tiled V^T path against the float64 oracle.
+
+svg_layout_permute_vt is bit-exact against the oracle's permutation followed
+by its key-tiled transpose.  svg_block_sparse_attn_csr_vt / svg_dense_attn_vt
+outputs are toleranced like every bf16 attention output (max-abs 2e-2,
+rel-L2 1e-2).  The cases cover 256-row work-groups whose q-blocks keep
+different tiles, q-blocks with no kept tile next to ones with tiles, ragged
+N (partial last tile and partial last work-group), both head dims and both
+q-block heights.  Inputs are seeded and synthetic (synth/).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from _helpers import to_dev, to_host_bits, to_f64, ints, check_close, BF16_MAX_ABS, BF16_REL_L2
+from oracle import masks, layout, attention
+from oracle.numerics import as_f64
+from synth import COG, HUNYUAN
+from synth.generators import structured_qkv, generator_labels, random_qkv, f32_to_bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+svg = pytest.importorskip("sparse_attention_video_online_amd.svg")
+
+
+def sync():
+    torch.cuda.synchronize()
+
+
+_cache = {}
+
+
+def inputs(w):
+    if w.name not in _cache:
+        _cache[w.name] = structured_qkv(w)
+    return _cache[w.name]
+
+
+def csr(bm):
+    """Device CSR lists of a host bitmap [H][nqb][nkb] (through the library's
+    compaction, itself bit-exact against the oracle in test_gpu_svg1)."""
+    return svg.svg_compact_block_mask(torch.from_numpy(np.ascontiguousarray(bm)).cuda())
+
+
+# ----------------------------------------------------------------------------
+# layout
+
+@pytest.mark.parametrize("shape", [(3, 20, 15, 2, 64), (4, 33, 0, 3, 128), (2, 64, 64, 1, 64), (1, 1, 0, 1, 128)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_layout_permute_vt_bit_exact_small(shape):
+    F, S, T, H, d = shape
+    N = F * S + T
+    rng = np.random.default_rng(N + d)
+    v = f32_to_bf16_bits(rng.standard_normal((H, N, d)).astype(np.float32))
+    labels = np.array([h % 2 for h in range(H)], dtype=np.int32)
+    vt = svg.svg_layout_permute_vt(to_dev(v, "bf16"), F, S, T, ints(labels))
+    sync()
+    ref = layout.key_tiled_transpose(layout.permute(v, F, S, T, labels), 64)
+    np.testing.assert_array_equal(to_host_bits(vt), ref)
+
+
+@pytest.mark.parametrize("w", [COG, HUNYUAN], ids=lambda w: w.name)
+def test_layout_permute_vt_bit_exact_full(w):
+    g = inputs(w)
+    labels = np.array([1 - (h % 2) for h in range(w.H)], dtype=np.int32)
+    vt = svg.svg_layout_permute_vt(to_dev(g["v"], w.dtype), w.F, w.S, w.T, ints(labels))
+    sync()
+    got = to_host_bits(vt)
+    for h in (0, 1):
+        ref = layout.key_tiled_transpose(layout.permute(g["v"][h:h + 1], w.F, w.S, w.T, labels[h:h + 1]), 64)
+        np.testing.assert_array_equal(got[h], ref[0])
+
+
+def test_layout_permute_vt_labels_null_permutes_every_head():
+    F, S, T, H, d = 5, 7, 3, 2, 64
+    N = F * S + T
+    v = f32_to_bf16_bits(np.random.default_rng(1).standard_normal((H, N, d)).astype(np.float32))
+    vt = svg.svg_layout_permute_vt(to_dev(v, "bf16"), F, S, T, None)
+    sync()
+    ref = layout.key_tiled_transpose(layout.permute(v, F, S, T, [1, 1]), 64)
+    np.testing.assert_array_equal(to_host_bits(vt), ref)
+
+
+# ----------------------------------------------------------------------------
+# attention
+
+def run_sparse_vt(w, g, labels):
+    q, k, v = (to_dev(g[x], w.dtype) for x in "qkv")
+    lab = ints(labels)
+    qp, kp = (svg.svg_layout_permute(t, w.F, w.S, w.T, lab) for t in (q, k))
+    vt = svg.svg_layout_permute_vt(v, w.F, w.S, w.T, lab)
+    bm = svg.svg_build_block_mask(lab, w.F, w.S, w.T, w.H, w.d, w.ks, w.wt, w.bq, w.bk)
+    row_ptr, kv_idx = svg.svg_compact_block_mask(bm)
+    op = svg.svg_block_sparse_attn_csr_vt(qp, kp, vt, row_ptr, kv_idx, w.F, w.S, w.T, w.bq, w.bk)
+    o = svg.svg_layout_unpermute(op, w.F, w.S, w.T, lab)
+    sync()
+    return o
+
+
+def oracle_sparse_head(w, g, h, label, qblocks=None):
+    q, k, v = (as_f64(g[x][h], w.dtype) for x in "qkv")
+    xs = layout.permute(np.stack([q, k, v]), w.F, w.S, w.T, [label] * 3)
+    bm = masks.block_bitmap_ranges(label, w.F, w.S, w.T, w.ks, w.wt, w.bq, w.bk)
+    parts = attention.block_sparse_attention(xs[0], xs[1], xs[2], bm, w.bq, w.bk, qblocks=qblocks)
+    inv = masks.executing_to_original(label, w.F, w.S, w.T)
+    return {qb: (inv[qb * w.bq:qb * w.bq + o.shape[0]], o) for qb, o in parts.items()}
+
+
+def test_attention_vt_cogvideox_full():
+    """CogVideoX shape (13 x 1350 + 224 tokens, 8 heads, d = 64, 64x64 tiles):
+    four q-blocks per work-group, every row of every head checked."""
+    w = COG
+    g = inputs(w)
+    labels = generator_labels(w)
+    got = to_f64(run_sparse_vt(w, g, labels))
+    for h in range(w.H):
+        ref = np.zeros((w.N, w.d))
+        for qb, (rows, orow) in oracle_sparse_head(w, g, h, int(labels[h])).items():
+            ref[rows] = orow
+        check_close(got[h], ref, BF16_MAX_ABS, BF16_REL_L2, f"cog head {h}")
+
+
+def test_attention_vt_hunyuan_sampled_qblocks():
+    """Full HunyuanVideo shape (N = 119,056, 24 heads, d = 128, 128x64
+    tiles, ~31% density) in the launch configuration the bench times;
+    sampled q-blocks of every head, including both q-blocks of the last,
+    partial work-group and pairs that straddle a frame boundary."""
+    w = HUNYUAN
+    g = inputs(w)
+    labels = generator_labels(w)
+    got = to_f64(run_sparse_vt(w, g, labels))
+    rng = np.random.default_rng(321)
+    for h in range(w.H):
+        qbs = sorted(set([0, 1, 28, 29, w.nqb - 1, w.nqb - 2] + list(rng.integers(0, w.nqb, size=3))))
+        for qb, (rows, orow) in oracle_sparse_head(w, g, h, int(labels[h]), qblocks=qbs).items():
+            check_close(got[h][rows], orow, BF16_MAX_ABS, BF16_REL_L2, f"hunyuan head {h} qb {qb}")
+
+
+@pytest.mark.parametrize("N,d,bq", [(75, 64, 64), (300, 128, 128), (1, 128, 128), (200, 128, 64),
+                                    (1000, 64, 128), (777, 128, 128), (4100, 64, 64)])
+def test_attention_vt_random_bitmap_ragged(N, d, bq):
+    H, bk = 2, 64
+    q, k, v = random_qkv(H, N, d, seed=N + d + bq, dtype="bf16", scale=1.5)
+    nqb, nkb = -(-N // bq), -(-N // bk)
+    rng = np.random.default_rng(N + 7)
+    bm = (rng.random((H, nqb, nkb)) < 0.5).astype(np.uint8)
+    bm[:, 0, :] = 0                            # no kept tile; its group partner keeps some
+    bm[0, -1, -1] = 1                          # the ragged tail tile
+    if nqb > 1:
+        bm[:, 1, :] = 1
+    row_ptr, kv_idx = csr(bm)
+    vt = svg.svg_layout_permute_vt(to_dev(v, "bf16"), 1, N, 0, None)
+    o = svg.svg_block_sparse_attn_csr_vt(to_dev(q, "bf16"), to_dev(k, "bf16"), vt, row_ptr, kv_idx,
+                                         1, N, 0, bq, bk)
+    sync()
+    got = to_f64(o)
+    for h in range(H):
+        ref = attention.block_sparse_attention_full(as_f64(q[h], "bf16"), as_f64(k[h], "bf16"),
+                                                    as_f64(v[h], "bf16"), bm[h], bq, bk)
+        check_close(got[h], ref, BF16_MAX_ABS, BF16_REL_L2, f"random bitmap head {h}")
+        if bm[h, 0].sum() == 0:
+            assert np.all(got[h][:min(bq, N)] == 0.0)
+
+
+def test_attention_vt_whole_group_empty():
+    """Every q-block of some work-groups keeps nothing: those rows are zero."""
+    H, N, d, bq, bk = 1, 1000, 128, 128, 64
+    q, k, v = random_qkv(H, N, d, seed=5, dtype="bf16", scale=1.0)
+    nqb, nkb = -(-N // bq), -(-N // bk)
+    bm = np.zeros((H, nqb, nkb), dtype=np.uint8)
+    bm[0, 2, 3] = 1
+    bm[0, 7, :] = 1
+    row_ptr, kv_idx = csr(bm)
+    vt = svg.svg_layout_permute_vt(to_dev(v, "bf16"), 1, N, 0, None)
+    o = svg.svg_block_sparse_attn_csr_vt(to_dev(q, "bf16"), to_dev(k, "bf16"), vt, row_ptr, kv_idx,
+                                         1, N, 0, bq, bk)
+    sync()
+    got = to_f64(o)
+    ref = attention.block_sparse_attention_full(as_f64(q[0], "bf16"), as_f64(k[0], "bf16"),
+                                                as_f64(v[0], "bf16"), bm[0], bq, bk)
+    check_close(got[0], ref, BF16_MAX_ABS, BF16_REL_L2, "sparse groups")
+    assert np.all(got[0][:256] == 0.0) and np.all(got[0][512:768] == 0.0)
+
+
+def test_dense_vt_cogvideox_sampled_rows():
+    w = COG
+    g = inputs(w)
+    q, k, v = (to_dev(g[x], w.dtype) for x in "qkv")
+    zeros = ints(np.zeros(w.H))
+    vt = svg.svg_layout_permute_vt(v, w.F, w.S, w.T, zeros)
+    o = svg.svg_dense_attn_vt(q, k, vt, w.F, w.S, w.T, w.bq, w.bk)
+    sync()
+    got = to_f64(o)
+    rows = np.r_[0:64, 8000:8064, w.N - 40:w.N]
+    for h in (0, 5):
+        ref = attention.dense_attention(*(as_f64(g[x][h], w.dtype) for x in "qkv"), rows=rows)
+        check_close(got[h][rows], ref, BF16_MAX_ABS, BF16_REL_L2, f"dense head {h}")
+
+
+def test_attention_vt_k_zero_closed_form():
+    """K = 0: each row's output is the mean of V over its q-block's kept keys."""
+    H, N, d = 2, 600, 64
+    rng = np.random.default_rng(9)
+    qb_ = f32_to_bf16_bits(rng.standard_normal((H, N, d)).astype(np.float32))
+    vb_ = f32_to_bf16_bits(rng.standard_normal((H, N, d)).astype(np.float32))
+    kb_ = np.zeros_like(qb_)
+    nqb = nkb = -(-N // 64)
+    bm = (rng.random((H, nqb, nkb)) < 0.4).astype(np.uint8)
+    bm[:, :, -1] = 1
+    row_ptr, kv_idx = csr(bm)
+    vt = svg.svg_layout_permute_vt(to_dev(vb_, "bf16"), 1, N, 0, None)
+    o = svg.svg_block_sparse_attn_csr_vt(to_dev(qb_, "bf16"), to_dev(kb_, "bf16"), vt, row_ptr, kv_idx,
+                                         1, N, 0, 64, 64)
+    sync()
+    got = to_f64(o)
+    vv = as_f64(vb_, "bf16")
+    for h in range(H):
+        for qb in range(nqb):
+            keys = [j for j in range(N) if bm[h, qb, j // 64]]
+            ref = vv[h][keys].mean(axis=0)
+            rows = slice(qb * 64, min(N, qb * 64 + 64))
+            check_close(got[h][rows], np.tile(ref, (got[h][rows].shape[0], 1)), 1e-2, 1e-2, f"kzero {h} {qb}")
+
+
+def test_attention_vt_deterministic_and_close_to_row_major():
+    w = COG
+    g = inputs(w)
+    labels = generator_labels(w)
+    a = to_host_bits(run_sparse_vt(w, g, labels))
+    b = to_host_bits(run_sparse_vt(w, g, labels))
+    np.testing.assert_array_equal(a, b)
+    q, k, v = (to_dev(g[x], w.dtype) for x in "qkv")
+    lab = ints(labels)
+    qp, kp, vp = (svg.svg_layout_permute(t, w.F, w.S, w.T, lab) for t in (q, k, v))
+    bm = svg.svg_build_block_mask(lab, w.F, w.S, w.T, w.H, w.d, w.ks, w.wt, w.bq, w.bk)
+    row_ptr, kv_idx = svg.svg_compact_block_mask(bm)
+    o_rm = svg.svg_layout_unpermute(svg.svg_block_sparse_attn_csr(qp, kp, vp, row_ptr, kv_idx, w.F, w.S, w.T,
+                                                                  w.bq, w.bk), w.F, w.S, w.T, lab)
+    sync()
+    check_close(as_f64(a, "bf16"), to_f64(o_rm), 1e-2, 5e-3, "vt vs row-major")
+
+
+def test_vt_rejects_unsupported_shapes():
+    q = torch.zeros(1, 100, 64, dtype=torch.float32, device="cuda:0")
+    vt = torch.zeros(1, 2, 64, 64, dtype=torch.float32, device="cuda:0")
+    with pytest.raises(svg.SvgError) as e:
+        svg.svg_dense_attn_vt(q, q.clone(), vt, 1, 100, 0, 64, 64)
+    assert e.value.status == svg.SVG_ERR_UNSUPPORTED
+    qb = torch.zeros(1, 100, 64, dtype=torch.bfloat16, device="cuda:0")
+    vtb = torch.zeros(1, 2, 64, 64, dtype=torch.bfloat16, device="cuda:0")
+    with pytest.raises(svg.SvgError) as e:
+        svg.svg_dense_attn_vt(qb, qb.clone(), vtb, 1, 100, 0, 16, 16)
+    assert e.value.status == svg.SVG_ERR_UNSUPPORTED
