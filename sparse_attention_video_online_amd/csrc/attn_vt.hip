@@ -42,6 +42,9 @@ constexpr int kNW = 8;           // waves per work-group
 constexpr int kMaxKb = 8192;     // union-list capacity (kv-blocks per head)
 constexpr int kWords = kMaxKb / 32;
 
+// (1, 1) in bf16, the second operand of the row-sum dot products
+constexpr bf16x2_t kOnesBf16x2 = {(__bf16)1.0f, (__bf16)1.0f};
+
 // s_waitcnt with vmcnt = n and no wait on the other counters (gfx9 encoding).
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
@@ -286,11 +289,12 @@ void attn_fwd_vt(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K, con
     const char *const Kn = kst(std::integral_constant<int, ST + 1>{});    // K(it+1)
     const char *const Vc = vst(std::integral_constant<int, ST>{});        // V(it)
     char *const Vdst = vst(std::integral_constant<int, ST + 2>{});        // V(it+2)
-    // (A) tile it: not kept by this wave's q-block -> all -inf; keys past N
+    // (A) tile it: not kept by this wave's q-block -> contributes nothing
+    // (its exponentials are taken as exp2(x*0 - inf) = 0 below); keys past N
     // exist only in the last kv-block
-    if (!(e0 & own_bit)) {
-      s0 = f32x16{} - INFINITY;
-      s1 = f32x16{} - INFINITY;
+    bool own = true;
+    if constexpr (!DENSE) own = (e0 & own_bit) != 0;
+    if (!own) {
       mx = -INFINITY;
     } else if (((e0 & 0xFFFFFF) + 1) * BK > N) {
       const int nvalid = N - (e0 & 0xFFFFFF) * BK;
@@ -313,7 +317,8 @@ void attn_fwd_vt(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K, con
     const int e4_raw = ent_raw(it + 4);
     constexpr int NKS = D / 16;
     constexpr int PER = 32 / NKS;
-    const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
+    const float cc = own ? c : 0.f;
+    const float mc = !own ? INFINITY : (m_run == -INFINITY) ? 0.f : m_run * c;
     f32x16 n0 = f32x16{}, n1 = f32x16{};
     uint32_t pw[16];
     float rs = 0.f;
@@ -334,10 +339,11 @@ void attn_fwd_vt(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K, con
         const int idx = ks * PER + e;      // 0..31: s0 then s1
         const float x0 = idx < 16 ? s0[idx] : s1[idx - 16];
         const float x1 = idx < 16 ? s0[idx + 1] : s1[idx - 15];
-        const float p0 = fast_exp2(__builtin_fmaf(x0, c, -mc));
-        const float p1 = fast_exp2(__builtin_fmaf(x1, c, -mc));
-        rs += p0 + p1;
+        const float p0 = fast_exp2(__builtin_fmaf(x0, cc, -mc));
+        const float p1 = fast_exp2(__builtin_fmaf(x1, cc, -mc));
         pw[idx >> 1] = pack_bf16x2(p0, p1);
+        // row sum of the probabilities as they enter the MFMA (bf16)
+        rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[idx >> 1]), kOnesBf16x2, rs, false);
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {  // chunks of P completed by this step

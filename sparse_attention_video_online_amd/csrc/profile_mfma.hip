@@ -33,7 +33,8 @@ ProfileGrid profile_grid(const Dims &dm, int n_s) {
   const int nqg = (n_s + PQ - 1) / PQ;
   int c = (1024 + dm.H * nqg - 1) / (dm.H * nqg);
   c = max(1, min(c, max(1, nkb / 4)));
-  const int tpc = (nkb + c - 1) / c;
+  int tpc = (nkb + c - 1) / c;
+  tpc = min(tpc, 4096);
   return ProfileGrid{nqg, (nkb + tpc - 1) / tpc, tpc};
 }
 
@@ -43,6 +44,7 @@ struct Parts {
   float *o;    // [H][n_s][C][3][D]
   float *ml;   // [H][n_s][C][3][2]
   double *se;  // [H][n_s][2]
+  int32_t *ord_s, *ord_t;  // [n_s] each
 };
 
 Parts carve(void *ws, const Dims &dm, int n_s, const ProfileGrid &g) {
@@ -52,80 +54,145 @@ Parts carve(void *ws, const Dims &dm, int n_s, const ProfileGrid &g) {
   Parts r;
   r.o = (float *)p;
   r.ml = (float *)(p + align256(no));
+  const size_t nse = (size_t)dm.H * n_s * 2 * sizeof(double);
   r.se = (double *)(p + align256(no) + align256(nml));
+  r.ord_s = (int32_t *)(p + align256(no) + align256(nml) + align256(nse));
+  r.ord_t = r.ord_s + align256((size_t)n_s * 4) / 4;
   return r;
 }
 
-// Frame of key `key` given the tile's first frame f0 and the next frame's
-// first key jb (a 64-key tile spans at most two frames when S >= 64).
-__device__ __forceinline__ int key_frame(int key, int f0, int jb, int S, bool wide) {
-  return wide ? f0 + (key >= jb) : key / S;
+constexpr int kMaxVisit = 4096;   // visit-list capacity (tiles per chunk)
+constexpr int kMaxRankSamples = 16384;
+
+// Orders of the samples for the work-groups of the masked passes: ord_s by
+// row index (a work-group's samples then share few frames), ord_t by
+// position-major index p*F + f (they then share few grid positions).  Text
+// rows sort last in both.  Ties keep the sample order.  Only the grouping of
+// samples into work-groups changes; each sample's result has its own slot.
+__global__ __launch_bounds__(256)
+void profile_order(const int32_t *__restrict__ sample_idx, int n_s, int F, int S, int32_t *__restrict__ ord_s,
+                   int32_t *__restrict__ ord_t) {
+  const int s = blockIdx.x * 256 + threadIdx.x;
+  if (s >= n_s) return;
+  if (n_s > kMaxRankSamples) {
+    ord_s[s] = s;
+    ord_t[s] = s;
+    return;
+  }
+  const int FS = F * S;
+  auto rpos = [&](int i) { return i >= FS ? i : (i % S) * F + i / S; };
+  const int i = sample_idx[s], r = rpos(i);
+  int rs = 0, rt = 0;
+  for (int u = 0; u < n_s; ++u) {
+    const int j = sample_idx[u], q = rpos(j);
+    rs += (j < i) || (j == i && u < s);
+    rt += (q < r) || (q == r && u < s);
+  }
+  ord_s[rs] = s;
+  ord_t[rt] = s;
 }
 
 // One pass of masked attention for the work-group's 128 sampled rows over
 // one chunk of key tiles.  KIND 0 = no mask (full), 1 = spatial,
-// 2 = temporal.  The spatial pass visits only the tiles that the samples'
-// frame windows (and the text keys) can reach.
+// 2 = temporal.  A prologue lists the chunk's tiles that some sample of the
+// work-group keeps (any key), and flags the tiles where some video sample
+// does not keep every video key: only those evaluate the token mask.
 template <int D, int KIND>
 __global__ __launch_bounds__(PNT, 2)
 void profile_pass_mfma(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K, const bf16_t *__restrict__ V,
-                       const int32_t *__restrict__ sample_idx, int n_s, int F, int S, int N, int ks, int wt,
-                       int nkb, int tpc, int nchunks, float c, float *__restrict__ part_o,
-                       float *__restrict__ part_ml) {
+                       const int32_t *__restrict__ sample_idx, const int32_t *__restrict__ order, int n_s, int F,
+                       int S, int N, int ks, int wt, int nkb, int tpc, int nchunks, float c,
+                       float *__restrict__ part_o, float *__restrict__ part_ml) {
   using C = Tile<D, PNT>;
   __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE];
-  __shared__ int frange[2];
+  __shared__ uint16_t vlist[kMaxVisit];   // tile - t0, bit 15: evaluate the mask
+  __shared__ int bnd[5];     // f_lo, f_hi, p_lo, p_hi, text query present
+  __shared__ int wcount[PNW + 1];
   const int h = blockIdx.z, chunk = blockIdx.y, qg = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
   const size_t hoff = (size_t)h * N * D;
   const bf16_t *Kh = K + hoff, *Vh = V + hoff;
 
-  const int sidx = qg * PQ + wave * 32 + l32;
-  const bool valid = sidx < n_s;
+  const int pos = qg * PQ + wave * 32 + l32;
+  const bool valid = pos < n_s;
+  const int sidx = valid ? order[pos] : 0;
   const int i = valid ? sample_idx[sidx] : 0;
   const int FS = F * S;
   const bool text_i = i >= FS;
   const int fi = text_i ? 0 : i / S;
   const int pi = text_i ? 0 : i - fi * S;
-  const long long tlo = (long long)pi * F - wt, thi = (long long)pi * F + F - 1 + wt;
+  // temporal window of this row in position-major units (wt clamped so the
+  // bounds stay in int32)
+  const int wtc = min(wt, N);
+  const int tlo = pi * F - wtc, thi = pi * F + F - 1 + wtc;
 
-  // tiles this pass visits: [t0, t1) of the chunk, and for the spatial pass
-  // only the video tiles [va, vb] and the text tiles [tb, nkb)
-  int t0 = chunk * tpc, t1 = min(nkb, t0 + tpc);
-  int va = 0, vb = nkb - 1, tb = nkb;
-  if (KIND == 1) {
-    if (tid == 0) {
-      frange[0] = F;
-      frange[1] = -1;
+  // ---- visit list of this chunk
+  const int t0 = chunk * tpc, t1 = min(nkb, t0 + tpc);
+  if (tid < 5) bnd[tid] = (tid & 1) ? -1 : 0x7fffffff;
+  if (tid == 4) bnd[4] = 0;
+  __syncthreads();
+  if (KIND != 0 && valid) {
+    if (text_i) {
+      atomicMax(&bnd[4], 1);
+    } else {
+      atomicMin(&bnd[0], fi);
+      atomicMax(&bnd[1], fi);
+      atomicMin(&bnd[2], pi);
+      atomicMax(&bnd[3], pi);
     }
-    __syncthreads();
-    if (valid) {
-      if (text_i) {
-        atomicMin(&frange[0], 0);
-        atomicMax(&frange[1], F - 1);
+  }
+  __syncthreads();
+  const int f_lo = bnd[0], f_hi = bnd[1], p_lo = bnd[2], p_hi = bnd[3];
+  const bool any_video = f_hi >= 0, any_text = bnd[4] != 0;
+  // union / intersection of the video samples' windows
+  const long long RU_lo = (long long)p_lo * F - wtc, RU_hi = (long long)p_hi * F + F - 1 + wtc;
+  const long long RI_lo = (long long)p_hi * F - wtc, RI_hi = (long long)p_lo * F + F - 1 + wtc;
+  int nv = 0;
+  for (int base = t0; base < t1; base += PNT) {
+    const int t = base + tid;
+    bool visit = false, needmask = false;
+    if (t < t1) {
+      if (KIND == 0) {
+        visit = true;
       } else {
-        atomicMin(&frange[0], fi);
-        atomicMax(&frange[1], fi);
+        const int k0 = t * BK, k1 = min(N, k0 + BK) - 1;
+        if (k1 >= FS || any_text) visit = true;   // text keys / text rows keep all
+        if (k0 < FS && any_video) {
+          const int kv1 = min(k1, FS - 1);
+          for (int f = k0 / S; f <= kv1 / S; ++f) {
+            const int a = max(k0, f * S) - f * S, b = min(kv1, f * S + S - 1) - f * S;
+            bool some, all;
+            if (KIND == 1) {
+              some = f >= f_lo - ks && f <= f_hi + ks;
+              all = f >= f_hi - ks && f <= f_lo + ks;
+            } else {
+              // positions p in [a, b] with p*F + f inside [RU_lo, RU_hi]
+              const long long plo = (RU_lo - f + F - 1) >= 0 ? (RU_lo - f + F - 1) / F : 0;
+              const long long phi = RU_hi - f >= 0 ? (RU_hi - f) / F : -1;
+              some = max((long long)a, plo) <= min((long long)b, phi);
+              all = (long long)a * F + f >= RI_lo && (long long)b * F + f <= RI_hi;
+            }
+            visit |= some;
+            needmask |= !all;
+          }
+        }
       }
     }
+    const unsigned long long bal = __builtin_amdgcn_ballot_w64(visit);
+    if (lane == 0) wcount[wave] = __builtin_popcountll(bal);
     __syncthreads();
-    const int f_lo = max(0, frange[0] - ks), f_hi = min(F - 1, frange[1] + ks);
-    if (frange[1] < 0) {
-      va = 1;
-      vb = 0;  // no valid sample: no video tiles
-    } else {
-      va = (f_lo * S) / BK;
-      vb = ((f_hi + 1) * S - 1) / BK;
+    int off = nv;
+    for (int w = 0; w < wave; ++w) off += wcount[w];
+    int tot = 0;
+    for (int w = 0; w < PNW; ++w) tot += wcount[w];
+    if (visit) {
+      const int rank = __builtin_popcountll(bal & ((1ull << lane) - 1ull));
+      vlist[off + rank] = (uint16_t)((t - t0) | (needmask ? 0x8000 : 0));
     }
-    tb = FS / BK;  // first tile holding a text key (== nkb when T == 0 and FS % BK == 0)
-    if (FS >= N) tb = nkb;
+    nv += tot;
+    __syncthreads();
   }
-  auto visit = [&](int t) { return KIND != 1 || (t >= va && t <= vb) || t >= tb; };
-  auto next_from = [&](int t) {
-    while (t < t1 && !visit(t)) ++t;
-    return t;
-  };
 
   bf16x8 qf[D / 16];
   load_q<D>(Q + hoff, valid ? i : -1, hi, qf);
@@ -138,16 +205,16 @@ void profile_pass_mfma(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ 
   auto rows_of = [&](int t) {
     return [=](int j) { const int key = t * BK + j; return key < N ? key : -1; };
   };
-  int t = next_from(t0);
-  if (t < t1) {
-    load_tile<D, PNT>(Kh, Vh, tid, rows_of(t), R);
+  if (nv > 0) {
+    load_tile<D, PNT>(Kh, Vh, tid, rows_of(t0 + (vlist[0] & 0x7FFF)), R);
     store_tile<D, PNT>(smem, tid, R);
   }
   __syncthreads();
-  for (int it = 0; t < t1; ++it) {
-    const int tn = next_from(t + 1);
-    const bool more = tn < t1;
-    if (more) load_tile<D, PNT>(Kh, Vh, tid, rows_of(tn), R);
+  for (int it = 0; it < nv; ++it) {
+    const int e = vlist[it];
+    const int t = t0 + (e & 0x7FFF);
+    const bool more = it + 1 < nv;
+    if (more) load_tile<D, PNT>(Kh, Vh, tid, rows_of(t0 + (vlist[it + 1] & 0x7FFF)), R);
     const char *Ks = smem + (it & 1) * C::STAGE;
     const char *Vs = Ks + C::KBYTES;
 
@@ -155,22 +222,19 @@ void profile_pass_mfma(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ 
     qk_tile<D, PNT>(Ks, qf, l32, hi, s0, s1);
     const int kbase = t * BK;
     if (kbase + BK > N) mask_tail(s0, s1, N - kbase, hi);
-    if (KIND != 0 && !text_i) {
-      const int f0 = kbase < FS ? kbase / S : F;
-      const int jb = (f0 + 1) * S;
-      const bool wide = S >= BK;
+    if (KIND != 0 && (e & 0x8000) && !text_i) {
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kbase + acc_key(b, r, hi);
           if (key >= FS) continue;  // text keys are always kept
-          const int fk = key_frame(key, f0, jb, S, wide);
+          const int fk = key / S;
           bool keep;
           if (KIND == 1) {
             keep = abs(fk - fi) <= ks;
           } else {
-            const long long rk = (long long)(key - fk * S) * F + fk;
+            const int rk = (key - fk * S) * F + fk;
             keep = rk >= tlo && rk <= thi;
           }
           if (!keep) {
@@ -186,7 +250,6 @@ void profile_pass_mfma(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ 
 
     if (more) store_tile<D, PNT>(smem + ((it + 1) & 1) * C::STAGE, tid, R);
     __syncthreads();
-    t = tn;
   }
 
   // partial result of this chunk: unnormalised O, running max, sum
@@ -281,7 +344,7 @@ size_t profile_mfma_ws_bytes(const Dims &dm, int n_s) {
   const ProfileGrid g = profile_grid(dm, n_s);
   return align256((size_t)dm.H * n_s * g.nchunks * 3 * dm.d * sizeof(float)) +
          align256((size_t)dm.H * n_s * g.nchunks * 3 * 2 * sizeof(float)) +
-         align256((size_t)dm.H * n_s * 2 * sizeof(double));
+         align256((size_t)dm.H * n_s * 2 * sizeof(double)) + 2 * align256((size_t)n_s * 4);
 }
 
 hipError_t launch_profile_mfma(const Dims &dm, const void *Q, const void *K, const void *V,
@@ -292,10 +355,12 @@ hipError_t launch_profile_mfma(const Dims &dm, const void *Q, const void *K, con
   const Parts p = carve(ws, dm, n_s, g);
   const int nkb = (dm.N + BK - 1) / BK;
   const dim3 grid(g.nqg, g.nchunks, dm.H);
+  hipLaunchKernelGGL(profile_order, dim3((n_s + 255) / 256), dim3(256), 0, st, sample_idx, n_s, dm.F, dm.S,
+                     p.ord_s, p.ord_t);
 #define SVG_PROFILE_PASS(DD, KK)                                                                            \
   hipLaunchKernelGGL((profile_pass_mfma<DD, KK>), grid, dim3(PNT), 0, st, (const bf16_t *)Q, (const bf16_t *)K, \
-                     (const bf16_t *)V, sample_idx, n_s, dm.F, dm.S, dm.N, ks, wt, nkb, g.tiles_per_chunk,        \
-                     g.nchunks, c, p.o, p.ml)
+                     (const bf16_t *)V, sample_idx, (KK) == 2 ? p.ord_t : p.ord_s, n_s, dm.F, dm.S, dm.N, ks, wt, \
+                     nkb, g.tiles_per_chunk, g.nchunks, c, p.o, p.ml)
   if (dm.d == 128) {
     SVG_PROFILE_PASS(128, 0);
     SVG_PROFILE_PASS(128, 1);

@@ -300,3 +300,43 @@ def test_profile_hunyuan_layer_labels():
         if not hd["ambiguous"]:
             assert lab[h] == hd["label"], (h, lab[h], hd)
         np.testing.assert_allclose(ms[h], [hd["mse_spatial"], hd["mse_temporal"]], rtol=5e-2, atol=1e-6)
+
+
+def test_profile_sample_order_invariant():
+    """The work-groups group samples by frame or by grid position; the labels
+    and MSEs do not depend on the order of sample_idx (up to the order of the
+    fp64 sums of squared errors)."""
+    w = COG
+    g = inputs(w)
+    si = sample_rows(w)
+    q, k, v = (to_dev(g[x], w.dtype) for x in "qkv")
+    la, ma = svg.svg_profile_heads(q, k, v, ints(si), w.F, w.S, w.T, w.ks, w.wt)
+    shuf = np.random.default_rng(4).permutation(si).astype(np.int32)
+    lb, mb = svg.svg_profile_heads(q, k, v, ints(shuf), w.F, w.S, w.T, w.ks, w.wt)
+    sync()
+    np.testing.assert_array_equal(la.cpu().numpy(), lb.cpu().numpy())
+    np.testing.assert_allclose(ma.double().cpu().numpy(), mb.double().cpu().numpy(), rtol=1e-6, atol=0)
+
+
+@pytest.mark.parametrize("ks,wt", [(1, 100), (2, 0), (0, 1350 * 13)])
+def test_profile_mask_widths_against_oracle(ks, wt):
+    """Masks of other widths (a temporal window that is not a multiple of F,
+    an empty one, one that covers every key) on unsorted samples that include
+    text rows: MSEs against the oracle, and labels where the oracle's margin
+    is clear."""
+    w = COG
+    g = inputs(w)
+    rng = np.random.default_rng(ks * 1000 + wt)
+    si = rng.choice(w.N, size=300, replace=False).astype(np.int32)
+    si[:5] = w.N - 1 - np.arange(5)                       # text rows
+    q, k, v = (to_dev(g[x], w.dtype) for x in "qkv")
+    labels, mse = svg.svg_profile_heads(q, k, v, ints(si), w.F, w.S, w.T, ks, wt)
+    sync()
+    ol, om = profile.profile_heads(*(as_f64(g[x], w.dtype) for x in "qkv"), w.F, w.S, w.T, si, ks, wt)
+    got = mse.double().cpu().numpy()
+    np.testing.assert_allclose(got, om, rtol=2e-2, atol=1e-6)
+    lab = labels.cpu().numpy()
+    for h in range(w.H):
+        a, b = om[h]
+        if abs(a - b) > 0.05 * max(a, b):
+            assert lab[h] == ol[h], (h, lab[h], ol[h], om[h])
