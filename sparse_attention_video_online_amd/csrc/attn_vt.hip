@@ -30,7 +30,7 @@
 // MFMA B-operand layout of P^T with keys in natural order.
 #include <type_traits>
 
-#include "attn_core.h"
+#include "attn_vt_core.h"
 
 namespace svgk {
 namespace {
@@ -39,71 +39,6 @@ using namespace core;
 
 constexpr int kWgRows = 256;     // query rows per work-group
 constexpr int kNW = 8;           // waves per work-group
-constexpr int kMaxKb = 8192;     // union-list capacity (kv-blocks per head)
-constexpr int kWords = kMaxKb / 32;
-
-// (1, 1) in bf16, the second operand of the row-sum dot products
-constexpr bf16x2_t kOnesBf16x2 = {(__bf16)1.0f, (__bf16)1.0f};
-
-// s_waitcnt with vmcnt = n and no wait on the other counters (gfx9 encoding).
-constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
-
-// Key (0..63) of accumulator value r of block b (0: keys 0-31, 1: 32-63)
-// under the K row order pi.
-__device__ __forceinline__ int acc_key_pi(int b, int r, int hi) {
-  return 32 * b + 16 * (r >> 3) + 8 * hi + (r & 7);
-}
-
-// pi(i): row i of a 32-key block of S^T holds key pi(i) (an involution).
-__device__ __forceinline__ int key_pi(int i) {
-  const int g = (i >> 2) & 3;
-  const int gp = (g == 1) ? 2 : (g == 2) ? 1 : g;
-  return (i & 16) | (gp << 2) | (i & 3);
-}
-
-// K operand offsets for S^T with rows in the pi order.
-template <int D>
-__device__ __forceinline__ void k_offsets_pi(int l32, int hi, int (&off)[D / 16]) {
-  const int row = key_pi(l32);
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks)
-    off[ks] = row * DTile<D>::ROWB + (((2 * ks + hi) ^ swz_k<D>(row)) << 4);
-}
-
-// V^T tile in LDS: D rows (dims) of 128 bytes (64 keys), 16-byte chunk c of
-// row d stored at position c ^ (d & 7).  Operand read of 16-key chunk j for
-// this lane: row d = 32*db + l32, chunk 2j + hi; offsets per j, db added as
-// an immediate (32 rows = 4 KB).
-__device__ __forceinline__ void vt_offsets(int l32, int hi, int (&off)[4]) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) off[j] = l32 * 128 + (((2 * j + hi) ^ (l32 & 7)) << 4);
-}
-
-// DMA of one tile whose first byte is `src`; units at or past `bytes` read
-// as zero (buffer range check on the per-lane offset).
-template <int D, int NW>
-__device__ __forceinline__ void dma_tile_buf(const char *src, int bytes, char *tile, int wave, const int *off) {
-  constexpr int PER_WAVE = DTile<D>::BLOCKS / NW;
-  const __amdgpu_buffer_rsrc_t rsrc =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(src), (short)0, bytes, 0x00020000);
-#pragma unroll
-  for (int i = 0; i < PER_WAVE; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t *)(tile + (wave * PER_WAVE + i) * 1024), 16, off[i],
-                                             0, 0, 0);
-}
-
-// DMA offsets of the V^T tile: lane's 16-byte unit p = blk*64 + lane lands at
-// LDS position p, which holds row p/8, logical chunk (p%8) ^ (row & 7).
-template <int D>
-__device__ __forceinline__ void vt_dma_offsets(int wave, int lane, int (&off)[DTile<D>::BLOCKS / kNW]) {
-  constexpr int PER = DTile<D>::BLOCKS / kNW;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int p = (wave * PER + i) * 64 + lane;
-    const int row = p >> 3;
-    off[i] = row * 128 + (((p & 7) ^ (row & 7)) << 4);
-  }
-}
 
 template <int D, int BQ, bool DENSE>
 __global__ __launch_bounds__(kWgRows * 2, 1)
@@ -152,73 +87,9 @@ void attn_fwd_vt(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K, con
   bf16_t *Oh = O + hoff;
   const int qrow = grp * kWgRows + wave * 32 + l32;
 
-  // ---- the union of the group's kept lists, ascending, with per-q-block flags
   int nt = nkb;
-  if constexpr (!DENSE) {
-    const int nw = (nkb + 31) >> 5;
-    for (int i = tid; i < G * kWords; i += kWgRows * 2) bits[i] = 0u;
-    __syncthreads();
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const int qb = grp * G + g;
-      if (qb < nqb) {
-        const int b = row_ptr[h * nqb + qb], e = row_ptr[h * nqb + qb + 1];
-        for (int i = b + tid; i < e; i += kWgRows * 2) {
-          const int kb = kv_idx[i];
-          atomicOr(&bits[g * kWords + (kb >> 5)], 1u << (kb & 31));
-        }
-      }
-    }
-    __syncthreads();
-    // per-word counts, exclusive scan by wave 0 (4 words per lane)
-    if (wave == 0) {
-      int cnt[4], tot = 0;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int w = 4 * lane + k;
-        uint32_t u = 0u;
-        if (w < nw) {
-#pragma unroll
-          for (int g = 0; g < G; ++g) u |= bits[g * kWords + w];
-        }
-        cnt[k] = __builtin_popcount(u);
-        tot += cnt[k];
-      }
-      int incl = tot;
-#pragma unroll
-      for (int s = 1; s < 64; s <<= 1) {
-        const int y = __shfl_up(incl, s);
-        if (lane >= s) incl += y;
-      }
-      int run = incl - tot;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        wsum[4 * lane + k] = run;
-        run += cnt[k];
-      }
-      if (lane == 63) wsum[kWords] = incl;
-    }
-    __syncthreads();
-    for (int w = tid; w < nw; w += kWgRows * 2) {
-      uint32_t fl[G], u = 0u;
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        fl[g] = bits[g * kWords + w];
-        u |= fl[g];
-      }
-      int pos = wsum[w];
-      while (u) {
-        const int b = __builtin_ctz(u);
-        u &= u - 1u;
-        int f = 0;
-#pragma unroll
-        for (int g = 0; g < G; ++g) f |= (int)((fl[g] >> b) & 1u) << g;
-        ulist[pos++] = (32 * w + b) | (f << 24);
-      }
-    }
-    nt = wsum[kWords];
-    __syncthreads();
-  }
+  if constexpr (!DENSE)
+    nt = build_union_list<G, kWgRows * 2>(row_ptr, kv_idx, h, grp, nqb, nkb, tid, lane, wave, ulist, bits, wsum);
 
   if (nt == 0) {  // no kept tile in the whole group: O = 0
     if (qrow < N) {
@@ -247,7 +118,7 @@ void attn_fwd_vt(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K, con
   k_offsets_pi<D>(l32, hi, koff);
   vt_offsets(l32, hi, voff);
   dma_offsets<D, kNW, false>(wave, lane, kdma);
-  vt_dma_offsets<D>(wave, lane, vdma);
+  vt_dma_offsets<D, kNW>(wave, lane, vdma);
   f32x16 o[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
@@ -277,7 +148,6 @@ void attn_fwd_vt(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K, con
   __syncthreads();
   f32x16 s0, s1;
   qk_tile_dma<D>(k0, qf, koff, s0, s1);
-  float mx = row_max3(s0, s1);
   __syncthreads();  // every wave is done with K(0) before K(3) overwrites it
 
   int it = 0;
@@ -289,51 +159,88 @@ void attn_fwd_vt(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K, con
     const char *const Kn = kst(std::integral_constant<int, ST + 1>{});    // K(it+1)
     const char *const Vc = vst(std::integral_constant<int, ST>{});        // V(it)
     char *const Vdst = vst(std::integral_constant<int, ST + 2>{});        // V(it+2)
-    // (A) tile it: not kept by this wave's q-block -> contributes nothing
-    // (its exponentials are taken as exp2(x*0 - inf) = 0 below); keys past N
-    // exist only in the last kv-block
+    constexpr int NKS = D / 16;            // QK steps of a tile
+    constexpr int PER = 32 / NKS;          // scores of S(it) per loop step
+    constexpr int LEAD = 2;                // QK steps issued before the statistics
+    // DMAs of V(it+2) and K(it+3) into the stages PV(it-1) and QK(it)
+    // released.  Their 2*PK instructions are spread over the loop steps
+    // below: issued back to back by every wave right after the barrier, they
+    // queue up in the load unit and hold the waves at issue.
+    const int kb_k = e3 & 0xFFFFFF, kb_v = e2 & 0xFFFFFF;
+    const int kleft = (N - kb_k * BK) * T::ROWB;
+    const __amdgpu_buffer_rsrc_t rk =
+        tile_rsrc(reinterpret_cast<const char *>(Kh) + (size_t)kb_k * TB, kleft < TB ? kleft : TB);
+    const __amdgpu_buffer_rsrc_t rv = tile_rsrc(reinterpret_cast<const char *>(Vth) + (size_t)kb_v * TB, TB);
+    auto dma_slot = [&](int ks) {
+#pragma unroll
+      for (int i = 0; i < 2 * PK; ++i) {
+        if (ks != i * (D / 16) / (2 * PK)) continue;
+        if (i & 1) dma_block(rv, Vdst, wave * PK + (i >> 1), vdma[i >> 1]);
+        else dma_block(rk, Kdst, wave * PK + (i >> 1), kdma[i >> 1]);
+      }
+    };
+    const int e4_raw = ent_raw(it + 4);
+    f32x16 n0 = f32x16{}, n1 = f32x16{};
+    auto kread = [&](int q, bf16x8 &a0, bf16x8 &a1) {
+      a0 = *reinterpret_cast<const bf16x8 *>(Kn + koff[q]);
+      a1 = *reinterpret_cast<const bf16x8 *>(Kn + koff[q] + 32 * T::ROWB);
+    };
+    bf16x8 kl0[LEAD], kl1[LEAD];
+#pragma unroll
+    for (int q = 0; q < LEAD; ++q) kread(q, kl0[q], kl1[q]);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // (A) statistics of S(it), overlapped with the first QK MFMAs of S(it+1).
+    // A tile this wave's q-block does not keep contributes nothing: its
+    // exponentials are taken as exp2(x*0 - inf) = 0.  Keys past N exist only
+    // in the last kv-block.
+    n0 = mfma32(kl0[0], qf[0], n0);
+    n1 = mfma32(kl1[0], qf[0], n1);
     bool own = true;
     if constexpr (!DENSE) own = (e0 & own_bit) != 0;
-    if (!own) {
-      mx = -INFINITY;
-    } else if (((e0 & 0xFFFFFF) + 1) * BK > N) {
+    // (scores of a tile this wave does not keep stay finite: exp2(x*0 - inf))
+    if (own && ((e0 & 0xFFFFFF) + 1) * BK > N) {
       const int nvalid = N - (e0 & 0xFFFFFF) * BK;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         if (acc_key_pi(0, r, hi) >= nvalid) s0[r] = -INFINITY;
         if (acc_key_pi(1, r, hi) >= nvalid) s1[r] = -INFINITY;
       }
-      mx = row_max3(s0, s1);
     }
+    float mx = lane_max_tree(s0, s1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 1; q < LEAD; ++q) {
+      n0 = mfma32(kl0[q], qf[q], n0);
+      n1 = mfma32(kl1[q], qf[q], n1);
+    }
+    mx = half_swap_max(mx);
+    if (!own) mx = -INFINITY;
     const float alpha = update_ref(mx, c, m_run, l_run);
-    rescale<D>(o, alpha);
-
-    // (B) DMAs, then D/16 hand-ordered steps (sched_barrier fences): step ks
-    // issues the two MFMAs of S(it+1) for dims 16ks..16ks+15 (K operands
-    // read one step ahead), the exponentials of 32/(D/16) scores of S(it),
-    // and, once a 16-key chunk of P(it) is complete, its O^T += V^T P^T MFMAs.
-    dma_v(e2, Vdst);
-    dma_k(e3, Kdst);
-    const int e4_raw = ent_raw(it + 4);
-    constexpr int NKS = D / 16;
-    constexpr int PER = 32 / NKS;
     const float cc = own ? c : 0.f;
     const float mc = !own ? INFINITY : (m_run == -INFINITY) ? 0.f : m_run * c;
-    f32x16 n0 = f32x16{}, n1 = f32x16{};
+    bf16x8 ka0, ka1;
+    kread(LEAD, ka0, ka1);
+    __builtin_amdgcn_sched_barrier(0);
+    rescale<D>(o, alpha);
+
+    // (B) NKS hand-ordered steps (sched_barrier fences): step ks issues the
+    // two MFMAs of S(it+1) for QK step ks + LEAD (K operands read one step
+    // ahead), the exponentials of PER scores of S(it), and, once a 16-key
+    // chunk of P(it) is complete, its O^T += V^T P^T MFMAs.
     uint32_t pw[16];
     float rs = 0.f;
-    bf16x8 ka0 = *reinterpret_cast<const bf16x8 *>(Kn + koff[0]);
-    bf16x8 ka1 = *reinterpret_cast<const bf16x8 *>(Kn + koff[0] + 32 * T::ROWB);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
+      const int q = ks + LEAD;
+      dma_slot(ks);
       bf16x8 kn0 = ka0, kn1 = ka1;
-      if (ks + 1 < NKS) {
-        kn0 = *reinterpret_cast<const bf16x8 *>(Kn + koff[ks + 1]);
-        kn1 = *reinterpret_cast<const bf16x8 *>(Kn + koff[ks + 1] + 32 * T::ROWB);
+      if (q + 1 < NKS) kread(q + 1, kn0, kn1);
+      if (q < NKS) {
+        n0 = mfma32(ka0, qf[q], n0);
+        n1 = mfma32(ka1, qf[q], n1);
       }
-      n0 = mfma32(ka0, qf[ks], n0);
-      n1 = mfma32(ka1, qf[ks], n1);
 #pragma unroll
       for (int e = 0; e < PER; e += 2) {
         const int idx = ks * PER + e;      // 0..31: s0 then s1
@@ -361,7 +268,6 @@ void attn_fwd_vt(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K, con
       __builtin_amdgcn_sched_barrier(0);
     }
     l_run += rs;
-    mx = row_max3(n0, n1);
 
     // (C) K(it+2) and V(it+1), issued one step ago, have landed once at most
     // this step's 2*PK DMAs are outstanding; then every wave's share is in
