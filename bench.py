@@ -59,7 +59,7 @@ def measured_traffic():
     copy of known size.  None if that record is missing or was taken on
     different kernel sources than the ones built here."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "attn_fwd_mfma_hunyuan_layer_traffic.json")
+    path = os.path.join(ROOT, "profiles", "attn_fwd_vt_hunyuan_layer_traffic.json")
     try:
         rec = json.load(open(path))
         h = hashlib.sha256()
@@ -120,7 +120,7 @@ def record_traffic(fetch_csv, write_csv):
            "fetch_scale": round(fs, 6), "write_scale": round(wsc, 6),
            "hbm_fetch_bytes_per_launch": int(fetch), "hbm_write_bytes_per_launch": int(write),
            "traffic_bytes_per_launch": int(fetch + write)}
-    out = os.path.join(ROOT, "profiles", "attn_fwd_mfma_hunyuan_layer_traffic.json")
+    out = os.path.join(ROOT, "profiles", "attn_fwd_vt_hunyuan_layer_traffic.json")
     with open(out, "w") as f:
         json.dump(rec, f, indent=1)
         f.write("\n")
