@@ -88,7 +88,12 @@ SVG2_COG = Workload(
     notes="Gaussian-mixture Q/K; k-means, cluster permute, top-p pairs, "
           "variable-size block-sparse attention")
 
-WORKLOADS = {w.name: w for w in (TINY, COG, HUNYUAN, HUNYUAN_LAYER, SVG2_COG)}
+SMOKE_BF16 = Workload(
+    name="smoke_bf16", F=4, S=256, T=32, H=2, d=128, dtype="bf16", bq=128, bk=64,
+    ks=1, wt=300, seed=6, grid=(16, 16), n_samples=64, structure_scale=3.0,
+    notes="head 0 spatial, head 1 temporal; the bf16 path of the HunyuanVideo layer at a small size")
+
+WORKLOADS = {w.name: w for w in (TINY, COG, HUNYUAN, HUNYUAN_LAYER, SVG2_COG, SMOKE_BF16)}
 
 # Extra mask-width points at the HunyuanVideo shape (density sweep).
 # (ks, wt) pairs chosen so that the spatial and temporal tile densities match.

@@ -56,7 +56,7 @@ def _structured_head(rng, F, S, T, d, kind, a):
 
 def head_kinds_and_scales(w: Workload, seed: int):
     """Per-head generator kind and structure scale for each workload."""
-    if w.name == "tiny":
+    if w.name in ("tiny", "smoke_bf16"):
         return [SPATIAL, TEMPORAL], [w.structure_scale] * 2
     if w.name == "cogvideox_shape":
         h2 = w.H // 2
