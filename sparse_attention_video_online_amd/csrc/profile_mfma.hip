@@ -72,24 +72,38 @@ constexpr int kMaxRankSamples = 16384;
 __global__ __launch_bounds__(256)
 void profile_order(const int32_t *__restrict__ sample_idx, int n_s, int F, int S, int32_t *__restrict__ ord_s,
                    int32_t *__restrict__ ord_t) {
+  __shared__ int ci[1024], cr[1024];
   const int s = blockIdx.x * 256 + threadIdx.x;
-  if (s >= n_s) return;
+  const bool act = s < n_s;
   if (n_s > kMaxRankSamples) {
-    ord_s[s] = s;
-    ord_t[s] = s;
+    if (act) {
+      ord_s[s] = s;
+      ord_t[s] = s;
+    }
     return;
   }
   const int FS = F * S;
   auto rpos = [&](int i) { return i >= FS ? i : (i % S) * F + i / S; };
-  const int i = sample_idx[s], r = rpos(i);
+  const int i = act ? sample_idx[s] : 0, r = rpos(i);
   int rs = 0, rt = 0;
-  for (int u = 0; u < n_s; ++u) {
-    const int j = sample_idx[u], q = rpos(j);
-    rs += (j < i) || (j == i && u < s);
-    rt += (q < r) || (q == r && u < s);
+  for (int base = 0; base < n_s; base += 1024) {
+    const int cnt = min(1024, n_s - base);
+    __syncthreads();
+    for (int u = threadIdx.x; u < cnt; u += 256) {
+      ci[u] = sample_idx[base + u];
+      cr[u] = rpos(ci[u]);
+    }
+    __syncthreads();
+    for (int u = 0; u < cnt; ++u) {
+      const int j = ci[u], q = cr[u], us = base + u;
+      rs += (j < i) || (j == i && us < s);
+      rt += (q < r) || (q == r && us < s);
+    }
   }
-  ord_s[rs] = s;
-  ord_t[rt] = s;
+  if (act) {
+    ord_s[rs] = s;
+    ord_t[rt] = s;
+  }
 }
 
 // One pass of masked attention for the work-group's 128 sampled rows over
@@ -223,13 +237,17 @@ void profile_pass_mfma(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ 
     const int kbase = t * BK;
     if (kbase + BK > N) mask_tail(s0, s1, N - kbase, hi);
     if (KIND != 0 && (e & 0x8000) && !text_i) {
+      // a 64-key tile spans at most two frames when S >= 64: one comparison
+      // against the next frame's first key replaces the division
+      const int f0 = min(kbase, FS - 1) / S, jb = (f0 + 1) * S;
+      const bool wide = S >= BK;
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kbase + acc_key(b, r, hi);
           if (key >= FS) continue;  // text keys are always kept
-          const int fk = key / S;
+          const int fk = wide ? f0 + (key >= jb) : key / S;
           bool keep;
           if (KIND == 1) {
             keep = abs(fk - fi) <= ks;
