@@ -66,6 +66,147 @@ void km_assign(const T *__restrict__ X, const double *__restrict__ cent, int N, 
   assign[(size_t)h * N + n] = arg;
 }
 
+// Assignment on the matrix cores (bf16 inputs).  ||x - c||^2 = ||x||^2 +
+// (||c||^2 - 2 x.c), and ||x||^2 is the same for every centroid, so the
+// argmin is that of ||c||^2 - 2 x.c.  x.c runs on v_mfma_f32_32x32x2_f32: x is
+// exact in fp32 (a bf16 value), c is the fp64 centroid rounded to fp32, and
+// the 64..128-term dot product accumulates in fp32.  That is the precision of
+// the vector kernel above, in another summation order; both decide as the
+// fp64 oracle wherever the runner-up is farther by more than ~1e-5 of the
+// distances.  Ties (identical centroids) keep the lower index: every lane
+// scans its centroid rows in increasing order with a strict "<", and the
+// two lanes of a point merge with the lower index on equality.
+//
+// km_prep writes, per head, the fp32 centroids as the MFMA's A operand wants
+// them: for each centroid, its even dims then its odd dims, as two rows of
+// D/2 floats padded to D/2 + 4 (so the 16 lanes of a ds_read_b128 fall in
+// distinct banks), and ||c||^2 (fp64, rounded; +inf for the padding rows up
+// to a multiple of 32, so they never win).
+constexpr int kKmPad = 4;
+
+template <int D>
+struct KmTab {
+  static constexpr int ROW = D / 2 + kKmPad;   // floats per half-row
+  __host__ __device__ static size_t floats(int kpad) { return (size_t)kpad * (2 * ROW + 1); }
+};
+
+template <int D>
+__global__ __launch_bounds__(256)
+void km_prep(const double *__restrict__ cent, int k, int kpad, float *__restrict__ tab) {
+  using TB = KmTab<D>;
+  const int h = blockIdx.y;
+  float *t = tab + (size_t)h * TB::floats(kpad);
+  float *cn = t + (size_t)kpad * 2 * TB::ROW;
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= kpad) return;
+  if (c >= k) {
+    cn[c] = INFINITY;
+    for (int e = 0; e < 2 * TB::ROW; ++e) t[(size_t)c * 2 * TB::ROW + e] = 0.f;
+    return;
+  }
+  const double *cr = cent + ((size_t)h * k + c) * D;
+  double n2 = 0.0;
+  for (int e = 0; e < D; ++e) {
+    const double v = cr[e];
+    n2 += v * v;
+    t[((size_t)c * 2 + (e & 1)) * TB::ROW + (e >> 1)] = (float)v;
+  }
+  for (int e = D / 2; e < TB::ROW; ++e) {
+    t[((size_t)c * 2) * TB::ROW + e] = 0.f;
+    t[((size_t)c * 2 + 1) * TB::ROW + e] = 0.f;
+  }
+  cn[c] = (float)n2;
+}
+
+// One wave = 64 points (two 32-point blocks), 4 waves per work-group.
+template <int D>
+__global__ __launch_bounds__(256)
+void km_assign_mfma(const bf16_t *__restrict__ X, const float *__restrict__ tab, int N, int k, int kpad,
+                    int32_t *__restrict__ assign) {
+  using TB = KmTab<D>;
+  extern __shared__ __attribute__((aligned(16))) float kt[];   // the head's table
+  const int h = blockIdx.y;
+  const size_t nf = TB::floats(kpad);
+  const float *th = tab + (size_t)h * nf;
+  for (size_t i = threadIdx.x * 4; i < nf; i += 256 * 4) {
+    if (i + 4 <= nf) *reinterpret_cast<f32x4 *>(kt + i) = *reinterpret_cast<const f32x4 *>(th + i);
+    else for (size_t j = i; j < nf; ++j) kt[j] = th[j];
+  }
+  __syncthreads();
+  const float *cn = kt + (size_t)kpad * 2 * TB::ROW;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int p0 = blockIdx.x * 256 + wave * 64 + l32, p1 = p0 + 32;
+  // B operands: x[point][2s + hi] for s = 0..D/2-1, fp32
+  float xb0[D / 2], xb1[D / 2];
+  auto load_x = [&](int p, float (&xb)[D / 2]) {
+    if (p < N) {
+      const bf16_t *xr = X + ((size_t)h * N + p) * D;
+#pragma unroll
+      for (int v = 0; v < D / 8; ++v) {
+        const u32x4 w = *reinterpret_cast<const u32x4 *>(xr + 8 * v);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)   // word q holds dims 8v + 2q (low half) and 8v + 2q + 1 (high half)
+          xb[4 * v + q] = __uint_as_float(hi ? (w[q] & 0xFFFF0000u) : (w[q] << 16));
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < D / 2; ++s) xb[s] = 0.f;
+    }
+  };
+  load_x(p0, xb0);
+  load_x(p1, xb1);
+  float best0 = INFINITY, best1 = INFINITY;
+  int arg0 = 0, arg1 = 0;
+  for (int cb = 0; cb < kpad / 32; ++cb) {
+    f32x16 a0 = f32x16{}, a1 = f32x16{};
+    const float *ar = kt + ((size_t)(cb * 32 + l32) * 2 + hi) * TB::ROW;
+#pragma unroll
+    for (int s4 = 0; s4 < D / 8; ++s4) {
+      const f32x4 a = *reinterpret_cast<const f32x4 *>(ar + 4 * s4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], xb0[4 * s4 + i], a0, 0, 0, 0);
+        a1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], xb1[4 * s4 + i], a1, 0, 0, 0);
+      }
+    }
+    // lane rows: centroid cb*32 + 8*(r/4) + 4*hi + r%4, increasing in r
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int cbase = cb * 32 + 8 * g + 4 * hi;
+      const f32x4 nn = *reinterpret_cast<const f32x4 *>(cn + cbase);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float d0 = __builtin_fmaf(-2.f, a0[4 * g + q], nn[q]);
+        const float d1 = __builtin_fmaf(-2.f, a1[4 * g + q], nn[q]);
+        if (d0 < best0) {
+          best0 = d0;
+          arg0 = cbase + q;
+        }
+        if (d1 < best1) {
+          best1 = d1;
+          arg1 = cbase + q;
+        }
+      }
+    }
+  }
+  // merge the two lanes of each point (lower index on equal distance)
+  auto merge = [&](float &b, int &a) {
+    const float ob = __shfl_xor(b, 32);
+    const int oa = __shfl_xor(a, 32);
+    if (ob < b || (ob == b && oa < a)) {
+      b = ob;
+      a = oa;
+    }
+  };
+  merge(best0, arg0);
+  merge(best1, arg1);
+  if (hi == 0) {
+    if (p0 < N) assign[(size_t)h * N + p0] = arg0;
+    if (p1 < N) assign[(size_t)h * N + p1] = arg1;
+  }
+}
+
 // Centroid of cluster j = mean of its members, taken in sorted (= index)
 // order.  An empty cluster keeps its centroid.
 template <typename T>
@@ -77,8 +218,21 @@ void km_update(const T *__restrict__ X, const int32_t *__restrict__ perm, const 
   const int32_t *p = perm + (size_t)h * N;
   const T *Xh = X + (size_t)h * N * D;
   if (e < D && o1 > o0) {
+    // members in batches of 8: their indices and values load independently,
+    // then the fp64 adds run in member order
     double s = 0.0;
-    for (int n = o0; n < o1; ++n) s += (double)to_f32<T>(Xh[(size_t)p[n] * D + e]);
+    int n = o0;
+    for (; n + 8 <= o1; n += 8) {
+      int idx[8];
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) idx[u] = p[n + u];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = to_f32<T>(Xh[(size_t)idx[u] * D + e]);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += (double)v[u];
+    }
+    for (; n < o1; ++n) s += (double)to_f32<T>(Xh[(size_t)p[n] * D + e]);
     cent[((size_t)h * k + j) * D + e] = s / (double)(o1 - o0);
   }
   if (e == 0) sizes[h * k + j] = o1 - o0;
@@ -372,13 +526,18 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 }  // namespace
 
 size_t kmeans_ws_bytes(const Dims &dm, int k) {
-  return align256((size_t)dm.H * dm.N * sizeof(int32_t)) + align256((size_t)dm.H * (k + 1) * sizeof(int32_t));
+  const int kpad = (k + 31) / 32 * 32;
+  const size_t tab = dm.d == 64 ? KmTab<64>::floats(kpad) : KmTab<128>::floats(kpad);
+  return align256((size_t)dm.H * dm.N * sizeof(int32_t)) + align256((size_t)dm.H * (k + 1) * sizeof(int32_t)) +
+         align256((size_t)dm.H * tab * sizeof(float));
 }
 
 hipError_t launch_kmeans(const Dims &dm, bool bf16, const void *X, int k, int iters, const int32_t *init_idx,
                          int32_t *assign, double *centroids, int32_t *sizes, void *ws, hipStream_t st) {
   int32_t *perm = (int32_t *)ws;
   int32_t *offs = (int32_t *)((char *)ws + align256((size_t)dm.H * dm.N * sizeof(int32_t)));
+  float *tab = (float *)((char *)offs + align256((size_t)dm.H * (k + 1) * sizeof(int32_t)));
+  const int kpad = (k + 31) / 32 * 32;
   if (bf16)
     hipLaunchKernelGGL(km_init<bf16_t>, dim3(k, dm.H), dim3(128), 0, st, (const bf16_t *)X, init_idx, dm.N, dm.d, k,
                        centroids);
@@ -393,8 +552,25 @@ hipError_t launch_kmeans(const Dims &dm, bool bf16, const void *X, int k, int it
     const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
+  // bf16: the MFMA assignment; its table takes kpad*(D+9) floats of LDS
+  const size_t mlds = (dm.d == 64 ? KmTab<64>::floats(kpad) : KmTab<128>::floats(kpad)) * sizeof(float);
+  const bool mfma = bf16 && mlds <= 160 * 1024;
+  if (mfma && mlds > 65536) {
+    const void *mf = dm.d == 64 ? (const void *)km_assign_mfma<64> : (const void *)km_assign_mfma<128>;
+    const hipError_t e = hipFuncSetAttribute(mf, hipFuncAttributeMaxDynamicSharedMemorySize, (int)mlds);
+    if (e != hipSuccess) return e;
+  }
+  const dim3 pgrid((kpad + 255) / 256, dm.H), mgrid((dm.N + 255) / 256, dm.H);
   for (int it = 0; it < iters; ++it) {
-    if (bf16 && dm.d == 64)
+    if (mfma && dm.d == 64) {
+      hipLaunchKernelGGL(km_prep<64>, pgrid, dim3(256), 0, st, centroids, k, kpad, tab);
+      hipLaunchKernelGGL(km_assign_mfma<64>, mgrid, dim3(256), mlds, st, (const bf16_t *)X, tab, dm.N, k, kpad,
+                         assign);
+    } else if (mfma) {
+      hipLaunchKernelGGL(km_prep<128>, pgrid, dim3(256), 0, st, centroids, k, kpad, tab);
+      hipLaunchKernelGGL(km_assign_mfma<128>, mgrid, dim3(256), mlds, st, (const bf16_t *)X, tab, dm.N, k, kpad,
+                         assign);
+    } else if (bf16 && dm.d == 64)
       hipLaunchKernelGGL((km_assign<bf16_t, 64>), grid, dim3(256), lds, st, (const bf16_t *)X, centroids, dm.N, k,
                          assign);
     else if (bf16)
