@@ -217,7 +217,8 @@ def bench_svg2(args):
     dm = svg.svg_dims(1, N, 0, H, d)
     ws_kq = torch.empty(svg.workspace_bytes(svg.SVG2_OP_KMEANS, dm, w.kq, svg2=True), dtype=torch.uint8, device=dev)
     ws_kk = torch.empty(svg.workspace_bytes(svg.SVG2_OP_KMEANS, dm, w.kk, svg2=True), dtype=torch.uint8, device=dev)
-    ws_cp = torch.empty(1, dtype=torch.uint8, device=dev)
+    ws_cp = torch.empty(max(1, svg.workspace_bytes(svg.SVG2_OP_CLUSTER_PERMUTE, dm, max(w.kq, w.kk), svg2=True)),
+                        dtype=torch.uint8, device=dev)
     ws_vl = torch.empty(svg.workspace_bytes(svg.SVG2_OP_VARLEN, dm, w.kq, w.kk, svg2=True), dtype=torch.uint8,
                         device=dev)
     stream = torch.cuda.current_stream()

@@ -15,6 +15,8 @@
 namespace svgk {
 namespace {
 
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
 // ---------------------------------------------------------------------------
 // k-means (Lloyd).  Assign: distances in fp32 from fp32 copies of the
 // centroids, strict "<" so ties keep the lower index.  Update: the members of
@@ -245,37 +247,76 @@ void km_update(const T *__restrict__ X, const int32_t *__restrict__ perm, const 
 // id bit).  A token's rank among equal ids in earlier lanes is a popcount.
 // Waves are ordered through per-wave, per-cluster counts in LDS.
 
-constexpr int kSortThreads = 1024;
-constexpr int kSortWaves = kSortThreads / 64;
+// Stable counting sort of each head's tokens by cluster id (k <= 256), in
+// three launches over chunks of kSortChunk tokens: per-chunk histograms; per
+// head, the cluster offsets and each chunk's first slot per cluster; then each
+// chunk places its tokens in index order.  Within a chunk, equal ids inside a
+// wave are found with 8 ballots (one per id bit) and a token's rank is a
+// popcount; per-wave counts order the waves, and the chunk's rounds of 256
+// tokens run in index order.  cnt is scratch of H * nchunks * k ints.
+constexpr int kSortChunk = 1024;
 
-__global__ __launch_bounds__(kSortThreads)
-void cluster_sort(const int32_t *__restrict__ assign, int N, int k, int32_t *__restrict__ perm,
-                  int32_t *__restrict__ offs) {
+__global__ __launch_bounds__(256)
+void sort_count(const int32_t *__restrict__ assign, int N, int k, int nch, int32_t *__restrict__ cnt) {
   __shared__ int32_t hist[256];
-  __shared__ int32_t start[256];     // offs[c] + tokens of cluster c placed in earlier rounds
-  __shared__ int32_t wcnt[kSortWaves][256];
-  const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = blockIdx.y, ch = blockIdx.x, tid = threadIdx.x;
+  hist[tid] = 0;
+  __syncthreads();
   const int32_t *a = assign + (size_t)h * N;
-  int32_t *p = perm + (size_t)h * N;
-  for (int c = tid; c < 256; c += kSortThreads) hist[c] = 0;
+  const int n0 = ch * kSortChunk, n1 = min(N, n0 + kSortChunk);
+  for (int n = n0 + tid; n < n1; n += 256) atomicAdd(&hist[a[n]], 1);
   __syncthreads();
-  for (int n = tid; n < N; n += kSortThreads) atomicAdd(&hist[a[n]], 1);
+  if (tid < k) cnt[((size_t)h * nch + ch) * k + tid] = hist[tid];
+}
+
+__global__ __launch_bounds__(256)
+void sort_scan(int k, int nch, int32_t *__restrict__ cnt, int32_t *__restrict__ offs) {
+  __shared__ int32_t tot[256];
+  const int h = blockIdx.x, c = threadIdx.x;
+  int32_t *ch = cnt + (size_t)h * nch * k;
+  int t = 0;
+  if (c < k)
+    for (int b = 0; b < nch; ++b) t += ch[(size_t)b * k + c];
+  tot[c] = c < k ? t : 0;
   __syncthreads();
-  if (tid == 0) {
+  if (c == 0) {  // exclusive scan over at most 256 clusters
     int run = 0;
-    for (int c = 0; c < k; ++c) {
-      offs[(size_t)h * (k + 1) + c] = run;
-      start[c] = run;
-      run += hist[c];
+    for (int j = 0; j < k; ++j) {
+      const int v = tot[j];
+      tot[j] = run;
+      run += v;
     }
     offs[(size_t)h * (k + 1) + k] = run;
   }
+  __syncthreads();
+  if (c < k) {
+    int run = tot[c];
+    offs[(size_t)h * (k + 1) + c] = run;
+    for (int b = 0; b < nch; ++b) {  // chunk b's first slot of cluster c
+      const int v = ch[(size_t)b * k + c];
+      ch[(size_t)b * k + c] = run;
+      run += v;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256)
+void sort_place(const int32_t *__restrict__ assign, int N, int k, int nch, const int32_t *__restrict__ cnt,
+                int32_t *__restrict__ perm) {
+  __shared__ int32_t start[256];
+  __shared__ int32_t wcnt[4][256];
+  __shared__ int32_t rcnt[256];
+  const int h = blockIdx.y, ch = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int32_t *a = assign + (size_t)h * N;
+  int32_t *p = perm + (size_t)h * N;
+  if (tid < k) start[tid] = cnt[((size_t)h * nch + ch) * k + tid];
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int base = 0; base < N; base += kSortThreads) {
-    for (int e = tid; e < kSortWaves * 256; e += kSortThreads) (&wcnt[0][0])[e] = 0;
+  const int n0 = ch * kSortChunk, n1 = min(N, n0 + kSortChunk);
+  for (int base = n0; base < n1; base += 256) {
+    for (int e = tid; e < 4 * 256; e += 256) (&wcnt[0][0])[e] = 0;
     __syncthreads();
     const int n = base + tid;
-    const bool valid = n < N;
+    const bool valid = n < n1;
     const int c = valid ? a[n] : 0;
     uint64_t same = __ballot(valid);
 #pragma unroll
@@ -286,21 +327,34 @@ void cluster_sort(const int32_t *__restrict__ assign, int N, int k, int32_t *__r
     const int rank = __popcll(same & below);
     if (valid && rank == 0) wcnt[wave][c] = __popcll(same);
     __syncthreads();
-    for (int cc = tid; cc < k; cc += kSortThreads) {  // exclusive prefix over waves
+    if (tid < k) {  // exclusive prefix over the 4 waves
       int run = 0;
-      for (int w = 0; w < kSortWaves; ++w) {
-        const int t = wcnt[w][cc];
-        wcnt[w][cc] = run;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int t = wcnt[w][tid];
+        wcnt[w][tid] = run;
         run += t;
       }
-      hist[cc] = run;  // this round's count of cluster cc
+      rcnt[tid] = run;
     }
     __syncthreads();
     if (valid) p[start[c] + wcnt[wave][c] + rank] = n;
     __syncthreads();
-    for (int cc = tid; cc < k; cc += kSortThreads) start[cc] += hist[cc];
-    __syncthreads();
+    if (tid < k) start[tid] += rcnt[tid];
   }
+}
+
+size_t sort_scratch_bytes(const Dims &dm, int k) {
+  const size_t nch = (dm.N + kSortChunk - 1) / kSortChunk;
+  return align256((size_t)dm.H * nch * k * sizeof(int32_t));
+}
+
+void launch_sort(const Dims &dm, const int32_t *assign, int k, int32_t *perm, int32_t *offs, int32_t *cnt,
+                 hipStream_t st) {
+  const int nch = (dm.N + kSortChunk - 1) / kSortChunk;
+  hipLaunchKernelGGL(sort_count, dim3(nch, dm.H), dim3(256), 0, st, assign, dm.N, k, nch, cnt);
+  hipLaunchKernelGGL(sort_scan, dim3(dm.H), dim3(256), 0, st, k, nch, cnt, offs);
+  hipLaunchKernelGGL(sort_place, dim3(nch, dm.H), dim3(256), 0, st, assign, dm.N, k, nch, cnt, perm);
 }
 
 // ---------------------------------------------------------------------------
@@ -521,7 +575,6 @@ constexpr int varlen_bq() { return D == 128 ? 128 : 64; }
 
 int varlen_max_tiles(const Dims &dm, int kq, int bq) { return (dm.N + bq - 1) / bq + kq; }
 
-size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 }  // namespace
 
@@ -529,7 +582,7 @@ size_t kmeans_ws_bytes(const Dims &dm, int k) {
   const int kpad = (k + 31) / 32 * 32;
   const size_t tab = dm.d == 64 ? KmTab<64>::floats(kpad) : KmTab<128>::floats(kpad);
   return align256((size_t)dm.H * dm.N * sizeof(int32_t)) + align256((size_t)dm.H * (k + 1) * sizeof(int32_t)) +
-         align256((size_t)dm.H * tab * sizeof(float));
+         align256((size_t)dm.H * tab * sizeof(float)) + sort_scratch_bytes(dm, k);
 }
 
 hipError_t launch_kmeans(const Dims &dm, bool bf16, const void *X, int k, int iters, const int32_t *init_idx,
@@ -538,6 +591,10 @@ hipError_t launch_kmeans(const Dims &dm, bool bf16, const void *X, int k, int it
   int32_t *offs = (int32_t *)((char *)ws + align256((size_t)dm.H * dm.N * sizeof(int32_t)));
   float *tab = (float *)((char *)offs + align256((size_t)dm.H * (k + 1) * sizeof(int32_t)));
   const int kpad = (k + 31) / 32 * 32;
+  int32_t *scnt = (int32_t *)((char *)tab +
+                              align256((size_t)dm.H *
+                                       (dm.d == 64 ? KmTab<64>::floats(kpad) : KmTab<128>::floats(kpad)) *
+                                       sizeof(float)));
   if (bf16)
     hipLaunchKernelGGL(km_init<bf16_t>, dim3(k, dm.H), dim3(128), 0, st, (const bf16_t *)X, init_idx, dm.N, dm.d, k,
                        centroids);
@@ -582,7 +639,7 @@ hipError_t launch_kmeans(const Dims &dm, bool bf16, const void *X, int k, int it
     else
       hipLaunchKernelGGL((km_assign<float, 128>), grid, dim3(256), lds, st, (const float *)X, centroids, dm.N, k,
                          assign);
-    hipLaunchKernelGGL(cluster_sort, dim3(dm.H), dim3(kSortThreads), 0, st, assign, dm.N, k, perm, offs);
+    launch_sort(dm, assign, k, perm, offs, scnt, st);
     if (bf16)
       hipLaunchKernelGGL(km_update<bf16_t>, dim3(k, dm.H), dim3(128), 0, st, (const bf16_t *)X, perm, offs, dm.N, k,
                          dm.d, centroids, sizes);
@@ -593,11 +650,11 @@ hipError_t launch_kmeans(const Dims &dm, bool bf16, const void *X, int k, int it
   return hipGetLastError();
 }
 
-size_t cluster_permute_ws_bytes(const Dims &, int) { return 0; }
+size_t cluster_permute_ws_bytes(const Dims &dm, int k) { return sort_scratch_bytes(dm, k); }
 
 hipError_t launch_cluster_permute(const Dims &dm, const int32_t *assign, int k, int32_t *perm, int32_t *offs,
-                                  void *, hipStream_t st) {
-  hipLaunchKernelGGL(cluster_sort, dim3(dm.H), dim3(kSortThreads), 0, st, assign, dm.N, k, perm, offs);
+                                  void *ws, hipStream_t st) {
+  launch_sort(dm, assign, k, perm, offs, (int32_t *)ws, st);
   return hipGetLastError();
 }
 
