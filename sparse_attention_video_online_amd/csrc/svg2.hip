@@ -277,17 +277,24 @@ void sort_scan(int k, int nch, int32_t *__restrict__ cnt, int32_t *__restrict__ 
   int t = 0;
   if (c < k)
     for (int b = 0; b < nch; ++b) t += ch[(size_t)b * k + c];
-  tot[c] = c < k ? t : 0;
-  __syncthreads();
-  if (c == 0) {  // exclusive scan over at most 256 clusters
-    int run = 0;
-    for (int j = 0; j < k; ++j) {
-      const int v = tot[j];
-      tot[j] = run;
-      run += v;
-    }
-    offs[(size_t)h * (k + 1) + k] = run;
+  // exclusive scan over the (at most 256) clusters: per wave, then across
+  // the 4 wave totals
+  const int lane = c & 63, wave = c >> 6;
+  const int v = c < k ? t : 0;
+  int incl = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(incl, d);
+    if (lane >= d) incl += y;
   }
+  if (lane == 63) tot[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += tot[w];
+  const int excl = before + incl - v;
+  if (c == 255) offs[(size_t)h * (k + 1) + k] = before + incl;
+  __syncthreads();
+  tot[c] = excl;
   __syncthreads();
   if (c < k) {
     int run = tot[c];
