@@ -73,6 +73,7 @@ def measured_traffic():
 
 
 TRAFFIC_SOURCES = ["sparse_attention_video_online_amd/csrc/attn_vt.hip",
+                   "sparse_attention_video_online_amd/csrc/attn_vt_core.h",
                    "sparse_attention_video_online_amd/csrc/attn_core.h",
                    "sparse_attention_video_online_amd/csrc/svg_common.h"]
 TRAFFIC_KERNEL = "attn_fwd_vt<128, 128, false>"

@@ -4,6 +4,8 @@
 // per-work-group union of the kept-tile lists.
 #pragma once
 
+#include <type_traits>
+
 #include "attn_core.h"
 
 namespace svgk {
@@ -184,6 +186,227 @@ __device__ __forceinline__ int build_union_list(const int32_t *__restrict__ row_
   const int nt = wsum[kWords];
   __syncthreads();
   return nt;
+}
+
+
+// The tile pipeline shared by the attention kernels on the V^T layout, for
+// one wave of NW: online-softmax attention of the wave's 32 query rows (B
+// operands qf, one row per lane pair) over the tiles ent_raw(0..nt-1).
+//   ent_raw(j): entry of tile j, kv-block in bits 0-23 and caller flags above;
+//               callers repeat the last entry for j >= nt (those DMAs land in
+//               free stages and are never read).  Read early, moved to a
+//               scalar register late.
+//   prep(s0, s1, e): masks the scores of the tile with entry e in place and
+//               returns whether the lane's row keeps any key of it.
+// K and V^T tiles come from Kh (row-major, N rows) and Vth (key-tiled, every
+// tile full) through three LDS stages each (k0..k2, v0..v2, TB bytes, all
+// waves of the work-group call this together: it contains barriers).  On
+// return o, m_run and l_run hold the un-normalised output, the reference
+// maximum and this lane's partial row sum.
+//
+// Per tile it, one wave:
+//   (A) the first QK MFMAs of S(it+1), then the statistics of S(it) (masks,
+//       row maximum as a max3 tree and a v_permlane32_swap, lazy reference
+//       update) behind them;
+//   (B) D/16 hand-ordered steps: the MFMAs of S(it+1), the exponentials of
+//       S(it), and the O^T += V^T P^T MFMAs of each completed 16-key chunk;
+//       the DMAs of V(it+2) and K(it+3) are spread over these steps;
+//   (C) wait until only this step's DMAs are in flight, one barrier.
+// S^T's rows (keys) are read from K in the order pi, so the accumulator
+// layout of S^T is the B-operand layout of P^T with keys in natural order.
+template <int D, int NW, typename EntRaw, typename Prep>
+__device__ __forceinline__ void vt_attend(int nt, EntRaw ent_raw, Prep prep, const bf16_t *__restrict__ Kh,
+                                          const bf16_t *__restrict__ Vth, int N, char *k0, char *k1, char *k2,
+                                          char *v0, char *v1, char *v2, const bf16x8 (&qf)[D / 16], int wave,
+                                          int lane, float c, f32x16 (&o)[D / 32], float &m_run, float &l_run) {
+  using T = DTile<D>;
+  constexpr int TB = T::TBYTES;            // K tile bytes == V^T tile bytes
+  constexpr int PK = T::BLOCKS / NW;       // DMA instructions per wave per tile
+  static_assert(T::BLOCKS % NW == 0, "tile DMA blocks must split over the waves");
+  auto kst = [&](auto i_c) -> char * {
+    constexpr int I = decltype(i_c)::value % 3;
+    if constexpr (I == 0) return k0;
+    else if constexpr (I == 1) return k1;
+    else return k2;
+  };
+  auto vst = [&](auto i_c) -> char * {
+    constexpr int I = decltype(i_c)::value % 3;
+    if constexpr (I == 0) return v0;
+    else if constexpr (I == 1) return v1;
+    else return v2;
+  };
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  using C2 = std::integral_constant<int, 2>;
+  auto ent = [&](int j) -> int { return __builtin_amdgcn_readfirstlane(ent_raw(j)); };
+  const int l32 = lane & 31, hi = lane >> 5;
+  int koff[D / 16], voff[4], kdma[PK], vdma[PK];
+  k_offsets_pi<D>(l32, hi, koff);
+  vt_offsets(l32, hi, voff);
+  dma_offsets<D, NW, false>(wave, lane, kdma);
+  vt_dma_offsets<D, NW>(wave, lane, vdma);
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
+  m_run = -INFINITY;
+  l_run = 0.f;
+
+  // Tile DMAs through a buffer resource based at the tile: rows past N fall
+  // outside the resource's range and read as zero (their scores are masked).
+  auto dma_k = [&](int e, char *tile) {
+    const int kb = e & 0xFFFFFF;
+    const int left = (N - kb * BK) * T::ROWB;
+    dma_tile_buf<D, NW>(reinterpret_cast<const char *>(Kh) + (size_t)kb * TB, left < TB ? left : TB, tile, wave,
+                        kdma);
+  };
+  auto dma_v = [&](int e, char *tile) {
+    const int kb = e & 0xFFFFFF;
+    dma_tile_buf<D, NW>(reinterpret_cast<const char *>(Vth) + (size_t)kb * TB, TB, tile, wave, vdma);
+  };
+
+  // prologue: K(0..2), V(0..1) in flight; S(0) = K(0) Q^T
+  int e0 = ent(0), e1 = ent(1), e2 = ent(2), e3 = ent(3);
+  dma_k(e0, k0);
+  dma_k(e1, k1);
+  dma_k(e2, k2);
+  dma_v(e0, v0);
+  dma_v(e1, v1);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  f32x16 s0, s1;
+  qk_tile_dma<D>(k0, qf, koff, s0, s1);
+  __syncthreads();  // every wave is done with K(0) before K(3) overwrites it
+
+  int it = 0;
+  // One tile; ST = it % 3 is a compile-time constant (the loop is unrolled
+  // by three), so every LDS address is a register plus an immediate.
+  auto step = [&](auto st_c) {
+    constexpr int ST = decltype(st_c)::value;
+    char *const Kdst = kst(std::integral_constant<int, ST>{});            // K(it+3)
+    const char *const Kn = kst(std::integral_constant<int, ST + 1>{});    // K(it+1)
+    const char *const Vc = vst(std::integral_constant<int, ST>{});        // V(it)
+    char *const Vdst = vst(std::integral_constant<int, ST + 2>{});        // V(it+2)
+    constexpr int NKS = D / 16;            // QK steps of a tile
+    constexpr int PER = 32 / NKS;          // scores of S(it) per loop step
+    constexpr int LEAD = 2;                // QK steps issued before the statistics
+    // DMAs of V(it+2) and K(it+3) into the stages PV(it-1) and QK(it)
+    // released.  Their 2*PK instructions are spread over the loop steps
+    // below: issued back to back by every wave right after the barrier, they
+    // queue up in the load unit and hold the waves at issue.
+    const int kb_k = e3 & 0xFFFFFF, kb_v = e2 & 0xFFFFFF;
+    const int kleft = (N - kb_k * BK) * T::ROWB;
+    const __amdgpu_buffer_rsrc_t rk =
+        tile_rsrc(reinterpret_cast<const char *>(Kh) + (size_t)kb_k * TB, kleft < TB ? kleft : TB);
+    const __amdgpu_buffer_rsrc_t rv = tile_rsrc(reinterpret_cast<const char *>(Vth) + (size_t)kb_v * TB, TB);
+    auto dma_slot = [&](int ks) {
+#pragma unroll
+      for (int i = 0; i < 2 * PK; ++i) {
+        if (ks != i * (D / 16) / (2 * PK)) continue;
+        if (i & 1) dma_block(rv, Vdst, wave * PK + (i >> 1), vdma[i >> 1]);
+        else dma_block(rk, Kdst, wave * PK + (i >> 1), kdma[i >> 1]);
+      }
+    };
+    const int e4_raw = ent_raw(it + 4);
+    f32x16 n0 = f32x16{}, n1 = f32x16{};
+    auto kread = [&](int q, bf16x8 &a0, bf16x8 &a1) {
+      a0 = *reinterpret_cast<const bf16x8 *>(Kn + koff[q]);
+      a1 = *reinterpret_cast<const bf16x8 *>(Kn + koff[q] + 32 * T::ROWB);
+    };
+    bf16x8 kl0[LEAD], kl1[LEAD];
+#pragma unroll
+    for (int q = 0; q < LEAD; ++q) kread(q, kl0[q], kl1[q]);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // (A) statistics of S(it), overlapped with the first QK MFMAs of S(it+1).
+    // prep masks S(it) and says whether this lane's rows keep the tile at
+    // all; a tile they do not keep contributes nothing: its exponentials are
+    // taken as exp2(x*0 - inf) = 0 (its scores stay finite).
+    n0 = mfma32(kl0[0], qf[0], n0);
+    n1 = mfma32(kl1[0], qf[0], n1);
+    const bool own = prep(s0, s1, e0);
+    float mx = lane_max_tree(s0, s1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 1; q < LEAD; ++q) {
+      n0 = mfma32(kl0[q], qf[q], n0);
+      n1 = mfma32(kl1[q], qf[q], n1);
+    }
+    mx = half_swap_max(mx);
+    if (!own) mx = -INFINITY;
+    const float alpha = update_ref(mx, c, m_run, l_run);
+    const float cc = own ? c : 0.f;
+    const float mc = !own ? INFINITY : (m_run == -INFINITY) ? 0.f : m_run * c;
+    bf16x8 ka0, ka1;
+    kread(LEAD, ka0, ka1);
+    __builtin_amdgcn_sched_barrier(0);
+    rescale<D>(o, alpha);
+
+    // (B) NKS hand-ordered steps (sched_barrier fences): step ks issues the
+    // two MFMAs of S(it+1) for QK step ks + LEAD (K operands read one step
+    // ahead), the exponentials of PER scores of S(it), and, once a 16-key
+    // chunk of P(it) is complete, its O^T += V^T P^T MFMAs.
+    uint32_t pw[16];
+    float rs = 0.f;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const int q = ks + LEAD;
+      dma_slot(ks);
+      bf16x8 kn0 = ka0, kn1 = ka1;
+      if (q + 1 < NKS) kread(q + 1, kn0, kn1);
+      if (q < NKS) {
+        n0 = mfma32(ka0, qf[q], n0);
+        n1 = mfma32(ka1, qf[q], n1);
+      }
+#pragma unroll
+      for (int e = 0; e < PER; e += 2) {
+        const int idx = ks * PER + e;      // 0..31: s0 then s1
+        const float x0 = idx < 16 ? s0[idx] : s1[idx - 16];
+        const float x1 = idx < 16 ? s0[idx + 1] : s1[idx - 15];
+        const float p0 = fast_exp2(__builtin_fmaf(x0, cc, -mc));
+        const float p1 = fast_exp2(__builtin_fmaf(x1, cc, -mc));
+        pw[idx >> 1] = pack_bf16x2(p0, p1);
+        // row sum of the probabilities as they enter the MFMA (bf16)
+        rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[idx >> 1]), kOnesBf16x2, rs, false);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {  // chunks of P completed by this step
+        if (8 * (j + 1) > (ks + 1) * PER || 8 * (j + 1) <= ks * PER) continue;
+        const bf16x8 pj = __builtin_bit_cast(bf16x8, u32x4{pw[4 * j], pw[4 * j + 1], pw[4 * j + 2], pw[4 * j + 3]});
+        bf16x8 va[D / 32];
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+          va[db] = *reinterpret_cast<const bf16x8 *>(Vc + voff[j] + db * 32 * 128);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) o[db] = mfma32(va[db], pj, o[db]);
+      }
+      ka0 = kn0;
+      ka1 = kn1;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    l_run += rs;
+
+    // (C) K(it+2) and V(it+1), issued one step ago, have landed once at most
+    // this step's 2*PK DMAs are outstanding; then every wave's share is in
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * PK));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    s0 = n0;
+    s1 = n1;
+    e0 = e1;
+    e1 = e2;
+    e2 = e3;
+    e3 = __builtin_amdgcn_readfirstlane(e4_raw);
+    ++it;
+  };
+
+  while (it + 3 <= nt) {
+    step(C0{});
+    step(C1{});
+    step(C2{});
+  }
+  if (it < nt) step(C0{});
+  if (it < nt) step(C1{});
 }
 
 }  // namespace core
