@@ -13,7 +13,7 @@ def build(force: bool = True) -> str:
         return LIB
     tmp = LIB + ".tmp"
     subprocess.run(["gcc", "-O2", "-fno-fast-math", "-fopenmp", "-fPIC", "-shared",
-                    SRC, "-o", tmp], check=True)
+                    SRC, "-o", tmp, "-lm"], check=True)
     os.replace(tmp, LIB)
     return LIB
 

@@ -15,16 +15,30 @@
  * The assign step of each point is independent, so points are split across
  * threads.  Each distance is summed over c in index order.  Each mean is
  * summed over points in index order.  No sum is reordered.
+ *
+ * Decision audit (optional, min_f32_ratio != NULL).  A float32 evaluation of
+ * a squared distance, as (x - m).(x - m) or as |m|^2 - 2 x.m plus |x|^2, with
+ * m rounded to float32 and its sums taken in any order, is off by at most
+ * B = (d + 4) u (|x|^2 + |m|^2 + 2 sum_c |x_c m_c|), u = 2^-24, to first
+ * order in u (the standard
+ * bound for a length-d dot product, gamma_d <= d u / (1 - d u), plus the
+ * roundings of m, of |m|^2 and of the final combination).  The float32
+ * argmin then equals this one whenever every other centroid j beats the
+ * winner a by D_j - D_a > B_j + B_a.  The audit reports the smallest
+ * (D_j - D_a) / (B_j + B_a) over all points, iterations and j != a; a
+ * centroid whose row equals the winner's bit for bit is skipped (it ties in
+ * every precision and the lower index wins on both sides).
  */
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 #include <float.h>
+#include <math.h>
 
 int oracle_lloyd_kmeans(const double *x, int64_t n, int32_t d, int32_t k,
                         const int32_t *init_idx, int32_t iters,
                         int32_t *assign, double *centroids, int64_t *sizes,
-                        double *min_rel_margin)
+                        double *min_rel_margin, double *min_f32_ratio)
 {
     if (n <= 0 || d <= 0 || k <= 0 || iters < 1) return 1;
     for (int32_t j = 0; j < k; ++j) {
@@ -33,10 +47,10 @@ int oracle_lloyd_kmeans(const double *x, int64_t n, int32_t d, int32_t k,
     }
     double *sums = (double *)malloc(sizeof(double) * (size_t)k * d);
     if (!sums) return 3;
-    double margin = DBL_MAX;
+    double margin = DBL_MAX, ratio = DBL_MAX;
     for (int32_t it = 0; it < iters; ++it) {
-        double it_margin = DBL_MAX;
-        #pragma omp parallel for schedule(static) reduction(min:it_margin)
+        double it_margin = DBL_MAX, it_ratio = DBL_MAX;
+        #pragma omp parallel for schedule(static) reduction(min:it_margin, it_ratio)
         for (int64_t i = 0; i < n; ++i) {
             const double *xi = x + i * d;
             double best = DBL_MAX, second = DBL_MAX;
@@ -55,8 +69,31 @@ int oracle_lloyd_kmeans(const double *x, int64_t n, int32_t d, int32_t k,
             double denom = best > 1e-300 ? best : 1e-300;
             double m = k > 1 ? (second - best) / denom : DBL_MAX;
             if (m < it_margin) it_margin = m;
+            if (min_f32_ratio && k > 1) {
+                const double u = 1.0 / 16777216.0;
+                const double *ca = centroids + (int64_t)arg * d;
+                double xx = 0.0, ba = 0.0;
+                for (int32_t c = 0; c < d; ++c) xx += xi[c] * xi[c];
+                for (int32_t c = 0; c < d; ++c) ba += ca[c] * ca[c] + 2.0 * fabs(xi[c] * ca[c]);
+                ba = (d + 4) * u * (xx + ba);
+                for (int32_t j = 0; j < k; ++j) {
+                    if (j == arg) continue;
+                    const double *cj = centroids + (int64_t)j * d;
+                    if (memcmp(cj, ca, sizeof(double) * d) == 0) continue;
+                    double dj = 0.0, bj = 0.0;
+                    for (int32_t c = 0; c < d; ++c) {
+                        double diff = xi[c] - cj[c];
+                        dj += diff * diff;
+                        bj += cj[c] * cj[c] + 2.0 * fabs(xi[c] * cj[c]);
+                    }
+                    bj = (d + 4) * u * (xx + bj);
+                    double r = (dj - best) / (ba + bj);
+                    if (r < it_ratio) it_ratio = r;
+                }
+            }
         }
         if (it_margin < margin) margin = it_margin;
+        if (it_ratio < ratio) ratio = it_ratio;
         memset(sums, 0, sizeof(double) * (size_t)k * d);
         for (int32_t j = 0; j < k; ++j) sizes[j] = 0;
         for (int64_t i = 0; i < n; ++i) {
@@ -74,5 +111,6 @@ int oracle_lloyd_kmeans(const double *x, int64_t n, int32_t d, int32_t k,
     }
     free(sums);
     if (min_rel_margin) *min_rel_margin = margin;
+    if (min_f32_ratio) *min_f32_ratio = ratio;
     return 0;
 }

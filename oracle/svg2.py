@@ -45,18 +45,23 @@ def _kmeans_lib():
         lib.oracle_lloyd_kmeans.argtypes = [
             ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
             ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
-            ctypes.c_void_p, ctypes.c_void_p]
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         _lib = lib
     return _lib
 
 
-def kmeans(x, init_idx, iters):
+def kmeans(x, init_idx, iters, f32_audit=False):
     """Lloyd k-means of the rows of x (float64 [n, d]) from centroids x[init_idx].
 
     Returns (assign int32[n], centroids float64[k, d], sizes int64[k],
     min_rel_margin).  The margin is the smallest (second-best - best) / best
     squared distance over all points and iterations.  It is used to audit
     that the assignments do not hinge on rounding.
+
+    With f32_audit, a fifth value follows: the smallest ratio of a distance
+    gap (any other centroid minus the winner) to the sum of the two
+    distances' worst-case float32 rounding error.  Above 1, every assignment
+    is the same under any float32 evaluation of the squared distances.
     """
     x = np.ascontiguousarray(x, dtype=np.float64)
     init_idx = np.ascontiguousarray(init_idx, dtype=np.int32)
@@ -66,11 +71,15 @@ def kmeans(x, init_idx, iters):
     cent = np.empty((k, d), dtype=np.float64)
     sizes = np.empty(k, dtype=np.int64)
     margin = ctypes.c_double(0.0)
+    ratio = ctypes.c_double(0.0)
     rc = _kmeans_lib().oracle_lloyd_kmeans(
         x.ctypes.data, n, d, k, init_idx.ctypes.data, iters, assign.ctypes.data,
-        cent.ctypes.data, sizes.ctypes.data, ctypes.byref(margin))
+        cent.ctypes.data, sizes.ctypes.data, ctypes.byref(margin),
+        ctypes.byref(ratio) if f32_audit else None)
     if rc != 0:
         raise ValueError(f"oracle k-means failed with code {rc}")
+    if f32_audit:
+        return assign, cent, sizes, margin.value, ratio.value
     return assign, cent, sizes, margin.value
 
 

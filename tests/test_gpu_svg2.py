@@ -108,8 +108,8 @@ def test_kmeans_small_shapes(N, d, k, iters, dtype):
     a, c, s = svg.svg_kmeans(to_dev(x, dtype), k, iters, ints(init))
     sync()
     for h in range(H):
-        oa, oc, os_, margin = osvg2.kmeans(as_f64(x[h], dtype), init[h], iters)
-        assert margin > 1e-3, margin
+        oa, oc, os_, margin, ratio = osvg2.kmeans(as_f64(x[h], dtype), init[h], iters, f32_audit=True)
+        assert margin > 1e-3 and ratio > 1.01, (margin, ratio)
         np.testing.assert_array_equal(a[h].cpu().numpy(), oa)
         np.testing.assert_array_equal(s[h].cpu().numpy(), os_)
         np.testing.assert_allclose(c[h].cpu().numpy(), oc, rtol=1e-12, atol=1e-12)

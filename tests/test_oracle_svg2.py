@@ -163,14 +163,39 @@ def test_svg2_workload_margin_audit():
     every k-means assignment beats the runner-up by >= 0.1% of its squared
     distance; every top-p crossing clears p by > 1e-8 on both sides, and the
     last kept cluster's probability beats the first dropped one by > 1e-8.
-    (The GPU path scores pairs in float64 from float64 centroids.)"""
+    (The GPU path scores pairs in float64 from float64 centroids.)  Every
+    assignment also clears the worst-case float32 rounding of the squared
+    distances (ratio > 1.01), so a float32 argmin in any summation order
+    takes the same decisions as the float64 one."""
     w = SVG2_COG
     g = mixture_qkv(w)
     for h in range(w.H):
         q = numerics.as_f64(g["q"][h], "bf16")
         k = numerics.as_f64(g["k"][h], "bf16")
-        aq, cq, sq, mq = svg2.kmeans(q, g["init_q"][h], w.iters)
-        ak, ck, sk, mk = svg2.kmeans(k, g["init_k"][h], w.iters)
+        aq, cq, sq, mq, rq = svg2.kmeans(q, g["init_q"][h], w.iters, f32_audit=True)
+        ak, ck, sk, mk, rk = svg2.kmeans(k, g["init_k"][h], w.iters, f32_audit=True)
         assert mq > 1e-3 and mk > 1e-3
+        assert rq > 1.01 and rk > 1.01, (h, rq, rk)
         ptr, idx, marg = svg2.select_pairs(cq, ck, sk, w.top_p)
         assert marg.min() > 1e-8, (h, marg.min(axis=0))
+
+
+def test_kmeans_f32_audit_closed_forms():
+    """The float32 decision audit on 1-D cases worked by hand (d = 1, so the
+    error bound is B = 5u (x^2 + m^2 + 2|x m|), u = 2^-24).  Points 1, 0, 3
+    against centroids 0 and 3 give gaps 3, 9, 9 over bounds 85u, 45u, 225u;
+    the smallest ratio is 3 / (85u).  A point 2^-30 off the midpoint of 0
+    and 1 gives gap 2^-29 over 12.5u: ratio 2^-5 / 12.5 = 0.0025, a decision
+    that float32 rounding could flip."""
+    x = np.array([[1.0], [0.0], [3.0]])
+    r = svg2.kmeans(x, [1, 2], 1, f32_audit=True)[4]
+    assert r == pytest.approx(3 * 2 ** 24 / 85, rel=1e-12)
+    x = np.array([[0.0], [1.0], [0.5 + 2.0 ** -30]])
+    r = svg2.kmeans(x, [0, 1], 1, f32_audit=True)[4]
+    assert r == pytest.approx(0.0025, rel=1e-6)
+    # A centroid equal to the winner bit for bit is no decision.  Centroids
+    # 0, 0, 4: point 0 vs 4 gives 16 / 80u, point 4 vs 0 gives 16 / 400u,
+    # point 1 vs 4 gives 8 / 130u; without the skip point 0 would give 0.
+    x = np.array([[0.0], [4.0], [1.0]])
+    r = svg2.kmeans(x, [0, 0, 1], 1, f32_audit=True)[4]
+    assert r == pytest.approx(16 / 400 * 2 ** 24, rel=1e-12)
