@@ -9,12 +9,14 @@
 // chunk of the N keys in 64-key tiles, with the S^T = K Q^T / O^T += V^T P^T
 // machinery of attn_core.h.  Each lane owns one sampled row.  Three passes
 // (full, spatial, temporal) each keep one online-softmax state, so a wave
-// holds one output accumulator and stays at two waves per SIMD.  The masks
-// are evaluated per score from the key index.  A tile with a frame boundary
-// inside needs one comparison, not a division.  The spatial pass visits
-// only the key tiles its samples' frame windows and the text keys can
-// reach.  Chunks are merged afterwards (flash-decoding style), and the
-// squared errors are summed in fp64 in a fixed order.
+// holds one output accumulator and stays at two waves per SIMD.  The masked
+// passes visit only the key tiles that some sample's window (or a text key)
+// reaches.  In a flagged tile each row keeps at most two key ranges, one
+// per frame the tile touches: a wave whose rows keep none of the tile skips
+// its math, a wave whose rows keep all of it needs no mask, and the others
+// test each score's key offset against the two ranges.  Chunks are merged
+// afterwards (flash-decoding style), and the squared errors are summed in
+// fp64 in a fixed order.
 #include "attn_core.h"
 
 namespace svgk {
@@ -123,7 +125,8 @@ void profile_pass_mfma(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ 
   __shared__ int bnd[5];     // f_lo, f_hi, p_lo, p_hi, text query present
   __shared__ int wcount[PNW + 1];
   const int h = blockIdx.z, chunk = blockIdx.y, qg = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   const size_t hoff = (size_t)h * N * D;
   const bf16_t *Kh = K + hoff, *Vh = V + hoff;
@@ -140,6 +143,21 @@ void profile_pass_mfma(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ 
   // bounds stay in int32)
   const int wtc = min(wt, N);
   const int tlo = pi * F - wtc, thi = pi * F + F - 1 + wtc;
+  // The same window per key frame f: positions pi - floor((wtc + f)/F) ..
+  // pi + floor((F - 1 + wtc - f)/F).  With wtc = wq*F + wr (0 <= wr < F) and
+  // 0 <= f < F the floors are wq + (f + wr >= F) and wq + (f < wr).
+  const int wq = wtc / F, wr = wtc - wq * F;
+  // Kept keys of frame f for this row, absolute [lo, hi] (lo > hi: none).
+  auto frame_keys = [&](int f, int &lo, int &hk) {
+    if (KIND == 1) {
+      const bool keep = abs(f - fi) <= ks;
+      lo = keep ? f * S : 1;
+      hk = keep ? f * S + S - 1 : 0;
+    } else {
+      lo = f * S + max(pi - (wq + (f + wr >= F)), 0);
+      hk = f * S + min(pi + (wq + (f < wr)), S - 1);
+    }
+  };
 
   // ---- visit list of this chunk
   const int t0 = chunk * tpc, t1 = min(nkb, t0 + tpc);
@@ -232,39 +250,86 @@ void profile_pass_mfma(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ 
     const char *Ks = smem + (it & 1) * C::STAGE;
     const char *Vs = Ks + C::KBYTES;
 
-    f32x16 s0, s1;
-    qk_tile<D, PNT>(Ks, qf, l32, hi, s0, s1);
     const int kbase = t * BK;
-    if (kbase + BK > N) mask_tail(s0, s1, N - kbase, hi);
-    if (KIND != 0 && (e & 0x8000) && !text_i) {
-      // a 64-key tile spans at most two frames when S >= 64: one comparison
-      // against the next frame's first key replaces the division
-      const int f0 = min(kbase, FS - 1) / S, jb = (f0 + 1) * S;
-      const bool wide = S >= BK;
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kbase + acc_key(b, r, hi);
-          if (key >= FS) continue;  // text keys are always kept
-          const int fk = wide ? f0 + (key >= jb) : key / S;
-          bool keep;
-          if (KIND == 1) {
-            keep = abs(fk - fi) <= ks;
+    // Token mask of a flagged tile.  With S >= 64 a tile holds keys of at
+    // most two frames (f0, then f0 + 1 from offset sp on; past the video the
+    // second part is the text keys, all kept), so this row keeps at most two
+    // offset ranges [a0, a0 + n0) and [a1, a1 + n1).  A wave none of whose
+    // rows keeps a key of the tile skips its math (the tile adds exact
+    // zeros); a wave whose rows keep every key needs no mask.
+    bool skip = false, ranges = false, perkey = false;
+    int a0 = 0, n0 = 0, a1 = 0, n1 = 0;
+    if (KIND != 0 && (e & 0x8000)) {
+      if (S >= BK) {
+        const int nvalid = min(BK, N - kbase);
+        if (text_i) {
+          n0 = nvalid;
+        } else {
+          const int f0 = min(kbase, FS - 1) / S;
+          const int sp = min(max((f0 + 1) * S - kbase, 0), BK);
+          int lo, hk;
+          frame_keys(f0, lo, hk);
+          a0 = max(lo - kbase, 0);
+          n0 = max(min(min(hk - kbase, sp - 1), nvalid - 1) - a0 + 1, 0);
+          if (f0 + 1 < F) {
+            frame_keys(f0 + 1, lo, hk);
           } else {
-            const int rk = (key - fk * S) * F + fk;
-            keep = rk >= tlo && rk <= thi;
+            lo = FS;
+            hk = N - 1;
           }
-          if (!keep) {
-            if (b == 0) s0[r] = -INFINITY; else s1[r] = -INFINITY;
+          a1 = max(lo - kbase, sp);
+          n1 = max(min(min(hk - kbase, BK - 1), nvalid - 1) - a1 + 1, 0);
+        }
+        const int kept = n0 + n1;
+        skip = __builtin_amdgcn_ballot_w64(valid && kept > 0) == 0;
+        ranges = __builtin_amdgcn_ballot_w64(valid && kept < nvalid) != 0;
+      } else {
+        perkey = !text_i;
+      }
+    }
+    if (!skip) {
+      f32x16 s0, s1;
+      qk_tile<D, PNT>(Ks, qf, l32, hi, s0, s1);
+      if (kbase + BK > N) mask_tail(s0, s1, N - kbase, hi);
+      if (ranges) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int off = acc_key(b, r, hi);
+            const bool keep = (unsigned)(off - a0) < (unsigned)n0 || (unsigned)(off - a1) < (unsigned)n1;
+            if (!keep) {
+              if (b == 0) s0[r] = -INFINITY; else s1[r] = -INFINITY;
+            }
+          }
+        }
+      } else if (perkey) {
+        // S < 64: a tile spans several frames; the mask per key
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kbase + acc_key(b, r, hi);
+            if (key >= FS) continue;  // text keys are always kept
+            const int fk = key / S;
+            bool keep;
+            if (KIND == 1) {
+              keep = abs(fk - fi) <= ks;
+            } else {
+              const int rk = (key - fk * S) * F + fk;
+              keep = rk >= tlo && rk <= thi;
+            }
+            if (!keep) {
+              if (b == 0) s0[r] = -INFINITY; else s1[r] = -INFINITY;
+            }
           }
         }
       }
+      bf16x8 pb[4];
+      const float alpha = softmax_step(s0, s1, c, m_run, l_run, pb);
+      rescale<D>(o, alpha);
+      pv_tile<D, PNT>(Vs, pb, l32, hi, o);
     }
-    bf16x8 pb[4];
-    const float alpha = softmax_step(s0, s1, c, m_run, l_run, pb);
-    rescale<D>(o, alpha);
-    pv_tile<D, PNT>(Vs, pb, l32, hi, o);
 
     if (more) store_tile<D, PNT>(smem + ((it + 1) & 1) * C::STAGE, tid, R);
     __syncthreads();

@@ -68,6 +68,13 @@ COG = Workload(
     n_samples=math.ceil(0.01 * (13 * 1350 + 224)), structure_scale=2.0,
     notes="heads 0-3 spatial, 4-7 temporal")
 
+SMALL_FRAMES = Workload(
+    name="small_frames", F=8, S=48, T=40, H=4, d=64, dtype="bf16",
+    bq=64, bk=64, ks=1, wt=50, seed=11, grid=(6, 8), n_samples=120,
+    structure_scale=2.0,
+    notes="frames shorter than a 64-key tile (a tile spans up to three "
+          "frames); heads alternate spatial / temporal")
+
 HUNYUAN = Workload(
     name="hunyuan_shape", F=33, S=3600, T=256, H=24, d=128, dtype="bf16",
     bq=128, bk=64, ks=5, wt=19800, seed=3, grid=(45, 80), n_samples=0,
@@ -93,7 +100,7 @@ SMOKE_BF16 = Workload(
     ks=1, wt=300, seed=6, grid=(16, 16), n_samples=64, structure_scale=3.0,
     notes="head 0 spatial, head 1 temporal; the bf16 path of the HunyuanVideo layer at a small size")
 
-WORKLOADS = {w.name: w for w in (TINY, COG, HUNYUAN, HUNYUAN_LAYER, SVG2_COG, SMOKE_BF16)}
+WORKLOADS = {w.name: w for w in (TINY, COG, SMALL_FRAMES, HUNYUAN, HUNYUAN_LAYER, SVG2_COG, SMOKE_BF16)}
 
 # Extra mask-width points at the HunyuanVideo shape (density sweep).
 # (ks, wt) pairs chosen so that the spatial and temporal tile densities match.

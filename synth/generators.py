@@ -58,6 +58,8 @@ def head_kinds_and_scales(w: Workload, seed: int):
     """Per-head generator kind and structure scale for each workload."""
     if w.name in ("tiny", "smoke_bf16"):
         return [SPATIAL, TEMPORAL], [w.structure_scale] * 2
+    if w.name == "small_frames":
+        return [SPATIAL, TEMPORAL] * (w.H // 2), [w.structure_scale] * w.H
     if w.name == "cogvideox_shape":
         h2 = w.H // 2
         return [SPATIAL] * h2 + [TEMPORAL] * (w.H - h2), [w.structure_scale] * w.H

@@ -17,7 +17,7 @@ from _helpers import (to_dev, to_host_bits, to_f64, ints, check_close, BF16_MAX_
                       F32_MAX_ABS, F32_REL_L2)
 from oracle import masks, layout, attention, profile
 from oracle.numerics import as_f64
-from synth import TINY, COG, HUNYUAN, HUNYUAN_LAYER
+from synth import TINY, COG, SMALL_FRAMES, HUNYUAN, HUNYUAN_LAYER
 from synth.generators import structured_qkv, sample_rows, generator_labels, random_qkv
 
 pytestmark = pytest.mark.gpu
@@ -318,6 +318,33 @@ def test_profile_sample_order_invariant():
     np.testing.assert_allclose(ma.double().cpu().numpy(), mb.double().cpu().numpy(), rtol=1e-6, atol=0)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_profile_small_frames(d):
+    """Frames shorter than a 64-key tile (S = 48: a tile spans up to three
+    frames), unsorted samples with text rows.  Structured heads: labels and
+    MSEs against the oracle.  Gaussian heads (every key matters, so a wrong
+    masked key moves both MSEs): MSEs against the oracle."""
+    from dataclasses import replace
+    w = replace(SMALL_FRAMES, d=d)
+    rng = np.random.default_rng(d)
+    si = rng.choice(w.N, size=w.n_samples, replace=False).astype(np.int32)
+    si[:3] = w.N - 1 - np.arange(3)                       # text rows
+    g = structured_qkv(w)
+    q, k, v = (to_dev(g[x], w.dtype) for x in "qkv")
+    labels, mse = svg.svg_profile_heads(q, k, v, ints(si), w.F, w.S, w.T, w.ks, w.wt)
+    sync()
+    ol, om = profile.profile_heads(*(as_f64(g[x], w.dtype) for x in "qkv"), w.F, w.S, w.T, si, w.ks, w.wt)
+    np.testing.assert_array_equal(labels.cpu().numpy(), ol)
+    np.testing.assert_allclose(mse.double().cpu().numpy(), om, rtol=2e-2, atol=1e-6)
+    qr, kr, vr = random_qkv(w.H, w.N, d, seed=d + 1, dtype="bf16")
+    _, mse = svg.svg_profile_heads(*(to_dev(x, "bf16") for x in (qr, kr, vr)), ints(si), w.F, w.S, w.T,
+                                   w.ks, w.wt)
+    sync()
+    _, om = profile.profile_heads(*(as_f64(x, "bf16") for x in (qr, kr, vr)), w.F, w.S, w.T, si, w.ks, w.wt)
+    assert om.min() > 1e-3
+    np.testing.assert_allclose(mse.double().cpu().numpy(), om, rtol=2e-2, atol=1e-6)
+
+
 @pytest.mark.parametrize("ks,wt", [(1, 100), (2, 0), (0, 1350 * 13)])
 def test_profile_mask_widths_against_oracle(ks, wt):
     """Masks of other widths (a temporal window that is not a multiple of F,
@@ -340,3 +367,14 @@ def test_profile_mask_widths_against_oracle(ks, wt):
         a, b = om[h]
         if abs(a - b) > 0.05 * max(a, b):
             assert lab[h] == ol[h], (h, lab[h], ol[h], om[h])
+    # Gaussian heads: every key carries weight, so a key masked wrongly on the
+    # GPU moves both MSEs.  (A window that covers every key leaves nothing
+    # to compare: its MSE is 0 on both sides, checked above.)
+    if wt < w.F * w.S // 2:
+        qr, kr, vr = random_qkv(2, w.N, w.d, seed=ks + wt, dtype="bf16")
+        _, mse = svg.svg_profile_heads(*(to_dev(x, "bf16") for x in (qr, kr, vr)), ints(si), w.F, w.S, w.T,
+                                       ks, wt)
+        sync()
+        _, om = profile.profile_heads(*(as_f64(x, "bf16") for x in (qr, kr, vr)), w.F, w.S, w.T, si, ks, wt)
+        assert om.min() > 1e-4
+        np.testing.assert_allclose(mse.double().cpu().numpy(), om, rtol=2e-2, atol=1e-6)
