@@ -39,8 +39,11 @@ void attn_fwd_mfma(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K,
   // LDS stages: K0 K1 V0 V1 (64 rows each)
   __shared__ __attribute__((aligned(1024))) char smem[4 * TB];
 
+  // A head's last q-blocks hold the text query rows, which keep every
+  // kv-block: they go first within their head (each XCD runs a contiguous
+  // slice of the work list in order), so that no XCD ends on one of them.
   const int work = xcd_remap(blockIdx.x, gridDim.x);
-  const int h = work / nqb, qb = work - h * nqb;
+  const int h = work / nqb, qb = nqb - 1 - (work - h * nqb);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
