@@ -141,22 +141,30 @@ __device__ __forceinline__ void qk_tile(const char *__restrict__ Ks, const bf16x
 __device__ __forceinline__ int acc_key(int b, int r, int hi) { return 32 * b + 8 * (r >> 2) + 4 * hi + (r & 3); }
 
 // Keys at tile positions >= nvalid do not exist: set their scores to -inf.
+// acc_key(b, r, hi) = acc_key(b, r, 0) + 4 hi: the constants are compared
+// against nvalid - 4 hi, so no per-key offsets stay live across a loop.
 __device__ __forceinline__ void mask_tail(f32x16 &s0, f32x16 &s1, int nvalid, int hi) {
+  const int nvh = nvalid - 4 * hi;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    if (acc_key(0, r, hi) >= nvalid) s0[r] = -INFINITY;
-    if (acc_key(1, r, hi) >= nvalid) s1[r] = -INFINITY;
+    if (acc_key(0, r, 0) >= nvh) s0[r] = -INFINITY;
+    if (acc_key(1, r, 0) >= nvh) s1[r] = -INFINITY;
   }
 }
 
 constexpr float kLazyLog2 = 8.f;
 
+// IEEE-754 maximum (v_maximum3_f32 on gfx950).  Unlike fmaxf it needs no
+// quieting of its operands in IEEE mode; scores and running maxima are
+// finite or -inf, never NaN, so the two agree here.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // Row maximum of the lane's query over the tile (both lane halves).
 __device__ __forceinline__ float row_max(const f32x16 &s0, const f32x16 &s1) {
   float mx = -INFINITY;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-  return fmaxf(mx, __shfl_xor(mx, 32));
+  for (int r = 0; r < 16; ++r) mx = vmax(mx, vmax(s0[r], s1[r]));
+  return vmax(mx, __shfl_xor(mx, 32));
 }
 
 // Moves the reference maximum if the tile raised the row maximum by more
@@ -357,18 +365,18 @@ __device__ __forceinline__ void dma_full_buf(const void *head, int head_bytes, i
                                              tile_byte_off, 0, 0);
 }
 
-// Row maximum with three-input maxima (v_max3_f32).
+// Row maximum with three-input maxima (v_maximum3_f32).
 __device__ __forceinline__ float row_max3(const f32x16 &s0, const f32x16 &s1) {
-  float a = fmaxf(fmaxf(s0[0], s0[1]), s0[2]);
-  float b = fmaxf(fmaxf(s1[0], s1[1]), s1[2]);
+  float a = vmax(vmax(s0[0], s0[1]), s0[2]);
+  float b = vmax(vmax(s1[0], s1[1]), s1[2]);
 #pragma unroll
   for (int r = 3; r < 15; r += 2) {
-    a = fmaxf(fmaxf(a, s0[r]), s0[r + 1]);
-    b = fmaxf(fmaxf(b, s1[r]), s1[r + 1]);
+    a = vmax(vmax(a, s0[r]), s0[r + 1]);
+    b = vmax(vmax(b, s1[r]), s1[r + 1]);
   }
-  a = fmaxf(fmaxf(a, s0[15]), b);
-  a = fmaxf(a, s1[15]);
-  return fmaxf(a, __shfl_xor(a, 32));
+  a = vmax(vmax(a, s0[15]), b);
+  a = vmax(a, s1[15]);
+  return vmax(a, __shfl_xor(a, 32));
 }
 
 // Per-lane byte offsets of the K operand reads (one per 16-dim step; the

@@ -106,11 +106,13 @@ void attn_fwd_vt(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K, con
     bool own = true;
     if constexpr (!DENSE) own = (e & own_bit) != 0;
     if (own && ((e & 0xFFFFFF) + 1) * BK > N) {  // keys past N: only in the last kv-block
-      const int nvalid = N - (e & 0xFFFFFF) * BK;
+      // key offset acc_key_pi(b, r, hi) = acc_key_pi(b, r, 0) + 8 hi: compare
+      // the constants against nvalid - 8 hi (no per-key offsets kept live)
+      const int nvh = N - (e & 0xFFFFFF) * BK - 8 * hi;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        if (acc_key_pi(0, r, hi) >= nvalid) s0[r] = -INFINITY;
-        if (acc_key_pi(1, r, hi) >= nvalid) s1[r] = -INFINITY;
+        if (acc_key_pi(0, r, 0) >= nvh) s0[r] = -INFINITY;
+        if (acc_key_pi(1, r, 0) >= nvh) s1[r] = -INFINITY;
       }
     }
     return own;

@@ -30,21 +30,21 @@ __device__ __forceinline__ int acc_key_pi(int b, int r, int hi) {
 __device__ __forceinline__ float lane_max_tree(const f32x16 &s0, const f32x16 &s1) {
   float a[11];
 #pragma unroll
-  for (int k = 0; k < 5; ++k) a[k] = fmaxf(fmaxf(s0[3 * k], s0[3 * k + 1]), s0[3 * k + 2]);
-  a[5] = fmaxf(fmaxf(s0[15], s1[0]), s1[1]);
+  for (int k = 0; k < 5; ++k) a[k] = vmax(vmax(s0[3 * k], s0[3 * k + 1]), s0[3 * k + 2]);
+  a[5] = vmax(vmax(s0[15], s1[0]), s1[1]);
 #pragma unroll
-  for (int k = 0; k < 4; ++k) a[6 + k] = fmaxf(fmaxf(s1[2 + 3 * k], s1[3 + 3 * k]), s1[4 + 3 * k]);
-  a[10] = fmaxf(s1[14], s1[15]);
-  const float b0 = fmaxf(fmaxf(a[0], a[1]), a[2]), b1 = fmaxf(fmaxf(a[3], a[4]), a[5]);
-  const float b2 = fmaxf(fmaxf(a[6], a[7]), a[8]), b3 = fmaxf(a[9], a[10]);
-  return fmaxf(fmaxf(b0, b1), fmaxf(b2, b3));
+  for (int k = 0; k < 4; ++k) a[6 + k] = vmax(vmax(s1[2 + 3 * k], s1[3 + 3 * k]), s1[4 + 3 * k]);
+  a[10] = vmax(s1[14], s1[15]);
+  const float b0 = vmax(vmax(a[0], a[1]), a[2]), b1 = vmax(vmax(a[3], a[4]), a[5]);
+  const float b2 = vmax(vmax(a[6], a[7]), a[8]), b3 = vmax(a[9], a[10]);
+  return vmax(vmax(b0, b1), vmax(b2, b3));
 }
 
 // Maximum with the partner lane l ^ 32 (the other half of the same query's
 // keys), through v_permlane32_swap instead of an LDS permute.
 __device__ __forceinline__ float half_swap_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 // pi(i): row i of a 32-key block of S^T holds key pi(i) (an involution).

@@ -292,12 +292,14 @@ void profile_pass_mfma(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ 
       qk_tile<D, PNT>(Ks, qf, l32, hi, s0, s1);
       if (kbase + BK > N) mask_tail(s0, s1, N - kbase, hi);
       if (ranges) {
+        // offset acc_key(b, r, hi) = acc_key(b, r, 0) + 4 hi
+        const int a0h = a0 - 4 * hi, a1h = a1 - 4 * hi;
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int off = acc_key(b, r, hi);
-            const bool keep = (unsigned)(off - a0) < (unsigned)n0 || (unsigned)(off - a1) < (unsigned)n1;
+            const int off = acc_key(b, r, 0);
+            const bool keep = (unsigned)(off - a0h) < (unsigned)n0 || (unsigned)(off - a1h) < (unsigned)n1;
             if (!keep) {
               if (b == 0) s0[r] = -INFINITY; else s1[r] = -INFINITY;
             }
