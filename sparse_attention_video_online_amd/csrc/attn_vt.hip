@@ -52,8 +52,12 @@ void attn_fwd_vt(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K, con
   constexpr int OWN_ALL = (1 << G) - 1;
   // Three LDS stages each for K and V^T.  Separate arrays: the compiler
   // then sees that a DMA into one stage cannot alias reads of another and
-  // adds no waits of its own beyond the true dependencies.
-  __shared__ __attribute__((aligned(1024))) char k0[TB], k1[TB], k2[TB], v0[TB], v1[TB], v2[TB];
+  // adds no waits of its own beyond the true dependencies.  Equal arrays are
+  // laid out in the order of their mangled names, so the V^T stages (V0..V2)
+  // come first, below 64 KB: each V^T read is then a lane register plus an
+  // immediate offset, with no address VALU (the K reads above 64 KB need one
+  // add per 16-dim step, shared by the tile's two key blocks).
+  __shared__ __attribute__((aligned(1024))) char k0[TB], k1[TB], k2[TB], V0[TB], V1[TB], V2[TB];
   __shared__ int ulist[DENSE ? 1 : kMaxKb];
   __shared__ uint32_t bits[DENSE ? 1 : G * kWords];
   __shared__ int wsum[DENSE ? 1 : kWords + 1];
@@ -117,7 +121,7 @@ void attn_fwd_vt(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K, con
     }
     return own;
   };
-  vt_attend<D, kNW>(nt, ent_raw, prep, Kh, Vth, N, k0, k1, k2, v0, v1, v2, qf, wave, lane, c, o, m_run, l_run);
+  vt_attend<D, kNW>(nt, ent_raw, prep, Kh, Vth, N, k0, k1, k2, V0, V1, V2, qf, wave, lane, c, o, m_run, l_run);
   __builtin_amdgcn_s_waitcnt(0);  // no DMA may land after the work-group ends
   store_o<D>(qrow < N ? Oh + (size_t)qrow * D : nullptr, o, l_run, hi);
 }
