@@ -249,6 +249,7 @@ __device__ __forceinline__ void vt_attend(int nt, EntRaw ent_raw, Prep prep, con
   for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
   m_run = -INFINITY;
   l_run = 0.f;
+  float mref_c = 0.f;   // m_run * c (0 while m_run is -inf)
 
   // Tile DMAs through a buffer resource based at the tile: rows past N fall
   // outside the resource's range and read as zero (their scores are masked).
@@ -332,13 +333,24 @@ __device__ __forceinline__ void vt_attend(int nt, EntRaw ent_raw, Prep prep, con
     }
     mx = half_swap_max(mx);
     if (!own) mx = -INFINITY;
-    const float alpha = update_ref(mx, c, m_run, l_run);
-    const float cc = own ? c : 0.f;
-    const float mc = !own ? INFINITY : (m_run == -INFINITY) ? 0.f : m_run * c;
+    // Lazy reference: it moves only when the tile raises the row maximum by
+    // more than 2^8 (exp2 units; from -inf it always moves).  A move, rare
+    // after the first tiles, rescales l and O in a wave-uniform branch, so
+    // the common step computes no rescale factor at all.
+    const bool move = mx > m_run && (mx - m_run) * c > kLazyLog2;
     bf16x8 ka0, ka1;
     kread(LEAD, ka0, ka1);
     __builtin_amdgcn_sched_barrier(0);
-    rescale<D>(o, alpha);
+    if (__builtin_amdgcn_ballot_w64(move)) {
+      const float alpha = move ? fast_exp2((m_run - mx) * c) : 1.f;
+      m_run = move ? mx : m_run;
+      mref_c = m_run == -INFINITY ? 0.f : m_run * c;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+    }
+    const float cc = own ? c : 0.f;
+    const float mc = own ? mref_c : INFINITY;
 
     // (B) NKS hand-ordered steps (sched_barrier fences): step ks issues the
     // two MFMAs of S(it+1) for QK step ks + LEAD (K operands read one step
