@@ -39,11 +39,14 @@ void attn_fwd_mfma(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K,
   // LDS stages: K0 K1 V0 V1 (64 rows each)
   __shared__ __attribute__((aligned(1024))) char smem[4 * TB];
 
-  // A head's last q-blocks hold the text query rows, which keep every
-  // kv-block: they go first within their head (each XCD runs a contiguous
-  // slice of the work list in order), so that no XCD ends on one of them.
+  // A head's last 512 query rows hold its text rows, which keep every
+  // kv-block: their q-blocks go first within the head (each XCD runs a
+  // contiguous slice of the work list in order), so that no XCD ends on one
+  // of them; the rest follow in ascending order for L2 reuse.
   const int work = xcd_remap(blockIdx.x, gridDim.x);
-  const int h = work / nqb, qb = nqb - 1 - (work - h * nqb);
+  const int h = work / nqb, local = work - h * nqb;
+  const int nlead = min(nqb, 512 / BQ);
+  const int qb = local < nlead ? nqb - 1 - local : local - nlead;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
