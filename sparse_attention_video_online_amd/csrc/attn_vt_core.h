@@ -75,6 +75,12 @@ __device__ __forceinline__ void vt_offsets(int l32, int hi, int (&off)[4]) {
   for (int j = 0; j < 4; ++j) off[j] = l32 * 128 + (((2 * j + hi) ^ swz_vt(l32)) << 4);
 }
 
+// Sub-step schedule of the P.V MFMAs: delay after the chunk's last
+// exponential, and lead of the V^T operand reads before the MFMAs.
+constexpr int kPvDelay = 1;
+constexpr int kVLead = 2;
+static_assert(kVLead >= 1, "a chunk's V^T operands are read in an earlier sub-step than its P.V");
+
 // DMA of one tile whose first byte is `src`; units at or past `bytes` read
 // as zero (buffer range check on the per-lane offset).
 template <int D, int NW>
@@ -358,6 +364,13 @@ __device__ __forceinline__ void vt_attend(int nt, EntRaw ent_raw, Prep prep, con
     // chunk of P(it) is complete, its O^T += V^T P^T MFMAs.
     uint32_t pw[16];
     float rs = 0.f;
+    // 16-key chunk j of P is complete after sub-step done(j); its P.V MFMAs
+    // go kPvDelay sub-steps later (the exponentials and packs have landed)
+    // and its V^T operands are read kVLead sub-steps before that.
+    constexpr int CPS = 8 / PER;            // sub-steps per chunk
+    auto pv_at = [&](int j) { return (j + 1) * CPS - 1 + kPvDelay; };
+    auto rd_at = [&](int j) { const int r = pv_at(j) - kVLead; return r < 0 ? 0 : r; };
+    bf16x8 va[2][D / 32];
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
@@ -381,19 +394,29 @@ __device__ __forceinline__ void vt_attend(int nt, EntRaw ent_raw, Prep prep, con
         rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[idx >> 1]), kOnesBf16x2, rs, false);
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {  // chunks of P completed by this step
-        if (8 * (j + 1) > (ks + 1) * PER || 8 * (j + 1) <= ks * PER) continue;
+      for (int j = 0; j < 4; ++j) {  // P.V of the chunks due in this sub-step
+        if (pv_at(j) != ks) continue;
         const bf16x8 pj = __builtin_bit_cast(bf16x8, u32x4{pw[4 * j], pw[4 * j + 1], pw[4 * j + 2], pw[4 * j + 3]});
-        bf16x8 va[D / 32];
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) o[db] = mfma32(va[j & 1][db], pj, o[db]);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {  // V^T operands read ahead of their P.V
+        if (rd_at(j) != ks) continue;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
-          va[db] = *reinterpret_cast<const bf16x8 *>(Vc + voff[j] + db * 32 * 128);
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) o[db] = mfma32(va[db], pj, o[db]);
+          va[j & 1][db] = *reinterpret_cast<const bf16x8 *>(Vc + voff[j] + db * 32 * 128);
       }
       ka0 = kn0;
       ka1 = kn1;
       __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {  // P.V due after the last sub-step
+      if (pv_at(j) < NKS) continue;
+      const bf16x8 pj = __builtin_bit_cast(bf16x8, u32x4{pw[4 * j], pw[4 * j + 1], pw[4 * j + 2], pw[4 * j + 3]});
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) o[db] = mfma32(va[j & 1][db], pj, o[db]);
     }
     l_run += rs;
 
