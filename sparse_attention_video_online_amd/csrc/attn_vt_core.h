@@ -1,5 +1,5 @@
-// Shared pieces of the attention kernels that read V in the key-tiled
-// transposed layout (attn_vt.hip, attn_vt64.hip): LDS swizzles and DMA
+// Shared pieces of the kernels that read V in the key-tiled transposed
+// layout (attn_vt.hip, and the profiler's full pass): LDS swizzles and DMA
 // offsets of the K and V^T tiles, the K row order pi, softmax helpers, and the
 // per-work-group union of the kept-tile lists.
 #pragma once
@@ -208,7 +208,8 @@ __device__ __forceinline__ int build_union_list(const int32_t *__restrict__ row_
 // tile full) through three LDS stages each (k0..k2, v0..v2, TB bytes, all
 // waves of the work-group call this together: it contains barriers).  On
 // return o, m_run and l_run hold the un-normalised output, the reference
-// maximum and this lane's partial row sum.
+// maximum and this lane's partial row sum: of the bf16 probabilities that
+// enter the P.V MFMAs (SUM_BF16), or of the fp32 ones.
 //
 // Per tile it, one wave:
 //   (A) the first QK MFMAs of S(it+1), then the statistics of S(it) (masks,
@@ -220,7 +221,7 @@ __device__ __forceinline__ int build_union_list(const int32_t *__restrict__ row_
 //   (C) wait until only this step's DMAs are in flight, one barrier.
 // S^T's rows (keys) are read from K in the order pi, so the accumulator
 // layout of S^T is the B-operand layout of P^T with keys in natural order.
-template <int D, int NW, typename EntRaw, typename Prep>
+template <int D, int NW, bool SUM_BF16 = true, typename EntRaw, typename Prep>
 __device__ __forceinline__ void vt_attend(int nt, EntRaw ent_raw, Prep prep, const bf16_t *__restrict__ Kh,
                                           const bf16_t *__restrict__ Vth, int N, char *k0, char *k1, char *k2,
                                           char *v0, char *v1, char *v2, const bf16x8 (&qf)[D / 16], int wave,
@@ -390,8 +391,10 @@ __device__ __forceinline__ void vt_attend(int nt, EntRaw ent_raw, Prep prep, con
         const float p0 = fast_exp2(__builtin_fmaf(x0, cc, -mc));
         const float p1 = fast_exp2(__builtin_fmaf(x1, cc, -mc));
         pw[idx >> 1] = pack_bf16x2(p0, p1);
-        // row sum of the probabilities as they enter the MFMA (bf16)
-        rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[idx >> 1]), kOnesBf16x2, rs, false);
+        if constexpr (SUM_BF16)  // row sum of the probabilities as they enter the MFMA (bf16)
+          rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[idx >> 1]), kOnesBf16x2, rs, false);
+        else  // row sum of the fp32 probabilities
+          rs += p0 + p1;
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {  // P.V of the chunks due in this sub-step

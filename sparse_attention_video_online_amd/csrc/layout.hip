@@ -65,12 +65,12 @@ void permute_rows_kernel(const u32x4 *__restrict__ X, const int32_t *__restrict_
 template <int D>
 __global__ __launch_bounds__(256)
 void vt_kernel(const u32x4 *__restrict__ X, u32x4 *__restrict__ Y, const int32_t *__restrict__ labels,
-               int F, int S, int N, int nkb) {
+               int F, int S, int N, int nkb, int identity) {
   constexpr int STR = D + 8;                 // padded row stride (halfwords)
   constexpr int CPR = D / 8;                 // 16-byte units per row
   __shared__ __attribute__((aligned(16))) uint16_t t[64 * STR];
   const int kb = blockIdx.x, h = blockIdx.y;
-  const bool perm = labels == nullptr || labels[h] == 1;
+  const bool perm = !identity && (labels == nullptr || labels[h] == 1);
   const u32x4 *Xh = X + (size_t)h * N * CPR;
   for (int u = threadIdx.x; u < 64 * CPR; u += 256) {
     const int row = u / CPR, ch = u - row * CPR;
@@ -100,15 +100,16 @@ void vt_kernel(const u32x4 *__restrict__ X, u32x4 *__restrict__ Y, const int32_t
 
 }  // namespace
 
-hipError_t launch_layout_vt(const Dims &dm, const void *V, void *Vt, const int32_t *labels, hipStream_t st) {
+hipError_t launch_layout_vt(const Dims &dm, const void *V, void *Vt, const int32_t *labels, hipStream_t st,
+                            bool identity) {
   const int nkb = (dm.N + 63) / 64;
   if (dm.N == 0 || dm.H == 0) return hipSuccess;
   if (dm.d == 128)
     hipLaunchKernelGGL(vt_kernel<128>, dim3(nkb, dm.H), dim3(256), 0, st, (const u32x4 *)V, (u32x4 *)Vt, labels,
-                       dm.F, dm.S, dm.N, nkb);
+                       dm.F, dm.S, dm.N, nkb, identity ? 1 : 0);
   else
     hipLaunchKernelGGL(vt_kernel<64>, dim3(nkb, dm.H), dim3(256), 0, st, (const u32x4 *)V, (u32x4 *)Vt, labels,
-                       dm.F, dm.S, dm.N, nkb);
+                       dm.F, dm.S, dm.N, nkb, identity ? 1 : 0);
   return hipGetLastError();
 }
 

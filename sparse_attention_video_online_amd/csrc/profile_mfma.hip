@@ -5,19 +5,20 @@
 // over its own kept keys with its own maximum.  Then per-head MSEs of the
 // masked outputs against the full one, and the label (ties -> spatial).
 //
-// Layout: a work-group gathers 128 sampled rows (4 waves x 32).  It walks one
-// chunk of the N keys in 64-key tiles, with the S^T = K Q^T / O^T += V^T P^T
-// machinery of attn_core.h.  Each lane owns one sampled row.  Three passes
-// (full, spatial, temporal) each keep one online-softmax state, so a wave
-// holds one output accumulator and stays at two waves per SIMD.  The masked
-// passes visit only the key tiles that some sample's window (or a text key)
-// reaches.  In a flagged tile each row keeps at most two key ranges, one
+// Three passes (full, spatial, temporal) each keep one online-softmax state
+// per sampled row and walk one chunk of the N keys per work-group in 64-key
+// tiles; each lane owns one sampled row.  The full pass runs the attention
+// kernel's V^T tile pipeline (vt_attend: 8 waves x 32 samples, K and the
+// key-tiled V^T of V DMA'd into LDS).  The masked passes use the S^T = K Q^T
+// / O^T += V^T P^T machinery of attn_core.h on 128 sampled rows (4 waves x
+// 32), grouped by frame or by grid position, and visit only the key tiles
+// that some sample's window (or a text key) reaches.  In a flagged tile each row keeps at most two key ranges, one
 // per frame the tile touches: a wave whose rows keep none of the tile skips
 // its math, a wave whose rows keep all of it needs no mask, and the others
 // test each score's key offset against the two ranges.  Chunks are merged
 // afterwards (flash-decoding style), and the squared errors are summed in
 // fp64 in a fixed order.
-#include "attn_core.h"
+#include "attn_vt_core.h"
 
 namespace svgk {
 namespace {
@@ -29,6 +30,35 @@ constexpr int PNT = PNW * 64;
 constexpr int PQ = PNW * 32;
 
 struct ProfileGrid { int nqg, nchunks, tiles_per_chunk; };
+
+// The full pass: 8 waves = 256 samples per work-group on the V^T tile
+// pipeline (vt_attend), one work-group per CU.
+constexpr int FNW = 8;
+constexpr int FNT = FNW * 64;
+constexpr int FQ = FNW * 32;
+constexpr int kFullSlots = 256;   // full-pass work-groups resident at once (one per CU, 256 CUs)
+
+// Key chunks of the full pass.  Every work-group has the same work, so the
+// pass takes about (rounds of resident work-groups) x (tiles per chunk + a
+// fixed cost of ~8 tiles per work-group); take the fewest.  At the
+// HunyuanVideo layer shape: 2 chunks, 240 work-groups in one round.
+ProfileGrid profile_grid_full(const Dims &dm, int n_s) {
+  const int nkb = (dm.N + BK - 1) / BK;
+  const int nqg = (n_s + FQ - 1) / FQ;
+  long long best = -1;
+  int best_tpc = nkb;
+  for (int c = 1; c <= min(nkb, 64); ++c) {
+    const int tpc = (nkb + c - 1) / c;
+    const long long nch = (nkb + tpc - 1) / tpc;
+    const long long rounds = ((long long)dm.H * nqg * nch + kFullSlots - 1) / kFullSlots;
+    const long long cost = rounds * (tpc + 8);
+    if (best < 0 || cost < best) {
+      best = cost;
+      best_tpc = tpc;
+    }
+  }
+  return ProfileGrid{nqg, (nkb + best_tpc - 1) / best_tpc, best_tpc};
+}
 
 // Key chunks per (head, sample group): about 2048 work-groups, four rounds
 // of the 512 resident ones.  Fewer chunks leave a masked pass's work in the
@@ -49,16 +79,19 @@ ProfileGrid profile_grid(const Dims &dm, int n_s) {
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 struct Parts {
-  float *o;    // [H][n_s][C][3][D]
+  float *o;    // [H][n_s][C][3][D], C = the larger of the passes' chunk counts
   float *ml;   // [H][n_s][C][3][2]
   double *se;  // [H][n_s][2]
   int32_t *ord_s, *ord_t;  // [n_s] each
+  bf16_t *vt;  // V in its own token order, key-tiled transposed: [H][nKB][D][64]
 };
 
-Parts carve(void *ws, const Dims &dm, int n_s, const ProfileGrid &g) {
+size_t vt_bytes(const Dims &dm) { return (size_t)dm.H * ((dm.N + BK - 1) / BK) * BK * dm.d * sizeof(bf16_t); }
+
+Parts carve(void *ws, const Dims &dm, int n_s, int C) {
   char *p = (char *)ws;
-  const size_t no = (size_t)dm.H * n_s * g.nchunks * 3 * dm.d * sizeof(float);
-  const size_t nml = (size_t)dm.H * n_s * g.nchunks * 3 * 2 * sizeof(float);
+  const size_t no = (size_t)dm.H * n_s * C * 3 * dm.d * sizeof(float);
+  const size_t nml = (size_t)dm.H * n_s * C * 3 * 2 * sizeof(float);
   Parts r;
   r.o = (float *)p;
   r.ml = (float *)(p + align256(no));
@@ -66,6 +99,7 @@ Parts carve(void *ws, const Dims &dm, int n_s, const ProfileGrid &g) {
   r.se = (double *)(p + align256(no) + align256(nml));
   r.ord_s = (int32_t *)(p + align256(no) + align256(nml) + align256(nse));
   r.ord_t = r.ord_s + align256((size_t)n_s * 4) / 4;
+  r.vt = (bf16_t *)((char *)r.ord_t + align256((size_t)n_s * 4));
   return r;
 }
 
@@ -123,7 +157,7 @@ template <int D, int KIND>
 __global__ __launch_bounds__(PNT, 2)
 void profile_pass_mfma(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K, const bf16_t *__restrict__ V,
                        const int32_t *__restrict__ sample_idx, const int32_t *__restrict__ order, int n_s, int F,
-                       int S, int N, int ks, int wt, int nkb, int tpc, int nchunks, float c,
+                       int S, int N, int ks, int wt, int nkb, int tpc, int cstride, float c,
                        float *__restrict__ part_o, float *__restrict__ part_ml) {
   using C = Tile<D, PNT>;
   __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE];
@@ -346,7 +380,70 @@ void profile_pass_mfma(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ 
   // partial result of this chunk: unnormalised O, running max, sum
   const float lt = l_run + __shfl_xor(l_run, 32);
   if (!valid) return;
-  const size_t slot = (((size_t)h * n_s + sidx) * nchunks + chunk) * 3 + KIND;
+  const size_t slot = (((size_t)h * n_s + sidx) * cstride + chunk) * 3 + KIND;
+  float *dst = part_o + slot * D;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      *reinterpret_cast<f32x4 *>(dst + 32 * db + 8 * g + 4 * hi) =
+          f32x4{o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]};
+  if (hi == 0) {
+    part_ml[slot * 2] = m_run;
+    part_ml[slot * 2 + 1] = lt;
+  }
+}
+
+// The full pass (no mask) for the work-group's 256 samples, in their given
+// order, over one chunk of key tiles, on the V^T tile pipeline: K and the
+// key-tiled V^T of V in its own token order DMA'd into three LDS stages,
+// MFMA QK and PV, lazy-rescale online softmax.  The partial result of the
+// chunk (O unnormalised, reference maximum, row sum) goes to slot (h,
+// sample, chunk, 0) of part_o / part_ml, strided by C chunks.
+template <int D>
+__global__ __launch_bounds__(FNT, 1)
+void profile_full_vt(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K, const bf16_t *__restrict__ Vt,
+                     const int32_t *__restrict__ sample_idx, int n_s, int N, int nkb, int tpc, int C, float c,
+                     float *__restrict__ part_o, float *__restrict__ part_ml) {
+  using T = DTile<D>;
+  constexpr int TB = T::TBYTES;
+  // V^T stages named to sort first, below 64 KB of LDS (immediate offsets)
+  __shared__ __attribute__((aligned(1024))) char k0[TB], k1[TB], k2[TB], V0[TB], V1[TB], V2[TB];
+  const int h = blockIdx.z, chunk = blockIdx.y, qg = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hi = lane >> 5;
+  const size_t hoff = (size_t)h * N * D;
+  const int pos = qg * FQ + wave * 32 + (lane & 31);
+  const bool valid = pos < n_s;
+  const int i = valid ? sample_idx[pos] : 0;
+  const int t0 = chunk * tpc;
+  const int nt = min(nkb, t0 + tpc) - t0;   // >= 1 by the chunking
+  auto ent_raw = [&](int j) -> int { return t0 + (j < nt ? j : nt - 1); };
+  auto prep = [&](f32x16 &s0, f32x16 &s1, int e) -> bool {
+    if ((e + 1) * BK > N) {  // keys past N: only in the last kv-block
+      const int nvh = N - e * BK - 8 * hi;   // acc_key_pi(b, r, hi) = acc_key_pi(b, r, 0) + 8 hi
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if (acc_key_pi(0, r, 0) >= nvh) s0[r] = -INFINITY;
+        if (acc_key_pi(1, r, 0) >= nvh) s1[r] = -INFINITY;
+      }
+    }
+    return true;
+  };
+  bf16x8 qf[D / 16];
+  load_q<D>(Q + hoff, valid ? i : -1, hi, qf);
+  f32x16 o[D / 32];
+  float m_run, l_run;
+  // Row sums of the fp32 probabilities, as the masked passes take them: the
+  // three outputs then share one rounding convention, and the small MSEs of
+  // heads whose masks both keep nearly all the weight stay comparable.
+  vt_attend<D, FNW, false>(nt, ent_raw, prep, K + hoff, Vt + (size_t)h * nkb * (BK * D), N, k0, k1, k2, V0, V1,
+                           V2, qf, wave, lane, c, o, m_run, l_run);
+  __builtin_amdgcn_s_waitcnt(0);  // no DMA may land after the work-group ends
+  const float lt = l_run + __shfl_xor(l_run, 32);
+  if (!valid) return;
+  const size_t slot = (((size_t)h * n_s + pos) * C + chunk) * 3;
   float *dst = part_o + slot * D;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
@@ -361,20 +458,28 @@ void profile_pass_mfma(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ 
 }
 
 // Merge the chunks of one sampled row; squared errors of the masked outputs.
+// Pass m has nch_m chunks; the slots are strided by C (the largest).  A
+// mask that keeps every key of every row (cover bit m) has the full output
+// as its output, exactly: that pass was not run.
 __global__ __launch_bounds__(128)
-void profile_combine(const float *__restrict__ part_o, const float *__restrict__ part_ml, int n_s, int nchunks,
-                     int D, float c, double *__restrict__ se) {
+void profile_combine(const float *__restrict__ part_o, const float *__restrict__ part_ml, int n_s, int C,
+                     int nch0, int nch12, int cover, int D, float c, double *__restrict__ se) {
   __shared__ double red[2][128];
   const int h = blockIdx.y, s = blockIdx.x, e = threadIdx.x;
   double out[3] = {0.0, 0.0, 0.0};
   for (int m = 0; m < 3; ++m) {
+    if (m > 0 && (cover >> m & 1)) {
+      out[m] = out[0];
+      continue;
+    }
+    const int nchunks = m == 0 ? nch0 : nch12;
     float M = -INFINITY;
     for (int ch = 0; ch < nchunks; ++ch)
-      M = fmaxf(M, part_ml[((((size_t)h * n_s + s) * nchunks + ch) * 3 + m) * 2]);
+      M = fmaxf(M, part_ml[((((size_t)h * n_s + s) * C + ch) * 3 + m) * 2]);
     const float Mr = M == -INFINITY ? 0.f : M;
     double L = 0.0, acc = 0.0;
     for (int ch = 0; ch < nchunks; ++ch) {
-      const size_t slot = (((size_t)h * n_s + s) * nchunks + ch) * 3 + m;
+      const size_t slot = (((size_t)h * n_s + s) * C + ch) * 3 + m;
       const float w = fast_exp2((part_ml[slot * 2] - Mr) * c);
       L += (double)w * part_ml[slot * 2 + 1];
       if (e < D) acc += (double)w * part_o[slot * D + e];
@@ -432,37 +537,52 @@ void profile_label(const double *__restrict__ se, int n_s, int D, int32_t *__res
 }  // namespace
 
 size_t profile_mfma_ws_bytes(const Dims &dm, int n_s) {
-  const ProfileGrid g = profile_grid(dm, n_s);
-  return align256((size_t)dm.H * n_s * g.nchunks * 3 * dm.d * sizeof(float)) +
-         align256((size_t)dm.H * n_s * g.nchunks * 3 * 2 * sizeof(float)) +
-         align256((size_t)dm.H * n_s * 2 * sizeof(double)) + 2 * align256((size_t)n_s * 4);
+  const int C = max(profile_grid(dm, n_s).nchunks, profile_grid_full(dm, n_s).nchunks);
+  return align256((size_t)dm.H * n_s * C * 3 * dm.d * sizeof(float)) +
+         align256((size_t)dm.H * n_s * C * 3 * 2 * sizeof(float)) +
+         align256((size_t)dm.H * n_s * 2 * sizeof(double)) + 2 * align256((size_t)n_s * 4) + align256(vt_bytes(dm));
 }
 
 hipError_t launch_profile_mfma(const Dims &dm, const void *Q, const void *K, const void *V,
                                const int32_t *sample_idx, int n_s, int ks, int wt, float scale, int32_t *labels,
                                float *mse, void *ws, hipStream_t st) {
   const float c = scale * kLog2e;
-  const ProfileGrid g = profile_grid(dm, n_s);
-  const Parts p = carve(ws, dm, n_s, g);
+  const ProfileGrid g = profile_grid(dm, n_s);        // masked passes
+  const ProfileGrid gf = profile_grid_full(dm, n_s);  // full pass
+  const int C = max(g.nchunks, gf.nchunks);
+  const Parts p = carve(ws, dm, n_s, C);
   const int nkb = (dm.N + BK - 1) / BK;
-  const dim3 grid(g.nqg, g.nchunks, dm.H);
+  const dim3 grid(g.nqg, g.nchunks, dm.H), gridf(gf.nqg, gf.nchunks, dm.H);
   hipLaunchKernelGGL(profile_order, dim3((n_s + 255) / 256), dim3(256), 0, st, sample_idx, n_s, dm.F, dm.S,
                      p.ord_s, p.ord_t);
+  // key-tiled V^T of V in its own token order, for the full pass
+  const hipError_t ev = launch_layout_vt(dm, V, p.vt, nullptr, st, true);
+  if (ev != hipSuccess) return ev;
 #define SVG_PROFILE_PASS(DD, KK)                                                                            \
   hipLaunchKernelGGL((profile_pass_mfma<DD, KK>), grid, dim3(PNT), 0, st, (const bf16_t *)Q, (const bf16_t *)K, \
                      (const bf16_t *)V, sample_idx, (KK) == 2 ? p.ord_t : p.ord_s, n_s, dm.F, dm.S, dm.N, ks, wt, \
-                     nkb, g.tiles_per_chunk, g.nchunks, c, p.o, p.ml)
+                     nkb, g.tiles_per_chunk, C, c, p.o, p.ml)
+#define SVG_PROFILE_FULL(DD)                                                                                  \
+  hipLaunchKernelGGL((profile_full_vt<DD>), gridf, dim3(FNT), 0, st, (const bf16_t *)Q, (const bf16_t *)K, p.vt, \
+                     sample_idx, n_s, dm.N, nkb, gf.tiles_per_chunk, C, c, p.o, p.ml)
+  // A mask that keeps every key of every row: the spatial one when every
+  // frame lies within ks of every other (ks >= F - 1), the temporal one when
+  // the window of position 0 reaches the last video key and that of position
+  // S - 1 the first (wt >= (S - 1) * F); text rows and keys are kept anyway.
+  const int cover = ((ks >= dm.F - 1) ? 2 : 0) | (((long long)wt >= (long long)(dm.S - 1) * dm.F) ? 4 : 0);
   if (dm.d == 128) {
-    SVG_PROFILE_PASS(128, 0);
-    SVG_PROFILE_PASS(128, 1);
-    SVG_PROFILE_PASS(128, 2);
+    SVG_PROFILE_FULL(128);
+    if (!(cover & 2)) SVG_PROFILE_PASS(128, 1);
+    if (!(cover & 4)) SVG_PROFILE_PASS(128, 2);
   } else {
-    SVG_PROFILE_PASS(64, 0);
-    SVG_PROFILE_PASS(64, 1);
-    SVG_PROFILE_PASS(64, 2);
+    SVG_PROFILE_FULL(64);
+    if (!(cover & 2)) SVG_PROFILE_PASS(64, 1);
+    if (!(cover & 4)) SVG_PROFILE_PASS(64, 2);
   }
 #undef SVG_PROFILE_PASS
-  hipLaunchKernelGGL(profile_combine, dim3(n_s, dm.H), dim3(128), 0, st, p.o, p.ml, n_s, g.nchunks, dm.d, c, p.se);
+#undef SVG_PROFILE_FULL
+  hipLaunchKernelGGL(profile_combine, dim3(n_s, dm.H), dim3(128), 0, st, p.o, p.ml, n_s, C, gf.nchunks, g.nchunks,
+                     cover, dm.d, c, p.se);
   hipLaunchKernelGGL(profile_label, dim3(dm.H), dim3(256), 0, st, p.se, n_s, dm.d, labels, mse);
   return hipGetLastError();
 }

@@ -71,7 +71,9 @@ hipError_t launch_attn_vt(const Dims &dm, const void *Q, const void *K, const vo
                           const int32_t *row_ptr, const int32_t *kv_idx, int bq, int bk, float scale,
                           hipStream_t st);
 int attn_vt_max_kv_blocks();
-hipError_t launch_layout_vt(const Dims &dm, const void *V, void *Vt, const int32_t *labels, hipStream_t st);
+// identity: keep every head's token order (the key-tiled V^T of V as given)
+hipError_t launch_layout_vt(const Dims &dm, const void *V, void *Vt, const int32_t *labels, hipStream_t st,
+                            bool identity = false);
 hipError_t launch_layout(const Dims &dm, int elem_bytes, const void *X, void *Y,
                          const int32_t *labels, bool inverse, hipStream_t st);
 hipError_t launch_permute_rows(const Dims &dm, int elem_bytes, const void *X, const int32_t *perm,
