@@ -349,7 +349,9 @@ def main():
 
     def attend():
         if use_vt:
-            svg.svg_block_sparse_attn_csr_vt(qp, kp, vt, row_ptr, kv_idx, F, S, T, bq, bk, out=op)
+            # Q read and O written in the original token order (the Q permute
+            # and the O unpermute happen in the kernel's row indexing)
+            svg.svg_block_sparse_attn_csr_vt_layout(q, kp, vt, row_ptr, kv_idx, labels, F, S, T, bq, bk, out=o)
         else:
             svg.svg_block_sparse_attn_csr(qp, kp, vp, row_ptr, kv_idx, F, S, T, bq, bk, out=op)
 
@@ -363,7 +365,8 @@ def main():
         svg.svg_build_block_mask(labels, F, S, T, H, d, ks, wt, bq, bk, out=bmask)
         svg.svg_compact_block_mask(bmask, row_ptr=row_ptr, kv_idx=kv_idx, ws=comp_ws)
         mark(2)
-        svg.svg_layout_permute(q, F, S, T, labels, out=qp)
+        if not use_vt:
+            svg.svg_layout_permute(q, F, S, T, labels, out=qp)
         svg.svg_layout_permute(k, F, S, T, labels, out=kp)
         if use_vt:
             svg.svg_layout_permute_vt(v, F, S, T, labels, out=vt)
@@ -376,8 +379,9 @@ def main():
         if i is not None:
             ev_a1[i].record(stream)
         mark(4)
-        svg.svg_layout_unpermute(op, F, S, T, labels, out=o)
-        mark(5)
+        if not use_vt:
+            svg.svg_layout_unpermute(op, F, S, T, labels, out=o)
+            mark(5)
 
     if args.pmc_target:
         # the layer's inputs for the attention kernel, then one launch each of
@@ -416,7 +420,10 @@ def main():
     se = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
     step(None, se)
     torch.cuda.synchronize()
-    names = ["profile", "mask_and_lists", "permute_qkv", "attention", "unpermute_o"]
+    if use_vt:  # Q and O stay in the original order: permute K and V (into Vt) only
+        names = ["profile", "mask_and_lists", "permute_k_vt", "attention"]
+    else:
+        names = ["profile", "mask_and_lists", "permute_qkv", "attention", "unpermute_o"]
     stage_ms = {n: se[j].elapsed_time(se[j + 1]) for j, n in enumerate(names)}
 
     # work done: valid pairs in kept tiles (from the device bitmap)
@@ -467,6 +474,7 @@ def main():
                    "bq": bq, "bk": bk, "ks_frames": ks, "wt_tokens": wt, "n_samples": int(sidx.numel()),
                    "tile_density": round(density, 4), "kept_tiles": tiles,
                    "labels": "".join(str(int(x)) for x in lab_host), "v_layout": args.v_layout,
+                   "qo_layout": "original order, permuted in the attention kernel" if use_vt else "permuted",
                    "parallelism": "single GPU"},
         "attn_ms": round(attn_ms, 4),
         "attn_tflops": round(attn_tflops, 2),

@@ -219,6 +219,16 @@ svg_status svg_dense_attn(const svg_dims *dims, svg_dtype dtype,
  *   output row equals theirs up to fp32 summation order.  bf16 only,
  *   (bq, bk) = (64, 64) or (128, 64), nKB <= 8192, N*d*2 < 2^31; otherwise
  *   SVG_ERR_UNSUPPORTED and nothing is enqueued.
+ * svg_block_sparse_attn_csr_vt_layout: the SVG1 layer's permute -> attention
+ *   -> inverse permute around one launch ([SVG1]: layout transformation,
+ *   custom kernels).  Q and O are in the original token order; K, Vt and the
+ *   kept-tile lists in each head's executing layout (per labels; NULL =
+ *   every head temporal, as svg_layout_permute).  O equals
+ *   svg_layout_unpermute(svg_block_sparse_attn_csr_vt(svg_layout_permute(Q),
+ *   K, Vt, ...), labels) bit for bit: the kernel reads Q row p*F + f of a
+ *   temporal head from frame-major row f*S + p and writes O back there.
+ *   Same limits and errors as svg_block_sparse_attn_csr_vt; labels is a
+ *   device pointer, int32[H], read on the device.
  * ------------------------------------------------------------------------- */
 size_t svg_vt_elems(const svg_dims *dims);
 svg_status svg_layout_permute_vt(const svg_dims *dims, svg_dtype dtype, const void *V, void *Vt,
@@ -228,6 +238,11 @@ svg_status svg_block_sparse_attn_csr_vt(const svg_dims *dims, svg_dtype dtype,
                                         const int32_t *row_ptr, const int32_t *kv_idx,
                                         int32_t bq, int32_t bk, float softmax_scale,
                                         void *O, void *stream);
+svg_status svg_block_sparse_attn_csr_vt_layout(const svg_dims *dims, svg_dtype dtype,
+                                               const void *Q, const void *K, const void *Vt,
+                                               const int32_t *row_ptr, const int32_t *kv_idx,
+                                               const int32_t *labels, int32_t bq, int32_t bk,
+                                               float softmax_scale, void *O, void *stream);
 svg_status svg_dense_attn_vt(const svg_dims *dims, svg_dtype dtype,
                              const void *Q, const void *K, const void *Vt,
                              int32_t bq, int32_t bk, float softmax_scale,

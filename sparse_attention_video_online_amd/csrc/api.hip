@@ -305,6 +305,19 @@ svg_status svg_block_sparse_attn_csr_vt(const svg_dims *dims, svg_dtype dtype, c
                     "svg_block_sparse_attn_csr_vt");
 }
 
+svg_status svg_block_sparse_attn_csr_vt_layout(const svg_dims *dims, svg_dtype dtype, const void *Q,
+                                               const void *K, const void *Vt, const int32_t *row_ptr,
+                                               const int32_t *kv_idx, const int32_t *labels, int32_t bq,
+                                               int32_t bk, float softmax_scale, void *O, void *stream) {
+  Dims dm{};
+  svg_status s;
+  if ((s = vt_checks(dims, dtype, Q, K, Vt, O, bq, bk, &dm)) != SVG_OK) return s;
+  if (!row_ptr || !kv_idx) return fail(SVG_ERR_NULL, "block_sparse_attn_csr_vt_layout: NULL list");
+  return hip_status(svgk::launch_attn_vt(dm, Q, K, Vt, O, row_ptr, kv_idx, bq, bk,
+                                         resolve_scale(softmax_scale, dm.d), (hipStream_t)stream, true, labels),
+                    "svg_block_sparse_attn_csr_vt_layout");
+}
+
 svg_status svg_dense_attn_vt(const svg_dims *dims, svg_dtype dtype, const void *Q, const void *K,
                              const void *Vt, int32_t bq, int32_t bk, float softmax_scale, void *O,
                              void *stream) {

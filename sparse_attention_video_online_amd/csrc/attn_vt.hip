@@ -45,7 +45,7 @@ __global__ __launch_bounds__(kWgRows * 2, 1)
 void attn_fwd_vt(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K, const bf16_t *__restrict__ Vt,
                  bf16_t *__restrict__ O, const int32_t *__restrict__ row_ptr,
                  const int32_t *__restrict__ kv_idx, int N, int nqb, int nkb, int ngrp,
-                 float c /* scale * log2(e) */) {
+                 float c /* scale * log2(e) */, const int32_t *__restrict__ labels, int qo_orig, int F, int S) {
   constexpr int G = kWgRows / BQ;          // q-blocks per work-group
   using T = DTile<D>;
   constexpr int TB = T::TBYTES;            // K tile bytes == V^T tile bytes
@@ -81,6 +81,14 @@ void attn_fwd_vt(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K, con
   const bf16_t *Vth = Vt + (size_t)h * nkb * (BK * D);
   bf16_t *Oh = O + hoff;
   const int qrow = grp * kWgRows + wave * 32 + l32;
+  // Q and O rows: the executing layout's row qrow, or (qo_orig) the original
+  // row it holds: for a temporal head (labels[h] == 1, or every head when
+  // labels is NULL) row p*F + f of the video holds frame-major row f*S + p.
+  int qsrc = qrow;
+  if (qo_orig && (labels == nullptr || labels[h] == 1) && qrow < F * S) {
+    const int p = qrow / F, f = qrow - p * F;
+    qsrc = f * S + p;
+  }
 
   int nt = nkb;
   if constexpr (!DENSE)
@@ -90,7 +98,7 @@ void attn_fwd_vt(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K, con
     if (qrow < N) {
 #pragma unroll
       for (int dd = hi * 8; dd < D; dd += 16)
-        *reinterpret_cast<u32x4 *>(Oh + (size_t)qrow * D + dd) = u32x4{0, 0, 0, 0};
+        *reinterpret_cast<u32x4 *>(Oh + (size_t)qsrc * D + dd) = u32x4{0, 0, 0, 0};
     }
     return;
   }
@@ -107,7 +115,7 @@ void attn_fwd_vt(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K, con
   const int own_bit = 1 << (24 + gw);
 
   bf16x8 qf[D / 16];
-  load_q<D>(Qh, qrow < N ? qrow : -1, hi, qf);
+  load_q<D>(Qh, qrow < N ? qsrc : -1, hi, qf);
   f32x16 o[D / 32];
   float m_run, l_run;
   auto prep = [&](f32x16 &s0, f32x16 &s1, int e) -> bool {
@@ -127,12 +135,13 @@ void attn_fwd_vt(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K, con
   };
   vt_attend<D, kNW>(nt, ent_raw, prep, Kh, Vth, N, k0, k1, k2, V0, V1, V2, qf, wave, lane, c, o, m_run, l_run);
   __builtin_amdgcn_s_waitcnt(0);  // no DMA may land after the work-group ends
-  store_o<D>(qrow < N ? Oh + (size_t)qrow * D : nullptr, o, l_run, hi);
+  store_o<D>(qrow < N ? Oh + (size_t)qsrc * D : nullptr, o, l_run, hi);
 }
 
 template <int D, int BQ>
 hipError_t launch_vt(const Dims &dm, const void *Q, const void *K, const void *Vt, void *O,
-                     const int32_t *row_ptr, const int32_t *kv_idx, float c, hipStream_t st) {
+                     const int32_t *row_ptr, const int32_t *kv_idx, float c, const int32_t *labels, int qo_orig,
+                     hipStream_t st) {
   constexpr int G = kWgRows / BQ;
   const int nqb = (dm.N + BQ - 1) / BQ, nkb = (dm.N + BK - 1) / BK;
   const int ngrp = (nqb + G - 1) / G;
@@ -141,11 +150,11 @@ hipError_t launch_vt(const Dims &dm, const void *Q, const void *K, const void *V
   if (row_ptr == nullptr)
     hipLaunchKernelGGL((attn_fwd_vt<D, BQ, true>), dim3(grid), dim3(kWgRows * 2), 0, st, (const bf16_t *)Q,
                        (const bf16_t *)K, (const bf16_t *)Vt, (bf16_t *)O, row_ptr, kv_idx, dm.N, nqb, nkb, ngrp,
-                       c);
+                       c, labels, qo_orig, dm.F, dm.S);
   else
     hipLaunchKernelGGL((attn_fwd_vt<D, BQ, false>), dim3(grid), dim3(kWgRows * 2), 0, st, (const bf16_t *)Q,
                        (const bf16_t *)K, (const bf16_t *)Vt, (bf16_t *)O, row_ptr, kv_idx, dm.N, nqb, nkb, ngrp,
-                       c);
+                       c, labels, qo_orig, dm.F, dm.S);
   return hipGetLastError();
 }
 
@@ -155,13 +164,14 @@ int attn_vt_max_kv_blocks() { return kMaxKb; }
 
 hipError_t launch_attn_vt(const Dims &dm, const void *Q, const void *K, const void *Vt, void *O,
                           const int32_t *row_ptr, const int32_t *kv_idx, int bq, int bk, float scale,
-                          hipStream_t st) {
+                          hipStream_t st, bool qo_orig, const int32_t *labels) {
   const float c = scale * kLog2e;
+  const int qo = qo_orig ? 1 : 0;
   if (bk != BK) return hipErrorInvalidValue;
-  if (dm.d == 128 && bq == 128) return launch_vt<128, 128>(dm, Q, K, Vt, O, row_ptr, kv_idx, c, st);
-  if (dm.d == 128 && bq == 64) return launch_vt<128, 64>(dm, Q, K, Vt, O, row_ptr, kv_idx, c, st);
-  if (dm.d == 64 && bq == 128) return launch_vt<64, 128>(dm, Q, K, Vt, O, row_ptr, kv_idx, c, st);
-  if (dm.d == 64 && bq == 64) return launch_vt<64, 64>(dm, Q, K, Vt, O, row_ptr, kv_idx, c, st);
+  if (dm.d == 128 && bq == 128) return launch_vt<128, 128>(dm, Q, K, Vt, O, row_ptr, kv_idx, c, labels, qo, st);
+  if (dm.d == 128 && bq == 64) return launch_vt<128, 64>(dm, Q, K, Vt, O, row_ptr, kv_idx, c, labels, qo, st);
+  if (dm.d == 64 && bq == 128) return launch_vt<64, 128>(dm, Q, K, Vt, O, row_ptr, kv_idx, c, labels, qo, st);
+  if (dm.d == 64 && bq == 64) return launch_vt<64, 64>(dm, Q, K, Vt, O, row_ptr, kv_idx, c, labels, qo, st);
   return hipErrorInvalidValue;
 }
 

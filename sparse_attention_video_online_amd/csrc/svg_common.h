@@ -67,9 +67,12 @@ hipError_t launch_attn_mfma(const Dims &dm, const void *Q, const void *K, const 
 hipError_t launch_attn_simt(const Dims &dm, bool bf16, const void *Q, const void *K, const void *V,
                             void *O, const int32_t *row_ptr, const int32_t *kv_idx, int bq, int bk,
                             float scale, hipStream_t st);
+// qo_orig: Q is read and O written in the original token order, rows
+// permuted per labels (NULL: every head) as the layout permute does; K and
+// Vt are in the executing layout either way.
 hipError_t launch_attn_vt(const Dims &dm, const void *Q, const void *K, const void *Vt, void *O,
                           const int32_t *row_ptr, const int32_t *kv_idx, int bq, int bk, float scale,
-                          hipStream_t st);
+                          hipStream_t st, bool qo_orig = false, const int32_t *labels = nullptr);
 int attn_vt_max_kv_blocks();
 // identity: keep every head's token order (the key-tiled V^T of V as given)
 hipError_t launch_layout_vt(const Dims &dm, const void *V, void *Vt, const int32_t *labels, hipStream_t st,

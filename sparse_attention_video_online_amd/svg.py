@@ -63,6 +63,7 @@ SIGNATURES = {
     "svg_vt_elems": [_DIMS],
     "svg_layout_permute_vt": [_DIMS, _I, _P, _P, _P, _P],
     "svg_block_sparse_attn_csr_vt": [_DIMS, _I, _P, _P, _P, _P, _P, _I, _I, _F, _P, _P],
+    "svg_block_sparse_attn_csr_vt_layout": [_DIMS, _I, _P, _P, _P, _P, _P, _P, _I, _I, _F, _P, _P],
     "svg_dense_attn_vt": [_DIMS, _I, _P, _P, _P, _I, _I, _F, _P, _P],
     "svg2_workspace_bytes": [_I, _DIMS, _I, _I],
     "svg_kmeans": [_DIMS, _I, _P, _I, _I, _P, _P, _P, _P, _P, _Z, _P],
@@ -274,6 +275,19 @@ def svg_block_sparse_attn_csr_vt(q, k, vt, row_ptr, kv_idx, F, S, T, bq, bk, sca
     _check(_lib.svg_block_sparse_attn_csr_vt(ctypes.byref(dm), dt, _ptr(q), _ptr(k), _ptr(vt), _ptr(row_ptr),
                                              _ptr(kv_idx), bq, bk, scale, _ptr(out), _stream()),
            "svg_block_sparse_attn_csr_vt")
+    return out
+
+
+def svg_block_sparse_attn_csr_vt_layout(q, k, vt, row_ptr, kv_idx, labels, F, S, T, bq, bk, scale=-1.0,
+                                        out=None):
+    """Q and the returned O in the original token order; K, Vt and the lists
+    in each head's executing layout per labels (None: every head temporal)."""
+    dm, dt = _qk_vt(q, k, vt, F, S, T)
+    out = torch.empty_like(q) if out is None else out
+    _check(_lib.svg_block_sparse_attn_csr_vt_layout(ctypes.byref(dm), dt, _ptr(q), _ptr(k), _ptr(vt),
+                                                    _ptr(row_ptr), _ptr(kv_idx), _ptr(labels), bq, bk, scale,
+                                                    _ptr(out), _stream()),
+           "svg_block_sparse_attn_csr_vt_layout")
     return out
 
 

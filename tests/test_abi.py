@@ -113,6 +113,15 @@ def test_vt_entry_points_validate_on_host():
     assert "kv-blocks" in svg.last_error()
     assert L.svg_block_sparse_attn_csr_vt(dims(), bf16, FAKE, FAKE, FAKE, None, FAKE, 64, 64, -1.0, FAKE2,
                                           None) == svg.SVG_ERR_NULL
+    # the original-order variant: same checks (NULL lists, NULL tensors, unsupported shapes)
+    assert L.svg_block_sparse_attn_csr_vt_layout(dims(), bf16, FAKE, FAKE, FAKE, FAKE, None, None, 64, 64, -1.0,
+                                                 FAKE2, None) == svg.SVG_ERR_NULL
+    assert L.svg_block_sparse_attn_csr_vt_layout(dims(), bf16, None, FAKE, FAKE, FAKE, FAKE, None, 64, 64, -1.0,
+                                                 FAKE2, None) == svg.SVG_ERR_NULL
+    assert L.svg_block_sparse_attn_csr_vt_layout(dims(), bf16, FAKE, FAKE, FAKE, FAKE, FAKE, None, 128, 128, -1.0,
+                                                 FAKE2, None) == svg.SVG_ERR_UNSUPPORTED
+    assert L.svg_block_sparse_attn_csr_vt_layout(dims(), 0, FAKE, FAKE, FAKE, FAKE, FAKE, None, 64, 64, -1.0,
+                                                 FAKE2, None) == svg.SVG_ERR_UNSUPPORTED
     # O overlapping an input
     assert L.svg_dense_attn_vt(dims(), bf16, FAKE, FAKE2, FAKE, 64, 64, -1.0, FAKE, None) == svg.SVG_ERR_RANGE
     assert L.svg_layout_permute_vt(dims(), 0, FAKE, FAKE2, None, None) == svg.SVG_ERR_UNSUPPORTED

@@ -121,6 +121,52 @@ def test_attention_vt_cogvideox_full():
         check_close(got[h], ref, BF16_MAX_ABS, BF16_REL_L2, f"cog head {h}")
 
 
+def test_attention_vt_layout_fused_cogvideox_bit_exact():
+    """svg_block_sparse_attn_csr_vt_layout (Q and O in the original token
+    order) equals permute -> svg_block_sparse_attn_csr_vt -> unpermute bit for
+    bit, with mixed labels; the unfused path is the oracle-checked one above."""
+    w = COG
+    g = inputs(w)
+    labels = generator_labels(w)
+    want = to_host_bits(run_sparse_vt(w, g, labels))
+    q, k, v = (to_dev(g[x], w.dtype) for x in "qkv")
+    lab = ints(labels)
+    kp = svg.svg_layout_permute(k, w.F, w.S, w.T, lab)
+    vt = svg.svg_layout_permute_vt(v, w.F, w.S, w.T, lab)
+    bm = svg.svg_build_block_mask(lab, w.F, w.S, w.T, w.H, w.d, w.ks, w.wt, w.bq, w.bk)
+    row_ptr, kv_idx = svg.svg_compact_block_mask(bm)
+    o = svg.svg_block_sparse_attn_csr_vt_layout(q, kp, vt, row_ptr, kv_idx, lab, w.F, w.S, w.T, w.bq, w.bk)
+    sync()
+    np.testing.assert_array_equal(to_host_bits(o), want)
+
+
+@pytest.mark.parametrize("F,S,T,d,bq", [(5, 23, 7, 64, 64), (3, 100, 0, 128, 128), (7, 64, 33, 128, 64)])
+def test_attention_vt_layout_fused_ragged_labels_null(F, S, T, d, bq):
+    """Ragged shapes, labels NULL (every head temporal) and a random bitmap:
+    the fused entry equals the unfused path bit for bit, and its output is
+    within the bf16 bar of the oracle."""
+    H, bk = 2, 64
+    N = F * S + T
+    q, k, v = random_qkv(H, N, d, seed=N + d, dtype="bf16", scale=1.5)
+    nqb, nkb = -(-N // bq), -(-N // bk)
+    bm = (np.random.default_rng(N).random((H, nqb, nkb)) < 0.6).astype(np.uint8)
+    row_ptr, kv_idx = csr(bm)
+    qd, kd, vd = (to_dev(x, "bf16") for x in (q, k, v))
+    qp, kp = (svg.svg_layout_permute(t, F, S, T, None) for t in (qd, kd))
+    vt = svg.svg_layout_permute_vt(vd, F, S, T, None)
+    want = svg.svg_layout_unpermute(svg.svg_block_sparse_attn_csr_vt(qp, kp, vt, row_ptr, kv_idx, F, S, T, bq, bk),
+                                    F, S, T, None)
+    o = svg.svg_block_sparse_attn_csr_vt_layout(qd, kp, vt, row_ptr, kv_idx, None, F, S, T, bq, bk)
+    sync()
+    np.testing.assert_array_equal(to_host_bits(o), to_host_bits(want))
+    got = to_f64(o)
+    for h in range(H):
+        xs = layout.permute(np.stack([as_f64(x[h], "bf16") for x in (q, k, v)]), F, S, T, [1, 1, 1])
+        ref_p = attention.block_sparse_attention_full(xs[0], xs[1], xs[2], bm[h], bq, bk)
+        ref = layout.unpermute(ref_p[None], F, S, T, [1])[0]
+        check_close(got[h], ref, BF16_MAX_ABS, BF16_REL_L2, f"fused ragged head {h}")
+
+
 def test_attention_vt_hunyuan_sampled_qblocks():
     """Full HunyuanVideo shape (N = 119,056, 24 heads, d = 128, 128x64
     tiles, ~31% density) in the launch configuration the bench times;
