@@ -441,7 +441,9 @@ def main():
 
     def dense_attend():
         if use_vt:
-            svg.svg_dense_attn_vt(qp, kp, vt, F, S, T, bq, bk, out=dense)
+            # every query row attends every key, so Q in its original order
+            # is as good as permuted (K and Vt share one key order)
+            svg.svg_dense_attn_vt(q, kp, vt, F, S, T, bq, bk, out=dense)
         else:
             svg.svg_dense_attn(qp, kp, vp, F, S, T, bq, bk, out=dense)
     dense_attend()
