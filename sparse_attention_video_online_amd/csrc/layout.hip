@@ -59,24 +59,40 @@ void permute_rows_kernel(const u32x4 *__restrict__ X, const int32_t *__restrict_
 
 // Vt tile (h, kb): the 64 executing-layout rows kb*64.. of head h, transposed
 // to [d][64 keys], zero past N.  Executing row r of a permuted head reads
-// frame-major row f*S + p (r = p*F + f, video rows only).  The tile is
-// staged in LDS row-major with a padded stride; every global access is a
-// 16-byte vector and consecutive threads touch consecutive 16-byte units.
+// frame-major row f*S + p (r = p*F + f, video rows only).  With frames set,
+// every head keeps its token order and each frame (then the text) starts a
+// new tile: tile kb < F*nbf (nbf = ceil(S/64) tiles a frame) holds rows
+// f*S + 64j .. of frame f = kb / nbf, j = kb % nbf, zero past the frame's
+// end; the text tiles follow.  The tile is staged in LDS row-major with a
+// padded stride; every global access is a 16-byte vector and consecutive
+// threads touch consecutive 16-byte units.
 template <int D>
 __global__ __launch_bounds__(256)
 void vt_kernel(const u32x4 *__restrict__ X, u32x4 *__restrict__ Y, const int32_t *__restrict__ labels,
-               int F, int S, int N, int nkb, int identity) {
+               int F, int S, int N, int nkb, int frames) {
   constexpr int STR = D + 8;                 // padded row stride (halfwords)
   constexpr int CPR = D / 8;                 // 16-byte units per row
   __shared__ __attribute__((aligned(16))) uint16_t t[64 * STR];
   const int kb = blockIdx.x, h = blockIdx.y;
-  const bool perm = !identity && (labels == nullptr || labels[h] == 1);
+  const bool perm = !frames && (labels == nullptr || labels[h] == 1);
+  const int nbf = (S + 63) / 64;
   const u32x4 *Xh = X + (size_t)h * N * CPR;
   for (int u = threadIdx.x; u < 64 * CPR; u += 256) {
     const int row = u / CPR, ch = u - row * CPR;
-    const int r = kb * 64 + row;
+    int r = kb * 64 + row;
+    bool in = r < N;
+    if (frames) {
+      if (kb < F * nbf) {
+        const int f = kb / nbf, rl = (kb - f * nbf) * 64 + row;
+        in = rl < S;
+        r = f * S + rl;
+      } else {
+        r = F * S + (kb - F * nbf) * 64 + row;
+        in = r < N;
+      }
+    }
     u32x4 v = u32x4{0, 0, 0, 0};
-    if (r < N) {
+    if (in) {
       int src = r;
       if (perm && r < F * S) {
         const int p = r / F, f = r - p * F;
@@ -101,15 +117,15 @@ void vt_kernel(const u32x4 *__restrict__ X, u32x4 *__restrict__ Y, const int32_t
 }  // namespace
 
 hipError_t launch_layout_vt(const Dims &dm, const void *V, void *Vt, const int32_t *labels, hipStream_t st,
-                            bool identity) {
-  const int nkb = (dm.N + 63) / 64;
+                            bool frames) {
+  const int nkb = frames ? vt_frame_tiles(dm) : (dm.N + 63) / 64;
   if (dm.N == 0 || dm.H == 0) return hipSuccess;
   if (dm.d == 128)
     hipLaunchKernelGGL(vt_kernel<128>, dim3(nkb, dm.H), dim3(256), 0, st, (const u32x4 *)V, (u32x4 *)Vt, labels,
-                       dm.F, dm.S, dm.N, nkb, identity ? 1 : 0);
+                       dm.F, dm.S, dm.N, nkb, frames ? 1 : 0);
   else
     hipLaunchKernelGGL(vt_kernel<64>, dim3(nkb, dm.H), dim3(256), 0, st, (const u32x4 *)V, (u32x4 *)Vt, labels,
-                       dm.F, dm.S, dm.N, nkb, identity ? 1 : 0);
+                       dm.F, dm.S, dm.N, nkb, frames ? 1 : 0);
   return hipGetLastError();
 }
 

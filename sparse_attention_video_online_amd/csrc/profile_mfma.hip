@@ -5,19 +5,22 @@
 // over its own kept keys with its own maximum.  Then per-head MSEs of the
 // masked outputs against the full one, and the label (ties -> spatial).
 //
-// Three passes (full, spatial, temporal) each keep one online-softmax state
-// per sampled row and walk one chunk of the N keys per work-group in 64-key
-// tiles; each lane owns one sampled row.  The full pass runs the attention
-// kernel's V^T tile pipeline (vt_attend: 8 waves x 32 samples, K and the
-// key-tiled V^T of V DMA'd into LDS).  The masked passes use the S^T = K Q^T
-// / O^T += V^T P^T machinery of attn_core.h on 128 sampled rows (4 waves x
-// 32), grouped by frame or by grid position, and visit only the key tiles
-// that some sample's window (or a text key) reaches.  In a flagged tile each row keeps at most two key ranges, one
-// per frame the tile touches: a wave whose rows keep none of the tile skips
-// its math, a wave whose rows keep all of it needs no mask, and the others
-// test each score's key offset against the two ranges.  Chunks are merged
-// afterwards (flash-decoding style), and the squared errors are summed in
-// fp64 in a fixed order.
+// Two passes.  The full pass runs the attention kernel's V^T tile pipeline
+// (vt_attend: 8 waves x 32 sampled rows, K and a key-tiled V^T DMA'd into
+// LDS) over key chunks that never cross a frame boundary: V^T is laid out
+// with every frame (then the text) starting a new 64-key tile, and each
+// chunk is one frame, or a part of one, or a part of the text.  A spatial
+// window is a run of whole frames plus the text, so the spatial output of a
+// row is the merge of the full pass's chunks inside its window: no spatial
+// pass is run.  The temporal pass uses the S^T = K Q^T / O^T += V^T P^T
+// machinery of attn_core.h on 128 sampled rows (4 waves x 32) grouped by
+// grid position, and visits only the key tiles that some sample's window
+// (or a text key) reaches.  In a flagged tile each row keeps at most two
+// key ranges, one per frame the tile touches: a wave whose rows keep none of
+// the tile skips its math, a wave whose rows keep all of it needs no mask,
+// and the others test each score's key offset against the two ranges.
+// Chunks are merged afterwards (flash-decoding style), and the squared
+// errors are summed in fp64 in a fixed order.
 #include "attn_vt_core.h"
 
 namespace svgk {
@@ -38,34 +41,42 @@ constexpr int FNT = FNW * 64;
 constexpr int FQ = FNW * 32;
 constexpr int kFullSlots = 256;   // full-pass work-groups resident at once (one per CU, 256 CUs)
 
-// Key chunks of the full pass.  Every work-group has the same work, so the
-// pass takes about (rounds of resident work-groups) x (tiles per chunk + a
-// fixed cost of ~8 tiles per work-group); take the fewest.  At the
-// HunyuanVideo layer shape: 2 chunks, 240 work-groups in one round.
-ProfileGrid profile_grid_full(const Dims &dm, int n_s) {
-  const int nkb = (dm.N + BK - 1) / BK;
-  const int nqg = (n_s + FQ - 1) / FQ;
-  long long best = -1;
-  int best_tpc = nkb;
-  for (int c = 1; c <= min(nkb, 64); ++c) {
-    const int tpc = (nkb + c - 1) / c;
-    const long long nch = (nkb + tpc - 1) / tpc;
-    const long long rounds = ((long long)dm.H * nqg * nch + kFullSlots - 1) / kFullSlots;
-    const long long cost = rounds * (tpc + 8);
-    if (best < 0 || cost < best) {
+// Key chunks of the full pass: each frame in P parts of tpp tiles, the
+// text in Pt parts of at most tpp tiles; chunk ch < F*P is part ch % P of
+// frame ch / P, the text parts follow.  The pass takes about
+// max(total work / resident work-groups, longest work-group), a work-group
+// costing its tiles plus a fixed ~8 tiles (Q load, pipeline fill, partial
+// store); take the cheapest tpp.  At the HunyuanVideo layer shape: whole
+// frames (57 tiles), 34 chunks, 4080 work-groups.
+struct FrameGrid { int nqg, nbf, nbt, tpp, P, Pt, nchunks; };
+
+FrameGrid profile_grid_full(const Dims &dm, int n_s) {
+  FrameGrid g;
+  g.nqg = (n_s + FQ - 1) / FQ;
+  g.nbf = (dm.S + BK - 1) / BK;
+  g.nbt = (dm.T + BK - 1) / BK;
+  double best = -1.0;
+  for (int P = 1; P <= g.nbf; ++P) {
+    const int tpp = (g.nbf + P - 1) / P;
+    const int Pf = (g.nbf + tpp - 1) / tpp, Pt = (g.nbt + tpp - 1) / tpp;
+    const double work = (double)dm.H * g.nqg *
+                        ((double)dm.F * (g.nbf + 8 * Pf) + (g.nbt + 8 * Pt));
+    const double cost = fmax(work / kFullSlots, (double)(tpp + 8));
+    if (best < 0.0 || cost < best) {
       best = cost;
-      best_tpc = tpc;
+      g.tpp = tpp;
+      g.P = Pf;
+      g.Pt = Pt;
     }
   }
-  return ProfileGrid{nqg, (nkb + best_tpc - 1) / best_tpc, best_tpc};
+  g.nchunks = dm.F * g.P + g.Pt;
+  return g;
 }
 
-// Key chunks per (head, sample group): about 2048 work-groups, four rounds
-// of the 512 resident ones.  Fewer chunks leave a masked pass's work in the
-// few work-groups whose chunk holds a sample group's frame window; more
-// chunks cost merge traffic.  At the HunyuanVideo layer shape (240 sample
-// groups) the three passes and the merge take 5.55 ms with 9-10 chunks,
-// 6.0 ms with 5 and 6.4 ms with 2 or 17.
+// Key chunks of the temporal pass per (head, sample group): about 2048
+// work-groups, four rounds of the 512 resident ones.  Fewer chunks leave the
+// work in the few work-groups whose chunk holds a sample group's windows;
+// more chunks cost merge traffic.
 ProfileGrid profile_grid(const Dims &dm, int n_s) {
   const int nkb = (dm.N + BK - 1) / BK;
   const int nqg = (n_s + PQ - 1) / PQ;
@@ -79,90 +90,84 @@ ProfileGrid profile_grid(const Dims &dm, int n_s) {
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 struct Parts {
-  float *o;    // [H][n_s][C][3][D], C = the larger of the passes' chunk counts
-  float *ml;   // [H][n_s][C][3][2]
-  double *se;  // [H][n_s][2]
-  int32_t *ord_s, *ord_t;  // [n_s] each
-  bf16_t *vt;  // V in its own token order, key-tiled transposed: [H][nKB][D][64]
+  float *fo, *fml;  // full pass: [H][n_s][Cf][D], [H][n_s][Cf][2] (O, max, sum)
+  float *to, *tml;  // temporal pass: [H][n_s][Ct][D], [H][n_s][Ct][2]
+  double *se;       // [H][n_s][2]
+  int32_t *ord_t;   // [n_s]
+  bf16_t *vt;       // V in its own token order, key-tiled transposed, frames
+                    // padded to whole tiles: [H][vt_frame_tiles][D][64]
+  size_t bytes;     // workspace size
 };
 
-size_t vt_bytes(const Dims &dm) { return (size_t)dm.H * ((dm.N + BK - 1) / BK) * BK * dm.d * sizeof(bf16_t); }
-
-Parts carve(void *ws, const Dims &dm, int n_s, int C) {
-  char *p = (char *)ws;
-  const size_t no = (size_t)dm.H * n_s * C * 3 * dm.d * sizeof(float);
-  const size_t nml = (size_t)dm.H * n_s * C * 3 * 2 * sizeof(float);
+// Workspace layout for Cf full-pass and Ct temporal chunks (ws may be null
+// to get the size only).
+Parts carve(void *ws, const Dims &dm, int n_s, int Cf, int Ct) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char *q = (char *)((uintptr_t)ws + off);
+    off += align256(bytes);
+    return q;
+  };
+  const size_t rows = (size_t)dm.H * n_s;
   Parts r;
-  r.o = (float *)p;
-  r.ml = (float *)(p + align256(no));
-  const size_t nse = (size_t)dm.H * n_s * 2 * sizeof(double);
-  r.se = (double *)(p + align256(no) + align256(nml));
-  r.ord_s = (int32_t *)(p + align256(no) + align256(nml) + align256(nse));
-  r.ord_t = r.ord_s + align256((size_t)n_s * 4) / 4;
-  r.vt = (bf16_t *)((char *)r.ord_t + align256((size_t)n_s * 4));
+  r.fo = (float *)take(rows * Cf * dm.d * sizeof(float));
+  r.fml = (float *)take(rows * Cf * 2 * sizeof(float));
+  r.to = (float *)take(rows * Ct * dm.d * sizeof(float));
+  r.tml = (float *)take(rows * Ct * 2 * sizeof(float));
+  r.se = (double *)take(rows * 2 * sizeof(double));
+  r.ord_t = (int32_t *)take((size_t)n_s * 4);
+  r.vt = (bf16_t *)take((size_t)dm.H * vt_frame_tiles(dm) * BK * dm.d * sizeof(bf16_t));
+  r.bytes = off;
   return r;
 }
 
 constexpr int kMaxVisit = 4096;   // visit-list capacity (tiles per chunk)
 constexpr int kMaxRankSamples = 16384;
 
-// Orders of the samples for the work-groups of the masked passes: ord_s by
-// row index (a work-group's samples then share few frames), ord_t by
-// position-major index p*F + f (they then share few grid positions).  Text
-// rows sort last in both.  Ties keep the sample order.  Only the grouping of
+// Order of the samples for the work-groups of the temporal pass: by
+// position-major index p*F + f (a work-group's samples then share few grid
+// positions), text rows last, ties in sample order.  Only the grouping of
 // samples into work-groups changes; each sample's result has its own slot.
 __global__ __launch_bounds__(256)
-void profile_order(const int32_t *__restrict__ sample_idx, int n_s, int F, int S, int32_t *__restrict__ ord_s,
-                   int32_t *__restrict__ ord_t) {
-  __shared__ int ci[1024], cr[1024];
+void profile_order(const int32_t *__restrict__ sample_idx, int n_s, int F, int S, int32_t *__restrict__ ord_t) {
+  __shared__ int cr[1024];
   const int s = blockIdx.x * 256 + threadIdx.x;
   const bool act = s < n_s;
   if (n_s > kMaxRankSamples) {
-    if (act) {
-      ord_s[s] = s;
-      ord_t[s] = s;
-    }
+    if (act) ord_t[s] = s;
     return;
   }
   const int FS = F * S;
   auto rpos = [&](int i) { return i >= FS ? i : (i % S) * F + i / S; };
   const int i = act ? sample_idx[s] : 0, r = rpos(i);
-  int rs = 0, rt = 0;
+  int rt = 0;
   for (int base = 0; base < n_s; base += 1024) {
     const int cnt = min(1024, n_s - base);
     __syncthreads();
-    for (int u = threadIdx.x; u < cnt; u += 256) {
-      ci[u] = sample_idx[base + u];
-      cr[u] = rpos(ci[u]);
-    }
+    for (int u = threadIdx.x; u < cnt; u += 256) cr[u] = rpos(sample_idx[base + u]);
     __syncthreads();
     for (int u = 0; u < cnt; ++u) {
-      const int j = ci[u], q = cr[u], us = base + u;
-      rs += (j < i) || (j == i && us < s);
+      const int q = cr[u], us = base + u;
       rt += (q < r) || (q == r && us < s);
     }
   }
-  if (act) {
-    ord_s[rs] = s;
-    ord_t[rt] = s;
-  }
+  if (act) ord_t[rt] = s;
 }
 
-// One pass of masked attention for the work-group's 128 sampled rows over
-// one chunk of key tiles.  KIND 0 = no mask (full), 1 = spatial,
-// 2 = temporal.  A prologue lists the chunk's tiles that some sample of the
+// The temporal pass for the work-group's 128 sampled rows over one chunk of
+// key tiles.  A prologue lists the chunk's tiles that some sample of the
 // work-group keeps (any key), and flags the tiles where some video sample
 // does not keep every video key: only those evaluate the token mask.
-template <int D, int KIND>
+template <int D>
 __global__ __launch_bounds__(PNT, 2)
-void profile_pass_mfma(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K, const bf16_t *__restrict__ V,
-                       const int32_t *__restrict__ sample_idx, const int32_t *__restrict__ order, int n_s, int F,
-                       int S, int N, int ks, int wt, int nkb, int tpc, int cstride, float c,
-                       float *__restrict__ part_o, float *__restrict__ part_ml) {
+void profile_temporal_mfma(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K, const bf16_t *__restrict__ V,
+                           const int32_t *__restrict__ sample_idx, const int32_t *__restrict__ order, int n_s,
+                           int F, int S, int N, int wt, int nkb, int tpc, int cstride, float c,
+                           float *__restrict__ part_o, float *__restrict__ part_ml) {
   using C = Tile<D, PNT>;
   __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE];
   __shared__ uint16_t vlist[kMaxVisit];   // tile - t0, bit 15: evaluate the mask
-  __shared__ int bnd[5];     // f_lo, f_hi, p_lo, p_hi, text query present
+  __shared__ int bnd[5];     // -, video query present, p_lo, p_hi, text query present
   __shared__ int wcount[PNW + 1];
   const int h = blockIdx.z, chunk = blockIdx.y, qg = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -189,14 +194,8 @@ void profile_pass_mfma(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ 
   const int wq = wtc / F, wr = wtc - wq * F;
   // Kept keys of frame f for this row, absolute [lo, hi] (lo > hi: none).
   auto frame_keys = [&](int f, int &lo, int &hk) {
-    if (KIND == 1) {
-      const bool keep = abs(f - fi) <= ks;
-      lo = keep ? f * S : 1;
-      hk = keep ? f * S + S - 1 : 0;
-    } else {
-      lo = f * S + max(pi - (wq + (f + wr >= F)), 0);
-      hk = f * S + min(pi + (wq + (f < wr)), S - 1);
-    }
+    lo = f * S + max(pi - (wq + (f + wr >= F)), 0);
+    hk = f * S + min(pi + (wq + (f < wr)), S - 1);
   };
 
   // ---- visit list of this chunk
@@ -204,19 +203,18 @@ void profile_pass_mfma(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ 
   if (tid < 5) bnd[tid] = (tid & 1) ? -1 : 0x7fffffff;
   if (tid == 4) bnd[4] = 0;
   __syncthreads();
-  if (KIND != 0 && valid) {
+  if (valid) {
     if (text_i) {
       atomicMax(&bnd[4], 1);
     } else {
-      atomicMin(&bnd[0], fi);
-      atomicMax(&bnd[1], fi);
+      atomicMax(&bnd[1], 1);
       atomicMin(&bnd[2], pi);
       atomicMax(&bnd[3], pi);
     }
   }
   __syncthreads();
-  const int f_lo = bnd[0], f_hi = bnd[1], p_lo = bnd[2], p_hi = bnd[3];
-  const bool any_video = f_hi >= 0, any_text = bnd[4] != 0;
+  const int p_lo = bnd[2], p_hi = bnd[3];
+  const bool any_video = bnd[1] > 0, any_text = bnd[4] != 0;
   // union / intersection of the video samples' windows
   const long long RU_lo = (long long)p_lo * F - wtc, RU_hi = (long long)p_hi * F + F - 1 + wtc;
   const long long RI_lo = (long long)p_hi * F - wtc, RI_hi = (long long)p_lo * F + F - 1 + wtc;
@@ -225,29 +223,17 @@ void profile_pass_mfma(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ 
     const int t = base + tid;
     bool visit = false, needmask = false;
     if (t < t1) {
-      if (KIND == 0) {
-        visit = true;
-      } else {
-        const int k0 = t * BK, k1 = min(N, k0 + BK) - 1;
-        if (k1 >= FS || any_text) visit = true;   // text keys / text rows keep all
-        if (k0 < FS && any_video) {
-          const int kv1 = min(k1, FS - 1);
-          for (int f = k0 / S; f <= kv1 / S; ++f) {
-            const int a = max(k0, f * S) - f * S, b = min(kv1, f * S + S - 1) - f * S;
-            bool some, all;
-            if (KIND == 1) {
-              some = f >= f_lo - ks && f <= f_hi + ks;
-              all = f >= f_hi - ks && f <= f_lo + ks;
-            } else {
-              // positions p in [a, b] with p*F + f inside [RU_lo, RU_hi]
-              const long long plo = (RU_lo - f + F - 1) >= 0 ? (RU_lo - f + F - 1) / F : 0;
-              const long long phi = RU_hi - f >= 0 ? (RU_hi - f) / F : -1;
-              some = max((long long)a, plo) <= min((long long)b, phi);
-              all = (long long)a * F + f >= RI_lo && (long long)b * F + f <= RI_hi;
-            }
-            visit |= some;
-            needmask |= !all;
-          }
+      const int k0 = t * BK, k1 = min(N, k0 + BK) - 1;
+      if (k1 >= FS || any_text) visit = true;   // text keys / text rows keep all
+      if (k0 < FS && any_video) {
+        const int kv1 = min(k1, FS - 1);
+        for (int f = k0 / S; f <= kv1 / S; ++f) {
+          const int a = max(k0, f * S) - f * S, b = min(kv1, f * S + S - 1) - f * S;
+          // positions p in [a, b] with p*F + f inside [RU_lo, RU_hi]
+          const long long plo = (RU_lo - f + F - 1) >= 0 ? (RU_lo - f + F - 1) / F : 0;
+          const long long phi = RU_hi - f >= 0 ? (RU_hi - f) / F : -1;
+          visit |= max((long long)a, plo) <= min((long long)b, phi);
+          needmask |= !((long long)a * F + f >= RI_lo && (long long)b * F + f <= RI_hi);
         }
       }
     }
@@ -299,7 +285,7 @@ void profile_pass_mfma(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ 
     // zeros); a wave whose rows keep every key needs no mask.
     bool skip = false, ranges = false, perkey = false;
     int a0 = 0, n0 = 0, a1 = 0, n1 = 0;
-    if (KIND != 0 && (e & 0x8000)) {
+    if (e & 0x8000) {
       if (S >= BK) {
         const int nvalid = min(BK, N - kbase);
         if (text_i) {
@@ -354,14 +340,8 @@ void profile_pass_mfma(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ 
             const int key = kbase + acc_key(b, r, hi);
             if (key >= FS) continue;  // text keys are always kept
             const int fk = key / S;
-            bool keep;
-            if (KIND == 1) {
-              keep = abs(fk - fi) <= ks;
-            } else {
-              const int rk = (key - fk * S) * F + fk;
-              keep = rk >= tlo && rk <= thi;
-            }
-            if (!keep) {
+            const int rk = (key - fk * S) * F + fk;
+            if (rk < tlo || rk > thi) {
               if (b == 0) s0[r] = -INFINITY; else s1[r] = -INFINITY;
             }
           }
@@ -380,7 +360,7 @@ void profile_pass_mfma(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ 
   // partial result of this chunk: unnormalised O, running max, sum
   const float lt = l_run + __shfl_xor(l_run, 32);
   if (!valid) return;
-  const size_t slot = (((size_t)h * n_s + sidx) * cstride + chunk) * 3 + KIND;
+  const size_t slot = ((size_t)h * n_s + sidx) * cstride + chunk;
   float *dst = part_o + slot * D;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
@@ -395,34 +375,51 @@ void profile_pass_mfma(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ 
 }
 
 // The full pass (no mask) for the work-group's 256 samples, in their given
-// order, over one chunk of key tiles, on the V^T tile pipeline: K and the
-// key-tiled V^T of V in its own token order DMA'd into three LDS stages,
-// MFMA QK and PV, lazy-rescale online softmax.  The partial result of the
-// chunk (O unnormalised, reference maximum, row sum) goes to slot (h,
-// sample, chunk, 0) of part_o / part_ml, strided by C chunks.
+// order, over one key chunk (a part of a frame, or of the text) on the V^T
+// tile pipeline: K and the frame-padded key-tiled V^T DMA'd into three LDS
+// stages, MFMA QK and PV, lazy-rescale online softmax.  The partial result
+// of the chunk (O unnormalised, reference maximum, row sum) goes to slot
+// (h, sample, chunk) of part_o / part_ml.  The work-groups of one chunk
+// (the sample groups) are consecutive on one XCD and share its L2.
 template <int D>
 __global__ __launch_bounds__(FNT, 1)
 void profile_full_vt(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K, const bf16_t *__restrict__ Vt,
-                     const int32_t *__restrict__ sample_idx, int n_s, int N, int nkb, int tpc, int C, float c,
-                     float *__restrict__ part_o, float *__restrict__ part_ml) {
-  using T = DTile<D>;
-  constexpr int TB = T::TBYTES;
+                     const int32_t *__restrict__ sample_idx, int n_s, int F, int S, int T, int nqg, int nbf,
+                     int nbt, int tpp, int P, int Cf, float c, float *__restrict__ part_o,
+                     float *__restrict__ part_ml) {
+  constexpr int TB = DTile<D>::TBYTES;
   // V^T stages named to sort first, below 64 KB of LDS (immediate offsets)
   __shared__ __attribute__((aligned(1024))) char k0[TB], k1[TB], k2[TB], V0[TB], V1[TB], V2[TB];
-  const int h = blockIdx.z, chunk = blockIdx.y, qg = blockIdx.x;
+  const int work = xcd_remap(blockIdx.x, gridDim.x);
+  const int qg = work % nqg, chunk = (work / nqg) % Cf, h = work / (nqg * Cf);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hi = lane >> 5;
+  const int N = F * S + T;
   const size_t hoff = (size_t)h * N * D;
   const int pos = qg * FQ + wave * 32 + (lane & 31);
   const bool valid = pos < n_s;
   const int i = valid ? sample_idx[pos] : 0;
-  const int t0 = chunk * tpc;
-  const int nt = min(nkb, t0 + tpc) - t0;   // >= 1 by the chunking
-  auto ent_raw = [&](int j) -> int { return t0 + (j < nt ? j : nt - 1); };
+  // the chunk's keys: rows krow0 .. krow0 + nrows - 1 (to the end of its
+  // frame or of the text), tiles vt0 .. vt0 + nt - 1 of the padded V^T
+  int krow0, nrows, vt0, nt;
+  if (chunk < F * P) {
+    const int f = chunk / P, t0 = (chunk - f * P) * tpp;
+    krow0 = f * S + t0 * BK;
+    nrows = S - t0 * BK;
+    vt0 = f * nbf + t0;
+    nt = min(nbf - t0, tpp);
+  } else {
+    const int t0 = (chunk - F * P) * tpp;
+    krow0 = F * S + t0 * BK;
+    nrows = T - t0 * BK;
+    vt0 = F * nbf + t0;
+    nt = min(nbt - t0, tpp);
+  }
+  auto ent_raw = [&](int j) -> int { return j < nt ? j : nt - 1; };
   auto prep = [&](f32x16 &s0, f32x16 &s1, int e) -> bool {
-    if ((e + 1) * BK > N) {  // keys past N: only in the last kv-block
-      const int nvh = N - e * BK - 8 * hi;   // acc_key_pi(b, r, hi) = acc_key_pi(b, r, 0) + 8 hi
+    if ((e + 1) * BK > nrows) {  // keys past the frame's end: only in its last tile
+      const int nvh = nrows - e * BK - 8 * hi;   // acc_key_pi(b, r, hi) = acc_key_pi(b, r, 0) + 8 hi
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         if (acc_key_pi(0, r, 0) >= nvh) s0[r] = -INFINITY;
@@ -435,15 +432,17 @@ void profile_full_vt(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K,
   load_q<D>(Q + hoff, valid ? i : -1, hi, qf);
   f32x16 o[D / 32];
   float m_run, l_run;
-  // Row sums of the fp32 probabilities, as the masked passes take them: the
+  // Row sums of the fp32 probabilities, as the temporal pass takes them: the
   // three outputs then share one rounding convention, and the small MSEs of
   // heads whose masks both keep nearly all the weight stay comparable.
-  vt_attend<D, FNW, false>(nt, ent_raw, prep, K + hoff, Vt + (size_t)h * nkb * (BK * D), N, k0, k1, k2, V0, V1,
-                           V2, qf, wave, lane, c, o, m_run, l_run);
+  const int nkbf = F * nbf + nbt;
+  vt_attend<D, FNW, false>(nt, ent_raw, prep, K + hoff + (size_t)krow0 * D,
+                           Vt + ((size_t)h * nkbf + vt0) * (BK * D), nrows, k0, k1, k2, V0, V1, V2, qf, wave, lane,
+                           c, o, m_run, l_run);
   __builtin_amdgcn_s_waitcnt(0);  // no DMA may land after the work-group ends
   const float lt = l_run + __shfl_xor(l_run, 32);
   if (!valid) return;
-  const size_t slot = (((size_t)h * n_s + pos) * C + chunk) * 3;
+  const size_t slot = ((size_t)h * n_s + pos) * Cf + chunk;
   float *dst = part_o + slot * D;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
@@ -457,34 +456,63 @@ void profile_full_vt(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K,
   }
 }
 
-// Merge the chunks of one sampled row; squared errors of the masked outputs.
-// Pass m has nch_m chunks; the slots are strided by C (the largest).  A
-// mask that keeps every key of every row (cover bit m) has the full output
-// as its output, exactly: that pass was not run.
+// Merge the chunks of one sampled row into its three outputs and take the
+// squared errors of the masked ones.  Full: every chunk of the full pass.
+// Spatial: the full pass's chunks of the frames within ks of the row's frame
+// and the text chunks (a text row keeps every key: its full output).
+// Temporal: the temporal pass's chunks.  A mask that keeps every key of
+// every row (cover bit 1: spatial, 2: temporal) has the full output as its
+// output, exactly: its merge is skipped (the temporal pass was not run).
 __global__ __launch_bounds__(128)
-void profile_combine(const float *__restrict__ part_o, const float *__restrict__ part_ml, int n_s, int C,
-                     int nch0, int nch12, int cover, int D, float c, double *__restrict__ se) {
+void profile_combine(const float *__restrict__ fo, const float *__restrict__ fml, int Cf, int P,
+                     const float *__restrict__ to, const float *__restrict__ tml, int Ct,
+                     const int32_t *__restrict__ sample_idx, int n_s, int F, int S, int ks, int cover, int D,
+                     float c, double *__restrict__ se) {
   __shared__ double red[2][128];
   const int h = blockIdx.y, s = blockIdx.x, e = threadIdx.x;
-  double out[3] = {0.0, 0.0, 0.0};
-  for (int m = 0; m < 3; ++m) {
-    if (m > 0 && (cover >> m & 1)) {
-      out[m] = out[0];
-      continue;
+  const int i = sample_idx[s];
+  const bool text_i = i >= F * S;
+  const int fi = text_i ? 0 : i / S;
+  const bool sp_all = text_i || (cover & 2);
+  auto in_window = [&](int ch) { return sp_all || ch >= F * P || abs(ch / P - fi) <= ks; };
+  const size_t rf = ((size_t)h * n_s + s) * Cf, rt = ((size_t)h * n_s + s) * Ct;
+  // maxima of the full and the spatial merge
+  float M0 = -INFINITY, M1 = -INFINITY;
+  for (int ch = 0; ch < Cf; ++ch) {
+    const float m = fml[(rf + ch) * 2];
+    M0 = fmaxf(M0, m);
+    if (in_window(ch)) M1 = fmaxf(M1, m);
+  }
+  const float M0r = M0 == -INFINITY ? 0.f : M0, M1r = M1 == -INFINITY ? 0.f : M1;
+  double L0 = 0.0, A0 = 0.0, L1 = 0.0, A1 = 0.0;
+  for (int ch = 0; ch < Cf; ++ch) {
+    const float m = fml[(rf + ch) * 2], l = fml[(rf + ch) * 2 + 1];
+    const float x = e < D ? fo[(rf + ch) * D + e] : 0.f;
+    const float w0 = fast_exp2((m - M0r) * c);
+    L0 += (double)w0 * l;
+    A0 += (double)w0 * x;
+    if (in_window(ch)) {
+      const float w1 = fast_exp2((m - M1r) * c);
+      L1 += (double)w1 * l;
+      A1 += (double)w1 * x;
     }
-    const int nchunks = m == 0 ? nch0 : nch12;
+  }
+  double out[3];
+  out[0] = L0 > 0.0 ? A0 / L0 : 0.0;
+  out[1] = L1 > 0.0 ? A1 / L1 : 0.0;
+  if (cover & 4) {
+    out[2] = out[0];
+  } else {
     float M = -INFINITY;
-    for (int ch = 0; ch < nchunks; ++ch)
-      M = fmaxf(M, part_ml[((((size_t)h * n_s + s) * C + ch) * 3 + m) * 2]);
+    for (int ch = 0; ch < Ct; ++ch) M = fmaxf(M, tml[(rt + ch) * 2]);
     const float Mr = M == -INFINITY ? 0.f : M;
     double L = 0.0, acc = 0.0;
-    for (int ch = 0; ch < nchunks; ++ch) {
-      const size_t slot = (((size_t)h * n_s + s) * C + ch) * 3 + m;
-      const float w = fast_exp2((part_ml[slot * 2] - Mr) * c);
-      L += (double)w * part_ml[slot * 2 + 1];
-      if (e < D) acc += (double)w * part_o[slot * D + e];
+    for (int ch = 0; ch < Ct; ++ch) {
+      const float w = fast_exp2((tml[(rt + ch) * 2] - Mr) * c);
+      L += (double)w * tml[(rt + ch) * 2 + 1];
+      if (e < D) acc += (double)w * to[(rt + ch) * D + e];
     }
-    out[m] = L > 0.0 ? acc / L : 0.0;
+    out[2] = L > 0.0 ? acc / L : 0.0;
   }
   const double ds = out[1] - out[0], dt = out[2] - out[0];
   red[0][e] = e < D ? ds * ds : 0.0;
@@ -537,52 +565,44 @@ void profile_label(const double *__restrict__ se, int n_s, int D, int32_t *__res
 }  // namespace
 
 size_t profile_mfma_ws_bytes(const Dims &dm, int n_s) {
-  const int C = max(profile_grid(dm, n_s).nchunks, profile_grid_full(dm, n_s).nchunks);
-  return align256((size_t)dm.H * n_s * C * 3 * dm.d * sizeof(float)) +
-         align256((size_t)dm.H * n_s * C * 3 * 2 * sizeof(float)) +
-         align256((size_t)dm.H * n_s * 2 * sizeof(double)) + 2 * align256((size_t)n_s * 4) + align256(vt_bytes(dm));
+  return carve(nullptr, dm, n_s, profile_grid_full(dm, n_s).nchunks, profile_grid(dm, n_s).nchunks).bytes;
 }
 
 hipError_t launch_profile_mfma(const Dims &dm, const void *Q, const void *K, const void *V,
                                const int32_t *sample_idx, int n_s, int ks, int wt, float scale, int32_t *labels,
                                float *mse, void *ws, hipStream_t st) {
   const float c = scale * kLog2e;
-  const ProfileGrid g = profile_grid(dm, n_s);        // masked passes
-  const ProfileGrid gf = profile_grid_full(dm, n_s);  // full pass
-  const int C = max(g.nchunks, gf.nchunks);
-  const Parts p = carve(ws, dm, n_s, C);
+  const ProfileGrid g = profile_grid(dm, n_s);       // temporal pass
+  const FrameGrid gf = profile_grid_full(dm, n_s);   // full pass
+  const Parts p = carve(ws, dm, n_s, gf.nchunks, g.nchunks);
   const int nkb = (dm.N + BK - 1) / BK;
-  const dim3 grid(g.nqg, g.nchunks, dm.H), gridf(gf.nqg, gf.nchunks, dm.H);
-  hipLaunchKernelGGL(profile_order, dim3((n_s + 255) / 256), dim3(256), 0, st, sample_idx, n_s, dm.F, dm.S,
-                     p.ord_s, p.ord_t);
-  // key-tiled V^T of V in its own token order, for the full pass
-  const hipError_t ev = launch_layout_vt(dm, V, p.vt, nullptr, st, true);
-  if (ev != hipSuccess) return ev;
-#define SVG_PROFILE_PASS(DD, KK)                                                                            \
-  hipLaunchKernelGGL((profile_pass_mfma<DD, KK>), grid, dim3(PNT), 0, st, (const bf16_t *)Q, (const bf16_t *)K, \
-                     (const bf16_t *)V, sample_idx, (KK) == 2 ? p.ord_t : p.ord_s, n_s, dm.F, dm.S, dm.N, ks, wt, \
-                     nkb, g.tiles_per_chunk, C, c, p.o, p.ml)
-#define SVG_PROFILE_FULL(DD)                                                                                  \
-  hipLaunchKernelGGL((profile_full_vt<DD>), gridf, dim3(FNT), 0, st, (const bf16_t *)Q, (const bf16_t *)K, p.vt, \
-                     sample_idx, n_s, dm.N, nkb, gf.tiles_per_chunk, C, c, p.o, p.ml)
   // A mask that keeps every key of every row: the spatial one when every
   // frame lies within ks of every other (ks >= F - 1), the temporal one when
   // the window of position 0 reaches the last video key and that of position
   // S - 1 the first (wt >= (S - 1) * F); text rows and keys are kept anyway.
   const int cover = ((ks >= dm.F - 1) ? 2 : 0) | (((long long)wt >= (long long)(dm.S - 1) * dm.F) ? 4 : 0);
+  hipLaunchKernelGGL(profile_order, dim3((n_s + 255) / 256), dim3(256), 0, st, sample_idx, n_s, dm.F, dm.S,
+                     p.ord_t);
+  // key-tiled V^T of V in its own token order, every frame from a new tile
+  const hipError_t ev = launch_layout_vt(dm, V, p.vt, nullptr, st, true);
+  if (ev != hipSuccess) return ev;
+  const dim3 gridf(gf.nqg * gf.nchunks * dm.H), grid(g.nqg, g.nchunks, dm.H);
+#define SVG_PROFILE_PASSES(DD)                                                                                   \
+  hipLaunchKernelGGL((profile_full_vt<DD>), gridf, dim3(FNT), 0, st, (const bf16_t *)Q, (const bf16_t *)K, p.vt, \
+                     sample_idx, n_s, dm.F, dm.S, dm.T, gf.nqg, gf.nbf, gf.nbt, gf.tpp, gf.P, gf.nchunks, c, p.fo, \
+                     p.fml);                                                                                     \
+  if (!(cover & 4))                                                                                             \
+    hipLaunchKernelGGL((profile_temporal_mfma<DD>), grid, dim3(PNT), 0, st, (const bf16_t *)Q, (const bf16_t *)K, \
+                       (const bf16_t *)V, sample_idx, p.ord_t, n_s, dm.F, dm.S, dm.N, wt, nkb, g.tiles_per_chunk,  \
+                       g.nchunks, c, p.to, p.tml)
   if (dm.d == 128) {
-    SVG_PROFILE_FULL(128);
-    if (!(cover & 2)) SVG_PROFILE_PASS(128, 1);
-    if (!(cover & 4)) SVG_PROFILE_PASS(128, 2);
+    SVG_PROFILE_PASSES(128);
   } else {
-    SVG_PROFILE_FULL(64);
-    if (!(cover & 2)) SVG_PROFILE_PASS(64, 1);
-    if (!(cover & 4)) SVG_PROFILE_PASS(64, 2);
+    SVG_PROFILE_PASSES(64);
   }
-#undef SVG_PROFILE_PASS
-#undef SVG_PROFILE_FULL
-  hipLaunchKernelGGL(profile_combine, dim3(n_s, dm.H), dim3(128), 0, st, p.o, p.ml, n_s, C, gf.nchunks, g.nchunks,
-                     cover, dm.d, c, p.se);
+#undef SVG_PROFILE_PASSES
+  hipLaunchKernelGGL(profile_combine, dim3(n_s, dm.H), dim3(128), 0, st, p.fo, p.fml, gf.nchunks, gf.P, p.to, p.tml,
+                     g.nchunks, sample_idx, n_s, dm.F, dm.S, ks, cover, dm.d, c, p.se);
   hipLaunchKernelGGL(profile_label, dim3(dm.H), dim3(256), 0, st, p.se, n_s, dm.d, labels, mse);
   return hipGetLastError();
 }

@@ -74,9 +74,13 @@ hipError_t launch_attn_vt(const Dims &dm, const void *Q, const void *K, const vo
                           const int32_t *row_ptr, const int32_t *kv_idx, int bq, int bk, float scale,
                           hipStream_t st, bool qo_orig = false, const int32_t *labels = nullptr);
 int attn_vt_max_kv_blocks();
-// identity: keep every head's token order (the key-tiled V^T of V as given)
+// frames: keep every head's token order, each frame and the text starting a
+// new 64-key tile (vt_frame_tiles(dm) tiles a head, zero past each end)
 hipError_t launch_layout_vt(const Dims &dm, const void *V, void *Vt, const int32_t *labels, hipStream_t st,
-                            bool identity = false);
+                            bool frames = false);
+inline int vt_frame_tiles(const Dims &dm) {
+  return dm.F * ((dm.S + 63) / 64) + (dm.T + 63) / 64;
+}
 hipError_t launch_layout(const Dims &dm, int elem_bytes, const void *X, void *Y,
                          const int32_t *labels, bool inverse, hipStream_t st);
 hipError_t launch_permute_rows(const Dims &dm, int elem_bytes, const void *X, const int32_t *perm,
