@@ -484,10 +484,12 @@ void profile_combine(const float *__restrict__ fo, const float *__restrict__ fml
     if (in_window(ch)) M1 = fmaxf(M1, m);
   }
   const float M0r = M0 == -INFINITY ? 0.f : M0, M1r = M1 == -INFINITY ? 0.f : M1;
+  // The merges run in chunk order; the loads of kB chunks go out together
+  // (one chunk at a time leaves the loop waiting on memory).
+  constexpr int kB = 8;
+  const int De = e < D ? e : 0;
   double L0 = 0.0, A0 = 0.0, L1 = 0.0, A1 = 0.0;
-  for (int ch = 0; ch < Cf; ++ch) {
-    const float m = fml[(rf + ch) * 2], l = fml[(rf + ch) * 2 + 1];
-    const float x = e < D ? fo[(rf + ch) * D + e] : 0.f;
+  auto add_full = [&](int ch, float m, float l, float x) {
     const float w0 = fast_exp2((m - M0r) * c);
     L0 += (double)w0 * l;
     A0 += (double)w0 * x;
@@ -496,7 +498,20 @@ void profile_combine(const float *__restrict__ fo, const float *__restrict__ fml
       L1 += (double)w1 * l;
       A1 += (double)w1 * x;
     }
+  };
+  int ch = 0;
+  for (; ch + kB <= Cf; ch += kB) {
+    float m[kB], l[kB], x[kB];
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      m[u] = fml[(rf + ch + u) * 2];
+      l[u] = fml[(rf + ch + u) * 2 + 1];
+      x[u] = fo[(rf + ch + u) * D + De];
+    }
+#pragma unroll
+    for (int u = 0; u < kB; ++u) add_full(ch + u, m[u], l[u], x[u]);
   }
+  for (; ch < Cf; ++ch) add_full(ch, fml[(rf + ch) * 2], fml[(rf + ch) * 2 + 1], fo[(rf + ch) * D + De]);
   double out[3];
   out[0] = L0 > 0.0 ? A0 / L0 : 0.0;
   out[1] = L1 > 0.0 ? A1 / L1 : 0.0;
@@ -507,11 +522,24 @@ void profile_combine(const float *__restrict__ fo, const float *__restrict__ fml
     for (int ch = 0; ch < Ct; ++ch) M = fmaxf(M, tml[(rt + ch) * 2]);
     const float Mr = M == -INFINITY ? 0.f : M;
     double L = 0.0, acc = 0.0;
-    for (int ch = 0; ch < Ct; ++ch) {
-      const float w = fast_exp2((tml[(rt + ch) * 2] - Mr) * c);
-      L += (double)w * tml[(rt + ch) * 2 + 1];
-      if (e < D) acc += (double)w * to[(rt + ch) * D + e];
+    auto add = [&](float m, float l, float x) {
+      const float w = fast_exp2((m - Mr) * c);
+      L += (double)w * l;
+      acc += (double)w * x;
+    };
+    int ct = 0;
+    for (; ct + kB <= Ct; ct += kB) {
+      float m[kB], l[kB], x[kB];
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        m[u] = tml[(rt + ct + u) * 2];
+        l[u] = tml[(rt + ct + u) * 2 + 1];
+        x[u] = to[(rt + ct + u) * D + De];
+      }
+#pragma unroll
+      for (int u = 0; u < kB; ++u) add(m[u], l[u], x[u]);
     }
+    for (; ct < Ct; ++ct) add(tml[(rt + ct) * 2], tml[(rt + ct) * 2 + 1], to[(rt + ct) * D + De]);
     out[2] = L > 0.0 ? acc / L : 0.0;
   }
   const double ds = out[1] - out[0], dt = out[2] - out[0];
