@@ -38,8 +38,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--density", default="k5", help="mask widths: k5 (31%%), k4 (26%%), cog_rule (~2%%)")
-    ap.add_argument("--workload", default="hunyuan_layer", choices=["hunyuan_layer", "svg2"],
+    ap.add_argument("--workload", default="hunyuan_layer", choices=["hunyuan_layer", "cogvideox_shape", "svg2"],
                     help="hunyuan_layer: the SVG1 layer step (default, the headline line); "
+                         "cogvideox_shape: the same step at the CogVideoX shape (13 x 1350 + 224 tokens, "
+                         "8 heads, d = 64, 64x64 tiles, its own mask rule; --density is ignored); "
                          "svg2: the SVG2 semantic path on the CogVideoX-shaped mixture workload")
     ap.add_argument("--pmc-target", action="store_true",
                     help="launch the block-sparse attention kernel once and a plain 1.46 GB copy "
@@ -315,11 +317,16 @@ def main():
     import numpy as np
     import torch
     from sparse_attention_video_online_amd import svg
-    from synth import HUNYUAN_LAYER as w
+    from synth import COG, HUNYUAN_LAYER
     from synth.configs import HUNYUAN_DENSITY_POINTS
     from synth.generators import sample_rows
 
-    ks, wt = HUNYUAN_DENSITY_POINTS[args.density]
+    if args.workload == "cogvideox_shape":
+        w = COG
+        ks, wt = w.ks, w.wt
+    else:
+        w = HUNYUAN_LAYER
+        ks, wt = HUNYUAN_DENSITY_POINTS[args.density]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     host = gen_inputs(w)
@@ -460,7 +467,7 @@ def main():
 
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
     result = {
-        "metric": "effective block-sparse attn TFLOP/s (whole SVG1 layer step) + speedup vs dense, N=119,056",
+        "metric": f"effective block-sparse attn TFLOP/s (whole SVG1 layer step) + speedup vs dense, N={N:,}",
         "value": round(flops / (ms_per_step * 1e-3) / 1e12, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -486,10 +493,11 @@ def main():
         "speedup_vs_dense_layer": round(dense_ms / ms_per_step, 3),
         "stage_ms": {kk: round(vv, 4) for kk, vv in stage_ms.items()},
         "roofline": {"bound": "mfma",
-                     "kernel": ("attn_fwd_vt<128,128>" if use_vt else "attn_fwd_mfma<128,128>") + " (block-sparse)",
+                     "kernel": (f"attn_fwd_vt<{d},{bq}>" if use_vt else f"attn_fwd_mfma<{d},{bq}>") + " (block-sparse)",
                      "achieved": round(attn_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic() if (args.density == "k5" and use_vt) else None,
+                     "traffic": (measured_traffic() if (w is HUNYUAN_LAYER and args.density == "k5" and use_vt)
+                                 else None),
                      "flop_per_launch": flops},
     }
     if not args.no_cpu_baseline:

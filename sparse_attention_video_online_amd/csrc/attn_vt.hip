@@ -28,7 +28,17 @@
 // S^T's rows (keys) are read from K in the order pi = swap of key groups
 // 4-7 and 8-11 in every 16, so the accumulator lane layout of S^T is the
 // MFMA B-operand layout of P^T with keys in natural order.
+//
+// The last 512 query rows of a head (the text rows, which keep every
+// kv-block, so their groups carry the longest lists) can be split by keys:
+// nsplit work-groups per such group each take a contiguous part of its union
+// list and store an unnormalised partial (O, reference maximum, row sum);
+// attn_vt_merge then combines the parts flash-decoding style.  Otherwise a
+// small head count leaves the whole launch waiting on these groups.
+#include <map>
+#include <mutex>
 #include <type_traits>
+#include <utility>
 
 #include "attn_vt_core.h"
 
@@ -40,12 +50,17 @@ using namespace core;
 constexpr int kWgRows = 256;     // query rows per work-group
 constexpr int kNW = 8;           // waves per work-group
 
+// Row stride (floats) of a partial: O, then the maximum and the sum, padded
+// so every row starts 16-byte aligned.
+template <int D> constexpr int kPartStride = D + 4;
+
 template <int D, int BQ, bool DENSE>
 __global__ __launch_bounds__(kWgRows * 2, 1)
 void attn_fwd_vt(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K, const bf16_t *__restrict__ Vt,
                  bf16_t *__restrict__ O, const int32_t *__restrict__ row_ptr,
                  const int32_t *__restrict__ kv_idx, int N, int nqb, int nkb, int ngrp,
-                 float c /* scale * log2(e) */, const int32_t *__restrict__ labels, int qo_orig, int F, int S) {
+                 float c /* scale * log2(e) */, const int32_t *__restrict__ labels, int qo_orig, int F, int S,
+                 int nsplit, float *__restrict__ part) {
   constexpr int G = kWgRows / BQ;          // q-blocks per work-group
   using T = DTile<D>;
   constexpr int TB = T::TBYTES;            // K tile bytes == V^T tile bytes
@@ -68,10 +83,16 @@ void attn_fwd_vt(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K, con
   // the head, so that no XCD ends on one of them.  The other groups follow
   // in ascending order, so neighbours that share kv-blocks run together and
   // hit in L2 (reversing the whole order instead doubles the HBM fetch).
+  // With nsplit > 1 each of the nlead leading groups is nsplit work items.
   const int work = xcd_remap(blockIdx.x, gridDim.x);
-  const int h = work / ngrp, local = work - h * ngrp;
   const int nlead = min(ngrp, 512 / kWgRows);
-  const int grp = local < nlead ? ngrp - 1 - local : local - nlead;
+  const int per_head = ngrp + nlead * (nsplit - 1);
+  const int h = work / per_head, local = work - h * per_head;
+  const bool lead = local < nlead * nsplit;
+  const int lg = lead ? local / nsplit : 0;          // leading group, 0 = the last group
+  const int split = lead ? local - lg * nsplit : 0;
+  const int grp = lead ? ngrp - 1 - lg : local - nlead * nsplit;
+  const bool parted = lead && nsplit > 1;           // stores a partial for attn_vt_merge
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
@@ -94,7 +115,25 @@ void attn_fwd_vt(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K, con
   if constexpr (!DENSE)
     nt = build_union_list<G, kWgRows * 2>(row_ptr, kv_idx, h, grp, nqb, nkb, tid, lane, wave, ulist, bits, wsum);
 
-  if (nt == 0) {  // no kept tile in the whole group: O = 0
+  // this work item's part of the union list: entries j0 .. j0 + ntile - 1
+  const int j0 = parted ? split * nt / nsplit : 0;
+  const int ntile = parted ? (split + 1) * nt / nsplit - j0 : nt;
+  // partial slot of this row: O (D floats), then the maximum and the sum
+  float *const prow = parted ? part + ((((size_t)h * nlead + lg) * nsplit + split) * kWgRows + wave * 32 + l32) *
+                                          kPartStride<D>
+                             : nullptr;
+
+  if (ntile == 0) {  // no kept tile in the whole group (or this part): O = 0
+    if (parted) {
+      for (int dd = hi * 8; dd < D; dd += 16)
+#pragma unroll
+        for (int u = 0; u < 8; ++u) prow[dd + u] = 0.f;
+      if (hi == 0) {
+        prow[D] = -INFINITY;
+        prow[D + 1] = 0.f;
+      }
+      return;
+    }
     if (qrow < N) {
 #pragma unroll
       for (int dd = hi * 8; dd < D; dd += 16)
@@ -108,7 +147,7 @@ void attn_fwd_vt(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K, con
   // read and the move to a scalar register are separate so a step can issue
   // the read early and take the value late.
   auto ent_raw = [&](int j) -> int {
-    const int i = j < nt ? j : nt - 1;
+    const int i = j0 + (j < ntile ? j : ntile - 1);
     if constexpr (DENSE) return i | (OWN_ALL << 24);
     else return ulist[i];
   };
@@ -133,9 +172,86 @@ void attn_fwd_vt(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K, con
     }
     return own;
   };
-  vt_attend<D, kNW>(nt, ent_raw, prep, Kh, Vth, N, k0, k1, k2, V0, V1, V2, qf, wave, lane, c, o, m_run, l_run);
+  vt_attend<D, kNW>(ntile, ent_raw, prep, Kh, Vth, N, k0, k1, k2, V0, V1, V2, qf, wave, lane, c, o, m_run,
+                    l_run);
   __builtin_amdgcn_s_waitcnt(0);  // no DMA may land after the work-group ends
+  if (parted) {
+    const float lt = l_run + __shfl_xor(l_run, 32);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<f32x4 *>(prow + 32 * db + 8 * g + 4 * hi) =
+            f32x4{o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]};
+    if (hi == 0) {
+      prow[D] = m_run;
+      prow[D + 1] = lt;
+    }
+    return;
+  }
   store_o<D>(qrow < N ? Oh + (size_t)qsrc * D : nullptr, o, l_run, hi);
+}
+
+// Combine the nsplit partials of each row of the leading groups:
+// O = sum_s w_s O_s / sum_s w_s l_s with w_s = exp2((m_s - M) c), M the
+// largest m_s; rows with no kept key get O = 0.  One work-group per row.
+template <int D>
+__global__ __launch_bounds__(D)
+void attn_vt_merge(const float *__restrict__ part, bf16_t *__restrict__ O, int N, int ngrp, int nlead, int nsplit,
+                   float c, const int32_t *__restrict__ labels, int qo_orig, int F, int S) {
+  const int r = blockIdx.x, lg = blockIdx.y, h = blockIdx.z, e = threadIdx.x;
+  const int qrow = (ngrp - 1 - lg) * kWgRows + r;
+  if (qrow >= N) return;
+  int qsrc = qrow;
+  if (qo_orig && (labels == nullptr || labels[h] == 1) && qrow < F * S) {
+    const int p = qrow / F, f = qrow - p * F;
+    qsrc = f * S + p;
+  }
+  const float *base = part + (((size_t)h * nlead + lg) * nsplit * kWgRows + r) * kPartStride<D>;
+  const size_t stride = (size_t)kWgRows * kPartStride<D>;   // between the parts of one row
+  float M = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, base[s * stride + D]);
+  float acc = 0.f, L = 0.f;
+  if (M != -INFINITY) {
+    for (int s = 0; s < nsplit; ++s) {
+      const float *ps = base + s * stride;
+      const float w = fast_exp2((ps[D] - M) * c);
+      L += w * ps[D + 1];
+      acc += w * ps[e];
+    }
+  }
+  O[((size_t)h * N + qsrc) * D + e] = f32_to_bf16(L > 0.f ? acc / L : 0.f);
+}
+
+// Partial buffers for the split groups, one per (device, stream), grown on
+// demand and kept: a call enqueues its kernels on its stream, so calls on
+// one stream never overlap and calls on different streams use different
+// buffers.
+std::mutex g_part_mu;
+std::map<std::pair<int, hipStream_t>, std::pair<void *, size_t>> g_part;
+
+hipError_t part_buffer(hipStream_t st, size_t bytes, float **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(g_part_mu);
+  auto &slot = g_part[{dev, st}];
+  if (slot.second < bytes) {
+    if (slot.first != nullptr) {
+      // earlier launches on this stream may still read the old buffer
+      e = hipStreamSynchronize(st);
+      if (e != hipSuccess) return e;
+      e = hipFree(slot.first);
+      if (e != hipSuccess) return e;
+      slot = {nullptr, 0};
+    }
+    void *p = nullptr;
+    e = hipMalloc(&p, bytes);
+    if (e != hipSuccess) return e;
+    slot = {p, bytes};
+  }
+  *out = static_cast<float *>(slot.first);
+  return hipSuccess;
 }
 
 template <int D, int BQ>
@@ -145,16 +261,30 @@ hipError_t launch_vt(const Dims &dm, const void *Q, const void *K, const void *V
   constexpr int G = kWgRows / BQ;
   const int nqb = (dm.N + BQ - 1) / BQ, nkb = (dm.N + BK - 1) / BK;
   const int ngrp = (nqb + G - 1) / G;
-  const int grid = dm.H * ngrp;
-  if (grid == 0) return hipSuccess;
+  if (dm.H * ngrp == 0) return hipSuccess;
+  const int nlead = min(ngrp, 512 / kWgRows);
+  // The leading (text) groups of a sparse launch keep every kv-block: split
+  // them into parts of about 48 tiles (at most 16), near a typical group's
+  // list.  Dense launches give every group the same list: no split.
+  const int nsplit = row_ptr == nullptr ? 1 : max(1, min(16, (nkb + 47) / 48));
+  float *part = nullptr;
+  if (nsplit > 1) {
+    const hipError_t e =
+        part_buffer(st, (size_t)dm.H * nlead * nsplit * kWgRows * kPartStride<D> * sizeof(float), &part);
+    if (e != hipSuccess) return e;
+  }
+  const int grid = dm.H * (ngrp + nlead * (nsplit - 1));
   if (row_ptr == nullptr)
     hipLaunchKernelGGL((attn_fwd_vt<D, BQ, true>), dim3(grid), dim3(kWgRows * 2), 0, st, (const bf16_t *)Q,
                        (const bf16_t *)K, (const bf16_t *)Vt, (bf16_t *)O, row_ptr, kv_idx, dm.N, nqb, nkb, ngrp,
-                       c, labels, qo_orig, dm.F, dm.S);
+                       c, labels, qo_orig, dm.F, dm.S, nsplit, part);
   else
     hipLaunchKernelGGL((attn_fwd_vt<D, BQ, false>), dim3(grid), dim3(kWgRows * 2), 0, st, (const bf16_t *)Q,
                        (const bf16_t *)K, (const bf16_t *)Vt, (bf16_t *)O, row_ptr, kv_idx, dm.N, nqb, nkb, ngrp,
-                       c, labels, qo_orig, dm.F, dm.S);
+                       c, labels, qo_orig, dm.F, dm.S, nsplit, part);
+  if (nsplit > 1)
+    hipLaunchKernelGGL((attn_vt_merge<D>), dim3(kWgRows, nlead, dm.H), dim3(D), 0, st, part, (bf16_t *)O, dm.N,
+                       ngrp, nlead, nsplit, c, labels, qo_orig, dm.F, dm.S);
   return hipGetLastError();
 }
 

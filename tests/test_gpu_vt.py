@@ -209,6 +209,42 @@ def test_attention_vt_random_bitmap_ragged(N, d, bq):
             assert np.all(got[h][:min(bq, N)] == 0.0)
 
 
+@pytest.mark.parametrize("keep_last,d,bq", [(0, 128, 128), (1, 128, 128), (3, 64, 64), (40, 128, 64)])
+def test_attention_vt_split_leading_groups(keep_last, d, bq):
+    """Above 48 kv-blocks the groups of the last 512 query rows are split by
+    keys over several work-groups and merged.  Here those rows keep exactly
+    keep_last kv-blocks (the same for each of their q-blocks), so some parts
+    get no tile at all (keep_last < number of parts), or every part a few."""
+    H, bk = 2, 64
+    N = 64 * 150 + 17                          # 151 kv-blocks: four parts
+    q, k, v = random_qkv(H, N, d, seed=keep_last + d, dtype="bf16", scale=1.5)
+    nqb, nkb = -(-N // bq), -(-N // bk)
+    rng = np.random.default_rng(keep_last + 11)
+    bm = (rng.random((H, nqb, nkb)) < 0.3).astype(np.uint8)
+    G = 256 // bq
+    ngrp = -(-nqb // G)
+    lead_qb = list(range(max(0, (ngrp - 2) * G), nqb))   # q-blocks of the last two groups
+    bm[:, lead_qb, :] = 0
+    if keep_last:
+        cols = np.sort(rng.choice(nkb - 1, size=keep_last - 1, replace=False)).tolist() + [nkb - 1]
+        for h in range(H):
+            for qb in lead_qb:
+                bm[h, qb, cols] = 1
+    row_ptr, kv_idx = csr(bm)
+    vt = svg.svg_layout_permute_vt(to_dev(v, "bf16"), 1, N, 0, None)
+    o = svg.svg_block_sparse_attn_csr_vt(to_dev(q, "bf16"), to_dev(k, "bf16"), vt, row_ptr, kv_idx,
+                                         1, N, 0, bq, bk)
+    sync()
+    got = to_f64(o)
+    lead_rows = slice(lead_qb[0] * bq, N)
+    for h in range(H):
+        ref = attention.block_sparse_attention_full(as_f64(q[h], "bf16"), as_f64(k[h], "bf16"),
+                                                    as_f64(v[h], "bf16"), bm[h], bq, bk)
+        check_close(got[h], ref, BF16_MAX_ABS, BF16_REL_L2, f"split leading groups head {h}")
+        if keep_last == 0:
+            assert np.all(got[h][lead_rows] == 0.0)
+
+
 def test_attention_vt_whole_group_empty():
     """Every q-block of some work-groups keeps nothing: those rows are zero."""
     H, N, d, bq, bk = 1, 1000, 128, 128, 64
