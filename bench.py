@@ -350,6 +350,7 @@ def main():
     qp, kp, vp, op, o = (torch.empty_like(q) for _ in range(5))
     use_vt = args.v_layout == "vt"
     vt = torch.empty(svg.svg_vt_elems(H, N, d), dtype=q.dtype, device=dev) if use_vt else None
+    attn_ws = svg.attn_vt_workspace(q, F, S, T, bq, bk) if use_vt else None
     stream = torch.cuda.current_stream()
     ev_a0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ev_a1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
@@ -358,7 +359,8 @@ def main():
         if use_vt:
             # Q read and O written in the original token order (the Q permute
             # and the O unpermute happen in the kernel's row indexing)
-            svg.svg_block_sparse_attn_csr_vt_layout(q, kp, vt, row_ptr, kv_idx, labels, F, S, T, bq, bk, out=o)
+            svg.svg_block_sparse_attn_csr_vt_layout(q, kp, vt, row_ptr, kv_idx, labels, F, S, T, bq, bk, out=o,
+                                                    ws=attn_ws)
         else:
             svg.svg_block_sparse_attn_csr(qp, kp, vp, row_ptr, kv_idx, F, S, T, bq, bk, out=op)
 

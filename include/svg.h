@@ -85,7 +85,8 @@ typedef struct { int32_t ks_frames, wt_tokens; } svg_mask_params;
 typedef enum {
   SVG_OP_PROFILE = 0,        /* a = n_samples                                  */
   SVG_OP_BLOCK_SPARSE = 1,   /* a = bq, b = bk  (bitmap -> CSR inside ws)      */
-  SVG_OP_COMPACT = 2         /* a = rows, b = nKB                              */
+  SVG_OP_COMPACT = 2,        /* a = rows, b = nKB                              */
+  SVG_OP_ATTN_VT = 3         /* a = bq, b = bk  (split text groups, may be 0)  */
 } svg_op;
 
 /* Bytes of workspace an op needs for these sizes (host-only, no HIP call). */
@@ -229,6 +230,16 @@ svg_status svg_dense_attn(const svg_dims *dims, svg_dtype dtype,
  *   temporal head from frame-major row f*S + p and writes O back there.
  *   Same limits and errors as svg_block_sparse_attn_csr_vt; labels is a
  *   device pointer, int32[H], read on the device.
+ * ws, ws_bytes (the two sparse entries): the groups of 256 query rows that
+ *   hold a head's last 512 rows (its text rows, which keep every kv-block)
+ *   are split by keys over several work-groups when nKB > 48: each part
+ *   stores an unnormalised partial (O, maximum, row sum) in ws and a merge
+ *   combines them (the flash-decoding split of the same softmax).  ws is
+ *   caller-owned device memory of svg_workspace_bytes(SVG_OP_ATTN_VT, dims,
+ *   bq, bk) bytes (0 when no split applies), or NULL: then no group is split
+ *   and only the fp32 summation order differs.  A non-NULL ws smaller than
+ *   that is SVG_ERR_WORKSPACE; ws must not overlap the other buffers.  Calls
+ *   that share one ws must not overlap in time.
  * ------------------------------------------------------------------------- */
 size_t svg_vt_elems(const svg_dims *dims);
 svg_status svg_layout_permute_vt(const svg_dims *dims, svg_dtype dtype, const void *V, void *Vt,
@@ -237,12 +248,13 @@ svg_status svg_block_sparse_attn_csr_vt(const svg_dims *dims, svg_dtype dtype,
                                         const void *Q, const void *K, const void *Vt,
                                         const int32_t *row_ptr, const int32_t *kv_idx,
                                         int32_t bq, int32_t bk, float softmax_scale,
-                                        void *O, void *stream);
+                                        void *O, void *ws, size_t ws_bytes, void *stream);
 svg_status svg_block_sparse_attn_csr_vt_layout(const svg_dims *dims, svg_dtype dtype,
                                                const void *Q, const void *K, const void *Vt,
                                                const int32_t *row_ptr, const int32_t *kv_idx,
                                                const int32_t *labels, int32_t bq, int32_t bk,
-                                               float softmax_scale, void *O, void *stream);
+                                               float softmax_scale, void *O, void *ws,
+                                               size_t ws_bytes, void *stream);
 svg_status svg_dense_attn_vt(const svg_dims *dims, svg_dtype dtype,
                              const void *Q, const void *K, const void *Vt,
                              int32_t bq, int32_t bk, float softmax_scale,

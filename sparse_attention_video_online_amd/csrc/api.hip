@@ -110,6 +110,9 @@ size_t svg_workspace_bytes(svg_op op, const svg_dims *dims, int32_t a, int32_t b
     case SVG_OP_BLOCK_SPARSE:
       if (check_dims(dims, &dm) != SVG_OK || check_blocks(a, b) != SVG_OK) return 0;
       return block_sparse_ws(dm, a, b);
+    case SVG_OP_ATTN_VT:
+      if (check_dims(dims, &dm) != SVG_OK) return 0;
+      return svgk::attn_vt_ws_bytes(dm, a, b);
   }
   return 0;
 }
@@ -292,29 +295,50 @@ static svg_status vt_checks(const svg_dims *dims, svg_dtype dtype, const void *Q
   return SVG_OK;
 }
 
+// The split-partials workspace of the sparse V^T entries: NULL (no split),
+// or at least attn_vt_ws_bytes and clear of the tensors.
+static svg_status attn_ws_check(const Dims &dm, int bq, int bk, const void *Q, const void *K, const void *Vt,
+                                const void *O, const void *ws, size_t ws_bytes) {
+  if (ws == nullptr) return SVG_OK;
+  const size_t need = svgk::attn_vt_ws_bytes(dm, bq, bk);
+  if (ws_bytes < need) return fail(SVG_ERR_WORKSPACE, "attention: workspace %zu < %zu bytes", ws_bytes, need);
+  const size_t bytes = (size_t)dm.H * dm.N * dm.d * 2;
+  const size_t tbytes = (size_t)dm.H * ((dm.N + 63) / 64) * 64 * dm.d * 2;
+  if (need > 0 && (overlaps2(ws, need, Q, bytes) || overlaps2(ws, need, K, bytes) ||
+                   overlaps2(ws, need, O, bytes) || overlaps2(ws, need, Vt, tbytes)))
+    return fail(SVG_ERR_RANGE, "attention: workspace overlaps a tensor");
+  return SVG_OK;
+}
+
 svg_status svg_block_sparse_attn_csr_vt(const svg_dims *dims, svg_dtype dtype, const void *Q,
                                         const void *K, const void *Vt, const int32_t *row_ptr,
                                         const int32_t *kv_idx, int32_t bq, int32_t bk,
-                                        float softmax_scale, void *O, void *stream) {
+                                        float softmax_scale, void *O, void *ws, size_t ws_bytes,
+                                        void *stream) {
   Dims dm{};
   svg_status s;
   if ((s = vt_checks(dims, dtype, Q, K, Vt, O, bq, bk, &dm)) != SVG_OK) return s;
   if (!row_ptr || !kv_idx) return fail(SVG_ERR_NULL, "block_sparse_attn_csr_vt: NULL list");
+  if ((s = attn_ws_check(dm, bq, bk, Q, K, Vt, O, ws, ws_bytes)) != SVG_OK) return s;
   return hip_status(svgk::launch_attn_vt(dm, Q, K, Vt, O, row_ptr, kv_idx, bq, bk,
-                                         resolve_scale(softmax_scale, dm.d), (hipStream_t)stream),
+                                         resolve_scale(softmax_scale, dm.d), (hipStream_t)stream, false,
+                                         nullptr, ws),
                     "svg_block_sparse_attn_csr_vt");
 }
 
 svg_status svg_block_sparse_attn_csr_vt_layout(const svg_dims *dims, svg_dtype dtype, const void *Q,
                                                const void *K, const void *Vt, const int32_t *row_ptr,
                                                const int32_t *kv_idx, const int32_t *labels, int32_t bq,
-                                               int32_t bk, float softmax_scale, void *O, void *stream) {
+                                               int32_t bk, float softmax_scale, void *O, void *ws,
+                                               size_t ws_bytes, void *stream) {
   Dims dm{};
   svg_status s;
   if ((s = vt_checks(dims, dtype, Q, K, Vt, O, bq, bk, &dm)) != SVG_OK) return s;
   if (!row_ptr || !kv_idx) return fail(SVG_ERR_NULL, "block_sparse_attn_csr_vt_layout: NULL list");
+  if ((s = attn_ws_check(dm, bq, bk, Q, K, Vt, O, ws, ws_bytes)) != SVG_OK) return s;
   return hip_status(svgk::launch_attn_vt(dm, Q, K, Vt, O, row_ptr, kv_idx, bq, bk,
-                                         resolve_scale(softmax_scale, dm.d), (hipStream_t)stream, true, labels),
+                                         resolve_scale(softmax_scale, dm.d), (hipStream_t)stream, true, labels,
+                                         ws),
                     "svg_block_sparse_attn_csr_vt_layout");
 }
 

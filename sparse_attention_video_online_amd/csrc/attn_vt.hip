@@ -32,13 +32,11 @@
 // The last 512 query rows of a head (the text rows, which keep every
 // kv-block, so their groups carry the longest lists) can be split by keys:
 // nsplit work-groups per such group each take a contiguous part of its union
-// list and store an unnormalised partial (O, reference maximum, row sum);
-// attn_vt_merge then combines the parts flash-decoding style.  Otherwise a
-// small head count leaves the whole launch waiting on these groups.
-#include <map>
-#include <mutex>
+// list and store an unnormalised partial (O, reference maximum, row sum) in
+// the caller's workspace; attn_vt_merge then combines the parts
+// flash-decoding style.  Otherwise a small head count leaves the whole
+// launch waiting on these groups.
 #include <type_traits>
-#include <utility>
 
 #include "attn_vt_core.h"
 
@@ -223,56 +221,23 @@ void attn_vt_merge(const float *__restrict__ part, bf16_t *__restrict__ O, int N
   O[((size_t)h * N + qsrc) * D + e] = f32_to_bf16(L > 0.f ? acc / L : 0.f);
 }
 
-// Partial buffers for the split groups, one per (device, stream), grown on
-// demand and kept: a call enqueues its kernels on its stream, so calls on
-// one stream never overlap and calls on different streams use different
-// buffers.
-std::mutex g_part_mu;
-std::map<std::pair<int, hipStream_t>, std::pair<void *, size_t>> g_part;
-
-hipError_t part_buffer(hipStream_t st, size_t bytes, float **out) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  std::lock_guard<std::mutex> lock(g_part_mu);
-  auto &slot = g_part[{dev, st}];
-  if (slot.second < bytes) {
-    if (slot.first != nullptr) {
-      // earlier launches on this stream may still read the old buffer
-      e = hipStreamSynchronize(st);
-      if (e != hipSuccess) return e;
-      e = hipFree(slot.first);
-      if (e != hipSuccess) return e;
-      slot = {nullptr, 0};
-    }
-    void *p = nullptr;
-    e = hipMalloc(&p, bytes);
-    if (e != hipSuccess) return e;
-    slot = {p, bytes};
-  }
-  *out = static_cast<float *>(slot.first);
-  return hipSuccess;
-}
+// Parts per leading group of a sparse launch: about 48 tiles each (near a
+// typical group's list), at most 16; none above 48 kv-blocks or for a dense
+// launch (every group has the same list).
+int attn_vt_nsplit(int nkb, bool dense) { return dense ? 1 : max(1, min(16, (nkb + 47) / 48)); }
 
 template <int D, int BQ>
 hipError_t launch_vt(const Dims &dm, const void *Q, const void *K, const void *Vt, void *O,
                      const int32_t *row_ptr, const int32_t *kv_idx, float c, const int32_t *labels, int qo_orig,
-                     hipStream_t st) {
+                     float *part, hipStream_t st) {
   constexpr int G = kWgRows / BQ;
   const int nqb = (dm.N + BQ - 1) / BQ, nkb = (dm.N + BK - 1) / BK;
   const int ngrp = (nqb + G - 1) / G;
   if (dm.H * ngrp == 0) return hipSuccess;
   const int nlead = min(ngrp, 512 / kWgRows);
-  // The leading (text) groups of a sparse launch keep every kv-block: split
-  // them into parts of about 48 tiles (at most 16), near a typical group's
-  // list.  Dense launches give every group the same list: no split.
-  const int nsplit = row_ptr == nullptr ? 1 : max(1, min(16, (nkb + 47) / 48));
-  float *part = nullptr;
-  if (nsplit > 1) {
-    const hipError_t e =
-        part_buffer(st, (size_t)dm.H * nlead * nsplit * kWgRows * kPartStride<D> * sizeof(float), &part);
-    if (e != hipSuccess) return e;
-  }
+  // The leading (text) groups keep every kv-block: split them by keys when
+  // the caller gives the partials' workspace.
+  const int nsplit = part == nullptr ? 1 : attn_vt_nsplit(nkb, row_ptr == nullptr);
   const int grid = dm.H * (ngrp + nlead * (nsplit - 1));
   if (row_ptr == nullptr)
     hipLaunchKernelGGL((attn_fwd_vt<D, BQ, true>), dim3(grid), dim3(kWgRows * 2), 0, st, (const bf16_t *)Q,
@@ -292,16 +257,30 @@ hipError_t launch_vt(const Dims &dm, const void *Q, const void *K, const void *V
 
 int attn_vt_max_kv_blocks() { return kMaxKb; }
 
+size_t attn_vt_ws_bytes(const Dims &dm, int bq, int bk) {
+  if (bk != BK || (bq != 64 && bq != 128) || dm.N < 1 || dm.H < 1 || (dm.d != 64 && dm.d != 128)) return 0;
+  const int nkb = (dm.N + BK - 1) / BK, nsplit = attn_vt_nsplit(nkb, false);
+  if (nsplit == 1) return 0;
+  const int ngrp = ((dm.N + bq - 1) / bq + kWgRows / bq - 1) / (kWgRows / bq);
+  const int nlead = min(ngrp, 512 / kWgRows);
+  return (size_t)dm.H * nlead * nsplit * kWgRows * (dm.d + 4) * sizeof(float);
+}
+
 hipError_t launch_attn_vt(const Dims &dm, const void *Q, const void *K, const void *Vt, void *O,
                           const int32_t *row_ptr, const int32_t *kv_idx, int bq, int bk, float scale,
-                          hipStream_t st, bool qo_orig, const int32_t *labels) {
+                          hipStream_t st, bool qo_orig, const int32_t *labels, void *ws) {
   const float c = scale * kLog2e;
   const int qo = qo_orig ? 1 : 0;
+  float *const part = static_cast<float *>(ws);
   if (bk != BK) return hipErrorInvalidValue;
-  if (dm.d == 128 && bq == 128) return launch_vt<128, 128>(dm, Q, K, Vt, O, row_ptr, kv_idx, c, labels, qo, st);
-  if (dm.d == 128 && bq == 64) return launch_vt<128, 64>(dm, Q, K, Vt, O, row_ptr, kv_idx, c, labels, qo, st);
-  if (dm.d == 64 && bq == 128) return launch_vt<64, 128>(dm, Q, K, Vt, O, row_ptr, kv_idx, c, labels, qo, st);
-  if (dm.d == 64 && bq == 64) return launch_vt<64, 64>(dm, Q, K, Vt, O, row_ptr, kv_idx, c, labels, qo, st);
+  if (dm.d == 128 && bq == 128)
+    return launch_vt<128, 128>(dm, Q, K, Vt, O, row_ptr, kv_idx, c, labels, qo, part, st);
+  if (dm.d == 128 && bq == 64)
+    return launch_vt<128, 64>(dm, Q, K, Vt, O, row_ptr, kv_idx, c, labels, qo, part, st);
+  if (dm.d == 64 && bq == 128)
+    return launch_vt<64, 128>(dm, Q, K, Vt, O, row_ptr, kv_idx, c, labels, qo, part, st);
+  if (dm.d == 64 && bq == 64)
+    return launch_vt<64, 64>(dm, Q, K, Vt, O, row_ptr, kv_idx, c, labels, qo, part, st);
   return hipErrorInvalidValue;
 }
 

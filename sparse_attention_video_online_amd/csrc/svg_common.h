@@ -72,7 +72,10 @@ hipError_t launch_attn_simt(const Dims &dm, bool bf16, const void *Q, const void
 // Vt are in the executing layout either way.
 hipError_t launch_attn_vt(const Dims &dm, const void *Q, const void *K, const void *Vt, void *O,
                           const int32_t *row_ptr, const int32_t *kv_idx, int bq, int bk, float scale,
-                          hipStream_t st, bool qo_orig = false, const int32_t *labels = nullptr);
+                          hipStream_t st, bool qo_orig = false, const int32_t *labels = nullptr,
+                          void *ws = nullptr);
+// Bytes of ws the sparse launch splits its text groups into (0: no split).
+size_t attn_vt_ws_bytes(const Dims &dm, int bq, int bk);
 int attn_vt_max_kv_blocks();
 // frames: keep every head's token order, each frame and the text starting a
 // new 64-key tile (vt_frame_tiles(dm) tiles a head, zero past each end)

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libsvg_hip.so")
 SVG_OK, SVG_ERR_NULL, SVG_ERR_SHAPE, SVG_ERR_DTYPE, SVG_ERR_UNSUPPORTED, SVG_ERR_RANGE, \
     SVG_ERR_WORKSPACE, SVG_ERR_HIP = range(8)
 SVG_F32, SVG_BF16 = 0, 1
-SVG_OP_PROFILE, SVG_OP_BLOCK_SPARSE, SVG_OP_COMPACT = 0, 1, 2
+SVG_OP_PROFILE, SVG_OP_BLOCK_SPARSE, SVG_OP_COMPACT, SVG_OP_ATTN_VT = 0, 1, 2, 3
 SVG2_OP_KMEANS, SVG2_OP_CLUSTER_PERMUTE, SVG2_OP_VARLEN = 0, 1, 2
 
 
@@ -62,8 +62,8 @@ SIGNATURES = {
     "svg_dense_attn": [_DIMS, _I, _P, _P, _P, _I, _I, _F, _P, _P],
     "svg_vt_elems": [_DIMS],
     "svg_layout_permute_vt": [_DIMS, _I, _P, _P, _P, _P],
-    "svg_block_sparse_attn_csr_vt": [_DIMS, _I, _P, _P, _P, _P, _P, _I, _I, _F, _P, _P],
-    "svg_block_sparse_attn_csr_vt_layout": [_DIMS, _I, _P, _P, _P, _P, _P, _P, _I, _I, _F, _P, _P],
+    "svg_block_sparse_attn_csr_vt": [_DIMS, _I, _P, _P, _P, _P, _P, _I, _I, _F, _P, _P, _Z, _P],
+    "svg_block_sparse_attn_csr_vt_layout": [_DIMS, _I, _P, _P, _P, _P, _P, _P, _I, _I, _F, _P, _P, _Z, _P],
     "svg_dense_attn_vt": [_DIMS, _I, _P, _P, _P, _I, _I, _F, _P, _P],
     "svg2_workspace_bytes": [_I, _DIMS, _I, _I],
     "svg_kmeans": [_DIMS, _I, _P, _I, _I, _P, _P, _P, _P, _P, _Z, _P],
@@ -269,24 +269,38 @@ def _qk_vt(q, k, vt, F, S, T):
     return svg_dims(F, S, T, H, d), _dtype(q)
 
 
-def svg_block_sparse_attn_csr_vt(q, k, vt, row_ptr, kv_idx, F, S, T, bq, bk, scale=-1.0, out=None):
+def attn_vt_workspace(q, F, S, T, bq, bk):
+    """Workspace for the split text groups of the sparse V^T attention
+    entries (None when no split applies)."""
+    n = workspace_bytes(SVG_OP_ATTN_VT, svg_dims(F, S, T, q.shape[0], q.shape[2]), bq, bk)
+    return torch.empty(n, dtype=torch.uint8, device=q.device) if n > 0 else None
+
+
+def svg_block_sparse_attn_csr_vt(q, k, vt, row_ptr, kv_idx, F, S, T, bq, bk, scale=-1.0, out=None, ws=None):
+    """ws: from attn_vt_workspace (allocated here when None)."""
     dm, dt = _qk_vt(q, k, vt, F, S, T)
     out = torch.empty_like(q) if out is None else out
+    ws = attn_vt_workspace(q, F, S, T, bq, bk) if ws is None else ws
     _check(_lib.svg_block_sparse_attn_csr_vt(ctypes.byref(dm), dt, _ptr(q), _ptr(k), _ptr(vt), _ptr(row_ptr),
-                                             _ptr(kv_idx), bq, bk, scale, _ptr(out), _stream()),
+                                             _ptr(kv_idx), bq, bk, scale, _ptr(out), _ptr(ws),
+                                             0 if ws is None else ws.numel() * ws.element_size(), _stream()),
            "svg_block_sparse_attn_csr_vt")
     return out
 
 
 def svg_block_sparse_attn_csr_vt_layout(q, k, vt, row_ptr, kv_idx, labels, F, S, T, bq, bk, scale=-1.0,
-                                        out=None):
+                                        out=None, ws=None):
     """Q and the returned O in the original token order; K, Vt and the lists
-    in each head's executing layout per labels (None: every head temporal)."""
+    in each head's executing layout per labels (None: every head temporal).
+    ws: from attn_vt_workspace (allocated here when None)."""
     dm, dt = _qk_vt(q, k, vt, F, S, T)
     out = torch.empty_like(q) if out is None else out
+    ws = attn_vt_workspace(q, F, S, T, bq, bk) if ws is None else ws
     _check(_lib.svg_block_sparse_attn_csr_vt_layout(ctypes.byref(dm), dt, _ptr(q), _ptr(k), _ptr(vt),
                                                     _ptr(row_ptr), _ptr(kv_idx), _ptr(labels), bq, bk, scale,
-                                                    _ptr(out), _stream()),
+                                                    _ptr(out), _ptr(ws),
+                                                    0 if ws is None else ws.numel() * ws.element_size(),
+                                                    _stream()),
            "svg_block_sparse_attn_csr_vt_layout")
     return out
 

@@ -37,6 +37,7 @@ def test_version_string():
 
 FAKE = ctypes.c_void_p(0x10000)      # never dereferenced: validation fails first
 FAKE2 = ctypes.c_void_p(0x20000000)
+FAKE3 = ctypes.c_void_p(0x40000000)
 
 
 def dims(F=4, S=64, T=16, H=2, d=64):
@@ -83,6 +84,10 @@ def test_workspace_sizes():
     assert ws >= rows * 4 + (rows + 1) * 4 + rows * nkb * 4
     assert L.svg_workspace_bytes(svg.SVG_OP_BLOCK_SPARSE, d, 32, 32) == 0
     assert L.svg_workspace_bytes(svg.SVG_OP_PROFILE, d, 178, 0) >= 3 * 8 * 178 * 64 * 4
+    # split text groups of the sparse V^T attention: 278 kv-blocks -> 6 parts
+    # of the 2 leading groups, 256 rows of d + 4 floats each; none at <= 48
+    assert L.svg_workspace_bytes(svg.SVG_OP_ATTN_VT, d, 64, 64) == 8 * 2 * 6 * 256 * (64 + 4) * 4
+    assert L.svg_workspace_bytes(svg.SVG_OP_ATTN_VT, dims(F=2, S=1536, T=0, H=2, d=128), 128, 64) == 0
 
 
 def test_svg2_validation():
@@ -112,16 +117,23 @@ def test_vt_entry_points_validate_on_host():
     assert L.svg_dense_attn_vt(big, bf16, FAKE, FAKE, FAKE, 128, 64, -1.0, FAKE2, None) == svg.SVG_ERR_UNSUPPORTED
     assert "kv-blocks" in svg.last_error()
     assert L.svg_block_sparse_attn_csr_vt(dims(), bf16, FAKE, FAKE, FAKE, None, FAKE, 64, 64, -1.0, FAKE2,
-                                          None) == svg.SVG_ERR_NULL
+                                          None, 0, None) == svg.SVG_ERR_NULL
     # the original-order variant: same checks (NULL lists, NULL tensors, unsupported shapes)
     assert L.svg_block_sparse_attn_csr_vt_layout(dims(), bf16, FAKE, FAKE, FAKE, FAKE, None, None, 64, 64, -1.0,
-                                                 FAKE2, None) == svg.SVG_ERR_NULL
+                                                 FAKE2, None, 0, None) == svg.SVG_ERR_NULL
     assert L.svg_block_sparse_attn_csr_vt_layout(dims(), bf16, None, FAKE, FAKE, FAKE, FAKE, None, 64, 64, -1.0,
-                                                 FAKE2, None) == svg.SVG_ERR_NULL
+                                                 FAKE2, None, 0, None) == svg.SVG_ERR_NULL
     assert L.svg_block_sparse_attn_csr_vt_layout(dims(), bf16, FAKE, FAKE, FAKE, FAKE, FAKE, None, 128, 128, -1.0,
-                                                 FAKE2, None) == svg.SVG_ERR_UNSUPPORTED
+                                                 FAKE2, None, 0, None) == svg.SVG_ERR_UNSUPPORTED
     assert L.svg_block_sparse_attn_csr_vt_layout(dims(), 0, FAKE, FAKE, FAKE, FAKE, FAKE, None, 64, 64, -1.0,
-                                                 FAKE2, None) == svg.SVG_ERR_UNSUPPORTED
+                                                 FAKE2, None, 0, None) == svg.SVG_ERR_UNSUPPORTED
+    # the split-partials workspace: too small, or overlapping a tensor
+    big_w = dims(F=4, S=64 * 40, T=64, H=2, d=128)       # 161 kv-blocks: split
+    need = L.svg_workspace_bytes(svg.SVG_OP_ATTN_VT, big_w, 128, 64)
+    assert L.svg_block_sparse_attn_csr_vt(big_w, bf16, FAKE, FAKE, FAKE, FAKE, FAKE, 128, 64, -1.0, FAKE2,
+                                          FAKE3, need - 1, None) == svg.SVG_ERR_WORKSPACE
+    assert L.svg_block_sparse_attn_csr_vt_layout(big_w, bf16, FAKE, FAKE, FAKE, FAKE, FAKE, None, 128, 64, -1.0,
+                                                 FAKE2, FAKE, need, None) == svg.SVG_ERR_RANGE
     # O overlapping an input
     assert L.svg_dense_attn_vt(dims(), bf16, FAKE, FAKE2, FAKE, 64, 64, -1.0, FAKE, None) == svg.SVG_ERR_RANGE
     assert L.svg_layout_permute_vt(dims(), 0, FAKE, FAKE2, None, None) == svg.SVG_ERR_UNSUPPORTED

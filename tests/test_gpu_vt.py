@@ -9,6 +9,8 @@ N (partial last tile and partial last work-group), both head dims and both
 q-block heights.  Inputs are seeded and synthetic (synth/).
 """
 
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -231,18 +233,28 @@ def test_attention_vt_split_leading_groups(keep_last, d, bq):
             for qb in lead_qb:
                 bm[h, qb, cols] = 1
     row_ptr, kv_idx = csr(bm)
+    qd, kd = to_dev(q, "bf16"), to_dev(k, "bf16")
     vt = svg.svg_layout_permute_vt(to_dev(v, "bf16"), 1, N, 0, None)
-    o = svg.svg_block_sparse_attn_csr_vt(to_dev(q, "bf16"), to_dev(k, "bf16"), vt, row_ptr, kv_idx,
-                                         1, N, 0, bq, bk)
+    o = svg.svg_block_sparse_attn_csr_vt(qd, kd, vt, row_ptr, kv_idx, 1, N, 0, bq, bk)
+    # the same entry with no workspace: no group is split
+    o_whole = torch.empty_like(o)
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+    dm = svg.svg_dims(1, N, 0, H, d)
+    assert svg.lib().svg_block_sparse_attn_csr_vt(
+        ctypes.byref(dm), svg.SVG_BF16, ptr(qd), ptr(kd), ptr(vt), ptr(row_ptr), ptr(kv_idx), bq, bk, -1.0,
+        ptr(o_whole), None, 0, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)) == svg.SVG_OK
     sync()
-    got = to_f64(o)
     lead_rows = slice(lead_qb[0] * bq, N)
-    for h in range(H):
-        ref = attention.block_sparse_attention_full(as_f64(q[h], "bf16"), as_f64(k[h], "bf16"),
-                                                    as_f64(v[h], "bf16"), bm[h], bq, bk)
-        check_close(got[h], ref, BF16_MAX_ABS, BF16_REL_L2, f"split leading groups head {h}")
-        if keep_last == 0:
-            assert np.all(got[h][lead_rows] == 0.0)
+    for name, out in (("split", o), ("whole", o_whole)):
+        got = to_f64(out)
+        for h in range(H):
+            ref = attention.block_sparse_attention_full(as_f64(q[h], "bf16"), as_f64(k[h], "bf16"),
+                                                        as_f64(v[h], "bf16"), bm[h], bq, bk)
+            check_close(got[h], ref, BF16_MAX_ABS, BF16_REL_L2, f"{name} leading groups head {h}")
+            if keep_last == 0:
+                assert np.all(got[h][lead_rows] == 0.0)
+    # rows outside the leading groups do not depend on the split
+    np.testing.assert_array_equal(to_host_bits(o)[:, :lead_qb[0] * bq], to_host_bits(o_whole)[:, :lead_qb[0] * bq])
 
 
 def test_attention_vt_whole_group_empty():
