@@ -76,20 +76,22 @@ void attn_fwd_vt(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K, con
   __shared__ int wsum[DENSE ? 1 : kWords + 1];
 
   // Each XCD runs a contiguous slice of the work list (a few heads) in
-  // order.  A head's last 512 query rows hold its text rows, which keep
-  // every kv-block (about 3x an average group): their groups go first within
-  // the head, so that no XCD ends on one of them.  The other groups follow
-  // in ascending order, so neighbours that share kv-blocks run together and
-  // hit in L2 (reversing the whole order instead doubles the HBM fetch).
-  // With nsplit > 1 each of the nlead leading groups is nsplit work items.
+  // order; within a head the groups go in ascending order, so neighbours
+  // that share kv-blocks run together and hit in L2 (reversing the whole
+  // order instead doubles the HBM fetch).  A head's last 512 query rows
+  // hold its text rows, which keep every kv-block.  Unsplit (nsplit = 1),
+  // their groups are about 3x an average one and go first within the head,
+  // so that no XCD ends on one.  Split, each is nsplit short work items that
+  // go last.
   const int work = xcd_remap(blockIdx.x, gridDim.x);
   const int nlead = min(ngrp, 512 / kWgRows);
   const int per_head = ngrp + nlead * (nsplit - 1);
   const int h = work / per_head, local = work - h * per_head;
-  const bool lead = local < nlead * nsplit;
-  const int lg = lead ? local / nsplit : 0;          // leading group, 0 = the last group
-  const int split = lead ? local - lg * nsplit : 0;
-  const int grp = lead ? ngrp - 1 - lg : local - nlead * nsplit;
+  const int jl = nsplit > 1 ? local - (ngrp - nlead) : local;   // index among the leading items
+  const bool lead = jl >= 0 && jl < nlead * nsplit;
+  const int lg = lead ? jl / nsplit : 0;             // leading group, 0 = the last group
+  const int split = lead ? jl - lg * nsplit : 0;
+  const int grp = lead ? ngrp - 1 - lg : (nsplit > 1 ? local : local - nlead);
   const bool parted = lead && nsplit > 1;           // stores a partial for attn_vt_merge
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -222,9 +224,19 @@ void attn_vt_merge(const float *__restrict__ part, bf16_t *__restrict__ O, int N
 }
 
 // Parts per leading group of a sparse launch: about 48 tiles each (near a
-// typical group's list), at most 16; none above 48 kv-blocks or for a dense
-// launch (every group has the same list).
-int attn_vt_nsplit(int nkb, bool dense) { return dense ? 1 : max(1, min(16, (nkb + 47) / 48)); }
+// typical group's list), at most 16.  None for a dense launch (every group
+// has the same list), at 48 kv-blocks or fewer, or when the launch is more
+// than kSplitRounds rounds of work-groups deep: the leading groups, started
+// first, then end long before the rest, and splitting them only costs L2
+// hits (at the HunyuanVideo layer shape, 44 rounds: 1.5x the HBM fetch of
+// the whole launch for a 0.3% shorter run).
+constexpr int kNumCu = 256;
+constexpr int kSplitRounds = 8;
+int attn_vt_nsplit(const Dims &dm, int ngrp, bool dense) {
+  const int nkb = (dm.N + BK - 1) / BK;
+  if (dense || (long long)dm.H * ngrp > (long long)kSplitRounds * kNumCu) return 1;
+  return max(1, min(16, (nkb + 47) / 48));
+}
 
 template <int D, int BQ>
 hipError_t launch_vt(const Dims &dm, const void *Q, const void *K, const void *Vt, void *O,
@@ -237,7 +249,7 @@ hipError_t launch_vt(const Dims &dm, const void *Q, const void *K, const void *V
   const int nlead = min(ngrp, 512 / kWgRows);
   // The leading (text) groups keep every kv-block: split them by keys when
   // the caller gives the partials' workspace.
-  const int nsplit = part == nullptr ? 1 : attn_vt_nsplit(nkb, row_ptr == nullptr);
+  const int nsplit = part == nullptr ? 1 : attn_vt_nsplit(dm, ngrp, row_ptr == nullptr);
   const int grid = dm.H * (ngrp + nlead * (nsplit - 1));
   if (row_ptr == nullptr)
     hipLaunchKernelGGL((attn_fwd_vt<D, BQ, true>), dim3(grid), dim3(kWgRows * 2), 0, st, (const bf16_t *)Q,
@@ -259,9 +271,9 @@ int attn_vt_max_kv_blocks() { return kMaxKb; }
 
 size_t attn_vt_ws_bytes(const Dims &dm, int bq, int bk) {
   if (bk != BK || (bq != 64 && bq != 128) || dm.N < 1 || dm.H < 1 || (dm.d != 64 && dm.d != 128)) return 0;
-  const int nkb = (dm.N + BK - 1) / BK, nsplit = attn_vt_nsplit(nkb, false);
-  if (nsplit == 1) return 0;
   const int ngrp = ((dm.N + bq - 1) / bq + kWgRows / bq - 1) / (kWgRows / bq);
+  const int nsplit = attn_vt_nsplit(dm, ngrp, false);
+  if (nsplit == 1) return 0;
   const int nlead = min(ngrp, 512 / kWgRows);
   return (size_t)dm.H * nlead * nsplit * kWgRows * (dm.d + 4) * sizeof(float);
 }
