@@ -345,6 +345,30 @@ def test_profile_small_frames(d):
     np.testing.assert_allclose(mse.double().cpu().numpy(), om, rtol=2e-2, atol=1e-6)
 
 
+@pytest.mark.parametrize("F,S,T,d", [(5, 200, 0, 64), (3, 128, 64, 128), (9, 70, 5, 64), (2, 1000, 130, 128)])
+def test_profile_frame_chunks_ragged(F, S, T, d):
+    """The full pass walks key chunks cut at frame boundaries (each frame
+    padded to whole 64-key tiles) and takes the spatial outputs from them:
+    frames that end mid-tile (S = 200, 70, 1000), whole tiles (S = 128), no
+    text (T = 0), a one-key-short text tile (T = 130, 63 + 64 + 3), frames
+    split into several parts (S = 1000).  Gaussian heads, so every key
+    carries weight: MSEs against the oracle, with samples in every frame and
+    in the text."""
+    H = 2
+    N = F * S + T
+    q, k, v = random_qkv(H, N, d, seed=F * S + T + d, dtype="bf16")
+    rng = np.random.default_rng(N)
+    si = rng.choice(N, size=min(N, 150), replace=False).astype(np.int32)
+    if T:
+        si[0] = N - 1                                     # a text row
+    for ks, wt in ((1 if F > 2 else 0, 3 * F), (0, S * F // 3)):   # windows that keep only some keys
+        labels, mse = svg.svg_profile_heads(*(to_dev(x, "bf16") for x in (q, k, v)), ints(si), F, S, T, ks, wt)
+        sync()
+        ol, om = profile.profile_heads(*(as_f64(x, "bf16") for x in (q, k, v)), F, S, T, si, ks, wt)
+        assert om.min() > 1e-4
+        np.testing.assert_allclose(mse.double().cpu().numpy(), om, rtol=2e-2, atol=1e-6)
+
+
 @pytest.mark.parametrize("ks,wt", [(1, 100), (2, 0), (0, 1350 * 13)])
 def test_profile_mask_widths_against_oracle(ks, wt):
     """Masks of other widths (a temporal window that is not a multiple of F,
