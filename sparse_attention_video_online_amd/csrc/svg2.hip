@@ -210,15 +210,21 @@ void km_assign_mfma(const bf16_t *__restrict__ X, const float *__restrict__ tab,
 }
 
 // Centroid of cluster j = mean of its members, taken in sorted (= index)
-// order.  An empty cluster keeps its centroid.
+// order.  An empty cluster keeps its centroid.  With tab (the MFMA
+// assignment), the block also writes centroid j's row of the next
+// iteration's table, as km_prep does (same values, same summation order of
+// ||c||^2), which saves a launch per iteration.
 template <typename T>
 __global__ __launch_bounds__(128)
 void km_update(const T *__restrict__ X, const int32_t *__restrict__ perm, const int32_t *__restrict__ offs, int N,
-               int k, int D, double *__restrict__ cent, int32_t *__restrict__ sizes) {
+               int k, int D, double *__restrict__ cent, int32_t *__restrict__ sizes, float *__restrict__ tab,
+               int kpad) {
+  __shared__ double cv[128];
   const int h = blockIdx.y, j = blockIdx.x, e = threadIdx.x;
   const int o0 = offs[(size_t)h * (k + 1) + j], o1 = offs[(size_t)h * (k + 1) + j + 1];
   const int32_t *p = perm + (size_t)h * N;
   const T *Xh = X + (size_t)h * N * D;
+  double *cj = cent + ((size_t)h * k + j) * D;
   if (e < D && o1 > o0) {
     // members in batches of 8: their indices and values load independently,
     // then the fp64 adds run in member order
@@ -235,9 +241,24 @@ void km_update(const T *__restrict__ X, const int32_t *__restrict__ perm, const 
       for (int u = 0; u < 8; ++u) s += (double)v[u];
     }
     for (; n < o1; ++n) s += (double)to_f32<T>(Xh[(size_t)p[n] * D + e]);
-    cent[((size_t)h * k + j) * D + e] = s / (double)(o1 - o0);
+    cj[e] = s / (double)(o1 - o0);
   }
   if (e == 0) sizes[h * k + j] = o1 - o0;
+  if (tab == nullptr) return;
+  if (e < D) cv[e] = cj[e];   // each thread reads back its own dim
+  __syncthreads();
+  const int row = D / 2 + kKmPad;
+  float *t = tab + (size_t)h * kpad * (2 * row + 1);
+  if (e < D) t[((size_t)j * 2 + (e & 1)) * row + (e >> 1)] = (float)cv[e];
+  if (e < 2 * kKmPad) t[((size_t)j * 2 + (e & 1)) * row + D / 2 + (e >> 1)] = 0.f;
+  if (e == 0) {
+    double n2 = 0.0;
+    for (int i = 0; i < D; ++i) {
+      const double v = cv[i];
+      n2 += v * v;
+    }
+    t[(size_t)kpad * 2 * row + j] = (float)n2;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -625,13 +646,16 @@ hipError_t launch_kmeans(const Dims &dm, bool bf16, const void *X, int k, int it
     if (e != hipSuccess) return e;
   }
   const dim3 pgrid((kpad + 255) / 256, dm.H), mgrid((dm.N + 255) / 256, dm.H);
+  // the table of the initial centroids; each update then writes the next one
+  if (mfma && dm.d == 64)
+    hipLaunchKernelGGL(km_prep<64>, pgrid, dim3(256), 0, st, centroids, k, kpad, tab);
+  else if (mfma)
+    hipLaunchKernelGGL(km_prep<128>, pgrid, dim3(256), 0, st, centroids, k, kpad, tab);
   for (int it = 0; it < iters; ++it) {
     if (mfma && dm.d == 64) {
-      hipLaunchKernelGGL(km_prep<64>, pgrid, dim3(256), 0, st, centroids, k, kpad, tab);
       hipLaunchKernelGGL(km_assign_mfma<64>, mgrid, dim3(256), mlds, st, (const bf16_t *)X, tab, dm.N, k, kpad,
                          assign);
     } else if (mfma) {
-      hipLaunchKernelGGL(km_prep<128>, pgrid, dim3(256), 0, st, centroids, k, kpad, tab);
       hipLaunchKernelGGL(km_assign_mfma<128>, mgrid, dim3(256), mlds, st, (const bf16_t *)X, tab, dm.N, k, kpad,
                          assign);
     } else if (bf16 && dm.d == 64)
@@ -647,12 +671,13 @@ hipError_t launch_kmeans(const Dims &dm, bool bf16, const void *X, int k, int it
       hipLaunchKernelGGL((km_assign<float, 128>), grid, dim3(256), lds, st, (const float *)X, centroids, dm.N, k,
                          assign);
     launch_sort(dm, assign, k, perm, offs, scnt, st);
+    float *const next_tab = (mfma && it + 1 < iters) ? tab : nullptr;
     if (bf16)
       hipLaunchKernelGGL(km_update<bf16_t>, dim3(k, dm.H), dim3(128), 0, st, (const bf16_t *)X, perm, offs, dm.N, k,
-                         dm.d, centroids, sizes);
+                         dm.d, centroids, sizes, next_tab, kpad);
     else
       hipLaunchKernelGGL(km_update<float>, dim3(k, dm.H), dim3(128), 0, st, (const float *)X, perm, offs, dm.N, k,
-                         dm.d, centroids, sizes);
+                         dm.d, centroids, sizes, next_tab, kpad);
   }
   return hipGetLastError();
 }
