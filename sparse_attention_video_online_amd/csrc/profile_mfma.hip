@@ -5,22 +5,19 @@
 // over its own kept keys with its own maximum.  Then per-head MSEs of the
 // masked outputs against the full one, and the label (ties -> spatial).
 //
-// Two passes.  The full pass runs the attention kernel's V^T tile pipeline
-// (vt_attend: 8 waves x 32 sampled rows, K and a key-tiled V^T DMA'd into
-// LDS) over key chunks that never cross a frame boundary: V^T is laid out
-// with every frame (then the text) starting a new 64-key tile, and each
-// chunk is one frame, or a part of one, or a part of the text.  A spatial
-// window is a run of whole frames plus the text, so the spatial output of a
-// row is the merge of the full pass's chunks inside its window: no spatial
-// pass is run.  The temporal pass uses the S^T = K Q^T / O^T += V^T P^T
-// machinery of attn_core.h on 128 sampled rows (4 waves x 32) grouped by
-// grid position, and visits only the key tiles that some sample's window
-// (or a text key) reaches.  In a flagged tile each row keeps at most two
-// key ranges, one per frame the tile touches: a wave whose rows keep none of
-// the tile skips its math, a wave whose rows keep all of it needs no mask,
-// and the others test each score's key offset against the two ranges.
-// Chunks are merged afterwards (flash-decoding style), and the squared
-// errors are summed in fp64 in a fixed order.
+// Two passes, both on the attention kernel's V^T tile pipeline (vt_attend:
+// 8 waves x 32 sampled rows, K and a key-tiled V^T DMA'd into LDS).  V^T is
+// laid out with every frame (then the text) starting a new 64-key tile.
+// The full pass walks key chunks that never cross a frame boundary: each is
+// one frame, or a part of one, or a part of the text.  A spatial window is a
+// run of whole frames plus the text, so the spatial output of a row is the
+// merge of the full pass's chunks inside its window: no spatial pass is run.
+// The temporal pass takes one work-group per (256 samples in position-major
+// order, frame): it walks the frame's tiles that its rows' position windows
+// reach, each row masking the keys outside its own window; the text keys,
+// kept by every row, come from the full pass's text chunks.  Chunks are
+// merged afterwards (flash-decoding style), and the squared errors are
+// summed in fp64 in a fixed order.
 #include "attn_vt_core.h"
 
 namespace svgk {
@@ -28,13 +25,7 @@ namespace {
 
 using namespace core;
 
-constexpr int PNW = 4;
-constexpr int PNT = PNW * 64;
-constexpr int PQ = PNW * 32;
-
-struct ProfileGrid { int nqg, nchunks, tiles_per_chunk; };
-
-// The full pass: 8 waves = 256 samples per work-group on the V^T tile
+// Both passes: 8 waves = 256 samples per work-group on the V^T tile
 // pipeline (vt_attend), one work-group per CU.
 constexpr int FNW = 8;
 constexpr int FNT = FNW * 64;
@@ -73,20 +64,6 @@ FrameGrid profile_grid_full(const Dims &dm, int n_s) {
   return g;
 }
 
-// Key chunks of the temporal pass per (head, sample group): about 2048
-// work-groups, four rounds of the 512 resident ones.  Fewer chunks leave the
-// work in the few work-groups whose chunk holds a sample group's windows;
-// more chunks cost merge traffic.
-ProfileGrid profile_grid(const Dims &dm, int n_s) {
-  const int nkb = (dm.N + BK - 1) / BK;
-  const int nqg = (n_s + PQ - 1) / PQ;
-  int c = (2048 + dm.H * nqg - 1) / (dm.H * nqg);
-  c = max(1, min(c, max(1, nkb / 4)));
-  int tpc = (nkb + c - 1) / c;
-  tpc = min(tpc, 4096);
-  return ProfileGrid{nqg, (nkb + tpc - 1) / tpc, tpc};
-}
-
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 struct Parts {
@@ -121,7 +98,6 @@ Parts carve(void *ws, const Dims &dm, int n_s, int Cf, int Ct) {
   return r;
 }
 
-constexpr int kMaxVisit = 4096;   // visit-list capacity (tiles per chunk)
 constexpr int kMaxRankSamples = 16384;
 
 // Order of the samples for the work-groups of the temporal pass: by
@@ -152,226 +128,6 @@ void profile_order(const int32_t *__restrict__ sample_idx, int n_s, int F, int S
     }
   }
   if (act) ord_t[rt] = s;
-}
-
-// The temporal pass for the work-group's 128 sampled rows over one chunk of
-// key tiles.  A prologue lists the chunk's tiles that some sample of the
-// work-group keeps (any key), and flags the tiles where some video sample
-// does not keep every video key: only those evaluate the token mask.
-template <int D>
-__global__ __launch_bounds__(PNT, 2)
-void profile_temporal_mfma(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K, const bf16_t *__restrict__ V,
-                           const int32_t *__restrict__ sample_idx, const int32_t *__restrict__ order, int n_s,
-                           int F, int S, int N, int wt, int nkb, int tpc, int cstride, float c,
-                           float *__restrict__ part_o, float *__restrict__ part_ml) {
-  using C = Tile<D, PNT>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE];
-  __shared__ uint16_t vlist[kMaxVisit];   // tile - t0, bit 15: evaluate the mask
-  __shared__ int bnd[5];     // -, video query present, p_lo, p_hi, text query present
-  __shared__ int wcount[PNW + 1];
-  const int h = blockIdx.z, chunk = blockIdx.y, qg = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31, hi = lane >> 5;
-  const size_t hoff = (size_t)h * N * D;
-  const bf16_t *Kh = K + hoff, *Vh = V + hoff;
-
-  const int pos = qg * PQ + wave * 32 + l32;
-  const bool valid = pos < n_s;
-  const int sidx = valid ? order[pos] : 0;
-  const int i = valid ? sample_idx[sidx] : 0;
-  const int FS = F * S;
-  const bool text_i = i >= FS;
-  const int fi = text_i ? 0 : i / S;
-  const int pi = text_i ? 0 : i - fi * S;
-  // temporal window of this row in position-major units (wt clamped so the
-  // bounds stay in int32)
-  const int wtc = min(wt, N);
-  const int tlo = pi * F - wtc, thi = pi * F + F - 1 + wtc;
-  // The same window per key frame f: positions pi - floor((wtc + f)/F) ..
-  // pi + floor((F - 1 + wtc - f)/F).  With wtc = wq*F + wr (0 <= wr < F) and
-  // 0 <= f < F the floors are wq + (f + wr >= F) and wq + (f < wr).
-  const int wq = wtc / F, wr = wtc - wq * F;
-  // Kept keys of frame f for this row, absolute [lo, hi] (lo > hi: none).
-  auto frame_keys = [&](int f, int &lo, int &hk) {
-    lo = f * S + max(pi - (wq + (f + wr >= F)), 0);
-    hk = f * S + min(pi + (wq + (f < wr)), S - 1);
-  };
-
-  // ---- visit list of this chunk
-  const int t0 = chunk * tpc, t1 = min(nkb, t0 + tpc);
-  if (tid < 5) bnd[tid] = (tid & 1) ? -1 : 0x7fffffff;
-  if (tid == 4) bnd[4] = 0;
-  __syncthreads();
-  if (valid) {
-    if (text_i) {
-      atomicMax(&bnd[4], 1);
-    } else {
-      atomicMax(&bnd[1], 1);
-      atomicMin(&bnd[2], pi);
-      atomicMax(&bnd[3], pi);
-    }
-  }
-  __syncthreads();
-  const int p_lo = bnd[2], p_hi = bnd[3];
-  const bool any_video = bnd[1] > 0, any_text = bnd[4] != 0;
-  // union / intersection of the video samples' windows
-  const long long RU_lo = (long long)p_lo * F - wtc, RU_hi = (long long)p_hi * F + F - 1 + wtc;
-  const long long RI_lo = (long long)p_hi * F - wtc, RI_hi = (long long)p_lo * F + F - 1 + wtc;
-  int nv = 0;
-  for (int base = t0; base < t1; base += PNT) {
-    const int t = base + tid;
-    bool visit = false, needmask = false;
-    if (t < t1) {
-      const int k0 = t * BK, k1 = min(N, k0 + BK) - 1;
-      if (k1 >= FS || any_text) visit = true;   // text keys / text rows keep all
-      if (k0 < FS && any_video) {
-        const int kv1 = min(k1, FS - 1);
-        for (int f = k0 / S; f <= kv1 / S; ++f) {
-          const int a = max(k0, f * S) - f * S, b = min(kv1, f * S + S - 1) - f * S;
-          // positions p in [a, b] with p*F + f inside [RU_lo, RU_hi]
-          const long long plo = (RU_lo - f + F - 1) >= 0 ? (RU_lo - f + F - 1) / F : 0;
-          const long long phi = RU_hi - f >= 0 ? (RU_hi - f) / F : -1;
-          visit |= max((long long)a, plo) <= min((long long)b, phi);
-          needmask |= !((long long)a * F + f >= RI_lo && (long long)b * F + f <= RI_hi);
-        }
-      }
-    }
-    const unsigned long long bal = __builtin_amdgcn_ballot_w64(visit);
-    if (lane == 0) wcount[wave] = __builtin_popcountll(bal);
-    __syncthreads();
-    int off = nv;
-    for (int w = 0; w < wave; ++w) off += wcount[w];
-    int tot = 0;
-    for (int w = 0; w < PNW; ++w) tot += wcount[w];
-    if (visit) {
-      const int rank = __builtin_popcountll(bal & ((1ull << lane) - 1ull));
-      vlist[off + rank] = (uint16_t)((t - t0) | (needmask ? 0x8000 : 0));
-    }
-    nv += tot;
-    __syncthreads();
-  }
-
-  bf16x8 qf[D / 16];
-  load_q<D>(Q + hoff, valid ? i : -1, hi, qf);
-  f32x16 o[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
-
-  Regs<D, PNT> R;
-  auto rows_of = [&](int t) {
-    return [=](int j) { const int key = t * BK + j; return key < N ? key : -1; };
-  };
-  if (nv > 0) {
-    load_tile<D, PNT>(Kh, Vh, tid, rows_of(t0 + (vlist[0] & 0x7FFF)), R);
-    store_tile<D, PNT>(smem, tid, R);
-  }
-  __syncthreads();
-  for (int it = 0; it < nv; ++it) {
-    const int e = vlist[it];
-    const int t = t0 + (e & 0x7FFF);
-    const bool more = it + 1 < nv;
-    if (more) load_tile<D, PNT>(Kh, Vh, tid, rows_of(t0 + (vlist[it + 1] & 0x7FFF)), R);
-    const char *Ks = smem + (it & 1) * C::STAGE;
-    const char *Vs = Ks + C::KBYTES;
-
-    const int kbase = t * BK;
-    // Token mask of a flagged tile.  With S >= 64 a tile holds keys of at
-    // most two frames (f0, then f0 + 1 from offset sp on; past the video the
-    // second part is the text keys, all kept), so this row keeps at most two
-    // offset ranges [a0, a0 + n0) and [a1, a1 + n1).  A wave none of whose
-    // rows keeps a key of the tile skips its math (the tile adds exact
-    // zeros); a wave whose rows keep every key needs no mask.
-    bool skip = false, ranges = false, perkey = false;
-    int a0 = 0, n0 = 0, a1 = 0, n1 = 0;
-    if (e & 0x8000) {
-      if (S >= BK) {
-        const int nvalid = min(BK, N - kbase);
-        if (text_i) {
-          n0 = nvalid;
-        } else {
-          const int f0 = min(kbase, FS - 1) / S;
-          const int sp = min(max((f0 + 1) * S - kbase, 0), BK);
-          int lo, hk;
-          frame_keys(f0, lo, hk);
-          a0 = max(lo - kbase, 0);
-          n0 = max(min(min(hk - kbase, sp - 1), nvalid - 1) - a0 + 1, 0);
-          if (f0 + 1 < F) {
-            frame_keys(f0 + 1, lo, hk);
-          } else {
-            lo = FS;
-            hk = N - 1;
-          }
-          a1 = max(lo - kbase, sp);
-          n1 = max(min(min(hk - kbase, BK - 1), nvalid - 1) - a1 + 1, 0);
-        }
-        const int kept = n0 + n1;
-        skip = __builtin_amdgcn_ballot_w64(valid && kept > 0) == 0;
-        ranges = __builtin_amdgcn_ballot_w64(valid && kept < nvalid) != 0;
-      } else {
-        perkey = !text_i;
-      }
-    }
-    if (!skip) {
-      f32x16 s0, s1;
-      qk_tile<D, PNT>(Ks, qf, l32, hi, s0, s1);
-      if (kbase + BK > N) mask_tail(s0, s1, N - kbase, hi);
-      if (ranges) {
-        // offset acc_key(b, r, hi) = acc_key(b, r, 0) + 4 hi
-        const int a0h = a0 - 4 * hi, a1h = a1 - 4 * hi;
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int off = acc_key(b, r, 0);
-            const bool keep = (unsigned)(off - a0h) < (unsigned)n0 || (unsigned)(off - a1h) < (unsigned)n1;
-            if (!keep) {
-              if (b == 0) s0[r] = -INFINITY; else s1[r] = -INFINITY;
-            }
-          }
-        }
-      } else if (perkey) {
-        // S < 64: a tile spans several frames; the mask per key
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kbase + acc_key(b, r, hi);
-            if (key >= FS) continue;  // text keys are always kept
-            const int fk = key / S;
-            const int rk = (key - fk * S) * F + fk;
-            if (rk < tlo || rk > thi) {
-              if (b == 0) s0[r] = -INFINITY; else s1[r] = -INFINITY;
-            }
-          }
-        }
-      }
-      bf16x8 pb[4];
-      const float alpha = softmax_step(s0, s1, c, m_run, l_run, pb);
-      rescale<D>(o, alpha);
-      pv_tile<D, PNT>(Vs, pb, l32, hi, o);
-    }
-
-    if (more) store_tile<D, PNT>(smem + ((it + 1) & 1) * C::STAGE, tid, R);
-    __syncthreads();
-  }
-
-  // partial result of this chunk: unnormalised O, running max, sum
-  const float lt = l_run + __shfl_xor(l_run, 32);
-  if (!valid) return;
-  const size_t slot = ((size_t)h * n_s + sidx) * cstride + chunk;
-  float *dst = part_o + slot * D;
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-      *reinterpret_cast<f32x4 *>(dst + 32 * db + 8 * g + 4 * hi) =
-          f32x4{o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]};
-  if (hi == 0) {
-    part_ml[slot * 2] = m_run;
-    part_ml[slot * 2 + 1] = lt;
-  }
 }
 
 // The full pass (no mask) for the work-group's 256 samples, in their given
@@ -456,6 +212,102 @@ void profile_full_vt(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K,
   }
 }
 
+// The temporal pass on the V^T tile pipeline: the work-group's 256 samples
+// (in position-major order, so they share few grid positions) against the
+// video keys of one frame f.  A row at grid position pi keeps, in frame f,
+// the positions pi - floor((w_t + f)/F) .. pi + floor((F - 1 + w_t - f)/F)
+// (its rank window p*F + f within [pi*F - w_t, pi*F + F - 1 + w_t]); the
+// work-group walks the frame's tiles that the union of its rows' ranges
+// touches, and each row masks the keys outside its own range.  Text rows are
+// skipped (they keep every key: their temporal output is the full one) and
+// the text keys, kept by every row, come from the full pass's text chunks in
+// the merge.  The partial of (sample, frame) goes to slot (h, sample, f).
+template <int D>
+__global__ __launch_bounds__(FNT, 1)
+void profile_temporal_vt(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K, const bf16_t *__restrict__ Vt,
+                         const int32_t *__restrict__ sample_idx, const int32_t *__restrict__ order, int n_s, int F,
+                         int S, int T, int wt, int nqg, int nbf, int nbt, float c, float *__restrict__ part_o,
+                         float *__restrict__ part_ml) {
+  constexpr int TB = DTile<D>::TBYTES;
+  // V^T stages named to sort first, below 64 KB of LDS (immediate offsets)
+  __shared__ __attribute__((aligned(1024))) char k0[TB], k1[TB], k2[TB], V0[TB], V1[TB], V2[TB];
+  __shared__ int prange[2];   // smallest and largest grid position of the video rows
+  const int work = xcd_remap(blockIdx.x, gridDim.x);
+  const int qg = work % nqg, f = (work / nqg) % F, h = work / (nqg * F);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hi = lane >> 5;
+  const int FS = F * S, N = FS + T;
+  const size_t hoff = (size_t)h * N * D;
+  const int pos = qg * FQ + wave * 32 + (lane & 31);
+  const int sidx = pos < n_s ? order[pos] : 0;
+  const int i = pos < n_s ? sample_idx[sidx] : FS;
+  const bool valid = i < FS;                    // a video row of this work-group
+  const int pi = valid ? i % S : 0;
+  // this row's kept positions in frame f (w_t clamped to N keeps int32)
+  const int wtc = min(wt, N);
+  const int wq = wtc / F, wr = wtc - wq * F;
+  const int lo = max(pi - (wq + (f + wr >= F)), 0), hk = min(pi + (wq + (f < wr)), S - 1);
+  if (tid == 0) {
+    prange[0] = 0x7fffffff;
+    prange[1] = -1;
+  }
+  __syncthreads();
+  if (valid) {
+    atomicMin(&prange[0], pi);
+    atomicMax(&prange[1], pi);
+  }
+  __syncthreads();
+  const int p_lo = prange[0], p_hi = prange[1];
+  if (p_hi < 0) return;   // no video row: nothing to compute (uniform)
+  // the union of the rows' ranges: local tiles t0 .. t0 + nt - 1 of frame f
+  const int u_lo = max(p_lo - (wq + (f + wr >= F)), 0), u_hi = min(p_hi + (wq + (f < wr)), S - 1);
+  const int t0 = u_lo / BK, nt = u_hi / BK - t0 + 1;
+  auto ent_raw = [&](int j) -> int { return t0 + (j < nt ? j : nt - 1); };
+  auto prep = [&](f32x16 &s0, f32x16 &s1, int e) -> bool {
+    const int kb = e * BK;
+    const bool own = valid && lo <= kb + BK - 1 && hk >= kb;
+    const bool whole = !valid || (lo <= kb && hk >= kb + BK - 1);
+    if (__builtin_amdgcn_ballot_w64(!whole)) {
+      // keep offset acc_key_pi(b, r, hi) = acc_key_pi(b, r, 0) + 8 hi iff it
+      // lies in [lo, hk] - kb.  A row that keeps none of the tile is left
+      // unmasked: the pipeline zeroes it by scaling with 0, and -inf * 0
+      // would be NaN.
+      const int a = own ? lo - kb - 8 * hi : 0;
+      const unsigned span = own ? (unsigned)(hk - lo) : 0xFFFFFFFFu;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if ((unsigned)(acc_key_pi(0, r, 0) - a) > span) s0[r] = -INFINITY;
+        if ((unsigned)(acc_key_pi(1, r, 0) - a) > span) s1[r] = -INFINITY;
+      }
+    }
+    return own;
+  };
+  bf16x8 qf[D / 16];
+  load_q<D>(Q + hoff, valid ? i : -1, hi, qf);
+  f32x16 o[D / 32];
+  float m_run, l_run;
+  const int nkbf = F * nbf + nbt;
+  vt_attend<D, FNW, false>(nt, ent_raw, prep, K + hoff + (size_t)f * S * D,
+                           Vt + ((size_t)h * nkbf + (size_t)f * nbf) * (BK * D), S, k0, k1, k2, V0, V1, V2, qf,
+                           wave, lane, c, o, m_run, l_run);
+  __builtin_amdgcn_s_waitcnt(0);  // no DMA may land after the work-group ends
+  const float lt = l_run + __shfl_xor(l_run, 32);
+  if (!valid) return;
+  const size_t slot = ((size_t)h * n_s + sidx) * F + f;
+  float *dst = part_o + slot * D;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      *reinterpret_cast<f32x4 *>(dst + 32 * db + 8 * g + 4 * hi) =
+          f32x4{o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]};
+  if (hi == 0) {
+    part_ml[slot * 2] = m_run;
+    part_ml[slot * 2 + 1] = lt;
+  }
+}
+
 // Merge the chunks of one sampled row into its three outputs and take the
 // squared errors of the masked ones.  Full: every chunk of the full pass.
 // Spatial: the full pass's chunks of the frames within ks of the row's frame
@@ -515,11 +367,14 @@ void profile_combine(const float *__restrict__ fo, const float *__restrict__ fml
   double out[3];
   out[0] = L0 > 0.0 ? A0 / L0 : 0.0;
   out[1] = L1 > 0.0 ? A1 / L1 : 0.0;
-  if (cover & 4) {
+  if ((cover & 4) || text_i) {
     out[2] = out[0];
   } else {
+    // the temporal pass's frame partials, then the full pass's text chunks
+    // (every row keeps the text keys)
     float M = -INFINITY;
     for (int ch = 0; ch < Ct; ++ch) M = fmaxf(M, tml[(rt + ch) * 2]);
+    for (int ch = F * P; ch < Cf; ++ch) M = fmaxf(M, fml[(rf + ch) * 2]);
     const float Mr = M == -INFINITY ? 0.f : M;
     double L = 0.0, acc = 0.0;
     auto add = [&](float m, float l, float x) {
@@ -540,6 +395,7 @@ void profile_combine(const float *__restrict__ fo, const float *__restrict__ fml
       for (int u = 0; u < kB; ++u) add(m[u], l[u], x[u]);
     }
     for (; ct < Ct; ++ct) add(tml[(rt + ct) * 2], tml[(rt + ct) * 2 + 1], to[(rt + ct) * D + De]);
+    for (int ch = F * P; ch < Cf; ++ch) add(fml[(rf + ch) * 2], fml[(rf + ch) * 2 + 1], fo[(rf + ch) * D + De]);
     out[2] = L > 0.0 ? acc / L : 0.0;
   }
   const double ds = out[1] - out[0], dt = out[2] - out[0];
@@ -593,17 +449,15 @@ void profile_label(const double *__restrict__ se, int n_s, int D, int32_t *__res
 }  // namespace
 
 size_t profile_mfma_ws_bytes(const Dims &dm, int n_s) {
-  return carve(nullptr, dm, n_s, profile_grid_full(dm, n_s).nchunks, profile_grid(dm, n_s).nchunks).bytes;
+  return carve(nullptr, dm, n_s, profile_grid_full(dm, n_s).nchunks, dm.F).bytes;
 }
 
 hipError_t launch_profile_mfma(const Dims &dm, const void *Q, const void *K, const void *V,
                                const int32_t *sample_idx, int n_s, int ks, int wt, float scale, int32_t *labels,
                                float *mse, void *ws, hipStream_t st) {
   const float c = scale * kLog2e;
-  const ProfileGrid g = profile_grid(dm, n_s);       // temporal pass
-  const FrameGrid gf = profile_grid_full(dm, n_s);   // full pass
-  const Parts p = carve(ws, dm, n_s, gf.nchunks, g.nchunks);
-  const int nkb = (dm.N + BK - 1) / BK;
+  const FrameGrid gf = profile_grid_full(dm, n_s);   // full pass; the temporal one takes one chunk per frame
+  const Parts p = carve(ws, dm, n_s, gf.nchunks, dm.F);
   // A mask that keeps every key of every row: the spatial one when every
   // frame lies within ks of every other (ks >= F - 1), the temporal one when
   // the window of position 0 reaches the last video key and that of position
@@ -614,15 +468,14 @@ hipError_t launch_profile_mfma(const Dims &dm, const void *Q, const void *K, con
   // key-tiled V^T of V in its own token order, every frame from a new tile
   const hipError_t ev = launch_layout_vt(dm, V, p.vt, nullptr, st, true);
   if (ev != hipSuccess) return ev;
-  const dim3 gridf(gf.nqg * gf.nchunks * dm.H), grid(g.nqg, g.nchunks, dm.H);
+  const dim3 gridf(gf.nqg * gf.nchunks * dm.H), gridt(gf.nqg * dm.F * dm.H);
 #define SVG_PROFILE_PASSES(DD)                                                                                   \
   hipLaunchKernelGGL((profile_full_vt<DD>), gridf, dim3(FNT), 0, st, (const bf16_t *)Q, (const bf16_t *)K, p.vt, \
                      sample_idx, n_s, dm.F, dm.S, dm.T, gf.nqg, gf.nbf, gf.nbt, gf.tpp, gf.P, gf.nchunks, c, p.fo, \
                      p.fml);                                                                                     \
   if (!(cover & 4))                                                                                             \
-    hipLaunchKernelGGL((profile_temporal_mfma<DD>), grid, dim3(PNT), 0, st, (const bf16_t *)Q, (const bf16_t *)K, \
-                       (const bf16_t *)V, sample_idx, p.ord_t, n_s, dm.F, dm.S, dm.N, wt, nkb, g.tiles_per_chunk,  \
-                       g.nchunks, c, p.to, p.tml)
+    hipLaunchKernelGGL((profile_temporal_vt<DD>), gridt, dim3(FNT), 0, st, (const bf16_t *)Q, (const bf16_t *)K,   \
+                       p.vt, sample_idx, p.ord_t, n_s, dm.F, dm.S, dm.T, wt, gf.nqg, gf.nbf, gf.nbt, c, p.to, p.tml)
   if (dm.d == 128) {
     SVG_PROFILE_PASSES(128);
   } else {
@@ -630,7 +483,7 @@ hipError_t launch_profile_mfma(const Dims &dm, const void *Q, const void *K, con
   }
 #undef SVG_PROFILE_PASSES
   hipLaunchKernelGGL(profile_combine, dim3(n_s, dm.H), dim3(128), 0, st, p.fo, p.fml, gf.nchunks, gf.P, p.to, p.tml,
-                     g.nchunks, sample_idx, n_s, dm.F, dm.S, ks, cover, dm.d, c, p.se);
+                     dm.F, sample_idx, n_s, dm.F, dm.S, ks, cover, dm.d, c, p.se);
   hipLaunchKernelGGL(profile_label, dim3(dm.H), dim3(256), 0, st, p.se, n_s, dm.d, labels, mse);
   return hipGetLastError();
 }
