@@ -204,8 +204,9 @@ __device__ __forceinline__ int build_union_list(const int32_t *__restrict__ row_
 //               scalar register late.
 //   prep(s0, s1, e): masks the scores of the tile with entry e in place and
 //               returns whether the lane's row keeps any key of it.
-// K and V^T tiles come from Kh (row-major, N rows) and Vth (key-tiled, every
-// tile full) through three LDS stages each (k0..k2, v0..v2, TB bytes, all
+// K and V^T tiles come from Kh (row-major, N rows; tile e starts at row
+// krow(e), by default kv-block * 64) and Vth (key-tiled, every tile full,
+// tile e at kv-block e) through three LDS stages each (k0..k2, v0..v2, TB bytes, all
 // waves of the work-group call this together: it contains barriers).  On
 // return o, m_run and l_run hold the un-normalised output, the reference
 // maximum and this lane's partial row sum: of the bf16 probabilities that
@@ -221,11 +222,17 @@ __device__ __forceinline__ int build_union_list(const int32_t *__restrict__ row_
 //   (C) wait until only this step's DMAs are in flight, one barrier.
 // S^T's rows (keys) are read from K in the order pi, so the accumulator
 // layout of S^T is the B-operand layout of P^T with keys in natural order.
-template <int D, int NW, bool SUM_BF16 = true, typename EntRaw, typename Prep>
+// The first K row of the tile with entry e: kv-block e of K.
+struct KvBlockRow {
+  __device__ int operator()(int e) const { return (e & 0xFFFFFF) * BK; }
+};
+
+template <int D, int NW, bool SUM_BF16 = true, typename EntRaw, typename Prep, typename KRow = KvBlockRow>
 __device__ __forceinline__ void vt_attend(int nt, EntRaw ent_raw, Prep prep, const bf16_t *__restrict__ Kh,
                                           const bf16_t *__restrict__ Vth, int N, char *k0, char *k1, char *k2,
                                           char *v0, char *v1, char *v2, const bf16x8 (&qf)[D / 16], int wave,
-                                          int lane, float c, f32x16 (&o)[D / 32], float &m_run, float &l_run) {
+                                          int lane, float c, f32x16 (&o)[D / 32], float &m_run, float &l_run,
+                                          KRow krow = KRow{}) {
   using T = DTile<D>;
   constexpr int TB = T::TBYTES;            // K tile bytes == V^T tile bytes
   constexpr int PK = T::BLOCKS / NW;       // DMA instructions per wave per tile
@@ -260,11 +267,25 @@ __device__ __forceinline__ void vt_attend(int nt, EntRaw ent_raw, Prep prep, con
 
   // Tile DMAs through a buffer resource based at the tile: rows past N fall
   // outside the resource's range and read as zero (their scores are masked).
+  // (The default keeps the kv-block arithmetic as is: the attention kernels
+  // compile to the same code as before the K row became a parameter.)
+  constexpr bool kBlockRows = std::is_same<KRow, KvBlockRow>::value;
+  auto k_row = [&](int e) -> int {
+    if constexpr (kBlockRows) return 0;
+    else return krow(e);
+  };
   auto dma_k = [&](int e, char *tile) {
-    const int kb = e & 0xFFFFFF;
-    const int left = (N - kb * BK) * T::ROWB;
-    dma_tile_buf<D, NW>(reinterpret_cast<const char *>(Kh) + (size_t)kb * TB, left < TB ? left : TB, tile, wave,
-                        kdma);
+    if constexpr (kBlockRows) {
+      const int kb = e & 0xFFFFFF;
+      const int left = (N - kb * BK) * T::ROWB;
+      dma_tile_buf<D, NW>(reinterpret_cast<const char *>(Kh) + (size_t)kb * TB, left < TB ? left : TB, tile, wave,
+                          kdma);
+    } else {
+      const int row0 = k_row(e);
+      const int left = (N - row0) * T::ROWB;
+      dma_tile_buf<D, NW>(reinterpret_cast<const char *>(Kh) + (size_t)row0 * T::ROWB, left < TB ? left : TB, tile,
+                          wave, kdma);
+    }
   };
   auto dma_v = [&](int e, char *tile) {
     const int kb = e & 0xFFFFFF;
@@ -300,10 +321,17 @@ __device__ __forceinline__ void vt_attend(int nt, EntRaw ent_raw, Prep prep, con
     // released.  Their 2*PK instructions are spread over the loop steps
     // below: issued back to back by every wave right after the barrier, they
     // queue up in the load unit and hold the waves at issue.
-    const int kb_k = e3 & 0xFFFFFF, kb_v = e2 & 0xFFFFFF;
-    const int kleft = (N - kb_k * BK) * T::ROWB;
-    const __amdgpu_buffer_rsrc_t rk =
-        tile_rsrc(reinterpret_cast<const char *>(Kh) + (size_t)kb_k * TB, kleft < TB ? kleft : TB);
+    const int kb_v = e2 & 0xFFFFFF;
+    __amdgpu_buffer_rsrc_t rk;
+    if constexpr (kBlockRows) {
+      const int kb_k = e3 & 0xFFFFFF;
+      const int kleft = (N - kb_k * BK) * T::ROWB;
+      rk = tile_rsrc(reinterpret_cast<const char *>(Kh) + (size_t)kb_k * TB, kleft < TB ? kleft : TB);
+    } else {
+      const int row_k = k_row(e3);
+      const int kleft = (N - row_k) * T::ROWB;
+      rk = tile_rsrc(reinterpret_cast<const char *>(Kh) + (size_t)row_k * T::ROWB, kleft < TB ? kleft : TB);
+    }
     const __amdgpu_buffer_rsrc_t rv = tile_rsrc(reinterpret_cast<const char *>(Vth) + (size_t)kb_v * TB, TB);
     auto dma_slot = [&](int ks) {
 #pragma unroll

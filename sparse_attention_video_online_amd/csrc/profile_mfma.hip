@@ -64,6 +64,33 @@ FrameGrid profile_grid_full(const Dims &dm, int n_s) {
   return g;
 }
 
+// Frames per temporal work-group.  Its walk is about (frames) x (tiles that
+// a 256-sample group's ranges reach in a frame: the positions the group
+// spans, S * 256 / n_s, plus a range on each side) plus ~8 tiles of fixed
+// cost; work-groups of one length finish in ceil(count / 256) rounds, so
+// take the fewest rounds x length.  At the HunyuanVideo layer shape: 2
+// frames (17 chunks, 2,040 work-groups of ~64 tiles).
+struct TemporalGrid { int fpc, nchunks; };
+
+TemporalGrid profile_grid_temporal(const Dims &dm, int n_s, int wt) {
+  const int nqg = (n_s + FQ - 1) / FQ, nbf = (dm.S + BK - 1) / BK;
+  const long long wq = min(wt, dm.N) / dm.F;
+  const long long span = min((long long)dm.S, (long long)dm.S * FQ / max(n_s, 1) + 2 * wq + 2);
+  const int ntf = min(nbf, (int)((span + BK - 1) / BK) + 1);
+  long long best = -1;
+  TemporalGrid g{1, dm.F};
+  for (int fpc = 1; fpc <= dm.F; ++fpc) {
+    const int nch = (dm.F + fpc - 1) / fpc;
+    const long long nwg = (long long)dm.H * nqg * nch;
+    const long long cost = (nwg + kFullSlots - 1) / kFullSlots * ((long long)fpc * ntf + 8);
+    if (best < 0 || cost < best) {
+      best = cost;
+      g = TemporalGrid{fpc, nch};
+    }
+  }
+  return g;
+}
+
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 struct Parts {
@@ -214,26 +241,28 @@ void profile_full_vt(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K,
 
 // The temporal pass on the V^T tile pipeline: the work-group's 256 samples
 // (in position-major order, so they share few grid positions) against the
-// video keys of one frame f.  A row at grid position pi keeps, in frame f,
-// the positions pi - floor((w_t + f)/F) .. pi + floor((F - 1 + w_t - f)/F)
-// (its rank window p*F + f within [pi*F - w_t, pi*F + F - 1 + w_t]); the
-// work-group walks the frame's tiles that the union of its rows' ranges
-// touches, and each row masks the keys outside its own range.  Text rows are
-// skipped (they keep every key: their temporal output is the full one) and
-// the text keys, kept by every row, come from the full pass's text chunks in
-// the merge.  The partial of (sample, frame) goes to slot (h, sample, f).
+// video keys of frames fa .. fa + fpc - 1, in one pipeline run.  A row at
+// grid position pi keeps, in frame f, the positions pi - floor((w_t + f)/F)
+// .. pi + floor((F - 1 + w_t - f)/F) (its rank window p*F + f within
+// [pi*F - w_t, pi*F + F - 1 + w_t]); the work-group walks, in each of its
+// frames, the tiles that the union of its rows' ranges touches, and each row
+// masks the keys outside its own range.  Text rows are skipped (they keep
+// every key: their temporal output is the full one) and the text keys, kept
+// by every row, come from the full pass's text chunks in the merge.  The
+// partial of (sample, frame group) goes to slot (h, sample, chunk).
 template <int D>
 __global__ __launch_bounds__(FNT, 1)
 void profile_temporal_vt(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K, const bf16_t *__restrict__ Vt,
                          const int32_t *__restrict__ sample_idx, const int32_t *__restrict__ order, int n_s, int F,
-                         int S, int T, int wt, int nqg, int nbf, int nbt, float c, float *__restrict__ part_o,
-                         float *__restrict__ part_ml) {
+                         int S, int T, int wt, int nqg, int nbf, int nbt, int fpc, int Ct, float c,
+                         float *__restrict__ part_o, float *__restrict__ part_ml) {
   constexpr int TB = DTile<D>::TBYTES;
   // V^T stages named to sort first, below 64 KB of LDS (immediate offsets)
   __shared__ __attribute__((aligned(1024))) char k0[TB], k1[TB], k2[TB], V0[TB], V1[TB], V2[TB];
   __shared__ int prange[2];   // smallest and largest grid position of the video rows
   const int work = xcd_remap(blockIdx.x, gridDim.x);
-  const int qg = work % nqg, f = (work / nqg) % F, h = work / (nqg * F);
+  const int qg = work % nqg, chunk = (work / nqg) % Ct, h = work / (nqg * Ct);
+  const int fa = chunk * fpc, nf = min(F, fa + fpc) - fa;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hi = lane >> 5;
@@ -244,10 +273,10 @@ void profile_temporal_vt(const bf16_t *__restrict__ Q, const bf16_t *__restrict_
   const int i = pos < n_s ? sample_idx[sidx] : FS;
   const bool valid = i < FS;                    // a video row of this work-group
   const int pi = valid ? i % S : 0;
-  // this row's kept positions in frame f (w_t clamped to N keeps int32)
+  // w_t clamped to N keeps int32; a row's range in frame f reaches wq or
+  // wq + 1 positions to each side
   const int wtc = min(wt, N);
   const int wq = wtc / F, wr = wtc - wq * F;
-  const int lo = max(pi - (wq + (f + wr >= F)), 0), hk = min(pi + (wq + (f < wr)), S - 1);
   if (tid == 0) {
     prange[0] = 0x7fffffff;
     prange[1] = -1;
@@ -260,12 +289,23 @@ void profile_temporal_vt(const bf16_t *__restrict__ Q, const bf16_t *__restrict_
   __syncthreads();
   const int p_lo = prange[0], p_hi = prange[1];
   if (p_hi < 0) return;   // no video row: nothing to compute (uniform)
-  // the union of the rows' ranges: local tiles t0 .. t0 + nt - 1 of frame f
-  const int u_lo = max(p_lo - (wq + (f + wr >= F)), 0), u_hi = min(p_hi + (wq + (f < wr)), S - 1);
-  const int t0 = u_lo / BK, nt = u_hi / BK - t0 + 1;
-  auto ent_raw = [&](int j) -> int { return t0 + (j < nt ? j : nt - 1); };
+  // local tiles t0 .. t0 + ntf - 1 cover the union of the rows' ranges in
+  // every frame; tile j of the walk is tile t0 + j % ntf of frame fa + j / ntf
+  const int t0 = max(p_lo - wq - 1, 0) / BK, ntf = min(p_hi + wq + 1, S - 1) / BK - t0 + 1;
+  const int nt = nf * ntf;
+  auto ent_raw = [&](int j) -> int {
+    const int jj = j < nt ? j : nt - 1;
+    const int fr = jj / ntf;
+    return (fa + fr) * nbf + t0 + (jj - fr * ntf);   // tile of the frame-padded V^T
+  };
+  // K is not padded: the tile's first row is frame f's row 64 t
+  auto krow = [=](int e) -> int {
+    const int f = e / nbf;
+    return f * S + (e - f * nbf) * BK;
+  };
   auto prep = [&](f32x16 &s0, f32x16 &s1, int e) -> bool {
-    const int kb = e * BK;
+    const int f = e / nbf, kb = (e - f * nbf) * BK;
+    const int lo = max(pi - (wq + (f + wr >= F)), 0), hk = min(pi + (wq + (f < wr)), S - 1);
     const bool own = valid && lo <= kb + BK - 1 && hk >= kb;
     const bool whole = !valid || (lo <= kb && hk >= kb + BK - 1);
     if (__builtin_amdgcn_ballot_w64(!whole)) {
@@ -288,13 +328,12 @@ void profile_temporal_vt(const bf16_t *__restrict__ Q, const bf16_t *__restrict_
   f32x16 o[D / 32];
   float m_run, l_run;
   const int nkbf = F * nbf + nbt;
-  vt_attend<D, FNW, false>(nt, ent_raw, prep, K + hoff + (size_t)f * S * D,
-                           Vt + ((size_t)h * nkbf + (size_t)f * nbf) * (BK * D), S, k0, k1, k2, V0, V1, V2, qf,
-                           wave, lane, c, o, m_run, l_run);
+  vt_attend<D, FNW, false>(nt, ent_raw, prep, K + hoff, Vt + (size_t)h * nkbf * (BK * D), N, k0, k1, k2, V0, V1,
+                           V2, qf, wave, lane, c, o, m_run, l_run, krow);
   __builtin_amdgcn_s_waitcnt(0);  // no DMA may land after the work-group ends
   const float lt = l_run + __shfl_xor(l_run, 32);
   if (!valid) return;
-  const size_t slot = ((size_t)h * n_s + sidx) * F + f;
+  const size_t slot = ((size_t)h * n_s + sidx) * Ct + chunk;
   float *dst = part_o + slot * D;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
@@ -449,15 +488,16 @@ void profile_label(const double *__restrict__ se, int n_s, int D, int32_t *__res
 }  // namespace
 
 size_t profile_mfma_ws_bytes(const Dims &dm, int n_s) {
-  return carve(nullptr, dm, n_s, profile_grid_full(dm, n_s).nchunks, dm.F).bytes;
+  return carve(nullptr, dm, n_s, profile_grid_full(dm, n_s).nchunks, dm.F).bytes;   // temporal chunks <= F
 }
 
 hipError_t launch_profile_mfma(const Dims &dm, const void *Q, const void *K, const void *V,
                                const int32_t *sample_idx, int n_s, int ks, int wt, float scale, int32_t *labels,
                                float *mse, void *ws, hipStream_t st) {
   const float c = scale * kLog2e;
-  const FrameGrid gf = profile_grid_full(dm, n_s);   // full pass; the temporal one takes one chunk per frame
-  const Parts p = carve(ws, dm, n_s, gf.nchunks, dm.F);
+  const FrameGrid gf = profile_grid_full(dm, n_s);          // full pass
+  const TemporalGrid gt = profile_grid_temporal(dm, n_s, wt);   // temporal pass
+  const Parts p = carve(ws, dm, n_s, gf.nchunks, dm.F);       // temporal partials laid out for up to F chunks
   // A mask that keeps every key of every row: the spatial one when every
   // frame lies within ks of every other (ks >= F - 1), the temporal one when
   // the window of position 0 reaches the last video key and that of position
@@ -468,14 +508,15 @@ hipError_t launch_profile_mfma(const Dims &dm, const void *Q, const void *K, con
   // key-tiled V^T of V in its own token order, every frame from a new tile
   const hipError_t ev = launch_layout_vt(dm, V, p.vt, nullptr, st, true);
   if (ev != hipSuccess) return ev;
-  const dim3 gridf(gf.nqg * gf.nchunks * dm.H), gridt(gf.nqg * dm.F * dm.H);
+  const dim3 gridf(gf.nqg * gf.nchunks * dm.H), gridt(gf.nqg * gt.nchunks * dm.H);
 #define SVG_PROFILE_PASSES(DD)                                                                                   \
   hipLaunchKernelGGL((profile_full_vt<DD>), gridf, dim3(FNT), 0, st, (const bf16_t *)Q, (const bf16_t *)K, p.vt, \
                      sample_idx, n_s, dm.F, dm.S, dm.T, gf.nqg, gf.nbf, gf.nbt, gf.tpp, gf.P, gf.nchunks, c, p.fo, \
                      p.fml);                                                                                     \
   if (!(cover & 4))                                                                                             \
     hipLaunchKernelGGL((profile_temporal_vt<DD>), gridt, dim3(FNT), 0, st, (const bf16_t *)Q, (const bf16_t *)K,   \
-                       p.vt, sample_idx, p.ord_t, n_s, dm.F, dm.S, dm.T, wt, gf.nqg, gf.nbf, gf.nbt, c, p.to, p.tml)
+                       p.vt, sample_idx, p.ord_t, n_s, dm.F, dm.S, dm.T, wt, gf.nqg, gf.nbf, gf.nbt, gt.fpc,        \
+                       gt.nchunks, c, p.to, p.tml)
   if (dm.d == 128) {
     SVG_PROFILE_PASSES(128);
   } else {
@@ -483,7 +524,7 @@ hipError_t launch_profile_mfma(const Dims &dm, const void *Q, const void *K, con
   }
 #undef SVG_PROFILE_PASSES
   hipLaunchKernelGGL(profile_combine, dim3(n_s, dm.H), dim3(128), 0, st, p.fo, p.fml, gf.nchunks, gf.P, p.to, p.tml,
-                     dm.F, sample_idx, n_s, dm.F, dm.S, ks, cover, dm.d, c, p.se);
+                     gt.nchunks, sample_idx, n_s, dm.F, dm.S, ks, cover, dm.d, c, p.se);
   hipLaunchKernelGGL(profile_label, dim3(dm.H), dim3(256), 0, st, p.se, n_s, dm.d, labels, mse);
   return hipGetLastError();
 }
