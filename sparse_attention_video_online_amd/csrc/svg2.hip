@@ -209,6 +209,157 @@ void km_assign_mfma(const bf16_t *__restrict__ X, const float *__restrict__ tab,
   }
 }
 
+// The assignment for d = 64 on the bf16 matrix cores.  Each fp64 centroid
+// value is split into three bf16 terms c = c1 + c2 + c3, each the bf16
+// rounding of what the earlier terms leave (24 significant bits in all), so
+// x.c = x.c1 + x.c2 + x.c3 with every product exact in fp32 (bf16 x bf16)
+// and the sum accumulated in fp32 on v_mfma_f32_32x32x16_bf16: the precision
+// of the fp32 kernel above, in another summation order, at 16 dims per
+// instruction instead of 2.  Table per head: for each centroid its three
+// terms as rows of D bf16, padded to 3 D + 8 (so the 32 lanes of a 16-byte
+// read spread over the banks), then ||c||^2 per centroid as in km_prep.
+template <int D>
+struct KmTab3 {
+  static constexpr int ROWH = 3 * D + 8;   // bf16 per centroid
+  __host__ __device__ static size_t floats(int kpad) { return (size_t)kpad * (ROWH / 2 + 1); }
+};
+
+__device__ __forceinline__ void split3(double c, bf16_t &c1, bf16_t &c2, bf16_t &c3) {
+  c1 = f32_to_bf16((float)c);
+  double r = c - (double)bf16_to_f32(c1);
+  c2 = f32_to_bf16((float)r);
+  r -= (double)bf16_to_f32(c2);
+  c3 = f32_to_bf16((float)r);
+}
+
+// Row j of the three-term table from the centroid's D fp64 values (one
+// thread per dim e < D; threads e < 8 also zero the padding; thread 0 takes
+// ||c||^2 in dim order, as km_prep).
+template <int D>
+__device__ __forceinline__ void km_tab3_row(const double *cv, int e, int j, int kpad, float *t) {
+  using TB = KmTab3<D>;
+  bf16_t *row = reinterpret_cast<bf16_t *>(t) + (size_t)j * TB::ROWH;
+  if (e < D) {
+    bf16_t c1, c2, c3;
+    split3(cv[e], c1, c2, c3);
+    row[e] = c1;
+    row[D + e] = c2;
+    row[2 * D + e] = c3;
+  }
+  if (e < 8) row[3 * D + e] = 0;
+  if (e == 0) {
+    double n2 = 0.0;
+    for (int i = 0; i < D; ++i) {
+      const double v = cv[i];
+      n2 += v * v;
+    }
+    t[(size_t)kpad * (TB::ROWH / 2) + j] = (float)n2;
+  }
+}
+
+// Initial three-term table: one block per centroid (padding rows: zero
+// terms, ||c||^2 = +inf so they never win).
+template <int D>
+__global__ __launch_bounds__(128)
+void km_prep3(const double *__restrict__ cent, int k, int kpad, float *__restrict__ tab) {
+  using TB = KmTab3<D>;
+  __shared__ double cv[D];
+  const int h = blockIdx.y, j = blockIdx.x, e = threadIdx.x;
+  float *t = tab + (size_t)h * TB::floats(kpad);
+  if (j >= k) {
+    bf16_t *row = reinterpret_cast<bf16_t *>(t) + (size_t)j * TB::ROWH;
+    for (int i = e; i < TB::ROWH; i += 128) row[i] = 0;
+    if (e == 0) t[(size_t)kpad * (TB::ROWH / 2) + j] = INFINITY;
+    return;
+  }
+  if (e < D) cv[e] = cent[((size_t)h * k + j) * D + e];
+  __syncthreads();
+  km_tab3_row<D>(cv, e, j, kpad, t);
+}
+
+// One wave = 64 points (two 32-point blocks), 4 waves per work-group.
+template <int D>
+__global__ __launch_bounds__(256)
+void km_assign_bf3(const bf16_t *__restrict__ X, const float *__restrict__ tab, int N, int k, int kpad,
+                   int32_t *__restrict__ assign) {
+  using TB = KmTab3<D>;
+  extern __shared__ __attribute__((aligned(16))) float kt[];   // the head's table
+  const int h = blockIdx.y;
+  const size_t nf = TB::floats(kpad);
+  const float *th = tab + (size_t)h * nf;
+  for (size_t i = threadIdx.x * 4; i < nf; i += 256 * 4) {
+    if (i + 4 <= nf) *reinterpret_cast<f32x4 *>(kt + i) = *reinterpret_cast<const f32x4 *>(th + i);
+    else for (size_t j = i; j < nf; ++j) kt[j] = th[j];
+  }
+  __syncthreads();
+  const bf16_t *ct = reinterpret_cast<const bf16_t *>(kt);
+  const float *cn = kt + (size_t)kpad * (TB::ROWH / 2);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int p0 = blockIdx.x * 256 + wave * 64 + l32, p1 = p0 + 32;
+  // B operands: dims 16 s + 8 hi .. + 7 of the lane's point
+  bf16x8 xb0[D / 16], xb1[D / 16];
+  auto load_x = [&](int p, bf16x8 (&xb)[D / 16]) {
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) {
+      u32x4 w = u32x4{0, 0, 0, 0};
+      if (p < N) w = *reinterpret_cast<const u32x4 *>(X + ((size_t)h * N + p) * D + 16 * st + 8 * hi);
+      xb[st] = __builtin_bit_cast(bf16x8, w);
+    }
+  };
+  load_x(p0, xb0);
+  load_x(p1, xb1);
+  float best0 = INFINITY, best1 = INFINITY;
+  int arg0 = 0, arg1 = 0;
+  for (int cb = 0; cb < kpad / 32; ++cb) {
+    f32x16 a0 = f32x16{}, a1 = f32x16{};
+    const bf16_t *ar = ct + (size_t)(cb * 32 + l32) * TB::ROWH + 8 * hi;
+#pragma unroll
+    for (int tm = 0; tm < 3; ++tm) {
+#pragma unroll
+      for (int st = 0; st < D / 16; ++st) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(ar + tm * D + 16 * st);
+        a0 = core::mfma32(a, xb0[st], a0);
+        a1 = core::mfma32(a, xb1[st], a1);
+      }
+    }
+    // lane rows: centroid cb*32 + 8*(r/4) + 4*hi + r%4, increasing in r
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int cbase = cb * 32 + 8 * g + 4 * hi;
+      const f32x4 nn = *reinterpret_cast<const f32x4 *>(cn + cbase);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float d0 = __builtin_fmaf(-2.f, a0[4 * g + q], nn[q]);
+        const float d1 = __builtin_fmaf(-2.f, a1[4 * g + q], nn[q]);
+        if (d0 < best0) {
+          best0 = d0;
+          arg0 = cbase + q;
+        }
+        if (d1 < best1) {
+          best1 = d1;
+          arg1 = cbase + q;
+        }
+      }
+    }
+  }
+  // merge the two lanes of each point (lower index on equal distance)
+  auto merge = [&](float &b, int &a) {
+    const float ob = __shfl_xor(b, 32);
+    const int oa = __shfl_xor(a, 32);
+    if (ob < b || (ob == b && oa < a)) {
+      b = ob;
+      a = oa;
+    }
+  };
+  merge(best0, arg0);
+  merge(best1, arg1);
+  if (hi == 0) {
+    if (p0 < N) assign[(size_t)h * N + p0] = arg0;
+    if (p1 < N) assign[(size_t)h * N + p1] = arg1;
+  }
+}
+
 // Centroid of cluster j = mean of its members, taken in sorted (= index)
 // order.  An empty cluster keeps its centroid.  With tab (the MFMA
 // assignment), the block also writes centroid j's row of the next
@@ -218,7 +369,7 @@ template <typename T>
 __global__ __launch_bounds__(128)
 void km_update(const T *__restrict__ X, const int32_t *__restrict__ perm, const int32_t *__restrict__ offs, int N,
                int k, int D, double *__restrict__ cent, int32_t *__restrict__ sizes, float *__restrict__ tab,
-               int kpad) {
+               int kpad, int tab3) {
   __shared__ double cv[128];
   const int h = blockIdx.y, j = blockIdx.x, e = threadIdx.x;
   const int o0 = offs[(size_t)h * (k + 1) + j], o1 = offs[(size_t)h * (k + 1) + j + 1];
@@ -247,6 +398,10 @@ void km_update(const T *__restrict__ X, const int32_t *__restrict__ perm, const 
   if (tab == nullptr) return;
   if (e < D) cv[e] = cj[e];   // each thread reads back its own dim
   __syncthreads();
+  if (tab3) {   // the three-term bf16 table (d = 64)
+    km_tab3_row<64>(cv, e, j, kpad, tab + (size_t)h * KmTab3<64>::floats(kpad));
+    return;
+  }
   const int row = D / 2 + kKmPad;
   float *t = tab + (size_t)h * kpad * (2 * row + 1);
   if (e < D) t[((size_t)j * 2 + (e & 1)) * row + (e >> 1)] = (float)cv[e];
@@ -608,7 +763,7 @@ int varlen_max_tiles(const Dims &dm, int kq, int bq) { return (dm.N + bq - 1) / 
 
 size_t kmeans_ws_bytes(const Dims &dm, int k) {
   const int kpad = (k + 31) / 32 * 32;
-  const size_t tab = dm.d == 64 ? KmTab<64>::floats(kpad) : KmTab<128>::floats(kpad);
+  const size_t tab = dm.d == 64 ? max(KmTab<64>::floats(kpad), KmTab3<64>::floats(kpad)) : KmTab<128>::floats(kpad);
   return align256((size_t)dm.H * dm.N * sizeof(int32_t)) + align256((size_t)dm.H * (k + 1) * sizeof(int32_t)) +
          align256((size_t)dm.H * tab * sizeof(float)) + sort_scratch_bytes(dm, k);
 }
@@ -619,10 +774,9 @@ hipError_t launch_kmeans(const Dims &dm, bool bf16, const void *X, int k, int it
   int32_t *offs = (int32_t *)((char *)ws + align256((size_t)dm.H * dm.N * sizeof(int32_t)));
   float *tab = (float *)((char *)offs + align256((size_t)dm.H * (k + 1) * sizeof(int32_t)));
   const int kpad = (k + 31) / 32 * 32;
-  int32_t *scnt = (int32_t *)((char *)tab +
-                              align256((size_t)dm.H *
-                                       (dm.d == 64 ? KmTab<64>::floats(kpad) : KmTab<128>::floats(kpad)) *
-                                       sizeof(float)));
+  const size_t tab_floats =
+      dm.d == 64 ? max(KmTab<64>::floats(kpad), KmTab3<64>::floats(kpad)) : KmTab<128>::floats(kpad);
+  int32_t *scnt = (int32_t *)((char *)tab + align256((size_t)dm.H * tab_floats * sizeof(float)));
   if (bf16)
     hipLaunchKernelGGL(km_init<bf16_t>, dim3(k, dm.H), dim3(128), 0, st, (const bf16_t *)X, init_idx, dm.N, dm.d, k,
                        centroids);
@@ -638,8 +792,16 @@ hipError_t launch_kmeans(const Dims &dm, bool bf16, const void *X, int k, int it
     if (e != hipSuccess) return e;
   }
   // bf16: the MFMA assignment; its table takes kpad*(D+9) floats of LDS
+  // bf16, d = 64: the three-term bf16 table on the bf16 matrix cores
+  const size_t lds3 = KmTab3<64>::floats(kpad) * sizeof(float);
+  const bool bf3 = bf16 && dm.d == 64 && lds3 <= 160 * 1024;
+  if (bf3 && lds3 > 65536) {
+    const hipError_t e = hipFuncSetAttribute((const void *)km_assign_bf3<64>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds3);
+    if (e != hipSuccess) return e;
+  }
   const size_t mlds = (dm.d == 64 ? KmTab<64>::floats(kpad) : KmTab<128>::floats(kpad)) * sizeof(float);
-  const bool mfma = bf16 && mlds <= 160 * 1024;
+  const bool mfma = bf16 && !bf3 && mlds <= 160 * 1024;
   if (mfma && mlds > 65536) {
     const void *mf = dm.d == 64 ? (const void *)km_assign_mfma<64> : (const void *)km_assign_mfma<128>;
     const hipError_t e = hipFuncSetAttribute(mf, hipFuncAttributeMaxDynamicSharedMemorySize, (int)mlds);
@@ -647,12 +809,17 @@ hipError_t launch_kmeans(const Dims &dm, bool bf16, const void *X, int k, int it
   }
   const dim3 pgrid((kpad + 255) / 256, dm.H), mgrid((dm.N + 255) / 256, dm.H);
   // the table of the initial centroids; each update then writes the next one
-  if (mfma && dm.d == 64)
+  if (bf3)
+    hipLaunchKernelGGL(km_prep3<64>, dim3(kpad, dm.H), dim3(128), 0, st, centroids, k, kpad, tab);
+  else if (mfma && dm.d == 64)
     hipLaunchKernelGGL(km_prep<64>, pgrid, dim3(256), 0, st, centroids, k, kpad, tab);
   else if (mfma)
     hipLaunchKernelGGL(km_prep<128>, pgrid, dim3(256), 0, st, centroids, k, kpad, tab);
   for (int it = 0; it < iters; ++it) {
-    if (mfma && dm.d == 64) {
+    if (bf3) {
+      hipLaunchKernelGGL(km_assign_bf3<64>, mgrid, dim3(256), lds3, st, (const bf16_t *)X, tab, dm.N, k, kpad,
+                         assign);
+    } else if (mfma && dm.d == 64) {
       hipLaunchKernelGGL(km_assign_mfma<64>, mgrid, dim3(256), mlds, st, (const bf16_t *)X, tab, dm.N, k, kpad,
                          assign);
     } else if (mfma) {
@@ -671,13 +838,13 @@ hipError_t launch_kmeans(const Dims &dm, bool bf16, const void *X, int k, int it
       hipLaunchKernelGGL((km_assign<float, 128>), grid, dim3(256), lds, st, (const float *)X, centroids, dm.N, k,
                          assign);
     launch_sort(dm, assign, k, perm, offs, scnt, st);
-    float *const next_tab = (mfma && it + 1 < iters) ? tab : nullptr;
+    float *const next_tab = ((mfma || bf3) && it + 1 < iters) ? tab : nullptr;
     if (bf16)
       hipLaunchKernelGGL(km_update<bf16_t>, dim3(k, dm.H), dim3(128), 0, st, (const bf16_t *)X, perm, offs, dm.N, k,
-                         dm.d, centroids, sizes, next_tab, kpad);
+                         dm.d, centroids, sizes, next_tab, kpad, bf3 ? 1 : 0);
     else
       hipLaunchKernelGGL(km_update<float>, dim3(k, dm.H), dim3(128), 0, st, (const float *)X, perm, offs, dm.N, k,
-                         dm.d, centroids, sizes, next_tab, kpad);
+                         dm.d, centroids, sizes, next_tab, kpad, 0);
   }
   return hipGetLastError();
 }

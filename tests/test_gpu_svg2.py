@@ -90,7 +90,8 @@ def test_kmeans_recovers_components():
     np.testing.assert_array_equal(r["ak"].cpu().numpy(), g["comp_k"])
 
 
-@pytest.mark.parametrize("N,d,k,iters,dtype", [(1000, 64, 7, 3, "bf16"), (333, 128, 256, 2, "bf16"),
+@pytest.mark.parametrize("N,d,k,iters,dtype", [(1000, 64, 7, 3, "bf16"), (700, 64, 45, 2, "bf16"),
+                                               (333, 128, 256, 2, "bf16"),
                                                (517, 64, 1, 1, "f32"), (300, 128, 16, 4, "f32")])
 def test_kmeans_small_shapes(N, d, k, iters, dtype):
     """Small well-separated mixtures (k components, one seeded member each
@@ -115,16 +116,18 @@ def test_kmeans_small_shapes(N, d, k, iters, dtype):
         np.testing.assert_allclose(c[h].cpu().numpy(), oc, rtol=1e-12, atol=1e-12)
 
 
-def test_kmeans_duplicate_init_tie_goes_to_lower_index():
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_kmeans_duplicate_init_tie_goes_to_lower_index(dtype):
     H, N, d = 1, 64, 64
-    x, _, _ = random_qkv(H, N, d, seed=5, dtype="f32")
+    x, _, _ = random_qkv(H, N, d, seed=5, dtype=dtype)
     init = np.array([[3, 3, 10]], dtype=np.int32)    # clusters 0 and 1 start equal
-    a, c, s = svg.svg_kmeans(to_dev(x, "f32"), 3, 1, ints(init))
+    a, c, s = svg.svg_kmeans(to_dev(x, dtype), 3, 1, ints(init))
     sync()
-    oa, oc, os_, _ = osvg2.kmeans(as_f64(x[0], "f32"), init[0], 1)
+    x64 = as_f64(x[0], dtype)
+    oa, oc, os_, _ = osvg2.kmeans(x64, init[0], 1)
     np.testing.assert_array_equal(a[0].cpu().numpy(), oa)
     assert s[0, 1].item() == 0                       # the tie never picks cluster 1
-    np.testing.assert_array_equal(c[0, 1].cpu().numpy(), x[0, 3].astype(np.float64))
+    np.testing.assert_array_equal(c[0, 1].cpu().numpy(), x64[3])
 
 
 def test_cluster_permute_bit_exact():
