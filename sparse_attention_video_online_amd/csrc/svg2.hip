@@ -10,6 +10,8 @@
 // kernels waste work.  The varlen kernel here therefore tiles the
 // concatenation of a query cluster's selected key ranges.  It does not tile
 // each cluster on its own.
+#include <algorithm>
+
 #include "attn_core.h"
 
 namespace svgk {
@@ -277,26 +279,22 @@ void km_prep3(const double *__restrict__ cent, int k, int kpad, float *__restric
   km_tab3_row<D>(cv, e, j, kpad, t);
 }
 
-// One wave = 64 points (two 32-point blocks), 4 waves per work-group.
+// Eight waves per work-group, grid (G, H) with G work-groups per head: the
+// head's table is copied to LDS once, then each wave takes 64-point groups
+// (two 32-point blocks) wave-major, group = pass * 8 G + wave * G + blockIdx.x,
+// so groups beyond the first pass spread over the work-groups' first waves.
+constexpr int kKmWaves = 8;
+
 template <int D>
-__global__ __launch_bounds__(256)
+__global__ __launch_bounds__(64 * kKmWaves)
 void km_assign_bf3(const bf16_t *__restrict__ X, const float *__restrict__ tab, int N, int k, int kpad,
                    int32_t *__restrict__ assign) {
   using TB = KmTab3<D>;
+  constexpr int NT = 64 * kKmWaves;
   extern __shared__ __attribute__((aligned(16))) float kt[];   // the head's table
   const int h = blockIdx.y;
-  const size_t nf = TB::floats(kpad);
-  const float *th = tab + (size_t)h * nf;
-  for (size_t i = threadIdx.x * 4; i < nf; i += 256 * 4) {
-    if (i + 4 <= nf) *reinterpret_cast<f32x4 *>(kt + i) = *reinterpret_cast<const f32x4 *>(th + i);
-    else for (size_t j = i; j < nf; ++j) kt[j] = th[j];
-  }
-  __syncthreads();
-  const bf16_t *ct = reinterpret_cast<const bf16_t *>(kt);
-  const float *cn = kt + (size_t)kpad * (TB::ROWH / 2);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
-  const int p0 = blockIdx.x * 256 + wave * 64 + l32, p1 = p0 + 32;
   // B operands: dims 16 s + 8 hi .. + 7 of the lane's point
   bf16x8 xb0[D / 16], xb1[D / 16];
   auto load_x = [&](int p, bf16x8 (&xb)[D / 16]) {
@@ -307,8 +305,36 @@ void km_assign_bf3(const bf16_t *__restrict__ X, const float *__restrict__ tab, 
       xb[st] = __builtin_bit_cast(bf16x8, w);
     }
   };
-  load_x(p0, xb0);
-  load_x(p1, xb1);
+  const int ngrp = (N + 63) / 64, gstep = (int)gridDim.x * kKmWaves;
+  int grp = wave * (int)gridDim.x + (int)blockIdx.x;
+  // the first group's points load while the table streams in
+  load_x(grp * 64 + l32, xb0);
+  load_x(grp * 64 + 32 + l32, xb1);
+  {
+    // kpad is a multiple of 32, so the table is whole 16-byte words
+    const int nf4 = (int)(TB::floats(kpad) / 4);
+    const f32x4 *th = reinterpret_cast<const f32x4 *>(tab + (size_t)h * TB::floats(kpad));
+    f32x4 *kt4 = reinterpret_cast<f32x4 *>(kt);
+    constexpr int U = 8;   // loads in flight per thread
+    for (int i0 = threadIdx.x; i0 < nf4; i0 += NT * U) {
+      f32x4 r[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (i0 + NT * u < nf4) r[u] = th[i0 + NT * u];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (i0 + NT * u < nf4) kt4[i0 + NT * u] = r[u];
+    }
+  }
+  __syncthreads();
+  const bf16_t *ct = reinterpret_cast<const bf16_t *>(kt);
+  const float *cn = kt + (size_t)kpad * (TB::ROWH / 2);
+  for (; grp < ngrp; grp += gstep) {
+  const int p0 = grp * 64 + l32, p1 = p0 + 32;
+  if (grp != wave * (int)gridDim.x + (int)blockIdx.x) {
+    load_x(p0, xb0);
+    load_x(p1, xb1);
+  }
   float best0 = INFINITY, best1 = INFINITY;
   int arg0 = 0, arg1 = 0;
   for (int cb = 0; cb < kpad / 32; ++cb) {
@@ -358,30 +384,39 @@ void km_assign_bf3(const bf16_t *__restrict__ X, const float *__restrict__ tab, 
     if (p0 < N) assign[(size_t)h * N + p0] = arg0;
     if (p1 < N) assign[(size_t)h * N + p1] = arg1;
   }
+  }
 }
 
-// Centroid of cluster j = mean of its members, taken in sorted (= index)
-// order.  An empty cluster keeps its centroid.  With tab (the MFMA
-// assignment), the block also writes centroid j's row of the next
-// iteration's table, as km_prep does (same values, same summation order of
-// ||c||^2), which saves a launch per iteration.
+// Centroid of cluster j = mean of its members.  The 256 threads take
+// 256 / D contiguous slices of the members (sorted, so in index order), one
+// thread per (slice, dim); the slice sums, each in member order, are added in
+// slice order.  Sums of bf16 values are exact in fp64 at any order while the
+// members' magnitudes span less than ~2^40, so the centroid is the oracle's
+// bit for bit; fp32 values agree to rounding.  An empty cluster keeps its
+// centroid.  With tab (the MFMA assignment), the block also writes centroid
+// j's row of the next iteration's table, as the prep kernels do (same values,
+// same summation order of ||c||^2), which saves a launch per iteration.
 template <typename T>
-__global__ __launch_bounds__(128)
+__global__ __launch_bounds__(256)
 void km_update(const T *__restrict__ X, const int32_t *__restrict__ perm, const int32_t *__restrict__ offs, int N,
                int k, int D, double *__restrict__ cent, int32_t *__restrict__ sizes, float *__restrict__ tab,
                int kpad, int tab3) {
   __shared__ double cv[128];
-  const int h = blockIdx.y, j = blockIdx.x, e = threadIdx.x;
+  __shared__ double part[256];
+  const int h = blockIdx.y, j = blockIdx.x, t = threadIdx.x;
+  const int ns = 256 / D, e = t % D, sl = t / D;
   const int o0 = offs[(size_t)h * (k + 1) + j], o1 = offs[(size_t)h * (k + 1) + j + 1];
+  const int len = o1 - o0;
   const int32_t *p = perm + (size_t)h * N;
   const T *Xh = X + (size_t)h * N * D;
   double *cj = cent + ((size_t)h * k + j) * D;
-  if (e < D && o1 > o0) {
+  {
     // members in batches of 8: their indices and values load independently,
     // then the fp64 adds run in member order
+    const int b1 = o0 + (int)((long long)len * (sl + 1) / ns);
+    int n = o0 + (int)((long long)len * sl / ns);
     double s = 0.0;
-    int n = o0;
-    for (; n + 8 <= o1; n += 8) {
+    for (; n + 8 <= b1; n += 8) {
       int idx[8];
       float v[8];
 #pragma unroll
@@ -391,28 +426,34 @@ void km_update(const T *__restrict__ X, const int32_t *__restrict__ perm, const 
 #pragma unroll
       for (int u = 0; u < 8; ++u) s += (double)v[u];
     }
-    for (; n < o1; ++n) s += (double)to_f32<T>(Xh[(size_t)p[n] * D + e]);
-    cj[e] = s / (double)(o1 - o0);
+    for (; n < b1; ++n) s += (double)to_f32<T>(Xh[(size_t)p[n] * D + e]);
+    part[t] = s;
   }
-  if (e == 0) sizes[h * k + j] = o1 - o0;
+  __syncthreads();
+  if (t < D && len > 0) {
+    double c = part[t];
+    for (int q = 1; q < ns; ++q) c += part[q * D + t];
+    cj[t] = c / (double)len;
+  }
+  if (t == 0) sizes[h * k + j] = len;
   if (tab == nullptr) return;
-  if (e < D) cv[e] = cj[e];   // each thread reads back its own dim
+  if (t < D) cv[t] = cj[t];   // each thread reads back its own dim
   __syncthreads();
   if (tab3) {   // the three-term bf16 table (d = 64)
-    km_tab3_row<64>(cv, e, j, kpad, tab + (size_t)h * KmTab3<64>::floats(kpad));
+    km_tab3_row<64>(cv, t, j, kpad, tab + (size_t)h * KmTab3<64>::floats(kpad));
     return;
   }
   const int row = D / 2 + kKmPad;
-  float *t = tab + (size_t)h * kpad * (2 * row + 1);
-  if (e < D) t[((size_t)j * 2 + (e & 1)) * row + (e >> 1)] = (float)cv[e];
-  if (e < 2 * kKmPad) t[((size_t)j * 2 + (e & 1)) * row + D / 2 + (e >> 1)] = 0.f;
-  if (e == 0) {
+  float *tr = tab + (size_t)h * kpad * (2 * row + 1);
+  if (t < D) tr[((size_t)j * 2 + (t & 1)) * row + (t >> 1)] = (float)cv[t];
+  if (t < 2 * kKmPad) tr[((size_t)j * 2 + (t & 1)) * row + D / 2 + (t >> 1)] = 0.f;
+  if (t == 0) {
     double n2 = 0.0;
     for (int i = 0; i < D; ++i) {
       const double v = cv[i];
       n2 += v * v;
     }
-    t[(size_t)kpad * 2 * row + j] = (float)n2;
+    tr[(size_t)kpad * 2 * row + j] = (float)n2;
   }
 }
 
@@ -808,6 +849,11 @@ hipError_t launch_kmeans(const Dims &dm, bool bf16, const void *X, int k, int it
     if (e != hipSuccess) return e;
   }
   const dim3 pgrid((kpad + 255) / 256, dm.H), mgrid((dm.N + 255) / 256, dm.H);
+  // bf16 assignment: work-groups per head so that all heads fit on the CUs at
+  // once (two per CU while two tables fit in LDS), none without a group
+  const int ngrp64 = (dm.N + 63) / 64;
+  const int per_cu = lds3 <= 80 * 1024 ? 2 : 1;
+  const int g3 = std::max(1, std::min((ngrp64 + kKmWaves - 1) / kKmWaves, 256 * per_cu / std::max(1, dm.H)));
   // the table of the initial centroids; each update then writes the next one
   if (bf3)
     hipLaunchKernelGGL(km_prep3<64>, dim3(kpad, dm.H), dim3(128), 0, st, centroids, k, kpad, tab);
@@ -817,8 +863,8 @@ hipError_t launch_kmeans(const Dims &dm, bool bf16, const void *X, int k, int it
     hipLaunchKernelGGL(km_prep<128>, pgrid, dim3(256), 0, st, centroids, k, kpad, tab);
   for (int it = 0; it < iters; ++it) {
     if (bf3) {
-      hipLaunchKernelGGL(km_assign_bf3<64>, mgrid, dim3(256), lds3, st, (const bf16_t *)X, tab, dm.N, k, kpad,
-                         assign);
+      hipLaunchKernelGGL(km_assign_bf3<64>, dim3(g3, dm.H), dim3(64 * kKmWaves), lds3, st, (const bf16_t *)X,
+                         tab, dm.N, k, kpad, assign);
     } else if (mfma && dm.d == 64) {
       hipLaunchKernelGGL(km_assign_mfma<64>, mgrid, dim3(256), mlds, st, (const bf16_t *)X, tab, dm.N, k, kpad,
                          assign);
@@ -840,10 +886,10 @@ hipError_t launch_kmeans(const Dims &dm, bool bf16, const void *X, int k, int it
     launch_sort(dm, assign, k, perm, offs, scnt, st);
     float *const next_tab = ((mfma || bf3) && it + 1 < iters) ? tab : nullptr;
     if (bf16)
-      hipLaunchKernelGGL(km_update<bf16_t>, dim3(k, dm.H), dim3(128), 0, st, (const bf16_t *)X, perm, offs, dm.N, k,
+      hipLaunchKernelGGL(km_update<bf16_t>, dim3(k, dm.H), dim3(256), 0, st, (const bf16_t *)X, perm, offs, dm.N, k,
                          dm.d, centroids, sizes, next_tab, kpad, bf3 ? 1 : 0);
     else
-      hipLaunchKernelGGL(km_update<float>, dim3(k, dm.H), dim3(128), 0, st, (const float *)X, perm, offs, dm.N, k,
+      hipLaunchKernelGGL(km_update<float>, dim3(k, dm.H), dim3(256), 0, st, (const float *)X, perm, offs, dm.N, k,
                          dm.d, centroids, sizes, next_tab, kpad, 0);
   }
   return hipGetLastError();
