@@ -122,6 +122,9 @@ void km_prep(const double *__restrict__ cent, int k, int kpad, float *__restrict
   cn[c] = (float)n2;
 }
 
+// Tokens per chunk of the stable counting sort by cluster (below).
+constexpr int kSortChunk = 1024;
+
 // One wave = 64 points (two 32-point blocks), 4 waves per work-group.
 template <int D>
 __global__ __launch_bounds__(256)
@@ -260,13 +263,19 @@ __device__ __forceinline__ void km_tab3_row(const double *cv, int e, int j, int 
 }
 
 // Initial three-term table: one block per centroid (padding rows: zero
-// terms, ||c||^2 = +inf so they never win).
+// terms, ||c||^2 = +inf so they never win); also zeroes the sort counts that
+// the first assignment fills.
 template <int D>
 __global__ __launch_bounds__(128)
-void km_prep3(const double *__restrict__ cent, int k, int kpad, float *__restrict__ tab) {
+void km_prep3(const double *__restrict__ cent, int N, int k, int kpad, float *__restrict__ tab,
+              int32_t *__restrict__ cnt) {
   using TB = KmTab3<D>;
   __shared__ double cv[D];
   const int h = blockIdx.y, j = blockIdx.x, e = threadIdx.x;
+  if (j < k) {   // column j of the sort's per-chunk counts starts at zero
+    const int nch = (N + kSortChunk - 1) / kSortChunk;
+    for (int b = e; b < nch; b += 128) cnt[((size_t)h * nch + b) * k + j] = 0;
+  }
   float *t = tab + (size_t)h * TB::floats(kpad);
   if (j >= k) {
     bf16_t *row = reinterpret_cast<bf16_t *>(t) + (size_t)j * TB::ROWH;
@@ -279,7 +288,9 @@ void km_prep3(const double *__restrict__ cent, int k, int kpad, float *__restric
   km_tab3_row<D>(cv, e, j, kpad, t);
 }
 
-// Eight waves per work-group, grid (G, H) with G work-groups per head: the
+// Eight waves per work-group, grid (G, H) with G work-groups per head.  Each
+// point also counts itself into its chunk's histogram of the cluster sort.
+// The
 // head's table is copied to LDS once, then each wave takes 64-point groups
 // (two 32-point blocks) wave-major, group = pass * 8 G + wave * G + blockIdx.x,
 // so groups beyond the first pass spread over the work-groups' first waves.
@@ -288,7 +299,7 @@ constexpr int kKmWaves = 8;
 template <int D>
 __global__ __launch_bounds__(64 * kKmWaves)
 void km_assign_bf3(const bf16_t *__restrict__ X, const float *__restrict__ tab, int N, int k, int kpad,
-                   int32_t *__restrict__ assign) {
+                   int32_t *__restrict__ assign, int32_t *__restrict__ cnt) {
   using TB = KmTab3<D>;
   constexpr int NT = 64 * kKmWaves;
   extern __shared__ __attribute__((aligned(16))) float kt[];   // the head's table
@@ -381,58 +392,87 @@ void km_assign_bf3(const bf16_t *__restrict__ X, const float *__restrict__ tab, 
   merge(best0, arg0);
   merge(best1, arg1);
   if (hi == 0) {
-    if (p0 < N) assign[(size_t)h * N + p0] = arg0;
-    if (p1 < N) assign[(size_t)h * N + p1] = arg1;
+    // the sort's per-chunk histograms (zeroed beforehand), counted here
+    int32_t *ch = cnt + (size_t)h * ((N + kSortChunk - 1) / kSortChunk) * k;
+    if (p0 < N) {
+      assign[(size_t)h * N + p0] = arg0;
+      atomicAdd(ch + (size_t)(p0 / kSortChunk) * k + arg0, 1);
+    }
+    if (p1 < N) {
+      assign[(size_t)h * N + p1] = arg1;
+      atomicAdd(ch + (size_t)(p1 / kSortChunk) * k + arg1, 1);
+    }
   }
   }
 }
 
-// Centroid of cluster j = mean of its members.  The 256 threads take
-// 256 / D contiguous slices of the members (sorted, so in index order), one
-// thread per (slice, dim); the slice sums, each in member order, are added in
-// slice order.  Sums of bf16 values are exact in fp64 at any order while the
-// members' magnitudes span less than ~2^40, so the centroid is the oracle's
-// bit for bit; fp32 values agree to rounding.  An empty cluster keeps its
-// centroid.  With tab (the MFMA assignment), the block also writes centroid
-// j's row of the next iteration's table, as the prep kernels do (same values,
-// same summation order of ||c||^2), which saves a launch per iteration.
+// Centroid of cluster j = mean of its members.  Each thread loads 16 bytes
+// of a member row (VE values); the 256 threads form 256 / (D / VE) member
+// slots, slot s taking members s, s + slots, ... of the cluster (sorted, so
+// in index order), each summing its members in order in fp64; the slot sums
+// are then added in slot order.  Sums of bf16 values are exact in fp64 at
+// any order while the members' magnitudes span less than ~2^40, so the
+// centroid is the oracle's bit for bit; fp32 values agree to rounding.  An
+// empty cluster keeps its centroid.  With tab (the MFMA assignment), the
+// block also writes centroid j's row of the next iteration's table, as the
+// prep kernels do (same values, same summation order of ||c||^2), which
+// saves a launch per iteration.  With cnt, it zeroes column j of the sort's
+// per-chunk counts for the next assignment to fill.
 template <typename T>
 __global__ __launch_bounds__(256)
 void km_update(const T *__restrict__ X, const int32_t *__restrict__ perm, const int32_t *__restrict__ offs, int N,
                int k, int D, double *__restrict__ cent, int32_t *__restrict__ sizes, float *__restrict__ tab,
-               int kpad, int tab3) {
+               int kpad, int tab3, int32_t *__restrict__ cnt) {
+  constexpr int VE = 16 / sizeof(T);
   __shared__ double cv[128];
-  __shared__ double part[256];
+  __shared__ double part[256 * VE];
   const int h = blockIdx.y, j = blockIdx.x, t = threadIdx.x;
-  const int ns = 256 / D, e = t % D, sl = t / D;
+  const int tpr = D / VE, slots = 256 / tpr, slot = t / tpr, q = t % tpr;
   const int o0 = offs[(size_t)h * (k + 1) + j], o1 = offs[(size_t)h * (k + 1) + j + 1];
   const int len = o1 - o0;
   const int32_t *p = perm + (size_t)h * N;
-  const T *Xh = X + (size_t)h * N * D;
+  const T *Xh = X + (size_t)h * N * D + q * VE;
   double *cj = cent + ((size_t)h * k + j) * D;
+  if (cnt != nullptr) {
+    const int nch = (N + kSortChunk - 1) / kSortChunk;
+    for (int b = t; b < nch; b += 256) cnt[((size_t)h * nch + b) * k + j] = 0;
+  }
   {
-    // members in batches of 8: their indices and values load independently,
-    // then the fp64 adds run in member order
-    const int b1 = o0 + (int)((long long)len * (sl + 1) / ns);
-    int n = o0 + (int)((long long)len * sl / ns);
-    double s = 0.0;
-    for (; n + 8 <= b1; n += 8) {
-      int idx[8];
-      float v[8];
+    double acc[VE];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) idx[u] = p[n + u];
+    for (int i = 0; i < VE; ++i) acc[i] = 0.0;
+    auto add_row = [&](const u32x4 &w) {
+      if constexpr (sizeof(T) == 2) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = to_f32<T>(Xh[(size_t)idx[u] * D + e]);
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] += (double)__uint_as_float(w[i] << 16);
+          acc[2 * i + 1] += (double)__uint_as_float(w[i] & 0xFFFF0000u);
+        }
+      } else {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) s += (double)v[u];
+        for (int i = 0; i < 4; ++i) acc[i] += (double)__uint_as_float(w[i]);
+      }
+    };
+    // four members a slot in flight: indices, then rows, then the adds in order
+    int n = o0 + slot;
+    for (; n + 3 * slots < o1; n += 4 * slots) {
+      int idx[4];
+      u32x4 w[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) idx[u] = p[n + u * slots];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) w[u] = *reinterpret_cast<const u32x4 *>(Xh + (size_t)idx[u] * D);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) add_row(w[u]);
     }
-    for (; n < b1; ++n) s += (double)to_f32<T>(Xh[(size_t)p[n] * D + e]);
-    part[t] = s;
+    for (; n < o1; n += slots) add_row(*reinterpret_cast<const u32x4 *>(Xh + (size_t)p[n] * D));
+#pragma unroll
+    for (int i = 0; i < VE; ++i) part[slot * D + q * VE + i] = acc[i];
   }
   __syncthreads();
   if (t < D && len > 0) {
     double c = part[t];
-    for (int q = 1; q < ns; ++q) c += part[q * D + t];
+    for (int sl = 1; sl < slots; ++sl) c += part[sl * D + t];
     cj[t] = c / (double)len;
   }
   if (t == 0) sizes[h * k + j] = len;
@@ -465,13 +505,14 @@ void km_update(const T *__restrict__ X, const int32_t *__restrict__ perm, const 
 // Waves are ordered through per-wave, per-cluster counts in LDS.
 
 // Stable counting sort of each head's tokens by cluster id (k <= 256), in
-// three launches over chunks of kSortChunk tokens: per-chunk histograms; per
-// head, the cluster offsets and each chunk's first slot per cluster; then each
-// chunk places its tokens in index order.  Within a chunk, equal ids inside a
+// two launches over chunks of kSortChunk tokens: per-chunk histograms (the
+// bf16 k-means assignment counts them itself); then each chunk takes from
+// all histograms its first slot per cluster (cluster offsets by a scan of
+// the totals, plus the counts of earlier chunks) and places its tokens in
+// index order.  Within a chunk, equal ids inside a
 // wave are found with 8 ballots (one per id bit) and a token's rank is a
 // popcount; per-wave counts order the waves, and the chunk's rounds of 256
 // tokens run in index order.  cnt is scratch of H * nchunks * k ints.
-constexpr int kSortChunk = 1024;
 
 __global__ __launch_bounds__(256)
 void sort_count(const int32_t *__restrict__ assign, int N, int k, int nch, int32_t *__restrict__ cnt) {
@@ -487,53 +528,46 @@ void sort_count(const int32_t *__restrict__ assign, int N, int k, int nch, int32
 }
 
 __global__ __launch_bounds__(256)
-void sort_scan(int k, int nch, int32_t *__restrict__ cnt, int32_t *__restrict__ offs) {
-  __shared__ int32_t tot[256];
-  const int h = blockIdx.x, c = threadIdx.x;
-  int32_t *ch = cnt + (size_t)h * nch * k;
-  int t = 0;
-  if (c < k)
-    for (int b = 0; b < nch; ++b) t += ch[(size_t)b * k + c];
-  // exclusive scan over the (at most 256) clusters: per wave, then across
-  // the 4 wave totals
-  const int lane = c & 63, wave = c >> 6;
-  const int v = c < k ? t : 0;
-  int incl = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(incl, d);
-    if (lane >= d) incl += y;
-  }
-  if (lane == 63) tot[wave] = incl;
-  __syncthreads();
-  int before = 0;
-  for (int w = 0; w < wave; ++w) before += tot[w];
-  const int excl = before + incl - v;
-  if (c == 255) offs[(size_t)h * (k + 1) + k] = before + incl;
-  __syncthreads();
-  tot[c] = excl;
-  __syncthreads();
-  if (c < k) {
-    int run = tot[c];
-    offs[(size_t)h * (k + 1) + c] = run;
-    for (int b = 0; b < nch; ++b) {  // chunk b's first slot of cluster c
-      const int v = ch[(size_t)b * k + c];
-      ch[(size_t)b * k + c] = run;
-      run += v;
-    }
-  }
-}
-
-__global__ __launch_bounds__(256)
 void sort_place(const int32_t *__restrict__ assign, int N, int k, int nch, const int32_t *__restrict__ cnt,
-                int32_t *__restrict__ perm) {
+                int32_t *__restrict__ perm, int32_t *__restrict__ offs) {
   __shared__ int32_t start[256];
   __shared__ int32_t wcnt[4][256];
   __shared__ int32_t rcnt[256];
   const int h = blockIdx.y, ch = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int32_t *a = assign + (size_t)h * N;
   int32_t *p = perm + (size_t)h * N;
-  if (tid < k) start[tid] = cnt[((size_t)h * nch + ch) * k + tid];
+  {
+    // cluster c's total and its count in earlier chunks, then an exclusive
+    // scan of the totals over the (at most 256) clusters: per wave, then
+    // across the 4 wave totals.  Chunk 0 writes the offsets.
+    const int32_t *cc = cnt + (size_t)h * nch * k;
+    int tot = 0, before = 0;
+    if (tid < k) {
+#pragma unroll 4
+      for (int b = 0; b < nch; ++b) {
+        const int v = cc[(size_t)b * k + tid];
+        tot += v;
+        before += b < ch ? v : 0;
+      }
+    }
+    int incl = tot;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(incl, d);
+      if (lane >= d) incl += y;
+    }
+    if (lane == 63) rcnt[wave] = incl;
+    __syncthreads();
+    int wbefore = 0;
+    for (int w = 0; w < wave; ++w) wbefore += rcnt[w];
+    const int excl = wbefore + incl - tot;
+    if (tid < k) start[tid] = excl + before;
+    if (ch == 0) {
+      if (tid < k) offs[(size_t)h * (k + 1) + tid] = excl;
+      if (tid == 255) offs[(size_t)h * (k + 1) + k] = wbefore + incl;
+    }
+    __syncthreads();
+  }
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   const int n0 = ch * kSortChunk, n1 = min(N, n0 + kSortChunk);
   for (int base = n0; base < n1; base += 256) {
@@ -573,12 +607,12 @@ size_t sort_scratch_bytes(const Dims &dm, int k) {
   return align256((size_t)dm.H * nch * k * sizeof(int32_t));
 }
 
+// counted: cnt already holds the per-chunk histograms of assign
 void launch_sort(const Dims &dm, const int32_t *assign, int k, int32_t *perm, int32_t *offs, int32_t *cnt,
-                 hipStream_t st) {
+                 hipStream_t st, bool counted = false) {
   const int nch = (dm.N + kSortChunk - 1) / kSortChunk;
-  hipLaunchKernelGGL(sort_count, dim3(nch, dm.H), dim3(256), 0, st, assign, dm.N, k, nch, cnt);
-  hipLaunchKernelGGL(sort_scan, dim3(dm.H), dim3(256), 0, st, k, nch, cnt, offs);
-  hipLaunchKernelGGL(sort_place, dim3(nch, dm.H), dim3(256), 0, st, assign, dm.N, k, nch, cnt, perm);
+  if (!counted) hipLaunchKernelGGL(sort_count, dim3(nch, dm.H), dim3(256), 0, st, assign, dm.N, k, nch, cnt);
+  hipLaunchKernelGGL(sort_place, dim3(nch, dm.H), dim3(256), 0, st, assign, dm.N, k, nch, cnt, perm, offs);
 }
 
 // ---------------------------------------------------------------------------
@@ -856,7 +890,7 @@ hipError_t launch_kmeans(const Dims &dm, bool bf16, const void *X, int k, int it
   const int g3 = std::max(1, std::min((ngrp64 + kKmWaves - 1) / kKmWaves, 256 * per_cu / std::max(1, dm.H)));
   // the table of the initial centroids; each update then writes the next one
   if (bf3)
-    hipLaunchKernelGGL(km_prep3<64>, dim3(kpad, dm.H), dim3(128), 0, st, centroids, k, kpad, tab);
+    hipLaunchKernelGGL(km_prep3<64>, dim3(kpad, dm.H), dim3(128), 0, st, centroids, dm.N, k, kpad, tab, scnt);
   else if (mfma && dm.d == 64)
     hipLaunchKernelGGL(km_prep<64>, pgrid, dim3(256), 0, st, centroids, k, kpad, tab);
   else if (mfma)
@@ -864,7 +898,7 @@ hipError_t launch_kmeans(const Dims &dm, bool bf16, const void *X, int k, int it
   for (int it = 0; it < iters; ++it) {
     if (bf3) {
       hipLaunchKernelGGL(km_assign_bf3<64>, dim3(g3, dm.H), dim3(64 * kKmWaves), lds3, st, (const bf16_t *)X,
-                         tab, dm.N, k, kpad, assign);
+                         tab, dm.N, k, kpad, assign, scnt);
     } else if (mfma && dm.d == 64) {
       hipLaunchKernelGGL(km_assign_mfma<64>, mgrid, dim3(256), mlds, st, (const bf16_t *)X, tab, dm.N, k, kpad,
                          assign);
@@ -883,14 +917,14 @@ hipError_t launch_kmeans(const Dims &dm, bool bf16, const void *X, int k, int it
     else
       hipLaunchKernelGGL((km_assign<float, 128>), grid, dim3(256), lds, st, (const float *)X, centroids, dm.N, k,
                          assign);
-    launch_sort(dm, assign, k, perm, offs, scnt, st);
+    launch_sort(dm, assign, k, perm, offs, scnt, st, bf3);
     float *const next_tab = ((mfma || bf3) && it + 1 < iters) ? tab : nullptr;
     if (bf16)
       hipLaunchKernelGGL(km_update<bf16_t>, dim3(k, dm.H), dim3(256), 0, st, (const bf16_t *)X, perm, offs, dm.N, k,
-                         dm.d, centroids, sizes, next_tab, kpad, bf3 ? 1 : 0);
+                         dm.d, centroids, sizes, next_tab, kpad, bf3 ? 1 : 0, bf3 ? scnt : nullptr);
     else
       hipLaunchKernelGGL(km_update<float>, dim3(k, dm.H), dim3(256), 0, st, (const float *)X, perm, offs, dm.N, k,
-                         dm.d, centroids, sizes, next_tab, kpad, 0);
+                         dm.d, centroids, sizes, next_tab, kpad, 0, nullptr);
   }
   return hipGetLastError();
 }
