@@ -498,21 +498,14 @@ void km_update(const T *__restrict__ X, const int32_t *__restrict__ perm, const 
 }
 
 // ---------------------------------------------------------------------------
-// Stable counting sort of tokens by cluster.  One work-group per head,
-// 1024 threads = 16 waves.  Tokens are taken in rounds of 1024 in index
-// order.  Inside a wave, equal cluster ids are found with 8 ballots (one per
-// id bit).  A token's rank among equal ids in earlier lanes is a popcount.
-// Waves are ordered through per-wave, per-cluster counts in LDS.
-
 // Stable counting sort of each head's tokens by cluster id (k <= 256), in
 // two launches over chunks of kSortChunk tokens: per-chunk histograms (the
 // bf16 k-means assignment counts them itself); then each chunk takes from
 // all histograms its first slot per cluster (cluster offsets by a scan of
 // the totals, plus the counts of earlier chunks) and places its tokens in
-// index order.  Within a chunk, equal ids inside a
-// wave are found with 8 ballots (one per id bit) and a token's rank is a
-// popcount; per-wave counts order the waves, and the chunk's rounds of 256
-// tokens run in index order.  cnt is scratch of H * nchunks * k ints.
+// index order.  Within a chunk, equal ids inside a wave are found with 8
+// ballots (one per id bit) and a token's rank is a popcount; per-wave counts
+// order the chunk's 16 waves.  cnt is scratch of H * nchunks * k ints.
 
 __global__ __launch_bounds__(256)
 void sort_count(const int32_t *__restrict__ assign, int N, int k, int nch, int32_t *__restrict__ cnt) {
@@ -527,79 +520,76 @@ void sort_count(const int32_t *__restrict__ assign, int N, int k, int nch, int32
   if (tid < k) cnt[((size_t)h * nch + ch) * k + tid] = hist[tid];
 }
 
-__global__ __launch_bounds__(256)
+// One thread per token of the chunk (kSortChunk threads, 16 waves).
+__global__ __launch_bounds__(kSortChunk)
 void sort_place(const int32_t *__restrict__ assign, int N, int k, int nch, const int32_t *__restrict__ cnt,
                 int32_t *__restrict__ perm, int32_t *__restrict__ offs) {
+  constexpr int NW = kSortChunk / 64;
   __shared__ int32_t start[256];
-  __shared__ int32_t wcnt[4][256];
-  __shared__ int32_t rcnt[256];
+  __shared__ int32_t wcnt[NW][256];
+  __shared__ int32_t wtot[4];
   const int h = blockIdx.y, ch = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int32_t *a = assign + (size_t)h * N;
-  int32_t *p = perm + (size_t)h * N;
-  {
-    // cluster c's total and its count in earlier chunks, then an exclusive
-    // scan of the totals over the (at most 256) clusters: per wave, then
-    // across the 4 wave totals.  Chunk 0 writes the offsets.
+  const int n = ch * kSortChunk + tid;
+  const bool valid = n < N;
+  const int c = valid ? a[n] : 0;
+  // cluster t's total and its count in earlier chunks (threads t < k), then
+  // an exclusive scan of the totals over the (at most 256) clusters by the
+  // first 4 waves: per wave, then across their totals.  Chunk 0 writes the
+  // offsets.
+  int tot = 0, before = 0, incl = 0;
+  if (tid < k) {
     const int32_t *cc = cnt + (size_t)h * nch * k;
-    int tot = 0, before = 0;
-    if (tid < k) {
 #pragma unroll 4
-      for (int b = 0; b < nch; ++b) {
-        const int v = cc[(size_t)b * k + tid];
-        tot += v;
-        before += b < ch ? v : 0;
-      }
+    for (int b = 0; b < nch; ++b) {
+      const int v = cc[(size_t)b * k + tid];
+      tot += v;
+      before += b < ch ? v : 0;
     }
-    int incl = tot;
+  }
+  if (wave < 4) {
+    incl = tot;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
       const int y = __shfl_up(incl, d);
       if (lane >= d) incl += y;
     }
-    if (lane == 63) rcnt[wave] = incl;
-    __syncthreads();
+    if (lane == 63) wtot[wave] = incl;
+  }
+  for (int e = tid; e < NW * 256; e += kSortChunk) (&wcnt[0][0])[e] = 0;
+  __syncthreads();
+  if (tid < 256) {
     int wbefore = 0;
-    for (int w = 0; w < wave; ++w) wbefore += rcnt[w];
+    for (int w = 0; w < wave; ++w) wbefore += wtot[w];
     const int excl = wbefore + incl - tot;
     if (tid < k) start[tid] = excl + before;
     if (ch == 0) {
       if (tid < k) offs[(size_t)h * (k + 1) + tid] = excl;
       if (tid == 255) offs[(size_t)h * (k + 1) + k] = wbefore + incl;
     }
-    __syncthreads();
   }
+  // equal ids within the wave: 8 ballots, one per id bit; rank = earlier lanes
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  const int n0 = ch * kSortChunk, n1 = min(N, n0 + kSortChunk);
-  for (int base = n0; base < n1; base += 256) {
-    for (int e = tid; e < 4 * 256; e += 256) (&wcnt[0][0])[e] = 0;
-    __syncthreads();
-    const int n = base + tid;
-    const bool valid = n < n1;
-    const int c = valid ? a[n] : 0;
-    uint64_t same = __ballot(valid);
+  uint64_t same = __ballot(valid);
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      const uint64_t bal = __ballot(valid && ((c >> b) & 1));
-      same &= ((c >> b) & 1) ? bal : ~bal;
-    }
-    const int rank = __popcll(same & below);
-    if (valid && rank == 0) wcnt[wave][c] = __popcll(same);
-    __syncthreads();
-    if (tid < k) {  // exclusive prefix over the 4 waves
-      int run = 0;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const int t = wcnt[w][tid];
-        wcnt[w][tid] = run;
-        run += t;
-      }
-      rcnt[tid] = run;
-    }
-    __syncthreads();
-    if (valid) p[start[c] + wcnt[wave][c] + rank] = n;
-    __syncthreads();
-    if (tid < k) start[tid] += rcnt[tid];
+  for (int b = 0; b < 8; ++b) {
+    const uint64_t bal = __ballot(valid && ((c >> b) & 1));
+    same &= ((c >> b) & 1) ? bal : ~bal;
   }
+  const int rank = __popcll(same & below);
+  if (valid && rank == 0) wcnt[wave][c] = __popcll(same);
+  __syncthreads();
+  if (tid < k) {  // exclusive prefix over the waves
+    int run = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const int t = wcnt[w][tid];
+      wcnt[w][tid] = run;
+      run += t;
+    }
+  }
+  __syncthreads();
+  if (valid) perm[(size_t)h * N + start[c] + wcnt[wave][c] + rank] = n;
 }
 
 size_t sort_scratch_bytes(const Dims &dm, int k) {
@@ -612,7 +602,7 @@ void launch_sort(const Dims &dm, const int32_t *assign, int k, int32_t *perm, in
                  hipStream_t st, bool counted = false) {
   const int nch = (dm.N + kSortChunk - 1) / kSortChunk;
   if (!counted) hipLaunchKernelGGL(sort_count, dim3(nch, dm.H), dim3(256), 0, st, assign, dm.N, k, nch, cnt);
-  hipLaunchKernelGGL(sort_place, dim3(nch, dm.H), dim3(256), 0, st, assign, dm.N, k, nch, cnt, perm, offs);
+  hipLaunchKernelGGL(sort_place, dim3(nch, dm.H), dim3(kSortChunk), 0, st, assign, dm.N, k, nch, cnt, perm, offs);
 }
 
 // ---------------------------------------------------------------------------
