@@ -619,8 +619,10 @@ void select_rows(const double *__restrict__ cq, const double *__restrict__ ck, c
                  int32_t *__restrict__ pair_idx) {
   __shared__ double prob[256];
   __shared__ double red[256];
+  __shared__ double sp[256];   // probabilities in rank order
   __shared__ int32_t order[256];
   __shared__ int32_t keep[256];
+  __shared__ int32_t wc[4];
   __shared__ int32_t nsel;
   const int h = blockIdx.y, i = blockIdx.x, j = threadIdx.x;
   const bool live = j < kk && size_k[h * kk + j] > 0;
@@ -650,7 +652,7 @@ void select_rows(const double *__restrict__ cq, const double *__restrict__ ck, c
   const double pj = e / red[0];
   prob[j] = live ? pj : -1.0;
   keep[j] = 0;
-  __syncthreads();
+  const int nlive = __syncthreads_count(live);
   if (live) {  // rank by (probability desc, index asc)
     int rank = 0;
     for (int t = 0; t < kk; ++t) {
@@ -658,47 +660,62 @@ void select_rows(const double *__restrict__ cq, const double *__restrict__ ck, c
       rank += (pt > pj) || (pt == pj && t < j);
     }
     order[rank] = j;
+    sp[rank] = pj;
   }
   __syncthreads();
   if (j == 0) {
-    int nlive = 0;
-    for (int t = 0; t < kk; ++t) nlive += prob[t] >= 0.0;
+    // the running sum in rank order, one add at a time; the first rank at
+    // which it reaches top_p closes the set (all live clusters if none)
     double run = 0.0;
     int n = nlive;
     for (int r = 0; r < nlive; ++r) {
-      run += prob[order[r]];
-      if (run >= top_p) {
-        n = r + 1;
-        break;
-      }
+      run += sp[r];
+      if (n == nlive && run >= top_p) n = r + 1;
     }
     nsel = n;
   }
   __syncthreads();
   if (j < nsel) keep[order[j]] = 1;
   __syncthreads();
-  if (j == 0) {
-    int32_t *row = pair_idx + (size_t)h * kq * kk + (size_t)i * kk;
-    int m = 0;
-    for (int t = 0; t < kk; ++t)
-      if (keep[t]) row[m++] = t;
-    pair_ptr[(size_t)h * (kq + 1) + i + 1] = m;
-  }
+  // the kept clusters in ascending order: ballot ranks within each wave,
+  // plus the counts of earlier waves
+  const int lane = j & 63, wave = j >> 6;
+  const bool kept = j < kk && keep[j];
+  const uint64_t m = __ballot(kept);
+  if (lane == 0) wc[wave] = __popcll(m);
+  __syncthreads();
+  int pos = __popcll(m & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
+  for (int w = 0; w < wave; ++w) pos += wc[w];
+  if (kept) pair_idx[(size_t)h * kq * kk + (size_t)i * kk + pos] = j;
+  if (j == 0) pair_ptr[(size_t)h * (kq + 1) + i + 1] = wc[0] + wc[1] + wc[2] + wc[3];
 }
 
 __global__ __launch_bounds__(256)
 void select_compact(int kq, int kk, int32_t *__restrict__ pair_ptr, int32_t *__restrict__ pair_idx) {
+  // Rows in batches of 8: every source of a batch is read before any of its
+  // targets is written.  Row i's target ends at the start of row i + 1's
+  // (the kept counts of rows < i + 1 sum to at most (i + 1) kk), so no write
+  // reaches the source of a later batch.
+  constexpr int B = 8;
   const int h = blockIdx.x, tid = threadIdx.x;
   int32_t *ptr = pair_ptr + (size_t)h * (kq + 1);
   int32_t *idx = pair_idx + (size_t)h * kq * kk;
   int run = 0;
-  for (int i = 0; i < kq; ++i) {
-    const int n = ptr[i + 1];
-    const int v = tid < n ? idx[(size_t)i * kk + tid] : 0;
+  for (int i = 0; i < kq; i += B) {
+    int n[B], v[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) n[b] = i + b < kq ? ptr[i + b + 1] : 0;
+#pragma unroll
+    for (int b = 0; b < B; ++b) v[b] = tid < n[b] ? idx[(size_t)(i + b) * kk + tid] : 0;
     __syncthreads();
-    if (tid < n) idx[run + tid] = v;
-    if (tid == 0) ptr[i] = run;
-    run += n;
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      if (i + b < kq) {
+        if (tid < n[b]) idx[run + tid] = v[b];
+        if (tid == 0) ptr[i + b] = run;
+        run += n[b];
+      }
+    }
     __syncthreads();
   }
   if (tid == 0) ptr[kq] = run;
