@@ -220,12 +220,37 @@ def bench_svg2(args):
     dm = svg.svg_dims(1, N, 0, H, d)
     ws_kq = torch.empty(svg.workspace_bytes(svg.SVG2_OP_KMEANS, dm, w.kq, svg2=True), dtype=torch.uint8, device=dev)
     ws_kk = torch.empty(svg.workspace_bytes(svg.SVG2_OP_KMEANS, dm, w.kk, svg2=True), dtype=torch.uint8, device=dev)
-    ws_cp = torch.empty(max(1, svg.workspace_bytes(svg.SVG2_OP_CLUSTER_PERMUTE, dm, max(w.kq, w.kk), svg2=True)),
-                        dtype=torch.uint8, device=dev)
+    ws_cp, ws_cp2 = (torch.empty(max(1, svg.workspace_bytes(svg.SVG2_OP_CLUSTER_PERMUTE, dm, max(w.kq, w.kk),
+                                                             svg2=True)), dtype=torch.uint8, device=dev)
+                     for _ in range(2))
     ws_vl = torch.empty(svg.workspace_bytes(svg.SVG2_OP_VARLEN, dm, w.kq, w.kk, svg2=True), dtype=torch.uint8,
                         device=dev)
     stream = torch.cuda.current_stream()
     names = ["kmeans_q", "kmeans_k", "cluster_sort_qk", "gather_qkv", "select_pairs", "varlen_attn"]
+
+    # The query chain (k-means, sort, gather of Q) and the key chain (k-means,
+    # sort, gathers of K and V) are independent: the timed step runs the key
+    # chain on a second stream (default priority) and joins before the pair
+    # selection.  The staged step below runs everything in order on one
+    # stream to time each stage.
+    side = torch.cuda.Stream()
+
+    def step_overlapped():
+        fork, join = torch.cuda.Event(), torch.cuda.Event()
+        fork.record(stream)
+        side.wait_event(fork)
+        with torch.cuda.stream(side):
+            svg.svg_kmeans(k, w.kk, w.iters, ik, assign=ak, centroids=ck, sizes=sk, ws=ws_kk)
+            svg.svg_cluster_permute(ak, w.kk, d, perm=pk, offs=ok, ws=ws_cp2)
+            svg.svg_permute_rows(k, pk, out=kp)
+            svg.svg_permute_rows(v, pk, out=vp)
+            join.record(side)
+        svg.svg_kmeans(q, w.kq, w.iters, iq, assign=aq, centroids=cq, sizes=sq, ws=ws_kq)
+        svg.svg_cluster_permute(aq, w.kq, d, perm=pq, offs=oq, ws=ws_cp)
+        svg.svg_permute_rows(q, pq, out=qp)
+        stream.wait_event(join)
+        svg.svg_select_pairs(cq, ck, sk, w.top_p, pair_ptr=ptr, pair_idx=idx)
+        svg.svg_varlen_attn(qp, kp, vp, oq, ok, ptr, idx, q_perm=pq, out=o, ws=ws_vl)
 
     def step(ev=None):
         def mark(j):
@@ -249,18 +274,22 @@ def bench_svg2(args):
         mark(6)
 
     for _ in range(args.warmup):
-        step()
+        step_overlapped()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(args.steps):
-        step()
+        step_overlapped()
     e1.record(stream)
     torch.cuda.synchronize()
     ms_per_step = e0.elapsed_time(e1) / args.steps
+    o_overlapped, idx_overlapped = o.clone(), idx.clone()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(7)]
     step(ev)
     torch.cuda.synchronize()
+    # the two-stream step computes exactly what the one-stream step does
+    if not (torch.equal(o_overlapped, o) and torch.equal(idx_overlapped, idx)):
+        raise SystemExit("svg2: two-stream and one-stream steps disagree")
     stage_ms = {n: ev[j].elapsed_time(ev[j + 1]) for j, n in enumerate(names)}
 
     # work: attention pairs from the selected clusters; bytes of the copies
@@ -282,6 +311,7 @@ def bench_svg2(args):
         "config": {"workload": w.name, "N": N, "H": H, "d": d, "kq": w.kq, "kk": w.kk, "iters": w.iters,
                    "top_p": w.top_p, "pair_density": round(pairs / (H * float(N) * N), 4)},
         "stage_ms": {kk_: round(vv, 4) for kk_, vv in stage_ms.items()},
+        "one_stream_ms": round(sum(stage_ms.values()), 4),
         "varlen_tflops": round(attn_flops / (stage_ms["varlen_attn"] * 1e-3) / 1e12, 2),
         "gather_gbs": round(gather_bytes / (stage_ms["gather_qkv"] * 1e-3) / 1e9, 1),
         "kmeans_vector_tflops": round(km_flops / ((stage_ms["kmeans_q"] + stage_ms["kmeans_k"]) * 1e-3) / 1e12, 2),
