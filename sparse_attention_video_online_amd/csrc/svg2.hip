@@ -845,7 +845,7 @@ int varlen_max_tiles(const Dims &dm, int kq, int bq) { return (dm.N + bq - 1) / 
 
 size_t kmeans_ws_bytes(const Dims &dm, int k) {
   const int kpad = (k + 31) / 32 * 32;
-  const size_t tab = dm.d == 64 ? max(KmTab<64>::floats(kpad), KmTab3<64>::floats(kpad)) : KmTab<128>::floats(kpad);
+  const size_t tab = dm.d == 64 ? KmTab3<64>::floats(kpad) : KmTab<128>::floats(kpad);
   return align256((size_t)dm.H * dm.N * sizeof(int32_t)) + align256((size_t)dm.H * (k + 1) * sizeof(int32_t)) +
          align256((size_t)dm.H * tab * sizeof(float)) + sort_scratch_bytes(dm, k);
 }
@@ -856,8 +856,7 @@ hipError_t launch_kmeans(const Dims &dm, bool bf16, const void *X, int k, int it
   int32_t *offs = (int32_t *)((char *)ws + align256((size_t)dm.H * dm.N * sizeof(int32_t)));
   float *tab = (float *)((char *)offs + align256((size_t)dm.H * (k + 1) * sizeof(int32_t)));
   const int kpad = (k + 31) / 32 * 32;
-  const size_t tab_floats =
-      dm.d == 64 ? max(KmTab<64>::floats(kpad), KmTab3<64>::floats(kpad)) : KmTab<128>::floats(kpad);
+  const size_t tab_floats = dm.d == 64 ? KmTab3<64>::floats(kpad) : KmTab<128>::floats(kpad);
   int32_t *scnt = (int32_t *)((char *)tab + align256((size_t)dm.H * tab_floats * sizeof(float)));
   if (bf16)
     hipLaunchKernelGGL(km_init<bf16_t>, dim3(k, dm.H), dim3(128), 0, st, (const bf16_t *)X, init_idx, dm.N, dm.d, k,
@@ -865,58 +864,39 @@ hipError_t launch_kmeans(const Dims &dm, bool bf16, const void *X, int k, int it
   else
     hipLaunchKernelGGL(km_init<float>, dim3(k, dm.H), dim3(128), 0, st, (const float *)X, init_idx, dm.N, dm.d, k,
                        centroids);
-  const size_t lds = (size_t)k * dm.d * sizeof(float);
-  const dim3 grid((dm.N + 255) / 256, dm.H);
-  const void *fn = bf16 ? (dm.d == 64 ? (const void *)km_assign<bf16_t, 64> : (const void *)km_assign<bf16_t, 128>)
+  // Assignment: bf16, d = 64 on the bf16 matrix cores (three-term table);
+  // bf16, d = 128 on the fp32 matrix cores (fp32 table); fp32 points on the
+  // vector ALUs.  With k <= 256 the tables fit in LDS (at most 101 and 137
+  // floats per centroid: 103 KB and 140 KB).
+  const bool bf3 = bf16 && dm.d == 64, mfma = bf16 && dm.d == 128;
+  const size_t lds = bf3 ? KmTab3<64>::floats(kpad) * sizeof(float)
+                   : mfma ? KmTab<128>::floats(kpad) * sizeof(float)
+                          : (size_t)k * dm.d * sizeof(float);
+  const void *fn = bf3 ? (const void *)km_assign_bf3<64>
+                 : mfma ? (const void *)km_assign_mfma<128>
                         : (dm.d == 64 ? (const void *)km_assign<float, 64> : (const void *)km_assign<float, 128>);
-  if (lds > 65536) {  // centroid table above 64 KiB: raise the dynamic LDS limit
+  if (lds > 160 * 1024) return hipErrorInvalidValue;
+  if (lds > 65536) {  // table above 64 KiB: raise the dynamic LDS limit
     const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  // bf16: the MFMA assignment; its table takes kpad*(D+9) floats of LDS
-  // bf16, d = 64: the three-term bf16 table on the bf16 matrix cores
-  const size_t lds3 = KmTab3<64>::floats(kpad) * sizeof(float);
-  const bool bf3 = bf16 && dm.d == 64 && lds3 <= 160 * 1024;
-  if (bf3 && lds3 > 65536) {
-    const hipError_t e = hipFuncSetAttribute((const void *)km_assign_bf3<64>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds3);
-    if (e != hipSuccess) return e;
-  }
-  const size_t mlds = (dm.d == 64 ? KmTab<64>::floats(kpad) : KmTab<128>::floats(kpad)) * sizeof(float);
-  const bool mfma = bf16 && !bf3 && mlds <= 160 * 1024;
-  if (mfma && mlds > 65536) {
-    const void *mf = dm.d == 64 ? (const void *)km_assign_mfma<64> : (const void *)km_assign_mfma<128>;
-    const hipError_t e = hipFuncSetAttribute(mf, hipFuncAttributeMaxDynamicSharedMemorySize, (int)mlds);
-    if (e != hipSuccess) return e;
-  }
-  const dim3 pgrid((kpad + 255) / 256, dm.H), mgrid((dm.N + 255) / 256, dm.H);
-  // bf16 assignment: work-groups per head so that all heads fit on the CUs at
+  const dim3 grid((dm.N + 255) / 256, dm.H), pgrid((kpad + 255) / 256, dm.H);
+  // bf16, d = 64: work-groups per head so that all heads fit on the CUs at
   // once (two per CU while two tables fit in LDS), none without a group
   const int ngrp64 = (dm.N + 63) / 64;
-  const int per_cu = lds3 <= 80 * 1024 ? 2 : 1;
+  const int per_cu = lds <= 80 * 1024 ? 2 : 1;
   const int g3 = std::max(1, std::min((ngrp64 + kKmWaves - 1) / kKmWaves, 256 * per_cu / std::max(1, dm.H)));
   // the table of the initial centroids; each update then writes the next one
   if (bf3)
     hipLaunchKernelGGL(km_prep3<64>, dim3(kpad, dm.H), dim3(128), 0, st, centroids, dm.N, k, kpad, tab, scnt);
-  else if (mfma && dm.d == 64)
-    hipLaunchKernelGGL(km_prep<64>, pgrid, dim3(256), 0, st, centroids, k, kpad, tab);
   else if (mfma)
     hipLaunchKernelGGL(km_prep<128>, pgrid, dim3(256), 0, st, centroids, k, kpad, tab);
   for (int it = 0; it < iters; ++it) {
-    if (bf3) {
-      hipLaunchKernelGGL(km_assign_bf3<64>, dim3(g3, dm.H), dim3(64 * kKmWaves), lds3, st, (const bf16_t *)X,
-                         tab, dm.N, k, kpad, assign, scnt);
-    } else if (mfma && dm.d == 64) {
-      hipLaunchKernelGGL(km_assign_mfma<64>, mgrid, dim3(256), mlds, st, (const bf16_t *)X, tab, dm.N, k, kpad,
-                         assign);
-    } else if (mfma) {
-      hipLaunchKernelGGL(km_assign_mfma<128>, mgrid, dim3(256), mlds, st, (const bf16_t *)X, tab, dm.N, k, kpad,
-                         assign);
-    } else if (bf16 && dm.d == 64)
-      hipLaunchKernelGGL((km_assign<bf16_t, 64>), grid, dim3(256), lds, st, (const bf16_t *)X, centroids, dm.N, k,
-                         assign);
-    else if (bf16)
-      hipLaunchKernelGGL((km_assign<bf16_t, 128>), grid, dim3(256), lds, st, (const bf16_t *)X, centroids, dm.N, k,
+    if (bf3)
+      hipLaunchKernelGGL(km_assign_bf3<64>, dim3(g3, dm.H), dim3(64 * kKmWaves), lds, st, (const bf16_t *)X, tab,
+                         dm.N, k, kpad, assign, scnt);
+    else if (mfma)
+      hipLaunchKernelGGL(km_assign_mfma<128>, grid, dim3(256), lds, st, (const bf16_t *)X, tab, dm.N, k, kpad,
                          assign);
     else if (dm.d == 64)
       hipLaunchKernelGGL((km_assign<float, 64>), grid, dim3(256), lds, st, (const float *)X, centroids, dm.N, k,
