@@ -288,13 +288,13 @@ void km_prep3(const double *__restrict__ cent, int N, int k, int kpad, float *__
   km_tab3_row<D>(cv, e, j, kpad, t);
 }
 
-// Eight waves per work-group, grid (G, H) with G work-groups per head.  Each
-// point also counts itself into its chunk's histogram of the cluster sort.
-// The
-// head's table is copied to LDS once, then each wave takes 64-point groups
-// (two 32-point blocks) wave-major, group = pass * 8 G + wave * G + blockIdx.x,
-// so groups beyond the first pass spread over the work-groups' first waves.
-constexpr int kKmWaves = 8;
+// kKmWaves waves per work-group, grid (G, H) with G work-groups per head.
+// The head's table is copied to LDS once, then each wave takes 64-point
+// groups (two 32-point blocks) wave-major, group = pass * kKmWaves * G +
+// wave * G + blockIdx.x, so groups beyond the first pass spread over the
+// work-groups' first waves.  Each point also counts itself into its chunk's
+// histogram of the cluster sort.
+constexpr int kKmWaves = 16;
 
 template <int D>
 __global__ __launch_bounds__(64 * kKmWaves)
