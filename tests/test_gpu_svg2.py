@@ -91,6 +91,8 @@ def test_kmeans_recovers_components():
 
 
 @pytest.mark.parametrize("N,d,k,iters,dtype", [(1000, 64, 7, 3, "bf16"), (700, 64, 45, 2, "bf16"),
+                                               (400, 64, 1, 2, "bf16"), (50, 64, 3, 2, "bf16"),
+                                               (1500, 64, 256, 2, "bf16"),
                                                (333, 128, 256, 2, "bf16"),
                                                (517, 64, 1, 1, "f32"), (300, 128, 16, 4, "f32")])
 def test_kmeans_small_shapes(N, d, k, iters, dtype):
