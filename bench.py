@@ -392,7 +392,8 @@ def main():
             svg.svg_block_sparse_attn_csr_vt_layout(q, kp, vt, row_ptr, kv_idx, labels, F, S, T, bq, bk, out=o,
                                                     ws=attn_ws)
         else:
-            svg.svg_block_sparse_attn_csr(qp, kp, vp, row_ptr, kv_idx, F, S, T, bq, bk, out=op)
+            svg.svg_block_sparse_attn_csr(qp, kp, vp, row_ptr, kv_idx, F, S, T, bq, bk, out=op,
+                                          rowmajor_kernel=True)
 
     def step(i=None, stage_events=None):
         def mark(j):

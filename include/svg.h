@@ -86,7 +86,8 @@ typedef enum {
   SVG_OP_PROFILE = 0,        /* a = n_samples                                  */
   SVG_OP_BLOCK_SPARSE = 1,   /* a = bq, b = bk  (bitmap -> CSR inside ws)      */
   SVG_OP_COMPACT = 2,        /* a = rows, b = nKB                              */
-  SVG_OP_ATTN_VT = 3         /* a = bq, b = bk  (split text groups, may be 0)  */
+  SVG_OP_ATTN_VT = 3,        /* a = bq, b = bk  (split text groups, may be 0)  */
+  SVG_OP_ATTN_CSR = 4        /* a = bq, b = bk  (Vt + split partials, may be 0) */
 } svg_op;
 
 /* Bytes of workspace an op needs for these sizes (host-only, no HIP call). */
@@ -179,11 +180,26 @@ svg_status svg_compact_block_mask(int32_t rows, int32_t nkb, const uint8_t *bloc
  * svg_block_sparse_attn:     takes the bitmap, compacts it into ws, then
  *                            runs the attention.  ws:
  *                            svg_workspace_bytes(SVG_OP_BLOCK_SPARSE,
- *                            dims, bq, bk).
+ *                            dims, bq, bk) bytes (the bf16 size; fp32 needs
+ *                            only the lists' part).
  * svg_block_sparse_attn_csr: takes prebuilt CSR lists over the H*nQB rows
- *                            (row h*nQB + qb), ascending kv-block ids.
+ *                            (row h*nQB + qb), ascending kv-block ids.  ws:
+ *                            NULL, or svg_workspace_bytes(SVG_OP_ATTN_CSR,
+ *                            dims, bq, bk) bytes.
  * svg_dense_attn:            every tile kept (the dense baseline), with no
  *                            list memory.
+ * Kernels: bf16 with bk = 64, bq = 64 or 128, nKB <= 8192 and N*d*2 < 2^31
+ * runs on the key-tiled V^T kernel below: V is first transposed into the
+ * workspace (svg_block_sparse_attn always; svg_block_sparse_attn_csr when ws
+ * is not NULL), and the text rows' groups may be split by keys as described
+ * for svg_block_sparse_attn_csr_vt.  Other bf16 shapes, and
+ * svg_block_sparse_attn_csr with ws == NULL, run on the row-major MFMA
+ * kernel; fp32 and bf16 (16, 16) run on the vector kernel.  Every kernel
+ * computes the same softmax; results differ only by fp32 summation order
+ * and the bf16 rounding of the row sum (the V^T kernel sums the bf16
+ * probabilities that enter P.V).  A ws that shares a byte with Q, K, V or O
+ * is SVG_ERR_RANGE; a smaller one SVG_ERR_WORKSPACE.  Calls that share one
+ * ws must not overlap in time.
  * ------------------------------------------------------------------------- */
 svg_status svg_block_sparse_attn(const svg_dims *dims, svg_dtype dtype,
                                  const void *Q, const void *K, const void *V,
@@ -194,7 +210,7 @@ svg_status svg_block_sparse_attn_csr(const svg_dims *dims, svg_dtype dtype,
                                      const void *Q, const void *K, const void *V,
                                      const int32_t *row_ptr, const int32_t *kv_idx,
                                      int32_t bq, int32_t bk, float softmax_scale,
-                                     void *O, void *stream);
+                                     void *O, void *ws, size_t ws_bytes, void *stream);
 svg_status svg_dense_attn(const svg_dims *dims, svg_dtype dtype,
                           const void *Q, const void *K, const void *V,
                           int32_t bq, int32_t bk, float softmax_scale,

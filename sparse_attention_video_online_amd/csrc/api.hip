@@ -74,10 +74,31 @@ bool overlaps2(const void *a, size_t la, const void *b, size_t lb) {
   return x < y + lb && y < x + la;
 }
 
-size_t block_sparse_ws(const Dims &dm, int bq, int bk) {
+// The bf16 block-sparse entries that take row-major V run on the key-tiled
+// V^T kernel wherever it covers the shape: V is first transposed into the
+// caller's workspace (then the split partials of the text groups follow).
+bool vt_covers(const Dims &dm, int bq, int bk) {
+  return bk == 64 && (bq == 64 || bq == 128) && (dm.N + 63) / 64 <= svgk::attn_vt_max_kv_blocks() &&
+         (int64_t)dm.N * dm.d * 2 < ((int64_t)1 << 31);
+}
+
+size_t vt_bytes(const Dims &dm) { return (size_t)dm.H * ((dm.N + 63) / 64) * 64 * dm.d * 2; }
+
+// Vt, then the split partials (0 when the V^T kernel does not cover the shape)
+size_t rowmajor_v_ws(const Dims &dm, int bq, int bk) {
+  if (!vt_covers(dm, bq, bk)) return 0;
+  return align256(vt_bytes(dm)) + align256(svgk::attn_vt_ws_bytes(dm, bq, bk));
+}
+
+size_t block_sparse_lists_ws(const Dims &dm, int bq, int bk) {
   const size_t nqb = (dm.N + bq - 1) / bq, nkb = (dm.N + bk - 1) / bk;
   const size_t rows = (size_t)dm.H * nqb;
   return svgk::compact_ws_bytes((int)rows) + align256((rows + 1) * 4) + align256(rows * nkb * 4);
+}
+
+// bf16 = false: the fp32 path needs the lists only
+size_t block_sparse_ws(const Dims &dm, int bq, int bk, bool bf16 = true) {
+  return block_sparse_lists_ws(dm, bq, bk) + (bf16 ? rowmajor_v_ws(dm, bq, bk) : 0);
 }
 
 hipError_t run_attention(const Dims &dm, svg_dtype dtype, const void *Q, const void *K,
@@ -90,6 +111,18 @@ hipError_t run_attention(const Dims &dm, svg_dtype dtype, const void *Q, const v
 }
 
 float resolve_scale(float s, int d) { return s < 0.f ? 1.f / sqrtf((float)d) : s; }
+
+// Row-major V through the V^T kernel: V -> Vt (rows as given) at the start of
+// vws, the split partials after it, then the attention.
+hipError_t run_attention_vt(const Dims &dm, const void *Q, const void *K, const void *V, void *O,
+                            const int32_t *row_ptr, const int32_t *kv_idx, int bq, int bk, float scale,
+                            void *vws, hipStream_t st) {
+  void *vt = vws;
+  void *part = svgk::attn_vt_ws_bytes(dm, bq, bk) > 0 ? (char *)vws + align256(vt_bytes(dm)) : nullptr;
+  hipError_t e = svgk::launch_layout_vt(dm, V, vt, nullptr, st, svgk::kVtIdentity);
+  if (e != hipSuccess) return e;
+  return svgk::launch_attn_vt(dm, Q, K, vt, O, row_ptr, kv_idx, bq, bk, scale, st, false, nullptr, part);
+}
 
 }  // namespace
 
@@ -108,11 +141,14 @@ size_t svg_workspace_bytes(svg_op op, const svg_dims *dims, int32_t a, int32_t b
       if (check_dims(dims, &dm) != SVG_OK || a < 1) return 0;
       return svgk::profile_ws_bytes(dm, a);
     case SVG_OP_BLOCK_SPARSE:
-      if (check_dims(dims, &dm) != SVG_OK || check_blocks(a, b) != SVG_OK) return 0;
+      if (check_dims(dims, &dm, false) != SVG_OK || check_blocks(a, b) != SVG_OK) return 0;
       return block_sparse_ws(dm, a, b);
     case SVG_OP_ATTN_VT:
       if (check_dims(dims, &dm) != SVG_OK) return 0;
       return svgk::attn_vt_ws_bytes(dm, a, b);
+    case SVG_OP_ATTN_CSR:
+      if (check_dims(dims, &dm, false) != SVG_OK || check_blocks(a, b) != SVG_OK) return 0;
+      return rowmajor_v_ws(dm, a, b);
   }
   return 0;
 }
@@ -201,6 +237,16 @@ static svg_status attn_checks(const svg_dims *dims, svg_dtype dtype, const void 
   return SVG_OK;
 }
 
+// A workspace the library writes must not share a byte with the tensors.
+static svg_status ws_clear(const Dims &dm, svg_dtype dtype, size_t need, const void *Q, const void *K,
+                           const void *V, const void *O, const void *ws, const char *what) {
+  const size_t bytes = (size_t)dm.H * dm.N * dm.d * elem_bytes(dtype);
+  if (need > 0 && (overlaps2(ws, need, Q, bytes) || overlaps2(ws, need, K, bytes) ||
+                   overlaps2(ws, need, V, bytes) || overlaps2(ws, need, O, bytes)))
+    return fail(SVG_ERR_RANGE, "%s: workspace overlaps a tensor", what);
+  return SVG_OK;
+}
+
 svg_status svg_block_sparse_attn(const svg_dims *dims, svg_dtype dtype, const void *Q, const void *K,
                                  const void *V, const uint8_t *block_mask, int32_t bq, int32_t bk,
                                  float softmax_scale, void *O, void *ws, size_t ws_bytes,
@@ -212,9 +258,11 @@ svg_status svg_block_sparse_attn(const svg_dims *dims, svg_dtype dtype, const vo
   const int nqb = (dm.N + bq - 1) / bq, nkb = (dm.N + bk - 1) / bk;
   const int64_t rows = (int64_t)dm.H * nqb;
   if (rows * nkb >= ((int64_t)1 << 31)) return fail(SVG_ERR_SHAPE, "block_sparse_attn: H*nQB*nKB >= 2^31");
-  const size_t need = block_sparse_ws(dm, bq, bk);
+  const bool bf16 = dtype == SVG_BF16;
+  const size_t need = block_sparse_ws(dm, bq, bk, bf16);
   if (ws == nullptr || ws_bytes < need)
     return fail(SVG_ERR_WORKSPACE, "block_sparse_attn: workspace %zu < %zu bytes", ws_bytes, need);
+  if ((s = ws_clear(dm, dtype, need, Q, K, V, O, ws, "block_sparse_attn")) != SVG_OK) return s;
   char *w = (char *)ws;
   const size_t c0 = svgk::compact_ws_bytes((int)rows);
   int32_t *row_ptr = (int32_t *)(w + c0);
@@ -222,21 +270,35 @@ svg_status svg_block_sparse_attn(const svg_dims *dims, svg_dtype dtype, const vo
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = svgk::launch_compact((int)rows, nkb, block_mask, row_ptr, kv_idx, w, st);
   if (e != hipSuccess) return hip_status(e, "svg_block_sparse_attn (compact)");
-  return hip_status(run_attention(dm, dtype, Q, K, V, O, row_ptr, kv_idx, bq, bk,
-                                  resolve_scale(softmax_scale, dm.d), st),
+  const float scale = resolve_scale(softmax_scale, dm.d);
+  if (bf16 && vt_covers(dm, bq, bk))
+    return hip_status(run_attention_vt(dm, Q, K, V, O, row_ptr, kv_idx, bq, bk, scale,
+                                       w + block_sparse_lists_ws(dm, bq, bk), st),
+                      "svg_block_sparse_attn");
+  return hip_status(run_attention(dm, dtype, Q, K, V, O, row_ptr, kv_idx, bq, bk, scale, st),
                     "svg_block_sparse_attn");
 }
 
 svg_status svg_block_sparse_attn_csr(const svg_dims *dims, svg_dtype dtype, const void *Q,
                                      const void *K, const void *V, const int32_t *row_ptr,
                                      const int32_t *kv_idx, int32_t bq, int32_t bk,
-                                     float softmax_scale, void *O, void *stream) {
+                                     float softmax_scale, void *O, void *ws, size_t ws_bytes,
+                                     void *stream) {
   Dims dm{};
   svg_status s;
   if ((s = attn_checks(dims, dtype, Q, K, V, O, bq, bk, &dm)) != SVG_OK) return s;
   if (!row_ptr || !kv_idx) return fail(SVG_ERR_NULL, "block_sparse_attn_csr: NULL list");
-  return hip_status(run_attention(dm, dtype, Q, K, V, O, row_ptr, kv_idx, bq, bk,
-                                  resolve_scale(softmax_scale, dm.d), (hipStream_t)stream),
+  const float scale = resolve_scale(softmax_scale, dm.d);
+  hipStream_t st = (hipStream_t)stream;
+  if (ws != nullptr && dtype == SVG_BF16 && vt_covers(dm, bq, bk)) {
+    const size_t need = rowmajor_v_ws(dm, bq, bk);
+    if (ws_bytes < need)
+      return fail(SVG_ERR_WORKSPACE, "block_sparse_attn_csr: workspace %zu < %zu bytes", ws_bytes, need);
+    if ((s = ws_clear(dm, dtype, need, Q, K, V, O, ws, "block_sparse_attn_csr")) != SVG_OK) return s;
+    return hip_status(run_attention_vt(dm, Q, K, V, O, row_ptr, kv_idx, bq, bk, scale, ws, st),
+                      "svg_block_sparse_attn_csr");
+  }
+  return hip_status(run_attention(dm, dtype, Q, K, V, O, row_ptr, kv_idx, bq, bk, scale, st),
                     "svg_block_sparse_attn_csr");
 }
 

@@ -506,7 +506,7 @@ hipError_t launch_profile_mfma(const Dims &dm, const void *Q, const void *K, con
   hipLaunchKernelGGL(profile_order, dim3((n_s + 255) / 256), dim3(256), 0, st, sample_idx, n_s, dm.F, dm.S,
                      p.ord_t);
   // key-tiled V^T of V in its own token order, every frame from a new tile
-  const hipError_t ev = launch_layout_vt(dm, V, p.vt, nullptr, st, true);
+  const hipError_t ev = launch_layout_vt(dm, V, p.vt, nullptr, st, kVtFrames);
   if (ev != hipSuccess) return ev;
   const dim3 gridf(gf.nqg * gf.nchunks * dm.H), gridt(gf.nqg * gt.nchunks * dm.H);
 #define SVG_PROFILE_PASSES(DD)                                                                                   \

@@ -77,10 +77,16 @@ hipError_t launch_attn_vt(const Dims &dm, const void *Q, const void *K, const vo
 // Bytes of ws the sparse launch splits its text groups into (0: no split).
 size_t attn_vt_ws_bytes(const Dims &dm, int bq, int bk);
 int attn_vt_max_kv_blocks();
-// frames: keep every head's token order, each frame and the text starting a
-// new 64-key tile (vt_frame_tiles(dm) tiles a head, zero past each end)
+// Row order of the key-tiled V^T copy:
+//   kVtLabels:   each head's executing layout per labels (NULL: every head
+//                position-major), as svg_layout_permute;
+//   kVtFrames:   every head's token order, each frame and the text starting
+//                a new 64-key tile (vt_frame_tiles(dm) tiles a head, zero
+//                past each end);
+//   kVtIdentity: every head's rows as given.
+enum { kVtLabels = 0, kVtFrames = 1, kVtIdentity = 2 };
 hipError_t launch_layout_vt(const Dims &dm, const void *V, void *Vt, const int32_t *labels, hipStream_t st,
-                            bool frames = false);
+                            int mode = kVtLabels);
 inline int vt_frame_tiles(const Dims &dm) {
   return dm.F * ((dm.S + 63) / 64) + (dm.T + 63) / 64;
 }

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libsvg_hip.so")
 SVG_OK, SVG_ERR_NULL, SVG_ERR_SHAPE, SVG_ERR_DTYPE, SVG_ERR_UNSUPPORTED, SVG_ERR_RANGE, \
     SVG_ERR_WORKSPACE, SVG_ERR_HIP = range(8)
 SVG_F32, SVG_BF16 = 0, 1
-SVG_OP_PROFILE, SVG_OP_BLOCK_SPARSE, SVG_OP_COMPACT, SVG_OP_ATTN_VT = 0, 1, 2, 3
+SVG_OP_PROFILE, SVG_OP_BLOCK_SPARSE, SVG_OP_COMPACT, SVG_OP_ATTN_VT, SVG_OP_ATTN_CSR = 0, 1, 2, 3, 4
 SVG2_OP_KMEANS, SVG2_OP_CLUSTER_PERMUTE, SVG2_OP_VARLEN = 0, 1, 2
 
 
@@ -58,7 +58,7 @@ SIGNATURES = {
     "svg_build_block_mask": [_DIMS, _MASK, _P, _I, _I, _P, _P],
     "svg_compact_block_mask": [_I, _I, _P, _P, _P, _P, _Z, _P],
     "svg_block_sparse_attn": [_DIMS, _I, _P, _P, _P, _P, _I, _I, _F, _P, _P, _Z, _P],
-    "svg_block_sparse_attn_csr": [_DIMS, _I, _P, _P, _P, _P, _P, _I, _I, _F, _P, _P],
+    "svg_block_sparse_attn_csr": [_DIMS, _I, _P, _P, _P, _P, _P, _I, _I, _F, _P, _P, _Z, _P],
     "svg_dense_attn": [_DIMS, _I, _P, _P, _P, _I, _I, _F, _P, _P],
     "svg_vt_elems": [_DIMS],
     "svg_layout_permute_vt": [_DIMS, _I, _P, _P, _P, _P],
@@ -107,7 +107,14 @@ def _check(status, name):
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    """Device pointer of a tensor argument (None -> NULL).  Every argument
+    check of a call runs before its first pointer is taken, so a CPU tensor
+    is reported only once its dtype and size are right."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor arguments must be device tensors")
+    return ctypes.c_void_p(t.data_ptr())
 
 
 def _stream():
@@ -122,26 +129,68 @@ def _dtype(t):
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
-def _need(t, name, dtype=None, numel=None):
-    if not t.is_cuda or not t.is_contiguous():
-        raise ValueError(f"{name} must be a contiguous device tensor")
+def _need(t, name, dtype=None, numel=None, min_numel=None):
+    """Checks a tensor argument before anything reaches the library: its
+    dtype, its element count (exact, or a capacity) and contiguity (_ptr
+    then requires a device tensor).  Every tensor the C ABI receives goes
+    through here, so a wrong dtype or size raises instead of letting a kernel
+    read or write past a buffer."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if numel is not None and t.numel() != numel:
         raise ValueError(f"{name} must have {numel} elements, got {t.numel()}")
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError(f"{name} must have at least {min_numel} elements, got {t.numel()}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _opt(t, name, **kw):
+    if t is not None:
+        _need(t, name, **kw)
+
+
+def _bytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
 
 
 def dims(F, S, T, H, d):
     return svg_dims(F, S, T, H, d)
 
 
-def _qkv(q, k, v, F, S, T):
-    H, N, d = q.shape
+def _shape3(x, name):
+    if not isinstance(x, torch.Tensor) or x.dim() != 3:
+        raise ValueError(f"{name} must be a [H][N][d] tensor")
+    return x.shape
+
+
+def _video_dims(x, F, S, T, name="X"):
+    H, N, d = _shape3(x, name)
     if N != F * S + T:
-        raise ValueError(f"N={N} != F*S+T={F * S + T}")
+        raise ValueError(f"{name}: N={N} != F*S+T={F * S + T}")
+    return svg_dims(F, S, T, H, d)
+
+
+def _qkv(q, k, v, F, S, T):
+    dm = _video_dims(q, F, S, T, "Q")
+    H, N, d = q.shape
+    dt = _dtype(q)
     for t, n in ((q, "Q"), (k, "K"), (v, "V")):
         _need(t, n, q.dtype, H * N * d)
-    return svg_dims(F, S, T, H, d), _dtype(q)
+    return dm, dt
+
+
+def _out_like(out, x, name="out"):
+    if out is None:
+        return torch.empty_like(x)
+    _need(out, name, x.dtype, x.numel())
+    return out
+
+
+def _labels(labels, H):
+    _opt(labels, "labels", dtype=torch.int32, numel=H)
 
 
 def workspace_bytes(op, dm, a=0, b=0, svg2=False):
@@ -149,8 +198,9 @@ def workspace_bytes(op, dm, a=0, b=0, svg2=False):
     return fn(op, ctypes.byref(dm), a, b)
 
 
-def _ws(nbytes, device, ws=None):
+def _ws(nbytes, device, ws=None, name="ws"):
     if ws is not None:
+        _need(ws, name, torch.uint8, min_numel=int(nbytes))
         return ws
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
@@ -160,42 +210,47 @@ def _ws(nbytes, device, ws=None):
 
 def svg_profile_heads(q, k, v, sample_idx, F, S, T, ks, wt, scale=-1.0, labels=None, mse=None, ws=None):
     dm, dt = _qkv(q, k, v, F, S, T)
-    H = q.shape[0]
+    H, N = q.shape[0], q.shape[1]
     _need(sample_idx, "sample_idx", torch.int32)
+    if not 1 <= sample_idx.numel() <= N:
+        raise ValueError(f"sample_idx must hold 1..N={N} rows, got {sample_idx.numel()}")
     labels = torch.empty(H, dtype=torch.int32, device=q.device) if labels is None else labels
     mse = torch.empty(H, 2, dtype=torch.float32, device=q.device) if mse is None else mse
+    _need(labels, "labels", torch.int32, H)
+    _need(mse, "mse", torch.float32, 2 * H)
     mp = svg_mask_params(ks, wt)
-    need = workspace_bytes(SVG_OP_PROFILE, dm, sample_idx.numel())
-    ws = _ws(need, q.device, ws)
+    ws = _ws(workspace_bytes(SVG_OP_PROFILE, dm, sample_idx.numel()), q.device, ws)
     _check(_lib.svg_profile_heads(ctypes.byref(dm), dt, _ptr(q), _ptr(k), _ptr(v), _ptr(sample_idx),
                                   sample_idx.numel(), ctypes.byref(mp), scale, _ptr(labels), _ptr(mse),
-                                  _ptr(ws), ws.numel(), _stream()), "svg_profile_heads")
+                                  _ptr(ws), _bytes(ws), _stream()), "svg_profile_heads")
     return labels, mse
 
 
-def svg_layout_permute(x, F, S, T, labels=None, out=None):
-    H, N, d = x.shape
-    dm = svg_dims(F, S, T, H, d)
-    out = torch.empty_like(x) if out is None else out
-    _check(_lib.svg_layout_permute(ctypes.byref(dm), _dtype(x), _ptr(x), _ptr(out), _ptr(labels), _stream()),
-           "svg_layout_permute")
+def _layout(fn, name, x, F, S, T, labels, out):
+    dm = _video_dims(x, F, S, T)
+    dt = _dtype(x)
+    _need(x, "X", x.dtype, x.numel())
+    _labels(labels, x.shape[0])
+    out = _out_like(out, x)
+    _check(fn(ctypes.byref(dm), dt, _ptr(x), _ptr(out), _ptr(labels), _stream()), name)
     return out
+
+
+def svg_layout_permute(x, F, S, T, labels=None, out=None):
+    return _layout(_lib.svg_layout_permute, "svg_layout_permute", x, F, S, T, labels, out)
 
 
 def svg_layout_unpermute(x, F, S, T, labels=None, out=None):
-    H, N, d = x.shape
-    dm = svg_dims(F, S, T, H, d)
-    out = torch.empty_like(x) if out is None else out
-    _check(_lib.svg_layout_unpermute(ctypes.byref(dm), _dtype(x), _ptr(x), _ptr(out), _ptr(labels), _stream()),
-           "svg_layout_unpermute")
-    return out
+    return _layout(_lib.svg_layout_unpermute, "svg_layout_unpermute", x, F, S, T, labels, out)
 
 
 def svg_build_block_mask(labels, F, S, T, H, d, ks, wt, bq, bk, out=None):
     dm = svg_dims(F, S, T, H, d)
     N = F * S + T
     nqb, nkb = -(-N // bq), -(-N // bk)
+    _need(labels, "labels", torch.int32, H)
     out = torch.empty(H, nqb, nkb, dtype=torch.uint8, device=labels.device) if out is None else out
+    _need(out, "block_mask", torch.uint8, H * nqb * nkb)
     mp = svg_mask_params(ks, wt)
     _check(_lib.svg_build_block_mask(ctypes.byref(dm), ctypes.byref(mp), _ptr(labels), bq, bk, _ptr(out),
                                      _stream()), "svg_build_block_mask")
@@ -203,38 +258,69 @@ def svg_build_block_mask(labels, F, S, T, H, d, ks, wt, bq, bk, out=None):
 
 
 def svg_compact_block_mask(block_mask, row_ptr=None, kv_idx=None, ws=None):
+    if not isinstance(block_mask, torch.Tensor) or block_mask.dim() < 1:
+        raise ValueError("block_mask must be a tensor whose last dimension is nKB")
     nkb = block_mask.shape[-1]
-    rows = block_mask.numel() // nkb
+    rows = block_mask.numel() // nkb if nkb else 0
+    _need(block_mask, "block_mask", torch.uint8)
     dev = block_mask.device
     row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=dev) if row_ptr is None else row_ptr
     kv_idx = torch.empty(max(rows * nkb, 1), dtype=torch.int32, device=dev) if kv_idx is None else kv_idx
+    _need(row_ptr, "row_ptr", torch.int32, rows + 1)
+    _need(kv_idx, "kv_idx", torch.int32, min_numel=rows * nkb)
     ws = _ws(_lib.svg_workspace_bytes(SVG_OP_COMPACT, None, rows, nkb), dev, ws)
     _check(_lib.svg_compact_block_mask(rows, nkb, _ptr(block_mask), _ptr(row_ptr), _ptr(kv_idx), _ptr(ws),
-                                       ws.numel(), _stream()), "svg_compact_block_mask")
+                                       _bytes(ws), _stream()), "svg_compact_block_mask")
     return row_ptr, kv_idx
+
+
+def _lists(row_ptr, kv_idx, H, N, bq):
+    nqb = -(-N // bq)
+    _need(row_ptr, "row_ptr", torch.int32, H * nqb + 1)
+    _need(kv_idx, "kv_idx", torch.int32)
 
 
 def svg_block_sparse_attn(q, k, v, block_mask, F, S, T, bq, bk, scale=-1.0, out=None, ws=None):
     dm, dt = _qkv(q, k, v, F, S, T)
-    out = torch.empty_like(q) if out is None else out
+    H, N = q.shape[0], q.shape[1]
+    _need(block_mask, "block_mask", torch.uint8, H * (-(-N // bq)) * (-(-N // bk)))
+    out = _out_like(out, q)
     ws = _ws(workspace_bytes(SVG_OP_BLOCK_SPARSE, dm, bq, bk), q.device, ws)
     _check(_lib.svg_block_sparse_attn(ctypes.byref(dm), dt, _ptr(q), _ptr(k), _ptr(v), _ptr(block_mask), bq, bk,
-                                      scale, _ptr(out), _ptr(ws), ws.numel(), _stream()), "svg_block_sparse_attn")
+                                      scale, _ptr(out), _ptr(ws), _bytes(ws), _stream()), "svg_block_sparse_attn")
     return out
 
 
-def svg_block_sparse_attn_csr(q, k, v, row_ptr, kv_idx, F, S, T, bq, bk, scale=-1.0, out=None):
+def attn_csr_workspace(q, F, S, T, bq, bk):
+    """Workspace of svg_block_sparse_attn_csr's V^T path (None when that
+    kernel does not cover the shape)."""
+    n = workspace_bytes(SVG_OP_ATTN_CSR, svg_dims(F, S, T, q.shape[0], q.shape[2]), bq, bk)
+    return torch.empty(n, dtype=torch.uint8, device=q.device) if n > 0 else None
+
+
+def svg_block_sparse_attn_csr(q, k, v, row_ptr, kv_idx, F, S, T, bq, bk, scale=-1.0, out=None, ws=None,
+                              rowmajor_kernel=False):
+    """ws: from attn_csr_workspace (allocated here when None).
+    rowmajor_kernel: pass no workspace, so the row-major MFMA kernel runs."""
     dm, dt = _qkv(q, k, v, F, S, T)
-    out = torch.empty_like(q) if out is None else out
+    _lists(row_ptr, kv_idx, q.shape[0], q.shape[1], bq)
+    out = _out_like(out, q)
+    if rowmajor_kernel:
+        ws = None
+    elif ws is None:
+        ws = attn_csr_workspace(q, F, S, T, bq, bk)
+    else:
+        _need(ws, "ws", torch.uint8, min_numel=workspace_bytes(SVG_OP_ATTN_CSR, dm, bq, bk))
     _check(_lib.svg_block_sparse_attn_csr(ctypes.byref(dm), dt, _ptr(q), _ptr(k), _ptr(v), _ptr(row_ptr),
-                                          _ptr(kv_idx), bq, bk, scale, _ptr(out), _stream()),
+                                          _ptr(kv_idx), bq, bk, scale, _ptr(out), _ptr(ws), _bytes(ws),
+                                          _stream()),
            "svg_block_sparse_attn_csr")
     return out
 
 
 def svg_dense_attn(q, k, v, F, S, T, bq, bk, scale=-1.0, out=None):
     dm, dt = _qkv(q, k, v, F, S, T)
-    out = torch.empty_like(q) if out is None else out
+    out = _out_like(out, q)
     _check(_lib.svg_dense_attn(ctypes.byref(dm), dt, _ptr(q), _ptr(k), _ptr(v), bq, bk, scale, _ptr(out),
                                _stream()), "svg_dense_attn")
     return out
@@ -249,24 +335,27 @@ def svg_vt_elems(H, N, d):
 def svg_layout_permute_vt(v, F, S, T, labels=None, out=None):
     """Vt (key-tiled transposed layout, shape [H][nKB][d][64]) of the
     executing-layout V."""
+    dm = _video_dims(v, F, S, T, "V")
     H, N, d = v.shape
-    dm = svg_dims(F, S, T, H, d)
+    dt = _dtype(v)
+    _need(v, "V", v.dtype, v.numel())
+    _labels(labels, H)
     nkb = -(-N // 64)
     out = torch.empty(H, nkb, d, 64, dtype=v.dtype, device=v.device) if out is None else out
     _need(out, "Vt", v.dtype, svg_vt_elems(H, N, d))
-    _check(_lib.svg_layout_permute_vt(ctypes.byref(dm), _dtype(v), _ptr(v), _ptr(out), _ptr(labels), _stream()),
+    _check(_lib.svg_layout_permute_vt(ctypes.byref(dm), dt, _ptr(v), _ptr(out), _ptr(labels), _stream()),
            "svg_layout_permute_vt")
     return out
 
 
 def _qk_vt(q, k, vt, F, S, T):
+    dm = _video_dims(q, F, S, T, "Q")
     H, N, d = q.shape
-    if N != F * S + T:
-        raise ValueError(f"N={N} != F*S+T={F * S + T}")
+    dt = _dtype(q)
     for t, n in ((q, "Q"), (k, "K")):
         _need(t, n, q.dtype, H * N * d)
     _need(vt, "Vt", q.dtype, svg_vt_elems(H, N, d))
-    return svg_dims(F, S, T, H, d), _dtype(q)
+    return dm, dt
 
 
 def attn_vt_workspace(q, F, S, T, bq, bk):
@@ -276,14 +365,22 @@ def attn_vt_workspace(q, F, S, T, bq, bk):
     return torch.empty(n, dtype=torch.uint8, device=q.device) if n > 0 else None
 
 
+def _vt_ws(ws, q, dm, F, S, T, bq, bk):
+    if ws is None:
+        return attn_vt_workspace(q, F, S, T, bq, bk)
+    _need(ws, "ws", torch.uint8, min_numel=workspace_bytes(SVG_OP_ATTN_VT, dm, bq, bk))
+    return ws
+
+
 def svg_block_sparse_attn_csr_vt(q, k, vt, row_ptr, kv_idx, F, S, T, bq, bk, scale=-1.0, out=None, ws=None):
     """ws: from attn_vt_workspace (allocated here when None)."""
     dm, dt = _qk_vt(q, k, vt, F, S, T)
-    out = torch.empty_like(q) if out is None else out
-    ws = attn_vt_workspace(q, F, S, T, bq, bk) if ws is None else ws
+    _lists(row_ptr, kv_idx, q.shape[0], q.shape[1], bq)
+    out = _out_like(out, q)
+    ws = _vt_ws(ws, q, dm, F, S, T, bq, bk)
     _check(_lib.svg_block_sparse_attn_csr_vt(ctypes.byref(dm), dt, _ptr(q), _ptr(k), _ptr(vt), _ptr(row_ptr),
-                                             _ptr(kv_idx), bq, bk, scale, _ptr(out), _ptr(ws),
-                                             0 if ws is None else ws.numel() * ws.element_size(), _stream()),
+                                             _ptr(kv_idx), bq, bk, scale, _ptr(out), _ptr(ws), _bytes(ws),
+                                             _stream()),
            "svg_block_sparse_attn_csr_vt")
     return out
 
@@ -294,20 +391,20 @@ def svg_block_sparse_attn_csr_vt_layout(q, k, vt, row_ptr, kv_idx, labels, F, S,
     in each head's executing layout per labels (None: every head temporal).
     ws: from attn_vt_workspace (allocated here when None)."""
     dm, dt = _qk_vt(q, k, vt, F, S, T)
-    out = torch.empty_like(q) if out is None else out
-    ws = attn_vt_workspace(q, F, S, T, bq, bk) if ws is None else ws
+    _lists(row_ptr, kv_idx, q.shape[0], q.shape[1], bq)
+    _labels(labels, q.shape[0])
+    out = _out_like(out, q)
+    ws = _vt_ws(ws, q, dm, F, S, T, bq, bk)
     _check(_lib.svg_block_sparse_attn_csr_vt_layout(ctypes.byref(dm), dt, _ptr(q), _ptr(k), _ptr(vt),
                                                     _ptr(row_ptr), _ptr(kv_idx), _ptr(labels), bq, bk, scale,
-                                                    _ptr(out), _ptr(ws),
-                                                    0 if ws is None else ws.numel() * ws.element_size(),
-                                                    _stream()),
+                                                    _ptr(out), _ptr(ws), _bytes(ws), _stream()),
            "svg_block_sparse_attn_csr_vt_layout")
     return out
 
 
 def svg_dense_attn_vt(q, k, vt, F, S, T, bq, bk, scale=-1.0, out=None):
     dm, dt = _qk_vt(q, k, vt, F, S, T)
-    out = torch.empty_like(q) if out is None else out
+    out = _out_like(out, q)
     _check(_lib.svg_dense_attn_vt(ctypes.byref(dm), dt, _ptr(q), _ptr(k), _ptr(vt), bq, bk, scale, _ptr(out),
                                   _stream()), "svg_dense_attn_vt")
     return out
@@ -316,64 +413,94 @@ def svg_dense_attn_vt(q, k, vt, F, S, T, bq, bk, scale=-1.0, out=None):
 # ----------------------------------------------------------------------------
 # SVG2 path
 
-def _flat_dims(x):
-    H, N, d = x.shape
+def _flat_dims(x, name="X"):
+    H, N, d = _shape3(x, name)
     return svg_dims(1, N, 0, H, d)
 
 
 def svg_kmeans(x, k, iters, init_idx, assign=None, centroids=None, sizes=None, ws=None):
-    H, N, d = x.shape
     dm = _flat_dims(x)
+    H, N, d = x.shape
+    dt = _dtype(x)
+    _need(x, "X", x.dtype, x.numel())
     dev = x.device
     _need(init_idx, "init_idx", torch.int32, H * k)
     assign = torch.empty(H, N, dtype=torch.int32, device=dev) if assign is None else assign
     centroids = torch.empty(H, k, d, dtype=torch.float64, device=dev) if centroids is None else centroids
     sizes = torch.empty(H, k, dtype=torch.int32, device=dev) if sizes is None else sizes
+    _need(assign, "assign", torch.int32, H * N)
+    _need(centroids, "centroids", torch.float64, H * k * d)
+    _need(sizes, "sizes", torch.int32, H * k)
     ws = _ws(workspace_bytes(SVG2_OP_KMEANS, dm, k, svg2=True), dev, ws)
-    _check(_lib.svg_kmeans(ctypes.byref(dm), _dtype(x), _ptr(x), k, iters, _ptr(init_idx), _ptr(assign),
-                           _ptr(centroids), _ptr(sizes), _ptr(ws), ws.numel(), _stream()), "svg_kmeans")
+    _check(_lib.svg_kmeans(ctypes.byref(dm), dt, _ptr(x), k, iters, _ptr(init_idx), _ptr(assign),
+                           _ptr(centroids), _ptr(sizes), _ptr(ws), _bytes(ws), _stream()), "svg_kmeans")
     return assign, centroids, sizes
 
 
 def svg_cluster_permute(assign, k, d=64, perm=None, offs=None, ws=None):
+    if not isinstance(assign, torch.Tensor) or assign.dim() != 2:
+        raise ValueError("assign must be an int32 [H][N] tensor")
     H, N = assign.shape
+    _need(assign, "assign", torch.int32, H * N)
     dm = svg_dims(1, N, 0, H, d)
     dev = assign.device
     perm = torch.empty(H, N, dtype=torch.int32, device=dev) if perm is None else perm
     offs = torch.empty(H, k + 1, dtype=torch.int32, device=dev) if offs is None else offs
+    _need(perm, "perm", torch.int32, H * N)
+    _need(offs, "offs", torch.int32, H * (k + 1))
     ws = _ws(workspace_bytes(SVG2_OP_CLUSTER_PERMUTE, dm, k, svg2=True), dev, ws)
     _check(_lib.svg_cluster_permute(ctypes.byref(dm), _ptr(assign), k, _ptr(perm), _ptr(offs), _ptr(ws),
-                                    ws.numel(), _stream()), "svg_cluster_permute")
+                                    _bytes(ws), _stream()), "svg_cluster_permute")
     return perm, offs
 
 
 def svg_permute_rows(x, perm, inverse=False, out=None):
     dm = _flat_dims(x)
-    out = torch.empty_like(x) if out is None else out
-    _check(_lib.svg_permute_rows(ctypes.byref(dm), _dtype(x), _ptr(x), _ptr(perm), _ptr(out), int(inverse),
+    H, N, d = x.shape
+    dt = _dtype(x)
+    _need(x, "X", x.dtype, x.numel())
+    _need(perm, "perm", torch.int32, H * N)
+    out = _out_like(out, x)
+    _check(_lib.svg_permute_rows(ctypes.byref(dm), dt, _ptr(x), _ptr(perm), _ptr(out), int(inverse),
                                  _stream()), "svg_permute_rows")
     return out
 
 
 def svg_select_pairs(cq, ck, size_k, top_p, scale=-1.0, pair_ptr=None, pair_idx=None):
-    H, kq, d = cq.shape
-    kk = ck.shape[1]
+    H, kq, d = _shape3(cq, "cq")
+    kk = _shape3(ck, "ck")[1]
+    _need(cq, "cq", torch.float64, H * kq * d)
+    _need(ck, "ck", torch.float64, H * kk * d)
+    _need(size_k, "size_k", torch.int32, H * kk)
     dm = svg_dims(1, 1, 0, H, d)
     dev = cq.device
     pair_ptr = torch.empty(H, kq + 1, dtype=torch.int32, device=dev) if pair_ptr is None else pair_ptr
     pair_idx = torch.empty(H, kq * kk, dtype=torch.int32, device=dev) if pair_idx is None else pair_idx
+    _need(pair_ptr, "pair_ptr", torch.int32, H * (kq + 1))
+    _need(pair_idx, "pair_idx", torch.int32, H * kq * kk)
     _check(_lib.svg_select_pairs(ctypes.byref(dm), _ptr(cq), _ptr(ck), _ptr(size_k), kq, kk, float(top_p),
                                  scale, _ptr(pair_ptr), _ptr(pair_idx), _stream()), "svg_select_pairs")
     return pair_ptr, pair_idx
 
 
 def svg_varlen_attn(qp, kp, vp, q_offs, k_offs, pair_ptr, pair_idx, q_perm=None, scale=-1.0, out=None, ws=None):
+    dm = _flat_dims(qp, "Qp")
     H, N, d = qp.shape
+    dt = _dtype(qp)
+    for t, n in ((qp, "Qp"), (kp, "Kp"), (vp, "Vp")):
+        _need(t, n, qp.dtype, H * N * d)
+    if not isinstance(q_offs, torch.Tensor) or q_offs.dim() != 2 or not isinstance(k_offs, torch.Tensor) \
+            or k_offs.dim() != 2:
+        raise ValueError("q_offs and k_offs must be int32 [H][k+1] tensors")
     kq, kk = q_offs.shape[1] - 1, k_offs.shape[1] - 1
-    dm = _flat_dims(qp)
-    out = torch.empty_like(qp) if out is None else out
+    _need(q_offs, "q_offs", torch.int32, H * (kq + 1))
+    _need(k_offs, "k_offs", torch.int32, H * (kk + 1))
+    _need(pair_ptr, "pair_ptr", torch.int32, H * (kq + 1))
+    _need(pair_idx, "pair_idx", torch.int32, H * kq * kk)
+    _opt(q_perm, "q_perm", dtype=torch.int32, numel=H * N)
+    out = _out_like(out, qp)
     ws = _ws(workspace_bytes(SVG2_OP_VARLEN, dm, kq, kk, svg2=True), qp.device, ws)
-    _check(_lib.svg_varlen_attn(ctypes.byref(dm), _dtype(qp), _ptr(qp), _ptr(kp), _ptr(vp), _ptr(q_offs),
+    _check(_lib.svg_varlen_attn(ctypes.byref(dm), dt, _ptr(qp), _ptr(kp), _ptr(vp), _ptr(q_offs),
                                 _ptr(k_offs), kq, kk, _ptr(pair_ptr), _ptr(pair_idx), _ptr(q_perm), scale,
-                                _ptr(out), _ptr(ws), ws.numel(), _stream()), "svg_varlen_attn")
+                                _ptr(out), _ptr(ws), _bytes(ws), _stream()), "svg_varlen_attn")
     return out
