@@ -176,6 +176,33 @@ def test_attention_cogvideox_bf16_full():
         check_close(got[h], ref, BF16_MAX_ABS, BF16_REL_L2, f"cog head {h}")
 
 
+def test_attention_cogvideox_bf16_rowmajor_kernel_full():
+    """The row-major MFMA kernel (svg_block_sparse_attn_csr with no
+    workspace) at the CogVideoX shape, every row of every head."""
+    w = COG
+    g = inputs(w)
+    labels = generator_labels(w)
+    q, k, v = (to_dev(g[x], w.dtype) for x in "qkv")
+    lab = ints(labels)
+    qp, kp, vp = (svg.svg_layout_permute(t, w.F, w.S, w.T, lab) for t in (q, k, v))
+    bm = svg.svg_build_block_mask(lab, w.F, w.S, w.T, w.H, w.d, w.ks, w.wt, w.bq, w.bk)
+    row_ptr, kv_idx = svg.svg_compact_block_mask(bm)
+    op = svg.svg_block_sparse_attn_csr(qp, kp, vp, row_ptr, kv_idx, w.F, w.S, w.T, w.bq, w.bk,
+                                       rowmajor_kernel=True)
+    o_vt = svg.svg_block_sparse_attn_csr(qp, kp, vp, row_ptr, kv_idx, w.F, w.S, w.T, w.bq, w.bk)
+    o = svg.svg_layout_unpermute(op, w.F, w.S, w.T, lab)
+    sync()
+    got = to_f64(o)
+    for h in range(w.H):
+        ref = np.zeros((w.N, w.d))
+        for qb, (rows, orow) in oracle_sparse_head(w, g, h, int(labels[h])).items():
+            ref[rows] = orow
+        check_close(got[h], ref, BF16_MAX_ABS, BF16_REL_L2, f"cog row-major head {h}")
+    # the workspace form of the same call runs the V^T kernel: the bitmap
+    # entry's output, bit for bit (same kernel, same lists)
+    np.testing.assert_array_equal(to_host_bits(o_vt), to_host_bits(run_sparse(w, g, labels)[1]))
+
+
 def test_dense_cogvideox_bf16_sampled_rows():
     w = COG
     g = inputs(w)
@@ -191,16 +218,20 @@ def test_dense_cogvideox_bf16_sampled_rows():
 
 def test_attention_hunyuan_sampled_qblocks():
     """Full-size HunyuanVideo shape (N = 119,056, 24 heads, d = 128, 128x64
-    tiles, ~31% density) in the launch configuration the bench times; the
-    oracle checks sampled q-blocks of every head (first, tail/text, random)."""
+    tiles, ~31% density) through svg_block_sparse_attn (bitmap in, V
+    row-major, run on the V^T kernel); the oracle checks 32 seeded q-blocks
+    of every head plus the first, frame-straddling, video/text and tail
+    ones."""
     w = HUNYUAN
     g = inputs(w)
     labels = generator_labels(w)
     o, _, _ = run_sparse(w, g, labels)
     got = to_f64(o)
     rng = np.random.default_rng(123)
+    vid_qb = (w.F * w.S) // w.bq
     for h in range(w.H):
-        qbs = sorted(set([0, w.nqb - 1, w.nqb - 2] + list(rng.integers(0, w.nqb, size=3))))
+        qbs = sorted(set([0, 28, vid_qb, w.nqb - 2, w.nqb - 1]) |
+                     set(int(x) for x in rng.choice(w.nqb, size=32, replace=False)))
         for qb, (rows, orow) in oracle_sparse_head(w, g, h, int(labels[h]), qblocks=qbs).items():
             check_close(got[h][rows], orow, BF16_MAX_ABS, BF16_REL_L2, f"hunyuan head {h} qb {qb}")
 
@@ -218,15 +249,21 @@ def test_attention_random_bitmap_ragged(N, d, bq, bk, dtype):
     bm[0, -1, -1] = 1                          # the ragged tail tile
     o = svg.svg_block_sparse_attn(to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype),
                                   torch.from_numpy(bm).cuda(), 1, N, 0, bq, bk)
+    outs = [("bitmap entry", o)]
+    if dtype == "bf16":   # the row-major MFMA kernel through the list entry with no workspace
+        rp, ki = svg.svg_compact_block_mask(torch.from_numpy(bm).cuda())
+        outs.append(("row-major kernel", svg.svg_block_sparse_attn_csr(
+            to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype), rp, ki, 1, N, 0, bq, bk, rowmajor_kernel=True)))
     sync()
-    got = to_f64(o)
     tol = (BF16_MAX_ABS, BF16_REL_L2) if dtype == "bf16" else (F32_MAX_ABS, F32_REL_L2)
-    for h in range(H):
-        ref = attention.block_sparse_attention_full(as_f64(q[h], dtype), as_f64(k[h], dtype),
-                                                    as_f64(v[h], dtype), bm[h], bq, bk)
-        check_close(got[h], ref, *tol, f"random bitmap head {h}")
-        if bm[h, 0].sum() == 0:
-            assert np.all(got[h][:min(bq, N)] == 0.0)
+    for name, out in outs:
+        got = to_f64(out)
+        for h in range(H):
+            ref = attention.block_sparse_attention_full(as_f64(q[h], dtype), as_f64(k[h], dtype),
+                                                        as_f64(v[h], dtype), bm[h], bq, bk)
+            check_close(got[h], ref, *tol, f"{name}: random bitmap head {h}")
+            if bm[h, 0].sum() == 0:
+                assert np.all(got[h][:min(bq, N)] == 0.0)
 
 
 def test_attention_k_zero_closed_form():

@@ -71,10 +71,36 @@ def gpu_pipeline():
     return _cache["gpu"]
 
 
+def exact_sum_span_ok(x64, assign, k):
+    """Whether every cluster's member sums are exact in float64 in any order:
+    for bf16 members (8-bit significands) the exponent span of a dimension's
+    nonzero values must be at most 45 - log2(cluster size)."""
+    e = np.frexp(x64)[1]
+    nz = x64 != 0
+    for j in range(k):
+        m = assign == j
+        n = int(m.sum())
+        if n == 0:
+            continue
+        ej, nzj = e[m], nz[m]
+        hi = np.where(nzj, ej, -10 ** 6).max(axis=0)
+        lo = np.where(nzj, ej, 10 ** 6).min(axis=0)
+        span = np.where(hi >= lo, hi - lo, 0)
+        if span.max() > 45 - np.log2(n):
+            return False
+    return True
+
+
 def test_kmeans_bit_exact_all_heads():
+    """Assignments, sizes and float64 centroids equal the oracle's bit for
+    bit; the centroid part rests on the exact-sum bound, checked here on the
+    inputs."""
     r = gpu_pipeline()
+    g = data()
     for h in range(W.H):
         o = oracle_head(h)
+        assert exact_sum_span_ok(as_f64(g["q"][h], "bf16"), o["aq"], W.kq)
+        assert exact_sum_span_ok(as_f64(g["k"][h], "bf16"), o["ak"], W.kk)
         np.testing.assert_array_equal(r["aq"][h].cpu().numpy(), o["aq"])
         np.testing.assert_array_equal(r["ak"][h].cpu().numpy(), o["ak"])
         np.testing.assert_array_equal(r["sq"][h].cpu().numpy(), o["sq"])

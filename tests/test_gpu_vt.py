@@ -34,9 +34,10 @@ _cache = {}
 
 
 def inputs(w):
-    if w.name not in _cache:
-        _cache[w.name] = structured_qkv(w)
-    return _cache[w.name]
+    key = (w.name, w.d, w.H)
+    if key not in _cache:
+        _cache[key] = structured_qkv(w)
+    return _cache[key]
 
 
 def csr(bm):
@@ -169,18 +170,27 @@ def test_attention_vt_layout_fused_ragged_labels_null(F, S, T, d, bq):
         check_close(got[h], ref, BF16_MAX_ABS, BF16_REL_L2, f"fused ragged head {h}")
 
 
+def hunyuan_qblocks(w, rng, n_random=32):
+    """q-blocks checked at the HunyuanVideo shape: the first ones, two that
+    straddle the frame 0/1 boundary of a spatial head (3600 = 28.125 x 128),
+    the one that straddles the video/text boundary, the text and ragged tail
+    ones (the last, partial work-group), and n_random seeded ones."""
+    fixed = [0, 1, 28, 29, (w.F * w.S) // w.bq, w.nqb - 2, w.nqb - 1]
+    return sorted(set(fixed) | set(int(x) for x in rng.choice(w.nqb, size=n_random, replace=False)))
+
+
 def test_attention_vt_hunyuan_sampled_qblocks():
     """Full HunyuanVideo shape (N = 119,056, 24 heads, d = 128, 128x64
     tiles, ~31% density) in the launch configuration the bench times;
-    sampled q-blocks of every head, including both q-blocks of the last,
-    partial work-group and pairs that straddle a frame boundary."""
+    32 seeded q-blocks of every head plus the first, frame-straddling,
+    text and tail ones (both q-blocks of the last, partial work-group)."""
     w = HUNYUAN
     g = inputs(w)
     labels = generator_labels(w)
     got = to_f64(run_sparse_vt(w, g, labels))
     rng = np.random.default_rng(321)
     for h in range(w.H):
-        qbs = sorted(set([0, 1, 28, 29, w.nqb - 1, w.nqb - 2] + list(rng.integers(0, w.nqb, size=3))))
+        qbs = hunyuan_qblocks(w, rng)
         for qb, (rows, orow) in oracle_sparse_head(w, g, h, int(labels[h]), qblocks=qbs).items():
             check_close(got[h][rows], orow, BF16_MAX_ABS, BF16_REL_L2, f"hunyuan head {h} qb {qb}")
 
@@ -292,6 +302,37 @@ def test_dense_vt_cogvideox_sampled_rows():
         check_close(got[h][rows], ref, BF16_MAX_ABS, BF16_REL_L2, f"dense head {h}")
 
 
+@pytest.mark.parametrize("d,bq", [(128, 128), (128, 64), (64, 128)])
+def test_dense_vt_hunyuan_shape_sampled_rows(d, bq):
+    """The dense baseline at the HunyuanVideo shape (33 x 3600 + 256 tokens)
+    in the instantiations the speedup is measured with: d = 128 with
+    128-row q-blocks (the bench's denominator, all 24 heads, Q in the
+    original order and K / Vt permuted per the labels, as the bench calls
+    it), d = 128 with 64-row q-blocks, and d = 64 with 128-row q-blocks (a
+    d = 64 draw of the same generator, 4 heads).  Rows: the first ones, a
+    frame boundary, the video/text boundary, the text tail, and seeded
+    random ones, against the oracle's dense rows."""
+    from dataclasses import replace
+    w = HUNYUAN if d == 128 else replace(HUNYUAN, d=64, H=4)
+    g = inputs(w)
+    labels = generator_labels(w)
+    q, k, v = (to_dev(g[x], w.dtype) for x in "qkv")
+    lab = ints(labels)
+    kp = svg.svg_layout_permute(k, w.F, w.S, w.T, lab)
+    vt = svg.svg_layout_permute_vt(v, w.F, w.S, w.T, lab)
+    o = svg.svg_dense_attn_vt(q, kp, vt, w.F, w.S, w.T, bq, 64)
+    sync()
+    got = to_f64(o)
+    rng = np.random.default_rng(d + bq)
+    vid = w.F * w.S
+    rows = np.unique(np.r_[0:40, w.S - 20:w.S + 20, vid - 24:vid + 24, w.N - 40:w.N,
+                           rng.choice(w.N, size=96, replace=False)])
+    heads = (0, 5, 11, w.H - 1) if w.H > 4 else range(w.H)
+    for h in heads:
+        ref = attention.dense_attention(*(as_f64(g[x][h], w.dtype) for x in "qkv"), rows=rows)
+        check_close(got[h][rows], ref, BF16_MAX_ABS, BF16_REL_L2, f"dense d={d} bq={bq} head {h}")
+
+
 def test_attention_vt_k_zero_closed_form():
     """K = 0: each row's output is the mean of V over its q-block's kept keys."""
     H, N, d = 2, 600, 64
@@ -330,7 +371,8 @@ def test_attention_vt_deterministic_and_close_to_row_major():
     bm = svg.svg_build_block_mask(lab, w.F, w.S, w.T, w.H, w.d, w.ks, w.wt, w.bq, w.bk)
     row_ptr, kv_idx = svg.svg_compact_block_mask(bm)
     o_rm = svg.svg_layout_unpermute(svg.svg_block_sparse_attn_csr(qp, kp, vp, row_ptr, kv_idx, w.F, w.S, w.T,
-                                                                  w.bq, w.bk), w.F, w.S, w.T, lab)
+                                                                  w.bq, w.bk, rowmajor_kernel=True),
+                                    w.F, w.S, w.T, lab)
     sync()
     # both paths round P to bf16; the V^T path also sums the rounded values
     # for the denominator, so the two differ by up to a few bf16 ulps of O
