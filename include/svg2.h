@@ -35,12 +35,16 @@ size_t svg2_workspace_bytes(svg2_op op, const svg_dims *dims, int32_t a, int32_t
  * Only N = F*S + T, H and d are read from dims.
  *
  * svg_kmeans: per head, Lloyd k-means of the N rows of X ([H][N][d], `dtype`).
- *   Starts from centroids X[h][init_idx[h][j]].  Runs `iters` rounds of:
+ *   Starts from centroids X[h][init_idx[h][j]] (init_idx in [0, N)).  Runs
+ *   `iters` rounds of:
  *     - assign: nearest centroid by squared L2 distance, ties to the lowest
  *       index;
  *     - update: mean of the members; an empty cluster keeps its centroid.
  *   Outputs the last assignment (int32 [H][N]), its centroids (double
- *   [H][k][d]; member sums are exact in double) and the sizes (int32 [H][k]).
+ *   [H][k][d]) and the sizes (int32 [H][k]).  For bf16 X the member sums
+ *   are exact in double, so equal to the index-order sums, while the
+ *   exponent span of a dimension's nonzero member values is at most
+ *   45 - log2(cluster size) bits.
  *   ws: svg2_workspace_bytes(SVG2_OP_KMEANS, dims, k, 0).
  *   1 <= k <= 256, iters >= 1.
  * ------------------------------------------------------------------------- */
@@ -53,6 +57,10 @@ svg_status svg_kmeans(const svg_dims *dims, svg_dtype dtype, const void *X, int3
  *   perm[h][n] = original index of the n-th token in cluster order; ties
  *                keep the original order.
  *   offs[h][c] = first sorted position of cluster c (int32 [H][k+1]).
+ * assign[h][n] must lie in [0, k).  A token whose id does not is skipped
+ * (no cluster counts it, offs[h][k] counts only the others, and perm[h]
+ * from offs[h][k] on is left unwritten), so a bad id never indexes outside
+ * a buffer; the call does not report it.
  * ws: svg2_workspace_bytes(SVG2_OP_CLUSTER_PERMUTE, dims, k, 0). */
 svg_status svg_cluster_permute(const svg_dims *dims, const int32_t *assign, int32_t k,
                                int32_t *perm, int32_t *offs, void *ws, size_t ws_bytes,

@@ -410,10 +410,15 @@ void km_assign_bf3(const bf16_t *__restrict__ X, const float *__restrict__ tab, 
 // of a member row (VE values); the 256 threads form 256 / (D / VE) member
 // slots, slot s taking members s, s + slots, ... of the cluster (sorted, so
 // in index order), each summing its members in order in fp64; the slot sums
-// are then added in slot order.  Sums of bf16 values are exact in fp64 at
-// any order while the members' magnitudes span less than ~2^40, so the
-// centroid is the oracle's bit for bit; fp32 values agree to rounding.  An
-// empty cluster keeps its centroid.  With tab (the MFMA assignment), the
+// are then added in slot order.  For bf16 values (8-bit significands) every
+// partial sum of n members is a multiple of the smallest member's last bit
+// and below n times the largest member, so it is exact in fp64 (53 bits), in
+// any order, while the exponent span of a dimension's nonzero member values
+// is at most 45 - log2(n): 31 bits for a cluster of 17,774 tokens, 17 at
+// 2^28.  Within that bound the centroid is the index-order sum's (the
+// oracle's) bit for bit; beyond it the two orders may differ in the last
+// bit.  fp32 values agree to rounding.  An empty cluster keeps its
+// centroid.  With tab (the MFMA assignment), the
 // block also writes centroid j's row of the next iteration's table, as the
 // prep kernels do (same values, same summation order of ||c||^2), which
 // saves a launch per iteration.  With cnt, it zeroes column j of the sort's
@@ -498,8 +503,9 @@ void km_update(const T *__restrict__ X, const int32_t *__restrict__ perm, const 
 }
 
 // ---------------------------------------------------------------------------
-// Stable counting sort of each head's tokens by cluster id (k <= 256), in
-// two launches over chunks of kSortChunk tokens: per-chunk histograms (the
+// Stable counting sort of each head's tokens by cluster id (k <= 256; ids
+// outside [0, k) are skipped by both kernels, so no index leaves its
+// buffer), in two launches over chunks of kSortChunk tokens: per-chunk histograms (the
 // bf16 k-means assignment counts them itself); then each chunk takes from
 // all histograms its first slot per cluster (cluster offsets by a scan of
 // the totals, plus the counts of earlier chunks) and places its tokens in
@@ -515,7 +521,10 @@ void sort_count(const int32_t *__restrict__ assign, int N, int k, int nch, int32
   __syncthreads();
   const int32_t *a = assign + (size_t)h * N;
   const int n0 = ch * kSortChunk, n1 = min(N, n0 + kSortChunk);
-  for (int n = n0 + tid; n < n1; n += 256) atomicAdd(&hist[a[n]], 1);
+  for (int n = n0 + tid; n < n1; n += 256) {
+    const int c = a[n];
+    if ((unsigned)c < (unsigned)k) atomicAdd(&hist[c], 1);   // ids outside [0, k) join no cluster
+  }
   __syncthreads();
   if (tid < k) cnt[((size_t)h * nch + ch) * k + tid] = hist[tid];
 }
@@ -531,8 +540,11 @@ void sort_place(const int32_t *__restrict__ assign, int N, int k, int nch, const
   const int h = blockIdx.y, ch = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int32_t *a = assign + (size_t)h * N;
   const int n = ch * kSortChunk + tid;
-  const bool valid = n < N;
-  const int c = valid ? a[n] : 0;
+  // a token whose id is outside [0, k) is skipped: no cluster counts it (as
+  // in sort_count), and it is not placed
+  const int craw = n < N ? a[n] : -1;
+  const bool valid = (unsigned)craw < (unsigned)k;
+  const int c = valid ? craw : 0;
   // cluster t's total and its count in earlier chunks (threads t < k), then
   // an exclusive scan of the totals over the (at most 256) clusters by the
   // first 4 waves: per wave, then across their totals.  Chunk 0 writes the
