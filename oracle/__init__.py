@@ -31,7 +31,9 @@ Modules:
   layout    -- frame-major <-> position-major permutation
   profile   -- online head profiling (sampled-row MSE, label)
   svg2      -- k-means, cluster permutation, top-p pairs, varlen attention
+  fp8       -- E4M3 quantization (per-token Q, per-key-block K scales) and
+               block-sparse attention over the dequantized values
 """
 
-from . import attention, masks, layout, profile, svg2  # noqa: F401
+from . import attention, masks, layout, profile, svg2, fp8  # noqa: F401
 from .numerics import bf16_bits_to_f64  # noqa: F401
