@@ -53,6 +53,29 @@ svg_status svg_kmeans(const svg_dims *dims, svg_dtype dtype, const void *X, int3
                       double *centroids, int32_t *sizes, void *ws, size_t ws_bytes,
                       void *stream);
 
+/* ---------------------------------------------------------------------------
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ *
+ * svg_kmeans_noalloc: svg_kmeans with no workspace argument.  Its scratch
+ *   (cluster order, offsets, centroid tables, sort counts) lives in a device
+ *   array the library holds, SVG_KMEANS_NOALLOC_SCRATCH_BYTES per GPU,
+ *   allocated when the library's code is loaded on that GPU and kept until
+ *   the process ends.  The call allocates nothing.  Outputs and errors are
+ *   those of svg_kmeans, bit for bit; a problem whose
+ *   svg2_workspace_bytes(SVG2_OP_KMEANS, dims, k, 0) exceeds the array is
+ *   SVG_ERR_WORKSPACE with nothing enqueued.  The current device's array is
+ *   used, so `stream` must belong to the current device.  All calls on one
+ *   GPU share its array: calls that overlap in time there (two streams, two
+ *   host threads) race and give wrong results.  A call overwrites every
+ *   scratch word before reading it, so one call's leftovers never reach the
+ *   next.
+ * ------------------------------------------------------------------------- */
+#define SVG_KMEANS_NOALLOC_SCRATCH_BYTES (32u << 20)
+svg_status svg_kmeans_noalloc(const svg_dims *dims, svg_dtype dtype, const void *X, int32_t k,
+                              int32_t iters, const int32_t *init_idx, int32_t *assign,
+                              double *centroids, int32_t *sizes, void *stream);
+
 /* Stable counting sort of tokens by cluster.
  *   perm[h][n] = original index of the n-th token in cluster order; ties
  *                keep the original order.

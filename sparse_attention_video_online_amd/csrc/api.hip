@@ -8,6 +8,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/svg2.h"
 #include "svg_common.h"
 
@@ -111,6 +113,35 @@ hipError_t run_attention(const Dims &dm, svg_dtype dtype, const void *Q, const v
 }
 
 float resolve_scale(float s, int d) { return s < 0.f ? 1.f / sqrtf((float)d) : s; }
+
+// Scratch of svg_kmeans_noalloc: one copy of this array per GPU, held for
+// the life of the process.  Host code never passes the array's name to a
+// kernel (on the host it is a stand-in, not a device address): it looks up
+// each device's address once, with that device current, and uses only that.
+constexpr size_t kNoallocScratchBytes = (size_t)SVG_KMEANS_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices] = {};
+
+// Device address of the current device's scratch copy.
+hipError_t scratch_of_current_device(void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return hipSuccess;
+}
 
 // Row-major V through the V^T kernel: V -> Vt (rows as given) at the start of
 // vws, the split partials after it, then the attention.
@@ -434,22 +465,51 @@ size_t svg2_workspace_bytes(svg2_op op, const svg_dims *dims, int32_t a, int32_t
   return 0;
 }
 
+static svg_status kmeans_checks(const svg_dims *dims, svg_dtype dtype, const void *X, int32_t k, int32_t iters,
+                                const int32_t *init_idx, int32_t *assign, double *centroids, int32_t *sizes,
+                                Dims *dm) {
+  svg_status s;
+  if ((s = check_dims(dims, dm, false)) != SVG_OK) return s;
+  if ((s = check_dtype(dtype)) != SVG_OK) return s;
+  if (!X || !init_idx || !assign || !centroids || !sizes) return fail(SVG_ERR_NULL, "kmeans: NULL pointer");
+  if (k < 1 || k > 256 || k > dm->N) return fail(SVG_ERR_RANGE, "kmeans: k=%d out of [1, min(256, N)]", k);
+  if (iters < 1) return fail(SVG_ERR_RANGE, "kmeans: iters=%d < 1", iters);
+  return SVG_OK;
+}
+
 svg_status svg_kmeans(const svg_dims *dims, svg_dtype dtype, const void *X, int32_t k, int32_t iters,
                       const int32_t *init_idx, int32_t *assign, double *centroids, int32_t *sizes,
                       void *ws, size_t ws_bytes, void *stream) {
   Dims dm{};
   svg_status s;
-  if ((s = check_dims(dims, &dm, false)) != SVG_OK) return s;
-  if ((s = check_dtype(dtype)) != SVG_OK) return s;
-  if (!X || !init_idx || !assign || !centroids || !sizes) return fail(SVG_ERR_NULL, "kmeans: NULL pointer");
-  if (k < 1 || k > 256 || k > dm.N) return fail(SVG_ERR_RANGE, "kmeans: k=%d out of [1, min(256, N)]", k);
-  if (iters < 1) return fail(SVG_ERR_RANGE, "kmeans: iters=%d < 1", iters);
+  if ((s = kmeans_checks(dims, dtype, X, k, iters, init_idx, assign, centroids, sizes, &dm)) != SVG_OK) return s;
   const size_t need = svgk::kmeans_ws_bytes(dm, k);
   if (ws == nullptr || ws_bytes < need)
     return fail(SVG_ERR_WORKSPACE, "kmeans: workspace %zu < %zu bytes", ws_bytes, need);
   return hip_status(svgk::launch_kmeans(dm, dtype == SVG_BF16, X, k, iters, init_idx, assign, centroids,
                                         sizes, ws, (hipStream_t)stream),
                     "svg_kmeans");
+}
+
+svg_status svg_kmeans_noalloc(const svg_dims *dims, svg_dtype dtype, const void *X, int32_t k, int32_t iters,
+                              const int32_t *init_idx, int32_t *assign, double *centroids, int32_t *sizes,
+                              void *stream) {
+  Dims dm{};
+  svg_status s;
+  if ((s = kmeans_checks(dims, dtype, X, k, iters, init_idx, assign, centroids, sizes, &dm)) != SVG_OK) return s;
+  const size_t need = svgk::kmeans_ws_bytes(dm, k);
+  if (need > kNoallocScratchBytes)
+    return fail(SVG_ERR_WORKSPACE, "kmeans_noalloc: needs %zu bytes of scratch, the library holds %zu", need,
+                kNoallocScratchBytes);
+  void *ws = nullptr;
+  hipError_t e = scratch_of_current_device(&ws);
+  if (e != hipSuccess) return hip_status(e, "svg_kmeans_noalloc (scratch address)");
+  // Every scratch word the kernels read is written earlier in the same call
+  // (the sort counts are zeroed by the first table kernel or fully written
+  // by the counting pass), so a previous call's contents do not matter.
+  return hip_status(svgk::launch_kmeans(dm, dtype == SVG_BF16, X, k, iters, init_idx, assign, centroids,
+                                        sizes, ws, (hipStream_t)stream),
+                    "svg_kmeans_noalloc");
 }
 
 svg_status svg_cluster_permute(const svg_dims *dims, const int32_t *assign, int32_t k, int32_t *perm,

@@ -67,6 +67,7 @@ SIGNATURES = {
     "svg_dense_attn_vt": [_DIMS, _I, _P, _P, _P, _I, _I, _F, _P, _P],
     "svg2_workspace_bytes": [_I, _DIMS, _I, _I],
     "svg_kmeans": [_DIMS, _I, _P, _I, _I, _P, _P, _P, _P, _P, _Z, _P],
+    "svg_kmeans_noalloc": [_DIMS, _I, _P, _I, _I, _P, _P, _P, _P, _P],
     "svg_cluster_permute": [_DIMS, _P, _I, _P, _P, _P, _Z, _P],
     "svg_permute_rows": [_DIMS, _I, _P, _P, _P, _I, _P],
     "svg_select_pairs": [_DIMS, _P, _P, _P, _I, _I, _D, _F, _P, _P, _P],

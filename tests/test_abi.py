@@ -139,3 +139,21 @@ def test_vt_entry_points_validate_on_host():
     assert L.svg_layout_permute_vt(dims(), 0, FAKE, FAKE2, None, None) == svg.SVG_ERR_UNSUPPORTED
     assert L.svg_layout_permute_vt(dims(), bf16, FAKE, FAKE, None, None) == svg.SVG_ERR_RANGE
     assert L.svg_layout_permute_vt(dims(), bf16, None, FAKE2, None, None) == svg.SVG_ERR_NULL
+
+
+def test_kmeans_noalloc_rejects_problems_beyond_its_scratch():
+    """The allocation-free k-means refuses, on the host, a problem whose
+    scratch exceeds the library's array, and checks its arguments like
+    svg_kmeans."""
+    L = svg.lib()
+    big = svg.svg_dims(1, 1 << 20, 0, 24, 128)      # ~100 MB of cluster order alone
+    need = L.svg2_workspace_bytes(svg.SVG2_OP_KMEANS, ctypes.byref(big), 256, 0)
+    assert need > (32 << 20)
+    assert L.svg_kmeans_noalloc(ctypes.byref(big), 1, FAKE, 256, 10, FAKE, FAKE2, FAKE3, FAKE2, None) \
+        == svg.SVG_ERR_WORKSPACE
+    assert "scratch" in svg.last_error()
+    small = svg.svg_dims(1, 1000, 0, 2, 64)
+    assert L.svg_kmeans_noalloc(ctypes.byref(small), 1, FAKE, 0, 10, FAKE, FAKE2, FAKE3, FAKE2, None) \
+        == svg.SVG_ERR_RANGE
+    assert L.svg_kmeans_noalloc(ctypes.byref(small), 1, None, 8, 10, FAKE, FAKE2, FAKE3, FAKE2, None) \
+        == svg.SVG_ERR_NULL
