@@ -276,6 +276,50 @@ svg_status svg_dense_attn_vt(const svg_dims *dims, svg_dtype dtype,
                              int32_t bq, int32_t bk, float softmax_scale,
                              void *O, void *stream);
 
+/* ---------------------------------------------------------------------------
+ * FP8 attention ([SVG-W] "Publication record and the road ahead": FP8
+ * attention is an open item of the plan; the pages give no method, so the
+ * quantization below is this library's definition).
+ *
+ * Format: OCP E4M3 codes (bias 7, largest finite 448, subnormals, no
+ * infinities), one byte per value, round to nearest with ties to even.
+ * Scales: for a group of values x (bf16) with largest magnitude a,
+ *   code = round_e4m3(fp32(x * (448 / a))),  scale = a / 448  (fp32);
+ * a group of zeros gets codes 0 and scale 0.  A code stands for
+ * decode(code) * scale.
+ *
+ * svg_quantize_fp8_rows: one scale per row (token) of X [H][N][d] bf16:
+ *   X8 uint8 [H][N][d], scale float [H][N].  Row order is kept (use it on Q
+ *   in the original token order).
+ * svg_layout_permute_fp8: K into each head's executing layout (per labels,
+ *   NULL = every head position-major, as svg_layout_permute), then one scale
+ *   per block of 64 rows of that layout: X8 uint8 [H][N][d], scale float
+ *   [H][ceil(N/64)].
+ * svg_block_sparse_attn_fp8_vt_layout: svg_block_sparse_attn_csr_vt_layout
+ *   with Q and K given as codes and scales: the logit of query i and key j
+ *   is (sum_c Q8_ic K8_jc) * qscale_i * kscale_block(j) * softmax_scale,
+ *   accumulated in fp32 on the FP8 matrix cores; softmax, the bf16 P.V with
+ *   Vt and the bf16 output O (original token order) are those of the bf16
+ *   entry.  Q8 / qscale in the original token order; K8 / kscale, Vt and the
+ *   lists in the executing layout.  No split of the text rows' groups.
+ * svg_dense_attn_fp8_vt: every tile kept, Q8 / K8 / Vt in one common order.
+ * Limits: bf16 inputs to the quantizers; d = 128, (bq, bk) = (64, 64) or
+ * (128, 64), nKB <= 8192 for the attention (else SVG_ERR_UNSUPPORTED).
+ * Buffers must not overlap their inputs (SVG_ERR_RANGE).
+ * ------------------------------------------------------------------------- */
+svg_status svg_quantize_fp8_rows(const svg_dims *dims, svg_dtype dtype, const void *X, uint8_t *X8,
+                                 float *scale, void *stream);
+svg_status svg_layout_permute_fp8(const svg_dims *dims, svg_dtype dtype, const void *X, uint8_t *X8,
+                                  float *scale, const int32_t *labels, void *stream);
+svg_status svg_block_sparse_attn_fp8_vt_layout(const svg_dims *dims, const uint8_t *Q8, const float *qscale,
+                                               const uint8_t *K8, const float *kscale, const void *Vt,
+                                               const int32_t *row_ptr, const int32_t *kv_idx,
+                                               const int32_t *labels, int32_t bq, int32_t bk,
+                                               float softmax_scale, void *O, void *stream);
+svg_status svg_dense_attn_fp8_vt(const svg_dims *dims, const uint8_t *Q8, const float *qscale,
+                                 const uint8_t *K8, const float *kscale, const void *Vt, int32_t bq,
+                                 int32_t bk, float softmax_scale, void *O, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -447,6 +447,81 @@ svg_status svg_dense_attn_vt(const svg_dims *dims, svg_dtype dtype, const void *
 }
 
 // ---------------------------------------------------------------------------
+// FP8 attention
+
+svg_status svg_quantize_fp8_rows(const svg_dims *dims, svg_dtype dtype, const void *X, uint8_t *X8, float *scale,
+                                 void *stream) {
+  Dims dm{};
+  svg_status s;
+  if ((s = check_dims(dims, &dm, false)) != SVG_OK) return s;
+  if ((s = check_dtype(dtype)) != SVG_OK) return s;
+  if (dtype != SVG_BF16) return fail(SVG_ERR_UNSUPPORTED, "quantize_fp8_rows: bf16 inputs only");
+  if (!X || !X8 || !scale) return fail(SVG_ERR_NULL, "quantize_fp8_rows: NULL pointer");
+  const size_t bytes = (size_t)dm.H * dm.N * dm.d * 2;
+  if (overlaps2(X, bytes, X8, bytes / 2) || overlaps2(X, bytes, scale, (size_t)dm.H * dm.N * 4))
+    return fail(SVG_ERR_RANGE, "quantize_fp8_rows: outputs overlap X");
+  return hip_status(svgk::launch_quant_rows_fp8(dm, X, X8, scale, (hipStream_t)stream), "svg_quantize_fp8_rows");
+}
+
+svg_status svg_layout_permute_fp8(const svg_dims *dims, svg_dtype dtype, const void *X, uint8_t *X8, float *scale,
+                                  const int32_t *labels, void *stream) {
+  Dims dm{};
+  svg_status s;
+  if ((s = check_dims(dims, &dm)) != SVG_OK) return s;
+  if ((s = check_dtype(dtype)) != SVG_OK) return s;
+  if (dtype != SVG_BF16) return fail(SVG_ERR_UNSUPPORTED, "layout_permute_fp8: bf16 inputs only");
+  if (!X || !X8 || !scale) return fail(SVG_ERR_NULL, "layout_permute_fp8: NULL pointer");
+  const size_t bytes = (size_t)dm.H * dm.N * dm.d * 2;
+  if (overlaps2(X, bytes, X8, bytes / 2) || overlaps2(X, bytes, scale, (size_t)dm.H * ((dm.N + 63) / 64) * 4))
+    return fail(SVG_ERR_RANGE, "layout_permute_fp8: outputs overlap X");
+  return hip_status(svgk::launch_layout_fp8(dm, X, X8, scale, labels, (hipStream_t)stream), "svg_layout_permute_fp8");
+}
+
+static svg_status fp8_attn_checks(const svg_dims *dims, const void *Q8, const float *qscale, const void *K8,
+                                  const float *kscale, const void *Vt, const void *O, int bq, int bk, Dims *dm) {
+  svg_status s;
+  if ((s = check_dims(dims, dm, false)) != SVG_OK) return s;
+  if (dm->d != 128) return fail(SVG_ERR_UNSUPPORTED, "fp8 attention: head dim %d unsupported (128)", dm->d);
+  if (bk != 64 || (bq != 64 && bq != 128))
+    return fail(SVG_ERR_UNSUPPORTED, "fp8 attention: block shape %dx%d unsupported ((64,64), (128,64))", bq, bk);
+  if ((dm->N + 63) / 64 > svgk::attn_vt_max_kv_blocks())
+    return fail(SVG_ERR_UNSUPPORTED, "fp8 attention: more than %d kv-blocks", svgk::attn_vt_max_kv_blocks());
+  if ((int64_t)dm->N * dm->d * 2 >= ((int64_t)1 << 31))
+    return fail(SVG_ERR_UNSUPPORTED, "fp8 attention: one head is >= 2 GiB");
+  if (!Q8 || !qscale || !K8 || !kscale || !Vt || !O) return fail(SVG_ERR_NULL, "fp8 attention: NULL pointer");
+  const size_t obytes = (size_t)dm->H * dm->N * dm->d * 2;
+  if (overlaps2(O, obytes, Q8, obytes / 2) || overlaps2(O, obytes, K8, obytes / 2) ||
+      overlaps2(O, obytes, Vt, vt_bytes(*dm)))
+    return fail(SVG_ERR_RANGE, "fp8 attention: O overlaps an input");
+  return SVG_OK;
+}
+
+svg_status svg_block_sparse_attn_fp8_vt_layout(const svg_dims *dims, const uint8_t *Q8, const float *qscale,
+                                               const uint8_t *K8, const float *kscale, const void *Vt,
+                                               const int32_t *row_ptr, const int32_t *kv_idx,
+                                               const int32_t *labels, int32_t bq, int32_t bk,
+                                               float softmax_scale, void *O, void *stream) {
+  Dims dm{};
+  svg_status s;
+  if ((s = fp8_attn_checks(dims, Q8, qscale, K8, kscale, Vt, O, bq, bk, &dm)) != SVG_OK) return s;
+  if (!row_ptr || !kv_idx) return fail(SVG_ERR_NULL, "block_sparse_attn_fp8_vt_layout: NULL list");
+  return hip_status(svgk::launch_attn_fp8(dm, Q8, qscale, K8, kscale, Vt, O, row_ptr, kv_idx, bq,
+                                          resolve_scale(softmax_scale, dm.d), labels, true, (hipStream_t)stream),
+                    "svg_block_sparse_attn_fp8_vt_layout");
+}
+
+svg_status svg_dense_attn_fp8_vt(const svg_dims *dims, const uint8_t *Q8, const float *qscale, const uint8_t *K8,
+                                 const float *kscale, const void *Vt, int32_t bq, int32_t bk, float softmax_scale,
+                                 void *O, void *stream) {
+  Dims dm{};
+  svg_status s;
+  if ((s = fp8_attn_checks(dims, Q8, qscale, K8, kscale, Vt, O, bq, bk, &dm)) != SVG_OK) return s;
+  return hip_status(svgk::launch_attn_fp8(dm, Q8, qscale, K8, kscale, Vt, O, nullptr, nullptr, bq,
+                                          resolve_scale(softmax_scale, dm.d), nullptr, false, (hipStream_t)stream),
+                    "svg_dense_attn_fp8_vt");
+}
+
+// ---------------------------------------------------------------------------
 // SVG2 path
 
 size_t svg2_workspace_bytes(svg2_op op, const svg_dims *dims, int32_t a, int32_t b) {

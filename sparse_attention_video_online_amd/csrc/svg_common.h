@@ -90,6 +90,13 @@ hipError_t launch_layout_vt(const Dims &dm, const void *V, void *Vt, const int32
 inline int vt_frame_tiles(const Dims &dm) {
   return dm.F * ((dm.S + 63) / 64) + (dm.T + 63) / 64;
 }
+// FP8 (E4M3) quantization and attention (d = 128 for the attention).
+hipError_t launch_quant_rows_fp8(const Dims &dm, const void *X, void *X8, float *scale, hipStream_t st);
+hipError_t launch_layout_fp8(const Dims &dm, const void *X, void *X8, float *scale, const int32_t *labels,
+                             hipStream_t st);
+hipError_t launch_attn_fp8(const Dims &dm, const void *Q8, const float *qscale, const void *K8, const float *kscale,
+                           const void *Vt, void *O, const int32_t *row_ptr, const int32_t *kv_idx, int bq,
+                           float scale, const int32_t *labels, bool qo_orig, hipStream_t st);
 hipError_t launch_layout(const Dims &dm, int elem_bytes, const void *X, void *Y,
                          const int32_t *labels, bool inverse, hipStream_t st);
 hipError_t launch_permute_rows(const Dims &dm, int elem_bytes, const void *X, const int32_t *perm,

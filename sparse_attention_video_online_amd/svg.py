@@ -65,6 +65,10 @@ SIGNATURES = {
     "svg_block_sparse_attn_csr_vt": [_DIMS, _I, _P, _P, _P, _P, _P, _I, _I, _F, _P, _P, _Z, _P],
     "svg_block_sparse_attn_csr_vt_layout": [_DIMS, _I, _P, _P, _P, _P, _P, _P, _I, _I, _F, _P, _P, _Z, _P],
     "svg_dense_attn_vt": [_DIMS, _I, _P, _P, _P, _I, _I, _F, _P, _P],
+    "svg_quantize_fp8_rows": [_DIMS, _I, _P, _P, _P, _P],
+    "svg_layout_permute_fp8": [_DIMS, _I, _P, _P, _P, _P, _P],
+    "svg_block_sparse_attn_fp8_vt_layout": [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _F, _P, _P],
+    "svg_dense_attn_fp8_vt": [_DIMS, _P, _P, _P, _P, _P, _I, _I, _F, _P, _P],
     "svg2_workspace_bytes": [_I, _DIMS, _I, _I],
     "svg_kmeans": [_DIMS, _I, _P, _I, _I, _P, _P, _P, _P, _P, _Z, _P],
     "svg_kmeans_noalloc": [_DIMS, _I, _P, _I, _I, _P, _P, _P, _P, _P],
@@ -408,6 +412,82 @@ def svg_dense_attn_vt(q, k, vt, F, S, T, bq, bk, scale=-1.0, out=None):
     out = _out_like(out, q)
     _check(_lib.svg_dense_attn_vt(ctypes.byref(dm), dt, _ptr(q), _ptr(k), _ptr(vt), bq, bk, scale, _ptr(out),
                                   _stream()), "svg_dense_attn_vt")
+    return out
+
+
+# ----------------------------------------------------------------------------
+# FP8 attention
+
+def svg_quantize_fp8_rows(x, out=None, scale=None):
+    """E4M3 codes (uint8 [H][N][d]) and per-row scales (float32 [H][N]) of a
+    bf16 [H][N][d] tensor."""
+    dm = _flat_dims(x)
+    H, N, d = x.shape
+    dt = _dtype(x)
+    _need(x, "X", torch.bfloat16, x.numel())
+    out = torch.empty(H, N, d, dtype=torch.uint8, device=x.device) if out is None else out
+    scale = torch.empty(H, N, dtype=torch.float32, device=x.device) if scale is None else scale
+    _need(out, "X8", torch.uint8, x.numel())
+    _need(scale, "scale", torch.float32, H * N)
+    _check(_lib.svg_quantize_fp8_rows(ctypes.byref(dm), dt, _ptr(x), _ptr(out), _ptr(scale), _stream()),
+           "svg_quantize_fp8_rows")
+    return out, scale
+
+
+def svg_layout_permute_fp8(x, F, S, T, labels=None, out=None, scale=None):
+    """x (bf16 [H][N][d]) in each head's executing layout as E4M3 codes, with
+    one float32 scale per 64-row block ([H][ceil(N/64)])."""
+    dm = _video_dims(x, F, S, T)
+    H, N, d = x.shape
+    dt = _dtype(x)
+    _need(x, "X", torch.bfloat16, x.numel())
+    _labels(labels, H)
+    nkb = -(-N // 64)
+    out = torch.empty(H, N, d, dtype=torch.uint8, device=x.device) if out is None else out
+    scale = torch.empty(H, nkb, dtype=torch.float32, device=x.device) if scale is None else scale
+    _need(out, "X8", torch.uint8, x.numel())
+    _need(scale, "scale", torch.float32, H * nkb)
+    _check(_lib.svg_layout_permute_fp8(ctypes.byref(dm), dt, _ptr(x), _ptr(out), _ptr(scale), _ptr(labels),
+                                       _stream()), "svg_layout_permute_fp8")
+    return out, scale
+
+
+def _fp8_args(q8, qs, k8, ks, vt, F, S, T):
+    dm = _video_dims(q8, F, S, T, "Q8")
+    H, N, d = q8.shape
+    _need(q8, "Q8", torch.uint8, H * N * d)
+    _need(k8, "K8", torch.uint8, H * N * d)
+    _need(qs, "qscale", torch.float32, H * N)
+    _need(ks, "kscale", torch.float32, H * (-(-N // 64)))
+    _need(vt, "Vt", torch.bfloat16, svg_vt_elems(H, N, d))
+    return dm
+
+
+def svg_block_sparse_attn_fp8_vt_layout(q8, qs, k8, ks, vt, row_ptr, kv_idx, labels, F, S, T, bq, bk,
+                                        scale=-1.0, out=None):
+    """FP8 Q K^T (codes + scales from the two quantizers), bf16 P.V; Q8 and
+    the returned O in the original token order, K8 / Vt / lists in the
+    executing layout."""
+    dm = _fp8_args(q8, qs, k8, ks, vt, F, S, T)
+    H, N, d = q8.shape
+    _lists(row_ptr, kv_idx, H, N, bq)
+    _labels(labels, H)
+    out = torch.empty(H, N, d, dtype=torch.bfloat16, device=q8.device) if out is None else out
+    _need(out, "out", torch.bfloat16, H * N * d)
+    _check(_lib.svg_block_sparse_attn_fp8_vt_layout(ctypes.byref(dm), _ptr(q8), _ptr(qs), _ptr(k8), _ptr(ks),
+                                                    _ptr(vt), _ptr(row_ptr), _ptr(kv_idx), _ptr(labels), bq, bk,
+                                                    scale, _ptr(out), _stream()),
+           "svg_block_sparse_attn_fp8_vt_layout")
+    return out
+
+
+def svg_dense_attn_fp8_vt(q8, qs, k8, ks, vt, F, S, T, bq, bk, scale=-1.0, out=None):
+    dm = _fp8_args(q8, qs, k8, ks, vt, F, S, T)
+    H, N, d = q8.shape
+    out = torch.empty(H, N, d, dtype=torch.bfloat16, device=q8.device) if out is None else out
+    _need(out, "out", torch.bfloat16, H * N * d)
+    _check(_lib.svg_dense_attn_fp8_vt(ctypes.byref(dm), _ptr(q8), _ptr(qs), _ptr(k8), _ptr(ks), _ptr(vt), bq, bk,
+                                      scale, _ptr(out), _stream()), "svg_dense_attn_fp8_vt")
     return out
 
 
