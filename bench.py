@@ -13,7 +13,11 @@ Printed metric: effective block-sparse attention TFLOP/s.  The flop count is
 step time.  Also reported: the attention kernel's own rate (HIP events on
 its stream), the speedup over this library's dense attention on the same
 tensors, per-stage times, the MFMA roofline fraction, and the CPU oracle's
-rate on a bounded sample.
+rate on a bounded sample.  The default run adds, as extra keys of the same
+line: the same layer step with the FP8 attention ("fp8"), the
+CogVideoX-shaped layer step ("cogvideox_shape": 13 x 1350 + 224 tokens, 8
+heads, d = 64) and the SVG2 semantic path on the CogVideoX-shaped mixture
+workload ("svg2").
 """
 
 import argparse
@@ -36,6 +40,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--dense-reps", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the FP8, CogVideoX-shaped and SVG2 legs of the default run")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--density", default="k5", help="mask widths: k5 (31%%), k4 (26%%), cog_rule (~2%%)")
     ap.add_argument("--workload", default="hunyuan_layer", choices=["hunyuan_layer", "cogvideox_shape", "svg2"],
@@ -49,6 +55,8 @@ def parse():
     ap.add_argument("--v-layout", default="vt", choices=["vt", "rowmajor"],
                     help="vt: V permuted straight into the key-tiled transposed layout and the 256-row "
                          "attention kernel (default); rowmajor: row-major V and the 128-row kernel")
+    ap.add_argument("--record-counters", metavar="DIR",
+                    help="host only: per-kernel HBM traffic / MFMA busy table from rocprofv3 runs under DIR")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="host only: turn the rocprofv3 FETCH_SIZE and WRITE_SIZE counter CSVs of two "
                          "--pmc-target runs into the per-launch HBM traffic record under profiles/")
@@ -130,6 +138,147 @@ def record_traffic(fetch_csv, write_csv):
     print(json.dumps(rec))
 
 
+COUNTERS_HEADER = """# HBM traffic, achieved bandwidth and MFMA busy time of the path's kernels
+
+Two programs, each run under rocprofv3 four times (kernel trace; FETCH_SIZE; WRITE_SIZE;
+SQ_VALU_MFMA_BUSY_CYCLES), from /tmp on the MI355X box (`<repo>` is the repository root,
+`<out>` the output folder):
+
+```
+# layer: the HunyuanVideo-shaped SVG1 layer step (33 x 3600 + 256 tokens, 24 heads, d = 128)
+ARGS="--no-extra --steps 2 --warmup 1 --no-cpu-baseline --dense-reps 1"
+# svg2: the SVG2 semantic path on the CogVideoX-shaped mixture workload
+ARGS="--workload svg2 --steps 3 --warmup 1 --no-cpu-baseline"
+rocprofv3 --kernel-trace --stats --output-format csv -d <out>/<prog>_trace -o run -- python3 <repo>/bench.py $ARGS
+rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/<prog>_fetch -o run -- python3 <repo>/bench.py $ARGS
+rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/<prog>_write -o run -- python3 <repo>/bench.py $ARGS
+rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES --output-format csv -d <out>/<prog>_sq -o run -- python3 <repo>/bench.py $ARGS
+python3 <repo>/bench.py --record-counters <out>        # writes this table
+```
+
+Durations are each dispatch's trace time; counters are joined to it by dispatch id.  Algorithmic
+bytes are what a launch must read and write once: a copy reads and writes its tensor; the
+profiler's full pass reads K, its V^T copy and the sampled Q rows; a k-means assignment reads the
+points and writes the assignment; an update reads the points (gathered through the cluster
+order) and the order; the sort reads the assignment and writes the order; a row gather reads
+and writes the tensor and reads the order.  The attention kernels are bound by the matrix
+cores, not by memory: their line is there for the traffic (the sparse kernel fetches ~18x its
+algorithmic bytes, ~78% of it served by the XCD L2s, at ~1.1 TB/s).  The SVG2 workload (36 MB
+of Q and K) stays in the L2s and the 256 MB Infinity Cache between launches, so its k-means
+kernels run at a few microseconds each and are bound by launch and per-kernel latency.
+
+"""
+
+
+COUNTER_KERNELS = ["layout_kernel", "vt_kernel", "profile_full_vt", "profile_temporal_vt", "profile_combine",
+                   "block_mask_kernel", "fill_kernel", "attn_fwd_vt", "km_assign_bf3", "km_update", "sort_place",
+                   "sort_count", "permute_rows_kernel", "select_rows", "varlen_attn", "km_prep3"]
+
+
+def record_counters(root):
+    """Per-kernel HBM traffic, achieved bandwidth and MFMA busy time from
+    rocprofv3 runs under `root`: for each of the two programs (layer: the
+    HunyuanVideo layer step, bench.py --no-extra; svg2: bench.py --workload
+    svg2) a kernel trace (<prog>_trace) and counter runs of FETCH_SIZE
+    (<prog>_fetch), WRITE_SIZE (<prog>_write) and SQ_VALU_MFMA_BUSY_CYCLES
+    (<prog>_sq), each written with --output-format csv.  Dispatches are
+    joined across runs by dispatch id (the programs are deterministic; the
+    kernel names must agree).  FETCH_SIZE and WRITE_SIZE are scaled by the
+    ratio of known to counted bytes of the layer program's layout_kernel
+    launches, plain copies of H*N*d*2 bytes each way.  MFMA busy is
+    SQ_VALU_MFMA_BUSY_CYCLES over the launch's SIMD cycles (duration x
+    2.4 GHz x 1024 SIMDs).  Writes profiles/path_kernels_hbm_mfma.md."""
+    import csv
+    import glob
+    from collections import defaultdict
+    from synth import HUNYUAN_LAYER as L, SVG2_COG as C
+
+    def find(prog, kind, suffix):
+        hits = glob.glob(os.path.join(root, f"{prog}_{kind}", "**", f"*{suffix}"), recursive=True)
+        if not hits:
+            raise SystemExit(f"record-counters: no *{suffix} under {prog}_{kind}")
+        return hits[0]
+
+    def trace(prog):
+        out = {}
+        for r in csv.DictReader(open(find(prog, "trace", "kernel_trace.csv"))):
+            out[int(r["Dispatch_Id"])] = (r["Kernel_Name"], (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
+        return out
+
+    def counters(prog, kind):
+        vals, names, grids = defaultdict(float), {}, {}
+        for r in csv.DictReader(open(find(prog, kind, "counter_collection.csv"))):
+            d = int(r["Dispatch_Id"])
+            vals[(d, r["Counter_Name"])] += float(r["Counter_Value"])
+            names[d] = r["Kernel_Name"]
+            grids[d] = int(r["Grid_Size"])
+        return vals, names, grids
+
+    def short(name):
+        for k in COUNTER_KERNELS:
+            i = name.find(k)
+            if i >= 0:
+                j = name.find("(", i)
+                return name[i:j] if j > 0 else name[i:]
+        return None
+
+    E = L.H * L.N * L.d * 2                   # one [H][N][d] bf16 tensor of the layer workload
+    EC = C.H * C.N * C.d * 2                  # one of the SVG2 workload
+    vt_attn = L.H * L.nkb * 64 * L.d * 2      # Vt of the attention
+    prof_tiles = L.F * -(-L.S // 64) + -(-L.T // 64)
+    vt_prof = L.H * prof_tiles * 64 * L.d * 2  # the profiler's Vt (every frame starts a tile)
+    attn_vt_grid = L.nkb * L.H * 256
+    alg = {   # algorithmic bytes per launch: what the step must read and write once
+        ("layer", "layout_kernel"): 2 * E,
+        ("layer", "vt_kernel<128> (attention V^T)"): E + vt_attn,
+        ("layer", "vt_kernel<128> (profiler V^T)"): E + vt_prof,
+        ("layer", "profile_full_vt<128>"): 2 * E + L.H * L.n_samples * L.d * 2,
+        ("svg2", "km_assign_bf3<64>"): EC + C.H * C.N * 4,
+        ("svg2", "km_update<unsigned short>"): EC + 2 * C.H * C.N * 4,
+        ("svg2", "sort_place"): 2 * C.H * C.N * 4,
+        ("svg2", "permute_rows_kernel"): 2 * EC + C.H * C.N * 4,
+    }
+
+    fetch_scale = write_scale = None
+    rows = []
+    for prog in ("layer", "svg2"):
+        tr = trace(prog)
+        fv, fnames, grids = counters(prog, "fetch")
+        wv, _, _ = counters(prog, "write")
+        sv, _, _ = counters(prog, "sq")
+        if prog == "layer":
+            copies = [d for d, n in fnames.items() if "layout_kernel" in n]
+            fetch_scale = E / (sum(fv[(d, "FETCH_SIZE")] for d in copies) / len(copies) * 1024.0)
+            write_scale = E / (sum(wv[(d, "WRITE_SIZE")] for d in copies) / len(copies) * 1024.0)
+        groups = defaultdict(list)
+        for d, (name, dur) in tr.items():
+            k = short(name)
+            if k is None or d not in fnames or short(fnames[d]) != k:
+                continue
+            if k.startswith("vt_kernel"):
+                k += " (attention V^T)" if grids[d] == attn_vt_grid else " (profiler V^T)"
+            groups[k].append((d, dur))
+        for k, ds in sorted(groups.items()):
+            t = sum(dur for _, dur in ds) / len(ds)
+            hbm = sum((fv[(d, "FETCH_SIZE")] * fetch_scale + wv[(d, "WRITE_SIZE")] * write_scale) * 1024.0
+                      for d, _ in ds) / len(ds)
+            busy = sum(sv.get((d, "SQ_VALU_MFMA_BUSY_CYCLES"), 0.0) for d, _ in ds) / len(ds) / (t * 2.4e9 * 1024)
+            rows.append((prog, k, len(ds), t, hbm, alg.get((prog, k)), busy))
+    out = os.path.join(ROOT, "profiles", "path_kernels_hbm_mfma.md")
+    with open(out, "w") as fh:
+        fh.write(COUNTERS_HEADER)
+        fh.write("| program | kernel | launches | avg ms | HBM GB / launch | HBM GB/s | algorithmic GB / launch | "
+                 "algorithmic GB/s | MFMA busy |\n|---|---|---|---|---|---|---|---|---|\n")
+        for prog, k, n, t, hbm, a, busy in rows:
+            al = "" if a is None else f"{a / 1e9:.4f}"
+            ag = "" if a is None else f"{a / t / 1e9:.0f}"
+            fh.write(f"| {prog} | `{k}` | {n} | {t * 1e3:.4f} | {hbm / 1e9:.4f} | {hbm / t / 1e9:.0f} | {al} | {ag} | "
+                     f"{busy * 100:.1f}% |\n")
+        fh.write(f"\nHBM bytes: FETCH_SIZE x {fetch_scale:.4f} + WRITE_SIZE x {write_scale:.4f} (KiB), the scales "
+                 f"taken from the layer program's layout_kernel launches ({E:,} bytes each way).\n")
+    print(open(out).read())
+
+
 def gen_inputs(w):
     """Seeded Q, K, V (bf16 bits) for every head, generated in parallel."""
     import concurrent.futures
@@ -189,7 +338,7 @@ def cpu_baseline(w, ks, wt, labels, seconds):
                       f"{heads} of this workload, {elapsed:.1f} s of attention time"}
 
 
-def bench_svg2(args):
+def bench_svg2(args, steps=None, warmup=None, cpu=False):
     """SVG2 path on the CogVideoX-shaped mixture workload (13 x 1350 + 224
     tokens, 8 heads, d = 64, bf16; k_q = 64, k_k = 256, 10 Lloyd iterations,
     top-p 0.9).  One step = k-means of Q and K, stable cluster sort of both,
@@ -273,16 +422,18 @@ def bench_svg2(args):
         svg.svg_varlen_attn(qp, kp, vp, oq, ok, ptr, idx, q_perm=pq, out=o, ws=ws_vl)
         mark(6)
 
-    for _ in range(args.warmup):
+    steps = args.steps if steps is None else steps
+    warmup = args.warmup if warmup is None else warmup
+    for _ in range(warmup):
         step_overlapped()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
-    for _ in range(args.steps):
+    for _ in range(steps):
         step_overlapped()
     e1.record(stream)
     torch.cuda.synchronize()
-    ms_per_step = e0.elapsed_time(e1) / args.steps
+    ms_per_step = e0.elapsed_time(e1) / steps
     o_overlapped, idx_overlapped = o.clone(), idx.clone()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(7)]
     step(ev)
@@ -305,7 +456,7 @@ def bench_svg2(args):
     km_flops = 3.0 * w.iters * H * N * d * (w.kq + w.kk)   # sub + fma per dim per centroid
     result = {
         "metric": "SVG2 semantic path ms per step (k-means, cluster sort, gathers, top-p, varlen attention)",
-        "value": round(ms_per_step, 4), "unit": "ms", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "value": round(ms_per_step, 4), "unit": "ms", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": round(ms_per_step, 4), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic (seeded Gaussian mixture)",
         "config": {"workload": w.name, "N": N, "H": H, "d": d, "kq": w.kq, "kk": w.kk, "iters": w.iters,
@@ -316,7 +467,7 @@ def bench_svg2(args):
         "gather_gbs": round(gather_bytes / (stage_ms["gather_qkv"] * 1e-3) / 1e9, 1),
         "kmeans_vector_tflops": round(km_flops / ((stage_ms["kmeans_q"] + stage_ms["kmeans_k"]) * 1e-3) / 1e12, 2),
     }
-    if not args.no_cpu_baseline:
+    if cpu:
         from oracle import svg2 as osvg2
         from oracle.numerics import as_f64
         t0 = time.perf_counter()
@@ -329,34 +480,22 @@ def bench_svg2(args):
         result["cpu_baseline"] = {"value": round(t * H * 1e3, 1), "unit": "ms", "cores": len(os.sched_getaffinity(0)),
                                   "kind": "oracle",
                                   "sample": f"float64 oracle SVG2 pipeline on head 0 ({t:.1f} s), times {H} heads"}
-    print(json.dumps(result), flush=True)
+    return result
 
 
-def main():
-    args = parse()
-    if args.record_traffic:
-        return record_traffic(*args.record_traffic)
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path shards by head "
-              f"with no exchange, see the design notes.", file=sys.stderr)
-        sys.exit(2)
-
-    if args.workload == "svg2":
-        return bench_svg2(args)
-
+def layer_bench(args, w, ks, wt, use_vt=True, steps=None, warmup=None, fp8_leg=False, cpu=False, pmc=False):
+    """The SVG1 layer step on workload w with mask widths (ks, wt): timed
+    steps, per-stage times, the dense baseline, and optionally the same
+    step with the FP8 attention.  Returns the result dict (the headline
+    fields when w is the default workload)."""
     import numpy as np
     import torch
     from sparse_attention_video_online_amd import svg
-    from synth import COG, HUNYUAN_LAYER
-    from synth.configs import HUNYUAN_DENSITY_POINTS
+    from synth import HUNYUAN_LAYER
     from synth.generators import sample_rows
 
-    if args.workload == "cogvideox_shape":
-        w = COG
-        ks, wt = w.ks, w.wt
-    else:
-        w = HUNYUAN_LAYER
-        ks, wt = HUNYUAN_DENSITY_POINTS[args.density]
+    steps = args.steps if steps is None else steps
+    warmup = args.warmup if warmup is None else warmup
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     host = gen_inputs(w)
@@ -378,12 +517,11 @@ def main():
     comp_ws = torch.empty(max(1, svg.lib().svg_workspace_bytes(svg.SVG_OP_COMPACT, None, rows, nkb)),
                           dtype=torch.uint8, device=dev)
     qp, kp, vp, op, o = (torch.empty_like(q) for _ in range(5))
-    use_vt = args.v_layout == "vt"
     vt = torch.empty(svg.svg_vt_elems(H, N, d), dtype=q.dtype, device=dev) if use_vt else None
     attn_ws = svg.attn_vt_workspace(q, F, S, T, bq, bk) if use_vt else None
     stream = torch.cuda.current_stream()
-    ev_a0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ev_a1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ev_a0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ev_a1 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
 
     def attend():
         if use_vt:
@@ -395,16 +533,19 @@ def main():
             svg.svg_block_sparse_attn_csr(qp, kp, vp, row_ptr, kv_idx, F, S, T, bq, bk, out=op,
                                           rowmajor_kernel=True)
 
-    def step(i=None, stage_events=None):
-        def mark(j):
-            if stage_events is not None:
-                stage_events[j].record(stream)
-        mark(0)
+    def front(mark):
         svg.svg_profile_heads(q, k, v, sidx, F, S, T, ks, wt, labels=labels, mse=mse, ws=prof_ws)
         mark(1)
         svg.svg_build_block_mask(labels, F, S, T, H, d, ks, wt, bq, bk, out=bmask)
         svg.svg_compact_block_mask(bmask, row_ptr=row_ptr, kv_idx=kv_idx, ws=comp_ws)
         mark(2)
+
+    def step(i=None, stage_events=None):
+        def mark(j):
+            if stage_events is not None:
+                stage_events[j].record(stream)
+        mark(0)
+        front(mark)
         if not use_vt:
             svg.svg_layout_permute(q, F, S, T, labels, out=qp)
         svg.svg_layout_permute(k, F, S, T, labels, out=kp)
@@ -423,7 +564,7 @@ def main():
             svg.svg_layout_unpermute(op, F, S, T, labels, out=o)
             mark(5)
 
-    if args.pmc_target:
+    if pmc:
         # the layer's inputs for the attention kernel, then one launch each of
         # the attention kernel and a plain copy of known size (H*N*d*2 bytes
         # read and written)
@@ -435,9 +576,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"pmc_target": True, "copy_bytes_each_way": q.numel() * 2,
                           "kept_tiles": int(bmask.sum())}), flush=True)
-        return
+        return None
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
 
@@ -446,14 +587,14 @@ def main():
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record(stream)
-    for i in range(args.steps):
+    for i in range(steps):
         step(i)
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    ms_per_step = t_start.elapsed_time(t_end) / steps
     attn_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(ev_a0, ev_a1)]))
-    print(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step (wall {wall:.2f} s), "
+    print(f"[bench] {w.name}: {steps} steps: {ms_per_step:.3f} ms/step (wall {wall:.2f} s), "
           f"attention {attn_ms:.3f} ms", file=sys.stderr, flush=True)
 
     # per-stage breakdown (one extra step with events between stages)
@@ -496,7 +637,7 @@ def main():
     d1.record(stream)
     torch.cuda.synchronize()
     dense_ms = d0.elapsed_time(d1) / args.dense_reps
-    print(f"[bench] dense attention {dense_ms:.3f} ms", file=sys.stderr, flush=True)
+    print(f"[bench] {w.name}: dense attention {dense_ms:.3f} ms", file=sys.stderr, flush=True)
 
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
     result = {
@@ -504,8 +645,8 @@ def main():
         "value": round(flops / (ms_per_step * 1e-3) / 1e12, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -515,7 +656,7 @@ def main():
         "config": {"workload": w.name, "F": F, "S": S, "T": T, "N": N, "N_video": F * S, "H": H, "d": d,
                    "bq": bq, "bk": bk, "ks_frames": ks, "wt_tokens": wt, "n_samples": int(sidx.numel()),
                    "tile_density": round(density, 4), "kept_tiles": tiles,
-                   "labels": "".join(str(int(x)) for x in lab_host), "v_layout": args.v_layout,
+                   "labels": "".join(str(int(x)) for x in lab_host), "v_layout": "vt" if use_vt else "rowmajor",
                    "qo_layout": "original order, permuted in the attention kernel" if use_vt else "permuted",
                    "parallelism": "single GPU"},
         "attn_ms": round(attn_ms, 4),
@@ -529,12 +670,116 @@ def main():
                      "kernel": (f"attn_fwd_vt<{d},{bq}>" if use_vt else f"attn_fwd_mfma<{d},{bq}>") + " (block-sparse)",
                      "achieved": round(attn_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": (measured_traffic() if (w is HUNYUAN_LAYER and args.density == "k5" and use_vt)
+                     "traffic": (measured_traffic() if (w is HUNYUAN_LAYER and ks == w.ks and wt == w.wt and use_vt)
                                  else None),
                      "flop_per_launch": flops},
     }
-    if not args.no_cpu_baseline:
+
+    if fp8_leg and use_vt and d == 128:
+        # The same step with the FP8 attention: K quantized in the executing
+        # layout (per 64-key block), Q per token in the original order, V^T
+        # as before; Q K^T on the FP8 matrix cores, P.V in bf16.
+        q8 = torch.empty(H, N, d, dtype=torch.uint8, device=dev)
+        k8 = torch.empty(H, N, d, dtype=torch.uint8, device=dev)
+        qsc = torch.empty(H, N, dtype=torch.float32, device=dev)
+        ksc = torch.empty(H, nkb, dtype=torch.float32, device=dev)
+        o8 = torch.empty_like(q)
+        f0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        f1 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+
+        def step8(i=None, stage_events=None):
+            def mark(j):
+                if stage_events is not None:
+                    stage_events[j].record(stream)
+            mark(0)
+            front(mark)
+            svg.svg_layout_permute_fp8(k, F, S, T, labels, out=k8, scale=ksc)
+            svg.svg_quantize_fp8_rows(q, out=q8, scale=qsc)
+            svg.svg_layout_permute_vt(v, F, S, T, labels, out=vt)
+            mark(3)
+            if i is not None:
+                f0[i].record(stream)
+            svg.svg_block_sparse_attn_fp8_vt_layout(q8, qsc, k8, ksc, vt, row_ptr, kv_idx, labels, F, S, T, bq, bk,
+                                                    out=o8)
+            if i is not None:
+                f1[i].record(stream)
+            mark(4)
+
+        for _ in range(warmup):
+            step8()
+        torch.cuda.synchronize()
+        t_start.record(stream)
+        for i in range(steps):
+            step8(i)
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        ms8 = t_start.elapsed_time(t_end) / steps
+        attn8 = float(np.mean([a.elapsed_time(b) for a, b in zip(f0, f1)]))
+        step8(None, se)
+        torch.cuda.synchronize()
+        st8 = {n: se[j].elapsed_time(se[j + 1]) for j, n in
+               enumerate(["profile", "mask_and_lists", "quantize_qk_permute_k_vt", "attention"])}
+        diff = (o8.float() - o.float())
+        result["fp8"] = {
+            "qk": "fp8 e4m3 (per-token Q, per-64-key K scales), P.V bf16",
+            "ms_per_step": round(ms8, 4), "value": round(flops / (ms8 * 1e-3) / 1e12, 3),
+            "attn_ms": round(attn8, 4), "attn_tflops": round(flops / (attn8 * 1e-3) / 1e12, 2),
+            "speedup_vs_bf16_attn": round(attn_ms / attn8, 3), "speedup_vs_dense_bf16_attn": round(dense_ms / attn8, 3),
+            "stage_ms": {kk: round(vv, 4) for kk, vv in st8.items()},
+            "rel_l2_vs_bf16_output": round(float(diff.norm() / o.float().norm()), 4)}
+        print(f"[bench] {w.name}: fp8 step {ms8:.3f} ms, fp8 attention {attn8:.3f} ms", file=sys.stderr, flush=True)
+    if cpu:
         result["cpu_baseline"] = cpu_baseline(w, ks, wt, lab_host, args.cpu_seconds)
+    return result
+
+
+def main():
+    args = parse()
+    if args.record_traffic:
+        return record_traffic(*args.record_traffic)
+    if args.record_counters:
+        return record_counters(args.record_counters)
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path shards by head "
+              f"with no exchange, see the design notes.", file=sys.stderr)
+        sys.exit(2)
+
+    if args.workload == "svg2":
+        print(json.dumps(bench_svg2(args, cpu=not args.no_cpu_baseline)), flush=True)
+        return
+
+    from synth import COG, HUNYUAN_LAYER
+    from synth.configs import HUNYUAN_DENSITY_POINTS
+
+    use_vt = args.v_layout == "vt"
+    if args.workload == "cogvideox_shape":
+        result = layer_bench(args, COG, COG.ks, COG.wt, use_vt, cpu=not args.no_cpu_baseline, pmc=args.pmc_target)
+        if result is not None:
+            print(json.dumps(result), flush=True)
+        return
+    ks, wt = HUNYUAN_DENSITY_POINTS[args.density]
+    default = args.density == "k5" and use_vt and not args.pmc_target
+    result = layer_bench(args, HUNYUAN_LAYER, ks, wt, use_vt, fp8_leg=default and not args.no_extra,
+                         pmc=args.pmc_target)
+    if result is None:
+        return
+    if default and not args.no_extra:
+        # the other two workloads of the path, for the record: the
+        # CogVideoX-shaped layer step and the SVG2 semantic path
+        import torch
+        torch.cuda.empty_cache()
+        cog = layer_bench(args, COG, COG.ks, COG.wt, True, steps=20, warmup=3)
+        result["cogvideox_shape"] = {k_: cog[k_] for k_ in ("ms_per_step", "value", "attn_ms", "attn_tflops",
+                                                             "dense_ms", "speedup_vs_dense_attn", "stage_ms")}
+        result["cogvideox_shape"]["tile_density"] = cog["config"]["tile_density"]
+        torch.cuda.empty_cache()
+        s2 = bench_svg2(args, steps=20, warmup=3)
+        result["svg2"] = {k_: s2[k_] for k_ in ("ms_per_step", "stage_ms", "one_stream_ms", "varlen_tflops",
+                                                 "gather_gbs")}
+        result["svg2"]["pair_density"] = s2["config"]["pair_density"]
+    if not args.no_cpu_baseline:
+        lab = [int(c) for c in result["config"]["labels"]]
+        result["cpu_baseline"] = cpu_baseline(HUNYUAN_LAYER, ks, wt, lab, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 
