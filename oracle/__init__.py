@@ -33,7 +33,9 @@ Modules:
   svg2      -- k-means, cluster permutation, top-p pairs, varlen attention
   fp8       -- E4M3 quantization (per-token Q, per-key-block K scales) and
                block-sparse attention over the dequantized values
+  ear       -- SVG-EAR: block centroids, error-aware routing, compensated
+               attention
 """
 
-from . import attention, masks, layout, profile, svg2, fp8  # noqa: F401
+from . import attention, masks, layout, profile, svg2, fp8, ear  # noqa: F401
 from .numerics import bf16_bits_to_f64  # noqa: F401
