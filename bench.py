@@ -14,7 +14,8 @@ step time.  Also reported: the attention kernel's own rate (HIP events on
 its stream), the speedup over this library's dense attention on the same
 tensors, per-stage times, the MFMA roofline fraction, and the CPU oracle's
 rate on a bounded sample.  The default run adds, as extra keys of the same
-line: the same layer step with the FP8 attention ("fp8"), the
+line: the same layer step with the FP8 attention ("fp8") and with SVG-EAR's
+compensation and routing ("ear"), the
 CogVideoX-shaped layer step ("cogvideox_shape": 13 x 1350 + 224 tokens, 8
 heads, d = 64) and the SVG2 semantic path on the CogVideoX-shaped mixture
 workload ("svg2").
@@ -30,6 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA peak
+EAR_ROUTE_K = 16                  # skipped blocks routed to exact per q-block (SVG-EAR leg)
 HBM_PEAK_GBS = 8000.0
 
 
@@ -728,6 +730,68 @@ def layer_bench(args, w, ks, wt, use_vt=True, steps=None, warmup=None, fp8_leg=F
             "stage_ms": {kk: round(vv, 4) for kk, vv in st8.items()},
             "rel_l2_vs_bf16_output": round(float(diff.norm() / o.float().norm()), 4)}
         print(f"[bench] {w.name}: fp8 step {ms8:.3f} ms, fp8 attention {attn8:.3f} ms", file=sys.stderr, flush=True)
+    if fp8_leg and use_vt:
+        # The same step with SVG-EAR: block statistics of K / V^T, routing of
+        # EAR_ROUTE_K skipped blocks per q-block into the exact sets, their
+        # lists, and the attention with the centroid compensation of every
+        # other block.  Also the distance of both outputs to dense attention
+        # on the same tensors (what the compensation is for).
+        exm = torch.empty(H, nqb, nkb, dtype=torch.uint8, device=dev)
+        ne = svg.svg_ear_centroid_elems(H, N, d)
+        kc = torch.empty(ne, dtype=torch.bfloat16, device=dev)
+        vct = torch.empty(ne, dtype=torch.bfloat16, device=dev)
+        kbar = torch.empty(H, d, nkb, dtype=torch.float64, device=dev)
+        rad = torch.empty(H, nkb, dtype=torch.float64, device=dev)
+        oe = torch.empty_like(q)
+        g0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        g1 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+
+        def step_ear(i=None, stage_events=None):
+            def mark(j):
+                if stage_events is not None:
+                    stage_events[j].record(stream)
+            mark(0)
+            svg.svg_profile_heads(q, k, v, sidx, F, S, T, ks, wt, labels=labels, mse=mse, ws=prof_ws)
+            svg.svg_build_block_mask(labels, F, S, T, H, d, ks, wt, bq, bk, out=bmask)
+            svg.svg_layout_permute(k, F, S, T, labels, out=kp)
+            svg.svg_layout_permute_vt(v, F, S, T, labels, out=vt)
+            mark(1)
+            svg.svg_ear_block_stats(kp, vt, F, S, T, kc=kc, vct=vct, kbar=kbar, radius=rad)
+            mark(2)
+            svg.svg_ear_route(q, labels, kbar, rad, bmask, F, S, T, bq, bk, EAR_ROUTE_K, out=exm)
+            svg.svg_compact_block_mask(exm, row_ptr=row_ptr, kv_idx=kv_idx, ws=comp_ws)
+            mark(3)
+            if i is not None:
+                g0[i].record(stream)
+            svg.svg_block_sparse_attn_ear_vt_layout(q, kp, vt, kc, vct, row_ptr, kv_idx, labels, F, S, T, bq, bk,
+                                                    out=oe)
+            if i is not None:
+                g1[i].record(stream)
+            mark(4)
+
+        for _ in range(warmup):
+            step_ear()
+        torch.cuda.synchronize()
+        t_start.record(stream)
+        for i in range(steps):
+            step_ear(i)
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        mse_ = t_start.elapsed_time(t_end) / steps
+        attn_e = float(np.mean([a.elapsed_time(b) for a, b in zip(g0, g1)]))
+        step_ear(None, se)
+        torch.cuda.synchronize()
+        ste = {n: se[j].elapsed_time(se[j + 1]) for j, n in
+               enumerate(["profile_masks_layouts", "block_stats", "route_and_lists", "attention"])}
+        # o still holds the SVG1 output of the staged step above
+        dn = dense.float().norm()
+        result["ear"] = {
+            "route_k": EAR_ROUTE_K, "ms_per_step": round(mse_, 4), "attn_ms": round(attn_e, 4),
+            "exact_tile_density": round(float(exm.float().mean()), 4),
+            "stage_ms": {kk: round(vv, 4) for kk, vv in ste.items()},
+            "rel_l2_vs_dense": round(float((oe.float() - dense.float()).norm() / dn), 5),
+            "svg1_rel_l2_vs_dense": round(float((o.float() - dense.float()).norm() / dn), 5)}
+        print(f"[bench] {w.name}: ear step {mse_:.3f} ms, ear attention {attn_e:.3f} ms", file=sys.stderr, flush=True)
     if cpu:
         result["cpu_baseline"] = cpu_baseline(w, ks, wt, lab_host, args.cpu_seconds)
     return result

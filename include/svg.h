@@ -277,6 +277,54 @@ svg_status svg_dense_attn_vt(const svg_dims *dims, svg_dtype dtype,
                              void *O, void *stream);
 
 /* ---------------------------------------------------------------------------
+ * SVG-EAR ([SVG-W] "Three generations of the same idea": skipped attention
+ * blocks are recovered by parameter-free centroid compensation, and
+ * error-aware routing computes high-error blocks exactly).  The pages give
+ * no formulas; this library's reading, per head in the executing layout,
+ * kv-block b = its n_b <= 64 keys:
+ *   - compensation: a block outside a q-block's exact set contributes one
+ *     centroid key kbar_b (mean key) with weight n_b and value vbar_b (mean
+ *     value): O = (sum_exact e^s v + sum_comp n_b e^t vbar) /
+ *     (sum_exact e^s + sum_comp n_b e^t), t = scale * q . kbar_b;
+ *   - routing: for q-block Q with mean query qbar, a skipped block's score is
+ *     ln n_b + scale qbar.kbar_b + ln(expm1(scale |qbar| r_b)), r_b the
+ *     block's key radius (the log of a bound on the centroid's error in the
+ *     block's attention mass); the route_k best (ties to the lower block)
+ *     join the exact set, as does the ragged last block (fewer than 64
+ *     keys), so every compensated block has n_b = 64.
+ *
+ * svg_ear_centroid_elems: elements of each centroid table,
+ *   H * ceil(nKB/64) * 64 * d (slots past the last block are zero).
+ * svg_ear_block_stats: from K [H][N][d] and Vt (svg_layout_permute_vt), both
+ *   in the executing layout: Kc (bf16 centroid keys, [H][tiles*64][d]), Vct
+ *   (bf16 value sums n_b * vbar_b in the key-tiled V^T layout,
+ *   [H][tiles][d][64]), kbar (double, dim-major [H][d][nKB]) and radius
+ *   (double [H][nKB]).
+ * svg_ear_route: from Q (original token order, mapped to the executing
+ *   layout per labels as the layout permute does), kbar, radius and the
+ *   block mask (uint8 [H][nQB][nKB]): exact_mask (same shape) = the mask,
+ *   the ragged last block and the routed blocks.  Decided in double.
+ *   route_k >= 0; bk = 64, bq = 64 or 128.
+ * svg_block_sparse_attn_ear_vt_layout: svg_block_sparse_attn_csr_vt_layout
+ *   over the CSR lists of exact_mask, plus the compensation of every other
+ *   block from Kc / Vct.  The lists must hold the ragged last block (as
+ *   exact_mask does).  nKB <= 8064; no split of the text rows' groups.
+ * Inputs bf16; outputs must not overlap inputs (SVG_ERR_RANGE).
+ * ------------------------------------------------------------------------- */
+size_t svg_ear_centroid_elems(const svg_dims *dims);
+svg_status svg_ear_block_stats(const svg_dims *dims, svg_dtype dtype, const void *K, const void *Vt,
+                               void *Kc, void *Vct, double *kbar, double *radius, void *stream);
+svg_status svg_ear_route(const svg_dims *dims, svg_dtype dtype, const void *Q, const int32_t *labels,
+                         const double *kbar, const double *radius, const uint8_t *block_mask, int32_t bq,
+                         int32_t bk, int32_t route_k, float softmax_scale, uint8_t *exact_mask,
+                         void *stream);
+svg_status svg_block_sparse_attn_ear_vt_layout(const svg_dims *dims, svg_dtype dtype, const void *Q,
+                                               const void *K, const void *Vt, const void *Kc,
+                                               const void *Vct, const int32_t *row_ptr,
+                                               const int32_t *kv_idx, const int32_t *labels, int32_t bq,
+                                               int32_t bk, float softmax_scale, void *O, void *stream);
+
+/* ---------------------------------------------------------------------------
  * FP8 attention ([SVG-W] "Publication record and the road ahead": FP8
  * attention is an open item of the plan; the pages give no method, so the
  * quantization below is this library's definition).

@@ -447,6 +447,72 @@ svg_status svg_dense_attn_vt(const svg_dims *dims, svg_dtype dtype, const void *
 }
 
 // ---------------------------------------------------------------------------
+// SVG-EAR
+
+size_t svg_ear_centroid_elems(const svg_dims *dims) {
+  Dims dm{};
+  if (check_dims(dims, &dm, false) != SVG_OK) return 0;
+  return (size_t)dm.H * svgk::ear_centroid_tiles(dm) * 64 * dm.d;
+}
+
+svg_status svg_ear_block_stats(const svg_dims *dims, svg_dtype dtype, const void *K, const void *Vt, void *Kc,
+                               void *Vct, double *kbar, double *radius, void *stream) {
+  Dims dm{};
+  svg_status s;
+  if ((s = check_dims(dims, &dm, false)) != SVG_OK) return s;
+  if ((s = check_dtype(dtype)) != SVG_OK) return s;
+  if (dtype != SVG_BF16) return fail(SVG_ERR_UNSUPPORTED, "ear_block_stats: bf16 only");
+  if (!K || !Vt || !Kc || !Vct || !kbar || !radius) return fail(SVG_ERR_NULL, "ear_block_stats: NULL pointer");
+  const size_t kb = (size_t)dm.H * dm.N * dm.d * 2, cb = svg_ear_centroid_elems(dims) * 2;
+  if (overlaps2(Kc, cb, K, kb) || overlaps2(Kc, cb, Vt, vt_bytes(dm)) || overlaps2(Vct, cb, K, kb) ||
+      overlaps2(Vct, cb, Vt, vt_bytes(dm)) || overlaps2(Kc, cb, Vct, cb))
+    return fail(SVG_ERR_RANGE, "ear_block_stats: outputs overlap the inputs or each other");
+  return hip_status(svgk::launch_ear_stats(dm, K, Vt, Kc, Vct, kbar, radius, (hipStream_t)stream),
+                    "svg_ear_block_stats");
+}
+
+svg_status svg_ear_route(const svg_dims *dims, svg_dtype dtype, const void *Q, const int32_t *labels,
+                         const double *kbar, const double *radius, const uint8_t *block_mask, int32_t bq, int32_t bk,
+                         int32_t route_k, float softmax_scale, uint8_t *exact_mask, void *stream) {
+  Dims dm{};
+  svg_status s;
+  if ((s = check_dims(dims, &dm)) != SVG_OK) return s;
+  if ((s = check_dtype(dtype)) != SVG_OK) return s;
+  if (dtype != SVG_BF16) return fail(SVG_ERR_UNSUPPORTED, "ear_route: bf16 only");
+  if (bk != 64 || (bq != 64 && bq != 128))
+    return fail(SVG_ERR_UNSUPPORTED, "ear_route: block shape %dx%d unsupported ((64,64), (128,64))", bq, bk);
+  if (!Q || !kbar || !radius || !block_mask || !exact_mask) return fail(SVG_ERR_NULL, "ear_route: NULL pointer");
+  if (route_k < 0) return fail(SVG_ERR_RANGE, "ear_route: route_k=%d < 0", route_k);
+  if (svgk::ear_route_qpw(dm) < 1) return fail(SVG_ERR_UNSUPPORTED, "ear_route: too many kv-blocks");
+  const size_t mb = (size_t)dm.H * ((dm.N + bq - 1) / bq) * ((dm.N + 63) / 64);
+  if (overlaps2(exact_mask, mb, block_mask, mb)) return fail(SVG_ERR_RANGE, "ear_route: exact_mask overlaps block_mask");
+  return hip_status(svgk::launch_ear_route(dm, Q, labels, kbar, radius, block_mask, bq, route_k,
+                                           (double)resolve_scale(softmax_scale, dm.d), exact_mask,
+                                           (hipStream_t)stream),
+                    "svg_ear_route");
+}
+
+svg_status svg_block_sparse_attn_ear_vt_layout(const svg_dims *dims, svg_dtype dtype, const void *Q, const void *K,
+                                               const void *Vt, const void *Kc, const void *Vct,
+                                               const int32_t *row_ptr, const int32_t *kv_idx,
+                                               const int32_t *labels, int32_t bq, int32_t bk,
+                                               float softmax_scale, void *O, void *stream) {
+  Dims dm{};
+  svg_status s;
+  if ((s = vt_checks(dims, dtype, Q, K, Vt, O, bq, bk, &dm)) != SVG_OK) return s;
+  if (!Kc || !Vct) return fail(SVG_ERR_NULL, "block_sparse_attn_ear: NULL centroid table");
+  if (!row_ptr || !kv_idx) return fail(SVG_ERR_NULL, "block_sparse_attn_ear: NULL list");
+  if ((dm.N + 63) / 64 > svgk::attn_ear_max_kv_blocks())
+    return fail(SVG_ERR_UNSUPPORTED, "block_sparse_attn_ear: more than %d kv-blocks", svgk::attn_ear_max_kv_blocks());
+  const size_t bytes = (size_t)dm.H * dm.N * dm.d * 2, cb = svg_ear_centroid_elems(dims) * 2;
+  if (overlaps2(O, bytes, Kc, cb) || overlaps2(O, bytes, Vct, cb))
+    return fail(SVG_ERR_RANGE, "block_sparse_attn_ear: O overlaps a centroid table");
+  return hip_status(svgk::launch_attn_vt_ear(dm, Q, K, Vt, Kc, Vct, O, row_ptr, kv_idx, bq,
+                                             resolve_scale(softmax_scale, dm.d), labels, (hipStream_t)stream),
+                    "svg_block_sparse_attn_ear_vt_layout");
+}
+
+// ---------------------------------------------------------------------------
 // FP8 attention
 
 svg_status svg_quantize_fp8_rows(const svg_dims *dims, svg_dtype dtype, const void *X, uint8_t *X8, float *scale,

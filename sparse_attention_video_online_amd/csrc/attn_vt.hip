@@ -52,13 +52,19 @@ constexpr int kNW = 8;           // waves per work-group
 // so every row starts 16-byte aligned.
 template <int D> constexpr int kPartStride = D + 4;
 
-template <int D, int BQ, bool DENSE>
+// COMP (SVG-EAR): after the exact tiles, each work-group walks the centroid
+// tiles (64 centroids of skipped blocks each, from Kc / Vct: the centroid
+// keys and the key-tiled value sums) that hold a centroid some q-block of the
+// group compensates; a q-block masks the centroids of its exact blocks and
+// the padding slots past the last block.
+template <int D, int BQ, bool DENSE, bool COMP = false>
 __global__ __launch_bounds__(kWgRows * 2, 1)
 void attn_fwd_vt(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K, const bf16_t *__restrict__ Vt,
                  bf16_t *__restrict__ O, const int32_t *__restrict__ row_ptr,
                  const int32_t *__restrict__ kv_idx, int N, int nqb, int nkb, int ngrp,
                  float c /* scale * log2(e) */, const int32_t *__restrict__ labels, int qo_orig, int F, int S,
-                 int nsplit, float *__restrict__ part) {
+                 int nsplit, float *__restrict__ part, const bf16_t *__restrict__ Kc,
+                 const bf16_t *__restrict__ Vct) {
   constexpr int G = kWgRows / BQ;          // q-blocks per work-group
   using T = DTile<D>;
   constexpr int TB = T::TBYTES;            // K tile bytes == V^T tile bytes
@@ -114,6 +120,38 @@ void attn_fwd_vt(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K, con
   int nt = nkb;
   if constexpr (!DENSE)
     nt = build_union_list<G, kWgRows * 2>(row_ptr, kv_idx, h, grp, nqb, nkb, tid, lane, wave, ulist, bits, wsum);
+  const int ntc = (nkb + 63) >> 6;   // centroid tiles (COMP)
+  const int nt_exact = nt;
+  if constexpr (COMP) {
+    // append the centroid tiles holding a centroid some q-block of the group
+    // compensates (flag g: q-block g has one in the tile)
+    __shared__ int ntot;
+    if (wave == 0) {
+      int base = nt;
+      const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+      for (int t0 = 0; t0 < ntc; t0 += 64) {
+        const int t = t0 + lane;
+        int fl = 0;
+        if (t < ntc) {
+          const int nv = min(64, nkb - 64 * t);
+          const uint64_t vm = nv >= 64 ? ~0ull : ((1ull << nv) - 1ull);
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            if (grp * G + g < nqb) {
+              const uint64_t ex = (uint64_t)bits[g * kWords + 2 * t] | ((uint64_t)bits[g * kWords + 2 * t + 1] << 32);
+              if (~ex & vm) fl |= 1 << g;
+            }
+          }
+        }
+        const uint64_t bal = __ballot(fl != 0);
+        if (fl) ulist[base + __popcll(bal & below)] = t | kCentFlag | (fl << 24);
+        base += __popcll(bal);
+      }
+      if (lane == 0) ntot = base;
+    }
+    __syncthreads();
+    nt = ntot;
+  }
 
   // this work item's part of the union list: entries j0 .. j0 + ntile - 1
   const int j0 = parted ? split * nt / nsplit : 0;
@@ -172,8 +210,53 @@ void attn_fwd_vt(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K, con
     }
     return own;
   };
-  vt_attend<D, kNW>(ntile, ent_raw, prep, Kh, Vth, N, k0, k1, k2, V0, V1, V2, qf, wave, lane, c, o, m_run,
-                    l_run);
+  // centroid tiles (COMP): mask this q-block's exact blocks and the padding
+  // slots past the last block
+  auto prep_c = [&](f32x16 &s0, f32x16 &s1, int e) -> bool {
+    const bool own = (e & own_bit) != 0;
+    if (own) {
+      // the q-block's exact flags over the tile's 64 centroids and the number
+      // that exist are wave-uniform: each key's decision is a scalar pair
+      // (lane half 0 / 1) picked per lane
+      const int t = e & kCentTileMask;
+      const uint32_t w0 = __builtin_amdgcn_readfirstlane(bits[gw * kWords + 2 * t]);
+      const uint32_t w1 = __builtin_amdgcn_readfirstlane(bits[gw * kWords + 2 * t + 1]);
+      const int nv = nkb - 64 * t;
+      auto drop = [&](uint32_t w, int key) { return ((w >> (key & 31)) & 1u) != 0 || key >= nv; };
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int k0 = 16 * (r >> 3) + (r & 7);    // acc_key_pi(0, r, hi) - 8 hi
+        if (hi ? drop(w0, k0 + 8) : drop(w0, k0)) s0[r] = -INFINITY;
+        if (hi ? drop(w1, k0 + 40) : drop(w1, k0 + 32)) s1[r] = -INFINITY;
+      }
+    }
+    return own;
+  };
+  if constexpr (COMP) {
+    // two pipeline passes: the exact tiles with the plain pipeline, then the
+    // centroid tiles continuing the same softmax state
+    const int nc = nt - nt_exact;
+    auto ent_x = [&](int j) -> int { return ulist[j < nt_exact ? j : nt_exact - 1]; };
+    auto ent_c = [&](int j) -> int { return ulist[nt_exact + (j < nc ? j : nc - 1)]; };
+    if (nt_exact > 0) {
+      vt_attend<D, kNW>(nt_exact, ent_x, prep, Kh, Vth, N, k0, k1, k2, V0, V1, V2, qf, wave, lane, c, o, m_run,
+                        l_run);
+    } else {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
+      m_run = -INFINITY;
+      l_run = 0.f;
+    }
+    if (nc > 0) {
+      __builtin_amdgcn_s_waitcnt(0);   // the first pass's trailing DMAs land before the stages are reused
+      __syncthreads();
+      vt_attend<D, kNW>(nc, ent_c, prep_c, Kh, Vth, N, k0, k1, k2, V0, V1, V2, qf, wave, lane, c, o, m_run, l_run,
+                        KvBlockRow{}, Centroids{Kc + (size_t)h * ntc * BK * D, Vct + (size_t)h * ntc * D * BK});
+    }
+  } else {
+    vt_attend<D, kNW>(ntile, ent_raw, prep, Kh, Vth, N, k0, k1, k2, V0, V1, V2, qf, wave, lane, c, o, m_run,
+                      l_run);
+  }
   __builtin_amdgcn_s_waitcnt(0);  // no DMA may land after the work-group ends
   if (parted) {
     const float lt = l_run + __shfl_xor(l_run, 32);
@@ -254,20 +337,48 @@ hipError_t launch_vt(const Dims &dm, const void *Q, const void *K, const void *V
   if (row_ptr == nullptr)
     hipLaunchKernelGGL((attn_fwd_vt<D, BQ, true>), dim3(grid), dim3(kWgRows * 2), 0, st, (const bf16_t *)Q,
                        (const bf16_t *)K, (const bf16_t *)Vt, (bf16_t *)O, row_ptr, kv_idx, dm.N, nqb, nkb, ngrp,
-                       c, labels, qo_orig, dm.F, dm.S, nsplit, part);
+                       c, labels, qo_orig, dm.F, dm.S, nsplit, part, nullptr, nullptr);
   else
     hipLaunchKernelGGL((attn_fwd_vt<D, BQ, false>), dim3(grid), dim3(kWgRows * 2), 0, st, (const bf16_t *)Q,
                        (const bf16_t *)K, (const bf16_t *)Vt, (bf16_t *)O, row_ptr, kv_idx, dm.N, nqb, nkb, ngrp,
-                       c, labels, qo_orig, dm.F, dm.S, nsplit, part);
+                       c, labels, qo_orig, dm.F, dm.S, nsplit, part, nullptr, nullptr);
   if (nsplit > 1)
     hipLaunchKernelGGL((attn_vt_merge<D>), dim3(kWgRows, nlead, dm.H), dim3(D), 0, st, part, (bf16_t *)O, dm.N,
                        ngrp, nlead, nsplit, c, labels, qo_orig, dm.F, dm.S);
   return hipGetLastError();
 }
 
+template <int D, int BQ>
+hipError_t launch_vt_ear(const Dims &dm, const void *Q, const void *K, const void *Vt, const void *Kc, const void *Vct,
+                         void *O, const int32_t *row_ptr, const int32_t *kv_idx, float c, const int32_t *labels,
+                         hipStream_t st) {
+  constexpr int G = kWgRows / BQ;
+  const int nqb = (dm.N + BQ - 1) / BQ, nkb = (dm.N + BK - 1) / BK;
+  const int ngrp = (nqb + G - 1) / G;
+  if (dm.H * ngrp == 0) return hipSuccess;
+  hipLaunchKernelGGL((attn_fwd_vt<D, BQ, false, true>), dim3(dm.H * ngrp), dim3(kWgRows * 2), 0, st,
+                     (const bf16_t *)Q, (const bf16_t *)K, (const bf16_t *)Vt, (bf16_t *)O, row_ptr, kv_idx, dm.N,
+                     nqb, nkb, ngrp, c, labels, 1, dm.F, dm.S, 1, nullptr, (const bf16_t *)Kc, (const bf16_t *)Vct);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 int attn_vt_max_kv_blocks() { return kMaxKb; }
+
+// The exact tiles and the centroid tiles share one union list.
+int attn_ear_max_kv_blocks() { return kMaxKb - kMaxKb / 64; }
+
+hipError_t launch_attn_vt_ear(const Dims &dm, const void *Q, const void *K, const void *Vt, const void *Kc,
+                              const void *Vct, void *O, const int32_t *row_ptr, const int32_t *kv_idx, int bq,
+                              float scale, const int32_t *labels, hipStream_t st) {
+  const float c = scale * kLog2e;
+  if (dm.d == 128 && bq == 128) return launch_vt_ear<128, 128>(dm, Q, K, Vt, Kc, Vct, O, row_ptr, kv_idx, c, labels, st);
+  if (dm.d == 128 && bq == 64) return launch_vt_ear<128, 64>(dm, Q, K, Vt, Kc, Vct, O, row_ptr, kv_idx, c, labels, st);
+  if (dm.d == 64 && bq == 128) return launch_vt_ear<64, 128>(dm, Q, K, Vt, Kc, Vct, O, row_ptr, kv_idx, c, labels, st);
+  if (dm.d == 64 && bq == 64) return launch_vt_ear<64, 64>(dm, Q, K, Vt, Kc, Vct, O, row_ptr, kv_idx, c, labels, st);
+  return hipErrorInvalidValue;
+}
 
 size_t attn_vt_ws_bytes(const Dims &dm, int bq, int bk) {
   if (bk != BK || (bq != 64 && bq != 128) || dm.N < 1 || dm.H < 1 || (dm.d != 64 && dm.d != 128)) return 0;

@@ -227,12 +227,32 @@ struct KvBlockRow {
   __device__ int operator()(int e) const { return (e & 0xFFFFFF) * BK; }
 };
 
-template <int D, int NW, bool SUM_BF16 = true, typename EntRaw, typename Prep, typename KRow = KvBlockRow>
+// Centroid tiles (the compensation of skipped blocks): an entry with
+// kCentFlag set names tile t = e & kCentTileMask of a second pair of tables,
+// 64 centroid keys of the head (row-major, like K) and the key-tiled V^T of
+// their value sums, each a whole zero-padded tile.  Each centroid stands for
+// 64 keys, so the tile's row sum counts 64 times (exact in fp32).  A pass
+// with Centroids continues the softmax state of an earlier pass (the caller
+// drains that pass's DMAs and passes a barrier between the two).
+// NoCentroids (the default) compiles none of it.
+constexpr int kCentFlag = 1 << 23;
+constexpr int kCentTileMask = 0x1FFF;
+struct NoCentroids {
+  static constexpr bool kOn = false;
+};
+struct Centroids {
+  static constexpr bool kOn = true;
+  const bf16_t *k;     // [tiles * 64][D] of this head
+  const bf16_t *vt;    // [tiles][D][64] of this head
+};
+
+template <int D, int NW, bool SUM_BF16 = true, typename EntRaw, typename Prep, typename KRow = KvBlockRow,
+          typename Cent = NoCentroids>
 __device__ __forceinline__ void vt_attend(int nt, EntRaw ent_raw, Prep prep, const bf16_t *__restrict__ Kh,
                                           const bf16_t *__restrict__ Vth, int N, char *k0, char *k1, char *k2,
                                           char *v0, char *v1, char *v2, const bf16x8 (&qf)[D / 16], int wave,
                                           int lane, float c, f32x16 (&o)[D / 32], float &m_run, float &l_run,
-                                          KRow krow = KRow{}) {
+                                          KRow krow = KRow{}, Cent cent = Cent{}) {
   using T = DTile<D>;
   constexpr int TB = T::TBYTES;            // K tile bytes == V^T tile bytes
   constexpr int PK = T::BLOCKS / NW;       // DMA instructions per wave per tile
@@ -259,11 +279,15 @@ __device__ __forceinline__ void vt_attend(int nt, EntRaw ent_raw, Prep prep, con
   vt_offsets(l32, hi, voff);
   dma_offsets<D, NW, false>(wave, lane, kdma);
   vt_dma_offsets<D, NW>(wave, lane, vdma);
+  // A centroid pass continues the softmax state (o, m_run, l_run) of the
+  // pass over the exact tiles before it; any other pass starts afresh.
+  if constexpr (!Cent::kOn) {
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
-  m_run = -INFINITY;
-  l_run = 0.f;
-  float mref_c = 0.f;   // m_run * c (0 while m_run is -inf)
+    for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
+    m_run = -INFINITY;
+    l_run = 0.f;
+  }
+  float mref_c = m_run == -INFINITY ? 0.f : m_run * c;   // m_run * c (0 while m_run is -inf)
 
   // Tile DMAs through a buffer resource based at the tile: rows past N fall
   // outside the resource's range and read as zero (their scores are masked).
@@ -275,6 +299,13 @@ __device__ __forceinline__ void vt_attend(int nt, EntRaw ent_raw, Prep prep, con
     else return krow(e);
   };
   auto dma_k = [&](int e, char *tile) {
+    if constexpr (Cent::kOn) {
+      if (e & kCentFlag) {
+        dma_tile_buf<D, NW>(reinterpret_cast<const char *>(cent.k) + (size_t)(e & kCentTileMask) * TB, TB, tile,
+                            wave, kdma);
+        return;
+      }
+    }
     if constexpr (kBlockRows) {
       const int kb = e & 0xFFFFFF;
       const int left = (N - kb * BK) * T::ROWB;
@@ -288,6 +319,13 @@ __device__ __forceinline__ void vt_attend(int nt, EntRaw ent_raw, Prep prep, con
     }
   };
   auto dma_v = [&](int e, char *tile) {
+    if constexpr (Cent::kOn) {
+      if (e & kCentFlag) {
+        dma_tile_buf<D, NW>(reinterpret_cast<const char *>(cent.vt) + (size_t)(e & kCentTileMask) * TB, TB, tile,
+                            wave, vdma);
+        return;
+      }
+    }
     const int kb = e & 0xFFFFFF;
     dma_tile_buf<D, NW>(reinterpret_cast<const char *>(Vth) + (size_t)kb * TB, TB, tile, wave, vdma);
   };
@@ -322,7 +360,7 @@ __device__ __forceinline__ void vt_attend(int nt, EntRaw ent_raw, Prep prep, con
     // below: issued back to back by every wave right after the barrier, they
     // queue up in the load unit and hold the waves at issue.
     const int kb_v = e2 & 0xFFFFFF;
-    __amdgpu_buffer_rsrc_t rk;
+    __amdgpu_buffer_rsrc_t rk, rv;
     if constexpr (kBlockRows) {
       const int kb_k = e3 & 0xFFFFFF;
       const int kleft = (N - kb_k * BK) * T::ROWB;
@@ -332,7 +370,13 @@ __device__ __forceinline__ void vt_attend(int nt, EntRaw ent_raw, Prep prep, con
       const int kleft = (N - row_k) * T::ROWB;
       rk = tile_rsrc(reinterpret_cast<const char *>(Kh) + (size_t)row_k * T::ROWB, kleft < TB ? kleft : TB);
     }
-    const __amdgpu_buffer_rsrc_t rv = tile_rsrc(reinterpret_cast<const char *>(Vth) + (size_t)kb_v * TB, TB);
+    rv = tile_rsrc(reinterpret_cast<const char *>(Vth) + (size_t)kb_v * TB, TB);
+    if constexpr (Cent::kOn) {
+      if (e3 & kCentFlag)
+        rk = tile_rsrc(reinterpret_cast<const char *>(cent.k) + (size_t)(e3 & kCentTileMask) * TB, TB);
+      if (e2 & kCentFlag)
+        rv = tile_rsrc(reinterpret_cast<const char *>(cent.vt) + (size_t)(e2 & kCentTileMask) * TB, TB);
+    }
     auto dma_slot = [&](int ks) {
 #pragma unroll
       for (int i = 0; i < 2 * PK; ++i) {
@@ -449,7 +493,10 @@ __device__ __forceinline__ void vt_attend(int nt, EntRaw ent_raw, Prep prep, con
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) o[db] = mfma32(va[j & 1][db], pj, o[db]);
     }
-    l_run += rs;
+    if constexpr (Cent::kOn)   // a centroid stands for 64 keys: its probability counts 64 times (exact)
+      l_run += (e0 & kCentFlag) ? 64.f * rs : rs;
+    else
+      l_run += rs;
 
     // (C) K(it+2) and V(it+1), issued one step ago, have landed once at most
     // this step's 2*PK DMAs are outstanding; then every wave's share is in

@@ -90,6 +90,18 @@ hipError_t launch_layout_vt(const Dims &dm, const void *V, void *Vt, const int32
 inline int vt_frame_tiles(const Dims &dm) {
   return dm.F * ((dm.S + 63) / 64) + (dm.T + 63) / 64;
 }
+// SVG-EAR: block centroids, routing, and the attention with compensation.
+int ear_centroid_tiles(const Dims &dm);
+int ear_route_qpw(const Dims &dm);
+int attn_ear_max_kv_blocks();
+hipError_t launch_ear_stats(const Dims &dm, const void *K, const void *Vt, void *Kc, void *Vct, double *kbar,
+                            double *rad, hipStream_t st);
+hipError_t launch_ear_route(const Dims &dm, const void *Q, const int32_t *labels, const double *kbar,
+                            const double *rad, const uint8_t *mask, int bq, int route_k, double tau, uint8_t *exact,
+                            hipStream_t st);
+hipError_t launch_attn_vt_ear(const Dims &dm, const void *Q, const void *K, const void *Vt, const void *Kc,
+                              const void *Vct, void *O, const int32_t *row_ptr, const int32_t *kv_idx, int bq,
+                              float scale, const int32_t *labels, hipStream_t st);
 // FP8 (E4M3) quantization and attention (d = 128 for the attention).
 hipError_t launch_quant_rows_fp8(const Dims &dm, const void *X, void *X8, float *scale, hipStream_t st);
 hipError_t launch_layout_fp8(const Dims &dm, const void *X, void *X8, float *scale, const int32_t *labels,

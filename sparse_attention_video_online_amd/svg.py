@@ -65,6 +65,10 @@ SIGNATURES = {
     "svg_block_sparse_attn_csr_vt": [_DIMS, _I, _P, _P, _P, _P, _P, _I, _I, _F, _P, _P, _Z, _P],
     "svg_block_sparse_attn_csr_vt_layout": [_DIMS, _I, _P, _P, _P, _P, _P, _P, _I, _I, _F, _P, _P, _Z, _P],
     "svg_dense_attn_vt": [_DIMS, _I, _P, _P, _P, _I, _I, _F, _P, _P],
+    "svg_ear_centroid_elems": [_DIMS],
+    "svg_ear_block_stats": [_DIMS, _I, _P, _P, _P, _P, _P, _P, _P],
+    "svg_ear_route": [_DIMS, _I, _P, _P, _P, _P, _P, _I, _I, _I, _F, _P, _P],
+    "svg_block_sparse_attn_ear_vt_layout": [_DIMS, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _F, _P, _P],
     "svg_quantize_fp8_rows": [_DIMS, _I, _P, _P, _P, _P],
     "svg_layout_permute_fp8": [_DIMS, _I, _P, _P, _P, _P, _P],
     "svg_block_sparse_attn_fp8_vt_layout": [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _F, _P, _P],
@@ -77,7 +81,7 @@ SIGNATURES = {
     "svg_select_pairs": [_DIMS, _P, _P, _P, _I, _I, _D, _F, _P, _P, _P],
     "svg_varlen_attn": [_DIMS, _I, _P, _P, _P, _P, _P, _I, _I, _P, _P, _P, _F, _P, _P, _Z, _P],
 }
-_RESTYPES = {"svg_workspace_bytes": _Z, "svg2_workspace_bytes": _Z, "svg_vt_elems": _Z,
+_RESTYPES = {"svg_workspace_bytes": _Z, "svg2_workspace_bytes": _Z, "svg_vt_elems": _Z, "svg_ear_centroid_elems": _Z,
              "svg_last_error": ctypes.c_char_p, "svg_version": ctypes.c_char_p}
 
 
@@ -412,6 +416,78 @@ def svg_dense_attn_vt(q, k, vt, F, S, T, bq, bk, scale=-1.0, out=None):
     out = _out_like(out, q)
     _check(_lib.svg_dense_attn_vt(ctypes.byref(dm), dt, _ptr(q), _ptr(k), _ptr(vt), bq, bk, scale, _ptr(out),
                                   _stream()), "svg_dense_attn_vt")
+    return out
+
+
+# ----------------------------------------------------------------------------
+# SVG-EAR
+
+def svg_ear_centroid_elems(H, N, d):
+    dm = svg_dims(1, N, 0, H, d)
+    return int(_lib.svg_ear_centroid_elems(ctypes.byref(dm)))
+
+
+def svg_ear_block_stats(k, vt, F, S, T, kc=None, vct=None, kbar=None, radius=None):
+    """Centroid tables (bf16 centroid keys, key-tiled bf16 value sums) and the
+    double centroids (dim-major, [H][d][nKB]) and radii of the kv-blocks of
+    K / Vt (executing layout)."""
+    dm = _video_dims(k, F, S, T, "K")
+    H, N, d = k.shape
+    dt = _dtype(k)
+    _need(k, "K", torch.bfloat16, k.numel())
+    _need(vt, "Vt", torch.bfloat16, svg_vt_elems(H, N, d))
+    ne = svg_ear_centroid_elems(H, N, d)
+    nkb = -(-N // 64)
+    dev = k.device
+    kc = torch.empty(ne, dtype=torch.bfloat16, device=dev) if kc is None else kc
+    vct = torch.empty(ne, dtype=torch.bfloat16, device=dev) if vct is None else vct
+    kbar = torch.empty(H, d, nkb, dtype=torch.float64, device=dev) if kbar is None else kbar
+    radius = torch.empty(H, nkb, dtype=torch.float64, device=dev) if radius is None else radius
+    _need(kc, "Kc", torch.bfloat16, ne)
+    _need(vct, "Vct", torch.bfloat16, ne)
+    _need(kbar, "kbar", torch.float64, H * nkb * d)
+    _need(radius, "radius", torch.float64, H * nkb)
+    _check(_lib.svg_ear_block_stats(ctypes.byref(dm), dt, _ptr(k), _ptr(vt), _ptr(kc), _ptr(vct), _ptr(kbar),
+                                    _ptr(radius), _stream()), "svg_ear_block_stats")
+    return kc, vct, kbar, radius
+
+
+def svg_ear_route(q, labels, kbar, radius, block_mask, F, S, T, bq, bk, route_k, scale=-1.0, out=None):
+    """The exact sets (uint8 [H][nQB][nKB]) from the block mask, the ragged
+    last block and the route_k routed blocks per q-block."""
+    dm = _video_dims(q, F, S, T, "Q")
+    H, N, d = q.shape
+    dt = _dtype(q)
+    _need(q, "Q", torch.bfloat16, q.numel())
+    _labels(labels, H)
+    nqb, nkb = -(-N // bq), -(-N // 64)
+    _need(kbar, "kbar", torch.float64, H * nkb * d)
+    _need(radius, "radius", torch.float64, H * nkb)
+    _need(block_mask, "block_mask", torch.uint8, H * nqb * nkb)
+    out = torch.empty(H, nqb, nkb, dtype=torch.uint8, device=q.device) if out is None else out
+    _need(out, "exact_mask", torch.uint8, H * nqb * nkb)
+    _check(_lib.svg_ear_route(ctypes.byref(dm), dt, _ptr(q), _ptr(labels), _ptr(kbar), _ptr(radius),
+                              _ptr(block_mask), bq, bk, int(route_k), scale, _ptr(out), _stream()), "svg_ear_route")
+    return out
+
+
+def svg_block_sparse_attn_ear_vt_layout(q, k, vt, kc, vct, row_ptr, kv_idx, labels, F, S, T, bq, bk, scale=-1.0,
+                                        out=None):
+    """Attention over the exact lists plus the centroid compensation of every
+    other block; Q and O in the original order, K / Vt / lists / tables in the
+    executing layout."""
+    dm, dt = _qk_vt(q, k, vt, F, S, T)
+    H, N, d = q.shape
+    ne = svg_ear_centroid_elems(H, N, d)
+    _need(kc, "Kc", torch.bfloat16, ne)
+    _need(vct, "Vct", torch.bfloat16, ne)
+    _lists(row_ptr, kv_idx, H, N, bq)
+    _labels(labels, H)
+    out = _out_like(out, q)
+    _check(_lib.svg_block_sparse_attn_ear_vt_layout(ctypes.byref(dm), dt, _ptr(q), _ptr(k), _ptr(vt), _ptr(kc),
+                                                    _ptr(vct), _ptr(row_ptr), _ptr(kv_idx), _ptr(labels), bq, bk,
+                                                    scale, _ptr(out), _stream()),
+           "svg_block_sparse_attn_ear_vt_layout")
     return out
 
 
