@@ -174,7 +174,7 @@ kernels run at a few microseconds each and are bound by launch and per-kernel la
 
 COUNTER_KERNELS = ["layout_kernel", "vt_kernel", "profile_full_vt", "profile_temporal_vt", "profile_combine",
                    "block_mask_kernel", "fill_kernel", "attn_fwd_vt", "km_assign_bf3", "km_update", "sort_place",
-                   "sort_count", "permute_rows_kernel", "select_rows", "varlen_attn", "km_prep3"]
+                   "sort_count", "permute_rows_kernel", "select_rows", "varlen_attn", "varlen_vt", "km_prep3"]
 
 
 def record_counters(root):
@@ -239,6 +239,7 @@ def record_counters(root):
         ("svg2", "km_update<unsigned short>"): EC + 2 * C.H * C.N * 4,
         ("svg2", "sort_place"): 2 * C.H * C.N * 4,
         ("svg2", "permute_rows_kernel"): 2 * EC + C.H * C.N * 4,
+        ("svg2", "vt_kernel<64> (V gather)"): EC + C.H * -(-C.N // 64) * 64 * C.d * 2 + C.H * C.N * 4,
     }
 
     fetch_scale = write_scale = None
@@ -258,7 +259,10 @@ def record_counters(root):
             if k is None or d not in fnames or short(fnames[d]) != k:
                 continue
             if k.startswith("vt_kernel"):
-                k += " (attention V^T)" if grids[d] == attn_vt_grid else " (profiler V^T)"
+                if prog == "svg2":
+                    k += " (V gather)"
+                else:
+                    k += " (attention V^T)" if grids[d] == attn_vt_grid else " (profiler V^T)"
             groups[k].append((d, dur))
         for k, ds in sorted(groups.items()):
             t = sum(dur for _, dur in ds) / len(ds)
@@ -368,6 +372,7 @@ def bench_svg2(args, steps=None, warmup=None, cpu=False):
     pq, pk, oq, ok = i32(H, N), i32(H, N), i32(H, w.kq + 1), i32(H, w.kk + 1)
     ptr, idx = i32(H, w.kq + 1), i32(H, w.kq * w.kk)
     qp, kp, vp, o = (torch.empty_like(q) for _ in range(4))
+    vt = torch.empty(svg.svg_vt_elems(H, N, d), dtype=q.dtype, device=dev)
     dm = svg.svg_dims(1, N, 0, H, d)
     ws_kq = torch.empty(svg.workspace_bytes(svg.SVG2_OP_KMEANS, dm, w.kq, svg2=True), dtype=torch.uint8, device=dev)
     ws_kk = torch.empty(svg.workspace_bytes(svg.SVG2_OP_KMEANS, dm, w.kk, svg2=True), dtype=torch.uint8, device=dev)
@@ -387,21 +392,22 @@ def bench_svg2(args, steps=None, warmup=None, cpu=False):
     side = torch.cuda.Stream()
 
     def step_overlapped():
+        cur = torch.cuda.current_stream()      # the capture stream while a graph is recorded
         fork, join = torch.cuda.Event(), torch.cuda.Event()
-        fork.record(stream)
+        fork.record(cur)
         side.wait_event(fork)
         with torch.cuda.stream(side):
             svg.svg_kmeans(k, w.kk, w.iters, ik, assign=ak, centroids=ck, sizes=sk, ws=ws_kk)
             svg.svg_cluster_permute(ak, w.kk, d, perm=pk, offs=ok, ws=ws_cp2)
             svg.svg_permute_rows(k, pk, out=kp)
-            svg.svg_permute_rows(v, pk, out=vp)
+            svg.svg_permute_rows_vt(v, pk, out=vt)
             join.record(side)
         svg.svg_kmeans(q, w.kq, w.iters, iq, assign=aq, centroids=cq, sizes=sq, ws=ws_kq)
         svg.svg_cluster_permute(aq, w.kq, d, perm=pq, offs=oq, ws=ws_cp)
         svg.svg_permute_rows(q, pq, out=qp)
-        stream.wait_event(join)
+        cur.wait_event(join)
         svg.svg_select_pairs(cq, ck, sk, w.top_p, pair_ptr=ptr, pair_idx=idx)
-        svg.svg_varlen_attn(qp, kp, vp, oq, ok, ptr, idx, q_perm=pq, out=o, ws=ws_vl)
+        svg.svg_varlen_attn_vt(qp, kp, vt, oq, ok, ptr, idx, q_perm=pq, out=o)
 
     def step(ev=None):
         def mark(j):
@@ -417,11 +423,11 @@ def bench_svg2(args, steps=None, warmup=None, cpu=False):
         mark(3)
         svg.svg_permute_rows(q, pq, out=qp)
         svg.svg_permute_rows(k, pk, out=kp)
-        svg.svg_permute_rows(v, pk, out=vp)
+        svg.svg_permute_rows_vt(v, pk, out=vt)
         mark(4)
         svg.svg_select_pairs(cq, ck, sk, w.top_p, pair_ptr=ptr, pair_idx=idx)
         mark(5)
-        svg.svg_varlen_attn(qp, kp, vp, oq, ok, ptr, idx, q_perm=pq, out=o, ws=ws_vl)
+        svg.svg_varlen_attn_vt(qp, kp, vt, oq, ok, ptr, idx, q_perm=pq, out=o)
         mark(6)
 
     steps = args.steps if steps is None else steps
@@ -435,15 +441,73 @@ def bench_svg2(args, steps=None, warmup=None, cpu=False):
         step_overlapped()
     e1.record(stream)
     torch.cuda.synchronize()
-    ms_per_step = e0.elapsed_time(e1) / steps
+    eager_ms = e0.elapsed_time(e1) / steps
+    o_eager, idx_eager = o.clone(), idx.clone()
+
+    def pairs_of(ix):
+        # the defined part of pair_idx: each head's first ptr[h][kq] entries
+        n = ptr[:, -1].cpu().tolist()
+        return torch.cat([ix[h, :n[h]] for h in range(H)])
+
+    def same(a, b, ia, ib):
+        return torch.equal(a, b) and torch.equal(pairs_of(ia), pairs_of(ib))
+
+    # The same two-stream step captured once in a HIP graph (its ~70
+    # dependent launches, most of them a few microseconds long, then go to
+    # the GPU in one submission); the timed steps replay it.  Every replay
+    # must give the eager step's output bit for bit.
+    graph_note = "the timed step replays a HIP graph of the two-stream step (equal to the eager step bit for bit)"
+    try:
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            step_overlapped()          # warm-up on the capture stream
+            torch.cuda.synchronize()
+            with torch.cuda.graph(graph, stream=cap):
+                step_overlapped()
+        torch.cuda.synchronize()
+        for _ in range(warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        if not same(o, o_eager, idx, idx_eager):
+            raise SystemExit("svg2: graph replay and eager step disagree")
+        e0.record(stream)
+        for _ in range(steps):
+            graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_per_step = e0.elapsed_time(e1) / steps
+        if not same(o, o_eager, idx, idx_eager):
+            raise SystemExit("svg2: graph replay and eager step disagree")
+    except RuntimeError as err:           # capture refused: report the eager step
+        torch.cuda.synchronize()
+        ms_per_step = eager_ms
+        graph_note = f"eager two-stream step (graph capture failed: {err})"
+        print(f"[bench] svg2: {graph_note}", file=sys.stderr, flush=True)
     o_overlapped, idx_overlapped = o.clone(), idx.clone()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(7)]
     step(ev)
     torch.cuda.synchronize()
     # the two-stream step computes exactly what the one-stream step does
-    if not (torch.equal(o_overlapped, o) and torch.equal(idx_overlapped, idx)):
+    if not same(o_overlapped, o, idx_overlapped, idx):
         raise SystemExit("svg2: two-stream and one-stream steps disagree")
     stage_ms = {n: ev[j].elapsed_time(ev[j + 1]) for j, n in enumerate(names)}
+    # the row-major varlen kernel on the same lists, for comparison (same
+    # result up to bf16 rounding of the accumulation order)
+    svg.svg_permute_rows(v, pk, out=vp)
+    o_rm = torch.empty_like(o)
+    for _ in range(3):
+        svg.svg_varlen_attn(qp, kp, vp, oq, ok, ptr, idx, q_perm=pq, out=o_rm, ws=ws_vl)
+    e0.record(stream)
+    for _ in range(10):
+        svg.svg_varlen_attn(qp, kp, vp, oq, ok, ptr, idx, q_perm=pq, out=o_rm, ws=ws_vl)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    rowmajor_ms = e0.elapsed_time(e1) / 10
+    rm_diff = (o_rm.float() - o.float()).abs().max().item()
+    if not rm_diff < 2e-2:
+        raise SystemExit(f"svg2: the two varlen kernels disagree (max abs {rm_diff})")
 
     # work: attention pairs from the selected clusters; bytes of the copies
     optr, oidx = ptr.cpu().numpy(), idx.cpu().numpy()
@@ -465,7 +529,11 @@ def bench_svg2(args, steps=None, warmup=None, cpu=False):
                    "top_p": w.top_p, "pair_density": round(pairs / (H * float(N) * N), 4)},
         "stage_ms": {kk_: round(vv, 4) for kk_, vv in stage_ms.items()},
         "one_stream_ms": round(sum(stage_ms.values()), 4),
+        "eager_two_stream_ms": round(eager_ms, 4),
+        "graph": graph_note,
         "varlen_tflops": round(attn_flops / (stage_ms["varlen_attn"] * 1e-3) / 1e12, 2),
+        "varlen_rowmajor_kernel_ms": round(rowmajor_ms, 4),
+        "varlen_kernels_max_abs_diff": rm_diff,
         "gather_gbs": round(gather_bytes / (stage_ms["gather_qkv"] * 1e-3) / 1e9, 1),
         "kmeans_vector_tflops": round(km_flops / ((stage_ms["kmeans_q"] + stage_ms["kmeans_k"]) * 1e-3) / 1e12, 2),
     }
@@ -838,8 +906,8 @@ def main():
         result["cogvideox_shape"]["tile_density"] = cog["config"]["tile_density"]
         torch.cuda.empty_cache()
         s2 = bench_svg2(args, steps=20, warmup=3)
-        result["svg2"] = {k_: s2[k_] for k_ in ("ms_per_step", "stage_ms", "one_stream_ms", "varlen_tflops",
-                                                 "gather_gbs")}
+        result["svg2"] = {k_: s2[k_] for k_ in ("ms_per_step", "stage_ms", "one_stream_ms", "eager_two_stream_ms",
+                                                 "varlen_tflops", "gather_gbs")}
         result["svg2"]["pair_density"] = s2["config"]["pair_density"]
     if not args.no_cpu_baseline:
         lab = [int(c) for c in result["config"]["labels"]]

@@ -131,6 +131,29 @@ svg_status svg_varlen_attn(const svg_dims *dims, svg_dtype dtype,
                            const int32_t *q_perm, float softmax_scale, void *O,
                            void *ws, size_t ws_bytes, void *stream);
 
+/* Rows of V gathered into the key-tiled V^T layout that svg_varlen_attn_vt
+ * reads (the value side of the cluster permutation, in one pass):
+ *   Vt[h][kb][c][j] = V[h][perm[h][64*kb + j]][c],  zero where 64*kb + j >= N.
+ * V: bf16 [H][N][d]; perm: int32 [H][N], each entry in [0, N) (not
+ * checked: an index out of range reads out of bounds); Vt: bf16
+ * [H][ceil(N/64)][d][64] (svg_vt_elems elements).  V and Vt must not
+ * overlap. */
+svg_status svg_permute_rows_vt(const svg_dims *dims, svg_dtype dtype, const void *V,
+                               const int32_t *perm, void *Vt, void *stream);
+
+/* svg_varlen_attn on the key-tiled V^T of Vp (as svg_permute_rows_vt writes
+ * it): the same result, token-exact.  One work-group takes 128 rows of one
+ * query cluster and walks the 64-key windows of Kp / Vt that its selected
+ * key ranges touch; each window carries a 64-bit mask of its selected keys
+ * and the others score -inf.  d = 64 or 128, N <= 131072 (2048 windows a
+ * head); q_offs, k_offs, pair_ptr and pair_idx as for svg_varlen_attn (in
+ * range by contract).  No workspace. */
+svg_status svg_varlen_attn_vt(const svg_dims *dims, svg_dtype dtype,
+                              const void *Qp, const void *Kp, const void *Vt,
+                              const int32_t *q_offs, const int32_t *k_offs, int32_t kq, int32_t kk,
+                              const int32_t *pair_ptr, const int32_t *pair_idx,
+                              const int32_t *q_perm, float softmax_scale, void *O, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -721,4 +721,41 @@ svg_status svg_varlen_attn(const svg_dims *dims, svg_dtype dtype, const void *Qp
                     "svg_varlen_attn");
 }
 
+svg_status svg_permute_rows_vt(const svg_dims *dims, svg_dtype dtype, const void *V, const int32_t *perm,
+                               void *Vt, void *stream) {
+  Dims dm{};
+  svg_status s;
+  if ((s = check_dims(dims, &dm, false)) != SVG_OK) return s;
+  if ((s = check_dtype(dtype)) != SVG_OK) return s;
+  if (dtype != SVG_BF16) return fail(SVG_ERR_UNSUPPORTED, "permute_rows_vt: bf16 only");
+  if (!V || !perm || !Vt) return fail(SVG_ERR_NULL, "permute_rows_vt: NULL pointer");
+  if (overlaps2(V, (size_t)dm.H * dm.N * dm.d * 2, Vt, vt_bytes(dm)))
+    return fail(SVG_ERR_RANGE, "permute_rows_vt: V and Vt overlap");
+  return hip_status(svgk::launch_layout_vt(dm, V, Vt, perm, (hipStream_t)stream, svgk::kVtGather),
+                    "svg_permute_rows_vt");
+}
+
+svg_status svg_varlen_attn_vt(const svg_dims *dims, svg_dtype dtype, const void *Qp, const void *Kp,
+                              const void *Vt, const int32_t *q_offs, const int32_t *k_offs, int32_t kq,
+                              int32_t kk, const int32_t *pair_ptr, const int32_t *pair_idx,
+                              const int32_t *q_perm, float softmax_scale, void *O, void *stream) {
+  Dims dm{};
+  svg_status s;
+  if ((s = check_dims(dims, &dm, false)) != SVG_OK) return s;
+  if ((s = check_dtype(dtype)) != SVG_OK) return s;
+  if (!Qp || !Kp || !Vt || !q_offs || !k_offs || !pair_ptr || !pair_idx || !O)
+    return fail(SVG_ERR_NULL, "varlen_attn_vt: NULL pointer");
+  if (dtype != SVG_BF16) return fail(SVG_ERR_UNSUPPORTED, "varlen_attn_vt: bf16 inputs only");
+  if (kq < 1 || kk < 1 || kk > 256) return fail(SVG_ERR_RANGE, "varlen_attn_vt: kq=%d kk=%d (kk <= 256)", kq, kk);
+  if (!svgk::varlen_vt_covers(dm))
+    return fail(SVG_ERR_UNSUPPORTED, "varlen_attn_vt: d=%d N=%d (d = 64 or 128, N <= %d)", dm.d, dm.N,
+                64 * svgk::varlen_vt_max_windows());
+  const size_t bytes = (size_t)dm.H * dm.N * dm.d * 2;
+  if (overlaps(O, Qp, bytes) || overlaps(O, Kp, bytes) || overlaps2(O, bytes, Vt, vt_bytes(dm)))
+    return fail(SVG_ERR_RANGE, "varlen_attn_vt: O overlaps an input");
+  return hip_status(svgk::launch_varlen_vt(dm, Qp, Kp, Vt, q_offs, k_offs, kq, kk, pair_ptr, pair_idx, q_perm,
+                                           resolve_scale(softmax_scale, dm.d), O, (hipStream_t)stream),
+                    "svg_varlen_attn_vt");
+}
+
 }  // extern "C"

@@ -216,19 +216,15 @@ void attn_fwd_vt(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K, con
     const bool own = (e & own_bit) != 0;
     if (own) {
       // the q-block's exact flags over the tile's 64 centroids and the number
-      // that exist are wave-uniform: each key's decision is a scalar pair
-      // (lane half 0 / 1) picked per lane
+      // that exist are wave-uniform; each lane shifts them to its own keys
+      // (k0 + 8 hi, k0 + 32 + 8 hi) and drops flagged or missing centroids
       const int t = e & kCentTileMask;
       const uint32_t w0 = __builtin_amdgcn_readfirstlane(bits[gw * kWords + 2 * t]);
       const uint32_t w1 = __builtin_amdgcn_readfirstlane(bits[gw * kWords + 2 * t + 1]);
-      const int nv = nkb - 64 * t;
-      auto drop = [&](uint32_t w, int key) { return ((w >> (key & 31)) & 1u) != 0 || key >= nv; };
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int k0 = 16 * (r >> 3) + (r & 7);    // acc_key_pi(0, r, hi) - 8 hi
-        if (hi ? drop(w0, k0 + 8) : drop(w0, k0)) s0[r] = -INFINITY;
-        if (hi ? drop(w1, k0 + 40) : drop(w1, k0 + 32)) s1[r] = -INFINITY;
-      }
+      const int nv = nkb - 64 * t;               // centroids that exist in the tile
+      auto below = [](int n) -> uint32_t { return n >= 32 ? ~0u : n <= 0 ? 0u : (1u << n) - 1u; };
+      const int sh = 8 * hi;
+      drop_scores(s0, s1, (w0 >> sh) | ~below(nv - sh), (w1 >> sh) | ~below(nv - 32 - sh));
     }
     return own;
   };

@@ -26,6 +26,21 @@ __device__ __forceinline__ int acc_key_pi(int b, int r, int hi) {
   return 32 * b + 16 * (r >> 3) + 8 * hi + (r & 7);
 }
 
+// Scores of keys named by per-lane drop words become -inf.  Bit k0 of d0
+// (d1) stands for accumulator value r of s0 (s1), k0 = 16 (r >> 3) + (r & 7),
+// i.e. key acc_key_pi(b, r, hi) - 32 b - 8 hi: callers shift their
+// wave-uniform key words right by 8 hi first.  Straight-line VALU (a bit test
+// and a select per score); written as a lane-varying shift of uniform words
+// so that no lane-divergent branch arises.
+__device__ __forceinline__ void drop_scores(f32x16 &s0, f32x16 &s1, uint32_t d0, uint32_t d1) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const uint32_t bit = 1u << (16 * (r >> 3) + (r & 7));
+    s0[r] = (d0 & bit) ? -INFINITY : s0[r];
+    s1[r] = (d1 & bit) ? -INFINITY : s1[r];
+  }
+}
+
 // Maximum of the lane's 32 scores as a tree of three-input maxima (depth 4).
 __device__ __forceinline__ float lane_max_tree(const f32x16 &s0, const f32x16 &s1) {
   float a[11];

@@ -60,7 +60,9 @@ void permute_rows_kernel(const u32x4 *__restrict__ X, const int32_t *__restrict_
 // Vt tile (h, kb): the 64 executing-layout rows kb*64.. of head h, transposed
 // to [d][64 keys], zero past N.  Mode kVtLabels: executing row r of a
 // permuted head reads frame-major row f*S + p (r = p*F + f, video rows
-// only).  Mode kVtIdentity: every head keeps its row order.  Mode kVtFrames:
+// only).  Mode kVtIdentity: every head keeps its row order.  Mode kVtGather:
+// row r of head h is row labels[h*N + r] of that head (labels is then a
+// per-head gather index, in range by contract).  Mode kVtFrames:
 // every head keeps its token order and each frame (then the text) starts a
 // new tile: tile kb < F*nbf (nbf = ceil(S/64) tiles a frame) holds rows
 // f*S + 64j .. of frame f = kb / nbf, j = kb % nbf, zero past the frame's
@@ -77,6 +79,7 @@ void vt_kernel(const u32x4 *__restrict__ X, u32x4 *__restrict__ Y, const int32_t
   const int kb = blockIdx.x, h = blockIdx.y;
   const bool frames = mode == kVtFrames;
   const bool perm = mode == kVtLabels && (labels == nullptr || labels[h] == 1);
+  const int32_t *gather = mode == kVtGather ? labels + (size_t)h * N : nullptr;
   const int nbf = (S + 63) / 64;
   const u32x4 *Xh = X + (size_t)h * N * CPR;
   for (int u = threadIdx.x; u < 64 * CPR; u += 256) {
@@ -100,6 +103,7 @@ void vt_kernel(const u32x4 *__restrict__ X, u32x4 *__restrict__ Y, const int32_t
         const int p = r / F, f = r - p * F;
         src = f * S + p;
       }
+      if (gather) src = gather[r];
       v = Xh[(size_t)src * CPR + ch];
     }
     *reinterpret_cast<u32x4 *>(t + row * STR + ch * 8) = v;

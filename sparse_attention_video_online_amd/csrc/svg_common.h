@@ -83,8 +83,10 @@ int attn_vt_max_kv_blocks();
 //   kVtFrames:   every head's token order, each frame and the text starting
 //                a new 64-key tile (vt_frame_tiles(dm) tiles a head, zero
 //                past each end);
-//   kVtIdentity: every head's rows as given.
-enum { kVtLabels = 0, kVtFrames = 1, kVtIdentity = 2 };
+//   kVtIdentity: every head's rows as given;
+//   kVtGather:   row r of head h is V row labels[h*N + r] of that head
+//                (labels: int32 [H][N] gather index).
+enum { kVtLabels = 0, kVtFrames = 1, kVtIdentity = 2, kVtGather = 3 };
 hipError_t launch_layout_vt(const Dims &dm, const void *V, void *Vt, const int32_t *labels, hipStream_t st,
                             int mode = kVtLabels);
 inline int vt_frame_tiles(const Dims &dm) {
@@ -137,5 +139,12 @@ hipError_t launch_varlen(const Dims &dm, bool bf16, const void *Qp, const void *
                          const int32_t *q_offs, const int32_t *k_offs, int kq, int kk,
                          const int32_t *pair_ptr, const int32_t *pair_idx, const int32_t *q_perm,
                          float scale, void *O, void *ws, hipStream_t st);
+// The same attention on the key-tiled V^T of Vp (d = 64 or 128, at most
+// varlen_vt_max_windows() 64-key windows a head); no workspace.
+int varlen_vt_max_windows();
+bool varlen_vt_covers(const Dims &dm);
+hipError_t launch_varlen_vt(const Dims &dm, const void *Qp, const void *Kp, const void *Vt, const int32_t *q_offs,
+                            const int32_t *k_offs, int kq, int kk, const int32_t *pair_ptr, const int32_t *pair_idx,
+                            const int32_t *q_perm, float scale, void *O, hipStream_t st);
 
 }  // namespace svgk

@@ -80,6 +80,8 @@ SIGNATURES = {
     "svg_permute_rows": [_DIMS, _I, _P, _P, _P, _I, _P],
     "svg_select_pairs": [_DIMS, _P, _P, _P, _I, _I, _D, _F, _P, _P, _P],
     "svg_varlen_attn": [_DIMS, _I, _P, _P, _P, _P, _P, _I, _I, _P, _P, _P, _F, _P, _P, _Z, _P],
+    "svg_permute_rows_vt": [_DIMS, _I, _P, _P, _P, _P],
+    "svg_varlen_attn_vt": [_DIMS, _I, _P, _P, _P, _P, _P, _I, _I, _P, _P, _P, _F, _P, _P],
 }
 _RESTYPES = {"svg_workspace_bytes": _Z, "svg2_workspace_bytes": _Z, "svg_vt_elems": _Z, "svg_ear_centroid_elems": _Z,
              "svg_last_error": ctypes.c_char_p, "svg_version": ctypes.c_char_p}
@@ -640,12 +642,8 @@ def svg_select_pairs(cq, ck, size_k, top_p, scale=-1.0, pair_ptr=None, pair_idx=
     return pair_ptr, pair_idx
 
 
-def svg_varlen_attn(qp, kp, vp, q_offs, k_offs, pair_ptr, pair_idx, q_perm=None, scale=-1.0, out=None, ws=None):
-    dm = _flat_dims(qp, "Qp")
-    H, N, d = qp.shape
-    dt = _dtype(qp)
-    for t, n in ((qp, "Qp"), (kp, "Kp"), (vp, "Vp")):
-        _need(t, n, qp.dtype, H * N * d)
+def _varlen_lists(qp, q_offs, k_offs, pair_ptr, pair_idx, q_perm):
+    H, N, _ = qp.shape
     if not isinstance(q_offs, torch.Tensor) or q_offs.dim() != 2 or not isinstance(k_offs, torch.Tensor) \
             or k_offs.dim() != 2:
         raise ValueError("q_offs and k_offs must be int32 [H][k+1] tensors")
@@ -655,9 +653,50 @@ def svg_varlen_attn(qp, kp, vp, q_offs, k_offs, pair_ptr, pair_idx, q_perm=None,
     _need(pair_ptr, "pair_ptr", torch.int32, H * (kq + 1))
     _need(pair_idx, "pair_idx", torch.int32, H * kq * kk)
     _opt(q_perm, "q_perm", dtype=torch.int32, numel=H * N)
+    return kq, kk
+
+
+def svg_varlen_attn(qp, kp, vp, q_offs, k_offs, pair_ptr, pair_idx, q_perm=None, scale=-1.0, out=None, ws=None):
+    dm = _flat_dims(qp, "Qp")
+    H, N, d = qp.shape
+    dt = _dtype(qp)
+    for t, n in ((qp, "Qp"), (kp, "Kp"), (vp, "Vp")):
+        _need(t, n, qp.dtype, H * N * d)
+    kq, kk = _varlen_lists(qp, q_offs, k_offs, pair_ptr, pair_idx, q_perm)
     out = _out_like(out, qp)
     ws = _ws(workspace_bytes(SVG2_OP_VARLEN, dm, kq, kk, svg2=True), qp.device, ws)
     _check(_lib.svg_varlen_attn(ctypes.byref(dm), dt, _ptr(qp), _ptr(kp), _ptr(vp), _ptr(q_offs),
                                 _ptr(k_offs), kq, kk, _ptr(pair_ptr), _ptr(pair_idx), _ptr(q_perm), scale,
                                 _ptr(out), _ptr(ws), _bytes(ws), _stream()), "svg_varlen_attn")
+    return out
+
+
+def svg_permute_rows_vt(v, perm, out=None):
+    """Key-tiled V^T ([H][nKB][d][64]) of the rows of v gathered by perm
+    (row r of head h is v[h][perm[h][r]])."""
+    dm = _flat_dims(v, "V")
+    H, N, d = v.shape
+    dt = _dtype(v)
+    _need(v, "V", v.dtype, v.numel())
+    _need(perm, "perm", torch.int32, H * N)
+    out = torch.empty(H, -(-N // 64), d, 64, dtype=v.dtype, device=v.device) if out is None else out
+    _need(out, "Vt", v.dtype, svg_vt_elems(H, N, d))
+    _check(_lib.svg_permute_rows_vt(ctypes.byref(dm), dt, _ptr(v), _ptr(perm), _ptr(out), _stream()),
+           "svg_permute_rows_vt")
+    return out
+
+
+def svg_varlen_attn_vt(qp, kp, vt, q_offs, k_offs, pair_ptr, pair_idx, q_perm=None, scale=-1.0, out=None):
+    """svg_varlen_attn with V given as the key-tiled V^T of Vp."""
+    dm = _flat_dims(qp, "Qp")
+    H, N, d = qp.shape
+    dt = _dtype(qp)
+    for t, n in ((qp, "Qp"), (kp, "Kp")):
+        _need(t, n, qp.dtype, H * N * d)
+    _need(vt, "Vt", qp.dtype, svg_vt_elems(H, N, d))
+    kq, kk = _varlen_lists(qp, q_offs, k_offs, pair_ptr, pair_idx, q_perm)
+    out = _out_like(out, qp)
+    _check(_lib.svg_varlen_attn_vt(ctypes.byref(dm), dt, _ptr(qp), _ptr(kp), _ptr(vt), _ptr(q_offs),
+                                   _ptr(k_offs), kq, kk, _ptr(pair_ptr), _ptr(pair_idx), _ptr(q_perm), scale,
+                                   _ptr(out), _stream()), "svg_varlen_attn_vt")
     return out

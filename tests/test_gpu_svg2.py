@@ -2,8 +2,10 @@
 
 Bit-exact: k-means assignments and sizes, centroids (member sums of bf16
 values are exact in float64 on both sides), cluster permutations and offsets,
-top-p pair lists.  Toleranced: varlen attention outputs (bf16: max-abs 2e-2,
-rel-L2 1e-2).  Inputs: the seeded Gaussian-mixture workload (synth/).
+top-p pair lists, the gathered key-tiled V^T.  Toleranced: varlen attention
+outputs of both kernels, row-major V and key-tiled V^T (bf16: max-abs 2e-2,
+rel-L2 1e-2).  Inputs: the seeded Gaussian-mixture workload (synth/) and
+seeded random cluster assignments with skewed sizes.
 """
 
 import json
@@ -65,9 +67,11 @@ def gpu_pipeline():
         vp = svg.svg_permute_rows(v, pk)
         ptr, idx = svg.svg_select_pairs(cq, ck, sk, W.top_p)
         o = svg.svg_varlen_attn(qp, kp, vp, oq, ok, ptr, idx, q_perm=pq)
+        vt = svg.svg_permute_rows_vt(v, pk)
+        o_vt = svg.svg_varlen_attn_vt(qp, kp, vt, oq, ok, ptr, idx, q_perm=pq)
         sync()
         _cache["gpu"] = dict(aq=aq, cq=cq, sq=sq, ak=ak, ck=ck, sk=sk, pq=pq, oq=oq, pk=pk, ok=ok,
-                             ptr=ptr, idx=idx, o=o)
+                             ptr=ptr, idx=idx, o=o, o_vt=o_vt)
     return _cache["gpu"]
 
 
@@ -235,13 +239,15 @@ def test_select_pairs_hand_cases_and_extremes():
             np.testing.assert_array_equal(idx[h].cpu().numpy()[:optr[-1]], oidx)
 
 
-def test_varlen_attention_pipeline_end_to_end():
+@pytest.mark.parametrize("key", ["o", "o_vt"])
+def test_varlen_attention_pipeline_end_to_end(key):
     """GPU pipeline (k-means, permutes, pairs, varlen attention, un-permute)
     against the oracle's varlen attention with the oracle's own clusters and
-    pairs, in original token order, all heads."""
+    pairs, in original token order, all heads; both kernels (row-major V,
+    key-tiled V^T gathered in one pass)."""
     r = gpu_pipeline()
     g = data()
-    got = to_f64(r["o"])
+    got = to_f64(r[key])
     for h in range(W.H):
         o = oracle_head(h)
         q, k, v = (as_f64(g[x][h], "bf16") for x in "qkv")
@@ -249,7 +255,8 @@ def test_varlen_attention_pipeline_end_to_end():
         check_close(got[h], ref, BF16_MAX_ABS, BF16_REL_L2, f"svg2 head {h}")
 
 
-def test_varlen_all_pairs_equals_dense():
+@pytest.mark.parametrize("vt_kernel", [False, True])
+def test_varlen_all_pairs_equals_dense(vt_kernel):
     """Every pair selected: varlen attention is dense attention (sampled rows)."""
     H, N, d, kq, kk = 2, 1500, 128, 5, 9
     q, k, v = random_qkv(H, N, d, seed=11, dtype="bf16")
@@ -262,7 +269,10 @@ def test_varlen_all_pairs_equals_dense():
     qp, kp, vp = svg.svg_permute_rows(qd, pq), svg.svg_permute_rows(kd, pk), svg.svg_permute_rows(vd, pk)
     ptr = torch.from_numpy(np.tile(np.arange(0, kq * kk + 1, kk, dtype=np.int32), (H, 1))).cuda()
     idx = torch.from_numpy(np.tile(np.tile(np.arange(kk, dtype=np.int32), kq), (H, 1))).cuda()
-    o = svg.svg_varlen_attn(qp, kp, vp, oq, ok, ptr, idx, q_perm=pq)
+    if vt_kernel:
+        o = svg.svg_varlen_attn_vt(qp, kp, svg.svg_permute_rows_vt(vd, pk), oq, ok, ptr, idx, q_perm=pq)
+    else:
+        o = svg.svg_varlen_attn(qp, kp, vp, oq, ok, ptr, idx, q_perm=pq)
     sync()
     got = to_f64(o)
     rows = np.r_[0:100, 700:760, N - 50:N]
@@ -271,7 +281,10 @@ def test_varlen_all_pairs_equals_dense():
         check_close(got[h][rows], ref, BF16_MAX_ABS, BF16_REL_L2, f"all-pairs head {h}")
 
 
-def test_varlen_k_zero_mean_of_selected_clusters():
+@pytest.mark.parametrize("vt_kernel", [False, True])
+def test_varlen_k_zero_mean_of_selected_clusters(vt_kernel):
+    """K = 0: every selected key scores alike, so a row's output is the mean
+    of the values of its selected clusters."""
     H, N, d, kq, kk = 1, 900, 64, 4, 6
     q, v, _ = random_qkv(H, N, d, seed=12, dtype="bf16")
     kz = np.zeros_like(q)
@@ -285,8 +298,12 @@ def test_varlen_k_zero_mean_of_selected_clusters():
     pk, ok = svg.svg_cluster_permute(ints(ak), kk, d)
     qp = svg.svg_permute_rows(to_dev(q, "bf16"), pq)
     kp = svg.svg_permute_rows(to_dev(kz, "bf16"), pk)
-    vp = svg.svg_permute_rows(to_dev(v, "bf16"), pk)
-    o = svg.svg_varlen_attn(qp, kp, vp, oq, ok, ints(ptr_np), ints(idx_np), q_perm=pq)
+    if vt_kernel:
+        vt = svg.svg_permute_rows_vt(to_dev(v, "bf16"), pk)
+        o = svg.svg_varlen_attn_vt(qp, kp, vt, oq, ok, ints(ptr_np), ints(idx_np), q_perm=pq)
+    else:
+        vp = svg.svg_permute_rows(to_dev(v, "bf16"), pk)
+        o = svg.svg_varlen_attn(qp, kp, vp, oq, ok, ints(ptr_np), ints(idx_np), q_perm=pq)
     sync()
     got = to_f64(o)[0]
     vv = as_f64(v[0], "bf16")
@@ -294,3 +311,88 @@ def test_varlen_k_zero_mean_of_selected_clusters():
         sel = idx_np[0, ptr_np[0, aq[0, i]]:ptr_np[0, aq[0, i] + 1]]
         ref = vv[np.isin(ak[0], sel)].mean(axis=0)
         check_close(got[i], ref, 1e-2, 1e-2, f"kzero row {i}")
+
+
+@pytest.mark.parametrize("N,d", [(1, 64), (63, 64), (200, 128), (4097, 64), (1000, 128)])
+def test_permute_rows_vt_bit_exact(N, d):
+    """The gathered key-tiled V^T against numpy: tile kb, channel c, key j
+    holds V[perm[64 kb + j]][c], zero past N."""
+    H = 3
+    v = random_qkv(H, N, d, seed=N + d, dtype="bf16")[2]
+    rng = np.random.default_rng(N)
+    perm = np.stack([rng.permutation(N) for _ in range(H)]).astype(np.int32)
+    vt = svg.svg_permute_rows_vt(to_dev(v, "bf16"), ints(perm))
+    sync()
+    nkb = -(-N // 64)
+    want = np.zeros((H, nkb * 64, d), dtype=v.dtype)
+    for h in range(H):
+        want[h, :N] = v[h][perm[h]]
+    want = want.reshape(H, nkb, 64, d).transpose(0, 1, 3, 2)
+    got = vt.cpu().view(torch.int16).numpy()
+    np.testing.assert_array_equal(got, want.view(np.int16))
+
+
+def skewed_assign(rng, N, k):
+    """Cluster ids with sizes spread over orders of magnitude (some empty):
+    small clusters share 64-key windows, large ones span several 128-row
+    chunks."""
+    w = np.exp(rng.normal(0.0, 1.5, size=k))
+    w[rng.random(k) < 0.15] = 0.0
+    w[0] = max(w[0], 1e-3)
+    return rng.choice(k, size=N, p=w / w.sum()).astype(np.int32)
+
+
+def random_pairs(rng, H, kq, kk, p):
+    """Random ascending pair lists, each query cluster keeping a fraction p
+    of the key clusters (cluster 1 keeps none)."""
+    ptr = np.zeros((H, kq + 1), np.int32)
+    idx = np.zeros((H, kq * kk), np.int32)
+    for h in range(H):
+        pos = 0
+        for i in range(kq):
+            sel = np.flatnonzero(rng.random(kk) < p) if i != 1 else np.array([], np.int64)
+            idx[h, pos:pos + sel.size] = sel
+            pos += sel.size
+            ptr[h, i + 1] = pos
+    return ptr, idx
+
+
+@pytest.mark.parametrize("N,d,kq,kk,p", [(777, 64, 6, 40, 0.3), (2500, 128, 9, 200, 0.1), (5000, 64, 20, 256, 0.5),
+                                         (3000, 128, 4, 7, 0.6)])
+def test_varlen_vt_random_clusters_against_oracle(N, d, kq, kk, p):
+    """Both varlen kernels against the oracle's token-exact definition on
+    random skewed clusters and random pair lists: empty clusters, clusters
+    smaller than a window and larger than a 128-row chunk, a query cluster
+    with no pairs (its rows are zero), ragged N."""
+    H = 2
+    rng = np.random.default_rng(N + kk)
+    q, k, v = random_qkv(H, N, d, seed=N + d, dtype="bf16", scale=1.5)
+    aq = np.stack([skewed_assign(rng, N, kq) for _ in range(H)])
+    ak = np.stack([skewed_assign(rng, N, kk) for _ in range(H)])
+    ptr, idx = random_pairs(rng, H, kq, kk, p)
+    pq, oq = svg.svg_cluster_permute(ints(aq), kq, d)
+    pk, ok = svg.svg_cluster_permute(ints(ak), kk, d)
+    qd, kd, vd = (to_dev(t, "bf16") for t in (q, k, v))
+    qp, kp = svg.svg_permute_rows(qd, pq), svg.svg_permute_rows(kd, pk)
+    o_rm = svg.svg_varlen_attn(qp, kp, svg.svg_permute_rows(vd, pk), oq, ok, ints(ptr), ints(idx), q_perm=pq)
+    o_vt = svg.svg_varlen_attn_vt(qp, kp, svg.svg_permute_rows_vt(vd, pk), oq, ok, ints(ptr), ints(idx), q_perm=pq)
+    sync()
+    for h in range(H):
+        ref = osvg2.varlen_attention(*(as_f64(x[h], "bf16") for x in (q, k, v)), aq[h], ak[h], ptr[h], idx[h])
+        assert np.all(ref[aq[h] == 1] == 0.0)
+        for name, o in (("row-major", o_rm), ("V^T", o_vt)):
+            check_close(to_f64(o)[h], ref, BF16_MAX_ABS, BF16_REL_L2, f"{name} varlen head {h}")
+
+
+def test_varlen_vt_rejects_uncovered_shapes():
+    """d outside {64, 128} or more than 2048 windows a head: an error, no
+    launch."""
+    H, N = 1, 64
+    for d, n in ((32, N), (64, 2048 * 64 + 1)):
+        x = torch.zeros(H, n, d, dtype=torch.bfloat16, device="cuda")
+        vt = torch.zeros(svg.svg_vt_elems(H, n, d), dtype=torch.bfloat16, device="cuda")
+        offs = torch.tensor([[0, n]], dtype=torch.int32, device="cuda")
+        ptr = torch.tensor([[0, 1]], dtype=torch.int32, device="cuda")
+        idx = torch.zeros(1, 1, dtype=torch.int32, device="cuda")
+        with pytest.raises(RuntimeError, match="varlen_attn_vt"):
+            svg.svg_varlen_attn_vt(x, x.clone(), vt, offs, offs, ptr, idx)
