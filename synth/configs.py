@@ -42,6 +42,13 @@ class Workload:
     kk: int = 0
     iters: int = 0
     top_p: float = 0.0
+    # HVA-style local-window clustering: window sizes (frames, rows, cols) for
+    # Q and K, blob components of the generator, per-step drift
+    win_q: tuple = (0, 0, 0)
+    win_k: tuple = (0, 0, 0)
+    blobs_q: int = 0
+    blobs_k: int = 0
+    drift: float = 0.0
     notes: str = ""
 
     @property
@@ -95,12 +102,20 @@ SVG2_COG = Workload(
     notes="Gaussian-mixture Q/K; k-means, cluster permute, top-p pairs, "
           "variable-size block-sparse attention")
 
+HVA_COG = Workload(
+    name="hva_cogvideox_shape", F=13, S=1350, T=224, H=8, d=64, dtype="bf16",
+    bq=64, bk=64, ks=0, wt=32, seed=7, grid=(30, 45),
+    iters=10, top_p=0.9, win_q=(4, 10, 15), win_k=(2, 6, 9), blobs_q=40, blobs_k=160, drift=0.1,
+    notes="spatially coherent blob Q/K; 3D local-window clustering (36 + 1 query "
+          "clusters, 175 + 1 key clusters), anchor and refresh steps, top-p pairs, "
+          "varlen attention")
+
 SMOKE_BF16 = Workload(
     name="smoke_bf16", F=4, S=256, T=32, H=2, d=128, dtype="bf16", bq=128, bk=64,
     ks=1, wt=300, seed=6, grid=(16, 16), n_samples=64, structure_scale=3.0,
     notes="head 0 spatial, head 1 temporal; the bf16 path of the HunyuanVideo layer at a small size")
 
-WORKLOADS = {w.name: w for w in (TINY, COG, SMALL_FRAMES, HUNYUAN, HUNYUAN_LAYER, SVG2_COG, SMOKE_BF16)}
+WORKLOADS = {w.name: w for w in (TINY, COG, SMALL_FRAMES, HUNYUAN, HUNYUAN_LAYER, SVG2_COG, HVA_COG, SMOKE_BF16)}
 
 # Extra mask-width points at the HunyuanVideo shape (density sweep).
 # (ks, wt) pairs chosen so that the spatial and temporal tile densities match.

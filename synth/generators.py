@@ -16,6 +16,14 @@ Sharing u between Q and K raises the logits of tokens in the same frame
 Mixture generator (semantic clusters).  Per head, Q tokens belong to one of kq
 components and K tokens to one of kk components, assigned uniformly at random;
 component means ~ N(0, 4 I), tokens = mean + 0.5 * N(0, I).  V ~ N(0, 1).
+
+Blob generator (spatially coherent clusters).  Per head and side, M blob
+centres uniform in the (frames, rows, cols) box of the latent grid; a video
+token belongs to the blob whose centre is nearest (frame offsets weighted by
+4, so blobs are flatter in time than in space); text tokens belong to one of
+two more components.  Means ~ N(0, 4 I), tokens = mean + 0.5 * N(0, I).  A
+later denoising step s adds s * drift * N(0, I) (its own seeded draw).
+V ~ N(0, 1).
 """
 
 import numpy as np
@@ -159,3 +167,37 @@ def random_qkv(H, N, d, seed, dtype="f32", scale=1.0):
     if dtype == "bf16":
         x = f32_to_bf16_bits(x)
     return x[0], x[1], x[2]
+
+
+def blob_qkv(w: Workload, seed: int = None, step: int = 0, heads=None):
+    """Blob-structured Q and K per head (w.blobs_q / w.blobs_k components),
+    V ~ N(0, 1).  Returns dict(q, k, v) as bf16 bits [H][N][d] (uint16) and
+    the generating blob of each token (blob_q, blob_k: int32 [H][N], text
+    components numbered after the blobs).  step > 0 perturbs Q and K by
+    step * w.drift * N(0, I) from a draw of its own (V is kept)."""
+    seed = w.seed if seed is None else seed
+    heads = range(w.H) if heads is None else heads
+    rows, cols = w.grid
+    assert rows * cols == w.S
+    N, d = w.N, w.d
+    f, y, x = np.meshgrid(np.arange(w.F), np.arange(rows), np.arange(cols), indexing="ij")
+    pos = np.stack([4.0 * f.ravel(), y.ravel(), x.ravel()], axis=1)
+    out = {n: np.empty((len(heads), N, d), dtype=np.uint16) for n in "qkv"}
+    blob = {n: np.empty((len(heads), N), dtype=np.int32) for n in "qk"}
+    for i, h in enumerate(heads):
+        rng = np.random.default_rng([seed, h, 7])
+        for side, m in (("q", w.blobs_q), ("k", w.blobs_k)):
+            centres = rng.random((m, 3)) * np.array([4.0 * w.F, rows, cols])
+            d2 = ((pos[:, None, :] - centres[None, :, :]) ** 2).sum(axis=2)
+            comp = np.empty(N, dtype=np.int64)
+            comp[:w.F * w.S] = d2.argmin(axis=1)
+            comp[w.F * w.S:] = m + rng.integers(0, 2, size=w.T)
+            means = rng.standard_normal((m + 2, d), dtype=np.float32) * np.float32(2.0)
+            val = means[comp] + np.float32(0.5) * rng.standard_normal((N, d), dtype=np.float32)
+            if step > 0:
+                srng = np.random.default_rng([seed, h, 7, step, 0 if side == "q" else 1])
+                val = val + np.float32(step * w.drift) * srng.standard_normal((N, d), dtype=np.float32)
+            out[side][i] = f32_to_bf16_bits(val)
+            blob[side][i] = comp
+        out["v"][i] = f32_to_bf16_bits(rng.standard_normal((N, d), dtype=np.float32))
+    return dict(q=out["q"], k=out["k"], v=out["v"], blob_q=blob["q"], blob_k=blob["k"])
