@@ -46,11 +46,13 @@ def parse():
                     help="skip the FP8, CogVideoX-shaped and SVG2 legs of the default run")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--density", default="k5", help="mask widths: k5 (31%%), k4 (26%%), cog_rule (~2%%)")
-    ap.add_argument("--workload", default="hunyuan_layer", choices=["hunyuan_layer", "cogvideox_shape", "svg2"],
+    ap.add_argument("--workload", default="hunyuan_layer",
+                    choices=["hunyuan_layer", "cogvideox_shape", "svg2", "hva"],
                     help="hunyuan_layer: the SVG1 layer step (default, the headline line); "
                          "cogvideox_shape: the same step at the CogVideoX shape (13 x 1350 + 224 tokens, "
                          "8 heads, d = 64, 64x64 tiles, its own mask rule; --density is ignored); "
-                         "svg2: the SVG2 semantic path on the CogVideoX-shaped mixture workload")
+                         "svg2: the SVG2 semantic path on the CogVideoX-shaped mixture workload; "
+                         "hva: local-window clustering (anchor and refresh steps) on the blob workload")
     ap.add_argument("--pmc-target", action="store_true",
                     help="launch the block-sparse attention kernel once and a plain 1.46 GB copy "
                          "(layout kernel with every head spatial) once, for hardware-counter runs")
@@ -865,6 +867,182 @@ def layer_bench(args, w, ks, wt, use_vt=True, steps=None, warmup=None, fp8_leg=F
     return result
 
 
+def bench_hva(args, steps=None, warmup=None):
+    """HVA-style clustering in the SVG2 step, on the CogVideoX-shaped blob
+    workload (13 x 1350 + 224 tokens, 8 heads, d = 64, bf16; windows of
+    4 x 10 x 15 tokens for Q (36 + 1 clusters) and 2 x 6 x 9 for K (175 + 1),
+    10 iterations, top-p 0.9).  Anchor step = local-window clustering of Q
+    and K, cluster sort, gathers (V into V^T), top-p pairs, varlen attention;
+    refresh step = the same with the Lowe-flagged subset re-assigned on the
+    next step's values instead of a full clustering.  Both run the key chain
+    on a second stream.  For comparison: SVG2 k-means with as many clusters
+    (from one seed token per window) on the same tensors, its clustering
+    time and objective at 10 and 50 iterations, and each path's output
+    against dense attention."""
+    import numpy as np
+    import torch
+    from sparse_attention_video_online_amd import svg
+    from synth import HVA_COG as w
+    from synth.generators import blob_qkv
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    rows, cols = w.grid
+    H, N, d = w.H, w.N, w.d
+    up = lambda x: torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+    g0, g1 = blob_qkv(w, step=0), blob_qkv(w, step=1)
+    q0, k0, v = up(g0["q"]), up(g0["k"]), up(g0["v"])
+    q1, k1 = up(g1["q"]), up(g1["k"])
+    kq = svg.svg_hva_clusters(w.F, rows, cols, w.T, w.win_q, H, d)
+    kk = svg.svg_hva_clusters(w.F, rows, cols, w.T, w.win_k, H, d)
+    i32 = lambda *sh: torch.empty(*sh, dtype=torch.int32, device=dev)
+    aq, ak = i32(H, N), i32(H, N)
+    cq = torch.empty(H, kq, d, dtype=torch.float64, device=dev)
+    ck = torch.empty(H, kk, d, dtype=torch.float64, device=dev)
+    sq, sk = i32(H, kq), i32(H, kk)
+    rq, rk = (torch.empty(H, N, dtype=torch.uint8, device=dev) for _ in range(2))
+    pq, pk, oq, ok = i32(H, N), i32(H, N), i32(H, kq + 1), i32(H, kk + 1)
+    ptr, idx = i32(H, kq + 1), i32(H, kq * kk)
+    qp, kp, o = (torch.empty_like(q0) for _ in range(3))
+    vt = torch.empty(svg.svg_vt_elems(H, N, d), dtype=q0.dtype, device=dev)
+    dm = svg.svg_dims(w.F, w.S, w.T, H, d)
+    ws = lambda n: torch.empty(max(1, n), dtype=torch.uint8, device=dev)
+    ws_q, ws_k = ws(svg.workspace_bytes(svg.SVG2_OP_HVA, dm, kq, svg2=True)), \
+        ws(svg.workspace_bytes(svg.SVG2_OP_HVA, dm, kk, svg2=True))
+    ws_c1, ws_c2 = (ws(svg.workspace_bytes(svg.SVG2_OP_CLUSTER_PERMUTE, dm, max(kq, kk), svg2=True))
+                    for _ in range(2))
+    side = torch.cuda.Stream()
+    stream = torch.cuda.current_stream()
+
+    def attention_tail(q, k):
+        svg.svg_select_pairs(cq, ck, sk, w.top_p, pair_ptr=ptr, pair_idx=idx)
+        svg.svg_varlen_attn_vt(qp, kp, vt, oq, ok, ptr, idx, q_perm=pq, out=o)
+
+    def step(anchor):
+        q, k = (q0, k0) if anchor else (q1, k1)
+        cur = torch.cuda.current_stream()
+        fork, join = torch.cuda.Event(), torch.cuda.Event()
+        fork.record(cur)
+        side.wait_event(fork)
+        with torch.cuda.stream(side):
+            if anchor:
+                svg.svg_hva_cluster(k, w.F, rows, cols, w.T, w.win_k, w.iters, assign=ak, centroids=ck, sizes=sk,
+                                    refresh=rk, ws=ws_k)
+            else:
+                svg.svg_hva_refresh(k, w.F, rows, cols, w.T, w.win_k, rk, ak, ck, sizes=sk, ws=ws_k)
+            svg.svg_cluster_permute(ak, kk, d, perm=pk, offs=ok, ws=ws_c2)
+            svg.svg_permute_rows(k, pk, out=kp)
+            svg.svg_permute_rows_vt(v, pk, out=vt)
+            join.record(side)
+        if anchor:
+            svg.svg_hva_cluster(q, w.F, rows, cols, w.T, w.win_q, w.iters, assign=aq, centroids=cq, sizes=sq,
+                                refresh=rq, ws=ws_q)
+        else:
+            svg.svg_hva_refresh(q, w.F, rows, cols, w.T, w.win_q, rq, aq, cq, sizes=sq, ws=ws_q)
+        svg.svg_cluster_permute(aq, kq, d, perm=pq, offs=oq, ws=ws_c1)
+        svg.svg_permute_rows(q, pq, out=qp)
+        cur.wait_event(join)
+        attention_tail(q, k)
+
+    steps = args.steps if steps is None else steps
+    warmup = args.warmup if warmup is None else warmup
+
+    def timed(fn, n, reps_warm):
+        for _ in range(reps_warm):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    # an anchor step, then refresh steps from its state (the refresh reads and
+    # writes the carried clusters, so each timed refresh starts from the last)
+    anchor_ms = timed(lambda: step(True), steps, warmup)
+    o_anchor = o.clone()
+    lists_anchor = [t.clone() for t in (ptr, idx, oq, ok)]
+    state = [t.clone() for t in (aq, cq, ak, ck)]
+    refresh_ms = timed(lambda: step(False), steps, warmup)
+    for t, s_ in zip((aq, cq, ak, ck), state):
+        t.copy_(s_)
+    # clustering alone, one stream
+    clus = {
+        "hva_anchor_q": timed(lambda: svg.svg_hva_cluster(q0, w.F, rows, cols, w.T, w.win_q, w.iters, assign=aq,
+                                                          centroids=cq, sizes=sq, refresh=rq, ws=ws_q), steps, 2),
+        "hva_anchor_k": timed(lambda: svg.svg_hva_cluster(k0, w.F, rows, cols, w.T, w.win_k, w.iters, assign=ak,
+                                                          centroids=ck, sizes=sk, refresh=rk, ws=ws_k), steps, 2),
+    }
+    a_q, c_q, a_k, c_k = aq.clone(), cq.clone(), ak.clone(), ck.clone()
+    flag_frac = {"q": float(rq.float().mean()), "k": float(rk.float().mean())}
+    # (each call refreshes the state the previous one left: same work)
+    clus["hva_refresh_q"] = timed(lambda: svg.svg_hva_refresh(q1, w.F, rows, cols, w.T, w.win_q, rq, aq, cq,
+                                                               sizes=sq, ws=ws_q), steps, 2)
+    clus["hva_refresh_k"] = timed(lambda: svg.svg_hva_refresh(k1, w.F, rows, cols, w.T, w.win_k, rk, ak, ck,
+                                                               sizes=sk, ws=ws_k), steps, 2)
+
+    # objective per token (float64, mean squared distance to the centroid)
+    def sse(x, a, c):
+        xf = x.double()
+        return float(((xf - torch.gather(c, 1, a.long()[..., None].expand(-1, -1, d))) ** 2).sum() / (H * N))
+
+    # SVG2 k-means on the same tensors, as many clusters, one seed token per
+    # window (its first token) and the text cluster's first token
+    def window_seeds(win):
+        wf, wy, wx = win
+        first = [(a * wf) * w.S + (b * wy) * cols + c * wx
+                 for a in range(-(-w.F // wf)) for b in range(-(-rows // wy)) for c in range(-(-cols // wx))]
+        if w.T:
+            first.append(w.F * w.S)
+        return torch.tensor([first] * H, dtype=torch.int32, device=dev)
+
+    km, kmc = {}, {}
+    for name, x, win, kc, a_h, c_h in (("q", q0, w.win_q, kq, a_q, c_q), ("k", k0, w.win_k, kk, a_k, c_k)):
+        seeds = window_seeds(win)
+        r = {"hva_sse": sse(x, a_h, c_h)}
+        for it in (50, w.iters):
+            a_, c_, s_ = svg.svg_kmeans(x, kc, it, seeds)
+            r[f"kmeans{it}_sse"] = sse(x, a_, c_)
+        kmc[name] = (a_, c_, s_)                # 10 iterations, for the attention below
+        r["kmeans_ms"] = timed(lambda: svg.svg_kmeans(x, kc, w.iters, seeds), steps, 2)
+        km[name] = r
+    # the same attention tail over the k-means clusters
+    (ka, kc_, ks), (kka, kkc, kks) = kmc["q"], kmc["k"]
+    kpq, koq = svg.svg_cluster_permute(ka, kq, d)
+    kpk, kok = svg.svg_cluster_permute(kka, kk, d)
+    kptr, kidx = svg.svg_select_pairs(kc_, kkc, kks, w.top_p)
+    o_km = svg.svg_varlen_attn_vt(svg.svg_permute_rows(q0, kpq), svg.svg_permute_rows(k0, kpk),
+                                  svg.svg_permute_rows_vt(v, kpk), koq, kok, kptr, kidx, q_perm=kpq)
+
+    # attention quality: each path's output against dense attention
+    vt_id = svg.svg_layout_permute_vt(v, 1, N, 0, torch.zeros(H, dtype=torch.int32, device=dev))
+    dense = svg.svg_dense_attn_vt(q0, k0, vt_id, 1, N, 0, 64, 64)
+    rel = lambda a, b: float((a.float() - b.float()).norm() / b.float().norm())
+
+    def pair_density(p_, i_, qo, ko):
+        # selected (query, key) token pairs over H N^2
+        p_, i_ = p_.cpu().numpy(), i_.cpu().numpy()
+        qs, ks_ = np.diff(qo.cpu().numpy(), axis=1), np.diff(ko.cpu().numpy(), axis=1)
+        tot = sum(int(qs[h, i]) * int(ks_[h, i_[h, p_[h, i]:p_[h, i + 1]]].sum())
+                  for h in range(H) for i in range(p_.shape[1] - 1))
+        return tot / (H * float(N) * N)
+    torch.cuda.synchronize()
+    return {
+        "workload": w.name, "kq": kq, "kk": kk, "iters": w.iters,
+        "anchor_step_ms": round(anchor_ms, 4), "refresh_step_ms": round(refresh_ms, 4),
+        "clustering_ms": {k_: round(v_, 4) for k_, v_ in clus.items()},
+        "kmeans_same_k_ms": {"q": round(km["q"]["kmeans_ms"], 4), "k": round(km["k"]["kmeans_ms"], 4)},
+        "refresh_fraction": {k_: round(v_, 4) for k_, v_ in flag_frac.items()},
+        "sse_per_token": {s_: {k_: round(v_, 3) for k_, v_ in km[s_].items() if k_.endswith("sse")} for s_ in km},
+        "rel_l2_vs_dense": round(rel(o_anchor, dense), 5),
+        "kmeans_rel_l2_vs_dense": round(rel(o_km, dense), 5),
+        "pair_density": round(pair_density(*lists_anchor), 4),
+        "kmeans_pair_density": round(pair_density(kptr, kidx, koq, kok), 4),
+    }
+
+
 def main():
     args = parse()
     if args.record_traffic:
@@ -878,6 +1056,9 @@ def main():
 
     if args.workload == "svg2":
         print(json.dumps(bench_svg2(args, cpu=not args.no_cpu_baseline)), flush=True)
+        return
+    if args.workload == "hva":
+        print(json.dumps(bench_hva(args)), flush=True)
         return
 
     from synth import COG, HUNYUAN_LAYER
@@ -909,6 +1090,8 @@ def main():
         result["svg2"] = {k_: s2[k_] for k_ in ("ms_per_step", "stage_ms", "one_stream_ms", "eager_two_stream_ms",
                                                  "varlen_tflops", "gather_gbs")}
         result["svg2"]["pair_density"] = s2["config"]["pair_density"]
+        torch.cuda.empty_cache()
+        result["hva"] = bench_hva(args, steps=20, warmup=3)
     if not args.no_cpu_baseline:
         lab = [int(c) for c in result["config"]["labels"]]
         result["cpu_baseline"] = cpu_baseline(HUNYUAN_LAYER, ks, wt, lab, args.cpu_seconds)

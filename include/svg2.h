@@ -25,7 +25,8 @@ extern "C" {
 typedef enum {
   SVG2_OP_KMEANS = 0,          /* a = k                 */
   SVG2_OP_CLUSTER_PERMUTE = 1, /* a = k                 */
-  SVG2_OP_VARLEN = 2           /* a = kq, b = kk        */
+  SVG2_OP_VARLEN = 2,          /* a = kq, b = kk        */
+  SVG2_OP_HVA = 3              /* a = k (svg_hva_clusters) */
 } svg2_op;
 
 /* Bytes of workspace an SVG2 op needs (host-only, no HIP call). */
@@ -153,6 +154,54 @@ svg_status svg_varlen_attn_vt(const svg_dims *dims, svg_dtype dtype,
                               const int32_t *q_offs, const int32_t *k_offs, int32_t kq, int32_t kk,
                               const int32_t *pair_ptr, const int32_t *pair_idx,
                               const int32_t *q_perm, float softmax_scale, void *O, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * HVA-style clustering (HyperVAttention, sections Approach and Key results:
+ * centroid search restricted to local 3D spatio-temporal windows; cluster
+ * assignments reused across denoising steps, with full clustering only at
+ * anchor steps and a Lowe's-ratio-selected subset refreshed otherwise).  The
+ * page gives no formulas; this library's reading, per head:
+ *   - video token (f, y, x) of the F x rows x cols grid (rows * cols = S) is
+ *     row f*S + y*cols + x; the T text rows follow;
+ *   - the grid is cut into windows of win[0] x win[1] x win[2] tokens (the
+ *     last ones along an axis may be smaller); window (a, b, c) is cluster
+ *     (a*nY + b)*nX + c, nF = ceil(F/win[0]), nY = ceil(rows/win[1]),
+ *     nX = ceil(cols/win[2]); the text rows form one more cluster,
+ *     C = nF*nY*nX, whose members never change;
+ *   - seeds: each window's mean, and the text rows' mean;
+ *   - a video token chooses among the centroids of its own and the adjacent
+ *     windows (|da|, |db|, |dc| <= 1), by the float32 distance
+ *     sum over dims in order of fl(fl(x - m)^2) with float32 adds (m: the
+ *     double centroid rounded to float32), ties to the lower cluster id;
+ *   - update: double means of the members (exact sums of bf16 values); an
+ *     empty cluster keeps its centroid;
+ *   - Lowe flags (last assignment of svg_hva_cluster): a video token whose
+ *     best and second-best distances satisfy d1 >= fl(lowe_r2 * d2) in
+ *     float32 (not distinctive) is flagged for refresh; text rows never.
+ *
+ * svg_hva_clusters: the number of clusters k = C + (T > 0), or 0 for
+ *   invalid arguments.
+ * svg_hva_cluster (anchor step): seeds, then iters >= 1 rounds of local
+ *   assignment and update.  Outputs assign int32 [H][N], centroids double
+ *   [H][k][d], sizes int32 [H][k], refresh uint8 [H][N] (the Lowe flags).
+ * svg_hva_refresh (non-anchor step, new values X): tokens with refresh != 0
+ *   are re-assigned among their candidates against the carried centroids
+ *   (as is any token whose cluster is not among its candidates), the others
+ *   keep assign; then one update from X.  assign and centroids are read and
+ *   written in place, sizes written.
+ * X bf16 [H][N][d], d = 64 or 128, F >= 1, rows * cols = S, windows >= 1.
+ * ws: svg2_workspace_bytes(SVG2_OP_HVA, dims, k, 0).  Outputs must not
+ * overlap X or ws (SVG_ERR_RANGE).
+ * ------------------------------------------------------------------------- */
+int32_t svg_hva_clusters(const svg_dims *dims, int32_t rows, int32_t cols, const int32_t win[3]);
+svg_status svg_hva_cluster(const svg_dims *dims, svg_dtype dtype, const void *X, int32_t rows,
+                           int32_t cols, const int32_t win[3], int32_t iters, float lowe_r2,
+                           int32_t *assign, double *centroids, int32_t *sizes, uint8_t *refresh,
+                           void *ws, size_t ws_bytes, void *stream);
+svg_status svg_hva_refresh(const svg_dims *dims, svg_dtype dtype, const void *X, int32_t rows,
+                           int32_t cols, const int32_t win[3], const uint8_t *refresh,
+                           int32_t *assign, double *centroids, int32_t *sizes, void *ws,
+                           size_t ws_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -602,6 +602,9 @@ size_t svg2_workspace_bytes(svg2_op op, const svg_dims *dims, int32_t a, int32_t
     case SVG2_OP_VARLEN:
       if (check_dims(dims, &dm, false) != SVG_OK || a < 1 || b < 1) return 0;
       return svgk::varlen_ws_bytes(dm, a, b);
+    case SVG2_OP_HVA:
+      if (check_dims(dims, &dm, false) != SVG_OK || a < 1) return 0;
+      return svgk::hva_ws_bytes(dm, a);
   }
   return 0;
 }
@@ -719,6 +722,89 @@ svg_status svg_varlen_attn(const svg_dims *dims, svg_dtype dtype, const void *Qp
                                         pair_idx, q_perm, resolve_scale(softmax_scale, dm.d), O, ws,
                                         (hipStream_t)stream),
                     "svg_varlen_attn");
+}
+
+static svg_status hva_geometry(const svg_dims *dims, int32_t rows, int32_t cols, const int32_t *win, Dims *dm) {
+  svg_status s;
+  if ((s = check_dims(dims, dm)) != SVG_OK) return s;
+  if (!win) return fail(SVG_ERR_NULL, "hva: NULL window");
+  if (rows < 1 || cols < 1 || (int64_t)rows * cols != dm->S)
+    return fail(SVG_ERR_SHAPE, "hva: rows=%d cols=%d do not tile S=%d", rows, cols, dm->S);
+  if (win[0] < 1 || win[1] < 1 || win[2] < 1)
+    return fail(SVG_ERR_RANGE, "hva: window %dx%dx%d", win[0], win[1], win[2]);
+  return SVG_OK;
+}
+
+static svg_status hva_checks(const svg_dims *dims, svg_dtype dtype, const void *X, int32_t rows, int32_t cols,
+                             const int32_t *win, Dims *dm) {
+  svg_status s;
+  if ((s = hva_geometry(dims, rows, cols, win, dm)) != SVG_OK) return s;
+  if ((s = check_dtype(dtype)) != SVG_OK) return s;
+  if (dtype != SVG_BF16) return fail(SVG_ERR_UNSUPPORTED, "hva: bf16 inputs only");
+  if (!X) return fail(SVG_ERR_NULL, "hva: NULL X");
+  return SVG_OK;
+}
+
+int32_t svg_hva_clusters(const svg_dims *dims, int32_t rows, int32_t cols, const int32_t win[3]) {
+  Dims dm{};
+  if (hva_geometry(dims, rows, cols, win, &dm) != SVG_OK) return 0;
+  const int64_t k = svgk::hva_clusters(dm, rows, cols, win);
+  return k > (int64_t)INT32_MAX ? 0 : (int32_t)k;
+}
+
+svg_status svg_hva_cluster(const svg_dims *dims, svg_dtype dtype, const void *X, int32_t rows, int32_t cols,
+                           const int32_t win[3], int32_t iters, float lowe_r2, int32_t *assign, double *centroids,
+                           int32_t *sizes, uint8_t *refresh, void *ws, size_t ws_bytes, void *stream) {
+  Dims dm{};
+  svg_status s;
+  if ((s = hva_checks(dims, dtype, X, rows, cols, win, &dm)) != SVG_OK) return s;
+  if (!assign || !centroids || !sizes || !refresh) return fail(SVG_ERR_NULL, "hva_cluster: NULL pointer");
+  if (iters < 1) return fail(SVG_ERR_RANGE, "hva_cluster: iters=%d < 1", iters);
+  if (!(lowe_r2 >= 0.f && lowe_r2 <= 1.f)) return fail(SVG_ERR_RANGE, "hva_cluster: lowe_r2=%g not in [0, 1]", lowe_r2);
+  const int k = svgk::hva_clusters(dm, rows, cols, win);
+  const size_t need = svgk::hva_ws_bytes(dm, k);
+  if (ws_bytes < need || ws == nullptr)
+    return fail(SVG_ERR_WORKSPACE, "hva_cluster: workspace %zu < %zu bytes", ws_bytes, need);
+  const size_t xb = (size_t)dm.H * dm.N * dm.d * 2, ab = (size_t)dm.H * dm.N * 4, rb = (size_t)dm.H * dm.N;
+  const size_t cb = (size_t)dm.H * k * dm.d * 8, sb = (size_t)dm.H * k * 4;
+  const void *outs[4] = {assign, centroids, sizes, refresh};
+  const size_t ob[4] = {ab, cb, sb, rb};
+  for (int i = 0; i < 4; ++i) {
+    if (overlaps2(outs[i], ob[i], X, xb) || overlaps2(outs[i], ob[i], ws, need))
+      return fail(SVG_ERR_RANGE, "hva_cluster: an output overlaps X or ws");
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps2(outs[i], ob[i], outs[j], ob[j])) return fail(SVG_ERR_RANGE, "hva_cluster: outputs overlap");
+  }
+  return hip_status(svgk::launch_hva_cluster(dm, X, rows, cols, win, iters, lowe_r2, assign, centroids, sizes,
+                                             refresh, ws, (hipStream_t)stream),
+                    "svg_hva_cluster");
+}
+
+svg_status svg_hva_refresh(const svg_dims *dims, svg_dtype dtype, const void *X, int32_t rows, int32_t cols,
+                           const int32_t win[3], const uint8_t *refresh, int32_t *assign, double *centroids,
+                           int32_t *sizes, void *ws, size_t ws_bytes, void *stream) {
+  Dims dm{};
+  svg_status s;
+  if ((s = hva_checks(dims, dtype, X, rows, cols, win, &dm)) != SVG_OK) return s;
+  if (!assign || !centroids || !sizes || !refresh) return fail(SVG_ERR_NULL, "hva_refresh: NULL pointer");
+  const int k = svgk::hva_clusters(dm, rows, cols, win);
+  const size_t need = svgk::hva_ws_bytes(dm, k);
+  if (ws_bytes < need || ws == nullptr)
+    return fail(SVG_ERR_WORKSPACE, "hva_refresh: workspace %zu < %zu bytes", ws_bytes, need);
+  const size_t xb = (size_t)dm.H * dm.N * dm.d * 2, ab = (size_t)dm.H * dm.N * 4, rb = (size_t)dm.H * dm.N;
+  const size_t cb = (size_t)dm.H * k * dm.d * 8, sb = (size_t)dm.H * k * 4;
+  const void *outs[3] = {assign, centroids, sizes};
+  const size_t ob[3] = {ab, cb, sb};
+  for (int i = 0; i < 3; ++i) {
+    if (overlaps2(outs[i], ob[i], X, xb) || overlaps2(outs[i], ob[i], ws, need) ||
+        overlaps2(outs[i], ob[i], refresh, rb))
+      return fail(SVG_ERR_RANGE, "hva_refresh: an output overlaps X, refresh or ws");
+    for (int j = i + 1; j < 3; ++j)
+      if (overlaps2(outs[i], ob[i], outs[j], ob[j])) return fail(SVG_ERR_RANGE, "hva_refresh: outputs overlap");
+  }
+  return hip_status(svgk::launch_hva_refresh(dm, X, rows, cols, win, refresh, assign, centroids, sizes, ws,
+                                             (hipStream_t)stream),
+                    "svg_hva_refresh");
 }
 
 svg_status svg_permute_rows_vt(const svg_dims *dims, svg_dtype dtype, const void *V, const int32_t *perm,

@@ -147,4 +147,14 @@ hipError_t launch_varlen_vt(const Dims &dm, const void *Qp, const void *Kp, cons
                             const int32_t *k_offs, int kq, int kk, const int32_t *pair_ptr, const int32_t *pair_idx,
                             const int32_t *q_perm, float scale, void *O, hipStream_t st);
 
+// HVA-style local-window clustering (bf16 inputs, d = 64 or 128).
+int hva_clusters(const Dims &dm, int rows, int cols, const int win[3]);
+size_t hva_ws_bytes(const Dims &dm, int k);
+hipError_t launch_hva_cluster(const Dims &dm, const void *X, int rows, int cols, const int win[3], int iters,
+                              float r2, int32_t *assign, double *cent, int32_t *sizes, uint8_t *flags, void *ws,
+                              hipStream_t st);
+hipError_t launch_hva_refresh(const Dims &dm, const void *X, int rows, int cols, const int win[3],
+                              const uint8_t *flags, int32_t *assign, double *cent, int32_t *sizes, void *ws,
+                              hipStream_t st);
+
 }  // namespace svgk

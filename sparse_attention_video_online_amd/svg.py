@@ -21,7 +21,7 @@ SVG_OK, SVG_ERR_NULL, SVG_ERR_SHAPE, SVG_ERR_DTYPE, SVG_ERR_UNSUPPORTED, SVG_ERR
     SVG_ERR_WORKSPACE, SVG_ERR_HIP = range(8)
 SVG_F32, SVG_BF16 = 0, 1
 SVG_OP_PROFILE, SVG_OP_BLOCK_SPARSE, SVG_OP_COMPACT, SVG_OP_ATTN_VT, SVG_OP_ATTN_CSR = 0, 1, 2, 3, 4
-SVG2_OP_KMEANS, SVG2_OP_CLUSTER_PERMUTE, SVG2_OP_VARLEN = 0, 1, 2
+SVG2_OP_KMEANS, SVG2_OP_CLUSTER_PERMUTE, SVG2_OP_VARLEN, SVG2_OP_HVA = 0, 1, 2, 3
 
 
 class svg_dims(ctypes.Structure):
@@ -81,9 +81,12 @@ SIGNATURES = {
     "svg_select_pairs": [_DIMS, _P, _P, _P, _I, _I, _D, _F, _P, _P, _P],
     "svg_varlen_attn": [_DIMS, _I, _P, _P, _P, _P, _P, _I, _I, _P, _P, _P, _F, _P, _P, _Z, _P],
     "svg_permute_rows_vt": [_DIMS, _I, _P, _P, _P, _P],
+    "svg_hva_clusters": [_DIMS, _I, _I, _P],
+    "svg_hva_cluster": [_DIMS, _I, _P, _I, _I, _P, _I, _F, _P, _P, _P, _P, _P, _Z, _P],
+    "svg_hva_refresh": [_DIMS, _I, _P, _I, _I, _P, _P, _P, _P, _P, _P, _Z, _P],
     "svg_varlen_attn_vt": [_DIMS, _I, _P, _P, _P, _P, _P, _I, _I, _P, _P, _P, _F, _P, _P],
 }
-_RESTYPES = {"svg_workspace_bytes": _Z, "svg2_workspace_bytes": _Z, "svg_vt_elems": _Z, "svg_ear_centroid_elems": _Z,
+_RESTYPES = {"svg_hva_clusters": _I, "svg_workspace_bytes": _Z, "svg2_workspace_bytes": _Z, "svg_vt_elems": _Z, "svg_ear_centroid_elems": _Z,
              "svg_last_error": ctypes.c_char_p, "svg_version": ctypes.c_char_p}
 
 
@@ -700,3 +703,66 @@ def svg_varlen_attn_vt(qp, kp, vt, q_offs, k_offs, pair_ptr, pair_idx, q_perm=No
                                    _ptr(k_offs), kq, kk, _ptr(pair_ptr), _ptr(pair_idx), _ptr(q_perm), scale,
                                    _ptr(out), _stream()), "svg_varlen_attn_vt")
     return out
+
+
+# ----------------------------------------------------------------------------
+# HVA-style local-window clustering
+
+def _win(win):
+    w = (ctypes.c_int32 * 3)(*[int(v) for v in win])
+    return w
+
+
+def svg_hva_clusters(F, rows, cols, T, win, H=1, d=64):
+    """Number of clusters of the window grid (windows plus the text cluster)."""
+    return int(_lib.svg_hva_clusters(ctypes.byref(svg_dims(F, rows * cols, T, H, d)), rows, cols, _win(win)))
+
+
+def svg_hva_cluster(x, F, rows, cols, T, win, iters, lowe_r2=0.64, assign=None, centroids=None, sizes=None,
+                    refresh=None, ws=None):
+    """Anchor step: local-window k-means of x [H][N][d] (bf16).  Returns
+    assign [H][N], centroids [H][k][d] (float64), sizes [H][k], refresh
+    flags [H][N] (uint8)."""
+    dm = _video_dims(x, F, rows * cols, T)
+    H, N, d = x.shape
+    dt = _dtype(x)
+    _need(x, "X", x.dtype, x.numel())
+    k = svg_hva_clusters(F, rows, cols, T, win, H, d)
+    if k < 1:
+        raise SvgError(-1, f"svg_hva_clusters: {last_error()}")
+    dev = x.device
+    assign = torch.empty(H, N, dtype=torch.int32, device=dev) if assign is None else assign
+    centroids = torch.empty(H, k, d, dtype=torch.float64, device=dev) if centroids is None else centroids
+    sizes = torch.empty(H, k, dtype=torch.int32, device=dev) if sizes is None else sizes
+    refresh = torch.empty(H, N, dtype=torch.uint8, device=dev) if refresh is None else refresh
+    _need(assign, "assign", torch.int32, H * N)
+    _need(centroids, "centroids", torch.float64, H * k * d)
+    _need(sizes, "sizes", torch.int32, H * k)
+    _need(refresh, "refresh", torch.uint8, H * N)
+    ws = _ws(workspace_bytes(SVG2_OP_HVA, dm, k, svg2=True), dev, ws)
+    _check(_lib.svg_hva_cluster(ctypes.byref(dm), dt, _ptr(x), rows, cols, _win(win), iters, float(lowe_r2),
+                                _ptr(assign), _ptr(centroids), _ptr(sizes), _ptr(refresh), _ptr(ws), _bytes(ws),
+                                _stream()), "svg_hva_cluster")
+    return assign, centroids, sizes, refresh
+
+
+def svg_hva_refresh(x, F, rows, cols, T, win, refresh, assign, centroids, sizes=None, ws=None):
+    """Non-anchor step: flagged tokens re-assigned against the carried
+    centroids, then one update from x; assign and centroids in place.
+    Returns (assign, centroids, sizes)."""
+    dm = _video_dims(x, F, rows * cols, T)
+    H, N, d = x.shape
+    dt = _dtype(x)
+    _need(x, "X", x.dtype, x.numel())
+    k = svg_hva_clusters(F, rows, cols, T, win, H, d)
+    if k < 1:
+        raise SvgError(-1, f"svg_hva_clusters: {last_error()}")
+    sizes = torch.empty(H, k, dtype=torch.int32, device=x.device) if sizes is None else sizes
+    _need(refresh, "refresh", torch.uint8, H * N)
+    _need(assign, "assign", torch.int32, H * N)
+    _need(centroids, "centroids", torch.float64, H * k * d)
+    _need(sizes, "sizes", torch.int32, H * k)
+    ws = _ws(workspace_bytes(SVG2_OP_HVA, dm, k, svg2=True), x.device, ws)
+    _check(_lib.svg_hva_refresh(ctypes.byref(dm), dt, _ptr(x), rows, cols, _win(win), _ptr(refresh), _ptr(assign),
+                                _ptr(centroids), _ptr(sizes), _ptr(ws), _bytes(ws), _stream()), "svg_hva_refresh")
+    return assign, centroids, sizes

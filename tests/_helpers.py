@@ -49,3 +49,23 @@ def check_close(got, ref, max_abs, rel_l2, what=""):
     rl2 = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30))
     assert mx <= max_abs and rl2 <= rel_l2, f"{what}: max-abs {mx:.3e} rel-L2 {rl2:.3e}"
     return mx, rl2
+
+
+def exact_sum_span_ok(x64, assign, k):
+    """Whether every cluster's member sums are exact in float64 in any order:
+    for bf16 members (8-bit significands) the exponent span of a dimension's
+    nonzero values must be at most 45 - log2(cluster size)."""
+    e = np.frexp(x64)[1]
+    nz = x64 != 0
+    for j in range(k):
+        m = assign == j
+        n = int(m.sum())
+        if n == 0:
+            continue
+        ej, nzj = e[m], nz[m]
+        hi = np.where(nzj, ej, -10 ** 6).max(axis=0)
+        lo = np.where(nzj, ej, 10 ** 6).min(axis=0)
+        span = np.where(hi >= lo, hi - lo, 0)
+        if span.max() > 45 - np.log2(n):
+            return False
+    return True

@@ -157,3 +157,38 @@ def test_kmeans_noalloc_rejects_problems_beyond_its_scratch():
         == svg.SVG_ERR_RANGE
     assert L.svg_kmeans_noalloc(ctypes.byref(small), 1, None, 8, 10, FAKE, FAKE2, FAKE3, FAKE2, None) \
         == svg.SVG_ERR_NULL
+
+
+def test_hva_cluster_count_and_host_checks():
+    """svg_hva_clusters agrees with the oracle's count (windows plus the text
+    cluster); the HVA entries reject bad geometry, dtype and workspace on
+    the host."""
+    from oracle import hva
+    win = lambda *w: (ctypes.c_int32 * 3)(*w)
+    for F, rows, cols, T, w in ((13, 30, 45, 224, (2, 6, 9)), (13, 30, 45, 224, (4, 10, 15)), (3, 4, 5, 0, (2, 2, 2)),
+                                (1, 1, 7, 3, (1, 1, 7)), (5, 6, 6, 1, (9, 9, 9))):
+        got = svg.lib().svg_hva_clusters(dims(F=F, S=rows * cols, T=T), rows, cols, win(*w))
+        assert got == hva.n_clusters(F, rows, cols, T, w)
+    L = svg.lib()
+    d0 = dims(F=13, S=1350, T=224, H=2, d=64)
+    assert L.svg_hva_clusters(d0, 30, 44, win(2, 6, 9)) == 0                 # rows * cols != S
+    assert L.svg_hva_clusters(d0, 30, 45, win(0, 6, 9)) == 0
+    assert L.svg_hva_clusters(d0, 30, 45, None) == 0
+    o1, o2, o3, o4 = (ctypes.c_void_p(a) for a in (0x100000000, 0x200000000, 0x300000000, 0x400000000))
+    wsp = ctypes.c_void_p(0x500000000)
+
+    def cl(dt=1, x=FAKE, rows=30, w=(2, 6, 9), iters=10, r2=0.64, ws=wsp, wsb=1 << 30, outs=(o1, o2, o3, o4)):
+        return L.svg_hva_cluster(d0, dt, x, rows, 45, win(*w), iters, ctypes.c_float(r2), *outs, ws, wsb, None)
+
+    assert cl(dt=0) == svg.SVG_ERR_UNSUPPORTED                               # fp32
+    assert cl(x=None) == svg.SVG_ERR_NULL
+    assert cl(rows=29) == svg.SVG_ERR_SHAPE
+    assert cl(w=(2, 0, 9)) == svg.SVG_ERR_RANGE
+    assert cl(iters=0) == svg.SVG_ERR_RANGE
+    assert cl(r2=1.5) == svg.SVG_ERR_RANGE
+    assert cl(wsb=16) == svg.SVG_ERR_WORKSPACE
+    assert cl(outs=(o1, o1, o3, o4)) == svg.SVG_ERR_RANGE                    # two outputs share memory
+    assert L.svg_hva_refresh(d0, 1, FAKE, 30, 45, win(2, 6, 9), None, o1, o2, o3, wsp, 1 << 30,
+                             None) == svg.SVG_ERR_NULL
+    need = svg.lib().svg2_workspace_bytes(svg.SVG2_OP_HVA, d0, 176, 0)
+    assert need >= 2 * 176 * 64 * 12

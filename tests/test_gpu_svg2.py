@@ -16,7 +16,7 @@ import pytest
 import torch
 
 from conftest import GOLDEN
-from _helpers import to_dev, to_f64, ints, check_close, BF16_MAX_ABS, BF16_REL_L2
+from _helpers import to_dev, to_f64, ints, check_close, exact_sum_span_ok, BF16_MAX_ABS, BF16_REL_L2
 from oracle import svg2 as osvg2
 from oracle.attention import dense_attention
 from oracle.numerics import as_f64
@@ -73,26 +73,6 @@ def gpu_pipeline():
         _cache["gpu"] = dict(aq=aq, cq=cq, sq=sq, ak=ak, ck=ck, sk=sk, pq=pq, oq=oq, pk=pk, ok=ok,
                              ptr=ptr, idx=idx, o=o, o_vt=o_vt)
     return _cache["gpu"]
-
-
-def exact_sum_span_ok(x64, assign, k):
-    """Whether every cluster's member sums are exact in float64 in any order:
-    for bf16 members (8-bit significands) the exponent span of a dimension's
-    nonzero values must be at most 45 - log2(cluster size)."""
-    e = np.frexp(x64)[1]
-    nz = x64 != 0
-    for j in range(k):
-        m = assign == j
-        n = int(m.sum())
-        if n == 0:
-            continue
-        ej, nzj = e[m], nz[m]
-        hi = np.where(nzj, ej, -10 ** 6).max(axis=0)
-        lo = np.where(nzj, ej, 10 ** 6).min(axis=0)
-        span = np.where(hi >= lo, hi - lo, 0)
-        if span.max() > 45 - np.log2(n):
-            return False
-    return True
 
 
 def test_kmeans_bit_exact_all_heads():
