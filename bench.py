@@ -90,7 +90,7 @@ TRAFFIC_SOURCES = ["sparse_attention_video_online_amd/csrc/attn_vt.hip",
                    "sparse_attention_video_online_amd/csrc/attn_vt_core.h",
                    "sparse_attention_video_online_amd/csrc/attn_core.h",
                    "sparse_attention_video_online_amd/csrc/svg_common.h"]
-TRAFFIC_KERNEL = "attn_fwd_vt<128, 128, false>"
+TRAFFIC_KERNEL = "attn_fwd_vt<128, 128, false, false>"
 
 
 def record_traffic(fetch_csv, write_csv):
@@ -144,7 +144,7 @@ def record_traffic(fetch_csv, write_csv):
 
 COUNTERS_HEADER = """# HBM traffic, achieved bandwidth and MFMA busy time of the path's kernels
 
-Two programs, each run under rocprofv3 four times (kernel trace; FETCH_SIZE; WRITE_SIZE;
+Three programs, each run under rocprofv3 four times (kernel trace; FETCH_SIZE; WRITE_SIZE;
 SQ_VALU_MFMA_BUSY_CYCLES), from /tmp on the MI355X box (`<repo>` is the repository root,
 `<out>` the output folder):
 
@@ -153,6 +153,8 @@ SQ_VALU_MFMA_BUSY_CYCLES), from /tmp on the MI355X box (`<repo>` is the reposito
 ARGS="--no-extra --steps 2 --warmup 1 --no-cpu-baseline --dense-reps 1"
 # svg2: the SVG2 semantic path on the CogVideoX-shaped mixture workload
 ARGS="--workload svg2 --steps 3 --warmup 1 --no-cpu-baseline"
+# hva: local-window clustering (anchor and refresh steps) on the CogVideoX-shaped blob workload
+ARGS="--workload hva --steps 3 --warmup 1"
 rocprofv3 --kernel-trace --stats --output-format csv -d <out>/<prog>_trace -o run -- python3 <repo>/bench.py $ARGS
 rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/<prog>_fetch -o run -- python3 <repo>/bench.py $ARGS
 rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/<prog>_write -o run -- python3 <repo>/bench.py $ARGS
@@ -169,21 +171,25 @@ and writes the tensor and reads the order.  The attention kernels are bound by t
 cores, not by memory: their line is there for the traffic (the sparse kernel fetches ~18x its
 algorithmic bytes, ~78% of it served by the XCD L2s, at ~1.1 TB/s).  The SVG2 workload (36 MB
 of Q and K) stays in the L2s and the 256 MB Infinity Cache between launches, so its k-means
-kernels run at a few microseconds each and are bound by launch and per-kernel latency.
+kernels run at a few microseconds each and are bound by launch and per-kernel latency.  The
+local-window assignment (`hva_assign`) reads each token's row once and runs its distances on the
+vector ALUs (a float32 expression the oracle evaluates identically), so its MFMA column is empty.
 
 """
 
 
 COUNTER_KERNELS = ["layout_kernel", "vt_kernel", "profile_full_vt", "profile_temporal_vt", "profile_combine",
                    "block_mask_kernel", "fill_kernel", "attn_fwd_vt", "km_assign_bf3", "km_update", "sort_place",
-                   "sort_count", "permute_rows_kernel", "select_rows", "varlen_attn", "varlen_vt", "km_prep3"]
+                   "sort_count", "permute_rows_kernel", "select_rows", "varlen_attn", "varlen_vt", "km_prep3",
+                   "hva_assign", "hva_finalize", "hva_prep"]
 
 
 def record_counters(root):
     """Per-kernel HBM traffic, achieved bandwidth and MFMA busy time from
-    rocprofv3 runs under `root`: for each of the two programs (layer: the
+    rocprofv3 runs under `root`: for each of the three programs (layer: the
     HunyuanVideo layer step, bench.py --no-extra; svg2: bench.py --workload
-    svg2) a kernel trace (<prog>_trace) and counter runs of FETCH_SIZE
+    svg2; hva: bench.py --workload hva) a kernel trace (<prog>_trace) and
+    counter runs of FETCH_SIZE
     (<prog>_fetch), WRITE_SIZE (<prog>_write) and SQ_VALU_MFMA_BUSY_CYCLES
     (<prog>_sq), each written with --output-format csv.  Dispatches are
     joined across runs by dispatch id (the programs are deterministic; the
@@ -195,7 +201,7 @@ def record_counters(root):
     import csv
     import glob
     from collections import defaultdict
-    from synth import HUNYUAN_LAYER as L, SVG2_COG as C
+    from synth import HUNYUAN_LAYER as L, SVG2_COG as C, HVA_COG as V
 
     def find(prog, kind, suffix):
         hits = glob.glob(os.path.join(root, f"{prog}_{kind}", "**", f"*{suffix}"), recursive=True)
@@ -242,11 +248,14 @@ def record_counters(root):
         ("svg2", "sort_place"): 2 * C.H * C.N * 4,
         ("svg2", "permute_rows_kernel"): 2 * EC + C.H * C.N * 4,
         ("svg2", "vt_kernel<64> (V gather)"): EC + C.H * -(-C.N // 64) * 64 * C.d * 2 + C.H * C.N * 4,
+        ("hva", "hva_assign<64>"): V.H * V.N * V.d * 2 + V.H * V.N * 4,
+        ("hva", "vt_kernel<64> (V gather)"): V.H * V.N * V.d * 2 + V.H * -(-V.N // 64) * 64 * V.d * 2 + V.H * V.N * 4,
+        ("hva", "permute_rows_kernel"): 2 * V.H * V.N * V.d * 2 + V.H * V.N * 4,
     }
 
     fetch_scale = write_scale = None
     rows = []
-    for prog in ("layer", "svg2"):
+    for prog in ("layer", "svg2", "hva"):
         tr = trace(prog)
         fv, fnames, grids = counters(prog, "fetch")
         wv, _, _ = counters(prog, "write")
@@ -261,7 +270,7 @@ def record_counters(root):
             if k is None or d not in fnames or short(fnames[d]) != k:
                 continue
             if k.startswith("vt_kernel"):
-                if prog == "svg2":
+                if prog in ("svg2", "hva"):
                     k += " (V gather)"
                 else:
                     k += " (attention V^T)" if grids[d] == attn_vt_grid else " (profiler V^T)"
