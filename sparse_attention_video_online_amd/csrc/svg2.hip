@@ -625,27 +625,58 @@ void launch_sort(const Dims &dm, const int32_t *assign, int k, int32_t *perm, in
 // counts and moves each row left to its final offset (row by row: a row's
 // target never overlaps a later row's slot).
 
+template <int D>
 __global__ __launch_bounds__(256)
 void select_rows(const double *__restrict__ cq, const double *__restrict__ ck, const int32_t *__restrict__ size_k,
-                 int kq, int kk, int D, double top_p, double scale, int32_t *__restrict__ pair_ptr,
+                 int kq, int kk, double top_p, double scale, int32_t *__restrict__ pair_ptr,
                  int32_t *__restrict__ pair_idx) {
   __shared__ double prob[256];
   __shared__ double red[256];
   __shared__ double sp[256];   // probabilities in rank order
+  __shared__ double dotv[256];
   __shared__ int32_t order[256];
   __shared__ int32_t keep[256];
   __shared__ int32_t wc[4];
   __shared__ int32_t nsel;
   const int h = blockIdx.y, i = blockIdx.x, j = threadIdx.x;
+  const int lane = j & 63, wave = j >> 6;
+  // c_q,i . c_k,j: wave w takes clusters w, w + 4, ...; its lanes hold the
+  // query centroid's dims (D / 64 each) and read a key centroid's row
+  // coalesced, four rows in flight; a butterfly over the lanes sums each
+  // product.  This summation order is the library's own (a float64 dot
+  // product has no one order); the cut below depends on it only where the
+  // probabilities tie within rounding, which the tests audit against.
+  {
+    constexpr int PL = D / 64;
+    double a[PL];
+#pragma unroll
+    for (int u = 0; u < PL; ++u) a[u] = cq[((size_t)h * kq + i) * D + u * 64 + lane];
+    const double *kb = ck + (size_t)h * kk * D;
+    for (int j0 = wave; j0 < kk; j0 += 16) {
+      double part[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int jj = j0 + 4 * r;
+        double t = 0.0;
+        if (jj < kk) {
+#pragma unroll
+          for (int u = 0; u < PL; ++u) t = fma(a[u], kb[(size_t)jj * D + u * 64 + lane], t);
+        }
+        part[r] = t;
+      }
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) part[r] += __shfl_xor(part[r], off, 64);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (lane == 0 && j0 + 4 * r < kk) dotv[j0 + 4 * r] = part[r];
+    }
+  }
+  __syncthreads();
   const bool live = j < kk && size_k[h * kk + j] > 0;
   double l = -INFINITY;
-  if (live) {
-    const double *a = cq + ((size_t)h * kq + i) * D;
-    const double *b = ck + ((size_t)h * kk + j) * D;
-    double s = 0.0;
-    for (int e = 0; e < D; ++e) s = fma(a[e], b[e], s);
-    l = s * scale + log((double)size_k[h * kk + j]);
-  }
+  if (live) l = dotv[j] * scale + log((double)size_k[h * kk + j]);
   red[j] = l;
   __syncthreads();
   for (int off = 128; off > 0; off >>= 1) {
@@ -691,7 +722,6 @@ void select_rows(const double *__restrict__ cq, const double *__restrict__ ck, c
   __syncthreads();
   // the kept clusters in ascending order: ballot ranks within each wave,
   // plus the counts of earlier waves
-  const int lane = j & 63, wave = j >> 6;
   const bool kept = j < kk && keep[j];
   const uint64_t m = __ballot(kept);
   if (lane == 0) wc[wave] = __popcll(m);
@@ -939,8 +969,12 @@ hipError_t launch_cluster_permute(const Dims &dm, const int32_t *assign, int k, 
 hipError_t launch_select_pairs(const Dims &dm, const double *cq, const double *ck, const int32_t *size_k, int kq,
                                int kk, double top_p, double scale, int32_t *pair_ptr, int32_t *pair_idx,
                                hipStream_t st) {
-  hipLaunchKernelGGL(select_rows, dim3(kq, dm.H), dim3(256), 0, st, cq, ck, size_k, kq, kk, dm.d, top_p, scale,
-                     pair_ptr, pair_idx);
+  if (dm.d == 128)
+    hipLaunchKernelGGL(select_rows<128>, dim3(kq, dm.H), dim3(256), 0, st, cq, ck, size_k, kq, kk, top_p, scale,
+                       pair_ptr, pair_idx);
+  else
+    hipLaunchKernelGGL(select_rows<64>, dim3(kq, dm.H), dim3(256), 0, st, cq, ck, size_k, kq, kk, top_p, scale,
+                       pair_ptr, pair_idx);
   hipLaunchKernelGGL(select_compact, dim3(dm.H), dim3(256), 0, st, kq, kk, pair_ptr, pair_idx);
   return hipGetLastError();
 }
