@@ -180,7 +180,7 @@ vector ALUs (a float32 expression the oracle evaluates identically), so its MFMA
 
 COUNTER_KERNELS = ["layout_kernel", "vt_kernel", "profile_full_vt", "profile_temporal_vt", "profile_combine",
                    "block_mask_kernel", "fill_kernel", "attn_fwd_vt", "km_assign_bf3", "km_update", "sort_place",
-                   "sort_count", "permute_rows_kernel", "select_rows", "varlen_attn", "varlen_vt", "km_prep3",
+                   "sort_count", "permute_rows_kernel", "select_rows", "varlen_gather", "varlen_vt", "km_prep3",
                    "hva_assign", "hva_finalize", "hva_prep"]
 
 
@@ -411,14 +411,14 @@ def bench_svg2(args, steps=None, warmup=None, cpu=False):
             svg.svg_kmeans(k, w.kk, w.iters, ik, assign=ak, centroids=ck, sizes=sk, ws=ws_kk)
             svg.svg_cluster_permute(ak, w.kk, d, perm=pk, offs=ok, ws=ws_cp2)
             svg.svg_permute_rows(k, pk, out=kp)
-            svg.svg_permute_rows_vt(v, pk, out=vt)
+            svg.svg_permute_rows(v, pk, out=vp)
             join.record(side)
         svg.svg_kmeans(q, w.kq, w.iters, iq, assign=aq, centroids=cq, sizes=sq, ws=ws_kq)
         svg.svg_cluster_permute(aq, w.kq, d, perm=pq, offs=oq, ws=ws_cp)
         svg.svg_permute_rows(q, pq, out=qp)
         cur.wait_event(join)
         svg.svg_select_pairs(cq, ck, sk, w.top_p, pair_ptr=ptr, pair_idx=idx)
-        svg.svg_varlen_attn_vt(qp, kp, vt, oq, ok, ptr, idx, q_perm=pq, out=o)
+        svg.svg_varlen_attn(qp, kp, vp, oq, ok, ptr, idx, q_perm=pq, out=o, ws=ws_vl)
 
     def step(ev=None):
         def mark(j):
@@ -434,11 +434,11 @@ def bench_svg2(args, steps=None, warmup=None, cpu=False):
         mark(3)
         svg.svg_permute_rows(q, pq, out=qp)
         svg.svg_permute_rows(k, pk, out=kp)
-        svg.svg_permute_rows_vt(v, pk, out=vt)
+        svg.svg_permute_rows(v, pk, out=vp)
         mark(4)
         svg.svg_select_pairs(cq, ck, sk, w.top_p, pair_ptr=ptr, pair_idx=idx)
         mark(5)
-        svg.svg_varlen_attn_vt(qp, kp, vt, oq, ok, ptr, idx, q_perm=pq, out=o)
+        svg.svg_varlen_attn(qp, kp, vp, oq, ok, ptr, idx, q_perm=pq, out=o, ws=ws_vl)
         mark(6)
 
     steps = args.steps if steps is None else steps
@@ -504,21 +504,22 @@ def bench_svg2(args, steps=None, warmup=None, cpu=False):
     if not same(o_overlapped, o, idx_overlapped, idx):
         raise SystemExit("svg2: two-stream and one-stream steps disagree")
     stage_ms = {n: ev[j].elapsed_time(ev[j + 1]) for j, n in enumerate(names)}
-    # the row-major varlen kernel on the same lists, for comparison (same
-    # result up to bf16 rounding of the accumulation order)
-    svg.svg_permute_rows(v, pk, out=vp)
-    o_rm = torch.empty_like(o)
+    # the varlen kernel on the key-tiled V^T (64-key windows with key masks)
+    # on the same lists, for comparison (same result up to the bf16 rounding
+    # of the accumulation order)
+    svg.svg_permute_rows_vt(v, pk, out=vt)
+    o_vt = torch.empty_like(o)
     for _ in range(3):
-        svg.svg_varlen_attn(qp, kp, vp, oq, ok, ptr, idx, q_perm=pq, out=o_rm, ws=ws_vl)
+        svg.svg_varlen_attn_vt(qp, kp, vt, oq, ok, ptr, idx, q_perm=pq, out=o_vt)
     e0.record(stream)
     for _ in range(10):
-        svg.svg_varlen_attn(qp, kp, vp, oq, ok, ptr, idx, q_perm=pq, out=o_rm, ws=ws_vl)
+        svg.svg_varlen_attn_vt(qp, kp, vt, oq, ok, ptr, idx, q_perm=pq, out=o_vt)
     e1.record(stream)
     torch.cuda.synchronize()
-    rowmajor_ms = e0.elapsed_time(e1) / 10
-    rm_diff = (o_rm.float() - o.float()).abs().max().item()
-    if not rm_diff < 2e-2:
-        raise SystemExit(f"svg2: the two varlen kernels disagree (max abs {rm_diff})")
+    vt_ms = e0.elapsed_time(e1) / 10
+    vt_diff = (o_vt.float() - o.float()).abs().max().item()
+    if not vt_diff < 2e-2:
+        raise SystemExit(f"svg2: the two varlen kernels disagree (max abs {vt_diff})")
 
     # work: attention pairs from the selected clusters; bytes of the copies
     optr, oidx = ptr.cpu().numpy(), idx.cpu().numpy()
@@ -543,8 +544,8 @@ def bench_svg2(args, steps=None, warmup=None, cpu=False):
         "eager_two_stream_ms": round(eager_ms, 4),
         "graph": graph_note,
         "varlen_tflops": round(attn_flops / (stage_ms["varlen_attn"] * 1e-3) / 1e12, 2),
-        "varlen_rowmajor_kernel_ms": round(rowmajor_ms, 4),
-        "varlen_kernels_max_abs_diff": rm_diff,
+        "varlen_vt_windows_kernel_ms": round(vt_ms, 4),
+        "varlen_kernels_max_abs_diff": vt_diff,
         "gather_gbs": round(gather_bytes / (stage_ms["gather_qkv"] * 1e-3) / 1e9, 1),
         "kmeans_vector_tflops": round(km_flops / ((stage_ms["kmeans_q"] + stage_ms["kmeans_k"]) * 1e-3) / 1e12, 2),
     }
@@ -881,7 +882,7 @@ def bench_hva(args, steps=None, warmup=None):
     workload (13 x 1350 + 224 tokens, 8 heads, d = 64, bf16; windows of
     4 x 10 x 15 tokens for Q (36 + 1 clusters) and 2 x 6 x 9 for K (175 + 1),
     10 iterations, top-p 0.9).  Anchor step = local-window clustering of Q
-    and K, cluster sort, gathers (V into V^T), top-p pairs, varlen attention;
+    and K, cluster sort, gathers of Q, K and V, top-p pairs, varlen attention;
     refresh step = the same with the Lowe-flagged subset re-assigned on the
     next step's values instead of a full clustering.  Both run the key chain
     on a second stream.  For comparison: SVG2 k-means with as many clusters
@@ -912,8 +913,7 @@ def bench_hva(args, steps=None, warmup=None):
     rq, rk = (torch.empty(H, N, dtype=torch.uint8, device=dev) for _ in range(2))
     pq, pk, oq, ok = i32(H, N), i32(H, N), i32(H, kq + 1), i32(H, kk + 1)
     ptr, idx = i32(H, kq + 1), i32(H, kq * kk)
-    qp, kp, o = (torch.empty_like(q0) for _ in range(3))
-    vt = torch.empty(svg.svg_vt_elems(H, N, d), dtype=q0.dtype, device=dev)
+    qp, kp, vp, o = (torch.empty_like(q0) for _ in range(4))
     dm = svg.svg_dims(w.F, w.S, w.T, H, d)
     ws = lambda n: torch.empty(max(1, n), dtype=torch.uint8, device=dev)
     ws_q, ws_k = ws(svg.workspace_bytes(svg.SVG2_OP_HVA, dm, kq, svg2=True)), \
@@ -925,7 +925,7 @@ def bench_hva(args, steps=None, warmup=None):
 
     def attention_tail(q, k):
         svg.svg_select_pairs(cq, ck, sk, w.top_p, pair_ptr=ptr, pair_idx=idx)
-        svg.svg_varlen_attn_vt(qp, kp, vt, oq, ok, ptr, idx, q_perm=pq, out=o)
+        svg.svg_varlen_attn(qp, kp, vp, oq, ok, ptr, idx, q_perm=pq, out=o)
 
     def step(anchor):
         q, k = (q0, k0) if anchor else (q1, k1)
@@ -941,7 +941,7 @@ def bench_hva(args, steps=None, warmup=None):
                 svg.svg_hva_refresh(k, w.F, rows, cols, w.T, w.win_k, rk, ak, ck, sizes=sk, ws=ws_k)
             svg.svg_cluster_permute(ak, kk, d, perm=pk, offs=ok, ws=ws_c2)
             svg.svg_permute_rows(k, pk, out=kp)
-            svg.svg_permute_rows_vt(v, pk, out=vt)
+            svg.svg_permute_rows(v, pk, out=vp)
             join.record(side)
         if anchor:
             svg.svg_hva_cluster(q, w.F, rows, cols, w.T, w.win_q, w.iters, assign=aq, centroids=cq, sizes=sq,
@@ -1022,8 +1022,8 @@ def bench_hva(args, steps=None, warmup=None):
     kpq, koq = svg.svg_cluster_permute(ka, kq, d)
     kpk, kok = svg.svg_cluster_permute(kka, kk, d)
     kptr, kidx = svg.svg_select_pairs(kc_, kkc, kks, w.top_p)
-    o_km = svg.svg_varlen_attn_vt(svg.svg_permute_rows(q0, kpq), svg.svg_permute_rows(k0, kpk),
-                                  svg.svg_permute_rows_vt(v, kpk), koq, kok, kptr, kidx, q_perm=kpq)
+    o_km = svg.svg_varlen_attn(svg.svg_permute_rows(q0, kpq), svg.svg_permute_rows(k0, kpk),
+                               svg.svg_permute_rows(v, kpk), koq, kok, kptr, kidx, q_perm=kpq)
 
     # attention quality: each path's output against dense attention
     vt_id = svg.svg_layout_permute_vt(v, 1, N, 0, torch.zeros(H, dtype=torch.int32, device=dev))

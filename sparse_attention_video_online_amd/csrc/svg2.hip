@@ -7,9 +7,9 @@
 // k-means kernel, and runs a dynamic attention kernel.  Its install section:
 // block-sparse attention with varied block sizes.  HyperVAttention, sections
 // Problem and Surprising findings: cluster blocks are irregular, so tiled
-// kernels waste work.  The varlen kernel here therefore tiles the
-// concatenation of a query cluster's selected key ranges.  It does not tile
-// each cluster on its own.
+// kernels waste work.  The varlen attention (varlen_gather.hip) therefore
+// tiles the concatenation of a query cluster's selected key ranges.  It
+// does not tile each cluster on its own.
 #include <algorithm>
 
 #include "attn_core.h"
@@ -763,124 +763,6 @@ void select_compact(int kq, int kk, int32_t *__restrict__ pair_ptr, int32_t *__r
   if (tid == 0) ptr[kq] = run;
 }
 
-// ---------------------------------------------------------------------------
-// Variable-size block-sparse attention over cluster pairs.
-//
-// Work list: per head, each query cluster is cut into tiles of BQ rows.  A
-// work-group takes one tile and walks the concatenation of its cluster's
-// selected key ranges, in 64-key tiles.  Key j of that concatenation lives
-// at row k_offs[c] + (j - start of c's range) of Kp / Vp, for its cluster
-// c.  Only the last tile has keys past the end.
-
-struct QTile { int cluster, r0, r1, pad; };
-
-template <int BQ>
-__global__ __launch_bounds__(64)
-void varlen_tiles(const int32_t *__restrict__ q_offs, int kq, int max_tiles, QTile *__restrict__ tiles,
-                  int32_t *__restrict__ ntiles) {
-  const int h = blockIdx.x;
-  if (threadIdx.x != 0) return;
-  const int32_t *o = q_offs + (size_t)h * (kq + 1);
-  QTile *t = tiles + (size_t)h * max_tiles;
-  int n = 0;
-  for (int i = 0; i < kq; ++i)
-    for (int r = o[i]; r < o[i + 1]; r += BQ) t[n++] = QTile{i, r, min(o[i + 1], r + BQ), 0};
-  ntiles[h] = n;
-}
-
-constexpr int kMaxSel = 256;
-
-template <int D, int BQ>
-__global__ __launch_bounds__(BQ / 32 * 64, 2)
-void varlen_attn(const bf16_t *__restrict__ Qp, const bf16_t *__restrict__ Kp, const bf16_t *__restrict__ Vp,
-                 const int32_t *__restrict__ k_offs, int kq, int kk, const int32_t *__restrict__ pair_ptr,
-                 const int32_t *__restrict__ pair_idx, const int32_t *__restrict__ q_perm,
-                 const QTile *__restrict__ tiles, const int32_t *__restrict__ ntiles, int max_tiles, int N,
-                 float c, bf16_t *__restrict__ O) {
-  constexpr int NT = BQ / 32 * 64;
-  using C = core::Tile<D, NT>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE];
-  __shared__ int32_t seg_v[kMaxSel + 1];   // start of each selected range in the concatenation
-  __shared__ int32_t seg_row[kMaxSel];     // its first row in Kp / Vp
-
-  const int h = blockIdx.y, t = blockIdx.x;
-  if (t >= ntiles[h]) return;
-  const QTile qt = tiles[(size_t)h * max_tiles + t];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l32 = lane & 31, hi = lane >> 5;
-  const size_t hoff = (size_t)h * N * D;
-  const int32_t *ptr = pair_ptr + (size_t)h * (kq + 1);
-  const int32_t *sel = pair_idx + (size_t)h * kq * kk + ptr[qt.cluster];
-  const int nsel = ptr[qt.cluster + 1] - ptr[qt.cluster];
-  const int32_t *ko = k_offs + (size_t)h * (kk + 1);
-  if (tid == 0) {
-    int run = 0;
-    for (int m = 0; m < nsel; ++m) {
-      const int cl = sel[m];
-      seg_v[m] = run;
-      seg_row[m] = ko[cl];
-      run += ko[cl + 1] - ko[cl];
-    }
-    seg_v[nsel] = run;
-  }
-  __syncthreads();
-  const int nkeys = seg_v[nsel];
-
-  const int qrow = qt.r0 + wave * 32 + l32;
-  const bool qvalid = qrow < qt.r1;
-  bf16x8 qf[D / 16];
-  core::load_q<D>(Qp + hoff, qvalid ? qrow : -1, hi, qf);
-  f32x16 o[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
-
-  const int ntile = (nkeys + core::BK - 1) / core::BK;
-  auto rows_of = [&](int tile) {
-    return [=](int j) {
-      const int v = tile * core::BK + j;
-      if (v >= nkeys) return -1;
-      int lo = 0, hi_ = nsel - 1;  // last segment with seg_v <= v
-      while (lo < hi_) {
-        const int mid = (lo + hi_ + 1) >> 1;
-        if (seg_v[mid] <= v) lo = mid; else hi_ = mid - 1;
-      }
-      return seg_row[lo] + (v - seg_v[lo]);
-    };
-  };
-  core::Regs<D, NT> R;
-  if (ntile > 0) {
-    core::load_tile<D, NT>(Kp + hoff, Vp + hoff, tid, rows_of(0), R);
-    core::store_tile<D, NT>(smem, tid, R);
-  }
-  __syncthreads();
-  for (int it = 0; it < ntile; ++it) {
-    const bool more = it + 1 < ntile;
-    if (more) core::load_tile<D, NT>(Kp + hoff, Vp + hoff, tid, rows_of(it + 1), R);
-    const char *Ks = smem + (it & 1) * C::STAGE;
-    const char *Vs = Ks + C::KBYTES;
-    f32x16 s0, s1;
-    core::qk_tile<D, NT>(Ks, qf, l32, hi, s0, s1);
-    if ((it + 1) * core::BK > nkeys) core::mask_tail(s0, s1, nkeys - it * core::BK, hi);
-    bf16x8 pb[4];
-    const float alpha = core::softmax_step(s0, s1, c, m_run, l_run, pb);
-    core::rescale<D>(o, alpha);
-    core::pv_tile<D, NT>(Vs, pb, l32, hi, o);
-    if (more) core::store_tile<D, NT>(smem + ((it + 1) & 1) * C::STAGE, tid, R);
-    __syncthreads();
-  }
-  bf16_t *orow = nullptr;
-  if (qvalid) {
-    const int dst = q_perm ? q_perm[(size_t)h * N + qrow] : qrow;
-    orow = O + hoff + (size_t)dst * D;
-  }
-  core::store_o<D>(orow, o, l_run, hi);
-}
-
-template <int D>
-constexpr int varlen_bq() { return D == 128 ? 128 : 64; }
-
-int varlen_max_tiles(const Dims &dm, int kq, int bq) { return (dm.N + bq - 1) / bq + kq; }
 
 
 }  // namespace
@@ -979,33 +861,21 @@ hipError_t launch_select_pairs(const Dims &dm, const double *cq, const double *c
   return hipGetLastError();
 }
 
-size_t varlen_ws_bytes(const Dims &dm, int kq, int) {
-  const int bq = dm.d == 128 ? 128 : 64;
-  return align256((size_t)dm.H * varlen_max_tiles(dm, kq, bq) * sizeof(QTile)) + align256((size_t)dm.H * 4);
-}
+size_t varlen_ws_bytes(const Dims &, int, int) { return 0; }
+
+// varlen_gather.hip: the attention with the selected keys gathered by the
+// tile DMA (d = 64 or 128; no workspace)
+hipError_t launch_varlen_gather(const Dims &dm, const void *Qp, const void *Kp, const void *Vp,
+                                const int32_t *q_offs, const int32_t *k_offs, int kq, int kk,
+                                const int32_t *pair_ptr, const int32_t *pair_idx, const int32_t *q_perm,
+                                float scale, void *O, hipStream_t st);
 
 hipError_t launch_varlen(const Dims &dm, bool bf16, const void *Qp, const void *Kp, const void *Vp,
                          const int32_t *q_offs, const int32_t *k_offs, int kq, int kk, const int32_t *pair_ptr,
-                         const int32_t *pair_idx, const int32_t *q_perm, float scale, void *O, void *ws,
+                         const int32_t *pair_idx, const int32_t *q_perm, float scale, void *O, void *,
                          hipStream_t st) {
   if (!bf16) return hipErrorInvalidValue;
-  const float c = scale * kLog2e;
-  const int bq = dm.d == 128 ? 128 : 64;
-  const int mt = varlen_max_tiles(dm, kq, bq);
-  QTile *tiles = (QTile *)ws;
-  int32_t *ntiles = (int32_t *)((char *)ws + align256((size_t)dm.H * mt * sizeof(QTile)));
-  if (dm.d == 128) {
-    hipLaunchKernelGGL(varlen_tiles<128>, dim3(dm.H), dim3(64), 0, st, q_offs, kq, mt, tiles, ntiles);
-    hipLaunchKernelGGL((varlen_attn<128, 128>), dim3(mt, dm.H), dim3(256), 0, st, (const bf16_t *)Qp,
-                       (const bf16_t *)Kp, (const bf16_t *)Vp, k_offs, kq, kk, pair_ptr, pair_idx, q_perm, tiles,
-                       ntiles, mt, dm.N, c, (bf16_t *)O);
-  } else {
-    hipLaunchKernelGGL(varlen_tiles<64>, dim3(dm.H), dim3(64), 0, st, q_offs, kq, mt, tiles, ntiles);
-    hipLaunchKernelGGL((varlen_attn<64, 64>), dim3(mt, dm.H), dim3(128), 0, st, (const bf16_t *)Qp,
-                       (const bf16_t *)Kp, (const bf16_t *)Vp, k_offs, kq, kk, pair_ptr, pair_idx, q_perm, tiles,
-                       ntiles, mt, dm.N, c, (bf16_t *)O);
-  }
-  return hipGetLastError();
+  return launch_varlen_gather(dm, Qp, Kp, Vp, q_offs, k_offs, kq, kk, pair_ptr, pair_idx, q_perm, scale, O, st);
 }
 
 }  // namespace svgk
