@@ -124,8 +124,8 @@ svg_status svg_select_pairs(const svg_dims *dims, const double *cq, const double
  * no rounding to tiles.
  * Row n of the result is written to O[h][q_perm[h][n]] when q_perm is
  * non-NULL (back to original order), else to O[h][n].
- * One work-group takes 64 (d = 64) or 128 (d = 128) rows of one query
- * cluster and walks the concatenation of its selected key ranges in 64-key
+ * One work-group takes 128 rows of one query cluster and walks the
+ * concatenation of its selected key ranges in 64-key
  * tiles; the tile DMA gathers the K and V rows of each tile from a table of
  * source rows in LDS.  d = 64 or 128; q_offs, k_offs, pair_ptr and
  * pair_idx in range by contract (as svg_select_pairs and

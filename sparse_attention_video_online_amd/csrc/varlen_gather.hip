@@ -315,7 +315,10 @@ hipError_t launch_vg(const Dims &dm, const void *Qp, const void *Kp, const void 
                      const int32_t *k_offs, int kq, int kk, const int32_t *pair_ptr, const int32_t *pair_idx,
                      const int32_t *q_perm, float c, void *O, hipStream_t st) {
   // a grid row per head: at most ceil(N / BQ) + kq chunks (each cluster's
-  // last chunk may be partial); surplus work-groups exit at once
+  // last chunk may be partial); surplus work-groups exit at once.  128 rows
+  // (four waves) a work-group at both head dims: at d = 64 each K / V tile
+  // then serves twice the rows of 64-row chunks, 17% faster on the SVG2
+  // mixture lists despite the more ragged last chunk of a cluster.
   const dim3 grid((dm.N + BQ - 1) / BQ + kq, dm.H), block(BQ / 32 * 64);
   hipLaunchKernelGGL((varlen_gather<D, BQ>), grid, block, 0, st, (const bf16_t *)Qp, (const bf16_t *)Kp,
                      (const bf16_t *)Vp, q_offs, k_offs, kq, kk, pair_ptr, pair_idx, q_perm, dm.N, c, (bf16_t *)O);
@@ -333,7 +336,7 @@ hipError_t launch_varlen_gather(const Dims &dm, const void *Qp, const void *Kp, 
   if (dm.d == 128)
     return launch_vg<128, 128>(dm, Qp, Kp, Vp, q_offs, k_offs, kq, kk, pair_ptr, pair_idx, q_perm, c, O, st);
   if (dm.d == 64)
-    return launch_vg<64, 64>(dm, Qp, Kp, Vp, q_offs, k_offs, kq, kk, pair_ptr, pair_idx, q_perm, c, O, st);
+    return launch_vg<64, 128>(dm, Qp, Kp, Vp, q_offs, k_offs, kq, kk, pair_ptr, pair_idx, q_perm, c, O, st);
   return hipErrorInvalidValue;
 }
 
