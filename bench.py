@@ -721,6 +721,32 @@ def layer_bench(args, w, ks, wt, use_vt=True, steps=None, warmup=None, fp8_leg=F
     dense_ms = d0.elapsed_time(d1) / args.dense_reps
     print(f"[bench] {w.name}: dense attention {dense_ms:.3f} ms", file=sys.stderr, flush=True)
 
+    # the attention with K's permute fused into its tile DMA (K read from
+    # the original rows) against the separate K permute + attention
+    fused = None
+    if use_vt:
+        o_f = torch.empty_like(q)
+
+        def timed(fn, reps):
+            fn()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record(stream)
+            for _ in range(reps):
+                fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / reps
+        f_ms = timed(lambda: svg.svg_block_sparse_attn_csr_vt_fused(q, k, vt, row_ptr, kv_idx, labels, F, S, T, bq,
+                                                                     bk, out=o_f, ws=attn_ws), max(steps, 2))
+        kperm_ms = timed(lambda: svg.svg_layout_permute(k, F, S, T, labels, out=kp), max(steps, 2))
+        fused = {"attn_ms": round(f_ms, 4), "k_permute_ms": round(kperm_ms, 4),
+                 "separate_ms": round(attn_ms + kperm_ms, 4),
+                 "same_output": bool(torch.equal(o_f.view(torch.int16), o.view(torch.int16)))}
+        del o_f
+        print(f"[bench] {w.name}: attention with K gathered in the kernel {f_ms:.3f} ms "
+              f"(separate: {attn_ms:.3f} + K permute {kperm_ms:.3f})", file=sys.stderr, flush=True)
+
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
     result = {
         "metric": f"effective block-sparse attn TFLOP/s (whole SVG1 layer step) + speedup vs dense, N={N:,}",
@@ -748,6 +774,7 @@ def layer_bench(args, w, ks, wt, use_vt=True, steps=None, warmup=None, fp8_leg=F
         "speedup_vs_dense_attn": round(dense_ms / attn_ms, 3),
         "speedup_vs_dense_layer": round(dense_ms / ms_per_step, 3),
         "stage_ms": {kk: round(vv, 4) for kk, vv in stage_ms.items()},
+        "k_gather_fused": fused,
         "roofline": {"bound": "mfma",
                      "kernel": (f"attn_fwd_vt<{d},{bq}>" if use_vt else f"attn_fwd_mfma<{d},{bq}>") + " (block-sparse)",
                      "achieved": round(attn_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -1092,7 +1119,8 @@ def main():
         torch.cuda.empty_cache()
         cog = layer_bench(args, COG, COG.ks, COG.wt, True, steps=20, warmup=3)
         result["cogvideox_shape"] = {k_: cog[k_] for k_ in ("ms_per_step", "value", "attn_ms", "attn_tflops",
-                                                             "dense_ms", "speedup_vs_dense_attn", "stage_ms")}
+                                                             "dense_ms", "speedup_vs_dense_attn", "stage_ms",
+                                                             "k_gather_fused")}
         result["cogvideox_shape"]["tile_density"] = cog["config"]["tile_density"]
         torch.cuda.empty_cache()
         s2 = bench_svg2(args, steps=20, warmup=3)

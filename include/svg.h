@@ -246,7 +246,14 @@ svg_status svg_dense_attn(const svg_dims *dims, svg_dtype dtype,
  *   temporal head from frame-major row f*S + p and writes O back there.
  *   Same limits and errors as svg_block_sparse_attn_csr_vt; labels is a
  *   device pointer, int32[H], read on the device.
- * ws, ws_bytes (the two sparse entries): the groups of 256 query rows that
+ * svg_block_sparse_attn_csr_vt_fused: the same with K in the original token
+ *   order too (only Vt and the lists are in the executing layout): the
+ *   layout transformation of [SVG1] fused into the kernel's loads and
+ *   stores.  The tile DMA gathers each K tile's rows (row p*F + f of a
+ *   temporal head's video from frame-major row f*S + p) through a table of
+ *   source rows in LDS.  O equals svg_block_sparse_attn_csr_vt_layout's
+ *   with K = svg_layout_permute(K) bit for bit.  Same limits and errors.
+ * ws, ws_bytes (the three sparse entries): the groups of 256 query rows that
  *   hold a head's last 512 rows (its text rows, which keep every kv-block)
  *   are split by keys over several work-groups when nKB > 48: each part
  *   stores an unnormalised partial (O, maximum, row sum) in ws and a merge
@@ -271,6 +278,12 @@ svg_status svg_block_sparse_attn_csr_vt_layout(const svg_dims *dims, svg_dtype d
                                                const int32_t *labels, int32_t bq, int32_t bk,
                                                float softmax_scale, void *O, void *ws,
                                                size_t ws_bytes, void *stream);
+svg_status svg_block_sparse_attn_csr_vt_fused(const svg_dims *dims, svg_dtype dtype,
+                                              const void *Q, const void *K, const void *Vt,
+                                              const int32_t *row_ptr, const int32_t *kv_idx,
+                                              const int32_t *labels, int32_t bq, int32_t bk,
+                                              float softmax_scale, void *O, void *ws,
+                                              size_t ws_bytes, void *stream);
 svg_status svg_dense_attn_vt(const svg_dims *dims, svg_dtype dtype,
                              const void *Q, const void *K, const void *Vt,
                              int32_t bq, int32_t bk, float softmax_scale,

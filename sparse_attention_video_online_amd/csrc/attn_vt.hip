@@ -57,14 +57,14 @@ template <int D> constexpr int kPartStride = D + 4;
 // keys and the key-tiled value sums) that hold a centroid some q-block of the
 // group compensates; a q-block masks the centroids of its exact blocks and
 // the padding slots past the last block.
-template <int D, int BQ, bool DENSE, bool COMP = false>
+template <int D, int BQ, bool DENSE, bool COMP = false, bool KGATHER = false>
 __global__ __launch_bounds__(kWgRows * 2, 1)
 void attn_fwd_vt(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K, const bf16_t *__restrict__ Vt,
                  bf16_t *__restrict__ O, const int32_t *__restrict__ row_ptr,
                  const int32_t *__restrict__ kv_idx, int N, int nqb, int nkb, int ngrp,
                  float c /* scale * log2(e) */, const int32_t *__restrict__ labels, int qo_orig, int F, int S,
                  int nsplit, float *__restrict__ part, const bf16_t *__restrict__ Kc,
-                 const bf16_t *__restrict__ Vct) {
+                 const bf16_t *__restrict__ Vct, uint32_t fm = 0, int fk = 0) {
   constexpr int G = kWgRows / BQ;          // q-blocks per work-group
   using T = DTile<D>;
   constexpr int TB = T::TBYTES;            // K tile bytes == V^T tile bytes
@@ -249,6 +249,12 @@ void attn_fwd_vt(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K, con
       vt_attend<D, kNW>(nc, ent_c, prep_c, Kh, Vth, N, k0, k1, k2, V0, V1, V2, qf, wave, lane, c, o, m_run, l_run,
                         KvBlockRow{}, Centroids{Kc + (size_t)h * ntc * BK * D, Vct + (size_t)h * ntc * D * BK});
     }
+  } else if constexpr (KGATHER) {
+    // K in the original token order: its rows gathered by the tile DMA
+    __shared__ int kring[4 * BK];
+    const bool perm = F > 1 && (labels == nullptr || labels[h] == 1);
+    vt_attend<D, kNW>(ntile, ent_raw, prep, Kh, Vth, N, k0, k1, k2, V0, V1, V2, qf, wave, lane, c, o, m_run,
+                      l_run, GatherRows{kring, F, S, N, fm, fk, perm});
   } else {
     vt_attend<D, kNW>(ntile, ent_raw, prep, Kh, Vth, N, k0, k1, k2, V0, V1, V2, qf, wave, lane, c, o, m_run,
                       l_run);
@@ -320,7 +326,7 @@ int attn_vt_nsplit(const Dims &dm, int ngrp, bool dense) {
 template <int D, int BQ>
 hipError_t launch_vt(const Dims &dm, const void *Q, const void *K, const void *Vt, void *O,
                      const int32_t *row_ptr, const int32_t *kv_idx, float c, const int32_t *labels, int qo_orig,
-                     float *part, hipStream_t st) {
+                     float *part, hipStream_t st, bool k_orig = false) {
   constexpr int G = kWgRows / BQ;
   const int nqb = (dm.N + BQ - 1) / BQ, nkb = (dm.N + BK - 1) / BK;
   const int ngrp = (nqb + G - 1) / G;
@@ -330,7 +336,25 @@ hipError_t launch_vt(const Dims &dm, const void *Q, const void *K, const void *V
   // the caller gives the partials' workspace.
   const int nsplit = part == nullptr ? 1 : attn_vt_nsplit(dm, ngrp, row_ptr == nullptr);
   const int grid = dm.H * (ngrp + nlead * (nsplit - 1));
-  if (row_ptr == nullptr)
+  if (k_orig) {
+    // r / F by a multiply: fk = floor(log2 F), fm = ceil(2^(32+fk) / F); a
+    // power of two takes fm = 2^31 and fk - 1 (exact: a shift); F = 1 is
+    // the identity and never divides
+    const int F = dm.F > 1 ? dm.F : 2;
+    int fk = 0;
+    while ((2 << fk) <= F) ++fk;
+    uint32_t fm;
+    if ((F & (F - 1)) == 0) {
+      fm = 0x80000000u;
+      fk -= 1;
+    } else {
+      const uint64_t one = 1;
+      fm = (uint32_t)(((one << (32 + fk)) + F - 1) / F);
+    }
+    hipLaunchKernelGGL((attn_fwd_vt<D, BQ, false, false, true>), dim3(grid), dim3(kWgRows * 2), 0, st,
+                       (const bf16_t *)Q, (const bf16_t *)K, (const bf16_t *)Vt, (bf16_t *)O, row_ptr, kv_idx, dm.N,
+                       nqb, nkb, ngrp, c, labels, qo_orig, dm.F, dm.S, nsplit, part, nullptr, nullptr, fm, fk);
+  } else if (row_ptr == nullptr)
     hipLaunchKernelGGL((attn_fwd_vt<D, BQ, true>), dim3(grid), dim3(kWgRows * 2), 0, st, (const bf16_t *)Q,
                        (const bf16_t *)K, (const bf16_t *)Vt, (bf16_t *)O, row_ptr, kv_idx, dm.N, nqb, nkb, ngrp,
                        c, labels, qo_orig, dm.F, dm.S, nsplit, part, nullptr, nullptr);
@@ -400,6 +424,25 @@ hipError_t launch_attn_vt(const Dims &dm, const void *Q, const void *K, const vo
     return launch_vt<64, 128>(dm, Q, K, Vt, O, row_ptr, kv_idx, c, labels, qo, part, st);
   if (dm.d == 64 && bq == 64)
     return launch_vt<64, 64>(dm, Q, K, Vt, O, row_ptr, kv_idx, c, labels, qo, part, st);
+  return hipErrorInvalidValue;
+}
+
+// The block-sparse launch with Q, K and O in the original token order (K
+// rows gathered by the tile DMA).
+hipError_t launch_attn_vt_korig(const Dims &dm, const void *Q, const void *K, const void *Vt, void *O,
+                                const int32_t *row_ptr, const int32_t *kv_idx, int bq, int bk, float scale,
+                                const int32_t *labels, void *ws, hipStream_t st) {
+  const float c = scale * kLog2e;
+  float *const part = static_cast<float *>(ws);
+  if (bk != BK || row_ptr == nullptr) return hipErrorInvalidValue;
+  if (dm.d == 128 && bq == 128)
+    return launch_vt<128, 128>(dm, Q, K, Vt, O, row_ptr, kv_idx, c, labels, 1, part, st, true);
+  if (dm.d == 128 && bq == 64)
+    return launch_vt<128, 64>(dm, Q, K, Vt, O, row_ptr, kv_idx, c, labels, 1, part, st, true);
+  if (dm.d == 64 && bq == 128)
+    return launch_vt<64, 128>(dm, Q, K, Vt, O, row_ptr, kv_idx, c, labels, 1, part, st, true);
+  if (dm.d == 64 && bq == 64)
+    return launch_vt<64, 64>(dm, Q, K, Vt, O, row_ptr, kv_idx, c, labels, 1, part, st, true);
   return hipErrorInvalidValue;
 }
 

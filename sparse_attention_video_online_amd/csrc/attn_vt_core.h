@@ -19,6 +19,8 @@ constexpr bf16x2_t kOnesBf16x2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 // s_waitcnt with vmcnt = n and no wait on the other counters (gfx9 encoding).
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+// s_waitcnt with lgkmcnt = 0 and no wait on vmcnt or expcnt.
+constexpr int kWaitLgkm0 = 0xF | (0x3 << 14) | (0x7 << 4);
 
 // Key (0..63) of accumulator value r of block b (0: keys 0-31, 1: 32-63)
 // under the K row order pi.
@@ -242,6 +244,34 @@ struct KvBlockRow {
   __device__ int operator()(int e) const { return (e & 0xFFFFFF) * BK; }
 };
 
+// K rows gathered from the original token order (the layout permute fused
+// into the tile DMA).  Row r of the executing layout of a permuted head is
+// row p*F + f = r of the video, holding original row f*S + p; other heads'
+// rows and the text rows stay where they are.  Wave 0 writes the source rows
+// of a tile's 64 keys to one slot of a four-slot ring in LDS one step before
+// the tile's DMA (tiles it .. it+3 in the prologue, tile it+4 during step
+// it); every wave then takes its units' rows from the ring and issues the
+// DMA through one buffer resource over the head.  Keys past N read row N-1
+// (their scores are masked).
+// r / F is umulhi(r, fm) >> fk with fk = floor(log2 F), fm = ceil(2^(32+fk) / F):
+// the product overshoots r / F by less than r / 2^(32+fk) < 2^-(8+fk) < 1/F
+// for r < 2^24, so the floor is exact (N here is at most 2^19).
+struct GatherRows {
+  int *ring;     // LDS, 4 x 64 ints
+  int F, S, N;
+  uint32_t fm;
+  int fk;
+  bool perm;     // the head is permuted (temporal)
+  __device__ int src(int r) const {
+    r = r < N ? r : N - 1;
+    if (perm && r < F * S) {
+      const int p = (int)(__umulhi((uint32_t)r, fm) >> fk), f = r - p * F;
+      return f * S + p;
+    }
+    return r;
+  }
+};
+
 // Centroid tiles (the compensation of skipped blocks): an entry with
 // kCentFlag set names tile t = e & kCentTileMask of a second pair of tables,
 // 64 centroid keys of the head (row-major, like K) and the key-tiled V^T of
@@ -294,6 +324,25 @@ __device__ __forceinline__ void vt_attend(int nt, EntRaw ent_raw, Prep prep, con
   vt_offsets(l32, hi, voff);
   dma_offsets<D, NW, false>(wave, lane, kdma);
   vt_dma_offsets<D, NW>(wave, lane, vdma);
+  constexpr bool kGatherK = std::is_same<KRow, GatherRows>::value;
+  int kgr[kGatherK ? PK : 1], kgc[kGatherK ? PK : 1];   // row in the tile, byte in the row, of K unit i
+  if constexpr (kGatherK) {
+#pragma unroll
+    for (int i = 0; i < PK; ++i) {
+      kgr[i] = kdma[i] / T::ROWB;
+      kgc[i] = kdma[i] % T::ROWB;
+    }
+  }
+  // wave 0: the source rows of the tile with entry e into ring slot `slot`
+  auto kfill = [&](int slot, int e) {
+    if constexpr (kGatherK)
+      if (wave == 0) krow.ring[slot * BK + lane] = krow.src((e & 0xFFFFFF) * BK + lane);
+  };
+  // a gathered K tile whose rows are in ring slot `slot` (wave's share)
+  auto kgoff = [&](int slot, int i) -> int {
+    if constexpr (kGatherK) return krow.ring[slot * BK + kgr[i]] * T::ROWB + kgc[i];
+    else return 0;
+  };
   // A centroid pass continues the softmax state (o, m_run, l_run) of the
   // pass over the exact tiles before it; any other pass starts afresh.
   if constexpr (!Cent::kOn) {
@@ -310,7 +359,7 @@ __device__ __forceinline__ void vt_attend(int nt, EntRaw ent_raw, Prep prep, con
   // compile to the same code as before the K row became a parameter.)
   constexpr bool kBlockRows = std::is_same<KRow, KvBlockRow>::value;
   auto k_row = [&](int e) -> int {
-    if constexpr (kBlockRows) return 0;
+    if constexpr (kBlockRows || kGatherK) return 0;   // (gathered K takes its rows from the ring)
     else return krow(e);
   };
   auto dma_k = [&](int e, char *tile) {
@@ -347,9 +396,23 @@ __device__ __forceinline__ void vt_attend(int nt, EntRaw ent_raw, Prep prep, con
 
   // prologue: K(0..2), V(0..1) in flight; S(0) = K(0) Q^T
   int e0 = ent(0), e1 = ent(1), e2 = ent(2), e3 = ent(3);
-  dma_k(e0, k0);
-  dma_k(e1, k1);
-  dma_k(e2, k2);
+  if constexpr (kGatherK) {
+    kfill(0, e0);
+    kfill(1, e1);
+    kfill(2, e2);
+    kfill(3, e3);
+    __syncthreads();
+    const __amdgpu_buffer_rsrc_t rh = tile_rsrc(reinterpret_cast<const char *>(Kh), N * T::ROWB);
+    char *const kst0[3] = {k0, k1, k2};
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
+#pragma unroll
+      for (int i = 0; i < PK; ++i) dma_block(rh, kst0[t], wave * PK + i, kgoff(t, i));
+  } else {
+    dma_k(e0, k0);
+    dma_k(e1, k1);
+    dma_k(e2, k2);
+  }
   dma_v(e0, v0);
   dma_v(e1, v1);
   __builtin_amdgcn_s_waitcnt(0);
@@ -376,7 +439,12 @@ __device__ __forceinline__ void vt_attend(int nt, EntRaw ent_raw, Prep prep, con
     // queue up in the load unit and hold the waves at issue.
     const int kb_v = e2 & 0xFFFFFF;
     __amdgpu_buffer_rsrc_t rk, rv;
-    if constexpr (kBlockRows) {
+    int kgo[kGatherK ? PK : 1];
+    if constexpr (kGatherK) {
+      rk = tile_rsrc(reinterpret_cast<const char *>(Kh), N * T::ROWB);
+#pragma unroll
+      for (int i = 0; i < PK; ++i) kgo[i] = kgoff((it + 3) & 3, i);
+    } else if constexpr (kBlockRows) {
       const int kb_k = e3 & 0xFFFFFF;
       const int kleft = (N - kb_k * BK) * T::ROWB;
       rk = tile_rsrc(reinterpret_cast<const char *>(Kh) + (size_t)kb_k * TB, kleft < TB ? kleft : TB);
@@ -397,6 +465,7 @@ __device__ __forceinline__ void vt_attend(int nt, EntRaw ent_raw, Prep prep, con
       for (int i = 0; i < 2 * PK; ++i) {
         if (ks != i * (D / 16) / (2 * PK)) continue;
         if (i & 1) dma_block(rv, Vdst, wave * PK + (i >> 1), vdma[i >> 1]);
+        else if constexpr (kGatherK) dma_block(rk, Kdst, wave * PK + (i >> 1), kgo[i >> 1]);
         else dma_block(rk, Kdst, wave * PK + (i >> 1), kdma[i >> 1]);
       }
     };
@@ -470,6 +539,10 @@ __device__ __forceinline__ void vt_attend(int nt, EntRaw ent_raw, Prep prep, con
         n0 = mfma32(ka0, qf[q], n0);
         n1 = mfma32(ka1, qf[q], n1);
       }
+      // tile it+4's rows into the slot of tile it (read three steps ago),
+      // once the entry's LDS read has surely landed (the K operand reads
+      // issued after it have been waited for)
+      if (ks == 1) kfill(it & 3, e4_raw);
 #pragma unroll
       for (int e = 0; e < PER; e += 2) {
         const int idx = ks * PER + e;      // 0..31: s0 then s1
@@ -515,6 +588,8 @@ __device__ __forceinline__ void vt_attend(int nt, EntRaw ent_raw, Prep prep, con
 
     // (C) K(it+2) and V(it+1), issued one step ago, have landed once at most
     // this step's 2*PK DMAs are outstanding; then every wave's share is in
+    // (and, gathering K, wave 0's ring writes are done)
+    if constexpr (kGatherK) __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * PK));
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();

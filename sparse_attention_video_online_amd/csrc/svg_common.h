@@ -74,6 +74,11 @@ hipError_t launch_attn_vt(const Dims &dm, const void *Q, const void *K, const vo
                           const int32_t *row_ptr, const int32_t *kv_idx, int bq, int bk, float scale,
                           hipStream_t st, bool qo_orig = false, const int32_t *labels = nullptr,
                           void *ws = nullptr);
+// The sparse launch with Q, K and O in the original token order (K rows
+// gathered by the tile DMA; Vt and the lists in the executing layout).
+hipError_t launch_attn_vt_korig(const Dims &dm, const void *Q, const void *K, const void *Vt, void *O,
+                                const int32_t *row_ptr, const int32_t *kv_idx, int bq, int bk, float scale,
+                                const int32_t *labels, void *ws, hipStream_t st);
 // Bytes of ws the sparse launch splits its text groups into (0: no split).
 size_t attn_vt_ws_bytes(const Dims &dm, int bq, int bk);
 int attn_vt_max_kv_blocks();

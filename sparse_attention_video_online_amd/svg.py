@@ -64,6 +64,7 @@ SIGNATURES = {
     "svg_layout_permute_vt": [_DIMS, _I, _P, _P, _P, _P],
     "svg_block_sparse_attn_csr_vt": [_DIMS, _I, _P, _P, _P, _P, _P, _I, _I, _F, _P, _P, _Z, _P],
     "svg_block_sparse_attn_csr_vt_layout": [_DIMS, _I, _P, _P, _P, _P, _P, _P, _I, _I, _F, _P, _P, _Z, _P],
+    "svg_block_sparse_attn_csr_vt_fused": [_DIMS, _I, _P, _P, _P, _P, _P, _P, _I, _I, _F, _P, _P, _Z, _P],
     "svg_dense_attn_vt": [_DIMS, _I, _P, _P, _P, _I, _I, _F, _P, _P],
     "svg_ear_centroid_elems": [_DIMS],
     "svg_ear_block_stats": [_DIMS, _I, _P, _P, _P, _P, _P, _P, _P],
@@ -413,6 +414,22 @@ def svg_block_sparse_attn_csr_vt_layout(q, k, vt, row_ptr, kv_idx, labels, F, S,
                                                     _ptr(row_ptr), _ptr(kv_idx), _ptr(labels), bq, bk, scale,
                                                     _ptr(out), _ptr(ws), _bytes(ws), _stream()),
            "svg_block_sparse_attn_csr_vt_layout")
+    return out
+
+
+def svg_block_sparse_attn_csr_vt_fused(q, k, vt, row_ptr, kv_idx, labels, F, S, T, bq, bk, scale=-1.0,
+                                       out=None, ws=None):
+    """Q, K and the returned O in the original token order; Vt and the lists
+    in each head's executing layout per labels (None: every head temporal)."""
+    dm, dt = _qk_vt(q, k, vt, F, S, T)
+    _lists(row_ptr, kv_idx, q.shape[0], q.shape[1], bq)
+    _labels(labels, q.shape[0])
+    out = _out_like(out, q)
+    ws = _vt_ws(ws, q, dm, F, S, T, bq, bk)
+    _check(_lib.svg_block_sparse_attn_csr_vt_fused(ctypes.byref(dm), dt, _ptr(q), _ptr(k), _ptr(vt),
+                                                   _ptr(row_ptr), _ptr(kv_idx), _ptr(labels), bq, bk, scale,
+                                                   _ptr(out), _ptr(ws), _bytes(ws), _stream()),
+           "svg_block_sparse_attn_csr_vt_fused")
     return out
 
 

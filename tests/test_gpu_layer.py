@@ -46,7 +46,8 @@ def layer_inputs(w):
 
 
 def run_layer_step(w, q, k, v, sidx):
-    """The bench's step, with the bench's buffers and calls."""
+    """The bench's step, with the bench's buffers and calls; the attention
+    with K gathered in the kernel must give the same O bit for bit."""
     F, S, T, H, d, N, bq, bk = w.F, w.S, w.T, w.H, w.d, w.N, w.bq, w.bk
     dev = q.device
     labels = torch.empty(H, dtype=torch.int32, device=dev)
@@ -64,7 +65,11 @@ def run_layer_step(w, q, k, v, sidx):
     svg.svg_layout_permute_vt(v, F, S, T, labels, out=vt)
     svg.svg_block_sparse_attn_csr_vt_layout(q, kp, vt, row_ptr, kv_idx, labels, F, S, T, bq, bk, out=o,
                                             ws=attn_ws)
+    # the same attention with K's permute fused into the tile DMA: bit for bit
+    o2 = svg.svg_block_sparse_attn_csr_vt_fused(q, k, vt, row_ptr, kv_idx, labels, F, S, T, bq, bk, ws=attn_ws)
     torch.cuda.synchronize()
+    assert torch.equal(o2.view(torch.int16), o.view(torch.int16))
+    del o2
     return labels, bmask, row_ptr, kv_idx, o
 
 

@@ -170,6 +170,30 @@ def test_attention_vt_layout_fused_ragged_labels_null(F, S, T, d, bq):
         check_close(got[h], ref, BF16_MAX_ABS, BF16_REL_L2, f"fused ragged head {h}")
 
 
+@pytest.mark.parametrize("F,S,T,d,bq,labels", [(5, 23, 7, 64, 64, None), (3, 100, 0, 128, 128, [1, 0]),
+                                                 (7, 64, 33, 128, 64, [0, 1]), (8, 40, 5, 64, 128, None),
+                                                 (1, 300, 20, 128, 128, None), (33, 36, 16, 128, 128, [1, 1])])
+def test_attention_vt_fused_k_gather_bit_exact(F, S, T, d, bq, labels):
+    """svg_block_sparse_attn_csr_vt_fused (K too in the original order, its
+    rows gathered by the tile DMA) equals the _vt_layout entry on the
+    permuted K bit for bit: ragged N, F a power of two (8), F = 1, F = 33 and
+    a non-multiple of 64, labels NULL and mixed, a random bitmap."""
+    H, bk = 2, 64
+    N = F * S + T
+    q, k, v = random_qkv(H, N, d, seed=3 * N + d, dtype="bf16", scale=1.5)
+    nqb, nkb = -(-N // bq), -(-N // bk)
+    bm = (np.random.default_rng(N + 1).random((H, nqb, nkb)) < 0.6).astype(np.uint8)
+    row_ptr, kv_idx = csr(bm)
+    qd, kd, vd = (to_dev(x, "bf16") for x in (q, k, v))
+    lab = None if labels is None else ints(np.asarray(labels, np.int32))
+    kp = svg.svg_layout_permute(kd, F, S, T, lab)
+    vt = svg.svg_layout_permute_vt(vd, F, S, T, lab)
+    want = svg.svg_block_sparse_attn_csr_vt_layout(qd, kp, vt, row_ptr, kv_idx, lab, F, S, T, bq, bk)
+    o = svg.svg_block_sparse_attn_csr_vt_fused(qd, kd, vt, row_ptr, kv_idx, lab, F, S, T, bq, bk)
+    sync()
+    np.testing.assert_array_equal(to_host_bits(o), to_host_bits(want))
+
+
 def hunyuan_qblocks(w, rng, n_random=32):
     """q-blocks checked at the HunyuanVideo shape: the first ones, two that
     straddle the frame 0/1 boundary of a spatial head (3600 = 28.125 x 128),
