@@ -288,13 +288,14 @@ void km_prep3(const double *__restrict__ cent, int N, int k, int kpad, float *__
   km_tab3_row<D>(cv, e, j, kpad, t);
 }
 
-// kKmWaves waves per work-group, grid (G, H) with G work-groups per head.
+// kKmWaves waves per work-group (12: with the read-ahead below, 16 would
+// spill), grid (G, H) with G work-groups per head.
 // The head's table is copied to LDS once, then each wave takes 64-point
 // groups (two 32-point blocks) wave-major, group = pass * kKmWaves * G +
 // wave * G + blockIdx.x, so groups beyond the first pass spread over the
 // work-groups' first waves.  Each point also counts itself into its chunk's
 // histogram of the cluster sort.
-constexpr int kKmWaves = 16;
+constexpr int kKmWaves = 12;
 
 template <int D>
 __global__ __launch_bounds__(64 * kKmWaves)
@@ -349,16 +350,20 @@ void km_assign_bf3(const bf16_t *__restrict__ X, const float *__restrict__ tab, 
   float best0 = INFINITY, best1 = INFINITY;
   int arg0 = 0, arg1 = 0;
   for (int cb = 0; cb < kpad / 32; ++cb) {
-    f32x16 a0 = f32x16{}, a1 = f32x16{};
+    // the block's 12 table operands read together, then its 24 MFMAs (one
+    // LDS latency exposed per block, not one per MFMA pair): x.c as the
+    // three terms in order, 16 dims a step
     const bf16_t *ar = ct + (size_t)(cb * 32 + l32) * TB::ROWH + 8 * hi;
+    bf16x8 av[3 * (D / 16)];
 #pragma unroll
-    for (int tm = 0; tm < 3; ++tm) {
+    for (int i = 0; i < 3 * (D / 16); ++i)
+      av[i] = *reinterpret_cast<const bf16x8 *>(ar + (i / (D / 16)) * D + 16 * (i % (D / 16)));
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 a0 = f32x16{}, a1 = f32x16{};
 #pragma unroll
-      for (int st = 0; st < D / 16; ++st) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(ar + tm * D + 16 * st);
-        a0 = core::mfma32(a, xb0[st], a0);
-        a1 = core::mfma32(a, xb1[st], a1);
-      }
+    for (int i = 0; i < 3 * (D / 16); ++i) {
+      a0 = core::mfma32(av[i], xb0[i % (D / 16)], a0);
+      a1 = core::mfma32(av[i], xb1[i % (D / 16)], a1);
     }
     // lane rows: centroid cb*32 + 8*(r/4) + 4*hi + r%4, increasing in r
 #pragma unroll
@@ -458,19 +463,20 @@ void km_update(const T *__restrict__ X, const int32_t *__restrict__ perm, const 
         for (int i = 0; i < 4; ++i) acc[i] += (double)__uint_as_float(w[i]);
       }
     };
-    // four members a slot in flight: indices, then rows, then the adds in order
-    int n = o0 + slot;
-    for (; n + 3 * slots < o1; n += 4 * slots) {
+    // up to four members a slot in flight (a short cluster's last members
+    // too): indices, then rows, then the adds in order
+    for (int n = o0 + slot; n < o1; n += 4 * slots) {
       int idx[4];
       u32x4 w[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) idx[u] = p[n + u * slots];
+      for (int u = 0; u < 4; ++u) idx[u] = n + u * slots < o1 ? p[n + u * slots] : -1;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) w[u] = *reinterpret_cast<const u32x4 *>(Xh + (size_t)idx[u] * D);
+      for (int u = 0; u < 4; ++u)
+        if (idx[u] >= 0) w[u] = *reinterpret_cast<const u32x4 *>(Xh + (size_t)idx[u] * D);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) add_row(w[u]);
+      for (int u = 0; u < 4; ++u)
+        if (idx[u] >= 0) add_row(w[u]);
     }
-    for (; n < o1; n += slots) add_row(*reinterpret_cast<const u32x4 *>(Xh + (size_t)p[n] * D));
 #pragma unroll
     for (int i = 0; i < VE; ++i) part[slot * D + q * VE + i] = acc[i];
   }
