@@ -90,7 +90,7 @@ TRAFFIC_SOURCES = ["sparse_attention_video_online_amd/csrc/attn_vt.hip",
                    "sparse_attention_video_online_amd/csrc/attn_vt_core.h",
                    "sparse_attention_video_online_amd/csrc/attn_core.h",
                    "sparse_attention_video_online_amd/csrc/svg_common.h"]
-TRAFFIC_KERNEL = "attn_fwd_vt<128, 128, false, false>"
+TRAFFIC_KERNEL = "attn_fwd_vt<128, 128, false, false, false>"
 
 
 def record_traffic(fetch_csv, write_csv):
