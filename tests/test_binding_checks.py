@@ -105,3 +105,53 @@ def test_right_arguments_on_the_host_are_refused_as_host_tensors():
     x = bf16(H, N, d)
     raises(ValueError, "device tensors", svg.svg_layout_permute, x, F, S, T, i32(H))
     raises(ValueError, "device tensors", svg.svg_permute_rows, x, i32(H, N))
+
+
+def test_fused_ear_and_fp8_attention_arguments():
+    q, k = bf16(H, N, d), bf16(H, N, d)
+    nqb, nkb = -(-N // 64), -(-N // 64)
+    vt = bf16(svg.svg_vt_elems(H, N, d))
+    rp, ki = i32(H * nqb + 1), i32(4)
+    raises(TypeError, "labels must be torch.int32", svg.svg_block_sparse_attn_csr_vt_fused, q, k, vt, rp, ki,
+           torch.tensor([1, 1]), F, S, T, 64, 64)
+    raises(ValueError, "Vt must have", svg.svg_block_sparse_attn_csr_vt_fused, q, k, bf16(9), rp, ki, i32(H),
+           F, S, T, 64, 64)
+    raises(TypeError, "row_ptr must be torch.int32", svg.svg_block_sparse_attn_csr_vt_fused, q, k, vt,
+           torch.zeros(H * nqb + 1, dtype=torch.int64), ki, i32(H), F, S, T, 64, 64)
+    ne = svg.svg_ear_centroid_elems(H, N, d)
+    raises(ValueError, "Vt must have", svg.svg_ear_block_stats, k, bf16(5), F, S, T)
+    raises(TypeError, "kbar must be torch.float64", svg.svg_ear_block_stats, k, vt, F, S, T,
+           kbar=torch.zeros(H, d, nkb))
+    raises(ValueError, "block_mask must have", svg.svg_ear_route, q, i32(H), torch.zeros(H, d, nkb, dtype=torch.float64),
+           torch.zeros(H, nkb, dtype=torch.float64), torch.zeros(H, nqb, nkb - 1, dtype=torch.uint8), F, S, T, 64, 64, 16)
+    raises(ValueError, "Kc must have", svg.svg_block_sparse_attn_ear_vt_layout, q, k, vt, bf16(ne - 1), bf16(ne), rp,
+           ki, i32(H), F, S, T, 64, 64)
+    q8, k8 = torch.zeros(H, N, d, dtype=torch.uint8), torch.zeros(H, N, d, dtype=torch.uint8)
+    qs, ks = torch.zeros(H, N), torch.zeros(H, nkb)
+    raises(TypeError, "X must be torch.bfloat16", svg.svg_quantize_fp8_rows, torch.zeros(H, N, d))
+    raises(ValueError, "scale must have", svg.svg_layout_permute_fp8, k, F, S, T, None, None, torch.zeros(H, nkb + 1))
+    raises(TypeError, "Q8 must be torch.uint8", svg.svg_block_sparse_attn_fp8_vt_layout, q, qs, k8, ks, vt, rp, ki,
+           i32(H), F, S, T, 64, 64)
+    raises(ValueError, "kscale must have", svg.svg_dense_attn_fp8_vt, q8, qs, k8, torch.zeros(H, nkb - 1), vt,
+           F, S, T, 64, 64)
+
+
+def test_varlen_vt_and_hva_arguments():
+    x = bf16(H, N, d)
+    raises(TypeError, "perm must be torch.int32", svg.svg_permute_rows_vt, x, torch.zeros(H, N, dtype=torch.int64))
+    raises(ValueError, "Vt must have", svg.svg_permute_rows_vt, x, i32(H, N), bf16(7))
+    qo, ko = i32(H, 5), i32(H, 7)
+    raises(ValueError, "Vt must have", svg.svg_varlen_attn_vt, x, x, bf16(3), qo, ko, i32(H, 5), i32(H, 4 * 6))
+    raises(ValueError, "pair_idx must have", svg.svg_varlen_attn_vt, x, x, bf16(svg.svg_vt_elems(H, N, d)), qo, ko,
+           i32(H, 5), i32(H, 4 * 5))
+    rows, cols, win = 4, 4, (2, 2, 2)
+    raises(ValueError, r"F\*S\+T", svg.svg_hva_cluster, bf16(H, N, d), F, rows, cols, T, win, 2)
+    n = F * rows * cols + T
+    y = bf16(H, n, d)
+    k = svg.svg_hva_clusters(F, rows, cols, T, win, H, d)
+    raises(TypeError, "assign must be torch.int32", svg.svg_hva_cluster, y, F, rows, cols, T, win, 2,
+           assign=torch.zeros(H, n, dtype=torch.int64))
+    raises(ValueError, "centroids must have", svg.svg_hva_refresh, y, F, rows, cols, T, win,
+           torch.zeros(H, n, dtype=torch.uint8), i32(H, n), torch.zeros(H, k - 1, d, dtype=torch.float64))
+    raises(TypeError, "refresh must be torch.uint8", svg.svg_hva_refresh, y, F, rows, cols, T, win,
+           i32(H, n), i32(H, n), torch.zeros(H, k, d, dtype=torch.float64))
