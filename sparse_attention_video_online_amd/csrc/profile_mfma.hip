@@ -17,7 +17,8 @@
 // reach, each row masking the keys outside its own window; the text keys,
 // kept by every row, come from the full pass's text chunks.  Chunks are
 // merged afterwards (flash-decoding style), and the squared errors are
-// summed in fp64 in a fixed order.
+// summed in fp64 in a fixed order.  A narrow temporal window (a few keys
+// per frame) goes to a one-wave-per-row vector kernel instead.
 #include "attn_vt_core.h"
 
 namespace svgk {
@@ -347,6 +348,109 @@ void profile_temporal_vt(const bf16_t *__restrict__ Q, const bf16_t *__restrict_
   }
 }
 
+// The temporal pass for narrow windows (2 w_t + F <= kNarrowKeys video keys
+// a row, e.g. w_t = 32 at F = 13: 77), where a tile walk would compute
+// whole frames of keys that every row but a few masks.  One wave per sampled
+// video row, in float32 on the vector ALUs: each lane takes up to four keys
+// of the row's window (executing row r = p F + f is video row f S + p), the
+// scores are q.k summed over the dims in order, the wave's maximum and
+// sum are reduced, and each lane accumulates one or two dims of O over the
+// keys in order.  The partial (O unnormalised, the maximum, the sum) takes
+// the row's single temporal slot (Ct = 1), as the tile pass does per chunk.
+// Text rows keep every key (their temporal output is the full one) and are
+// skipped.
+constexpr int kNarrowKeys = 256;
+
+template <int D>
+__global__ __launch_bounds__(256)
+void profile_temporal_narrow(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K,
+                             const bf16_t *__restrict__ V, const int32_t *__restrict__ sample_idx, int n_s, int F,
+                             int S, int T, int wt, float c, float *__restrict__ part_o, float *__restrict__ part_ml) {
+  __shared__ float qs[4][D];
+  __shared__ float ps[4][kNarrowKeys];
+  __shared__ int rs[4][kNarrowKeys];
+  const int h = blockIdx.y, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int s = blockIdx.x * 4 + wave;
+  const int FS = F * S, N = FS + T;
+  const int i = s < n_s ? sample_idx[s] : FS;
+  if (i >= FS) return;                         // wave-uniform; no barrier below
+  const size_t hoff = (size_t)h * N * D;
+  const bf16_t *Kh = K + hoff, *Vh = V + hoff;
+  const int p = i % S;
+  const int r0 = max(0, p * F - wt), r1 = min(FS - 1, p * F + F - 1 + wt);
+  const int nk = r1 - r0 + 1;                  // <= 2 wt + F <= kNarrowKeys (checked by the launch)
+  for (int e = lane; e < D; e += 64) qs[wave][e] = bf16_to_f32(Q[hoff + (size_t)i * D + e]);
+  __builtin_amdgcn_wave_barrier();
+  // scores of the lane's keys j = lane + 64 u
+  float sc[4];
+  int src[4];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int j = lane + 64 * u;
+    sc[u] = -INFINITY;
+    src[u] = 0;
+    if (j < nk) {
+      const int r = r0 + j, pp = r / F;
+      src[u] = (r - pp * F) * S + pp;
+      const u32x4 *kr = reinterpret_cast<const u32x4 *>(Kh + (size_t)src[u] * D);
+      float acc = 0.f;
+#pragma unroll
+      for (int v = 0; v < D / 8; ++v) {
+        const u32x4 w = kr[v];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc = __builtin_fmaf(qs[wave][8 * v + 2 * q], __uint_as_float(w[q] << 16), acc);
+          acc = __builtin_fmaf(qs[wave][8 * v + 2 * q + 1], __uint_as_float(w[q] & 0xFFFF0000u), acc);
+        }
+      }
+      sc[u] = acc;
+      mx = fmaxf(mx, acc);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  float l = 0.f;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int j = lane + 64 * u;
+    const float pj = j < nk ? fast_exp2((sc[u] - mx) * c) : 0.f;
+    l += pj;
+    if (j < nk) {
+      ps[wave][j] = pj;
+      rs[wave][j] = src[u];
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off);
+  __builtin_amdgcn_wave_barrier();
+  // O: lane's dims lane (+ 64), keys in order, eight rows' loads in flight
+  constexpr int DL = D / 64;
+  float o[DL];
+#pragma unroll
+  for (int t = 0; t < DL; ++t) o[t] = 0.f;
+  for (int j0 = 0; j0 < nk; j0 += 8) {
+    float vv[8][DL];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int t = 0; t < DL; ++t)
+        vv[u][t] = j0 + u < nk ? bf16_to_f32(Vh[(size_t)rs[wave][j0 + u] * D + lane + 64 * t]) : 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (j0 + u < nk)
+#pragma unroll
+        for (int t = 0; t < DL; ++t) o[t] = __builtin_fmaf(ps[wave][j0 + u], vv[u][t], o[t]);
+  }
+  const size_t slot = (size_t)h * n_s + s;     // Ct = 1
+#pragma unroll
+  for (int t = 0; t < DL; ++t) part_o[slot * D + lane + 64 * t] = o[t];
+  if (lane == 0) {
+    part_ml[slot * 2] = mx;
+    part_ml[slot * 2 + 1] = l;
+  }
+}
+
 // Merge the chunks of one sampled row into its three outputs and take the
 // squared errors of the masked ones.  Full: every chunk of the full pass.
 // Spatial: the full pass's chunks of the frames within ks of the row's frame
@@ -503,8 +607,13 @@ hipError_t launch_profile_mfma(const Dims &dm, const void *Q, const void *K, con
   // the window of position 0 reaches the last video key and that of position
   // S - 1 the first (wt >= (S - 1) * F); text rows and keys are kept anyway.
   const int cover = ((ks >= dm.F - 1) ? 2 : 0) | (((long long)wt >= (long long)(dm.S - 1) * dm.F) ? 4 : 0);
-  hipLaunchKernelGGL(profile_order, dim3((n_s + 255) / 256), dim3(256), 0, st, sample_idx, n_s, dm.F, dm.S,
-                     p.ord_t);
+  // a narrow temporal window: one wave per row on the vector ALUs (no
+  // sample order, one temporal slot a row); else the tile pass
+  const bool narrow = !(cover & 4) && 2LL * wt + dm.F <= kNarrowKeys;
+  const int ct = narrow ? 1 : gt.nchunks;
+  if (!narrow)
+    hipLaunchKernelGGL(profile_order, dim3((n_s + 255) / 256), dim3(256), 0, st, sample_idx, n_s, dm.F, dm.S,
+                       p.ord_t);
   // key-tiled V^T of V in its own token order, every frame from a new tile
   const hipError_t ev = launch_layout_vt(dm, V, p.vt, nullptr, st, kVtFrames);
   if (ev != hipSuccess) return ev;
@@ -513,7 +622,11 @@ hipError_t launch_profile_mfma(const Dims &dm, const void *Q, const void *K, con
   hipLaunchKernelGGL((profile_full_vt<DD>), gridf, dim3(FNT), 0, st, (const bf16_t *)Q, (const bf16_t *)K, p.vt, \
                      sample_idx, n_s, dm.F, dm.S, dm.T, gf.nqg, gf.nbf, gf.nbt, gf.tpp, gf.P, gf.nchunks, c, p.fo, \
                      p.fml);                                                                                     \
-  if (!(cover & 4))                                                                                             \
+  if (narrow)                                                                                                   \
+    hipLaunchKernelGGL((profile_temporal_narrow<DD>), dim3((n_s + 3) / 4, dm.H), dim3(256), 0, st,                \
+                       (const bf16_t *)Q, (const bf16_t *)K, (const bf16_t *)V, sample_idx, n_s, dm.F, dm.S, dm.T, \
+                       wt, c, p.to, p.tml);                                                                     \
+  else if (!(cover & 4))                                                                                        \
     hipLaunchKernelGGL((profile_temporal_vt<DD>), gridt, dim3(FNT), 0, st, (const bf16_t *)Q, (const bf16_t *)K,   \
                        p.vt, sample_idx, p.ord_t, n_s, dm.F, dm.S, dm.T, wt, gf.nqg, gf.nbf, gf.nbt, gt.fpc,        \
                        gt.nchunks, c, p.to, p.tml)
@@ -524,7 +637,7 @@ hipError_t launch_profile_mfma(const Dims &dm, const void *Q, const void *K, con
   }
 #undef SVG_PROFILE_PASSES
   hipLaunchKernelGGL(profile_combine, dim3(n_s, dm.H), dim3(128), 0, st, p.fo, p.fml, gf.nchunks, gf.P, p.to, p.tml,
-                     gt.nchunks, sample_idx, n_s, dm.F, dm.S, ks, cover, dm.d, c, p.se);
+                     ct, sample_idx, n_s, dm.F, dm.S, ks, cover, dm.d, c, p.se);
   hipLaunchKernelGGL(profile_label, dim3(dm.H), dim3(256), 0, st, p.se, n_s, dm.d, labels, mse);
   return hipGetLastError();
 }
