@@ -458,13 +458,18 @@ void profile_temporal_narrow(const bf16_t *__restrict__ Q, const bf16_t *__restr
 // Temporal: the temporal pass's chunks.  A mask that keeps every key of
 // every row (cover bit 1: spatial, 2: temporal) has the full output as its
 // output, exactly: its merge is skipped (the temporal pass was not run).
-__global__ __launch_bounds__(128)
+// One wave per row (four rows per work-group), a lane per dim (two at
+// d = 128); the squared errors are summed over the dims by a fixed
+// butterfly in float64.
+template <int D>
+__global__ __launch_bounds__(256)
 void profile_combine(const float *__restrict__ fo, const float *__restrict__ fml, int Cf, int P,
                      const float *__restrict__ to, const float *__restrict__ tml, int Ct,
-                     const int32_t *__restrict__ sample_idx, int n_s, int F, int S, int ks, int cover, int D,
+                     const int32_t *__restrict__ sample_idx, int n_s, int F, int S, int ks, int cover,
                      float c, double *__restrict__ se) {
-  __shared__ double red[2][128];
-  const int h = blockIdx.y, s = blockIdx.x, e = threadIdx.x;
+  constexpr int DL = D / 64;
+  const int h = blockIdx.y, lane = threadIdx.x & 63, s = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (s >= n_s) return;                        // wave-uniform; no barrier below
   const int i = sample_idx[s];
   const bool text_i = i >= F * S;
   const int fi = text_i ? 0 : i / S;
@@ -482,79 +487,106 @@ void profile_combine(const float *__restrict__ fo, const float *__restrict__ fml
   // The merges run in chunk order; the loads of kB chunks go out together
   // (one chunk at a time leaves the loop waiting on memory).
   constexpr int kB = 8;
-  const int De = e < D ? e : 0;
-  double L0 = 0.0, A0 = 0.0, L1 = 0.0, A1 = 0.0;
-  auto add_full = [&](int ch, float m, float l, float x) {
+  double L0 = 0.0, L1 = 0.0, A0[DL], A1[DL];
+#pragma unroll
+  for (int t = 0; t < DL; ++t) A0[t] = A1[t] = 0.0;
+  auto add_full = [&](int ch, float m, float l, const float (&x)[DL]) {
     const float w0 = fast_exp2((m - M0r) * c);
     L0 += (double)w0 * l;
-    A0 += (double)w0 * x;
+#pragma unroll
+    for (int t = 0; t < DL; ++t) A0[t] += (double)w0 * x[t];
     if (in_window(ch)) {
       const float w1 = fast_exp2((m - M1r) * c);
       L1 += (double)w1 * l;
-      A1 += (double)w1 * x;
+#pragma unroll
+      for (int t = 0; t < DL; ++t) A1[t] += (double)w1 * x[t];
     }
   };
   int ch = 0;
   for (; ch + kB <= Cf; ch += kB) {
-    float m[kB], l[kB], x[kB];
+    float m[kB], l[kB], x[kB][DL];
 #pragma unroll
     for (int u = 0; u < kB; ++u) {
       m[u] = fml[(rf + ch + u) * 2];
       l[u] = fml[(rf + ch + u) * 2 + 1];
-      x[u] = fo[(rf + ch + u) * D + De];
+#pragma unroll
+      for (int t = 0; t < DL; ++t) x[u][t] = fo[(rf + ch + u) * D + lane + 64 * t];
     }
 #pragma unroll
     for (int u = 0; u < kB; ++u) add_full(ch + u, m[u], l[u], x[u]);
   }
-  for (; ch < Cf; ++ch) add_full(ch, fml[(rf + ch) * 2], fml[(rf + ch) * 2 + 1], fo[(rf + ch) * D + De]);
-  double out[3];
-  out[0] = L0 > 0.0 ? A0 / L0 : 0.0;
-  out[1] = L1 > 0.0 ? A1 / L1 : 0.0;
-  if ((cover & 4) || text_i) {
-    out[2] = out[0];
-  } else {
+  for (; ch < Cf; ++ch) {
+    float x[DL];
+#pragma unroll
+    for (int t = 0; t < DL; ++t) x[t] = fo[(rf + ch) * D + lane + 64 * t];
+    add_full(ch, fml[(rf + ch) * 2], fml[(rf + ch) * 2 + 1], x);
+  }
+  double out0[DL], out1[DL], out2[DL];
+#pragma unroll
+  for (int t = 0; t < DL; ++t) {
+    out0[t] = L0 > 0.0 ? A0[t] / L0 : 0.0;
+    out1[t] = L1 > 0.0 ? A1[t] / L1 : 0.0;
+    out2[t] = out0[t];
+  }
+  if (!((cover & 4) || text_i)) {
     // the temporal pass's frame partials, then the full pass's text chunks
     // (every row keeps the text keys)
     float M = -INFINITY;
-    for (int ch = 0; ch < Ct; ++ch) M = fmaxf(M, tml[(rt + ch) * 2]);
-    for (int ch = F * P; ch < Cf; ++ch) M = fmaxf(M, fml[(rf + ch) * 2]);
+    for (int ct = 0; ct < Ct; ++ct) M = fmaxf(M, tml[(rt + ct) * 2]);
+    for (int cc = F * P; cc < Cf; ++cc) M = fmaxf(M, fml[(rf + cc) * 2]);
     const float Mr = M == -INFINITY ? 0.f : M;
-    double L = 0.0, acc = 0.0;
-    auto add = [&](float m, float l, float x) {
+    double L = 0.0, acc[DL];
+#pragma unroll
+    for (int t = 0; t < DL; ++t) acc[t] = 0.0;
+    auto add = [&](float m, float l, const float (&x)[DL]) {
       const float w = fast_exp2((m - Mr) * c);
       L += (double)w * l;
-      acc += (double)w * x;
+#pragma unroll
+      for (int t = 0; t < DL; ++t) acc[t] += (double)w * x[t];
     };
     int ct = 0;
     for (; ct + kB <= Ct; ct += kB) {
-      float m[kB], l[kB], x[kB];
+      float m[kB], l[kB], x[kB][DL];
 #pragma unroll
       for (int u = 0; u < kB; ++u) {
         m[u] = tml[(rt + ct + u) * 2];
         l[u] = tml[(rt + ct + u) * 2 + 1];
-        x[u] = to[(rt + ct + u) * D + De];
+#pragma unroll
+        for (int t = 0; t < DL; ++t) x[u][t] = to[(rt + ct + u) * D + lane + 64 * t];
       }
 #pragma unroll
       for (int u = 0; u < kB; ++u) add(m[u], l[u], x[u]);
     }
-    for (; ct < Ct; ++ct) add(tml[(rt + ct) * 2], tml[(rt + ct) * 2 + 1], to[(rt + ct) * D + De]);
-    for (int ch = F * P; ch < Cf; ++ch) add(fml[(rf + ch) * 2], fml[(rf + ch) * 2 + 1], fo[(rf + ch) * D + De]);
-    out[2] = L > 0.0 ? acc / L : 0.0;
-  }
-  const double ds = out[1] - out[0], dt = out[2] - out[0];
-  red[0][e] = e < D ? ds * ds : 0.0;
-  red[1][e] = e < D ? dt * dt : 0.0;
-  __syncthreads();
-  for (int off = 64; off > 0; off >>= 1) {
-    if (e < off) {
-      red[0][e] += red[0][e + off];
-      red[1][e] += red[1][e + off];
+    for (; ct < Ct; ++ct) {
+      float x[DL];
+#pragma unroll
+      for (int t = 0; t < DL; ++t) x[t] = to[(rt + ct) * D + lane + 64 * t];
+      add(tml[(rt + ct) * 2], tml[(rt + ct) * 2 + 1], x);
     }
-    __syncthreads();
+    for (int cc = F * P; cc < Cf; ++cc) {
+      float x[DL];
+#pragma unroll
+      for (int t = 0; t < DL; ++t) x[t] = fo[(rf + cc) * D + lane + 64 * t];
+      add(fml[(rf + cc) * 2], fml[(rf + cc) * 2 + 1], x);
+    }
+#pragma unroll
+    for (int t = 0; t < DL; ++t) out2[t] = L > 0.0 ? acc[t] / L : 0.0;
   }
-  if (e == 0) {
-    se[((size_t)h * n_s + s) * 2] = red[0][0];
-    se[((size_t)h * n_s + s) * 2 + 1] = red[1][0];
+  double es = 0.0, et = 0.0;
+#pragma unroll
+  for (int t = 0; t < DL; ++t) {
+    const double ds = out1[t] - out0[t], dt = out2[t] - out0[t];
+    es += ds * ds;
+    et += dt * dt;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    es += __shfl_xor(es, off);
+    et += __shfl_xor(et, off);
+  }
+  if (lane == 0) {
+    se[((size_t)h * n_s + s) * 2] = es;
+    se[((size_t)h * n_s + s) * 2 + 1] = et;
   }
 }
 
@@ -636,8 +668,13 @@ hipError_t launch_profile_mfma(const Dims &dm, const void *Q, const void *K, con
     SVG_PROFILE_PASSES(64);
   }
 #undef SVG_PROFILE_PASSES
-  hipLaunchKernelGGL(profile_combine, dim3(n_s, dm.H), dim3(128), 0, st, p.fo, p.fml, gf.nchunks, gf.P, p.to, p.tml,
-                     ct, sample_idx, n_s, dm.F, dm.S, ks, cover, dm.d, c, p.se);
+  const dim3 gridc((n_s + 3) / 4, dm.H);
+  if (dm.d == 128)
+    hipLaunchKernelGGL(profile_combine<128>, gridc, dim3(256), 0, st, p.fo, p.fml, gf.nchunks, gf.P, p.to, p.tml, ct,
+                       sample_idx, n_s, dm.F, dm.S, ks, cover, c, p.se);
+  else
+    hipLaunchKernelGGL(profile_combine<64>, gridc, dim3(256), 0, st, p.fo, p.fml, gf.nchunks, gf.P, p.to, p.tml, ct,
+                       sample_idx, n_s, dm.F, dm.S, ks, cover, c, p.se);
   hipLaunchKernelGGL(profile_label, dim3(dm.H), dim3(256), 0, st, p.se, n_s, dm.d, labels, mse);
   return hipGetLastError();
 }
