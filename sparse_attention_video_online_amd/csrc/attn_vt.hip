@@ -250,11 +250,17 @@ void attn_fwd_vt(const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K, con
                         KvBlockRow{}, Centroids{Kc + (size_t)h * ntc * BK * D, Vct + (size_t)h * ntc * D * BK});
     }
   } else if constexpr (KGATHER) {
-    // K in the original token order: its rows gathered by the tile DMA
+    // K in the original token order: a permuted head's rows gathered by the
+    // tile DMA; any other head's K is already in its executing layout
     __shared__ int kring[4 * BK];
-    const bool perm = F > 1 && (labels == nullptr || labels[h] == 1);
-    vt_attend<D, kNW>(ntile, ent_raw, prep, Kh, Vth, N, k0, k1, k2, V0, V1, V2, qf, wave, lane, c, o, m_run,
-                      l_run, GatherRows{kring, F, S, N, fm, fk, perm});
+    if (F > 1 && (labels == nullptr || labels[h] == 1)) {
+      const int jq = lane / F;
+      vt_attend<D, kNW>(ntile, ent_raw, prep, Kh, Vth, N, k0, k1, k2, V0, V1, V2, qf, wave, lane, c, o, m_run,
+                        l_run, GatherRows{kring, F, S, N, fm, fk, jq, lane - jq * F});
+    } else {
+      vt_attend<D, kNW>(ntile, ent_raw, prep, Kh, Vth, N, k0, k1, k2, V0, V1, V2, qf, wave, lane, c, o, m_run,
+                        l_run);
+    }
   } else {
     vt_attend<D, kNW>(ntile, ent_raw, prep, Kh, Vth, N, k0, k1, k2, V0, V1, V2, qf, wave, lane, c, o, m_run,
                       l_run);

@@ -245,30 +245,34 @@ struct KvBlockRow {
 };
 
 // K rows gathered from the original token order (the layout permute fused
-// into the tile DMA).  Row r of the executing layout of a permuted head is
-// row p*F + f = r of the video, holding original row f*S + p; other heads'
-// rows and the text rows stay where they are.  Wave 0 writes the source rows
-// of a tile's 64 keys to one slot of a four-slot ring in LDS one step before
-// the tile's DMA (tiles it .. it+3 in the prologue, tile it+4 during step
-// it); every wave then takes its units' rows from the ring and issues the
-// DMA through one buffer resource over the head.  Keys past N read row N-1
-// (their scores are masked).
-// r / F is umulhi(r, fm) >> fk with fk = floor(log2 F), fm = ceil(2^(32+fk) / F):
-// the product overshoots r / F by less than r / 2^(32+fk) < 2^-(8+fk) < 1/F
-// for r < 2^24, so the floor is exact (N here is at most 2^19).
+// into the tile DMA), for a permuted (temporal) head: row r of the executing
+// layout is row p*F + f = r of the video, holding original row f*S + p; the
+// text rows stay where they are.  Wave 0 writes the source rows of a tile's
+// 64 keys to one slot of a four-slot ring in LDS one step before the tile's
+// DMA (tiles it .. it+3 in the prologue, tile it+4 during step it); every
+// wave then takes its units' rows from the ring and issues the DMA through
+// one buffer resource over the head.  Keys past N read row N-1 (their
+// scores are masked).
+// Lane j of a tile starting at r0: r0 = p0*F + f0 and j = jq*F + jr (jq, jr
+// the lane's constants), so r0 + j is position p0 + jq + carry, frame
+// f0 + jr - carry*F, with one carry at most.  r0 / F is umulhi(r0, fm) >> fk
+// with fk = floor(log2 F), fm = ceil(2^(32+fk) / F): the product overshoots
+// r0 / F by less than r0 / 2^(32+fk) < 2^-(8+fk) < 1/F for r0 < 2^24, so the
+// floor is exact (a head is under 2 GiB, so N < 2^24).
 struct GatherRows {
   int *ring;     // LDS, 4 x 64 ints
   int F, S, N;
   uint32_t fm;
   int fk;
-  bool perm;     // the head is permuted (temporal)
-  __device__ int src(int r) const {
-    r = r < N ? r : N - 1;
-    if (perm && r < F * S) {
-      const int p = (int)(__umulhi((uint32_t)r, fm) >> fk), f = r - p * F;
-      return f * S + p;
-    }
-    return r;
+  int jq, jr;    // the lane's j / F and j % F
+  __device__ int tile_src(int kb, int lane) const {
+    const int r0 = kb * 64;                   // wave-uniform
+    const int p0 = (int)(__umulhi((uint32_t)r0, fm) >> fk), f0 = r0 - p0 * F;
+    int f = f0 + jr;
+    const int cy = f >= F ? 1 : 0;
+    f -= cy * F;
+    const int r = r0 + lane;
+    return r < F * S ? f * S + p0 + jq + cy : min(r, N - 1);
   }
 };
 
@@ -336,7 +340,7 @@ __device__ __forceinline__ void vt_attend(int nt, EntRaw ent_raw, Prep prep, con
   // wave 0: the source rows of the tile with entry e into ring slot `slot`
   auto kfill = [&](int slot, int e) {
     if constexpr (kGatherK)
-      if (wave == 0) krow.ring[slot * BK + lane] = krow.src((e & 0xFFFFFF) * BK + lane);
+      if (wave == 0) krow.ring[slot * BK + lane] = krow.tile_src(__builtin_amdgcn_readfirstlane(e) & 0xFFFFFF, lane);
   };
   // a gathered K tile whose rows are in ring slot `slot` (wave's share)
   auto kgoff = [&](int slot, int i) -> int {
