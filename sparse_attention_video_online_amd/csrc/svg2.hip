@@ -646,38 +646,29 @@ void select_rows(const double *__restrict__ cq, const double *__restrict__ ck, c
   __shared__ int32_t nsel;
   const int h = blockIdx.y, i = blockIdx.x, j = threadIdx.x;
   const int lane = j & 63, wave = j >> 6;
-  // c_q,i . c_k,j: wave w takes clusters w, w + 4, ...; its lanes hold the
-  // query centroid's dims (D / 64 each) and read a key centroid's row
-  // coalesced, four rows in flight; a butterfly over the lanes sums each
-  // product.  This summation order is the library's own (a float64 dot
-  // product has no one order); the cut below depends on it only where the
-  // probabilities tie within rounding, which the tests audit against.
-  {
-    constexpr int PL = D / 64;
-    double a[PL];
+  // c_q,i . c_k,j: thread j takes key cluster j (kk <= 256) and sums the
+  // products over the dims in order, the query centroid broadcast from LDS
+  // and its own row's loads issued 32 dims at a time.  This summation order
+  // is the library's own (a float64 dot product has no one order); the cut
+  // below depends on it only where the probabilities tie within rounding,
+  // which the tests audit against.
+  if (j < D) red[j] = cq[((size_t)h * kq + i) * D + j];
+  __syncthreads();
+  if (j < kk) {
+    const double2 *kr = reinterpret_cast<const double2 *>(ck + ((size_t)h * kk + j) * D);
+    double t = 0.0;
 #pragma unroll
-    for (int u = 0; u < PL; ++u) a[u] = cq[((size_t)h * kq + i) * D + u * 64 + lane];
-    const double *kb = ck + (size_t)h * kk * D;
-    for (int j0 = wave; j0 < kk; j0 += 16) {
-      double part[4];
+    for (int c0 = 0; c0 < D / 2; c0 += 16) {
+      double2 w[16];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int jj = j0 + 4 * r;
-        double t = 0.0;
-        if (jj < kk) {
+      for (int u = 0; u < 16; ++u) w[u] = kr[c0 + u];
 #pragma unroll
-          for (int u = 0; u < PL; ++u) t = fma(a[u], kb[(size_t)jj * D + u * 64 + lane], t);
-        }
-        part[r] = t;
+      for (int u = 0; u < 16; ++u) {
+        t = fma(red[2 * (c0 + u)], w[u].x, t);
+        t = fma(red[2 * (c0 + u) + 1], w[u].y, t);
       }
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) part[r] += __shfl_xor(part[r], off, 64);
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (lane == 0 && j0 + 4 * r < kk) dotv[j0 + 4 * r] = part[r];
     }
+    dotv[j] = t;
   }
   __syncthreads();
   const bool live = j < kk && size_k[h * kk + j] > 0;
@@ -714,12 +705,25 @@ void select_rows(const double *__restrict__ cq, const double *__restrict__ ck, c
   __syncthreads();
   if (j == 0) {
     // the running sum in rank order, one add at a time; the first rank at
-    // which it reaches top_p closes the set (all live clusters if none)
+    // which it reaches top_p closes the set (all live clusters if none).
+    // The next eight terms load while eight are added.
     double run = 0.0;
     int n = nlive;
-    for (int r = 0; r < nlive; ++r) {
-      run += sp[r];
-      if (n == nlive && run >= top_p) n = r + 1;
+    double cur[8], nxt[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) cur[u] = u < nlive ? sp[u] : 0.0;
+    for (int r = 0; r < nlive; r += 8) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) nxt[u] = r + 8 + u < nlive ? sp[r + 8 + u] : 0.0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (r + u < nlive) {
+          run += cur[u];
+          if (n == nlive && run >= top_p) n = r + u + 1;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) cur[u] = nxt[u];
     }
     nsel = n;
   }
