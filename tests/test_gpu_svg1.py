@@ -406,12 +406,13 @@ def test_profile_frame_chunks_ragged(F, S, T, d):
         np.testing.assert_allclose(mse.double().cpu().numpy(), om, rtol=2e-2, atol=1e-6)
 
 
-@pytest.mark.parametrize("ks,wt", [(1, 100), (2, 0), (0, 1350 * 13)])
+@pytest.mark.parametrize("ks,wt", [(1, 100), (2, 0), (0, 1350 * 13), (0, 121), (0, 122)])
 def test_profile_mask_widths_against_oracle(ks, wt):
     """Masks of other widths (a temporal window that is not a multiple of F,
-    an empty one, one that covers every key) on unsorted samples that include
-    text rows: MSEs against the oracle, and labels where the oracle's margin
-    is clear."""
+    an empty one, one that covers every key, and the two sides of the
+    narrow-window kernel's bound: 2 w_t + F = 255 keys a row on the vector
+    path, 257 on the tile pass) on unsorted samples that include text rows:
+    MSEs against the oracle, and labels where the oracle's margin is clear."""
     w = COG
     g = inputs(w)
     rng = np.random.default_rng(ks * 1000 + wt)

@@ -172,12 +172,14 @@ def test_attention_vt_layout_fused_ragged_labels_null(F, S, T, d, bq):
 
 @pytest.mark.parametrize("F,S,T,d,bq,labels", [(5, 23, 7, 64, 64, None), (3, 100, 0, 128, 128, [1, 0]),
                                                  (7, 64, 33, 128, 64, [0, 1]), (8, 40, 5, 64, 128, None),
-                                                 (1, 300, 20, 128, 128, None), (33, 36, 16, 128, 128, [1, 1])])
+                                                 (1, 300, 20, 128, 128, None), (33, 36, 16, 128, 128, [1, 1]),
+                                                 (70, 9, 3, 64, 64, [1, 0]), (64, 5, 0, 64, 128, None)])
 def test_attention_vt_fused_k_gather_bit_exact(F, S, T, d, bq, labels):
     """svg_block_sparse_attn_csr_vt_fused (K too in the original order, its
     rows gathered by the tile DMA) equals the _vt_layout entry on the
-    permuted K bit for bit: ragged N, F a power of two (8), F = 1, F = 33 and
-    a non-multiple of 64, labels NULL and mixed, a random bitmap."""
+    permuted K bit for bit: ragged N, F a power of two (8, 64), F = 1, F = 33
+    and a non-multiple of 64, F = 70 (more frames than a tile has keys: a
+    lane's key offset is below F), labels NULL and mixed, a random bitmap."""
     H, bk = 2, 64
     N = F * S + T
     q, k, v = random_qkv(H, N, d, seed=3 * N + d, dtype="bf16", scale=1.5)
