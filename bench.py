@@ -601,12 +601,22 @@ def layer_bench(args, w, ks, wt, use_vt=True, steps=None, warmup=None, fp8_leg=F
     qp, kp, vp, op, o = (torch.empty_like(q) for _ in range(5))
     vt = torch.empty(svg.svg_vt_elems(H, N, d), dtype=q.dtype, device=dev) if use_vt else None
     attn_ws = svg.attn_vt_workspace(q, F, S, T, bq, bk) if use_vt else None
+    # K's permute: at d = 64 gathered by the attention's tile DMA (the whole
+    # CogVideoX-shaped step is ~4% faster so), at d = 128 a separate pass (the
+    # gathering kernel's attention is ~1.5% slower there than the permute
+    # it saves)
+    k_gather = use_vt and d == 64
     stream = torch.cuda.current_stream()
     ev_a0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ev_a1 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
 
     def attend():
-        if use_vt:
+        if k_gather:
+            # Q, K read and O written in the original token order (the
+            # permutes happen in the kernel's row indexing and tile DMA)
+            svg.svg_block_sparse_attn_csr_vt_fused(q, k, vt, row_ptr, kv_idx, labels, F, S, T, bq, bk, out=o,
+                                                   ws=attn_ws)
+        elif use_vt:
             # Q read and O written in the original token order (the Q permute
             # and the O unpermute happen in the kernel's row indexing)
             svg.svg_block_sparse_attn_csr_vt_layout(q, kp, vt, row_ptr, kv_idx, labels, F, S, T, bq, bk, out=o,
@@ -630,7 +640,8 @@ def layer_bench(args, w, ks, wt, use_vt=True, steps=None, warmup=None, fp8_leg=F
         front(mark)
         if not use_vt:
             svg.svg_layout_permute(q, F, S, T, labels, out=qp)
-        svg.svg_layout_permute(k, F, S, T, labels, out=kp)
+        if not k_gather:
+            svg.svg_layout_permute(k, F, S, T, labels, out=kp)
         if use_vt:
             svg.svg_layout_permute_vt(v, F, S, T, labels, out=vt)
         else:
@@ -683,7 +694,9 @@ def layer_bench(args, w, ks, wt, use_vt=True, steps=None, warmup=None, fp8_leg=F
     se = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
     step(None, se)
     torch.cuda.synchronize()
-    if use_vt:  # Q and O stay in the original order: permute K and V (into Vt) only
+    if k_gather:  # Q, K and O stay in the original order: V into Vt only
+        names = ["profile", "mask_and_lists", "permute_vt", "attention"]
+    elif use_vt:  # Q and O stay in the original order: permute K and V (into Vt) only
         names = ["profile", "mask_and_lists", "permute_k_vt", "attention"]
     else:
         names = ["profile", "mask_and_lists", "permute_qkv", "attention", "unpermute_o"]
@@ -701,6 +714,8 @@ def layer_bench(args, w, ks, wt, use_vt=True, steps=None, warmup=None, fp8_leg=F
 
     # dense baseline: this library's attention with every tile kept
     dense = torch.empty_like(q)
+    if k_gather:   # the executing-layout K of the last step, for the baseline and the comparison below
+        svg.svg_layout_permute(k, F, S, T, labels, out=kp)
 
     def dense_attend():
         if use_vt:
@@ -721,8 +736,9 @@ def layer_bench(args, w, ks, wt, use_vt=True, steps=None, warmup=None, fp8_leg=F
     dense_ms = d0.elapsed_time(d1) / args.dense_reps
     print(f"[bench] {w.name}: dense attention {dense_ms:.3f} ms", file=sys.stderr, flush=True)
 
-    # the attention with K's permute fused into its tile DMA (K read from
-    # the original rows) against the separate K permute + attention
+    # the two forms of K's permute side by side: gathered by the attention's
+    # tile DMA (K read from the original rows) and a separate pass before
+    # the attention on the permuted copy; the step uses the one k_gather names
     fused = None
     if use_vt:
         o_f = torch.empty_like(q)
@@ -737,15 +753,24 @@ def layer_bench(args, w, ks, wt, use_vt=True, steps=None, warmup=None, fp8_leg=F
             b.record(stream)
             torch.cuda.synchronize()
             return a.elapsed_time(b) / reps
+        reps = max(steps, 2)
         f_ms = timed(lambda: svg.svg_block_sparse_attn_csr_vt_fused(q, k, vt, row_ptr, kv_idx, labels, F, S, T, bq,
-                                                                     bk, out=o_f, ws=attn_ws), max(steps, 2))
-        kperm_ms = timed(lambda: svg.svg_layout_permute(k, F, S, T, labels, out=kp), max(steps, 2))
-        fused = {"attn_ms": round(f_ms, 4), "k_permute_ms": round(kperm_ms, 4),
-                 "separate_ms": round(attn_ms + kperm_ms, 4),
-                 "same_output": bool(torch.equal(o_f.view(torch.int16), o.view(torch.int16)))}
-        del o_f
-        print(f"[bench] {w.name}: attention with K gathered in the kernel {f_ms:.3f} ms "
-              f"(separate: {attn_ms:.3f} + K permute {kperm_ms:.3f})", file=sys.stderr, flush=True)
+                                                                     bk, out=o_f, ws=attn_ws), reps)
+        l_ms = timed(lambda: svg.svg_block_sparse_attn_csr_vt_layout(q, kp, vt, row_ptr, kv_idx, labels, F, S, T, bq,
+                                                                      bk, out=o_f, ws=attn_ws), reps)
+        kperm_ms = timed(lambda: svg.svg_layout_permute(k, F, S, T, labels, out=kp), reps)
+        o_l = torch.empty_like(q)
+        svg.svg_block_sparse_attn_csr_vt_fused(q, k, vt, row_ptr, kv_idx, labels, F, S, T, bq, bk, out=o_f,
+                                               ws=attn_ws)
+        svg.svg_block_sparse_attn_csr_vt_layout(q, kp, vt, row_ptr, kv_idx, labels, F, S, T, bq, bk, out=o_l,
+                                                ws=attn_ws)
+        torch.cuda.synchronize()
+        fused = {"used_in_step": k_gather, "attn_ms": round(f_ms, 4), "layout_attn_ms": round(l_ms, 4),
+                 "k_permute_ms": round(kperm_ms, 4), "separate_ms": round(l_ms + kperm_ms, 4),
+                 "same_output": bool(torch.equal(o_f.view(torch.int16), o_l.view(torch.int16)))}
+        del o_f, o_l
+        print(f"[bench] {w.name}: attention with K gathered in the kernel {f_ms:.3f} ms, on the permuted K "
+              f"{l_ms:.3f} ms + K permute {kperm_ms:.3f} ms", file=sys.stderr, flush=True)
 
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
     result = {
@@ -766,6 +791,8 @@ def layer_bench(args, w, ks, wt, use_vt=True, steps=None, warmup=None, fp8_leg=F
                    "tile_density": round(density, 4), "kept_tiles": tiles,
                    "labels": "".join(str(int(x)) for x in lab_host), "v_layout": "vt" if use_vt else "rowmajor",
                    "qo_layout": "original order, permuted in the attention kernel" if use_vt else "permuted",
+                   "k_layout": ("original order, gathered by the attention's tile DMA" if k_gather
+                                else "permuted by a separate pass"),
                    "parallelism": "single GPU"},
         "attn_ms": round(attn_ms, 4),
         "attn_tflops": round(attn_tflops, 2),
