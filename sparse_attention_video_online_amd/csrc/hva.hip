@@ -61,10 +61,12 @@ void hva_prep(int k, const double *__restrict__ cent, float *__restrict__ c32, d
 // cluster is not among its candidates searches as well).
 //
 // The search keeps two candidates' sums in flight (independent chains, each
-// still summed over the dims in order).  The member sums are then formed
-// with the work-group's two waves each walking half of its tokens, one dim
-// (d = 64) or two per lane: one LDS float64 add per token and dim with no
-// two lanes on one address.
+// still summed over the dims in order).  For the member sums each token's
+// row is also staged in LDS and the tokens are ordered by their chosen
+// candidate (a counting sort in LDS); the work-group's two waves each walk
+// half of that order, one dim (d = 64) or two per lane, adding runs of one
+// candidate in registers and each run to the head's float64 sums with one
+// global atomic per dim.
 template <int D>
 __global__ __launch_bounds__(kHvaThreads)
 void hva_assign(const bf16_t *__restrict__ X, HvaGrid g, int chunks, int N, int mode, const float *__restrict__ c32,
@@ -72,10 +74,10 @@ void hva_assign(const bf16_t *__restrict__ X, HvaGrid g, int chunks, int N, int 
                 float r2, double *__restrict__ sums, int32_t *__restrict__ counts) {
 #pragma clang fp contract(off)
   __shared__ float cm[kHvaCand * D];        // candidate centroids, float32
-  __shared__ double acc[kHvaCand * D];      // member sums per candidate slot
-  __shared__ int cnt[kHvaCand];
+  __shared__ __attribute__((aligned(16))) bf16_t xs[kHvaThreads * D];   // the tokens' rows
+  __shared__ int cnt[kHvaCand], cur[kHvaCand];
   __shared__ int cid[kHvaCand];
-  __shared__ int trow[kHvaThreads], tslot[kHvaThreads];
+  __shared__ int tslot[kHvaThreads], ord[kHvaThreads];
   __shared__ int s_ncand, s_own;
   const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S = g.rows * g.cols;
@@ -121,7 +123,6 @@ void hva_assign(const bf16_t *__restrict__ X, HvaGrid g, int chunks, int N, int 
     s_ncand = n;
     s_own = own;
   }
-  for (int i = tid; i < kHvaCand * D; i += kHvaThreads) acc[i] = 0.0;
   if (tid < kHvaCand) cnt[tid] = 0;
   __syncthreads();
   const int ncand = s_ncand, own = s_own;
@@ -146,6 +147,8 @@ void hva_assign(const bf16_t *__restrict__ X, HvaGrid g, int chunks, int N, int 
     u32x4 xv[D / 8];
 #pragma unroll
     for (int v = 0; v < D / 8; ++v) xv[v] = src[v];
+#pragma unroll
+    for (int v = 0; v < D / 8; ++v) reinterpret_cast<u32x4 *>(xs + tid * D)[v] = xv[v];
     int slot = text ? 0 : own;
     bool look = search;
     if (search && mode == kHvaRefresh) {
@@ -211,34 +214,71 @@ void hva_assign(const bf16_t *__restrict__ X, HvaGrid g, int chunks, int N, int 
       flag_out[(size_t)h * N + row] = 0;
     }
     assign[(size_t)h * N + row] = cid[slot];
-    trow[tid] = row;
     tslot[tid] = slot;
     __hip_atomic_fetch_add(&cnt[slot], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
   __syncthreads();
-  // member sums: each wave walks half of the tokens (coalesced row reads,
-  // four in flight), lanes over the dims (distinct LDS addresses in a wave)
-  constexpr int PL = D / 64;                  // dims per lane
-#pragma unroll 4
-  for (int j = wave; j < nt; j += kHvaThreads / 64) {
-    const int sl = tslot[j];
-    const bf16_t *xr = Xh + (size_t)trow[j] * D + PL * lane;
-    if constexpr (PL == 1) {
-      const float v = __uint_as_float((uint32_t)(*reinterpret_cast<const uint16_t *>(xr)) << 16);
-      __hip_atomic_fetch_add(&acc[sl * D + lane], (double)v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    } else {
-      const uint32_t u = *reinterpret_cast<const uint32_t *>(xr);
-      __hip_atomic_fetch_add(&acc[sl * D + 2 * lane], (double)__uint_as_float(u << 16), __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_WORKGROUP);
-      __hip_atomic_fetch_add(&acc[sl * D + 2 * lane + 1], (double)__uint_as_float(u & 0xFFFF0000u),
-                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  // the tokens in order of their candidate (any order within one)
+  if (tid == 0) {
+    int run = 0;
+    for (int sl = 0; sl < ncand; ++sl) {
+      cur[sl] = run;
+      run += cnt[sl];
     }
   }
   __syncthreads();
-  for (int i = tid; i < ncand * D; i += kHvaThreads) {
-    const int sl = i / D;
-    if (cnt[sl] > 0) unsafeAtomicAdd(&sums[(cbase + cid[sl]) * D + (i % D)], acc[i]);
+  if (tid < nt)
+    ord[__hip_atomic_fetch_add(&cur[tslot[tid]], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)] = tid;
+  __syncthreads();
+  // member sums: each wave walks half of that order, lanes over the dims;
+  // a run of one candidate adds up in registers (float64) and goes to the
+  // head's sums when the candidate changes
+  constexpr int PL = D / 64;                  // dims per lane
+  const int half = (nt + 1) / 2, p0 = wave * half, p1 = min(nt, p0 + half);
+  double racc[PL];
+#pragma unroll
+  for (int u = 0; u < PL; ++u) racc[u] = 0.0;
+  int rs = -1;                               // the run's candidate (wave-uniform)
+  auto flush = [&]() {
+    if (rs >= 0) {
+#pragma unroll
+      for (int u = 0; u < PL; ++u) unsafeAtomicAdd(&sums[(cbase + cid[rs]) * D + PL * lane + u], racc[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < PL; ++u) racc[u] = 0.0;
+  };
+  // lane q holds the wave's q-th token and its candidate (half <= 64); the
+  // loop reads them back with readlane and loads eight rows' values at a time
+  const int np = p1 - p0;
+  const int my_tk = lane < np ? ord[p0 + lane] : 0;
+  const int my_sl = lane < np ? tslot[my_tk] : -1;
+  for (int q0 = 0; q0 < np; q0 += 8) {
+    float val[8][PL];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int tk = __builtin_amdgcn_readlane(my_tk, q0 + u < np ? q0 + u : 0);
+      const bf16_t *xr = xs + tk * D + PL * lane;
+      if constexpr (PL == 1) {
+        val[u][0] = __uint_as_float((uint32_t)(*reinterpret_cast<const uint16_t *>(xr)) << 16);
+      } else {
+        const uint32_t w = *reinterpret_cast<const uint32_t *>(xr);
+        val[u][0] = __uint_as_float(w << 16);
+        val[u][1] = __uint_as_float(w & 0xFFFF0000u);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (q0 + u >= np) break;
+      const int sl = __builtin_amdgcn_readlane(my_sl, q0 + u);
+      if (sl != rs) {
+        flush();
+        rs = sl;
+      }
+#pragma unroll
+      for (int t = 0; t < PL; ++t) racc[t] += (double)val[u][t];
+    }
   }
+  flush();
   if (tid < ncand && cnt[tid] > 0) atomicAdd(&counts[cbase + cid[tid]], cnt[tid]);
 }
 
