@@ -124,19 +124,30 @@ void ear_route(const bf16_t *__restrict__ Q, const int32_t *__restrict__ labels,
   //    original order as the layout permute maps them)
   if (wave < qpw && Qw < nqb) {
     const int r0 = Qw * bq, r1 = min(N, r0 + bq);
+    // rows in batches of 32: their loads go out together, then the adds in
+    // row order
     double acc[D / 64];
 #pragma unroll
     for (int u = 0; u < D / 64; ++u) acc[u] = 0.0;
-#pragma unroll 8
-    for (int r = r0; r < r1; ++r) {
-      int src = r;
-      if (perm && r < F * S) {
-        const int p = r / F, f = r - p * F;
-        src = f * S + p;
-      }
-      const bf16_t *qr = Q + ((size_t)h * N + src) * D;
+    for (int rb = r0; rb < r1; rb += 32) {
+      float xv[32][D / 64];
 #pragma unroll
-      for (int u = 0; u < D / 64; ++u) acc[u] += (double)bf16_to_f32(qr[64 * u + lane]);
+      for (int j = 0; j < 32; ++j) {
+        const int r = rb + j;
+        int src = r < r1 ? r : r0;
+        if (perm && src < F * S) {
+          const int p = src / F, f = src - p * F;
+          src = f * S + p;
+        }
+        const bf16_t *qr = Q + ((size_t)h * N + src) * D;
+#pragma unroll
+        for (int u = 0; u < D / 64; ++u) xv[j][u] = bf16_to_f32(qr[64 * u + lane]);
+      }
+#pragma unroll
+      for (int j = 0; j < 32; ++j)
+        if (rb + j < r1)
+#pragma unroll
+          for (int u = 0; u < D / 64; ++u) acc[u] += (double)xv[j][u];
     }
     double n2 = 0.0;
 #pragma unroll
