@@ -208,33 +208,77 @@ void ear_route(const bf16_t *__restrict__ Q, const int32_t *__restrict__ labels,
   }
   __syncthreads();
   // 3. wave w picks route_k candidates of q-block q0 + w: the largest score,
-  //    the lower index on ties (-inf scores are candidates too)
+  //    the lower index on ties (-inf scores are candidates too).  A lane
+  //    holds the scores of blocks lane, lane + 64, ... (at most kRouteRegs)
+  //    in registers with a bit per taken one; each pick is a lane-local
+  //    maximum and a butterfly over the lanes.  Longer rows (more than
+  //    64 * kRouteRegs blocks) read their scores from LDS instead.
   if (wave < nq) {
     double *s = sc + (size_t)wave * nkb;
     uint8_t *ch = chosen + (size_t)wave * nkb;
-    for (int it = 0; it < route_k; ++it) {
-      double best = NAN;
-      int bi = -1;
-      for (int b = lane; b < nkb; b += 64) {
-        const double v = s[b];
-        if (v != v || ch[b]) continue;
-        if (bi < 0 || v > best) {   // ascending b per lane: equal keeps the lower
-          best = v;
-          bi = b;
-        }
+    constexpr int kRouteRegs = 32;
+    if (nkb <= 64 * kRouteRegs) {
+      double v[kRouteRegs];
+      uint32_t live = 0;                     // bit i: block lane + 64 i is a candidate not yet taken
+#pragma unroll
+      for (int i = 0; i < kRouteRegs; ++i) {
+        const int b = lane + 64 * i;
+        v[i] = b < nkb ? s[b] : NAN;
+        if (v[i] == v[i]) live |= 1u << i;
       }
-      for (int off = 1; off < 64; off <<= 1) {
-        const double ob = __shfl_xor(best, off);
-        const int oi = __shfl_xor(bi, off);
-        if (oi >= 0 && (bi < 0 || ob > best || (ob == best && oi < bi))) {
-          best = ob;
-          bi = oi;
+      for (int it = 0; it < route_k; ++it) {
+        double best = NAN;
+        int bi = -1;
+#pragma unroll
+        for (int i = 0; i < kRouteRegs; ++i)
+          if (((live >> i) & 1) && (bi < 0 || v[i] > best)) {   // ascending block per lane: equal keeps the lower
+            best = v[i];
+            bi = lane + 64 * i;
+          }
+        for (int off = 1; off < 64; off <<= 1) {
+          const double ob = __shfl_xor(best, off);
+          const int oi = __shfl_xor(bi, off);
+          if (oi >= 0 && (bi < 0 || ob > best || (ob == best && oi < bi))) {
+            best = ob;
+            bi = oi;
+          }
         }
+        if (bi < 0) break;                   // no candidate left (wave-uniform)
+        if ((bi & 63) == lane) live &= ~(1u << (bi >> 6));
       }
-      if (bi < 0) break;                // no candidate left (wave-uniform)
-      if (lane == 0) ch[bi] = 1;
+      // the taken blocks: candidates no longer live
+#pragma unroll
+      for (int i = 0; i < kRouteRegs; ++i) {
+        const int b = lane + 64 * i;
+        if (b < nkb && v[i] == v[i] && !((live >> i) & 1)) ch[b] = 1;
+      }
       __builtin_amdgcn_s_waitcnt(0);
       __builtin_amdgcn_wave_barrier();
+    } else {
+      for (int it = 0; it < route_k; ++it) {
+        double best = NAN;
+        int bi = -1;
+        for (int b = lane; b < nkb; b += 64) {
+          const double v = s[b];
+          if (v != v || ch[b]) continue;
+          if (bi < 0 || v > best) {   // ascending b per lane: equal keeps the lower
+            best = v;
+            bi = b;
+          }
+        }
+        for (int off = 1; off < 64; off <<= 1) {
+          const double ob = __shfl_xor(best, off);
+          const int oi = __shfl_xor(bi, off);
+          if (oi >= 0 && (bi < 0 || ob > best || (ob == best && oi < bi))) {
+            best = ob;
+            bi = oi;
+          }
+        }
+        if (bi < 0) break;                // no candidate left (wave-uniform)
+        if (lane == 0) ch[bi] = 1;
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_wave_barrier();
+      }
     }
     uint8_t *out = exact + ((size_t)h * nqb + q0 + wave) * nkb;
     const uint8_t *in = mask + ((size_t)h * nqb + q0 + wave) * nkb;
