@@ -121,42 +121,54 @@ void ear_route(const bf16_t *__restrict__ Q, const int32_t *__restrict__ labels,
   const bool ragged = (N % 64) != 0;
   const int Qw = q0 + wave;
   // 1. mean query of q-block Qw (executing-layout rows, read from the
-  //    original order as the layout permute maps them)
+  //    original order as the layout permute maps them).  Lane l reads 16
+  //    bytes (8 dims) of row r0 + 4 j + l / (D / 8) for j = 0, 1, ..: all its
+  //    rows' loads go out in batches of 8, the sums are float64 (exact for
+  //    bf16 values, so the grouping of the rows changes no bit), and the
+  //    64 / (D / 8) row groups are added by a butterfly at the end.
   if (wave < qpw && Qw < nqb) {
+    constexpr int LPR = D / 8;                // lanes per row
+    constexpr int RPI = 64 / LPR;             // rows per load instruction
     const int r0 = Qw * bq, r1 = min(N, r0 + bq);
-    // rows in batches of 32: their loads go out together, then the adds in
-    // row order
-    double acc[D / 64];
+    const int sub = lane / LPR, part = lane % LPR;
+    double acc[8];
 #pragma unroll
-    for (int u = 0; u < D / 64; ++u) acc[u] = 0.0;
-    for (int rb = r0; rb < r1; rb += 32) {
-      float xv[32][D / 64];
+    for (int e = 0; e < 8; ++e) acc[e] = 0.0;
+    for (int rb = r0; rb < r1; rb += 8 * RPI) {
+      u32x4 w[8];
 #pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        const int r = rb + j;
+      for (int j = 0; j < 8; ++j) {
+        const int r = rb + RPI * j + sub;
         int src = r < r1 ? r : r0;
         if (perm && src < F * S) {
           const int p = src / F, f = src - p * F;
           src = f * S + p;
         }
-        const bf16_t *qr = Q + ((size_t)h * N + src) * D;
-#pragma unroll
-        for (int u = 0; u < D / 64; ++u) xv[j][u] = bf16_to_f32(qr[64 * u + lane]);
+        w[j] = reinterpret_cast<const u32x4 *>(Q + ((size_t)h * N + src) * D)[part];
       }
 #pragma unroll
-      for (int j = 0; j < 32; ++j)
-        if (rb + j < r1)
+      for (int j = 0; j < 8; ++j)
+        if (rb + RPI * j + sub < r1)
 #pragma unroll
-          for (int u = 0; u < D / 64; ++u) acc[u] += (double)xv[j][u];
+          for (int q = 0; q < 4; ++q) {
+            acc[2 * q] += (double)__uint_as_float(w[j][q] << 16);
+            acc[2 * q + 1] += (double)__uint_as_float(w[j][q] & 0xFFFF0000u);
+          }
     }
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], off);
     double n2 = 0.0;
+    if (sub == 0) {
 #pragma unroll
-    for (int u = 0; u < D / 64; ++u) {
-      const double m = acc[u] / (double)(r1 - r0);
-      qbar[wave * D + 64 * u + lane] = m;
-      n2 += m * m;
+      for (int e = 0; e < 8; ++e) {
+        const double m = acc[e] / (double)(r1 - r0);
+        qbar[wave * D + 8 * part + e] = m;
+        n2 += m * m;
+      }
     }
-    for (int s = 1; s < 64; s <<= 1) n2 += __shfl_xor(n2, s);
+    for (int s2 = 1; s2 < 64; s2 <<= 1) n2 += __shfl_xor(n2, s2);
     if (lane == 0) qnorm[wave] = sqrt(n2);
   }
   __syncthreads();
