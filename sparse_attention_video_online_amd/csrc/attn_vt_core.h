@@ -161,6 +161,7 @@ __device__ __forceinline__ int build_union_list(const int32_t *__restrict__ row_
   }
   __syncthreads();
   // per-word counts, exclusive scan by wave 0 (4 words per lane)
+  static_assert(kWords == 4 * 64, "wave 0 scans the bitmap's words four per lane");
   if (wave == 0) {
     int cnt[4], tot = 0;
 #pragma unroll
