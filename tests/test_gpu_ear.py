@@ -122,6 +122,32 @@ def test_ear_chain_against_oracle(F, S, T, d, bq, route_k):
             check_close(got[rows], orow, BF16_MAX_ABS, BF16_REL_L2, f"ear head {h} qb {qb}")
 
 
+def test_ear_route_past_register_capacity():
+    """More than 2,048 kv-blocks a head (35 x 3800 + 70 tokens: 2,080 blocks,
+    a ragged last one): the routing keeps its candidate scores in LDS
+    instead of registers.  Exact sets bit-exact for both heads (after the
+    margin audit); O against the oracle on seeded q-blocks plus the first,
+    video/text and last ones."""
+    H, F, S, T, d, bq, route_k = 2, 35, 3800, 70, 128, 128, 16
+    N = F * S + T
+    q, k, v = random_qkv(H, N, d, seed=77, dtype="bf16", scale=1.5)
+    labels = [0, 1]
+    nqb, nkb = -(-N // bq), -(-N // 64)
+    assert nkb > 2048
+    bm = (np.random.default_rng(78).random((H, nqb, nkb)) < 0.3).astype(np.uint8)
+    g = gpu_ear(q, k, v, F, S, T, labels, bm, bq, route_k)
+    got = to_f64(g["o"])
+    rng = np.random.default_rng(79)
+    fixed = [0, (F * S) // bq, nqb - 1]
+    for h in range(H):
+        qbs = sorted(set(fixed) | set(int(x) for x in rng.choice(nqb, size=5, replace=False)))
+        o = oracle_head(q[h], k[h], v[h], F, S, T, labels[h], bm[h], bq, route_k, qblocks=qbs)
+        assert route_margin_ok(o["scores"], bm[h], o["exact"], N, route_k)
+        np.testing.assert_array_equal(g["exact"][h].cpu().numpy(), o["exact"])
+        for qb, (rows, orow) in o["o"].items():
+            check_close(got[h][rows], orow, BF16_MAX_ABS, BF16_REL_L2, f"ear wide head {h} qb {qb}")
+
+
 def test_ear_equal_keys_per_block_is_dense_attention():
     """Keys equal within each 64-key block of the executing layout: the
     centroid stands in exactly, so the compensated output is dense
