@@ -29,6 +29,27 @@ definition, stated here and checked against itself nowhere else:
 Everything after the quantization runs in float64, so this oracle says what
 the FP8 path should return up to the rounding of its fp32 accumulation and
 of the bf16 probabilities and output.
+
+The FP8 P.V mode (also this library's definition) quantizes the other
+product as well:
+* V gets one scale per channel (column d) over all N tokens of the head,
+  coded as above: v_code = round_e4m3(fp32(v * (448 / a_d))), scale
+  a_d / 448.
+* P: a query row walks its q-block's kept tiles in ascending order with a
+  lazy reference m.  Logits are taken in exp2 units, y = log2(e) * scale *
+  (q~ . k~).  A tile whose largest y exceeds m by more than 8 (or the first
+  kept tile) moves m to that maximum, and the sums so far are multiplied by
+  2^(m_old - m_new).  Each key's probability p = 2^(y - m) (at most 2^8) is
+  coded as round_e4m3(fp32(p)) with no scale; the sums take the decoded
+  codes p8.
+* O = (sum_j p8_j * decode(v_code_j)) / (sum_j p8_j), times the channel
+  scales.
+Because each p8 is a rounding of an exponential, a logit error of a few
+fp32 units can move a p that sits next to a rounding boundary to the
+neighbouring code.  fp8_pv_block_sparse_attention therefore also returns,
+for each row, a bound on what such moves can change: the codes whose p lies
+within a relative eps of a boundary are "undecided" and each may take
+either neighbour.
 """
 
 import numpy as np
@@ -130,3 +151,92 @@ def fp8_block_sparse_attention(q, k, v, bitmap, bq, bk, scale=None, qblocks=None
     kd = dequantize(kc, ks, bk)
     scale = default_scale(q.shape[1]) if scale is None else scale
     return block_sparse_attention(qd, kd, np.asarray(v, dtype=np.float64), bitmap, bq, bk, scale, qblocks)
+
+
+LAZY_LOG2 = 8.0          # the reference moves when a tile's maximum exceeds it by more than this (exp2 units)
+
+
+def quantize_channels(x):
+    """Per-channel scales: one per column of x [N][d] over all N rows (the V
+    side of the FP8 P.V mode).  Returns the codes [N][d] and the fp32 scale
+    of each column."""
+    codes_t, scales = quantize_groups(np.asarray(x, dtype=np.float32).T, 1)
+    return np.ascontiguousarray(codes_t.T), scales
+
+
+def _lazy_references(tile_max):
+    """The lazy reference of each (row, kept tile), walking the tiles in
+    order: [R][T] float64 (tile_max: [R][T], the tiles' largest logits in
+    exp2 units).  Also returns, per row, whether some move decision lies
+    within 1e-3 of the threshold (then fp32 rounding could decide it the
+    other way)."""
+    R, T = tile_max.shape
+    ref = np.empty((R, T))
+    m = np.full(R, -np.inf)
+    near = np.zeros(R, dtype=bool)
+    for t in range(T):
+        mt = tile_max[:, t]
+        first = np.isneginf(m)
+        with np.errstate(invalid="ignore"):
+            gap = mt - m
+        near |= ~first & (np.abs(gap - LAZY_LOG2) < 1e-3)
+        m = np.where(first | (gap > LAZY_LOG2), mt, m)
+        ref[:, t] = m
+    return ref, near
+
+
+def fp8_pv_block_sparse_attention(q, k, v, bitmap, bq, bk, scale=None, qblocks=None, eps=1e-4):
+    """Block-sparse attention of one head in the FP8 P.V mode (definition
+    above): FP8 Q and K as in fp8_block_sparse_attention, V coded per
+    channel, P coded after the lazy reference.  q, k, v: [N][d] values
+    exact in fp32, in the executing layout.
+
+    Returns {qb: (O rows, bound rows, ambiguous rows)}: O in float64; bound
+    [R], the largest change of any O value that moving the undecided codes
+    (p within a relative eps of a rounding boundary) could make, to first
+    order; ambiguous [R] bool, rows with a reference move within 1e-3 of the
+    threshold."""
+    q = np.asarray(q, dtype=np.float32)
+    N, d = q.shape
+    qc, qs = quantize_rows(q)
+    kc, ks = quantize_key_blocks(k, bk)
+    qd = dequantize(qc, qs, 1)
+    kd = dequantize(kc, ks, bk)
+    vc, vs = quantize_channels(v)
+    v8 = e4m3_decode(vc)                                  # unscaled code values
+    vmax = np.abs(v8 * vs.astype(np.float64)[None, :]).max(axis=1) if N else np.zeros(0)
+    scale = default_scale(d) if scale is None else scale
+    c = scale * np.log2(np.e)
+    nqb = bitmap.shape[0]
+    qblocks = range(nqb) if qblocks is None else qblocks
+    out = {}
+    for qb in qblocks:
+        r0, r1 = qb * bq, min(N, (qb + 1) * bq)
+        R = r1 - r0
+        kept = np.flatnonzero(bitmap[qb])
+        if kept.size == 0:
+            out[qb] = (np.zeros((R, d)), np.zeros(R), np.zeros(R, dtype=bool))
+            continue
+        cols = [np.arange(kb * bk, min(N, (kb + 1) * bk)) for kb in kept]
+        tile_of = np.concatenate([np.full(cc.size, t) for t, cc in enumerate(cols)])
+        cols = np.concatenate(cols)
+        y = (qd[r0:r1] @ kd[cols].T) * c                  # [R][keys], exp2 units
+        tmax = np.stack([y[:, tile_of == t].max(axis=1) for t in range(kept.size)], axis=1)
+        ref, near = _lazy_references(tmax)
+        mfin = ref[:, -1]
+        p = np.exp2(y - ref[:, tile_of])                  # each key against its tile's reference
+        p32 = p.astype(np.float32)
+        p8 = e4m3_decode(e4m3_round(p32))
+        lo = e4m3_decode(e4m3_round((p * (1 - eps)).astype(np.float32)))
+        up = e4m3_decode(e4m3_round((p * (1 + eps)).astype(np.float32)))
+        step = np.maximum(np.abs(p8 - lo), np.abs(up - p8))
+        w = np.exp2(ref[:, tile_of] - mfin[:, None])      # the rescales by later moves
+        pw = p8 * w
+        l = pw.sum(axis=1)
+        o = (pw @ v8[cols]) * vs.astype(np.float64)[None, :]
+        with np.errstate(invalid="ignore", divide="ignore"):
+            O = np.where(l[:, None] > 0, o / l[:, None], 0.0)
+            sw = step * w
+            bound = np.where(l > 0, (sw @ vmax[cols] + sw.sum(axis=1) * np.abs(O).max(axis=1)) / l, 0.0)
+        out[qb] = (O, bound, near)
+    return out

@@ -139,3 +139,141 @@ def test_round_top_of_the_range():
     assert int(fp8.e4m3_round(np.array([464.0], np.float32))[0]) == 0x7E
     with pytest.raises(ValueError):
         fp8.e4m3_round(np.array([470.0], np.float32))
+
+
+# ---------------------------------------------------------------------------
+# The FP8 P.V mode: per-channel V codes, probabilities coded after the lazy
+# reference.
+
+def test_quantize_channels_known_values():
+    """Column maxima 448 (scale 1: the codes are the values), 7 (values
+    decode(c) / 64: inv = 64 exactly) and 0 (codes 0, scale 0)."""
+    rng = np.random.default_rng(21)
+    finite = FINITE[np.abs(fp8.e4m3_decode(FINITE)) < 448]
+    x = np.zeros((50, 3), np.float32)
+    x[:, 0] = fp8.e4m3_decode(rng.choice(finite, size=50))
+    x[7, 0] = -448.0
+    x[:, 1] = fp8.e4m3_decode(rng.choice(finite, size=50)) / 64
+    x[3, 1] = 7.0
+    codes, scales = fp8.quantize_channels(x)
+    assert codes.shape == x.shape
+    np.testing.assert_array_equal(scales, np.array([1.0, 7.0 / 448.0, 0.0], np.float32))
+    np.testing.assert_array_equal(fp8.e4m3_decode(codes[:, 0]), x[:, 0])
+    np.testing.assert_array_equal(fp8.e4m3_decode(codes[:, 1]) * np.float64(scales[1]), x[:, 1])
+    assert np.all(codes[:, 2] == 0)
+
+
+def _exact_v(rng, N, d):
+    """V whose every column has maximum magnitude 448 and only code values
+    (channel scale 1: the codes stand for V exactly)."""
+    finite = FINITE[np.abs(fp8.e4m3_decode(FINITE)) <= 64]
+    v = fp8.e4m3_decode(rng.choice(finite, size=(N, d))).astype(np.float32)
+    v[rng.integers(0, N), :] = 448.0
+    return v
+
+
+def test_fp8_pv_equal_logits_is_the_kept_keys_mean():
+    """q = 0: every logit is 0, every p is 1 (a code value), so each row's
+    output is the mean of V over its q-block's kept keys."""
+    rng = np.random.default_rng(22)
+    N, d, bq, bk = 150, 64, 64, 64
+    q = np.zeros((N, d), np.float32)
+    k = rng.standard_normal((N, d)).astype(np.float32)
+    v = _exact_v(rng, N, d)
+    bm = (rng.random((3, 3)) < 0.6).astype(np.uint8)
+    bm[0] = 0
+    bm[1, 2] = 1                                     # the short last block
+    got = fp8.fp8_pv_block_sparse_attention(q, k, v, bm, bq, bk)
+    for qb in range(3):
+        O, bound, near = got[qb]
+        kept = np.flatnonzero(bm[qb])
+        if kept.size == 0:
+            assert np.all(O == 0)
+            continue
+        cols = np.concatenate([np.arange(kb * bk, min(N, (kb + 1) * bk)) for kb in kept])
+        want = v[cols].astype(np.float64).mean(axis=0)
+        np.testing.assert_allclose(O, np.broadcast_to(want, O.shape), rtol=0, atol=1e-12)
+        assert np.all(bound == 0) and not near.any()
+
+
+def _integer_logit_inputs(rng, N, d, bk, lift_block):
+    """Q and K exactly representable (row / block maxima 448 in dims that
+    the dot products never use), with integer dot products in [-3, 3], plus
+    +12 on every key of block lift_block (dim 2: q = 4, k = 3)."""
+    q = np.zeros((N, d), np.float32)
+    k = np.zeros((N, d), np.float32)
+    q[:, 0] = 448.0                                  # q . k never meets dim 0 (k = 0 there)
+    k[::bk, 1] = 448.0                               # each 64-row block's maximum; q = 0 in dim 1
+    for x in (q, k):
+        for r in range(N):
+            dims = rng.choice(np.arange(3, d), size=3, replace=False)
+            x[r, dims] = rng.choice([-1.0, 1.0], size=3)
+    q[:, 2] = 4.0
+    k[lift_block * bk:(lift_block + 1) * bk, 2] = 3.0
+    return q, k
+
+
+def test_fp8_pv_exact_powers_equal_plain_attention_with_a_move():
+    """Logits that are integers in exp2 units (scale ln 2): every p is a
+    power of two, a code value, so the FP8 P.V output is plain attention
+    with the same V.  Rows whose q-block keeps block 3 see its logits 12
+    above the others: the reference moves there (by more than 8) and the
+    earlier sums, coded against the old reference, are rescaled exactly
+    (those q-blocks keep no later block, whose p would fall below the
+    smallest code)."""
+    rng = np.random.default_rng(23)
+    N, d, bq, bk = 5 * 64 + 17, 64, 64, 64
+    q, k = _integer_logit_inputs(rng, N, d, bk, lift_block=3)
+    v = _exact_v(rng, N, d)
+    nb = -(-N // 64)
+    bm = (rng.random((nb, nb)) < 0.6).astype(np.uint8)
+    bm[:, 0] = 1
+    bm[:3, 3] = 1
+    bm[:3, 4:] = 0                                   # nothing after the lift (its p would leave the code range)
+    bm[3:, 3] = 0
+    bm[4, 5] = 1
+    ln2 = float(np.log(2.0))
+    got = fp8.fp8_pv_block_sparse_attention(q, k, v, bm, bq, bk, scale=ln2)
+    want = block_sparse_attention(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64), bm, bq, bk,
+                                  scale=ln2)
+    for qb in range(nb):
+        O, bound, near = got[qb]
+        assert not near.any()
+        np.testing.assert_allclose(O, want[qb], rtol=0, atol=1e-12)
+
+
+def test_fp8_pv_probability_rounding_hand_case():
+    """Two keys with logits 0 and 1/2 (exp2 units): p = 2^-1/2 = 0.7071 is
+    coded as 0.6875 (1.375 * 2^-1; the neighbours are 0.6875 and 0.75), the
+    largest as 1.  V = [[448, 1], [1, 448]] is coded exactly, so
+    O = (0.6875 * v0 + v1) / 1.6875."""
+    q = np.array([[448.0, 1.0], [448.0, 1.0]], np.float32)
+    k = np.array([[0.0, 0.0], [0.0, 1.0]], np.float32)
+    v = np.array([[448.0, 1.0], [1.0, 448.0]], np.float32)
+    scale = 0.5 / float(np.log2(np.e))
+    O, bound, near = fp8.fp8_pv_block_sparse_attention(q, k, v, np.ones((1, 1), np.uint8), 64, 64, scale=scale)[0]
+    want = (0.6875 * np.array([448.0, 1.0]) + np.array([1.0, 448.0])) / 1.6875
+    np.testing.assert_allclose(O, np.stack([want, want]), rtol=1e-14, atol=0)
+    assert np.all(bound == 0) and not near.any()
+
+
+def test_fp8_pv_bound_covers_logit_perturbations():
+    """Logits moved by a relative 1e-6 (a scale change) can only move
+    undecided codes, and the output changes within the returned bound."""
+    rng = np.random.default_rng(24)
+    N, d, bq, bk = 3 * 64 + 9, 64, 64, 64
+    q = (rng.standard_normal((N, d)) * 1.5).astype(np.float32)
+    k = (rng.standard_normal((N, d)) * 1.5).astype(np.float32)
+    v = rng.standard_normal((N, d)).astype(np.float32)
+    nb = -(-N // 64)
+    bm = np.ones((nb, nb), np.uint8)
+    base = fp8.fp8_pv_block_sparse_attention(q, k, v, bm, bq, bk)
+    assert sum(float(b.sum()) for _, b, _ in base.values()) > 0      # some codes are undecided
+    for delta in (1e-6, -1e-6, 3e-7):
+        s = (1 + delta) / np.sqrt(d)
+        moved = fp8.fp8_pv_block_sparse_attention(q, k, v, bm, bq, bk, scale=s)
+        for qb in range(nb):
+            O0, bound, _ = base[qb]
+            O1 = moved[qb][0]
+            # the logits' own change moves every p by a relative ~|y| * delta * ln 2
+            assert np.all(np.abs(O1 - O0).max(axis=1) <= bound * 1.01 + 1e-4 * np.abs(O0).max(axis=1))
