@@ -61,15 +61,24 @@ E4M3_MIN_NORMAL = 2.0 ** -6
 E4M3_SUBNORMAL_STEP = 2.0 ** -9
 
 
-def e4m3_decode(codes) -> np.ndarray:
-    """uint8 codes -> float64 values (NaN for 0x7F / 0xFF)."""
-    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+def _e4m3_values() -> np.ndarray:
+    """The value of each of the 256 codes (NaN for 0x7F / 0xFF)."""
+    c = np.arange(256, dtype=np.int64)
     sign = np.where(c & 0x80, -1.0, 1.0)
     e = (c >> 3) & 0xF
     m = c & 0x7
     mag = np.where(e == 0, m * E4M3_SUBNORMAL_STEP, (1.0 + m / 8.0) * np.ldexp(1.0, e - 7))
     mag = np.where((e == 0xF) & (m == 0x7), np.nan, mag)
     return sign * mag
+
+
+_E4M3_VALUES = _e4m3_values()
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """uint8 codes -> float64 values (NaN for 0x7F / 0xFF), from the table
+    of all 256 codes."""
+    return _E4M3_VALUES[np.asarray(codes).astype(np.uint8)]
 
 
 def e4m3_round(y) -> np.ndarray:
@@ -110,17 +119,21 @@ def quantize_groups(x, group_rows: int):
     x32 = np.asarray(x, dtype=np.float32)
     N = x32.shape[0]
     ng = -(-N // group_rows)
-    codes = np.zeros(x32.shape, dtype=np.uint8)
+    if N == 0 or x32.size == 0:
+        return np.zeros(x32.shape, dtype=np.uint8), np.zeros(ng, dtype=np.float32)
+    # every group at once: rows padded with zeros to whole groups (a zero
+    # never raises a group's maximum and is not returned)
+    blk = np.zeros((ng * group_rows,) + x32.shape[1:], dtype=np.float32)
+    blk[:N] = x32
+    blk = blk.reshape(ng, group_rows, -1)
+    a = np.abs(blk).max(axis=(1, 2))                      # fp32 group maxima
+    live = a > 0
+    inv = np.zeros(ng, dtype=np.float32)
+    inv[live] = np.float32(E4M3_MAX) / a[live]            # fp32 division, rounded once
+    y = (blk * inv[:, None, None]).astype(np.float32)     # fp32 products, rounded once
+    codes = e4m3_round(y).reshape(ng * group_rows, -1)[:N].reshape(x32.shape)
     scales = np.zeros(ng, dtype=np.float32)
-    for g in range(ng):
-        blk = x32[g * group_rows:(g + 1) * group_rows]
-        a = np.float32(np.abs(blk).max()) if blk.size else np.float32(0)
-        if a == 0:
-            continue
-        inv = np.float32(E4M3_MAX) / a                    # fp32 division, rounded once
-        y = (blk * inv).astype(np.float32)                # fp32 product, rounded once
-        codes[g * group_rows:(g + 1) * group_rows] = e4m3_round(y)
-        scales[g] = a / np.float32(E4M3_MAX)
+    scales[live] = a[live] / np.float32(E4M3_MAX)
     return codes, scales
 
 
@@ -198,9 +211,7 @@ def fp8_pv_block_sparse_attention(q, k, v, bitmap, bq, bk, scale=None, qblocks=N
     threshold."""
     q = np.asarray(q, dtype=np.float32)
     N, d = q.shape
-    qc, qs = quantize_rows(q)
     kc, ks = quantize_key_blocks(k, bk)
-    qd = dequantize(qc, qs, 1)
     kd = dequantize(kc, ks, bk)
     vc, vs = quantize_channels(v)
     v8 = e4m3_decode(vc)                                  # unscaled code values
@@ -220,16 +231,22 @@ def fp8_pv_block_sparse_attention(q, k, v, bitmap, bq, bk, scale=None, qblocks=N
         cols = [np.arange(kb * bk, min(N, (kb + 1) * bk)) for kb in kept]
         tile_of = np.concatenate([np.full(cc.size, t) for t, cc in enumerate(cols)])
         cols = np.concatenate(cols)
-        y = (qd[r0:r1] @ kd[cols].T) * c                  # [R][keys], exp2 units
-        tmax = np.stack([y[:, tile_of == t].max(axis=1) for t in range(kept.size)], axis=1)
+        qc, qs = quantize_rows(q[r0:r1])                  # per-row scales: the block's rows alone
+        y = (dequantize(qc, qs, 1) @ kd[cols].T) * c      # [R][keys], exp2 units
+        starts = np.concatenate([[0], np.flatnonzero(np.diff(tile_of)) + 1])   # each tile's first column
+        tmax = np.maximum.reduceat(y, starts, axis=1)                          # [R][T] tile maxima
         ref, near = _lazy_references(tmax)
         mfin = ref[:, -1]
         p = np.exp2(y - ref[:, tile_of])                  # each key against its tile's reference
-        p32 = p.astype(np.float32)
-        p8 = e4m3_decode(e4m3_round(p32))
-        lo = e4m3_decode(e4m3_round((p * (1 - eps)).astype(np.float32)))
-        up = e4m3_decode(e4m3_round((p * (1 + eps)).astype(np.float32)))
-        step = np.maximum(np.abs(p8 - lo), np.abs(up - p8))
+        code = e4m3_round(p.astype(np.float32)).astype(np.int64)     # 0 .. 0x78 (p <= 2^8)
+        p8 = e4m3_decode(code)
+        # undecided: p within a relative eps of the midpoint to a neighbouring
+        # code (positive codes are ordered like their values)
+        nxt = e4m3_decode(np.minimum(code + 1, 0x7E))
+        prv = e4m3_decode(np.maximum(code - 1, 0))
+        und_up = p * (1 + eps) >= (p8 + nxt) / 2
+        und_lo = (code > 0) & (p * (1 - eps) <= (p8 + prv) / 2)
+        step = np.maximum(np.where(und_up, nxt - p8, 0.0), np.where(und_lo, p8 - prv, 0.0))
         w = np.exp2(ref[:, tile_of] - mfin[:, None])      # the rescales by later moves
         pw = p8 * w
         l = pw.sum(axis=1)
