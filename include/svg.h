@@ -364,6 +364,27 @@ svg_status svg_block_sparse_attn_ear_vt_layout(const svg_dims *dims, svg_dtype d
  *   entry.  Q8 / qscale in the original token order; K8 / kscale, Vt and the
  *   lists in the executing layout.  No split of the text rows' groups.
  * svg_dense_attn_fp8_vt: every tile kept, Q8 / K8 / Vt in one common order.
+ *
+ * The FP8 P.V mode (also this library's definition) codes V and the
+ * probabilities as well:
+ * svg_layout_permute_vt_fp8: V [H][N][d] bf16 -> vamax float [H][d], each
+ *   channel's largest magnitude over the head's N tokens (channel scale
+ *   vamax / 448), and Vt8 uint8 [H][ceil(N/64)][d][64]: V in the executing
+ *   layout (per labels, as svg_layout_permute_vt), key-tiled and transposed,
+ *   code round_e4m3(fp32(v * (448 / vamax_d))).  Within a tile row, byte
+ *   j = 32 h + b holds key 32 (b >> 4) + 16 ((b >> 3) & 1) + 8 h + (b & 7)
+ *   (the order the attention holds its probabilities in); keys past N are
+ *   code 0.  Runs three kernels on the stream; Vt8 and vamax are written
+ *   whole.
+ * svg_block_sparse_attn_fp8pv_vt_layout: svg_block_sparse_attn_fp8_vt_layout
+ *   with V given as Vt8 / vamax, and P coded too: a query row walks its
+ *   q-block's kept tiles in ascending order with a lazy reference m of its
+ *   logits y (exp2 units), moved to a tile's maximum when that exceeds m by
+ *   more than 8 (the sums so far rescaled by 2^(m_old - m_new)); each
+ *   p = 2^(y - m) <= 2^8 becomes round_e4m3(fp32(p)) with no scale; P.V and
+ *   the row sum take those codes on the FP8 matrix cores (fp32
+ *   accumulation), and O = (P8 . V8) / sum(P8) times the channel scales
+ *   (bf16, original token order).
  * Limits: bf16 inputs to the quantizers; d = 128, (bq, bk) = (64, 64) or
  * (128, 64), nKB <= 8192 for the attention (else SVG_ERR_UNSUPPORTED).
  * Buffers must not overlap their inputs (SVG_ERR_RANGE).
@@ -380,6 +401,13 @@ svg_status svg_block_sparse_attn_fp8_vt_layout(const svg_dims *dims, const uint8
 svg_status svg_dense_attn_fp8_vt(const svg_dims *dims, const uint8_t *Q8, const float *qscale,
                                  const uint8_t *K8, const float *kscale, const void *Vt, int32_t bq,
                                  int32_t bk, float softmax_scale, void *O, void *stream);
+svg_status svg_layout_permute_vt_fp8(const svg_dims *dims, svg_dtype dtype, const void *V, uint8_t *Vt8,
+                                     float *vamax, const int32_t *labels, void *stream);
+svg_status svg_block_sparse_attn_fp8pv_vt_layout(const svg_dims *dims, const uint8_t *Q8, const float *qscale,
+                                                 const uint8_t *K8, const float *kscale, const uint8_t *Vt8,
+                                                 const float *vamax, const int32_t *row_ptr,
+                                                 const int32_t *kv_idx, const int32_t *labels, int32_t bq,
+                                                 int32_t bk, float softmax_scale, void *O, void *stream);
 
 #ifdef __cplusplus
 }

@@ -559,8 +559,10 @@ svg_status svg_layout_permute_fp8(const svg_dims *dims, svg_dtype dtype, const v
   return hip_status(svgk::launch_layout_fp8(dm, X, X8, scale, labels, (hipStream_t)stream), "svg_layout_permute_fp8");
 }
 
+// vt_div: 1 for bf16 V^T tiles, 2 for the V^T code tiles of the P.V mode
 static svg_status fp8_attn_checks(const svg_dims *dims, const void *Q8, const float *qscale, const void *K8,
-                                  const float *kscale, const void *Vt, const void *O, int bq, int bk, Dims *dm) {
+                                  const float *kscale, const void *Vt, const void *O, int bq, int bk, Dims *dm,
+                                  int vt_div = 1) {
   svg_status s;
   if ((s = check_dims(dims, dm, false)) != SVG_OK) return s;
   if (dm->d != 128) return fail(SVG_ERR_UNSUPPORTED, "fp8 attention: head dim %d unsupported (128)", dm->d);
@@ -573,7 +575,7 @@ static svg_status fp8_attn_checks(const svg_dims *dims, const void *Q8, const fl
   if (!Q8 || !qscale || !K8 || !kscale || !Vt || !O) return fail(SVG_ERR_NULL, "fp8 attention: NULL pointer");
   const size_t obytes = (size_t)dm->H * dm->N * dm->d * 2;
   if (overlaps2(O, obytes, Q8, obytes / 2) || overlaps2(O, obytes, K8, obytes / 2) ||
-      overlaps2(O, obytes, Vt, vt_bytes(*dm)))
+      overlaps2(O, obytes, Vt, vt_bytes(*dm) / vt_div))
     return fail(SVG_ERR_RANGE, "fp8 attention: O overlaps an input");
   return SVG_OK;
 }
@@ -587,7 +589,7 @@ svg_status svg_block_sparse_attn_fp8_vt_layout(const svg_dims *dims, const uint8
   svg_status s;
   if ((s = fp8_attn_checks(dims, Q8, qscale, K8, kscale, Vt, O, bq, bk, &dm)) != SVG_OK) return s;
   if (!row_ptr || !kv_idx) return fail(SVG_ERR_NULL, "block_sparse_attn_fp8_vt_layout: NULL list");
-  return hip_status(svgk::launch_attn_fp8(dm, Q8, qscale, K8, kscale, Vt, O, row_ptr, kv_idx, bq,
+  return hip_status(svgk::launch_attn_fp8(dm, Q8, qscale, K8, kscale, Vt, nullptr, O, row_ptr, kv_idx, bq,
                                           resolve_scale(softmax_scale, dm.d), labels, true, (hipStream_t)stream),
                     "svg_block_sparse_attn_fp8_vt_layout");
 }
@@ -598,9 +600,41 @@ svg_status svg_dense_attn_fp8_vt(const svg_dims *dims, const uint8_t *Q8, const 
   Dims dm{};
   svg_status s;
   if ((s = fp8_attn_checks(dims, Q8, qscale, K8, kscale, Vt, O, bq, bk, &dm)) != SVG_OK) return s;
-  return hip_status(svgk::launch_attn_fp8(dm, Q8, qscale, K8, kscale, Vt, O, nullptr, nullptr, bq,
+  return hip_status(svgk::launch_attn_fp8(dm, Q8, qscale, K8, kscale, Vt, nullptr, O, nullptr, nullptr, bq,
                                           resolve_scale(softmax_scale, dm.d), nullptr, false, (hipStream_t)stream),
                     "svg_dense_attn_fp8_vt");
+}
+
+svg_status svg_layout_permute_vt_fp8(const svg_dims *dims, svg_dtype dtype, const void *V, uint8_t *Vt8,
+                                     float *vamax, const int32_t *labels, void *stream) {
+  Dims dm{};
+  svg_status s;
+  if ((s = check_dims(dims, &dm, false)) != SVG_OK) return s;
+  if (dtype != SVG_BF16) return fail(SVG_ERR_UNSUPPORTED, "layout_permute_vt_fp8: bf16 inputs only");
+  if (dm.d != 128) return fail(SVG_ERR_UNSUPPORTED, "layout_permute_vt_fp8: head dim %d unsupported (128)", dm.d);
+  if (!V || !Vt8 || !vamax) return fail(SVG_ERR_NULL, "layout_permute_vt_fp8: NULL pointer");
+  const size_t vbytes = (size_t)dm.H * dm.N * dm.d * 2, tbytes = vt_bytes(dm) / 2;
+  if (overlaps2(Vt8, tbytes, V, vbytes) || overlaps2(vamax, (size_t)dm.H * dm.d * 4, V, vbytes) ||
+      overlaps2(vamax, (size_t)dm.H * dm.d * 4, Vt8, tbytes))
+    return fail(SVG_ERR_RANGE, "layout_permute_vt_fp8: buffers overlap");
+  return hip_status(svgk::launch_layout_vt_fp8(dm, V, Vt8, vamax, labels, (hipStream_t)stream),
+                    "svg_layout_permute_vt_fp8");
+}
+
+svg_status svg_block_sparse_attn_fp8pv_vt_layout(const svg_dims *dims, const uint8_t *Q8, const float *qscale,
+                                                 const uint8_t *K8, const float *kscale, const uint8_t *Vt8,
+                                                 const float *vamax, const int32_t *row_ptr,
+                                                 const int32_t *kv_idx, const int32_t *labels, int32_t bq,
+                                                 int32_t bk, float softmax_scale, void *O, void *stream) {
+  Dims dm{};
+  svg_status s;
+  if ((s = fp8_attn_checks(dims, Q8, qscale, K8, kscale, Vt8, O, bq, bk, &dm, 2)) != SVG_OK) return s;
+  if (!row_ptr || !kv_idx || !vamax) return fail(SVG_ERR_NULL, "block_sparse_attn_fp8pv_vt_layout: NULL pointer");
+  if (overlaps2(O, (size_t)dm.H * dm.N * dm.d * 2, vamax, (size_t)dm.H * dm.d * 4))
+    return fail(SVG_ERR_RANGE, "block_sparse_attn_fp8pv_vt_layout: O overlaps vamax");
+  return hip_status(svgk::launch_attn_fp8(dm, Q8, qscale, K8, kscale, Vt8, vamax, O, row_ptr, kv_idx, bq,
+                                          resolve_scale(softmax_scale, dm.d), labels, true, (hipStream_t)stream),
+                    "svg_block_sparse_attn_fp8pv_vt_layout");
 }
 
 // ---------------------------------------------------------------------------

@@ -22,6 +22,18 @@
 //                    (d = 128): K tiles of 64 rows x 128 bytes in LDS, four
 //                    32x32x64 MFMAs per tile and wave instead of sixteen
 //                    32x32x16 bf16 ones.
+//
+// The FP8 P.V mode codes the other product as well (also this library's
+// definition):
+//   - V: one scale per channel over the head's tokens, amax_d / 448, codes
+//     round_e4m3(fp32(v * (448 / amax_d))), stored key-tiled and transposed
+//     (chan_amax, layout_vt_fp8);
+//   - P: each probability 2^(y - m) against the lazy reference m (at most
+//     2^8, so no scale) coded round_e4m3(fp32(p)) by v_cvt_pk_fp8_f32;
+//   - P.V: four 32x32x64 MFMAs per tile and wave over the codes (instead of
+//     sixteen bf16 ones), and the row sum as a fifth MFMA of the codes
+//     against a block of ones (no vector-ALU sum); the channel scales
+//     multiply O once at the end.
 #include <type_traits>
 
 #include "attn_vt_core.h"
@@ -137,6 +149,106 @@ void layout_fp8(const u32x4 *__restrict__ X, uint8_t *__restrict__ X8, float *__
 }
 
 // ---------------------------------------------------------------------------
+// V for the FP8 P.V mode (d = 128).
+//
+// The V^T code tile of 64 keys is 128 rows (dims) of 64 bytes.  Byte j of a
+// row holds key tau(j): j = 32 hi + b holds key 32 (b >> 4) + 16 ((b >> 3) & 1)
+// + 8 hi + (b & 7), the order in which a lane of lane half hi holds its 32
+// probabilities of a tile after Q K^T (its 16 scores of each 32-key block,
+// keys 16 (r >> 3) + 8 hi + (r & 7)).  Then a lane's 32 A-operand bytes (row
+// d, bytes 32 hi ..) and its 32 B-operand bytes (its probabilities in
+// register order) name the same keys slot by slot.
+
+constexpr int kV8Bytes = 128 * 64;     // V^T code tile: 128 dims x 64 keys
+constexpr int kChanRows = 512;         // rows per chan_amax work-group
+
+__device__ __forceinline__ int v8_key(int j) {
+  const int hi = j >> 5, b = j & 31;
+  return 32 * (b >> 4) + 16 * ((b >> 3) & 1) + 8 * hi + (b & 7);
+}
+
+__global__ __launch_bounds__(256)
+void zero_f32(float *__restrict__ x, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) x[i] = 0.f;
+}
+
+// Largest magnitude of each channel (d = 128) over the head's tokens, as
+// the bits of a non-negative float (their unsigned order is the float
+// order): one work-group per (kChanRows rows, head) takes the maximum of its
+// rows and raises amax[h][d] with an atomic maximum (zeroed beforehand).
+__global__ __launch_bounds__(256)
+void chan_amax(const u32x4 *__restrict__ X, uint32_t *__restrict__ amax, int N) {
+  constexpr int D = 128, CPR = D / 8;   // 16 units of 8 dims per row
+  __shared__ float red[16][D];
+  const int h = blockIdx.y, tid = threadIdx.x;
+  const int u = tid & (CPR - 1), r0 = blockIdx.x * kChanRows + (tid >> 4);
+  const u32x4 *Xh = X + (size_t)h * N * CPR;
+  float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int r = r0; r < N && r < (int)(blockIdx.x + 1) * kChanRows; r += 16) {
+    const u32x4 w = Xh[(size_t)r * CPR + u];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      m[2 * i] = fmaxf(m[2 * i], fabsf(__uint_as_float(w[i] << 16)));
+      m[2 * i + 1] = fmaxf(m[2 * i + 1], fabsf(__uint_as_float(w[i] & 0xFFFF0000u)));
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) red[tid >> 4][8 * u + i] = m[i];
+  __syncthreads();
+  if (tid < D) {
+    float a = red[0][tid];
+    for (int g = 1; g < 16; ++g) a = fmaxf(a, red[g][tid]);
+    atomicMax(amax + (size_t)h * D + tid, __float_as_uint(a));
+  }
+}
+
+// One work-group per (64-key tile of the executing layout, head): the rows
+// gathered as the layout permute does, then each 16-byte unit of the code
+// tile (row d = u / 4, bytes 16 (u % 4) ..) coded from the channel's amax.
+// Keys past N are zero codes.
+__global__ __launch_bounds__(256)
+void layout_vt_fp8(const u32x4 *__restrict__ X, const float *__restrict__ amax, u32x4 *__restrict__ Y,
+                   const int32_t *__restrict__ labels, int F, int S, int N, int nkb) {
+  constexpr int D = 128, CPR = D / 8, STR = D + 8;   // padded LDS row (halfwords)
+  __shared__ __attribute__((aligned(16))) uint16_t t[64 * STR];
+  __shared__ float inv[D];
+  const int kb = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const bool perm = labels == nullptr || labels[h] == 1;
+  const u32x4 *Xh = X + (size_t)h * N * CPR;
+  if (tid < D) inv[tid] = quant_inv(amax[(size_t)h * D + tid]);
+  for (int u = tid; u < 64 * CPR; u += 256) {
+    const int row = u / CPR, ch = u - row * CPR;
+    const int r = kb * 64 + row;
+    u32x4 v = u32x4{0, 0, 0, 0};
+    if (r < N) {
+      int src = r;
+      if (perm && r < F * S) {
+        const int p = r / F, f = r - p * F;
+        src = f * S + p;
+      }
+      v = Xh[(size_t)src * CPR + ch];
+    }
+    *reinterpret_cast<u32x4 *>(t + row * STR + ch * 8) = v;
+  }
+  __syncthreads();
+  u32x4 *Yt = Y + ((size_t)h * nkb + kb) * (kV8Bytes / 16);
+  for (int u = tid; u < kV8Bytes / 16; u += 256) {
+    const int d = u >> 2, j0 = (u & 3) * 16;
+    const float s = inv[d];
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float f[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) f[e] = __uint_as_float((uint32_t)t[v8_key(j0 + 4 * i + e) * STR + d] << 16) * s;
+      w[i] = (uint32_t)cvt_fp8x2<true>(f[2], f[3], cvt_fp8x2<false>(f[0], f[1], 0));
+    }
+    Yt[u] = u32x4{w[0], w[1], w[2], w[3]};
+  }
+}
+
+// ---------------------------------------------------------------------------
 // The attention (d = 128).
 
 constexpr int kD = 128;
@@ -147,6 +259,7 @@ constexpr int kVtBytes = DTile<kD>::TBYTES;     // bf16 V^T tile
 constexpr int kK8Blocks = kK8Bytes / 1024;      // 1 KB DMA blocks: one per wave
 constexpr int kVBlocks = kVtBytes / 1024;       // two per wave
 static_assert(kK8Blocks == kNW && kVBlocks == 2 * kNW, "DMA split assumes d = 128 and 8 waves");
+static_assert(kV8Bytes / 1024 == kNW, "one DMA block of the V^T code tile per wave");
 
 // K8 tile row r: 16-byte chunk c stored at position c ^ swz8(r).  The 16
 // lanes a ds_read_b128 serves (16 keys, one logical chunk) then cover all 64
@@ -172,9 +285,13 @@ __device__ __forceinline__ f32x16 mfma_fp8(const i32x8 &a, const i32x8 &b, const
 // as vt_attend; tsc(j) gives tile j's K scale (read early, like the entry).
 // cq = softmax_scale * log2(e) * this lane's Q scale (> 0).  On return o
 // and l_run are the un-normalised output and the lane's partial row sum.
-template <typename EntRaw, typename TileScale, typename Prep>
+// PV8: V^T is the code tile (Vth points at the head's code tiles), P.V and
+// the row sum run on the fp8 matrix cores once the tile's 32 probabilities
+// are coded, and l_run is half the row sum (the partner lane holds the same
+// sum, and the store adds the two halves).
+template <bool PV8, typename EntRaw, typename TileScale, typename Prep>
 __device__ __forceinline__ void vt_attend_qk8(int nt, EntRaw ent_raw, TileScale tsc, Prep prep,
-                                              const uint8_t *__restrict__ K8h, const bf16_t *__restrict__ Vth,
+                                              const uint8_t *__restrict__ K8h, const void *__restrict__ Vth,
                                               int N, char *k0, char *k1, char *k2, char *v0, char *v1, char *v2,
                                               const i32x8 (&qf)[2], float cq, int wave, int lane,
                                               f32x16 (&o)[kD / 32], float &l_run) {
@@ -204,12 +321,28 @@ __device__ __forceinline__ void vt_attend_qk8(int nt, EntRaw ent_raw, TileScale 
 #pragma unroll
     for (int u = 0; u < 2; ++u) koff[ks][u] = krow * kD + (((4 * ks + 2 * hi + u) ^ swz8(krow)) << 4);
   int voff[4], vdma[2];
-  vt_offsets(l32, hi, voff);
-  vt_dma_offsets<kD, kNW>(wave, lane, vdma);
+  if constexpr (PV8) {
+    // code tile row d: 16-byte chunk c at position c ^ ((d >> 2) & 3), so the
+    // 16 rows of one ds_read_b128 (one logical chunk) cover all 64 banks; a
+    // lane reads chunks 2 hi and 2 hi + 1 of row 32 db + l32
+    const int sw = (l32 >> 2) & 3;
+    voff[0] = l32 * 64 + (((2 * hi) ^ sw) << 4);
+    voff[1] = l32 * 64 + (((2 * hi + 1) ^ sw) << 4);
+    const int p = wave * 64 + lane;            // DMA unit: LDS position p, row p / 4
+    const int row = p >> 2;
+    vdma[0] = row * 64 + (((p & 3) ^ ((row >> 2) & 3)) << 4);
+  } else {
+    vt_offsets(l32, hi, voff);
+    vt_dma_offsets<kD, kNW>(wave, lane, vdma);
+  }
   const int kdma = k8_dma_offset(wave, lane);
+  constexpr int kVTile = PV8 ? kV8Bytes : kVtBytes;
 #pragma unroll
   for (int db = 0; db < kD / 32; ++db) o[db] = f32x16{};
   l_run = 0.f;
+  f32x16 lsum = f32x16{};     // PV8: the row sum, as the product of the codes with a block of ones
+  const i32x8 ones8 = i32x8{0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                            0x38383838, 0x38383838, 0x38383838, 0x38383838};   // E4M3 1.0
   float mref_c = -INFINITY;   // reference maximum of the scaled exponent arguments
 
   auto k_rsrc = [&](int e) {
@@ -219,13 +352,17 @@ __device__ __forceinline__ void vt_attend_qk8(int nt, EntRaw ent_raw, TileScale 
   };
   auto v_rsrc = [&](int e) {
     const int kb = e & 0xFFFFFF;
-    return tile_rsrc(reinterpret_cast<const char *>(Vth) + (size_t)kb * kVtBytes, kVtBytes);
+    return tile_rsrc(reinterpret_cast<const char *>(Vth) + (size_t)kb * kVTile, kVTile);
   };
   auto dma_k = [&](int e, char *tile) { dma_block(k_rsrc(e), tile, wave, kdma); };
   auto dma_v = [&](int e, char *tile) {
     const auto r = v_rsrc(e);
-    dma_block(r, tile, 2 * wave, vdma[0]);
-    dma_block(r, tile, 2 * wave + 1, vdma[1]);
+    if constexpr (PV8) {
+      dma_block(r, tile, wave, vdma[0]);
+    } else {
+      dma_block(r, tile, 2 * wave, vdma[0]);
+      dma_block(r, tile, 2 * wave + 1, vdma[1]);
+    }
   };
   auto kread = [&](const char *Kt, int ks, int b, i32x8 &a) {
     const i32x4 x = *reinterpret_cast<const i32x4 *>(Kt + koff[ks][0] + b * 32 * kD);
@@ -292,6 +429,7 @@ __device__ __forceinline__ void vt_attend_qk8(int nt, EntRaw ent_raw, TileScale 
       const float alpha = move ? fast_exp2(mref_c - mxc) : 1.f;
       mref_c = move ? mxc : mref_c;
       l_run *= alpha;
+      if constexpr (PV8) lsum *= alpha;
 #pragma unroll
       for (int db = 0; db < kD / 32; ++db) o[db] *= alpha;
     }
@@ -303,16 +441,22 @@ __device__ __forceinline__ void vt_attend_qk8(int nt, EntRaw ent_raw, TileScale 
     // its last exponential (V^T operands read two sub-steps ahead); the
     // three DMAs of V(it+2) and K(it+3) spread over sub-steps 0, 3 and 6.
     uint32_t pw[16];
+    int pw8[8];                            // PV8: byte b of the 32 = code of score b (s0 then s1)
     float rs = 0.f;
     auto pv_at = [&](int j) { return 2 * j + 2; };
     auto rd_at = [&](int j) { return 2 * j; };
     bf16x8 va[2][kD / 32];
+    i32x8 va8[kD / 32];
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       if (ks == 0) dma_block(rk, Kdst, wave, kdma);
-      if (ks == 3) dma_block(rv, Vdst, 2 * wave, vdma[0]);
-      if (ks == 6) dma_block(rv, Vdst, 2 * wave + 1, vdma[1]);
+      if constexpr (PV8) {
+        if (ks == 4) dma_block(rv, Vdst, wave, vdma[0]);
+      } else {
+        if (ks == 3) dma_block(rv, Vdst, 2 * wave, vdma[0]);
+        if (ks == 6) dma_block(rv, Vdst, 2 * wave + 1, vdma[1]);
+      }
       if (ks == 0) n0 = mfma_fp8(a0, qf[1], n0);
       if (ks == 1) n1 = mfma_fp8(a1, qf[1], n1);
 #pragma unroll
@@ -322,8 +466,25 @@ __device__ __forceinline__ void vt_attend_qk8(int nt, EntRaw ent_raw, TileScale 
         const float x1 = idx < 16 ? s0[idx + 1] : s1[idx - 15];
         const float p0 = fast_exp2(__builtin_fmaf(x0, cc, -mc));
         const float p1 = fast_exp2(__builtin_fmaf(x1, cc, -mc));
-        pw[idx >> 1] = pack_bf16x2(p0, p1);
-        rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[idx >> 1]), kOnesBf16x2, rs, false);
+        if constexpr (PV8) {
+          if ((idx & 3) == 0) pw8[idx >> 2] = cvt_fp8x2<false>(p0, p1, 0);
+          else pw8[idx >> 2] = cvt_fp8x2<true>(p0, p1, pw8[idx >> 2]);
+        } else {
+          pw[idx >> 1] = pack_bf16x2(p0, p1);
+          rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[idx >> 1]), kOnesBf16x2, rs, false);
+        }
+      }
+      if constexpr (PV8) {
+        // the code tile's operands of dim block ks - 4, read in the second
+        // half of the step (V(it) stays in its stage for the whole step)
+        if (ks >= 4) {
+          const int db = ks - 4;
+          const i32x4 x = *reinterpret_cast<const i32x4 *>(Vc + voff[0] + db * 32 * 64);
+          const i32x4 y = *reinterpret_cast<const i32x4 *>(Vc + voff[1] + db * 32 * 64);
+          va8[db] = i32x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        continue;
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -341,16 +502,22 @@ __device__ __forceinline__ void vt_attend_qk8(int nt, EntRaw ent_raw, TileScale 
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    {  // the last chunk's P.V, due after the last sub-step
+    if constexpr (PV8) {  // the tile's P.V and row sum on the coded probabilities
+      const i32x8 p8 = i32x8{pw8[0], pw8[1], pw8[2], pw8[3], pw8[4], pw8[5], pw8[6], pw8[7]};
+#pragma unroll
+      for (int db = 0; db < kD / 32; ++db) o[db] = mfma_fp8(va8[db], p8, o[db]);
+      lsum = mfma_fp8(ones8, p8, lsum);
+    } else {  // the last chunk's P.V, due after the last sub-step
       const bf16x8 pj = __builtin_bit_cast(bf16x8, u32x4{pw[12], pw[13], pw[14], pw[15]});
 #pragma unroll
       for (int db = 0; db < kD / 32; ++db) o[db] = mfma32(va[1][db], pj, o[db]);
+      l_run += rs;
     }
-    l_run += rs;
 
     // (C) K(it+2) and V(it+1), issued one step ago, have landed once at most
-    // this step's 3 DMAs are outstanding; then every wave's share is in
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(3));
+    // this step's DMAs (3; PV8: 2) are outstanding; then every wave's share
+    // is in
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(PV8 ? 2 : 3));
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -372,20 +539,25 @@ __device__ __forceinline__ void vt_attend_qk8(int nt, EntRaw ent_raw, TileScale 
   }
   if (it < nt) step(C0{});
   if (it < nt) step(C1{});
+  if constexpr (PV8) l_run = 0.5f * lsum[0];
 }
 
-template <int BQ, bool DENSE>
+// PV8: Vt holds the V^T code tiles and vamax [H][128] the channels' largest
+// magnitudes (the channel scale is amax / 448, applied to O at the end).
+template <int BQ, bool DENSE, bool PV8>
 __global__ __launch_bounds__(kWgRows * 2, 1)
 void attn_fwd_fp8(const uint8_t *__restrict__ Q8, const float *__restrict__ qscale, const uint8_t *__restrict__ K8,
-                  const float *__restrict__ kscale, const bf16_t *__restrict__ Vt, bf16_t *__restrict__ O,
-                  const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ kv_idx, int N, int nqb, int nkb,
-                  int ngrp, float c, const int32_t *__restrict__ labels, int qo_orig, int F, int S) {
+                  const float *__restrict__ kscale, const void *__restrict__ Vt, const float *__restrict__ vamax,
+                  bf16_t *__restrict__ O, const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ kv_idx,
+                  int N, int nqb, int nkb, int ngrp, float c, const int32_t *__restrict__ labels, int qo_orig, int F,
+                  int S) {
   constexpr int G = kWgRows / BQ;
   constexpr int OWN_ALL = (1 << G) - 1;
+  constexpr int kVTile = PV8 ? kV8Bytes : kVtBytes;
   // V^T stages first (uppercase names sort first): their reads take
   // immediate offsets below 64 KB
-  __shared__ __attribute__((aligned(1024))) char k0[kK8Bytes], k1[kK8Bytes], k2[kK8Bytes], V0[kVtBytes],
-      V1[kVtBytes], V2[kVtBytes];
+  __shared__ __attribute__((aligned(1024))) char k0[kK8Bytes], k1[kK8Bytes], k2[kK8Bytes], V0[kVTile],
+      V1[kVTile], V2[kVTile];
   __shared__ int ulist[DENSE ? 1 : kMaxKb];
   __shared__ float uscale[kMaxKb];
   __shared__ uint32_t bits[DENSE ? 1 : G * kWords];
@@ -402,7 +574,7 @@ void attn_fwd_fp8(const uint8_t *__restrict__ Q8, const float *__restrict__ qsca
   const size_t hoff = (size_t)h * N * kD;
   const uint8_t *K8h = K8 + hoff;
   const float *ksh = kscale + (size_t)h * nkb;
-  const bf16_t *Vth = Vt + (size_t)h * nkb * (BK * kD);
+  const char *Vth = reinterpret_cast<const char *>(Vt) + (size_t)h * nkb * kVTile;
   bf16_t *Oh = O + hoff;
   const int qrow = grp * kWgRows + wave * 32 + l32;
   int qsrc = qrow;
@@ -470,28 +642,44 @@ void attn_fwd_fp8(const uint8_t *__restrict__ Q8, const float *__restrict__ qsca
   };
   f32x16 o[kD / 32];
   float l_run;
-  vt_attend_qk8(nt, ent_raw, tsc, prep, K8h, Vth, N, k0, k1, k2, V0, V1, V2, qf, cq, wave, lane, o, l_run);
+  vt_attend_qk8<PV8>(nt, ent_raw, tsc, prep, K8h, Vth, N, k0, k1, k2, V0, V1, V2, qf, cq, wave, lane, o, l_run);
   __builtin_amdgcn_s_waitcnt(0);  // no DMA may land after the work-group ends
+  if constexpr (PV8) {  // the channel scales: this lane's dims 32 db + 8 g + 4 hi + 0..3
+    const float *va = vamax + (size_t)h * kD;
+#pragma unroll
+    for (int db = 0; db < kD / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 a = *reinterpret_cast<const f32x4 *>(va + 32 * db + 8 * g + 4 * hi);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o[db][4 * g + q] *= a[q] / kE4M3Max;
+      }
+  }
   store_o<kD>(qrow < N ? Oh + (size_t)qsrc * kD : nullptr, o, l_run, hi);
 }
 
 template <int BQ>
 hipError_t launch_fp8(const Dims &dm, const void *Q8, const float *qs, const void *K8, const float *ks,
-                      const void *Vt, void *O, const int32_t *row_ptr, const int32_t *kv_idx, float c,
-                      const int32_t *labels, int qo_orig, hipStream_t st) {
+                      const void *Vt, const float *vamax, void *O, const int32_t *row_ptr, const int32_t *kv_idx,
+                      float c, const int32_t *labels, int qo_orig, hipStream_t st) {
   constexpr int G = kWgRows / BQ;
   const int nqb = (dm.N + BQ - 1) / BQ, nkb = (dm.N + BK - 1) / BK;
   const int ngrp = (nqb + G - 1) / G;
   if (dm.H * ngrp == 0) return hipSuccess;
   const int grid = dm.H * ngrp;
-  if (row_ptr == nullptr)
-    hipLaunchKernelGGL((attn_fwd_fp8<BQ, true>), dim3(grid), dim3(kWgRows * 2), 0, st, (const uint8_t *)Q8, qs,
-                       (const uint8_t *)K8, ks, (const bf16_t *)Vt, (bf16_t *)O, row_ptr, kv_idx, dm.N, nqb, nkb,
-                       ngrp, c, labels, qo_orig, dm.F, dm.S);
-  else
-    hipLaunchKernelGGL((attn_fwd_fp8<BQ, false>), dim3(grid), dim3(kWgRows * 2), 0, st, (const uint8_t *)Q8, qs,
-                       (const uint8_t *)K8, ks, (const bf16_t *)Vt, (bf16_t *)O, row_ptr, kv_idx, dm.N, nqb, nkb,
-                       ngrp, c, labels, qo_orig, dm.F, dm.S);
+#define SVG_FP8_LAUNCH(DENSE, PV8)                                                                              \
+  hipLaunchKernelGGL((attn_fwd_fp8<BQ, DENSE, PV8>), dim3(grid), dim3(kWgRows * 2), 0, st, (const uint8_t *)Q8, qs, \
+                     (const uint8_t *)K8, ks, Vt, vamax, (bf16_t *)O, row_ptr, kv_idx, dm.N, nqb, nkb, ngrp, c,     \
+                     labels, qo_orig, dm.F, dm.S)
+  if (vamax != nullptr) {
+    if (row_ptr == nullptr) return hipErrorInvalidValue;   // the P.V mode is block-sparse only
+    SVG_FP8_LAUNCH(false, true);
+  } else if (row_ptr == nullptr) {
+    SVG_FP8_LAUNCH(true, false);
+  } else {
+    SVG_FP8_LAUNCH(false, false);
+  }
+#undef SVG_FP8_LAUNCH
   return hipGetLastError();
 }
 
@@ -525,13 +713,30 @@ hipError_t launch_layout_fp8(const Dims &dm, const void *X, void *X8, float *sca
 }
 
 hipError_t launch_attn_fp8(const Dims &dm, const void *Q8, const float *qscale, const void *K8, const float *kscale,
-                           const void *Vt, void *O, const int32_t *row_ptr, const int32_t *kv_idx, int bq,
-                           float scale, const int32_t *labels, bool qo_orig, hipStream_t st) {
+                           const void *Vt, const float *vamax, void *O, const int32_t *row_ptr,
+                           const int32_t *kv_idx, int bq, float scale, const int32_t *labels, bool qo_orig,
+                           hipStream_t st) {
   if (dm.d != 128) return hipErrorInvalidValue;
   const float c = scale * kLog2e;
-  if (bq == 128) return launch_fp8<128>(dm, Q8, qscale, K8, kscale, Vt, O, row_ptr, kv_idx, c, labels, qo_orig, st);
-  if (bq == 64) return launch_fp8<64>(dm, Q8, qscale, K8, kscale, Vt, O, row_ptr, kv_idx, c, labels, qo_orig, st);
+  if (bq == 128)
+    return launch_fp8<128>(dm, Q8, qscale, K8, kscale, Vt, vamax, O, row_ptr, kv_idx, c, labels, qo_orig, st);
+  if (bq == 64)
+    return launch_fp8<64>(dm, Q8, qscale, K8, kscale, Vt, vamax, O, row_ptr, kv_idx, c, labels, qo_orig, st);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_layout_vt_fp8(const Dims &dm, const void *V, void *Vt8, float *vamax, const int32_t *labels,
+                                hipStream_t st) {
+  if (dm.d != 128) return hipErrorInvalidValue;
+  const int nkb = (dm.N + 63) / 64;
+  if (dm.N == 0 || dm.H == 0) return hipSuccess;
+  const int n = dm.H * 128;
+  hipLaunchKernelGGL(zero_f32, dim3((n + 255) / 256), dim3(256), 0, st, vamax, n);
+  hipLaunchKernelGGL(chan_amax, dim3((dm.N + kChanRows - 1) / kChanRows, dm.H), dim3(256), 0, st, (const u32x4 *)V,
+                     reinterpret_cast<uint32_t *>(vamax), dm.N);
+  hipLaunchKernelGGL(layout_vt_fp8, dim3(nkb, dm.H), dim3(256), 0, st, (const u32x4 *)V, vamax, (u32x4 *)Vt8, labels,
+                     dm.F, dm.S, dm.N, nkb);
+  return hipGetLastError();
 }
 
 }  // namespace svgk

@@ -113,9 +113,15 @@ hipError_t launch_attn_vt_ear(const Dims &dm, const void *Q, const void *K, cons
 hipError_t launch_quant_rows_fp8(const Dims &dm, const void *X, void *X8, float *scale, hipStream_t st);
 hipError_t launch_layout_fp8(const Dims &dm, const void *X, void *X8, float *scale, const int32_t *labels,
                              hipStream_t st);
+// vamax non-null: the FP8 P.V mode (Vt = V^T code tiles of launch_layout_vt_fp8)
 hipError_t launch_attn_fp8(const Dims &dm, const void *Q8, const float *qscale, const void *K8, const float *kscale,
-                           const void *Vt, void *O, const int32_t *row_ptr, const int32_t *kv_idx, int bq,
-                           float scale, const int32_t *labels, bool qo_orig, hipStream_t st);
+                           const void *Vt, const float *vamax, void *O, const int32_t *row_ptr,
+                           const int32_t *kv_idx, int bq, float scale, const int32_t *labels, bool qo_orig,
+                           hipStream_t st);
+// V (d = 128) -> per-channel largest magnitudes vamax [H][128] and the V^T
+// code tiles [H][ceil(N/64)][128][64] of the executing layout (per labels)
+hipError_t launch_layout_vt_fp8(const Dims &dm, const void *V, void *Vt8, float *vamax, const int32_t *labels,
+                                hipStream_t st);
 hipError_t launch_layout(const Dims &dm, int elem_bytes, const void *X, void *Y,
                          const int32_t *labels, bool inverse, hipStream_t st);
 hipError_t launch_permute_rows(const Dims &dm, int elem_bytes, const void *X, const int32_t *perm,

@@ -74,6 +74,8 @@ SIGNATURES = {
     "svg_layout_permute_fp8": [_DIMS, _I, _P, _P, _P, _P, _P],
     "svg_block_sparse_attn_fp8_vt_layout": [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _F, _P, _P],
     "svg_dense_attn_fp8_vt": [_DIMS, _P, _P, _P, _P, _P, _I, _I, _F, _P, _P],
+    "svg_layout_permute_vt_fp8": [_DIMS, _I, _P, _P, _P, _P, _P],
+    "svg_block_sparse_attn_fp8pv_vt_layout": [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _F, _P, _P],
     "svg2_workspace_bytes": [_I, _DIMS, _I, _I],
     "svg_kmeans": [_DIMS, _I, _P, _I, _I, _P, _P, _P, _P, _P, _Z, _P],
     "svg_kmeans_noalloc": [_DIMS, _I, _P, _I, _I, _P, _P, _P, _P, _P],
@@ -586,6 +588,49 @@ def svg_dense_attn_fp8_vt(q8, qs, k8, ks, vt, F, S, T, bq, bk, scale=-1.0, out=N
     _need(out, "out", torch.bfloat16, H * N * d)
     _check(_lib.svg_dense_attn_fp8_vt(ctypes.byref(dm), _ptr(q8), _ptr(qs), _ptr(k8), _ptr(ks), _ptr(vt), bq, bk,
                                       scale, _ptr(out), _stream()), "svg_dense_attn_fp8_vt")
+    return out
+
+
+def svg_layout_permute_vt_fp8(v, F, S, T, labels=None, out=None, amax=None):
+    """V (bf16 [H][N][128]) for the FP8 P.V mode: each channel's largest
+    magnitude (float32 [H][128]) and the key-tiled V^T codes of the executing
+    layout (uint8, ceil(N/64) tiles of 128 x 64 per head)."""
+    dm = _video_dims(v, F, S, T, "V")
+    H, N, d = v.shape
+    dt = _dtype(v)
+    _need(v, "V", torch.bfloat16, v.numel())
+    _labels(labels, H)
+    nt = svg_vt_elems(H, N, d)
+    out = torch.empty(nt, dtype=torch.uint8, device=v.device) if out is None else out
+    amax = torch.empty(H, d, dtype=torch.float32, device=v.device) if amax is None else amax
+    _need(out, "Vt8", torch.uint8, nt)
+    _need(amax, "vamax", torch.float32, H * d)
+    _check(_lib.svg_layout_permute_vt_fp8(ctypes.byref(dm), dt, _ptr(v), _ptr(out), _ptr(amax), _ptr(labels),
+                                          _stream()), "svg_layout_permute_vt_fp8")
+    return out, amax
+
+
+def svg_block_sparse_attn_fp8pv_vt_layout(q8, qs, k8, ks, vt8, vamax, row_ptr, kv_idx, labels, F, S, T, bq, bk,
+                                          scale=-1.0, out=None):
+    """The FP8 P.V mode: FP8 Q K^T as svg_block_sparse_attn_fp8_vt_layout,
+    then probabilities coded after the lazy reference and P.V on the V codes
+    (svg_layout_permute_vt_fp8); O bf16 in the original token order."""
+    dm = _video_dims(q8, F, S, T, "Q8")
+    H, N, d = q8.shape
+    _need(q8, "Q8", torch.uint8, H * N * d)
+    _need(k8, "K8", torch.uint8, H * N * d)
+    _need(qs, "qscale", torch.float32, H * N)
+    _need(ks, "kscale", torch.float32, H * (-(-N // 64)))
+    _need(vt8, "Vt8", torch.uint8, svg_vt_elems(H, N, d))
+    _need(vamax, "vamax", torch.float32, H * d)
+    _lists(row_ptr, kv_idx, H, N, bq)
+    _labels(labels, H)
+    out = torch.empty(H, N, d, dtype=torch.bfloat16, device=q8.device) if out is None else out
+    _need(out, "out", torch.bfloat16, H * N * d)
+    _check(_lib.svg_block_sparse_attn_fp8pv_vt_layout(ctypes.byref(dm), _ptr(q8), _ptr(qs), _ptr(k8), _ptr(ks),
+                                                      _ptr(vt8), _ptr(vamax), _ptr(row_ptr), _ptr(kv_idx),
+                                                      _ptr(labels), bq, bk, scale, _ptr(out), _stream()),
+           "svg_block_sparse_attn_fp8pv_vt_layout")
     return out
 
 
