@@ -14,7 +14,8 @@ step time.  Also reported: the attention kernel's own rate (HIP events on
 its stream), the speedup over this library's dense attention on the same
 tensors, per-stage times, the MFMA roofline fraction, and the CPU oracle's
 rate on a bounded sample.  The default run adds, as extra keys of the same
-line: the same layer step with the FP8 attention ("fp8") and with SVG-EAR's
+line: the same layer step with the FP8 attention ("fp8": FP8 Q K^T, and in
+"fp8.pv" FP8 P.V as well) and with SVG-EAR's
 compensation and routing ("ear"), the
 CogVideoX-shaped layer step ("cogvideox_shape": 13 x 1350 + 224 tokens, 8
 heads, d = 64) and the SVG2 semantic path on the CogVideoX-shaped mixture
@@ -864,6 +865,58 @@ def layer_bench(args, w, ks, wt, use_vt=True, steps=None, warmup=None, fp8_leg=F
             "stage_ms": {kk: round(vv, 4) for kk, vv in st8.items()},
             "rel_l2_vs_bf16_output": round(float(diff.norm() / o.float().norm()), 4)}
         print(f"[bench] {w.name}: fp8 step {ms8:.3f} ms, fp8 attention {attn8:.3f} ms", file=sys.stderr, flush=True)
+
+        # The FP8 P.V mode: V coded per channel into key-tiled V^T code tiles
+        # (instead of the bf16 V^T), probabilities coded after the lazy
+        # reference, P.V and the row sum on the FP8 matrix cores.
+        vt8 = torch.empty(svg.svg_vt_elems(H, N, d), dtype=torch.uint8, device=dev)
+        vam = torch.empty(H, d, dtype=torch.float32, device=dev)
+        o8p = torch.empty_like(q)
+
+        def step8p(i=None, stage_events=None):
+            def mark(j):
+                if stage_events is not None:
+                    stage_events[j].record(stream)
+            mark(0)
+            front(mark)
+            svg.svg_layout_permute_fp8(k, F, S, T, labels, out=k8, scale=ksc)
+            svg.svg_quantize_fp8_rows(q, out=q8, scale=qsc)
+            svg.svg_layout_permute_vt_fp8(v, F, S, T, labels, out=vt8, amax=vam)
+            mark(3)
+            if i is not None:
+                f0[i].record(stream)
+            svg.svg_block_sparse_attn_fp8pv_vt_layout(q8, qsc, k8, ksc, vt8, vam, row_ptr, kv_idx, labels, F, S, T,
+                                                      bq, bk, out=o8p)
+            if i is not None:
+                f1[i].record(stream)
+            mark(4)
+
+        for _ in range(warmup):
+            step8p()
+        torch.cuda.synchronize()
+        t_start.record(stream)
+        for i in range(steps):
+            step8p(i)
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        ms8p = t_start.elapsed_time(t_end) / steps
+        attn8p = float(np.mean([a.elapsed_time(b) for a, b in zip(f0, f1)]))
+        step8p(None, se)
+        torch.cuda.synchronize()
+        st8p = {n: se[j].elapsed_time(se[j + 1]) for j, n in
+                enumerate(["profile", "mask_and_lists", "quantize_qkv_permute_k_vt", "attention"])}
+        diffp = (o8p.float() - o.float())
+        result["fp8"]["pv"] = {
+            "mode": "fp8 e4m3 Q K^T as above; V per-channel codes, P coded after the lazy reference, P.V fp8",
+            "ms_per_step": round(ms8p, 4), "value": round(flops / (ms8p * 1e-3) / 1e12, 3),
+            "attn_ms": round(attn8p, 4), "attn_tflops": round(flops / (attn8p * 1e-3) / 1e12, 2),
+            "speedup_vs_bf16_attn": round(attn_ms / attn8p, 3),
+            "speedup_vs_dense_bf16_attn": round(dense_ms / attn8p, 3),
+            "stage_ms": {kk: round(vv, 4) for kk, vv in st8p.items()},
+            "rel_l2_vs_bf16_output": round(float(diffp.norm() / o.float().norm()), 4)}
+        del vt8, o8p
+        print(f"[bench] {w.name}: fp8 P.V step {ms8p:.3f} ms, attention {attn8p:.3f} ms", file=sys.stderr,
+              flush=True)
     if fp8_leg and use_vt:
         # The same step with SVG-EAR: block statistics of K / V^T, routing of
         # EAR_ROUTE_K skipped blocks per q-block into the exact sets, their

@@ -134,6 +134,13 @@ def test_fused_ear_and_fp8_attention_arguments():
            i32(H), F, S, T, 64, 64)
     raises(ValueError, "kscale must have", svg.svg_dense_attn_fp8_vt, q8, qs, k8, torch.zeros(H, nkb - 1), vt,
            F, S, T, 64, 64)
+    vt8, va = torch.zeros(svg.svg_vt_elems(H, N, d), dtype=torch.uint8), torch.zeros(H, d)
+    raises(TypeError, "V must be torch.bfloat16", svg.svg_layout_permute_vt_fp8, torch.zeros(H, N, d), F, S, T)
+    raises(ValueError, "vamax must have", svg.svg_layout_permute_vt_fp8, k, F, S, T, None, None, torch.zeros(H, d - 1))
+    raises(TypeError, "Vt8 must be torch.uint8", svg.svg_block_sparse_attn_fp8pv_vt_layout, q8, qs, k8, ks, vt, va,
+           rp, ki, i32(H), F, S, T, 64, 64)
+    raises(ValueError, "vamax must have", svg.svg_block_sparse_attn_fp8pv_vt_layout, q8, qs, k8, ks, vt8,
+           torch.zeros(H, d + 1), rp, ki, i32(H), F, S, T, 64, 64)
 
 
 def test_varlen_vt_and_hva_arguments():
