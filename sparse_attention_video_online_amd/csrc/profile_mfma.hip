@@ -134,7 +134,7 @@ constexpr int kMaxRankSamples = 16384;
 // samples into work-groups changes; each sample's result has its own slot.
 __global__ __launch_bounds__(256)
 void profile_order(const int32_t *__restrict__ sample_idx, int n_s, int F, int S, int32_t *__restrict__ ord_t) {
-  __shared__ int cr[1024];
+  __shared__ __attribute__((aligned(16))) int cr[1024];
   const int s = blockIdx.x * 256 + threadIdx.x;
   const bool act = s < n_s;
   if (n_s > kMaxRankSamples) {
@@ -150,7 +150,18 @@ void profile_order(const int32_t *__restrict__ sample_idx, int n_s, int F, int S
     __syncthreads();
     for (int u = threadIdx.x; u < cnt; u += 256) cr[u] = rpos(sample_idx[base + u]);
     __syncthreads();
-    for (int u = 0; u < cnt; ++u) {
+    // four ranks a 16-byte LDS read, several reads in flight
+    const int c4 = cnt & ~3;
+#pragma unroll 4
+    for (int u = 0; u < c4; u += 4) {
+      const int4 q = *reinterpret_cast<const int4 *>(cr + u);
+      const int us = base + u;
+      rt += (q.x < r) || (q.x == r && us < s);
+      rt += (q.y < r) || (q.y == r && us + 1 < s);
+      rt += (q.z < r) || (q.z == r && us + 2 < s);
+      rt += (q.w < r) || (q.w == r && us + 3 < s);
+    }
+    for (int u = c4; u < cnt; ++u) {
       const int q = cr[u], us = base + u;
       rt += (q < r) || (q == r && us < s);
     }
