@@ -231,10 +231,12 @@ def oracle_pv8_original(q, k, v, F, S, T, label, bm, bq, qblocks=None):
 
 def check_pv8(got_rows, orow, bound, amb, what):
     """|GPU - oracle| within the bf16 bar plus the row's bound, and rel-L2
-    within the bf16 bar over the rows whose bound is below 1e-3; rows with
-    an ambiguous reference move are left out (none are expected)."""
+    within the bf16 bar over the rows whose bound is below 1e-3.  Rows whose
+    lazy-reference move lies within 1e-3 of the threshold (the fp32 logits
+    may decide it either way, and then every later code of the row differs)
+    are left out, at most 5% of a q-block's rows."""
     keep = ~amb
-    assert keep.mean() > 0.99, f"{what}: {int(amb.sum())} rows with an ambiguous reference move"
+    assert keep.mean() >= 0.95, f"{what}: {int(amb.sum())} rows with an ambiguous reference move"
     err = np.abs(got_rows - orow)[keep]
     lim = BF16_MAX_ABS + bound[keep][:, None]
     assert np.all(err <= lim), f"{what}: max excess {float((err - lim).max()):.3e}"
@@ -302,13 +304,13 @@ def test_fp8pv_layer_step_hunyuan_sampled_qblocks():
     del q, k, v, q8, k8, vt8, vt, o, o_qk8
     rng = np.random.default_rng(78)
     fixed = [0, (w.F * w.S) // w.bq, w.nqb - 1]
+    qbs_of = [sorted(set(fixed) | set(int(x) for x in rng.choice(w.nqb, size=3, replace=False))) for _ in range(8)]
 
     def head(h):
         label = int(lab[h])
         obm = masks.block_bitmap_ranges(label, w.F, w.S, w.T, w.ks, w.wt, w.bq, w.bk)
-        qbs = sorted(set(fixed) | set(int(x) for x in rng.choice(w.nqb, size=3, replace=False)))
         return h, oracle_pv8_original(host["q"][h], host["k"][h], host["v"][h], w.F, w.S, w.T, label, obm, w.bq,
-                                      qbs)
+                                      qbs_of[h])
 
     with concurrent.futures.ThreadPoolExecutor(max_workers=8) as ex:
         refs = list(ex.map(head, range(8)))
