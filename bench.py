@@ -522,6 +522,22 @@ def bench_svg2(args, steps=None, warmup=None, cpu=False):
     if not vt_diff < 2e-2:
         raise SystemExit(f"svg2: the two varlen kernels disagree (max abs {vt_diff})")
 
+    # The round of each head's k-means whose assignment equals the previous
+    # round's (None: none within the run): from there on the library skips
+    # the head's kernels, as every later round would repeat that round.
+    def fixed_point_round(x, kc, init):
+        prev, r = None, [None] * H
+        for n in range(1, w.iters + 1):
+            a_ = svg.svg_kmeans(x, kc, n, init)[0].cpu()
+            if prev is not None:
+                for h in range(H):
+                    if r[h] is None and torch.equal(a_[h], prev[h]):
+                        r[h] = n - 1
+            prev = a_
+        return r
+
+    fixed_q, fixed_k = fixed_point_round(q, w.kq, iq), fixed_point_round(k, w.kk, ik)
+
     # work: attention pairs from the selected clusters; bytes of the copies
     optr, oidx = ptr.cpu().numpy(), idx.cpu().numpy()
     qs, ks_ = np.diff(oq.cpu().numpy(), axis=1), np.diff(ok.cpu().numpy(), axis=1)
@@ -532,7 +548,6 @@ def bench_svg2(args, steps=None, warmup=None, cpu=False):
             pairs += int(qs[h, i]) * int(ks_[h, sel].sum())
     attn_flops = 4.0 * d * pairs
     gather_bytes = 3 * 2 * H * N * d * 2
-    km_flops = 3.0 * w.iters * H * N * d * (w.kq + w.kk)   # sub + fma per dim per centroid
     result = {
         "metric": "SVG2 semantic path ms per step (k-means, cluster sort, gathers, top-p, varlen attention)",
         "value": round(ms_per_step, 4), "unit": "ms", "n_gpus": 1, "steps": steps, "warmup": warmup,
@@ -548,7 +563,10 @@ def bench_svg2(args, steps=None, warmup=None, cpu=False):
         "varlen_vt_windows_kernel_ms": round(vt_ms, 4),
         "varlen_kernels_max_abs_diff": vt_diff,
         "gather_gbs": round(gather_bytes / (stage_ms["gather_qkv"] * 1e-3) / 1e9, 1),
-        "kmeans_vector_tflops": round(km_flops / ((stage_ms["kmeans_q"] + stage_ms["kmeans_k"]) * 1e-3) / 1e12, 2),
+        "kmeans_fixed_point_round": {"q": fixed_q, "k": fixed_k},
+        "kmeans_note": (f"{w.iters} Lloyd rounds per head; a head whose assignment stands still (the round above, "
+                        "0-based) is at a fixed point and its later rounds' kernels return at once: the outputs "
+                        f"are those of all {w.iters} rounds, bit for bit"),
     }
     if cpu:
         from oracle import svg2 as osvg2

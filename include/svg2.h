@@ -42,7 +42,11 @@ size_t svg2_workspace_bytes(svg2_op op, const svg_dims *dims, int32_t a, int32_t
  *       index;
  *     - update: mean of the members; an empty cluster keeps its centroid.
  *   Outputs the last assignment (int32 [H][N]), its centroids (double
- *   [H][k][d]) and the sizes (int32 [H][k]).  For bf16 X the member sums
+ *   [H][k][d]) and the sizes (int32 [H][k]).  A round whose assignment
+ *   equals the previous round's is a fixed point of these two steps: every
+ *   later round would repeat it.  The kernels of a head's remaining rounds
+ *   then return at once; the outputs are those of all `iters` rounds, bit
+ *   for bit.  For bf16 X the member sums
  *   are exact in double, so equal to the index-order sums, while the
  *   exponent span of a dimension's nonzero member values is at most
  *   45 - log2(cluster size) bits.

@@ -19,6 +19,34 @@ namespace {
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
+// Fixed point of Lloyd's map: an assignment equal to the previous one gives
+// back, through the (deterministic) update, the centroids it was computed
+// from, so every later iteration repeats that assignment and those
+// centroids bit for bit.  chg[2][H] records per head whether the assignment
+// of iteration it changed any point (slot it & 1); once one did not, the
+// head's kernels of the remaining iterations return at once.  The outputs
+// are those of all iterations.  chg == nullptr: every iteration runs (the
+// cluster sort outside k-means).
+struct KmFix {
+  int32_t *chg;
+  int it;
+  // this iteration's assignment is the previous one's: nothing left to do
+  __device__ bool skip_assign(int h) const { return chg && it > 0 && chg[((it - 1) & 1) * gridDim.y + h] == 0; }
+  // this iteration's assignment changed nothing: its sort and update repeat the previous ones
+  __device__ bool skip_rest(int h) const { return chg && chg[(it & 1) * gridDim.y + h] == 0; }
+  // whether the assigning kernel compares against the previous assignment
+  __device__ bool track() const { return chg && it > 0; }
+  // an assigning wave reports its points: moved (it > 0), or the first iteration
+  __device__ void report(int h, bool moved, int lane) const {
+    if (!chg) return;
+    if (it == 0) {
+      if (blockIdx.x == 0 && threadIdx.x == 0) chg[h] = 1;
+    } else if (__ballot(moved) != 0ull && lane == 0) {
+      chg[(it & 1) * gridDim.y + h] = 1;
+    }
+  }
+};
+
 // ---------------------------------------------------------------------------
 // k-means (Lloyd).  Assign: distances in fp32 from fp32 copies of the
 // centroids, strict "<" so ties keep the lower index.  Update: the members of
@@ -30,8 +58,9 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 template <typename T>
 __global__ __launch_bounds__(128)
 void km_init(const T *__restrict__ X, const int32_t *__restrict__ init_idx, int N, int D, int k,
-             double *__restrict__ cent) {
+             double *__restrict__ cent, int32_t *__restrict__ chg) {
   const int h = blockIdx.y, j = blockIdx.x;
+  if (chg != nullptr && j == 0 && threadIdx.x < 2) chg[threadIdx.x * gridDim.y + h] = 0;
   const int src = init_idx[h * k + j];
   for (int e = threadIdx.x; e < D; e += blockDim.x)
     cent[((size_t)h * k + j) * D + e] = (double)to_f32<T>(X[((size_t)h * N + src) * D + e]);
@@ -40,14 +69,16 @@ void km_init(const T *__restrict__ X, const int32_t *__restrict__ init_idx, int 
 template <typename T, int D>
 __global__ __launch_bounds__(256)
 void km_assign(const T *__restrict__ X, const double *__restrict__ cent, int N, int k,
-               int32_t *__restrict__ assign) {
+               int32_t *__restrict__ assign, KmFix fx) {
   extern __shared__ float cs[];  // [k][D]
   const int h = blockIdx.y;
+  if (fx.skip_assign(h)) return;
   const double *ch = cent + (size_t)h * k * D;
   for (int e = threadIdx.x; e < k * D; e += blockDim.x) cs[e] = (float)ch[e];
   __syncthreads();
-  const int n = blockIdx.x * blockDim.x + threadIdx.x;
-  if (n >= N) return;
+  const int n0 = blockIdx.x * blockDim.x + threadIdx.x;
+  const bool in = n0 < N;
+  const int n = in ? n0 : N - 1;   // lanes past N compute a real point and store nothing
   const T *xr = X + ((size_t)h * N + n) * D;
   float x[D];
 #pragma unroll
@@ -67,7 +98,12 @@ void km_assign(const T *__restrict__ X, const double *__restrict__ cent, int N, 
       arg = j;
     }
   }
-  assign[(size_t)h * N + n] = arg;
+  bool moved = false;
+  if (in) {
+    if (fx.track()) moved = assign[(size_t)h * N + n] != arg;
+    assign[(size_t)h * N + n] = arg;
+  }
+  fx.report(h, moved, threadIdx.x & 63);
 }
 
 // Assignment on the matrix cores (bf16 inputs).  ||x - c||^2 = ||x||^2 +
@@ -129,10 +165,11 @@ constexpr int kSortChunk = 1024;
 template <int D>
 __global__ __launch_bounds__(256)
 void km_assign_mfma(const bf16_t *__restrict__ X, const float *__restrict__ tab, int N, int k, int kpad,
-                    int32_t *__restrict__ assign) {
+                    int32_t *__restrict__ assign, KmFix fx) {
   using TB = KmTab<D>;
   extern __shared__ __attribute__((aligned(16))) float kt[];   // the head's table
   const int h = blockIdx.y;
+  if (fx.skip_assign(h)) return;
   const size_t nf = TB::floats(kpad);
   const float *th = tab + (size_t)h * nf;
   for (size_t i = threadIdx.x * 4; i < nf; i += 256 * 4) {
@@ -208,10 +245,19 @@ void km_assign_mfma(const bf16_t *__restrict__ X, const float *__restrict__ tab,
   };
   merge(best0, arg0);
   merge(best1, arg1);
+  bool moved = false;
   if (hi == 0) {
-    if (p0 < N) assign[(size_t)h * N + p0] = arg0;
-    if (p1 < N) assign[(size_t)h * N + p1] = arg1;
+    int32_t *a = assign + (size_t)h * N;
+    if (p0 < N) {
+      if (fx.track()) moved |= a[p0] != arg0;
+      a[p0] = arg0;
+    }
+    if (p1 < N) {
+      if (fx.track()) moved |= a[p1] != arg1;
+      a[p1] = arg1;
+    }
   }
+  fx.report(h, moved, lane);
 }
 
 // The assignment for d = 64 on the bf16 matrix cores.  Each fp64 centroid
@@ -300,11 +346,12 @@ constexpr int kKmWaves = 12;
 template <int D>
 __global__ __launch_bounds__(64 * kKmWaves)
 void km_assign_bf3(const bf16_t *__restrict__ X, const float *__restrict__ tab, int N, int k, int kpad,
-                   int32_t *__restrict__ assign, int32_t *__restrict__ cnt) {
+                   int32_t *__restrict__ assign, int32_t *__restrict__ cnt, KmFix fx) {
   using TB = KmTab3<D>;
   constexpr int NT = 64 * kKmWaves;
   extern __shared__ __attribute__((aligned(16))) float kt[];   // the head's table
   const int h = blockIdx.y;
+  if (fx.skip_assign(h)) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
   // B operands: dims 16 s + 8 hi .. + 7 of the lane's point
@@ -341,6 +388,7 @@ void km_assign_bf3(const bf16_t *__restrict__ X, const float *__restrict__ tab, 
   __syncthreads();
   const bf16_t *ct = reinterpret_cast<const bf16_t *>(kt);
   const float *cn = kt + (size_t)kpad * (TB::ROWH / 2);
+  bool moved = false;
   for (; grp < ngrp; grp += gstep) {
   const int p0 = grp * 64 + l32, p1 = p0 + 32;
   if (grp != wave * (int)gridDim.x + (int)blockIdx.x) {
@@ -399,16 +447,20 @@ void km_assign_bf3(const bf16_t *__restrict__ X, const float *__restrict__ tab, 
   if (hi == 0) {
     // the sort's per-chunk histograms (zeroed beforehand), counted here
     int32_t *ch = cnt + (size_t)h * ((N + kSortChunk - 1) / kSortChunk) * k;
+    int32_t *a = assign + (size_t)h * N;
     if (p0 < N) {
-      assign[(size_t)h * N + p0] = arg0;
+      if (fx.track()) moved |= a[p0] != arg0;
+      a[p0] = arg0;
       atomicAdd(ch + (size_t)(p0 / kSortChunk) * k + arg0, 1);
     }
     if (p1 < N) {
-      assign[(size_t)h * N + p1] = arg1;
+      if (fx.track()) moved |= a[p1] != arg1;
+      a[p1] = arg1;
       atomicAdd(ch + (size_t)(p1 / kSortChunk) * k + arg1, 1);
     }
   }
   }
+  fx.report(h, moved, lane);
 }
 
 // Centroid of cluster j = mean of its members.  Each thread loads 16 bytes
@@ -427,16 +479,23 @@ void km_assign_bf3(const bf16_t *__restrict__ X, const float *__restrict__ tab, 
 // block also writes centroid j's row of the next iteration's table, as the
 // prep kernels do (same values, same summation order of ||c||^2), which
 // saves a launch per iteration.  With cnt, it zeroes column j of the sort's
-// per-chunk counts for the next assignment to fill.
+// per-chunk counts for the next assignment to fill.  A head whose assignment
+// of this iteration changed no point skips its update (KmFix): the result
+// would be the centroids it already holds.
 template <typename T>
 __global__ __launch_bounds__(256)
 void km_update(const T *__restrict__ X, const int32_t *__restrict__ perm, const int32_t *__restrict__ offs, int N,
                int k, int D, double *__restrict__ cent, int32_t *__restrict__ sizes, float *__restrict__ tab,
-               int kpad, int tab3, int32_t *__restrict__ cnt) {
+               int kpad, int tab3, int32_t *__restrict__ cnt, KmFix fx) {
   constexpr int VE = 16 / sizeof(T);
   __shared__ double cv[128];
   __shared__ double part[256 * VE];
   const int h = blockIdx.y, j = blockIdx.x, t = threadIdx.x;
+  if (fx.chg != nullptr) {
+    // the next assignment's flag starts clear, whether or not this update runs
+    if (j == 0 && t == 0) fx.chg[((fx.it + 1) & 1) * gridDim.y + h] = 0;
+    if (fx.skip_rest(h)) return;
+  }
   const int tpr = D / VE, slots = 256 / tpr, slot = t / tpr, q = t % tpr;
   const int o0 = offs[(size_t)h * (k + 1) + j], o1 = offs[(size_t)h * (k + 1) + j + 1];
   const int len = o1 - o0;
@@ -520,9 +579,10 @@ void km_update(const T *__restrict__ X, const int32_t *__restrict__ perm, const 
 // order the chunk's 16 waves.  cnt is scratch of H * nchunks * k ints.
 
 __global__ __launch_bounds__(256)
-void sort_count(const int32_t *__restrict__ assign, int N, int k, int nch, int32_t *__restrict__ cnt) {
+void sort_count(const int32_t *__restrict__ assign, int N, int k, int nch, int32_t *__restrict__ cnt, KmFix fx) {
   __shared__ int32_t hist[256];
   const int h = blockIdx.y, ch = blockIdx.x, tid = threadIdx.x;
+  if (fx.skip_rest(h)) return;
   hist[tid] = 0;
   __syncthreads();
   const int32_t *a = assign + (size_t)h * N;
@@ -538,12 +598,13 @@ void sort_count(const int32_t *__restrict__ assign, int N, int k, int nch, int32
 // One thread per token of the chunk (kSortChunk threads, 16 waves).
 __global__ __launch_bounds__(kSortChunk)
 void sort_place(const int32_t *__restrict__ assign, int N, int k, int nch, const int32_t *__restrict__ cnt,
-                int32_t *__restrict__ perm, int32_t *__restrict__ offs) {
+                int32_t *__restrict__ perm, int32_t *__restrict__ offs, KmFix fx) {
   constexpr int NW = kSortChunk / 64;
   __shared__ int32_t start[256];
   __shared__ int32_t wcnt[NW][256];
   __shared__ int32_t wtot[4];
   const int h = blockIdx.y, ch = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (fx.skip_rest(h)) return;
   const int32_t *a = assign + (size_t)h * N;
   const int n = ch * kSortChunk + tid;
   // a token whose id is outside [0, k) is skipped: no cluster counts it (as
@@ -617,10 +678,11 @@ size_t sort_scratch_bytes(const Dims &dm, int k) {
 
 // counted: cnt already holds the per-chunk histograms of assign
 void launch_sort(const Dims &dm, const int32_t *assign, int k, int32_t *perm, int32_t *offs, int32_t *cnt,
-                 hipStream_t st, bool counted = false) {
+                 hipStream_t st, bool counted = false, KmFix fx = KmFix{nullptr, 0}) {
   const int nch = (dm.N + kSortChunk - 1) / kSortChunk;
-  if (!counted) hipLaunchKernelGGL(sort_count, dim3(nch, dm.H), dim3(256), 0, st, assign, dm.N, k, nch, cnt);
-  hipLaunchKernelGGL(sort_place, dim3(nch, dm.H), dim3(kSortChunk), 0, st, assign, dm.N, k, nch, cnt, perm, offs);
+  if (!counted) hipLaunchKernelGGL(sort_count, dim3(nch, dm.H), dim3(256), 0, st, assign, dm.N, k, nch, cnt, fx);
+  hipLaunchKernelGGL(sort_place, dim3(nch, dm.H), dim3(kSortChunk), 0, st, assign, dm.N, k, nch, cnt, perm, offs,
+                     fx);
 }
 
 // ---------------------------------------------------------------------------
@@ -781,7 +843,8 @@ size_t kmeans_ws_bytes(const Dims &dm, int k) {
   const int kpad = (k + 31) / 32 * 32;
   const size_t tab = dm.d == 64 ? KmTab3<64>::floats(kpad) : KmTab<128>::floats(kpad);
   return align256((size_t)dm.H * dm.N * sizeof(int32_t)) + align256((size_t)dm.H * (k + 1) * sizeof(int32_t)) +
-         align256((size_t)dm.H * tab * sizeof(float)) + sort_scratch_bytes(dm, k);
+         align256((size_t)dm.H * tab * sizeof(float)) + sort_scratch_bytes(dm, k) +
+         align256((size_t)2 * dm.H * sizeof(int32_t));
 }
 
 hipError_t launch_kmeans(const Dims &dm, bool bf16, const void *X, int k, int iters, const int32_t *init_idx,
@@ -792,12 +855,13 @@ hipError_t launch_kmeans(const Dims &dm, bool bf16, const void *X, int k, int it
   const int kpad = (k + 31) / 32 * 32;
   const size_t tab_floats = dm.d == 64 ? KmTab3<64>::floats(kpad) : KmTab<128>::floats(kpad);
   int32_t *scnt = (int32_t *)((char *)tab + align256((size_t)dm.H * tab_floats * sizeof(float)));
+  int32_t *chg = (int32_t *)((char *)scnt + sort_scratch_bytes(dm, k));   // [2][H], see KmFix
   if (bf16)
     hipLaunchKernelGGL(km_init<bf16_t>, dim3(k, dm.H), dim3(128), 0, st, (const bf16_t *)X, init_idx, dm.N, dm.d, k,
-                       centroids);
+                       centroids, chg);
   else
     hipLaunchKernelGGL(km_init<float>, dim3(k, dm.H), dim3(128), 0, st, (const float *)X, init_idx, dm.N, dm.d, k,
-                       centroids);
+                       centroids, chg);
   // Assignment: bf16, d = 64 on the bf16 matrix cores (three-term table);
   // bf16, d = 128 on the fp32 matrix cores (fp32 table); fp32 points on the
   // vector ALUs.  With k <= 256 the tables fit in LDS (at most 101 and 137
@@ -826,26 +890,27 @@ hipError_t launch_kmeans(const Dims &dm, bool bf16, const void *X, int k, int it
   else if (mfma)
     hipLaunchKernelGGL(km_prep<128>, pgrid, dim3(256), 0, st, centroids, k, kpad, tab);
   for (int it = 0; it < iters; ++it) {
+    const KmFix fx{chg, it};
     if (bf3)
       hipLaunchKernelGGL(km_assign_bf3<64>, dim3(g3, dm.H), dim3(64 * kKmWaves), lds, st, (const bf16_t *)X, tab,
-                         dm.N, k, kpad, assign, scnt);
+                         dm.N, k, kpad, assign, scnt, fx);
     else if (mfma)
       hipLaunchKernelGGL(km_assign_mfma<128>, grid, dim3(256), lds, st, (const bf16_t *)X, tab, dm.N, k, kpad,
-                         assign);
+                         assign, fx);
     else if (dm.d == 64)
       hipLaunchKernelGGL((km_assign<float, 64>), grid, dim3(256), lds, st, (const float *)X, centroids, dm.N, k,
-                         assign);
+                         assign, fx);
     else
       hipLaunchKernelGGL((km_assign<float, 128>), grid, dim3(256), lds, st, (const float *)X, centroids, dm.N, k,
-                         assign);
-    launch_sort(dm, assign, k, perm, offs, scnt, st, bf3);
+                         assign, fx);
+    launch_sort(dm, assign, k, perm, offs, scnt, st, bf3, fx);
     float *const next_tab = ((mfma || bf3) && it + 1 < iters) ? tab : nullptr;
     if (bf16)
       hipLaunchKernelGGL(km_update<bf16_t>, dim3(k, dm.H), dim3(256), 0, st, (const bf16_t *)X, perm, offs, dm.N, k,
-                         dm.d, centroids, sizes, next_tab, kpad, bf3 ? 1 : 0, bf3 ? scnt : nullptr);
+                         dm.d, centroids, sizes, next_tab, kpad, bf3 ? 1 : 0, bf3 ? scnt : nullptr, fx);
     else
       hipLaunchKernelGGL(km_update<float>, dim3(k, dm.H), dim3(256), 0, st, (const float *)X, perm, offs, dm.N, k,
-                         dm.d, centroids, sizes, next_tab, kpad, 0, nullptr);
+                         dm.d, centroids, sizes, next_tab, kpad, 0, nullptr, fx);
   }
   return hipGetLastError();
 }

@@ -128,6 +128,51 @@ def test_kmeans_small_shapes(N, d, k, iters, dtype):
         np.testing.assert_allclose(c[h].cpu().numpy(), oc, rtol=1e-12, atol=1e-12)
 
 
+# Heads that reach a fixed point of Lloyd's map (an assignment equal to the
+# previous one) after different numbers of iterations, or not within the
+# run: (sigma, seed) of a 24-component mixture per head, and the iteration
+# after which the oracle's assignment stops changing, for the record.
+_FIXED_POINT_HEADS = {
+    (64, "bf16"): [(0.5, 5), (6.0, 7), (6.0, 6), (6.0, 5)],     # 1, 4, 6, 7
+    (64, "f32"): [(0.5, 5), (5.0, 5), (6.0, 5), (6.5, 5)],      # 1, 4, 7, 11
+    (128, "bf16"): [(0.5, 5), (5.0, 5), (6.0, 6), (6.0, 7)],    # 1, 3, 5, 7 (sigma x 1.41)
+    (128, "f32"): [(0.5, 5), (5.0, 5), (6.0, 7), (7.0, 5)],     # 1, 3, 7, 8 (sigma x 1.41)
+}
+
+
+@pytest.mark.parametrize("iters", [5, 10])
+@pytest.mark.parametrize("d,dtype", sorted(_FIXED_POINT_HEADS))
+def test_kmeans_heads_reaching_a_fixed_point_at_different_iterations(d, dtype, iters):
+    """Each head stops its iterations once its assignment stands still; the
+    outputs must still be those of all iterations, head by head.  The second
+    call reuses the output buffers (the first iteration compares against
+    nothing)."""
+    from synth.generators import f32_to_bf16_bits
+    N, k = 900, 24
+    xs, inits = [], []
+    for sig, seed in _FIXED_POINT_HEADS[(d, dtype)]:
+        rng = np.random.default_rng(seed)
+        comp = rng.integers(0, k, size=N)
+        comp[:k] = np.arange(k)
+        means = rng.standard_normal((k, d)).astype(np.float32) * 4
+        s = sig * (1 if d == 64 else 1.41)
+        xs.append(means[comp] + s * rng.standard_normal((N, d)).astype(np.float32))
+        inits.append([np.flatnonzero(comp == j)[0] for j in range(k)])
+    x32 = np.stack(xs)
+    x = f32_to_bf16_bits(x32) if dtype == "bf16" else x32
+    init = np.asarray(inits, dtype=np.int32)
+    xd = to_dev(x, dtype)
+    a, c, s_ = svg.svg_kmeans(xd, k, 10 if iters == 5 else 3, ints(init))
+    a, c, s_ = svg.svg_kmeans(xd, k, iters, ints(init), assign=a, centroids=c, sizes=s_)
+    sync()
+    for h in range(len(inits)):
+        oa, oc, os_, margin, ratio = osvg2.kmeans(as_f64(x[h], dtype), init[h], iters, f32_audit=True)
+        assert ratio > 1.01, (h, ratio)
+        np.testing.assert_array_equal(a[h].cpu().numpy(), oa)
+        np.testing.assert_array_equal(s_[h].cpu().numpy(), os_)
+        np.testing.assert_allclose(c[h].cpu().numpy(), oc, rtol=1e-12, atol=1e-12)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_kmeans_duplicate_init_tie_goes_to_lower_index(dtype):
     H, N, d = 1, 64, 64
