@@ -413,6 +413,41 @@ def test_varlen_vt_random_clusters_against_oracle(N, d, kq, kk, p):
             check_close(to_f64(o)[h], ref, BF16_MAX_ABS, BF16_REL_L2, f"{name} varlen head {h}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_varlen_lists_at_tile_boundaries(d):
+    """Selected lists of 1, 64 (one whole tile), 512 (eight), 513 (a 1-key
+    last tile), 2,063 and all 3,000 keys, and none, on query clusters of 1
+    to 2,049 rows (up to 17 128-row chunks), against the oracle's
+    token-exact definition."""
+    H = 2
+    sizes_k = [512, 1, 63, 64, 2000, 360]                 # N = 3000
+    sizes_q = [300, 129, 1, 200, 64, 257, 2049]
+    N = sum(sizes_k)
+    assert sum(sizes_q) == N
+    lists = [[0], [0, 1], [2, 4], [3], [1], list(range(6)), []]
+    kq, kk = len(sizes_q), len(sizes_k)
+    rng = np.random.default_rng(17)
+    aq = np.stack([rng.permutation(np.repeat(np.arange(kq), sizes_q)) for _ in range(H)]).astype(np.int32)
+    ak = np.stack([rng.permutation(np.repeat(np.arange(kk), sizes_k)) for _ in range(H)]).astype(np.int32)
+    ptr = np.zeros((H, kq + 1), np.int32)
+    idx = np.zeros((H, kq * kk), np.int32)
+    for h in range(H):
+        flat = [j for l in lists for j in l]
+        idx[h, :len(flat)] = flat
+        ptr[h, 1:] = np.cumsum([len(l) for l in lists])
+    q, k, v = random_qkv(H, N, d, seed=d, dtype="bf16", scale=1.5)
+    pq, oq = svg.svg_cluster_permute(ints(aq), kq, d)
+    pk, ok = svg.svg_cluster_permute(ints(ak), kk, d)
+    qd, kd, vd = (to_dev(t, "bf16") for t in (q, k, v))
+    qp, kp = svg.svg_permute_rows(qd, pq), svg.svg_permute_rows(kd, pk)
+    o = svg.svg_varlen_attn(qp, kp, svg.svg_permute_rows(vd, pk), oq, ok, ints(ptr), ints(idx), q_perm=pq)
+    sync()
+    for h in range(H):
+        ref = osvg2.varlen_attention(*(as_f64(x[h], "bf16") for x in (q, k, v)), aq[h], ak[h], ptr[h], idx[h])
+        assert np.all(ref[aq[h] == 6] == 0.0)
+        check_close(to_f64(o)[h], ref, BF16_MAX_ABS, BF16_REL_L2, f"varlen tile boundaries head {h}")
+
+
 def test_varlen_vt_rejects_uncovered_shapes():
     """d outside {64, 128} or more than 2048 windows a head: an error, no
     launch."""
