@@ -172,7 +172,10 @@ and writes the tensor and reads the order.  The attention kernels are bound by t
 cores, not by memory: their line is there for the traffic (the sparse kernel fetches ~18x its
 algorithmic bytes, ~78% of it served by the XCD L2s, at ~1.1 TB/s).  The SVG2 workload (36 MB
 of Q and K) stays in the L2s and the 256 MB Infinity Cache between launches, so its k-means
-kernels run at a few microseconds each and are bound by launch and per-kernel latency.  The
+kernels run at a few microseconds each and are bound by launch and per-kernel latency.  A
+k-means head whose assignment stood still has its later rounds' kernels return at once: their
+launches (FETCH_SIZE under 1% of the algorithmic bytes) have rows of their own, "round after the
+fixed point".  The
 local-window assignment (`hva_assign`) reads each token's row once and runs its distances on the
 vector ALUs (a float32 expression the oracle evaluates identically), so its MFMA column is empty.
 
@@ -254,6 +257,12 @@ def record_counters(root):
         ("hva", "permute_rows_kernel"): 2 * V.H * V.N * V.d * 2 + V.H * V.N * 4,
     }
 
+    KMEANS_ROUND_KERNELS = {("svg2", "km_assign_bf3<64>"), ("svg2", "km_update<unsigned short>"),
+                            ("svg2", "sort_place"), ("hva", "km_assign_bf3<64>"),
+                            ("hva", "km_update<unsigned short>"), ("hva", "sort_place")}
+    alg[("hva", "km_assign_bf3<64>")] = V.H * V.N * V.d * 2 + V.H * V.N * 4
+    alg[("hva", "km_update<unsigned short>")] = V.H * V.N * V.d * 2 + 2 * V.H * V.N * 4
+    alg[("hva", "sort_place")] = 2 * V.H * V.N * 4
     fetch_scale = write_scale = None
     rows = []
     for prog in ("layer", "svg2", "hva"):
@@ -275,6 +284,8 @@ def record_counters(root):
                     k += " (V gather)"
                 else:
                     k += " (attention V^T)" if grids[d] == attn_vt_grid else " (profiler V^T)"
+            if (prog, k) in KMEANS_ROUND_KERNELS and fv[(d, "FETCH_SIZE")] * 1024.0 < 0.01 * alg[(prog, k)]:
+                k += " (round after the fixed point)"   # the head's kernels returned at once
             groups[k].append((d, dur))
         for k, ds in sorted(groups.items()):
             t = sum(dur for _, dur in ds) / len(ds)
@@ -1223,7 +1234,7 @@ def main():
         torch.cuda.empty_cache()
         s2 = bench_svg2(args, steps=20, warmup=3)
         result["svg2"] = {k_: s2[k_] for k_ in ("ms_per_step", "stage_ms", "one_stream_ms", "eager_two_stream_ms",
-                                                 "varlen_tflops", "gather_gbs")}
+                                                 "varlen_tflops", "gather_gbs", "kmeans_fixed_point_round")}
         result["svg2"]["pair_density"] = s2["config"]["pair_density"]
         torch.cuda.empty_cache()
         result["hva"] = bench_hva(args, steps=20, warmup=3)

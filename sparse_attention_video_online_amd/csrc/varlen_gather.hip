@@ -83,23 +83,27 @@ void varlen_gather(const bf16_t *__restrict__ Qp, const bf16_t *__restrict__ Kp,
   __shared__ int segv[257];                   // start of each selected range in the concatenation
   __shared__ int segr[256];                   // its first row in Kp / Vp
   __shared__ int tmp[NW + 1];
-  __shared__ int s_cl, s_r0, s_r1;
+  __shared__ int s_cl, s_r0, s_r1, s_p0, s_p1;
   const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
 
-  // 1. this work-group's (query cluster, BQ-row chunk)
+  // 1. this work-group's (query cluster, BQ-row chunk); each thread also
+  // loads its cluster's pair-list bounds, so the finder hands them on
   const int32_t *qo = q_offs + (size_t)h * (kq + 1);
+  const int32_t *ptr = pair_ptr + (size_t)h * (kq + 1);
   if (tid == 0) s_cl = -1;
   {
     const int t = blockIdx.x;
     int done = 0;
     for (int i0 = 0; i0 < kq; i0 += NT) {
       const int i = i0 + tid;
-      int a = 0, b = 0;
+      int a = 0, b = 0, pa = 0, pb = 0;
       if (i < kq) {
         a = qo[i];
         b = qo[i + 1];
+        pa = ptr[i];
+        pb = ptr[i + 1];
       }
       const int nch = (b - a + BQ - 1) / BQ;
       const int incl = done + vg_inclusive_sum<NW>(nch, lane, wave, tmp);
@@ -107,6 +111,8 @@ void varlen_gather(const bf16_t *__restrict__ Qp, const bf16_t *__restrict__ Kp,
         s_cl = i;
         s_r0 = a + (t - (incl - nch)) * BQ;
         s_r1 = min(b, s_r0 + BQ);
+        s_p0 = pa;
+        s_p1 = pb;
       }
       __syncthreads();
       done += tmp[NW];
@@ -117,11 +123,18 @@ void varlen_gather(const bf16_t *__restrict__ Qp, const bf16_t *__restrict__ Kp,
   const int cl = s_cl;
   if (cl < 0) return;                        // past the head's last chunk (uniform)
   const int r0 = s_r0, r1 = s_r1;
+  // the wave's 32 query rows and their output rows, loaded now so that the
+  // loads overlap the dependent loads of step 2
+  const size_t hoff = (size_t)h * N * D;
+  const int qrow = r0 + wave * 32 + l32;
+  const bool qvalid = qrow < r1;
+  bf16x8 qf[D / 16];
+  load_q<D>(Qp + hoff, qvalid ? qrow : -1, hi, qf);
+  const int dst = !qvalid ? -1 : q_perm ? q_perm[(size_t)h * N + qrow] : qrow;
 
   // 2. the selected ranges, laid end to end
-  const int32_t *ptr = pair_ptr + (size_t)h * (kq + 1);
-  const int32_t *sel = pair_idx + (size_t)h * kq * kk + ptr[cl];
-  const int nsel = ptr[cl + 1] - ptr[cl];
+  const int32_t *sel = pair_idx + (size_t)h * kq * kk + s_p0;
+  const int nsel = s_p1 - s_p0;
   const int32_t *ko = k_offs + (size_t)h * (kk + 1);
   {
     int run = 0;
@@ -146,12 +159,7 @@ void varlen_gather(const bf16_t *__restrict__ Qp, const bf16_t *__restrict__ Kp,
   __syncthreads();
   const int nkeys = segv[nsel];
 
-  // 3. the wave's 32 query rows
-  const size_t hoff = (size_t)h * N * D;
-  const int qrow = r0 + wave * 32 + l32;
-  const bool qvalid = qrow < r1;
-  bf16x8 qf[D / 16];
-  load_q<D>(Qp + hoff, qvalid ? qrow : -1, hi, qf);
+  // 3. the output accumulators
   f32x16 o[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
@@ -302,12 +310,7 @@ void varlen_gather(const bf16_t *__restrict__ Qp, const bf16_t *__restrict__ Kp,
     __syncthreads();                          // the row table is rebuilt for the next chunk
   }
 
-  bf16_t *orow = nullptr;
-  if (qvalid) {
-    const int dst = q_perm ? q_perm[(size_t)h * N + qrow] : qrow;
-    orow = O + hoff + (size_t)dst * D;
-  }
-  store_o<D>(orow, o, l_run, hi);
+  store_o<D>(qvalid ? O + hoff + (size_t)dst * D : nullptr, o, l_run, hi);
 }
 
 template <int D, int BQ>
