@@ -63,7 +63,8 @@ svg_status svg_kmeans(const svg_dims *dims, svg_dtype dtype, const void *X, int3
  * capture, tight serving loops, harnesses that forbid hipMalloc):
  *
  * svg_kmeans_noalloc: svg_kmeans with no workspace argument.  Its scratch
- *   (cluster order, offsets, centroid tables, sort counts) lives in a device
+ *   (cluster order, offsets, centroid tables, sort counts, the per-head
+ *   fixed-point flags) lives in a device
  *   array the library holds, SVG_KMEANS_NOALLOC_SCRATCH_BYTES per GPU,
  *   allocated when the library's code is loaded on that GPU and kept until
  *   the process ends.  The call allocates nothing.  Outputs and errors are
